@@ -1,0 +1,250 @@
+/*
+ * moe_mi355x.h -- C ABI of the MI355X (gfx950) MoE expert-layer library.
+ *
+ * One Mixture-of-Experts layer on one GPU's share of experts: top-k routing or
+ * Router Replay of recorded expert ids, the expert-grouped token permutation,
+ * block-scaled FP8 e4m3 quantisation, an MFMA FP8 grouped GEMM with a fused
+ * SwiGLU epilogue, the weighted combine, and the training backward.
+ *
+ * Sources (cited by page and section):
+ *   [R3]  "RL at 1T scale: a deep dive into prime-rl performance", section
+ *         "Router Replay": routing decisions captured at inference are replayed
+ *         in the trainer; the record is shaped [num_layers, top_k, seq_len] and is
+ *         handled as an opaque tensor by device ops only (no host conversion).
+ *   [EP]  same page, sections "Wide Expert Parallelism" and "Parallelism
+ *         strategies / Expert Parallel": each GPU holds its own experts; tokens
+ *         are dispatched to them and combined back once per layer.
+ *   [FP8] same page, section "FP8 Training": trainer GEMMs run in block-scaled
+ *         FP8 as proposed by DeepSeek-V3 (here: 1x128 activation tiles, 128x128
+ *         weight tiles, fp32 scales, e4m3 codes).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers to caller-owned memory unless stated.  The
+ *     library never allocates device memory and never synchronises; every call
+ *     enqueues its kernels on `stream` and returns once they are launched.
+ *     Outputs are valid when the stream reaches that point; inputs must stay
+ *     unchanged until then.
+ *   - bf16 is passed as uint16_t bit patterns, FP8 as uint8_t OCP E4M3FN codes
+ *     (bias 7, max +-448, NaN 0x7F/0xFF, no infinity), scales as fp32, indices as
+ *     int32, all row-major and densely packed unless a leading dimension is given.
+ *   - Argument and shape errors are detected on the host before any HIP call and
+ *     return a negative moe_status; nothing is launched then.  moe_last_error()
+ *     returns a thread-local message for the last failure on the calling thread.
+ *   - Data-dependent problems (a replayed id out of range, a row capacity that is
+ *     too small) are reported by OR-ing MOE_FLAG_* bits into the nullable device
+ *     word `dev_status`; the library never clears it.  Kernels never write out of
+ *     bounds on such input.
+ *   - Calls are deterministic: the same inputs give bitwise-equal outputs.
+ *
+ * Supported shapes: hidden size d and expert FFN size f multiples of 128;
+ * 1 <= top_k <= 16; 1 <= E <= 1024; local experts [e0, e0+L) inside [0, E).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    MOE_ERR_SHAPE = -2,       /* sizes inconsistent or out of the supported range  */
+    MOE_ERR_UNSUPPORTED = -3, /* a mode or combination the library does not offer  */
+    MOE_ERR_WORKSPACE = -4,   /* workspace smaller than the required size          */
+    MOE_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed        */
+} moe_status;
+
+enum { MOE_FLAG_BAD_ID = 1, MOE_FLAG_DUP_ID = 2, MOE_FLAG_ROW_CAP = 4 };
+
+/* Rows of the expert-grouped layout are padded per expert to a multiple of this. */
+#define MOE_ROW_ALIGN 128
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Row capacity sufficient for any valid routing of T tokens with top_k = k onto L
+ * local experts: T*min(k, L) real rows + up to 127 padding rows per expert,
+ * rounded up to a multiple of 128.  Returns -1 for negative arguments. */
+int64_t moe_row_cap(int64_t T, int32_t k, int32_t L);
+
+/* ---- routing ------------------------------------------------------------- */
+
+/* Top-k routing over fp32 router logits.
+ * logits [T, E] fp32.  For each token, selects the k largest logits, ties broken
+ * by the lower expert id, with IEEE comparison (-0 == +0); ids[t, 0] is the
+ * largest.  Gates w[t, j] = softmax of the k selected logits (the full softmax
+ * renormalised over the selection).  Logits must be finite.
+ * Outputs: ids [T, k] int32, w [T, k] fp32.  T = 0 is a no-op.             */
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
+                   int32_t* ids, float* w, hipStream_t stream);
+
+/* Top-k routing that also records the selection for Router Replay [R3]: as
+ * moe_route_topk, and additionally writes rec[layer, j, s0 + t] = ids[t, j] into
+ * the record rec [n_layers, k, seq_len] int32 (the inference-side capture).
+ * Requires 0 <= layer < n_layers and s0 + T <= seq_len.                      */
+int moe_route_topk_capture(const float* logits, int64_t T, int32_t E, int32_t k,
+                           int32_t* ids, float* w,
+                           int32_t* rec, int32_t n_layers, int64_t seq_len,
+                           int32_t layer, int64_t s0, hipStream_t stream);
+
+/* Router Replay load [R3]: replays recorded expert ids instead of recomputing
+ * top-k.  rec [n_layers, k, seq_len] int32 is the recorded payload; the call
+ * processes tokens s0 .. s0+T-1 of layer `layer`:
+ *     ids[t, j] = rec[layer, j, s0 + t]            (verbatim, recorded slot order)
+ *     w[t, :]   = softmax of logits[t, ids[t, :]]  (max shift over the k gathered)
+ * logits [T, E] fp32 are the trainer's logits for those tokens.  A token with an
+ * id outside [0, E) sets MOE_FLAG_BAD_ID and gets w = 0 for all slots; a token
+ * with a repeated id sets MOE_FLAG_DUP_ID and keeps its computed gates.
+ * dev_status may be NULL (flags are then dropped).                           */
+int moe_replay_load(const int32_t* rec, int32_t n_layers, int32_t k, int64_t seq_len,
+                    int32_t layer, int64_t s0, int64_t T, const float* logits, int32_t E,
+                    int32_t* ids, float* w, int32_t* dev_status, hipStream_t stream);
+
+/* ---- dispatch (local permutation) [EP] ---------------------------------- */
+
+/* Workspace bytes moe_permute needs for T tokens, top-k k, L local experts. */
+int moe_permute_workspace(int64_t T, int32_t k, int32_t L, size_t* bytes);
+
+/* Expert-grouped permutation of the (token, slot) pairs whose expert lies in
+ * [e0, e0+L).  Pair p = t*k + j, local expert le = ids[t, j] - e0.
+ *   counts[e]   (int32 [L])     local pairs of expert e
+ *   offsets[e]  (int32 [L+1])   offsets[0] = 0, offsets[e+1] = offsets[e] +
+ *                               ceil(counts[e]/128)*128
+ *   row_pair[r] (int32 [row_cap]) pair held by row r, -1 for padding rows
+ *                               r < offsets[L]; entries at and past offsets[L]
+ *                               are left unchanged
+ *   pair_row[p] (int32 [T, k])  row of pair p, -1 for non-local pairs
+ * The pairs of expert e occupy rows offsets[e] ... in ascending p (stable).
+ * If offsets[L] > row_cap, MOE_FLAG_ROW_CAP is set and pairs whose row would be
+ * >= row_cap get pair_row = -1 (they are dropped, nothing is written out of
+ * bounds).  row_cap must be a multiple of 128; moe_row_cap() is always enough
+ * for distinct ids per token.
+ * Optional fused row gather (x != NULL): x [T, d] bf16.  For every real row r:
+ *   x_perm[r, :] = x[t(r), :]                        (if x_perm != NULL, bf16)
+ *   xq[r, :], xq_s[r, :] = 1x128 FP8 quantisation of x[t(r), :]   (if xq != NULL;
+ *                          xq [row_cap, d] u8, xq_s [row_cap, d/128] fp32)
+ * Padding rows of x_perm / xq / xq_s are not written.
+ * ws: device workspace of at least moe_permute_workspace() bytes.            */
+int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L,
+                int64_t row_cap, int32_t* counts, int32_t* offsets,
+                int32_t* row_pair, int32_t* pair_row,
+                const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq, float* xq_s,
+                void* ws, size_t ws_bytes, int32_t* dev_status, hipStream_t stream);
+
+/* ---- block-scaled FP8 quantisation [FP8] -------------------------------- */
+
+enum { MOE_TILE_1x128 = 0, MOE_TILE_128x128 = 1 };
+enum { MOE_SRC_BF16 = 0, MOE_SRC_F32 = 1 };
+
+/* Quantise src viewed as `groups` matrices of [rows, cols] (row stride ld
+ * elements, group stride rows*ld) to OCP e4m3 with one fp32 scale per tile:
+ *     a = max(max|v|, 2^-40);  inv = 448 / a;  s = a / 448  (fp32, correctly
+ *     rounded);  q = e4m3_rne_satfinite(fp32(v * inv))
+ * tile MOE_TILE_1x128:   q [groups*rows, cols], scales [groups*rows, cols/128]
+ * tile MOE_TILE_128x128: q [groups, rows, cols], scales [groups, rows/128, cols/128];
+ *                        if qT != NULL also the per-group transpose
+ *                        qT [groups, cols, rows] with scalesT [groups, cols/128, rows/128]
+ *                        (used by the dgrad GEMMs, which read the weights transposed).
+ * cols % 128 == 0; for 128x128 also rows % 128 == 0.                          */
+int moe_quant_fp8(const void* src, int32_t src_type, int64_t groups, int64_t rows,
+                  int64_t cols, int64_t ld, int32_t tile, uint8_t* q, float* scales,
+                  uint8_t* qT, float* scalesT, hipStream_t stream);
+
+/* 128x1 quantisation along rows of the expert-grouped layout, transposed output,
+ * for the wgrad GEMMs (operands re-quantised along their contraction axis, the
+ * token axis).  Source row r is  v[r, c] = fp32(w[p] * src[p / k, c])  for the
+ * pair p = row_pair[r] (w == NULL: v = src[p / k, c]); padding rows are 0.
+ * Tiles are the 128-row blocks [128b, 128b+128) for 128b < offsets[L] (every
+ * block lies inside one expert because segments are 128-aligned).
+ *   src [T, cols] bf16;  qT [cols, row_cap] u8;  sT [cols, row_cap/128] fp32.
+ * Columns at and past offsets[L] are left unchanged.                          */
+int moe_quant_fp8_rows_t(const uint16_t* src, const float* w, const int32_t* row_pair,
+                         const int32_t* offsets, int32_t L, int64_t row_cap, int32_t k,
+                         int64_t cols, uint8_t* qT, float* sT, hipStream_t stream);
+
+/* ---- grouped GEMM [FP8] ------------------------------------------------- */
+
+enum {
+    MOE_EPI_STORE_BF16 = 0,      /* out  = bf16 [row_cap, N]                             */
+    MOE_EPI_SWIGLU_Q8 = 1,       /* N = 2f: h = silu(G)*U (G = cols [0,f), U = [f,2f));
+                                    out = hq u8 [row_cap, f], out_s = [row_cap, f/128]   */
+    MOE_EPI_SWIGLU_Q8_SAVE = 2,  /* as SWIGLU_Q8, and out2 = bf16 [G, U] [row_cap, 2f]   */
+    MOE_EPI_STORE_F32 = 3,       /* out  = fp32 accumulators [row_cap, N] (inspection)  */
+    MOE_EPI_SWIGLU_F32 = 4,      /* out  = fp32 h [row_cap, f] before quantisation
+                                    (inspection of the fused quantiser's input)         */
+    MOE_EPI_DSWIGLU_Q8 = 5       /* backward through SwiGLU: acc = dH [row_cap, f],
+                                    epi_in = saved bf16 [G, U] [row_cap, 2f];
+                                    dG = dH*U*s(G)*(1+G*(1-s(G))), dU = dH*G*s(G) (s =
+                                    sigmoid); out = dGU q 1x128 [row_cap, 2f] + out_s
+                                    [row_cap, 2f/128]; out2 = dGU q 128x1 transposed
+                                    [2f, row_cap] + out2_s [2f, row_cap/128]; out3 =
+                                    recomputed h = G*s(G)*U q 128x1 transposed [f,
+                                    row_cap] + out3_s [f, row_cap/128]                 */
+};
+
+/* Per-expert GEMM over the expert-grouped rows: for expert e, real rows
+ * r in [offsets[e], offsets[e] + counts[e]):
+ *     acc[r, n] = sum over 128-blocks c of K:
+ *                 a_s[r, c] * b_s[e, n/128, c] * sum_i dec(a[r, 128c+i]) * dec(b[e, n, 128c+i])
+ * accumulated in fp32, then passed through the epilogue.
+ *   a [row_cap, K] e4m3, a_s [row_cap, K/128];  b [L, N, K] e4m3 (weights [out, in];
+ *   the dgrad products pass the transposed weights from moe_quant_fp8's qT),
+ *   b_s [L, N/128, K/128].  K, N multiples of 128.  Padding rows of the outputs
+ *   are not written.  Rows past row_cap are never touched.                   */
+int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* b, const float* b_s,
+                         const int32_t* counts, const int32_t* offsets, int32_t L,
+                         int64_t row_cap, int32_t N, int32_t K, int32_t epilogue,
+                         const uint16_t* epi_in, void* out, float* out_s,
+                         void* out2, float* out2_s, void* out3, float* out3_s,
+                         hipStream_t stream);
+
+/* Weight-gradient grouped GEMM: for every local expert e,
+ *     dW[e][m, n] = sum over the 128-row token blocks b of e's padded segment:
+ *                   aT_s[m, b] * bT_s[n, b] * sum_{r in b} dec(aT[m, r]) * dec(bT[n, r])
+ * accumulated in fp32 and stored as bf16.
+ *   aT [M, row_cap] e4m3, aT_s [M, row_cap/128]; bT [N, row_cap], bT_s [N, row_cap/128]
+ *   (from moe_quant_fp8_rows_t or the DSWIGLU epilogue); dW [L, M, N] bf16.
+ *   An expert with no rows gets dW[e] = 0.  M, N multiples of 128.           */
+int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8_t* bT,
+                               const float* bT_s, const int32_t* offsets, int32_t L,
+                               int64_t row_cap, int32_t M, int32_t N, uint16_t* dW,
+                               hipStream_t stream);
+
+/* ---- combine [EP] ------------------------------------------------------- */
+
+/* Weighted combine (the local half of the per-layer combine):
+ *     y[t, :] = bf16( sum over local slots j, ascending, of w[t, j] * y_perm[pair_row[t, j], :] )
+ * summed in fp32; tokens with no local pair get +0.  w == NULL uses weights of 1
+ * (the unpermute-sum of the input gradient).
+ *   y_perm [row_cap, d] bf16, pair_row [T, k], w [T, k] fp32, y [T, d] bf16.  */
+int moe_unpermute_combine(const uint16_t* y_perm, const int32_t* pair_row, const float* w,
+                          int64_t T, int32_t k, int32_t d, int64_t row_cap, uint16_t* y,
+                          hipStream_t stream);
+
+/* Combine backward: for every local pair (t, j) held by row r = pair_row[t, j]:
+ *     dY[r, :]     = fp32(w[t, j] * dy[t, :])  -> 1x128 e4m3 (if dyq != NULL):
+ *                    dyq [row_cap, d] u8, dyq_s [row_cap, d/128] fp32
+ *     d_gate[t, j] = sum_n dy[t, n] * y_perm[r, n]   (fp32; 0 for non-local slots)
+ *   dy [T, d] bf16, y_perm [row_cap, d] bf16 (the forward's expert outputs),
+ *   pair_row [T, k], w [T, k] fp32, d_gate [T, k] fp32.
+ * The 128x1 transposed copy of dY for wgrad comes from moe_quant_fp8_rows_t.   */
+int moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, const int32_t* pair_row,
+                         const float* w, int64_t T, int32_t k, int32_t d, int64_t row_cap,
+                         uint8_t* dyq, float* dyq_s, float* d_gate, hipStream_t stream);
+
+/* Backward of the softmax over the selected logits (complete when every expert
+ * is local; under expert parallelism d_gate must first be summed over GPUs):
+ *     d_logits[t, ids[t, j]] += w[t, j] * (d_gate[t, j] - sum_j' w[t, j'] d_gate[t, j'])
+ * and 0 at unselected experts.  d_logits [T, E] fp32.                          */
+int moe_gate_backward(const float* d_gate, const float* w, const int32_t* ids, int64_t T,
+                      int32_t k, int32_t E, float* d_logits, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

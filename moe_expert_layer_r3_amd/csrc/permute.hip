@@ -1,0 +1,260 @@
+// Dispatch on one GPU's share of experts ("RL at 1T scale", sections "Wide
+// Expert Parallelism" and "Expert Parallel"): the per-layer dispatch becomes a
+// local, stable, expert-grouped permutation of the (token, slot) pairs.
+//
+//   1. hist    : per chunk of CHUNK pairs, count local pairs per expert (LDS)
+//   2. scan    : per expert, exclusive scan of the chunk counts; counts; the
+//                128-aligned offsets; padding rows of row_pair = -1
+//   3. scatter : per chunk, rank every pair among the earlier pairs of its
+//                expert (wave ballots, in pair order) and write row_pair /
+//                pair_row -- deterministic, no order-dependent atomics
+//   4. gather  : token-major: each token row of x is read once, quantised to
+//                1x128 e4m3 once, and written to each of its local rows.
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int PCHUNK = 4096;       // pairs per chunk (one block)
+constexpr int PBLOCK = 256;        // threads per block in hist / scatter
+constexpr int PWAVES = PBLOCK / 64;
+constexpr int PER_WAVE = PCHUNK / PWAVES;  // 1024 consecutive pairs per wave
+constexpr int MAXL = 1024;
+
+__global__ __launch_bounds__(PBLOCK) void perm_hist_kernel(const int32_t* __restrict__ ids, int64_t P, int e0,
+                                                           int L, int32_t* __restrict__ chunk_counts) {
+    __shared__ int cnt[MAXL];
+    for (int e = threadIdx.x; e < L; e += PBLOCK) cnt[e] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * PCHUNK;
+    for (int i = threadIdx.x; i < PCHUNK; i += PBLOCK) {
+        int64_t p = base + i;
+        if (p < P) {
+            int le = ids[p] - e0;
+            if (le >= 0 && le < L) atomicAdd(&cnt[le], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < L; e += PBLOCK) chunk_counts[(int64_t)blockIdx.x * L + e] = cnt[e];
+}
+
+// Single block of 1024 threads; thread e owns expert e.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunk, int L,
+                                                         int64_t row_cap, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ row_pair,
+                                                         int32_t* __restrict__ status) {
+    __shared__ int64_t part[1024];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < L) {
+        for (int c = 0; c < nchunk; ++c) {
+            int v = chunk_counts[(int64_t)c * L + e];
+            chunk_counts[(int64_t)c * L + e] = run;
+            run += v;
+        }
+    }
+    const int64_t padded = e < L ? ((int64_t)run + MOE_ROW_ALIGN - 1) / MOE_ROW_ALIGN * MOE_ROW_ALIGN : 0;
+    // inclusive scan of padded sizes over the block (Hillis-Steele in LDS)
+    part[e] = padded;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        int64_t add = e >= off ? part[e - off] : 0;
+        __syncthreads();
+        part[e] += add;
+        __syncthreads();
+    }
+    if (e < L) {
+        const int64_t end = part[e];
+        const int64_t start = end - padded;
+        counts[e] = run;
+        offsets[e + 1] = (int32_t)(end > 0x7FFFFFFF ? 0x7FFFFFFF : end);
+        if (e == 0) offsets[0] = 0;
+        for (int64_t r = start + run; r < end; ++r)
+            if (r < row_cap) row_pair[r] = -1;
+        if (e == L - 1 && end > row_cap && status) atomicOr(status, MOE_FLAG_ROW_CAP);
+    }
+}
+
+__global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __restrict__ ids, int64_t P, int e0,
+                                                              int L, int64_t row_cap,
+                                                              const int32_t* __restrict__ chunk_base,
+                                                              const int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ row_pair,
+                                                              int32_t* __restrict__ pair_row) {
+    // run[w][e]: pairs of expert e seen so far by wave w (first pass: totals)
+    __shared__ int run[PWAVES][MAXL];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int e = threadIdx.x; e < L; e += PBLOCK)
+        for (int w = 0; w < PWAVES; ++w) run[w][e] = 0;
+    __syncthreads();
+    const int64_t wbase = (int64_t)blockIdx.x * PCHUNK + (int64_t)wave * PER_WAVE;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    // pass 1: per-wave totals per expert
+    for (int it = 0; it < PER_WAVE / 64; ++it) {
+        int64_t p = wbase + it * 64 + lane;
+        int le = -1;
+        if (p < P) {
+            le = ids[p] - e0;
+            if (le < 0 || le >= L) le = -1;
+        }
+        uint64_t active = __ballot(le >= 0);
+        while (active) {
+            int leader = __ffsll((unsigned long long)active) - 1;
+            int e = __shfl(le, leader);
+            uint64_t m = __ballot(le == e) & active;
+            if (lane == leader) run[wave][e] += __popcll(m);
+            active &= ~m;
+        }
+    }
+    __syncthreads();
+    // exclusive prefix over waves, per expert
+    for (int e = threadIdx.x; e < L; e += PBLOCK) {
+        int acc = 0;
+        for (int w = 0; w < PWAVES; ++w) {
+            int v = run[w][e];
+            run[w][e] = acc;
+            acc += v;
+        }
+    }
+    __syncthreads();
+    // pass 2: ranks in pair order, write rows
+    for (int it = 0; it < PER_WAVE / 64; ++it) {
+        int64_t p = wbase + it * 64 + lane;
+        int le = -1;
+        if (p < P) {
+            le = ids[p] - e0;
+            if (le < 0 || le >= L) le = -1;
+        }
+        int64_t row = -1;
+        uint64_t active = __ballot(le >= 0);
+        while (active) {
+            int leader = __ffsll((unsigned long long)active) - 1;
+            int e = __shfl(le, leader);
+            uint64_t m = __ballot(le == e) & active;
+            int before = run[wave][e];
+            if (le == e) {
+                row = (int64_t)offsets[e] + chunk_base[(int64_t)blockIdx.x * L + e] + before +
+                      __popcll(m & lt_mask);
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (lane == leader) run[wave][e] = before + __popcll(m);
+            __builtin_amdgcn_wave_barrier();
+            active &= ~m;
+        }
+        if (p < P) {
+            if (row >= row_cap) row = -1;
+            pair_row[p] = (int32_t)row;
+            if (row >= 0) row_pair[row] = (int32_t)p;
+        }
+    }
+}
+
+// Token-major gather with fused 1x128 quantisation.  A work item is one
+// 128-wide tile of one token row, handled by 16 lanes of 8 bf16 values each.
+__global__ __launch_bounds__(256) void gather_quant_kernel(const uint16_t* __restrict__ x, int64_t T, int d, int k,
+                                                           const int32_t* __restrict__ pair_row,
+                                                           uint16_t* __restrict__ x_perm,
+                                                           uint8_t* __restrict__ xq, float* __restrict__ xq_s) {
+    const int ntile = d >> 7;
+    const int64_t item = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+    const int sub = threadIdx.x & 15;
+    const bool live = item < T * ntile;
+    const int64_t t = live ? item / ntile : 0;
+    const int tile = live ? (int)(item - t * ntile) : 0;
+    bool any_local = false;
+    if (live)
+        for (int j = 0; j < k; ++j) any_local |= pair_row[t * k + j] >= 0;
+    // all 16 lanes of an item agree; items never straddle a group of 16 lanes
+    if (!any_local) return;
+    const int64_t col = (int64_t)tile * 128 + sub * 8;
+    const uint4 raw = *reinterpret_cast<const uint4*>(x + t * d + col);
+    float v[8];
+    v[0] = bf16_lo(raw.x); v[1] = bf16_hi(raw.x);
+    v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);
+    v[4] = bf16_lo(raw.z); v[5] = bf16_hi(raw.z);
+    v[6] = bf16_lo(raw.w); v[7] = bf16_hi(raw.w);
+    uint2 packed = make_uint2(0, 0);
+    float s = 0.f;
+    if (xq) {
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+        am = group_max<16>(am);
+        TileScale ts = tile_scale(am);
+        s = ts.s;
+        packed.x = cvt_e4m3x4(v[0] * ts.inv, v[1] * ts.inv, v[2] * ts.inv, v[3] * ts.inv);
+        packed.y = cvt_e4m3x4(v[4] * ts.inv, v[5] * ts.inv, v[6] * ts.inv, v[7] * ts.inv);
+    }
+    for (int j = 0; j < k; ++j) {
+        const int64_t r = pair_row[t * k + j];
+        if (r < 0) continue;
+        if (x_perm) *reinterpret_cast<uint4*>(x_perm + r * d + col) = raw;
+        if (xq) {
+            *reinterpret_cast<uint2*>(xq + r * d + col) = packed;
+            if (sub == 0) xq_s[r * ntile + tile] = s;
+        }
+    }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+static int64_t perm_chunks(int64_t T, int32_t k) { return (T * k + PCHUNK - 1) / PCHUNK; }
+
+extern "C" int moe_permute_workspace(int64_t T, int32_t k, int32_t L, size_t* bytes) {
+    MOE_REQUIRE(bytes, MOE_ERR_NULL, "permute_workspace: NULL bytes");
+    MOE_REQUIRE(T >= 0 && k >= 1 && k <= 16 && L >= 1 && L <= MAXL, MOE_ERR_SHAPE,
+                "permute_workspace: bad T/k/L");
+    int64_t n = perm_chunks(T, k);
+    *bytes = (size_t)((n > 0 ? n : 1) * L * sizeof(int32_t));
+    return MOE_OK;
+}
+
+extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L, int64_t row_cap,
+                           int32_t* counts, int32_t* offsets, int32_t* row_pair, int32_t* pair_row,
+                           const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq, float* xq_s, void* ws,
+                           size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
+    MOE_REQUIRE(T >= 0 && T <= ((int64_t)1 << 31) / 16, MOE_ERR_SHAPE, "permute: bad T=%lld", (long long)T);
+    MOE_REQUIRE(k >= 1 && k <= 16, MOE_ERR_SHAPE, "permute: k=%d outside [1, 16]", k);
+    MOE_REQUIRE(L >= 1 && L <= MAXL && e0 >= 0, MOE_ERR_SHAPE, "permute: L=%d outside [1, 1024] or e0<0", L);
+    MOE_REQUIRE(row_cap >= 0 && row_cap % MOE_ROW_ALIGN == 0 && row_cap <= 0x7FFFFFFF, MOE_ERR_SHAPE,
+                "permute: row_cap=%lld must be a multiple of 128 below 2^31", (long long)row_cap);
+    MOE_REQUIRE(counts && offsets && (T == 0 || (ids && pair_row)) && (row_cap == 0 || row_pair), MOE_ERR_NULL,
+                "permute: NULL ids/counts/offsets/row_pair/pair_row");
+    if (x) {
+        MOE_REQUIRE(d > 0 && d % 128 == 0, MOE_ERR_SHAPE, "permute: d=%d must be a positive multiple of 128", d);
+        MOE_REQUIRE(x_perm || xq, MOE_ERR_NULL, "permute: x given but neither x_perm nor xq");
+        MOE_REQUIRE(!xq || xq_s, MOE_ERR_NULL, "permute: xq without xq_s");
+    } else {
+        MOE_REQUIRE(!x_perm && !xq, MOE_ERR_NULL, "permute: x_perm/xq given without x");
+    }
+    size_t need = 0;
+    moe_permute_workspace(T, k, L, &need);
+    MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "permute: workspace %zu < %zu bytes", ws_bytes, need);
+
+    const int64_t P = T * k;
+    const int nchunk = (int)perm_chunks(T, k);
+    int32_t* chunk = static_cast<int32_t*>(ws);
+    if (nchunk > 0) {
+        perm_hist_kernel<<<dim3(nchunk), dim3(PBLOCK), 0, stream>>>(ids, P, e0, L, chunk);
+        MOE_LAUNCH_CHECK("perm_hist_kernel");
+    }
+    perm_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(chunk, nchunk, L, row_cap, counts, offsets, row_pair,
+                                                         dev_status);
+    MOE_LAUNCH_CHECK("perm_scan_kernel");
+    if (nchunk > 0) {
+        perm_scatter_kernel<<<dim3(nchunk), dim3(PBLOCK), 0, stream>>>(ids, P, e0, L, row_cap, chunk, offsets,
+                                                                       row_pair, pair_row);
+        MOE_LAUNCH_CHECK("perm_scatter_kernel");
+    }
+    if (x && T > 0) {
+        const int64_t items = T * (d / 128);
+        const int64_t threads = items * 16;
+        gather_quant_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
+            x, T, d, k, pair_row, x_perm, xq, xq_s);
+        MOE_LAUNCH_CHECK("gather_quant_kernel");
+    }
+    return MOE_OK;
+}

@@ -1,0 +1,227 @@
+// Routing kernels: wavefront top-k with softmax gates (optionally recording the
+// selection for Router Replay), the Router Replay load, and the gate backward.
+//
+// Router Replay follows "RL at 1T scale", section "Router Replay": the recorded
+// payload [num_layers, top_k, seq_len] stays on the device and is consumed by
+// device kernels only.
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int MAXK = 16;
+
+// One wavefront per token row.  Lane l holds logits l, l+64, ... (VPL values);
+// k rounds of a wave-wide arg-max under the key (value desc, id asc) pick the
+// slots in order.  IEEE comparison makes -0 and +0 equal, so they fall back to
+// the id order.
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                   int k, int32_t* __restrict__ ids, float* __restrict__ w,
+                                                   int32_t* __restrict__ rec, int64_t rec_stride, int64_t s0) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (row >= T) return;
+    const float* src = logits + row * E;
+    float v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        int e = lane + 64 * i;
+        v[i] = e < E ? src[e] : -INFINITY;
+    }
+    uint32_t taken = 0;
+    float my_val = 0.f;
+    int my_id = 0;
+    for (int s = 0; s < k; ++s) {
+        // lane-local best among untaken values; ids grow with i, so '>' keeps the lower id
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            int e = lane + 64 * i;
+            bool ok = e < E && !((taken >> i) & 1u);
+            if (ok && (bi == 0x7FFFFFFF || v[i] > bv)) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            float ov = __shfl_xor(bv, m);
+            int oi = __shfl_xor(bi, m);
+            bool take = (oi != 0x7FFFFFFF) &&
+                        (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
+            if (take) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (lane == s) {
+            my_val = bv;
+            my_id = bi;
+        }
+    }
+    // softmax over the selection; slot 0 holds the max
+    float m = __shfl(my_val, 0);
+    float ex = lane < k ? expf(my_val - m) : 0.f;
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += __shfl(ex, j);  // ascending slot order
+    if (lane < k) {
+        ids[row * k + lane] = my_id;
+        w[row * k + lane] = ex / sum;
+        if (rec) rec[(int64_t)lane * rec_stride + s0 + row] = my_id;
+    }
+}
+
+// One thread per token: read the k recorded ids (coalesced along the sequence
+// for each slot), validate, gather the k logits, softmax.
+__global__ __launch_bounds__(256) void replay_kernel(const int32_t* __restrict__ rec, int k, int64_t S,
+                                                     int64_t s0, int64_t T, const float* __restrict__ logits,
+                                                     int E, int32_t* __restrict__ ids, float* __restrict__ w,
+                                                     int32_t* __restrict__ status) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    int id[MAXK];
+    bool bad = false, dup = false;
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j) {
+        if (j < k) {
+            id[j] = rec[(int64_t)j * S + s0 + t];
+            bad |= (id[j] < 0) | (id[j] >= E);
+        }
+    }
+#pragma unroll
+    for (int j = 1; j < MAXK; ++j)
+#pragma unroll
+        for (int i = 0; i < MAXK; ++i)
+            if (i < j && j < k) dup |= id[i] == id[j];
+    float g[MAXK];
+    float m = -INFINITY;
+    if (!bad) {
+#pragma unroll
+        for (int j = 0; j < MAXK; ++j)
+            if (j < k) {
+                g[j] = logits[t * E + id[j]];
+                m = fmaxf(m, g[j]);
+            }
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j)
+        if (j < k) {
+            g[j] = bad ? 0.f : expf(g[j] - m);
+            sum += g[j];
+        }
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j)
+        if (j < k) {
+            ids[t * k + j] = id[j];
+            w[t * k + j] = bad ? 0.f : g[j] / sum;
+        }
+    int flags = (bad ? MOE_FLAG_BAD_ID : 0) | (dup ? MOE_FLAG_DUP_ID : 0);
+    if (flags && status) atomicOr(status, flags);
+}
+
+// d_logits row per block: zero the row, then add the k slot contributions in
+// slot order (a repeated id sums its slots).
+__global__ __launch_bounds__(256) void gate_backward_kernel(const float* __restrict__ d_gate,
+                                                            const float* __restrict__ w,
+                                                            const int32_t* __restrict__ ids, int k, int E,
+                                                            float* __restrict__ d_logits) {
+    const int64_t t = blockIdx.x;
+    float* out = d_logits + t * E;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = 0.f;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float dot = 0.f;
+        for (int j = 0; j < k; ++j) dot += w[t * k + j] * d_gate[t * k + j];
+        for (int j = 0; j < k; ++j) {
+            int e = ids[t * k + j];
+            if (e >= 0 && e < E) out[e] += w[t * k + j] * (d_gate[t * k + j] - dot);
+        }
+    }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+static int launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w,
+                       int32_t* rec, int64_t rec_stride, int64_t s0, hipStream_t stream) {
+    if (T == 0) return MOE_OK;
+    const int waves_per_block = 4;
+    dim3 grid((unsigned)((T + waves_per_block - 1) / waves_per_block)), block(64 * waves_per_block);
+    int vpl = (E + 63) / 64;
+    if (vpl <= 1)
+        topk_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+    else if (vpl <= 2)
+        topk_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+    else if (vpl <= 4)
+        topk_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+    else if (vpl <= 8)
+        topk_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+    else
+        topk_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+    MOE_LAUNCH_CHECK("topk_kernel");
+    return MOE_OK;
+}
+
+static int check_topk_args(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w) {
+    MOE_REQUIRE(T >= 0 && T <= (int64_t)1 << 40, MOE_ERR_SHAPE, "route_topk: bad T=%lld", (long long)T);
+    MOE_REQUIRE(E >= 1 && E <= 1024, MOE_ERR_SHAPE, "route_topk: E=%d outside [1, 1024]", E);
+    MOE_REQUIRE(k >= 1 && k <= MAXK && k <= E, MOE_ERR_SHAPE, "route_topk: k=%d outside [1, min(16, E)]", k);
+    MOE_REQUIRE(T == 0 || (logits && ids && w), MOE_ERR_NULL, "route_topk: NULL logits/ids/w");
+    return MOE_OK;
+}
+
+extern "C" int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w,
+                              hipStream_t stream) {
+    int rc = check_topk_args(logits, T, E, k, ids, w);
+    if (rc) return rc;
+    return launch_topk(logits, T, E, k, ids, w, nullptr, 0, 0, stream);
+}
+
+extern "C" int moe_route_topk_capture(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids,
+                                      float* w, int32_t* rec, int32_t n_layers, int64_t seq_len, int32_t layer,
+                                      int64_t s0, hipStream_t stream) {
+    int rc = check_topk_args(logits, T, E, k, ids, w);
+    if (rc) return rc;
+    MOE_REQUIRE(rec, MOE_ERR_NULL, "route_topk_capture: NULL record");
+    MOE_REQUIRE(n_layers >= 1 && layer >= 0 && layer < n_layers, MOE_ERR_SHAPE,
+                "route_topk_capture: layer %d outside [0, %d)", layer, n_layers);
+    MOE_REQUIRE(s0 >= 0 && seq_len >= 0 && s0 + T <= seq_len, MOE_ERR_SHAPE,
+                "route_topk_capture: tokens [%lld, %lld) outside seq_len %lld", (long long)s0,
+                (long long)(s0 + T), (long long)seq_len);
+    return launch_topk(logits, T, E, k, ids, w, rec + (int64_t)layer * k * seq_len, seq_len, s0, stream);
+}
+
+extern "C" int moe_replay_load(const int32_t* rec, int32_t n_layers, int32_t k, int64_t seq_len, int32_t layer,
+                               int64_t s0, int64_t T, const float* logits, int32_t E, int32_t* ids, float* w,
+                               int32_t* dev_status, hipStream_t stream) {
+    MOE_REQUIRE(k >= 1 && k <= MAXK, MOE_ERR_SHAPE, "replay_load: k=%d outside [1, 16]", k);
+    MOE_REQUIRE(E >= 1 && E <= 1024, MOE_ERR_SHAPE, "replay_load: E=%d outside [1, 1024]", E);
+    MOE_REQUIRE(n_layers >= 1 && layer >= 0 && layer < n_layers, MOE_ERR_SHAPE,
+                "replay_load: layer %d outside [0, %d)", layer, n_layers);
+    MOE_REQUIRE(T >= 0 && s0 >= 0 && seq_len >= 0 && s0 + T <= seq_len, MOE_ERR_SHAPE,
+                "replay_load: tokens [%lld, %lld) outside seq_len %lld", (long long)s0, (long long)(s0 + T),
+                (long long)seq_len);
+    if (T == 0) return MOE_OK;
+    MOE_REQUIRE(rec && logits && ids && w, MOE_ERR_NULL, "replay_load: NULL rec/logits/ids/w");
+    const int64_t S = seq_len;
+    dim3 block(256), grid((unsigned)((T + 255) / 256));
+    replay_kernel<<<grid, block, 0, stream>>>(rec + (int64_t)layer * k * S, k, S, s0, T, logits, E, ids, w,
+                                              dev_status);
+    MOE_LAUNCH_CHECK("replay_kernel");
+    return MOE_OK;
+}
+
+extern "C" int moe_gate_backward(const float* d_gate, const float* w, const int32_t* ids, int64_t T, int32_t k,
+                                 int32_t E, float* d_logits, hipStream_t stream) {
+    MOE_REQUIRE(T >= 0 && k >= 1 && k <= MAXK && E >= 1 && E <= 1024, MOE_ERR_SHAPE,
+                "gate_backward: bad T/k/E");
+    if (T == 0) return MOE_OK;
+    MOE_REQUIRE(d_gate && w && ids && d_logits, MOE_ERR_NULL, "gate_backward: NULL argument");
+    gate_backward_kernel<<<dim3((unsigned)T), dim3(256), 0, stream>>>(d_gate, w, ids, k, E, d_logits);
+    MOE_LAUNCH_CHECK("gate_backward_kernel");
+    return MOE_OK;
+}

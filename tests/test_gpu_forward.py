@@ -1,0 +1,354 @@
+"""GPU parity of the forward path against the oracle, through the C ABI.
+
+Integer and byte outputs (ids, permutation indices, FP8 codes and scales) must be
+bit-exact; gates within 1e-6 absolute; GEMM and layer outputs within a relative
+Frobenius error of 2e-3 against the oracle's fp64 accumulation over the same
+FP8 operands."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import blockfp8 as OQ
+from oracle import dispatch as OD
+from oracle import gemm as OG
+from oracle import layer as OL
+from oracle import routing as OR
+from oracle.numerics import bf16 as obf16, e4m3_encode, f32 as of32
+from moe_expert_layer_r3_amd import ops, synth
+from gpu_util import DEV, bf16_tensor, gpu, ids_for_counts, np64, npi, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+# ------------------------------------------------------------------ quantisation
+
+def test_quant_1x128_bf16():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((301, 512)) * np.exp2(rng.integers(-30, 30, (301, 1)))
+    x[5] = 0.0
+    x[6, :128] = 2.0 ** -130          # fp32 denormal tile -> eps floor
+    x[7, 3] = -0.0
+    xb = obf16(x)
+    say("quant 1x128 bf16 [301, 512]")
+    q, s = ops.quant_fp8(bf16_tensor(xb))
+    rq, rs = OQ.quant_1x128(xb)
+    assert np.array_equal(npi(q), rq)
+    assert np.array_equal(npi(s).astype(np.float64), rs)
+
+
+def test_quant_cvt_sweep_fp32():
+    """Through the public quantiser with tiles whose amax is 448 (so inv = s = 1):
+    q = e4m3(v) exactly, for a dense sweep of fp32 patterns covering every e4m3
+    rounding boundary, subnormals and signed zero."""
+    mant = np.arange(0, 1 << 23, 5, dtype=np.uint32)
+    vals = []
+    for e in range(-14, 9):
+        v = (((e + 127) << 23) | mant).view(np.float32)
+        vals.append(v[np.abs(v) <= 448.0])
+    v = np.concatenate(vals + [np.array([0.0, -0.0, 1e-40, -1e-40, 2.0 ** -10, 3 * 2.0 ** -10], np.float32)])
+    sign = np.where(np.arange(len(v)) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    v = v * sign
+    n = (len(v) + 126) // 127
+    tiles = np.zeros((n, 128), dtype=np.float32)
+    tiles[:, 0] = 448.0
+    flat = tiles[:, 1:].reshape(-1)
+    flat[:len(v)] = v
+    tiles[:, 1:] = flat.reshape(n, 127)
+    say(f"quant cvt sweep: {len(v)} values")
+    q, s = ops.quant_fp8(gpu(tiles))
+    assert np.all(npi(s) == 1.0)
+    got = npi(q)[:, 1:].reshape(-1)[:len(v)]
+    ref = e4m3_encode(v.astype(np.float64))
+    bad = np.flatnonzero(got != ref)
+    assert len(bad) == 0, f"{len(bad)} mismatches, first {v[bad[:5]]} got {got[bad[:5]]} ref {ref[bad[:5]]}"
+
+
+def test_quant_128x128_and_transpose():
+    rng = np.random.default_rng(1)
+    w = obf16(rng.standard_normal((3, 256, 384)) * 0.02)
+    w[1, :128, 128:256] *= 1000.0
+    w[2, 128:, :128] = 0.0
+    say("quant 128x128 [3, 256, 384] + transpose")
+    q, s, qT, sT = ops.quant_fp8(bf16_tensor(w), tile=ops.TILE_128x128, transpose=True)
+    rq, rs = OQ.quant_128x128(w)
+    assert np.array_equal(npi(q), rq)
+    assert np.array_equal(npi(s).astype(np.float64), rs)
+    assert np.array_equal(npi(qT), np.swapaxes(rq, 1, 2))
+    assert np.array_equal(npi(sT).astype(np.float64), np.swapaxes(rs, 1, 2))
+
+
+# ------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("T,E,k,mode", [(1000, 256, 8, "normal"), (333, 200, 16, "normal"), (65, 8, 2, "normal"),
+                                        (7, 1, 1, "normal"), (257, 64, 6, "ties"), (40, 130, 5, "zeros")])
+def test_topk(T, E, k, mode):
+    rng = np.random.default_rng(T * 7 + E)
+    if mode == "ties":
+        lg = rng.integers(0, 3, (T, E)).astype(np.float32)
+    elif mode == "zeros":
+        lg = np.where(rng.random((T, E)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        lg[:, ::7] = 1.0
+    else:
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+    say(f"topk T={T} E={E} k={k} {mode}")
+    ids, w = ops.route_topk(gpu(lg), k)
+    rids, rw = OR.topk(lg, k)
+    assert np.array_equal(npi(ids), rids)
+    assert np.max(np.abs(np64(w) - rw)) <= 1e-6
+
+
+def test_capture_replay_roundtrip():
+    rng = np.random.default_rng(5)
+    NL, S, E, k = 3, 3000, 256, 8
+    rec = torch.zeros((NL, k, S), dtype=torch.int32, device=DEV)
+    lgs = [rng.standard_normal((S, E)).astype(np.float32) for _ in range(NL)]
+    routed = {}
+    for l in range(NL):
+        for s0, n in [(0, 1000), (1000, 1500), (2500, 500)]:
+            ids, w = ops.route_topk(gpu(lgs[l][s0:s0 + n]), k, capture=(rec, l, s0))
+            routed[(l, s0)] = (npi(ids), npi(w))
+    say("capture done; replaying")
+    rrec = OR.capture([OR.topk(lgs[l], k)[0] for l in range(NL)])
+    assert np.array_equal(npi(rec), rrec)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for (l, s0), (ids0, w0) in routed.items():
+        n = len(ids0)
+        ids, w = ops.replay_load(rec, l, s0, gpu(lgs[l][s0:s0 + n]), status)
+        assert np.array_equal(npi(ids), ids0)
+        assert np.array_equal(npi(w), w0)      # same arithmetic in the same order
+    assert int(status.item()) == 0
+
+
+def test_replay_vs_oracle_and_flags():
+    wl = synth.tiny_variant(synth.WORKLOADS["replay"], seq_len=4096)
+    rec = synth.replay_record(wl)
+    lg = synth.logits(wl, layer=2, t0=1024, T=2048)
+    say("replay chunk layer 2, tokens 1024..3071")
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ids, w = ops.replay_load(gpu(rec), 2, 1024, gpu(lg), status)
+    rids, rw, rst = OR.replay(rec, 2, 1024, 2048, lg)
+    assert rst == 0 and int(status.item()) == 0
+    assert np.array_equal(npi(ids), rids)
+    assert np.max(np.abs(np64(w) - rw)) <= 1e-6
+    bad = rec.copy()
+    bad[0, 3, 10] = 256
+    bad[0, 5, 11] = -3
+    bad[0, 1, 12] = bad[0, 0, 12]
+    status.zero_()
+    ids, w = ops.replay_load(gpu(bad), 0, 0, gpu(synth.logits(wl, 0, 0, 64)), status)
+    rids, rw, rst = OR.replay(bad, 0, 0, 64, synth.logits(wl, 0, 0, 64))
+    assert int(status.item()) == rst == (OR.FLAG_BAD_ID | OR.FLAG_DUP_ID)
+    assert np.array_equal(npi(ids), rids)
+    assert np.all(npi(w)[10] == 0) and np.all(npi(w)[11] == 0)
+    assert np.max(np.abs(np64(w) - rw)) <= 1e-6
+
+
+# ------------------------------------------------------------------ permutation
+
+def _check_permute(ids, e0, L, x=None):
+    T, k = ids.shape
+    res = ops.permute(gpu(ids), e0, L, x=None if x is None else bf16_tensor(x), x_perm=x is not None)
+    c, o, rp, pr = OD.permute_index(ids, e0, L)
+    assert np.array_equal(npi(res["counts"]), c)
+    assert np.array_equal(npi(res["offsets"]), o)
+    n = int(o[-1])
+    assert np.array_equal(npi(res["row_pair"])[:n], rp)
+    assert np.array_equal(npi(res["pair_row"]), pr)
+    if x is not None:
+        real = rp >= 0
+        xq, xs = OQ.quant_1x128(x)
+        assert np.array_equal(npi(res["xq"])[:n][real], xq[rp[real] // k])
+        assert np.array_equal(npi(res["xq_s"])[:n][real].astype(np.float64), xs[rp[real] // k])
+        assert np.array_equal(np64(res["x_perm"])[:n][real], x[rp[real] // k])
+    return res
+
+
+@pytest.mark.parametrize("T,E,k,e0,L", [(8192, 256, 8, 0, 32), (5000, 256, 8, 96, 32), (1, 8, 2, 0, 8),
+                                        (4097, 16, 3, 4, 8), (300, 8, 2, 0, 8), (20000, 512, 4, 500, 12)])
+def test_permute_topk_routes(T, E, k, e0, L):
+    rng = np.random.default_rng(T + L)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ids, _ = OR.topk(lg, k) if T <= 5000 else (np.argsort(-lg, axis=1, kind="stable")[:, :k].astype(np.int32), None)
+    x = obf16(rng.standard_normal((T, 256))) if T <= 5000 else None
+    say(f"permute T={T} E={E} k={k} e0={e0} L={L}")
+    _check_permute(ids, e0, L, x)
+
+
+def test_permute_skewed_and_empty():
+    rng = np.random.default_rng(9)
+    ids = ids_for_counts([0, 1, 127, 128, 129, 0, 300, 5], k=8, E=64, e0=8, rng=rng)
+    x = obf16(rng.standard_normal((ids.shape[0], 384)))
+    say("permute skewed counts with empty experts")
+    _check_permute(ids, 8, 8, x)
+    hot = np.zeros((5000, 1), dtype=np.int32)
+    _check_permute(hot, 0, 4)
+
+
+def test_permute_row_cap_overflow_flag():
+    ids = np.zeros((100, 4), dtype=np.int32)       # repeated ids: 400 pairs on expert 0
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rcap = ops.row_cap(100, 4, 1)                   # 256 < 512 padded rows
+    say("permute row_cap overflow")
+    res = ops.permute(gpu(ids), 0, 1, rcap=rcap, status=status)
+    assert int(status.item()) & ops.FLAG_ROW_CAP
+    pr = npi(res["pair_row"]).ravel()
+    assert np.all(pr < rcap)
+    assert np.array_equal(pr[:rcap], np.arange(rcap)) and np.all(pr[rcap:] == -1)
+
+
+# ------------------------------------------------------------------ grouped GEMM
+
+def _gemm_problem(counts, K, N, seed, e0=0, E=64, k=8):
+    rng = np.random.default_rng(seed)
+    L = len(counts)
+    ids = ids_for_counts(counts, k=k, E=E, e0=e0, rng=rng)
+    T = ids.shape[0]
+    x = obf16(rng.standard_normal((T, K)))
+    res = ops.permute(gpu(ids), e0, L, x=bf16_tensor(x))
+    W = obf16(rng.standard_normal((L, N, K)) * 0.02)
+    W[0, :128] *= 50.0
+    wq, ws = ops.quant_fp8(bf16_tensor(W), tile=ops.TILE_128x128)
+    return res, wq, ws, L
+
+
+def _real_rows(res):
+    o = npi(res["offsets"])
+    c = npi(res["counts"])
+    return np.concatenate([np.arange(o[e], o[e] + c[e]) for e in range(len(c))]).astype(np.int64)
+
+
+@pytest.mark.parametrize("counts,K,N", [([0, 1, 130, 300], 256, 512), ([128, 256, 5, 0, 77, 129], 384, 256),
+                                        ([40], 128, 128), ([200, 3], 640, 384)])
+def test_gemm_store(counts, K, N):
+    res, wq, ws, L = _gemm_problem(counts, K, N, seed=K + N)
+    say(f"gemm STORE counts={counts} K={K} N={N}")
+    acc = ops.grouped_gemm(res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"], ops.EPI_STORE_F32)
+    y = ops.grouped_gemm(res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"], ops.EPI_STORE_BF16)
+    c, o = npi(res["counts"]), npi(res["offsets"])
+    ref = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]), c, o, npi(wq), npi(ws))
+    rows = _real_rows(res)
+    assert rel_fro(np64(acc)[rows], ref[rows]) <= 1e-5
+    assert rel_fro(np64(y)[rows], obf16(ref[rows])) <= TOL
+
+
+@pytest.mark.parametrize("counts,K,f", [([0, 1, 130, 300], 256, 256), ([129, 64], 384, 384), ([256], 128, 128)])
+def test_gemm_swiglu(counts, K, f):
+    res, wq, ws, L = _gemm_problem(counts, K, 2 * f, seed=K + f + 1)
+    say(f"gemm SWIGLU counts={counts} K={K} f={f}")
+    args = (res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"])
+    h32 = ops.grouped_gemm(*args, ops.EPI_SWIGLU_F32)
+    hq, hs = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8)
+    hq2, hs2, gu = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8_SAVE)
+    c, o = npi(res["counts"]), npi(res["offsets"])
+    GU = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]), c, o, npi(wq), npi(ws))
+    G, U = of32(GU[:, :f]), of32(GU[:, f:])
+    h_ref = OL.silu(G) * U
+    rows = _real_rows(res)
+    assert rel_fro(np64(h32)[rows], h_ref[rows]) <= 1e-5
+    # the fused quantiser, bit-exact on the GPU's own fp32 h
+    qref, sref = OQ.quant_1x128(np64(h32)[rows])
+    assert np.array_equal(npi(hq)[rows], qref)
+    assert np.array_equal(npi(hs)[rows].astype(np.float64), sref)
+    assert np.array_equal(npi(hq2)[rows], npi(hq)[rows]) and np.array_equal(npi(hs2)[rows], npi(hs)[rows])
+    assert rel_fro(np64(gu)[rows], obf16(GU[rows])) <= TOL
+
+
+# ------------------------------------------------------------------ combine
+
+def test_combine():
+    rng = np.random.default_rng(11)
+    T, E, k, e0, L, d = 3000, 64, 6, 16, 16, 384
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w = OR.topk(lg, k)
+    res = ops.permute(gpu(ids), e0, L)
+    rcap = res["row_cap"]
+    Y = obf16(rng.standard_normal((rcap, d)))
+    say("combine weighted and unweighted")
+    y = ops.combine(bf16_tensor(Y), res["pair_row"], gpu(w.astype(np.float32)))
+    pr = npi(res["pair_row"])
+    ref = OD.combine(Y, pr, w)
+    assert rel_fro(np64(y), ref) <= TOL
+    none = np.all(pr < 0, axis=1)
+    assert none.any() and np.all(np64(y)[none] == 0)
+    y1 = ops.combine(bf16_tensor(Y), res["pair_row"], None)
+    assert rel_fro(np64(y1), OD.combine(Y, pr, None)) <= TOL
+
+
+# ------------------------------------------------------------------ whole layer
+
+def _layer_forward_gpu(x, logits, W13, W2, k, e0, L):
+    wq13, ws13 = ops.quant_fp8(W13, tile=ops.TILE_128x128)
+    wq2, ws2 = ops.quant_fp8(W2, tile=ops.TILE_128x128)
+    ids, w = ops.route_topk(logits, k)
+    res = ops.permute(ids, e0, L, x=x)
+    hq, hs = ops.grouped_gemm(res["xq"], res["xq_s"], wq13, ws13, res["counts"], res["offsets"], ops.EPI_SWIGLU_Q8)
+    Y = ops.grouped_gemm(hq, hs, wq2, ws2, res["counts"], res["offsets"], ops.EPI_STORE_BF16)
+    y = ops.combine(Y, res["pair_row"], w)
+    return dict(ids=ids, w=w, res=res, hq=hq, hs=hs, Y=Y, y=y, wq13=wq13, ws13=ws13, wq2=wq2, ws2=ws2)
+
+
+def test_layer_tiny_forward():
+    wl = synth.WORKLOADS["tiny"]
+    lg = synth.logits(wl)
+    x = synth.x(wl)
+    W13 = synth.weights(wl, "w13")
+    W2 = synth.weights(wl, "w2")
+    say("tiny layer forward T=128 d=128 f=256 E=8 k=2")
+    out = _layer_forward_gpu(x.to(DEV), gpu(lg), W13.to(DEV), W2.to(DEV), wl.k, 0, wl.L)
+    ids, w = OR.topk(lg, wl.k)
+    assert np.array_equal(npi(out["ids"]), ids)
+    wq = OL.quantize_weights(np64(W13), np64(W2))
+    assert np.array_equal(npi(out["wq13"]), wq[0][0]) and np.array_equal(npi(out["wq2"]), wq[1][0])
+    fw = OL.forward(np64(x), ids, w, 0, wl.L, wq)
+    assert np.sum(npi(out["res"]["counts"])) == wl.T * wl.k
+    assert rel_fro(np64(out["y"]), fw["y"]) <= TOL
+    say("tiny layer rel err", rel_fro(np64(out["y"]), fw["y"]))
+
+
+def test_layer_ep8_full_size_sampled():
+    """T=8192, d=7168, f=2048, 32 of 256 experts, top-8 -- the full EP=8 share,
+    launched exactly as the benchmark launches it; outputs checked on samples."""
+    wl = synth.WORKLOADS["ep8"]
+    say("ep8: generating inputs")
+    lg = synth.logits(wl)
+    x = synth.x(wl)
+    W13 = synth.weights(wl, "w13")
+    W2 = synth.weights(wl, "w2")
+    say("ep8: GPU forward")
+    out = _layer_forward_gpu(x.to(DEV), gpu(lg), W13.to(DEV), W2.to(DEV), wl.k, wl.e0, wl.L)
+    torch.cuda.synchronize()
+    ids, w = OR.topk(lg, wl.k)
+    assert np.array_equal(npi(out["ids"]), ids)
+    assert np.max(np.abs(np64(out["w"]) - w)) <= 1e-6
+    c, o, rp, pr = OD.permute_index(ids, wl.e0, wl.L)
+    res = out["res"]
+    assert np.array_equal(npi(res["counts"]), c) and np.array_equal(npi(res["offsets"]), o)
+    assert np.array_equal(npi(res["pair_row"]), pr)
+    n = int(o[-1])
+    assert np.array_equal(npi(res["row_pair"])[:n], rp)
+    say("ep8: indices bit-exact; checking weights and sampled GEMM rows")
+    xs_np = np64(x)
+    for e in (0, 17):
+        rq, rs = OQ.quant_128x128(np64(W13[e:e + 1]))
+        assert np.array_equal(npi(out["wq13"][e]), rq[0]) and np.array_equal(npi(out["ws13"][e]).astype(np.float64), rs[0])
+        rq2, rs2 = OQ.quant_128x128(np64(W2[e:e + 1]))
+        assert np.array_equal(npi(out["wq2"][e]), rq2[0])
+        rows = np.arange(o[e], o[e] + c[e])[:: max(1, c[e] // 24)]
+        toks = rp[rows] // wl.k
+        xq, xsc = OQ.quant_1x128(xs_np[toks])
+        assert np.array_equal(npi(res["xq"])[rows], xq)
+        GU = OG.blockscaled_matmul(xq, xsc, rq[0], OG.expand_weight_scales(rs[0]))
+        h = OL.silu(of32(GU[:, :wl.f])) * of32(GU[:, wl.f:])
+        hq_g = npi(out["hq"])[rows]
+        hs_g = npi(out["hs"])[rows].astype(np.float64)
+        deq_g = OQ.dequant_1x128(hq_g, hs_g)
+        assert rel_fro(deq_g, h) <= 0.05            # FP8 of h itself: a few percent
+        Yref = obf16(OG.blockscaled_matmul(hq_g, hs_g, rq2[0], OG.expand_weight_scales(rs2[0])))
+        assert rel_fro(np64(out["Y"])[rows], Yref) <= TOL
+    toks = np.arange(0, wl.T, 97)
+    Yg = np64(out["Y"])
+    yref = OD.combine(Yg, pr[toks], w[toks])
+    assert rel_fro(np64(out["y"])[toks], yref) <= TOL
+    say("ep8 sampled parity ok")
