@@ -34,7 +34,22 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ep8", choices=["ep8", "hotspot"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, 5 times: under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters against a known
+    byte count (1 GiB read and 1 GiB written per dispatch)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}), flush=True)
 
 
 def gemm_algorithmic(P, L, d, f):
@@ -91,6 +106,9 @@ def cpu_baseline(wl, lg, x_bf16, W13, W2):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the expert-parallel exchange across GPUs is not part of it", file=sys.stderr)

@@ -20,6 +20,11 @@ from gpu_util import DEV, bf16_tensor, gpu, ids_for_counts, np64, npi, rel_fro, 
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
+# The f8f6f4 MFMA's own accumulation of a 128-term block differs from the exact
+# sum by about 1.4e-5 relative (measured); fp32 rounding alone would give ~1e-7.
+# Raw accumulators are held to this tighter bound to catch indexing mistakes
+# that would still pass TOL.
+ACC_TOL = 1e-4
 
 
 # ------------------------------------------------------------------ quantisation
@@ -67,9 +72,10 @@ def test_quant_cvt_sweep_fp32():
 
 def test_quant_128x128_and_transpose():
     rng = np.random.default_rng(1)
-    w = obf16(rng.standard_normal((3, 256, 384)) * 0.02)
+    w = rng.standard_normal((3, 256, 384)) * 0.02
     w[1, :128, 128:256] *= 1000.0
     w[2, 128:, :128] = 0.0
+    w = obf16(w)
     say("quant 128x128 [3, 256, 384] + transpose")
     q, s, qT, sT = ops.quant_fp8(bf16_tensor(w), tile=ops.TILE_128x128, transpose=True)
     rq, rs = OQ.quant_128x128(w)
@@ -229,7 +235,7 @@ def test_gemm_store(counts, K, N):
     c, o = npi(res["counts"]), npi(res["offsets"])
     ref = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]), c, o, npi(wq), npi(ws))
     rows = _real_rows(res)
-    assert rel_fro(np64(acc)[rows], ref[rows]) <= 1e-5
+    assert rel_fro(np64(acc)[rows], ref[rows]) <= ACC_TOL
     assert rel_fro(np64(y)[rows], obf16(ref[rows])) <= TOL
 
 
@@ -246,7 +252,7 @@ def test_gemm_swiglu(counts, K, f):
     G, U = of32(GU[:, :f]), of32(GU[:, f:])
     h_ref = OL.silu(G) * U
     rows = _real_rows(res)
-    assert rel_fro(np64(h32)[rows], h_ref[rows]) <= 1e-5
+    assert rel_fro(np64(h32)[rows], h_ref[rows]) <= ACC_TOL
     # the fused quantiser, bit-exact on the GPU's own fp32 h
     qref, sref = OQ.quant_1x128(np64(h32)[rows])
     assert np.array_equal(npi(hq)[rows], qref)
