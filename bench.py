@@ -65,6 +65,24 @@ def gemm_algorithmic(P, L, d, f):
     return g1_flops, g1_bytes, g2_flops, g2_bytes
 
 
+def measured_traffic(workload):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when the kernel source changed since then."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"gemm1_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(here, "moe_expert_layer_r3_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp"):
+        h.update(open(os.path.join(src, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
 def cpu_baseline(wl, lg, x_bf16, W13, W2):
     """The oracle on the host: routing + permutation for all tokens, expert work
     (gather, quantise, GEMMs, SwiGLU, combine) for 2 of the L local experts,
@@ -182,7 +200,7 @@ def main():
                    "local_pairs": P},
         "roofline": {"bound": "hbm", "kernel": "grouped GEMM1 + SwiGLU + quant (gemm_fp8_kernel<256,1>)",
                      "achieved": ach_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach_gbs / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": measured_traffic(wl.name)},
         "gemm_tflops": gemm_tflops,
         "gemm_mfma_frac": gemm_tflops / FP8_PEAK_TFLOPS,
         "kernel_ms": kern_ms,
