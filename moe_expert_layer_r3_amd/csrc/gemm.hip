@@ -6,18 +6,25 @@
 // both K-contiguous ("NT"), which is the operand layout the MFMA wants.
 //
 // Design (CDNA4, wave64):
-//   * block tile 128 x BN, K step 128 = one scale block; 4 waves as 2 x 2, each
-//     wave 64 x BN/2 built from 16x16x128 f8f6f4 MFMAs: one MFMA covers exactly
-//     one scale block, so its fresh fp32 result is rescaled by sA*sB and added
-//     to the fp32 accumulator (one VALU FMA per accumulator per K block).
-//   * operands stream global -> registers -> LDS, double buffered: the loads
-//     of K block kb+1 are in flight while block kb is multiplied; the LDS
-//     image of every 128-byte row is XOR swizzled in 16-byte chunks so the
-//     fragment reads are bank-conflict free.
+//   * block tile 128 x BN, K step 128 = one scale block; 8 waves (2 per SIMD)
+//     as 2 (M) x 4 (N), each wave 64 x BN/4 built from 16x16x128 f8f6f4 MFMAs.
+//     One MFMA covers exactly one scale block: its fresh fp32 partial is
+//     rescaled by sA*sB and added to the fp32 accumulator with one VALU FMA
+//     per element per block; MFMAs of the next n-subtile run meanwhile.
+//   * operands stream global -> LDS directly (global_load_lds_dwordx4), three
+//     stages deep: K blocks kb+1 and kb+2 are in flight while kb is
+//     multiplied; one barrier per K block.  The LDS image of every 128-byte
+//     row is XOR swizzled in 16-byte chunks (chunk c of row r is stored at
+//     c ^ (r & 7)), and the four 16-lane groups of a fragment read take the
+//     consecutive chunks g and g + 4: measured on gfx950, this pattern reads
+//     at the full LDS rate while chunk pairs {2g, 2g+1} run at half rate from
+//     bank conflicts.
 //   * persistent blocks walk an expert-major tile list built on the device from
 //     counts/offsets (no host sync); consecutive tiles share a weight tile and
 //     are mapped to the same XCD so that weight tile is fetched into one L2.
 //   * epilogues stage through LDS for coalesced 16-byte stores.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -25,10 +32,13 @@ namespace moe {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(4))) float* cfloat_ptr;
 
 constexpr int GBM = 128;
 constexpr int GBK = 128;
-constexpr int GTHREADS = 256;
+constexpr int GTHREADS = 512;
+constexpr int GWAVES = GTHREADS / 64;
 constexpr int GMAXL = 1024;
 constexpr int GMAXKB = 256;  // K <= 32768
 
@@ -52,6 +62,69 @@ struct GemmArgs {
     float* out3_s;
 };
 
+// 16- / 4-byte global -> LDS transfer (global_load_lds_dwordx4 / _dword): lane
+// l's bytes land at LDS byte address m0 + l*size (m0 = `lds`, wave-uniform).
+// Written as inline assembly so that the compiler does not know these VMEM
+// instructions write LDS: it would otherwise wait for all of them (vmcnt(0))
+// before every LDS read, serialising the pipeline.  Completion is awaited with
+// explicit vmcnt waits followed by a barrier before a stage is read.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+    asm volatile("global_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt immediate waiting for vmcnt <= N only (gfx9 encoding: vmcnt[3:0],
+// expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef const __attribute__((address_space(3))) u32x4* lds_u32x4_ptr;
+typedef const __attribute__((address_space(3))) v2u* lds_v2u_ptr;
+
+// Plain LDS loads (the compiler tracks their lgkmcnt).  `base` comes out of an
+// opaque move placed after the stage's barrier, so no read can be hoisted
+// above the barrier that makes the stage's DMA data visible.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds16(uint32_t addr) {
+    return *(lds_u32x4_ptr)(uintptr_t)(addr + OFF);
+}
+template <int OFF>
+__device__ __forceinline__ v2u lds8(uint32_t addr) {
+    return *(lds_v2u_ptr)(uintptr_t)(addr + OFF);
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__device__ __forceinline__ v8i join8(u32x4 lo, u32x4 hi) {
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    // E8M0 127 = 2^0: the hardware block scales are 1, the fp32 scales are
+    // applied by the caller
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
+}
+
 constexpr bool is_swiglu(int epi) {
     return epi == MOE_EPI_SWIGLU_Q8 || epi == MOE_EPI_SWIGLU_Q8_SAVE || epi == MOE_EPI_SWIGLU_F32;
 }
@@ -62,34 +135,29 @@ struct GemmSmem {
     static constexpr int B_BYTES = BN * GBK;
     static constexpr int S_BYTES = GBM * 4;
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-    static constexpr int TOTAL = 2 * STAGE;
+    static constexpr int NSTAGE = 3;
+    static constexpr int TOTAL = NSTAGE * STAGE;
 };
-
-// Byte offset of (row r, 16-byte chunk c) in a 128-byte-row operand image.
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
-
-// MFMA 16x16x128 operand fragment: lane l holds 32 K-bytes of row r, chunks
-// 2*(l/16) and 2*(l/16)+1 of the 128-byte K block.  A and B use the same
-// lane -> K mapping, so any fixed permutation of K inside the block leaves the
-// dot products unchanged.
-__device__ __forceinline__ v8i frag_read(const uint8_t* base, int r, int lane) {
-    const int c0 = (lane >> 4) * 2;
-    const u32x4 lo4 = *reinterpret_cast<const u32x4*>(base + swz(r, c0));
-    const u32x4 hi4 = *reinterpret_cast<const u32x4*>(base + swz(r, c0 + 1));
-    return v8i{(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w, (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
-}
 
 template <int BN, int EPI>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     using SM = GemmSmem<BN>;
+    constexpr int WN = BN / 4;        // wave tile columns
+    constexpr int NI = WN / 16;       // n-subtiles per wave
+    constexpr int ASEG = GBM / 8 / GWAVES;  // 1 KB A segments per wave
+    constexpr int BSEG = BN / 8 / GWAVES;   // 1 KB B segments per wave
+    constexpr int NLD = ASEG + BSEG + 1;    // DMA instructions per wave per stage
+    static_assert(!is_swiglu(EPI) || BN == 256, "SwiGLU tiles pair 128 G with 128 U columns");
+
     __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
     __shared__ int tile_base[GMAXL + 1];
     __shared__ int scan_tmp[GTHREADS];
-    __shared__ float bscale[2][GMAXKB];
-    __shared__ float rowmax[2][GBM];
+    __shared__ float rowmax[4][GBM];
+    __shared__ __attribute__((aligned(8))) float bscale[GMAXKB][2];  // this tile's B scales per K block
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wm = wave >> 2, wn = wave & 3;
     const int L = g.L, N = g.N, K = g.K;
     const int nkb = K / GBK;
     const int NT = N / BN;
@@ -97,11 +165,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 
     // ---- tile list: per-expert m-tiles of the (row_cap-clamped) padded segments
     {
-        int loc[4];
+        int loc[2];
         int sum = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid * 4 + i;
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid * 2 + i;
             int m = 0;
             if (e < L) {
                 int64_t lo = g.offsets[e], hi = g.offsets[e + 1];
@@ -122,8 +190,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         }
         int run = scan_tmp[tid] - sum;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid * 4 + i;
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid * 2 + i;
             if (e < L) tile_base[e] = run * NT;
             run += loc[i];
         }
@@ -133,8 +201,19 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     const int total = tile_base[L];
     const int G = gridDim.x;  // a multiple of 8
     const int lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    // per-lane LDS read offsets (stage-relative).  Lane l holds row l & 15 of a
+    // fragment and K chunks g and g + 4 of the 128-byte block (g = l >> 4);
+    // A and B use the same lane -> K mapping, so the MFMA sums the same
+    // products.  row & 7 == lane & 7 for every fragment row, so the swizzled
+    // chunk is fixed per lane.
+    const int l15 = lane & 15, l7 = lane & 7, c0 = lane >> 4;
+    const uint32_t a_rd0 = (wm * 64 + l15) * 128 + ((c0 ^ l7) << 4);
+    const uint32_t a_rd1 = (wm * 64 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    const uint32_t b_rd0 = SM::A_BYTES + (wn * WN + l15) * 128 + ((c0 ^ l7) << 4);
+    const uint32_t b_rd1 = SM::A_BYTES + (wn * WN + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    const uint32_t s_rd = SM::A_BYTES + SM::B_BYTES + (wm * 64 + (lane >> 4) * 4) * 4;
 
     for (int t = lb; t < total; t += G) {
         int lo = 0, hi = L;
@@ -142,145 +221,143 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
             const int mid = (lo + hi) >> 1;
             if (tile_base[mid] <= t) lo = mid; else hi = mid;
         }
-        const int e = lo;
-        const int mt_e = (tile_base[e + 1] - tile_base[e]) / NT;
-        const int local = t - tile_base[e];
+        const int e = __builtin_amdgcn_readfirstlane(lo);
+        const int tb0 = __builtin_amdgcn_readfirstlane(tile_base[e]);
+        const int tb1 = __builtin_amdgcn_readfirstlane(tile_base[e + 1]);
+        const int mt_e = (tb1 - tb0) / NT;
+        const int local = t - tb0;
         const int nt = local / mt_e, mt = local - nt * mt_e;
         const int64_t row0 = (int64_t)g.offsets[e] + (int64_t)mt * GBM;
         const int64_t real_end = (int64_t)g.offsets[e] + g.counts[e];
-        const int n0 = nt * BN;  // STORE: first output column; SwiGLU: nt*128 is the h column
+        const int n0 = nt * BN;  // STORE: first output column; SwiGLU: nt*128 is the first h column
 
         const uint8_t* Ag = g.a + row0 * K;
         const float* Asg = g.a_s + row0 * nkb;
         const uint8_t* Bg = g.b + (int64_t)e * N * K;
 
-        // B scales of the (at most two) 128-column blocks this tile touches
-        {
-            int blk0, blk1;
-            if constexpr (is_swiglu(EPI)) {
-                blk0 = nt;
-                blk1 = f / 128 + nt;
-            } else {
-                blk0 = n0 / 128;
-                blk1 = BN > 128 ? blk0 + 1 : blk0;
-            }
-            const float* bs = g.b_s + (int64_t)e * (N / 128) * nkb;
-            for (int i = tid; i < 2 * nkb; i += GTHREADS) {
-                const int which = i / nkb, kb = i - which * nkb;
-                bscale[which][kb] = bs[(int64_t)(which ? blk1 : blk0) * nkb + kb];
-            }
+        // B scale rows (128-column blocks) of this wave: for SwiGLU the G block
+        // (n-subtiles 0, 1) and the U block (2, 3); for stores one block holds
+        // all of the wave's columns.  They are staged in LDS for the tile so
+        // the K loop reads them together with the operand fragments.
+        const float* bs_base = g.b_s + (int64_t)e * (N / 128) * nkb;
+        int blk0, blk1;
+        if constexpr (is_swiglu(EPI)) {
+            blk0 = nt;              // G columns
+            blk1 = f / 128 + nt;    // U columns
+        } else {
+            blk0 = n0 / 128;        // columns [n0, n0 + 128)
+            blk1 = blk0 + (BN > 128 ? 1 : 0);
         }
+        for (int i = tid; i < 2 * nkb; i += GTHREADS) {
+            const int kb = i >> 1, which = i & 1;
+            bscale[kb][which] = bs_base[(int64_t)(which ? blk1 : blk0) * nkb + kb];
+        }
+        const uint32_t bs_rd = lds_addr(&bscale[0][0]);
+        // STORE: waves wn = 0, 1 use block blk0, wn = 2, 3 block blk1
+        const bool second_blk = !is_swiglu(EPI) && BN > 128 && wn >= 2;
 
+        // DMA sources.  Segment q (1 KB) holds tile rows 8q .. 8q+7; lane l moves
+        // LDS chunk (l & 7) of row 8q + l/8, i.e. global chunk (l & 7) ^ (row & 7)
+        // (the XOR swizzle is its own inverse; rows 8 apart share it).
+        const int ra = wave * (ASEG * 8) + (lane >> 3);
+        const uint8_t* a_src = Ag + (int64_t)ra * K + (((lane & 7) ^ (ra & 7)) << 4);
+        const int rb = wave * (BSEG * 8) + (lane >> 3);
+        int brow0;
+        if constexpr (is_swiglu(EPI)) {
+            // LDS B rows in 32-row blocks: block 2w' holds G columns nt*128 +
+            // 32w' + [0, 32), block 2w'+1 the U columns of the same h columns;
+            // wave w fills block w
+            brow0 = ((wave & 1) ? f : 0) + nt * 128 + (wave >> 1) * 32 + (lane >> 3);
+        } else {
+            brow0 = n0 + rb;
+        }
+        const uint8_t* b_src = Bg + (int64_t)brow0 * K + (((lane & 7) ^ (rb & 7)) << 4);
+        const float* s_src = Asg + (int64_t)(wave * 16 + (lane & 15)) * nkb;
+        const int64_t K8 = (int64_t)8 * K;
 
-        // Global -> register -> LDS staging.  Thread (wave, lane) moves 16-byte
-        // chunk `lane` of each 1 KB LDS segment q it owns; the global address is
-        // the inverse of the swizzle so the LDS image is the swizzled layout.
-        constexpr int NBL = BN / 32;  // B segments per wave
-        u32x4 ra[4], rb[NBL];
-        float rs = 0.f;
-        int64_t a_off[4], b_off[NBL];
+        auto issue = [&](int stage, int kb) {
+            const uint32_t sA = sbase + (uint32_t)(stage * SM::STAGE);
+            const uint32_t sB = sA + SM::A_BYTES;
+            const uint32_t sS = sB + SM::B_BYTES;
+            const int kofs = kb * GBK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = wave * 4 + i;
-            const int r = q * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ (r & 7);
-            a_off[i] = (int64_t)r * K + c * 16;
-        }
+            for (int i = 0; i < ASEG; ++i) dma16(a_src + i * K8 + kofs, sA + (wave * ASEG + i) * 1024);
 #pragma unroll
-        for (int i = 0; i < NBL; ++i) {
-            const int q = wave * NBL + i;
-            const int rr = q * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ (rr & 7);
-            int br;
-            if constexpr (is_swiglu(EPI)) {
-                const int blk = rr >> 6;
-                br = ((blk & 1) ? f : 0) + nt * 128 + (blk >> 1) * 64 + (rr & 63);
-            } else {
-                br = n0 + rr;
-            }
-            b_off[i] = (int64_t)br * K + c * 16;
-        }
-        const float* s_src = Asg + (int64_t)(wave * 32 + (lane & 31)) * nkb;
-#define MOE_GLOAD(kb_)                                                                               \
-    do {                                                                                             \
-        const int kofs_ = (kb_) * GBK;                                                               \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) ra[i] =                                        \
-            *reinterpret_cast<const u32x4*>(Ag + a_off[i] + kofs_);                                  \
-        _Pragma("unroll") for (int i = 0; i < NBL; ++i) rb[i] =                                      \
-            *reinterpret_cast<const u32x4*>(Bg + b_off[i] + kofs_);                                  \
-        if (lane < 32) rs = s_src[(kb_)];                                                            \
-    } while (0)
-#define MOE_LSTORE(stage_)                                                                           \
-    do {                                                                                             \
-        uint8_t* sA_ = smem + (stage_) * SM::STAGE;                                                  \
-        uint8_t* sB_ = sA_ + SM::A_BYTES;                                                            \
-        float* sS_ = reinterpret_cast<float*>(sB_ + SM::B_BYTES);                                    \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
-            *reinterpret_cast<u32x4*>(sA_ + (wave * 4 + i) * 1024 + lane * 16) = ra[i];              \
-        _Pragma("unroll") for (int i = 0; i < NBL; ++i)                                              \
-            *reinterpret_cast<u32x4*>(sB_ + (wave * NBL + i) * 1024 + lane * 16) = rb[i];            \
-        if (lane < 32) sS_[wave * 32 + lane] = rs;                                                   \
-    } while (0)
+            for (int i = 0; i < BSEG; ++i) dma16(b_src + i * K8 + kofs, sB + (wave * BSEG + i) * 1024);
+            if (lane < 16) dma4(s_src + kb, sS + wave * 64);  // 16 rows' A scales per wave
+        };
 
-        v4f acc[4][8];
+        v4f acc[4][NI];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = zero;
+            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        __syncthreads();  // bscale visible; previous tile's epilogue done with smem
-        MOE_GLOAD(0);
-        MOE_LSTORE(0);
-        __syncthreads();
-        constexpr int NI = BN == 128 ? 4 : 8;  // n-subtiles per wave
+        __syncthreads();  // the previous tile's epilogue is done with smem
+        issue(0, 0);
+        if (nkb > 1) issue(1, 1);
         for (int kb = 0; kb < nkb; ++kb) {
-            if (kb + 1 < nkb) MOE_GLOAD(kb + 1);
-            const uint8_t* sA = smem + (kb & 1) * SM::STAGE;
-            const uint8_t* sB = sA + SM::A_BYTES;
-            const float* sS = reinterpret_cast<const float*>(sB + SM::B_BYTES);
+            if (kb + 1 < nkb) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();  // stage kb landed for all waves; stage kb-1 no longer read
+            if (kb + 2 < nkb) issue((kb + 2) % 3, kb + 2);
+            const uint32_t base = opaque(sbase + (uint32_t)((kb % 3) * SM::STAGE));
+            const uint32_t bsa = opaque(bs_rd + kb * 8);
 
+            u32x4 alo[4], ahi[4], sa4[4], blo[2], bhi[2];
+            const v2u sbv = lds8<0>(bsa);
+            blo[0] = lds16<0>(base + b_rd0);
+            bhi[0] = lds16<0>(base + b_rd1);
+            static_for<0, 4>([&](auto ic) {
+                constexpr int mi = decltype(ic)::value;
+                alo[mi] = lds16<mi * 2048>(base + a_rd0);
+                ahi[mi] = lds16<mi * 2048>(base + a_rd1);
+                sa4[mi] = lds16<mi * 64>(base + s_rd);
+            });
             v8i af[4];
             v4f sc0[4], sc1[4];
-            // STORE: the wave's BN/2 columns lie in one 128-column block of B
-            const float sb0 = is_swiglu(EPI) ? bscale[0][kb] : bscale[(BN > 128 && wn) ? 1 : 0][kb];
-            const float sb1 = bscale[1][kb];
+            v4f pt[2][4];
+            // element values go through plain integers: __builtin_bit_cast of an
+            // ext_vector element lvalue reads element 0 with this compiler
+            const uint32_t sbx = sbv.x, sby = sbv.y;
+            const float sb0 = __uint_as_float(second_blk ? sby : sbx);
+            const float sb1 = __uint_as_float(sby);
+            const v8i bf0 = join8(blo[0], bhi[0]);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
-                af[mi] = frag_read(sA, wm * 64 + mi * 16 + (lane & 15), lane);
-                const float4 sa = *reinterpret_cast<const float4*>(sS + wm * 64 + mi * 16 + (lane >> 4) * 4);
-                sc0[mi] = v4f{sa.x * sb0, sa.y * sb0, sa.z * sb0, sa.w * sb0};
-                if constexpr (is_swiglu(EPI)) sc1[mi] = v4f{sa.x * sb1, sa.y * sb1, sa.z * sb1, sa.w * sb1};
+                af[mi] = join8(alo[mi], ahi[mi]);
+                const v4f sa = __builtin_bit_cast(v4f, sa4[mi]);
+                sc0[mi] = sa * sb0;
+                if constexpr (is_swiglu(EPI)) sc1[mi] = sa * sb1;
+                pt[0][mi] = mfma16x16x128(af[mi], bf0);
             }
-            // software pipeline: the MFMAs of n-subtile ni run while the
-            // rescale-accumulate of n-subtile ni-1 retires on the VALU
-            v4f pt[2][4];
-            {
-                const v8i bf = frag_read(sB, wn * (BN / 2) + (lane & 15), lane);
+            // software pipeline over n-subtiles: the MFMAs of subtile ni run
+            // while the rescale-accumulate of subtile ni-1 retires on the VALU
+            static_for<0, NI + 1>([&](auto nc) {
+                constexpr int ni = decltype(nc)::value;
+                if constexpr (ni < NI) {
+                    if constexpr (ni + 1 < NI) {
+                        blo[(ni + 1) & 1] = lds16<(ni + 1) * 2048>(base + b_rd0);
+                        bhi[(ni + 1) & 1] = lds16<(ni + 1) * 2048>(base + b_rd1);
+                    }
+                    if constexpr (ni > 0) {
+                        const v8i bf = join8(blo[ni & 1], bhi[ni & 1]);
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    pt[0][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf, zero, 0, 0, 0, 127, 0, 127);
-            }
-#pragma unroll
-            for (int ni = 1; ni <= NI; ++ni) {
-                if (ni < NI) {
-                    const v8i bf = frag_read(sB, wn * (BN / 2) + ni * 16 + (lane & 15), lane);
-#pragma unroll
-                    for (int mi = 0; mi < 4; ++mi)
-                        pt[ni & 1][mi] =
-                            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf, zero, 0, 0, 0, 127, 0, 127);
+                        for (int mi = 0; mi < 4; ++mi) pt[ni & 1][mi] = mfma16x16x128(af[mi], bf);
+                    }
                 }
-                const int pn = ni - 1;
-                const bool second = is_swiglu(EPI) && pn >= 4;
+                if constexpr (ni > 0) {
+                    constexpr int pn = ni - 1;
+                    constexpr bool second = is_swiglu(EPI) && pn >= NI / 2;
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) acc[mi][pn] += pt[pn & 1][mi] * (second ? sc1[mi] : sc0[mi]);
-            }
-            if (kb + 1 < nkb) MOE_LSTORE((kb + 1) & 1);
-            __syncthreads();
+                    for (int mi = 0; mi < 4; ++mi) acc[mi][pn] += pt[pn & 1][mi] * (second ? sc1[mi] : sc0[mi]);
+                }
+            });
         }
+        __syncthreads();  // every wave is done reading the operand stages
 
         // ---------------------------------------------------------- epilogues
-        // lane's rows: wm*64 + mi*16 + (lane>>4)*4 + i ; column within the wave
-        // tile: ni*16 + (lane & 15)
+        // lane's rows: wm*64 + mi*16 + (lane>>4)*4 + i ; columns within the
+        // tile: wn*WN + ni*16 + (lane & 15)
         const int rbase = wm * 64 + (lane >> 4) * 4;
         const int cl = lane & 15;
         if constexpr (EPI == MOE_EPI_STORE_F32) {
@@ -292,10 +369,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
                     const int64_t r = row0 + rbase + mi * 16 + i;
                     if (r >= real_end) continue;
 #pragma unroll
-                    for (int ni = 0; ni < 8; ++ni) {
-                        if (BN == 128 && ni >= 4) break;
-                        out[r * N + n0 + wn * (BN / 2) + ni * 16 + cl] = acc[mi][ni][i];
-                    }
+                    for (int ni = 0; ni < NI; ++ni) out[r * N + n0 + wn * WN + ni * 16 + cl] = acc[mi][ni][i];
                 }
         } else if constexpr (EPI == MOE_EPI_STORE_BF16) {
             constexpr int LDR = BN * 2 + 16;  // staged row stride (bytes)
@@ -303,15 +377,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 8; ++ni) {
-                    if (BN == 128 && ni >= 4) break;
+                for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = rbase + mi * 16 + i;
-                        const int c = wn * (BN / 2) + ni * 16 + cl;
+                        const int c = wn * WN + ni * 16 + cl;
                         *reinterpret_cast<uint16_t*>(smem + r * LDR + c * 2) = (uint16_t)f32_to_bf16(acc[mi][ni][i]);
                     }
-                }
             __syncthreads();
             uint16_t* out = static_cast<uint16_t*>(g.out);
             constexpr int CPR = BN / 8;  // 16-byte chunks per row
@@ -322,16 +394,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
                 *reinterpret_cast<uint4*>(out + (row0 + r) * N + n0 + ch * 8) = v;
             }
         } else if constexpr (is_swiglu(EPI)) {
-            // SwiGLU: n-subtile ni < 4 is G, ni + 4 is U of the same h column
-            // hcol = wn*64 + ni*16 + cl within this tile's 128 h columns
-            float h[4][4][4];
+            // n-subtiles 0, 1 are G and 2, 3 the U of the same h columns
+            // hcol = wn*32 + ni*16 + cl within this tile's 128 h columns
+            float h[4][2][4];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
+                for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float gv = acc[mi][ni][i], uv = acc[mi][ni + 4][i];
+                        const float gv = acc[mi][ni][i], uv = acc[mi][ni + 2][i];
                         h[mi][ni][i] = gv / (1.0f + expf(-gv)) * uv;
                     }
             const int hcol0 = nt * 128;
@@ -344,17 +416,15 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
                         const int64_t r = row0 + rbase + mi * 16 + i;
                         if (r >= real_end) continue;
 #pragma unroll
-                        for (int ni = 0; ni < 4; ++ni) out[r * f + hcol0 + wn * 64 + ni * 16 + cl] = h[mi][ni][i];
+                        for (int ni = 0; ni < 2; ++ni) out[r * f + hcol0 + wn * 32 + ni * 16 + cl] = h[mi][ni][i];
                     }
             } else {
-                // per-row amax over this wave's 64 h columns, then across the two N waves
+                // per-row amax over this wave's 32 h columns, then across the 4 N waves
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float m = 0.f;
-#pragma unroll
-                        for (int ni = 0; ni < 4; ++ni) m = fmaxf(m, fabsf(h[mi][ni][i]));
+                        float m = fmaxf(fabsf(h[mi][0][i]), fabsf(h[mi][1][i]));
                         m = group_max<16>(m);
                         if (cl == 0) rowmax[wn][rbase + mi * 16 + i] = m;
                     }
@@ -366,15 +436,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = rbase + mi * 16 + i;
-                        const TileScale ts = tile_scale(fmaxf(rowmax[0][r], rowmax[1][r]));
-                        if (cl == 0 && wn == 0 && row0 + r < real_end)
-                            g.out_s[(row0 + r) * (f / 128) + nt] = ts.s;
-#pragma unroll
-                        for (int ni = 0; ni < 4; ni += 2) {
-                            const int w2 = cvt_e4m3x2(h[mi][ni][i] * ts.inv, h[mi][ni + 1][i] * ts.inv);
-                            qt[r * LDQ + wn * 64 + ni * 16 + cl] = (uint8_t)(w2 & 0xFF);
-                            qt[r * LDQ + wn * 64 + (ni + 1) * 16 + cl] = (uint8_t)((w2 >> 8) & 0xFF);
-                        }
+                        const float am = fmaxf(fmaxf(rowmax[0][r], rowmax[1][r]), fmaxf(rowmax[2][r], rowmax[3][r]));
+                        const TileScale ts = tile_scale(am);
+                        if (cl == 0 && wn == 0 && row0 + r < real_end) g.out_s[(row0 + r) * (f / 128) + nt] = ts.s;
+                        const int w2 = cvt_e4m3x2(h[mi][0][i] * ts.inv, h[mi][1][i] * ts.inv);
+                        qt[r * LDQ + wn * 32 + cl] = (uint8_t)(w2 & 0xFF);
+                        qt[r * LDQ + wn * 32 + 16 + cl] = (uint8_t)((w2 >> 8) & 0xFF);
                     }
                 if constexpr (EPI == MOE_EPI_SWIGLU_Q8_SAVE) {
                     // G and U as bf16, staged after the byte tile
@@ -384,15 +451,15 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 #pragma unroll
                     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                        for (int ni = 0; ni < 4; ++ni)
+                        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 const int r = rbase + mi * 16 + i;
-                                const int c = wn * 64 + ni * 16 + cl;
+                                const int c = wn * 32 + ni * 16 + cl;
                                 *reinterpret_cast<uint16_t*>(gt + r * LDG + c * 2) =
                                     (uint16_t)f32_to_bf16(acc[mi][ni][i]);
                                 *reinterpret_cast<uint16_t*>(gt + r * LDG + 256 + c * 2) =
-                                    (uint16_t)f32_to_bf16(acc[mi][ni + 4][i]);
+                                    (uint16_t)f32_to_bf16(acc[mi][ni + 2][i]);
                             }
                 }
                 __syncthreads();
@@ -424,8 +491,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 template <int BN, int EPI>
 static int launch_gemm(const GemmArgs& a, hipStream_t stream) {
     const int ncu = num_cus();
-    int grid = ncu;  // one 256-thread block per CU (LDS bound), persistent
-    grid = (grid + 7) / 8 * 8;
+    const int grid = (ncu + 7) / 8 * 8;  // one 512-thread block per CU (LDS bound), persistent
     gemm_fp8_kernel<BN, EPI><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
     MOE_LAUNCH_CHECK("gemm_fp8_kernel");
     return MOE_OK;
@@ -454,10 +520,6 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
     MOE_REQUIRE(epilogue != MOE_EPI_SWIGLU_Q8 || out_s, MOE_ERR_NULL, "grouped_gemm: SWIGLU_Q8 needs out_s");
     MOE_REQUIRE(epilogue != MOE_EPI_SWIGLU_Q8_SAVE || (out_s && out2), MOE_ERR_NULL,
                 "grouped_gemm: SWIGLU_Q8_SAVE needs out_s and out2");
-    (void)epi_in;
-    (void)out2_s;
-    (void)out3;
-    (void)out3_s;
     MOE_REQUIRE((row_cap / GBM) * (N / 128) < ((int64_t)1 << 31), MOE_ERR_SHAPE,
                 "grouped_gemm: row_cap * N too large for the tile list");
     if (row_cap == 0) return MOE_OK;
