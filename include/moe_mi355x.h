@@ -175,16 +175,8 @@ enum {
                                     out = hq u8 [row_cap, f], out_s = [row_cap, f/128]   */
     MOE_EPI_SWIGLU_Q8_SAVE = 2,  /* as SWIGLU_Q8, and out2 = bf16 [G, U] [row_cap, 2f]   */
     MOE_EPI_STORE_F32 = 3,       /* out  = fp32 accumulators [row_cap, N] (inspection)  */
-    MOE_EPI_SWIGLU_F32 = 4,      /* out  = fp32 h [row_cap, f] before quantisation
+    MOE_EPI_SWIGLU_F32 = 4       /* out  = fp32 h [row_cap, f] before quantisation
                                     (inspection of the fused quantiser's input)         */
-    MOE_EPI_DSWIGLU_Q8 = 5       /* backward through SwiGLU: acc = dH [row_cap, f],
-                                    epi_in = saved bf16 [G, U] [row_cap, 2f];
-                                    dG = dH*U*s(G)*(1+G*(1-s(G))), dU = dH*G*s(G) (s =
-                                    sigmoid); out = dGU q 1x128 [row_cap, 2f] + out_s
-                                    [row_cap, 2f/128]; out2 = dGU q 128x1 transposed
-                                    [2f, row_cap] + out2_s [2f, row_cap/128]; out3 =
-                                    recomputed h = G*s(G)*U q 128x1 transposed [f,
-                                    row_cap] + out3_s [f, row_cap/128]                 */
 };
 
 /* Per-expert GEMM over the expert-grouped rows: for expert e, real rows
@@ -208,12 +200,35 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* b, c
  *                   aT_s[m, b] * bT_s[n, b] * sum_{r in b} dec(aT[m, r]) * dec(bT[n, r])
  * accumulated in fp32 and stored as bf16.
  *   aT [M, row_cap] e4m3, aT_s [M, row_cap/128]; bT [N, row_cap], bT_s [N, row_cap/128]
- *   (from moe_quant_fp8_rows_t or the DSWIGLU epilogue); dW [L, M, N] bf16.
+ *   (from moe_quant_fp8_rows_t or moe_swiglu_backward); dW [L, M, N] bf16.
  *   An expert with no rows gets dW[e] = 0.  M, N multiples of 128.           */
 int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8_t* bT,
                                const float* bT_s, const int32_t* offsets, int32_t L,
                                int64_t row_cap, int32_t M, int32_t N, uint16_t* dW,
                                hipStream_t stream);
+
+/* ---- SwiGLU backward [FP8] --------------------------------------------- */
+
+/* Backward through h = silu(G) * U for the rows of the expert-grouped layout
+ * ("RL at 1T scale", section "FP8 Training": every backward GEMM operand is
+ * block-quantised along that GEMM's contraction axis).  With s = sigmoid(G),
+ * in fp32, from dH (the dgrad GEMM through W2, MOE_EPI_STORE_F32) and the saved
+ * bf16 [G, U] (MOE_EPI_SWIGLU_Q8_SAVE's out2):
+ *     dG = dH * U * s * (1 + G * (1 - s)),  dU = dH * G * s,  H = G * s * U
+ * Outputs (quantised as in moe_quant_fp8):
+ *   dgu_q [row_cap, 2f] u8 + dgu_s [row_cap, 2f/128]   1x128 tiles of [dG, dU]
+ *   dgu_qT [2f, row_cap] u8 + dgu_sT [2f, row_cap/128] 128x1 tiles, transposed
+ *   h_qT [f, row_cap] u8 + h_sT [f, row_cap/128]       128x1 tiles of H, transposed
+ *   dgu_f32 [row_cap, 2f], h_f32 [row_cap, f]          optional (NULL = skip):
+ *                                                      the fp32 values quantised
+ * Padding rows (row_pair < 0) are 0 in the 128x1 tiles and are not written in
+ * the row-major outputs; rows at and past offsets[L] are not touched at all.
+ *   dH [row_cap, f] fp32, gu [row_cap, 2f] bf16, row_pair [row_cap]; f % 128 == 0. */
+int moe_swiglu_backward(const float* dH, const uint16_t* gu, const int32_t* row_pair,
+                        const int32_t* offsets, int32_t L, int64_t row_cap, int32_t f,
+                        uint8_t* dgu_q, float* dgu_s, uint8_t* dgu_qT, float* dgu_sT,
+                        uint8_t* h_qT, float* h_sT, float* dgu_f32, float* h_f32,
+                        hipStream_t stream);
 
 /* ---- combine [EP] ------------------------------------------------------- */
 

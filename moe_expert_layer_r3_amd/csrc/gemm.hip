@@ -23,17 +23,9 @@
 //     counts/offsets (no host sync); consecutive tiles share a weight tile and
 //     are mapped to the same XCD so that weight tile is fetched into one L2.
 //   * epilogues stage through LDS for coalesced 16-byte stores.
-#include <type_traits>
-
-#include "common.hpp"
+#include "mfma_common.hpp"
 
 namespace moe {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-typedef const __attribute__((address_space(4))) float* cfloat_ptr;
 
 constexpr int GBM = 128;
 constexpr int GBK = 128;
@@ -61,70 +53,6 @@ struct GemmArgs {
     void* out3;
     float* out3_s;
 };
-
-// 16- / 4-byte global -> LDS transfer (global_load_lds_dwordx4 / _dword): lane
-// l's bytes land at LDS byte address m0 + l*size (m0 = `lds`, wave-uniform).
-// Written as inline assembly so that the compiler does not know these VMEM
-// instructions write LDS: it would otherwise wait for all of them (vmcnt(0))
-// before every LDS read, serialising the pipeline.  Completion is awaited with
-// explicit vmcnt waits followed by a barrier before a stage is read.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-    asm volatile("global_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds) : "memory");
-}
-
-// s_waitcnt immediate waiting for vmcnt <= N only (gfx9 encoding: vmcnt[3:0],
-// expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-typedef const __attribute__((address_space(3))) u32x4* lds_u32x4_ptr;
-typedef const __attribute__((address_space(3))) v2u* lds_v2u_ptr;
-
-// Plain LDS loads (the compiler tracks their lgkmcnt).  `base` comes out of an
-// opaque move placed after the stage's barrier, so no read can be hoisted
-// above the barrier that makes the stage's DMA data visible.
-template <int OFF>
-__device__ __forceinline__ u32x4 lds16(uint32_t addr) {
-    return *(lds_u32x4_ptr)(uintptr_t)(addr + OFF);
-}
-template <int OFF>
-__device__ __forceinline__ v2u lds8(uint32_t addr) {
-    return *(lds_v2u_ptr)(uintptr_t)(addr + OFF);
-}
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-    asm volatile("" : "+v"(v));
-    return v;
-}
-
-__device__ __forceinline__ v8i join8(u32x4 lo, u32x4 hi) {
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b) {
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    // E8M0 127 = 2^0: the hardware block scales are 1, the fp32 scales are
-    // applied by the caller
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
-}
-
 constexpr bool is_swiglu(int epi) {
     return epi == MOE_EPI_SWIGLU_Q8 || epi == MOE_EPI_SWIGLU_Q8_SAVE || epi == MOE_EPI_SWIGLU_F32;
 }
@@ -540,12 +468,4 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
             return launch_gemm<256, MOE_EPI_SWIGLU_F32>(ga, stream);
     }
     return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm: epilogue %d", epilogue);
-}
-
-extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8_t* bT,
-                                          const float* bT_s, const int32_t* offsets, int32_t L, int64_t row_cap,
-                                          int32_t M, int32_t N, uint16_t* dW, hipStream_t stream) {
-    (void)aT; (void)aT_s; (void)bT; (void)bT_s; (void)offsets; (void)L; (void)row_cap; (void)M; (void)N;
-    (void)dW; (void)stream;
-    return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm_wgrad: not available in this build");
 }

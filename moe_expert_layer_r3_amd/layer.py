@@ -99,3 +99,94 @@ class ForwardPlan:
         rec("gemm2", self.gemm2, wts)
         rec("combine", self.combine)
         return self.y
+
+
+class TrainPlan(ForwardPlan):
+    """Device buffers for one forward + backward pass of T tokens.
+
+    Backward ("RL at 1T scale", section "FP8 Training": every backward GEMM operand
+    is block-quantised along that GEMM's contraction axis):
+      combine backward -> dY (1x128 FP8) and d_gate;  dY 128x1 (transposed)
+      dgrad GEMM through W2 (fp32 dH) -> SwiGLU backward -> [dG, dU] 1x128 and
+      128x1, recomputed H 128x1;  dgrad GEMM through W13 -> dX -> unpermute-sum dx
+      x 128x1 (transposed);  wgrad GEMMs dW2 = dY^T H, dW13 = [dG, dU]^T X
+      softmax-over-selection backward -> d_logits."""
+
+    def __init__(self, T, d, f, E, L, k, e0=0, device="cuda"):
+        super().__init__(T, d, f, E, L, k, e0=e0, device=device, save_gu=True)
+        dv = device
+        f32, u8, b16 = torch.float32, torch.uint8, torch.bfloat16
+        R = self.rcap
+        self.dyq = torch.empty((R, d), dtype=u8, device=dv)
+        self.dyq_s = torch.empty((R, d // 128), dtype=f32, device=dv)
+        self.d_gate = torch.empty((T, k), dtype=f32, device=dv)
+        self.dyqT = torch.empty((d, R), dtype=u8, device=dv)
+        self.dyqT_s = torch.empty((d, R // 128), dtype=f32, device=dv)
+        self.dH = torch.empty((R, f), dtype=f32, device=dv)
+        self.sb = dict(dgu_q=torch.empty((R, 2 * f), dtype=u8, device=dv),
+                       dgu_s=torch.empty((R, 2 * f // 128), dtype=f32, device=dv),
+                       dgu_qT=torch.empty((2 * f, R), dtype=u8, device=dv),
+                       dgu_sT=torch.empty((2 * f, R // 128), dtype=f32, device=dv),
+                       h_qT=torch.empty((f, R), dtype=u8, device=dv),
+                       h_sT=torch.empty((f, R // 128), dtype=f32, device=dv))
+        self.dX = torch.empty((R, d), dtype=b16, device=dv)
+        self.dx = torch.empty((T, d), dtype=b16, device=dv)
+        self.xqT = torch.empty((d, R), dtype=u8, device=dv)
+        self.xqT_s = torch.empty((d, R // 128), dtype=f32, device=dv)
+        self.dW2 = torch.empty((L, d, f), dtype=b16, device=dv)
+        self.dW13 = torch.empty((L, 2 * f, d), dtype=b16, device=dv)
+        self.d_logits = torch.empty((T, E), dtype=f32, device=dv)
+
+    def combine_bwd(self, dy):
+        _call("moe_combine_backward", _p(dy), _p(self.Y), _p(self.pair_row), _p(self.w), self.T, self.k, self.d,
+              self.rcap, _p(self.dyq), _p(self.dyq_s), _p(self.d_gate), _stream())
+        _call("moe_quant_fp8_rows_t", _p(dy), _p(self.w), _p(self.row_pair), _p(self.offsets), self.L, self.rcap,
+              self.k, self.d, _p(self.dyqT), _p(self.dyqT_s), _stream())
+
+    def dgrad2(self, wts):
+        _call("moe_grouped_gemm_fp8", _p(self.dyq), _p(self.dyq_s), _p(wts["w2qT"]), _p(wts["w2sT"]),
+              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.f, self.d, ops.EPI_STORE_F32, None,
+              _p(self.dH), None, None, None, None, None, _stream())
+
+    def swiglu_bwd(self):
+        s = self.sb
+        _call("moe_swiglu_backward", _p(self.dH), _p(self.gu), _p(self.row_pair), _p(self.offsets), self.L,
+              self.rcap, self.f, _p(s["dgu_q"]), _p(s["dgu_s"]), _p(s["dgu_qT"]), _p(s["dgu_sT"]),
+              _p(s["h_qT"]), _p(s["h_sT"]), None, None, _stream())
+
+    def dgrad1(self, wts):
+        _call("moe_grouped_gemm_fp8", _p(self.sb["dgu_q"]), _p(self.sb["dgu_s"]), _p(wts["w13qT"]),
+              _p(wts["w13sT"]), _p(self.counts), _p(self.offsets), self.L, self.rcap, self.d, 2 * self.f,
+              ops.EPI_STORE_BF16, None, _p(self.dX), None, None, None, None, None, _stream())
+        _call("moe_unpermute_combine", _p(self.dX), _p(self.pair_row), None, self.T, self.k, self.d, self.rcap,
+              _p(self.dx), _stream())
+
+    def wgrad(self, x):
+        _call("moe_quant_fp8_rows_t", _p(x), None, _p(self.row_pair), _p(self.offsets), self.L, self.rcap,
+              self.k, self.d, _p(self.xqT), _p(self.xqT_s), _stream())
+        _call("moe_grouped_gemm_fp8_wgrad", _p(self.dyqT), _p(self.dyqT_s), _p(self.sb["h_qT"]),
+              _p(self.sb["h_sT"]), _p(self.offsets), self.L, self.rcap, self.d, self.f, _p(self.dW2), _stream())
+        _call("moe_grouped_gemm_fp8_wgrad", _p(self.sb["dgu_qT"]), _p(self.sb["dgu_sT"]), _p(self.xqT),
+              _p(self.xqT_s), _p(self.offsets), self.L, self.rcap, 2 * self.f, self.d, _p(self.dW13), _stream())
+
+    def gate_bwd(self):
+        _call("moe_gate_backward", _p(self.d_gate), _p(self.w), _p(self.ids), self.T, self.k, self.E,
+              _p(self.d_logits), _stream())
+
+    def backward(self, x, dy, wts, events=None):
+        """Backward of the last ``forward`` for upstream gradient dy [T, d] bf16;
+        wts must hold the transposed weight copies (quantize_weights(transpose=True))."""
+        def rec(name, fn, *a):
+            if events is not None and name in events:
+                events[name][0].record()
+                fn(*a)
+                events[name][1].record()
+            else:
+                fn(*a)
+        rec("combine_bwd", self.combine_bwd, dy)
+        rec("dgrad2", self.dgrad2, wts)
+        rec("swiglu_bwd", self.swiglu_bwd)
+        rec("dgrad1", self.dgrad1, wts)
+        rec("wgrad", self.wgrad, x)
+        rec("gate_bwd", self.gate_bwd)
+        return self.dx, self.dW13, self.dW2, self.d_logits

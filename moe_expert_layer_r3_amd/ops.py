@@ -13,7 +13,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
-EPI_STORE_BF16, EPI_SWIGLU_Q8, EPI_SWIGLU_Q8_SAVE, EPI_STORE_F32, EPI_SWIGLU_F32, EPI_DSWIGLU_Q8 = range(6)
+EPI_STORE_BF16, EPI_SWIGLU_Q8, EPI_SWIGLU_Q8_SAVE, EPI_STORE_F32, EPI_SWIGLU_F32 = range(5)
 TILE_1x128, TILE_128x128 = 0, 1
 SRC_BF16, SRC_F32 = 0, 1
 FLAG_BAD_ID, FLAG_DUP_ID, FLAG_ROW_CAP = 1, 2, 4
@@ -47,6 +47,8 @@ _SIGS = {
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
                                             _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_gemm_fp8_wgrad": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P]),
+    "moe_swiglu_backward": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P]),
     "moe_unpermute_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I64, _P, _P]),
     "moe_combine_backward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _I64, _P, _P, _P, _P]),
     "moe_gate_backward": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
@@ -248,7 +250,7 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     a [rcap, K] u8, a_s [rcap, K/128]; b [L, N, K] u8, b_s [L, N/128, K/128].
     Returns the epilogue's outputs: STORE_BF16 -> y; STORE_F32 -> acc;
     SWIGLU_Q8 -> (hq, hq_s); SWIGLU_Q8_SAVE -> (hq, hq_s, gu);
-    SWIGLU_F32 -> h; DSWIGLU_Q8 -> (dgu_q, dgu_s, dguT_q, dguT_s, hT_q, hT_s)."""
+    SWIGLU_F32 -> h."""
     rcap = a.shape[0] if rcap is None else rcap
     L, N, K = b.shape
     dev = _dev(a)
@@ -270,15 +272,6 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     elif epilogue == EPI_SWIGLU_F32:
         out = torch.empty((rcap, f), dtype=torch.float32, device=dev)
         res = out
-    elif epilogue == EPI_DSWIGLU_Q8:
-        n2 = 2 * N                      # dGU has 2f columns, N = f here
-        out = torch.empty((rcap, n2), dtype=torch.uint8, device=dev)
-        out_s = torch.empty((rcap, n2 // 128), dtype=torch.float32, device=dev)
-        out2 = torch.empty((n2, rcap), dtype=torch.uint8, device=dev)
-        out2_s = torch.empty((n2, rcap // 128), dtype=torch.float32, device=dev)
-        out3 = torch.empty((N, rcap), dtype=torch.uint8, device=dev)
-        out3_s = torch.empty((N, rcap // 128), dtype=torch.float32, device=dev)
-        res = (out, out_s, out2, out2_s, out3, out3_s)
     else:
         raise ValueError(f"unknown epilogue {epilogue}")
     _call("moe_grouped_gemm_fp8", _p(a), _p(a_s), _p(b), _p(b_s), _p(counts), _p(offsets), L, rcap, N, K,
@@ -286,12 +279,39 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     return res
 
 
-def grouped_gemm_wgrad(aT, aT_s, bT, bT_s, offsets, L, rcap):
+def grouped_gemm_wgrad(aT, aT_s, bT, bT_s, offsets, L, rcap, out=None):
+    """dW [L, M, N] bf16 from the 128x1-quantised transposed operands aT [M, rcap], bT [N, rcap]."""
     M, N = aT.shape[0], bT.shape[0]
-    dW = torch.empty((L, M, N), dtype=torch.bfloat16, device=_dev(aT))
+    dW = torch.empty((L, M, N), dtype=torch.bfloat16, device=_dev(aT)) if out is None else out
     _call("moe_grouped_gemm_fp8_wgrad", _p(aT), _p(aT_s), _p(bT), _p(bT_s), _p(offsets), L, rcap, M, N, _p(dW),
           _stream(aT.device))
     return dW
+
+
+def swiglu_backward(dH, gu, row_pair, offsets, L, rcap, inspect=False, out=None):
+    """Backward through SwiGLU + FP8 re-quantisation of its results.
+
+    dH [rcap, f] fp32, gu [rcap, 2f] bf16 (saved G, U).  Returns a dict with
+    dgu_q, dgu_s (1x128), dgu_qT, dgu_sT (128x1, transposed), h_qT, h_sT and, when
+    inspect, the fp32 dgu and h that were quantised.  ``out`` may hold
+    preallocated tensors under the same names."""
+    _contig(dH, torch.float32, "dH")
+    _contig(gu, torch.bfloat16, "gu")
+    f = dH.shape[1]
+    dev = _dev(dH)
+    o = {} if out is None else dict(out)
+    shapes = dict(dgu_q=((rcap, 2 * f), torch.uint8), dgu_s=((rcap, 2 * f // 128), torch.float32),
+                  dgu_qT=((2 * f, rcap), torch.uint8), dgu_sT=((2 * f, rcap // 128), torch.float32),
+                  h_qT=((f, rcap), torch.uint8), h_sT=((f, rcap // 128), torch.float32))
+    if inspect:
+        shapes.update(dgu=((rcap, 2 * f), torch.float32), h=((rcap, f), torch.float32))
+    for name, (shape, dt) in shapes.items():
+        if name not in o:
+            o[name] = torch.empty(shape, dtype=dt, device=dev)
+    _call("moe_swiglu_backward", _p(dH), _p(gu), _p(row_pair), _p(offsets), L, rcap, f,
+          _p(o["dgu_q"]), _p(o["dgu_s"]), _p(o["dgu_qT"]), _p(o["dgu_sT"]), _p(o["h_qT"]), _p(o["h_sT"]),
+          _p(o.get("dgu")), _p(o.get("h")), _stream(dev))
+    return o
 
 
 # ---------------------------------------------------------------- combine
