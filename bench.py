@@ -1,18 +1,26 @@
 """Benchmark of the MoE expert layer on one MI355X.
 
-One step = one forward pass of the layer on the EP=8 share of a 256-expert top-8
-layer (T=8192 tokens, d=7168, f=2048 SwiGLU, local experts 0-31): top-k routing,
-the expert-grouped permutation with fused 1x128 FP8 quantisation, grouped GEMM1
-with the fused SwiGLU + quantisation epilogue, grouped GEMM2, weighted combine.
-Weights are quantised once (static weights) before the timed region; that cost
-is reported separately.  Inputs are seeded synthetic tensors already resident in
-HBM when timing starts.
+Headline step = one forward pass of the layer on the EP=8 share of a 256-expert
+top-8 layer (T=8192 tokens, d=7168, f=2048 SwiGLU, local experts 0-31): top-k
+routing, the expert-grouped permutation with fused 1x128 FP8 quantisation,
+grouped GEMM1 with the fused SwiGLU + quantisation epilogue, grouped GEMM2,
+weighted combine.  Weights are static there: quantised once before the timed
+region, that cost reported separately.  Inputs are seeded synthetic tensors
+already resident in HBM when timing starts.
 
-Prints one JSON line (rank 0).  Besides the throughput it reports the roofline
-fraction of the dominant kernel (grouped GEMM1, HBM-bound at this shape) from
-HIP events recorded on the launch stream, and the oracle's throughput on the
-host cores (a bounded sample: all tokens routed and permuted, expert work for
-2 of the 32 local experts, extrapolated linearly in the number of experts)."""
+Further legs, reported as sub-objects of the same JSON line:
+  hotspot  the same forward with Zipf-skewed routing (unequal expert loads)
+  train    forward + backward at T=16384 (dgrad and wgrad GEMMs on FP8 operands
+           re-quantised along their contraction axis), weights re-quantised
+           every step (the step time is also given without that part)
+  replay   Router Replay of a recorded [4, 8, 131072] id tensor: every layer's
+           131072 tokens in 16384-token chunks, each layer with its own weights
+
+Prints one JSON line.  Besides the throughput it reports the roofline fraction
+of the headline step's dominant kernel (grouped GEMM1, HBM-bound at this shape)
+from HIP events recorded on the launch stream, and the oracle's throughput on
+the host cores (a bounded sample: all tokens routed and permuted, expert work
+for 2 of the 32 local experts, extrapolated linearly in the number of experts)."""
 
 import argparse
 import json
@@ -25,6 +33,7 @@ import torch
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+METRIC = "MoE-layer tokens/s + FP8 grouped-GEMM TFLOP/s (% of MFMA peak)"
 
 
 def parse():
@@ -32,7 +41,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ep8", choices=["ep8", "hotspot"])
+    ap.add_argument("--workload", default="ep8", choices=["ep8", "hotspot"],
+                    help="workload of the headline forward step")
+    ap.add_argument("--legs", default="hotspot,train,replay",
+                    help="comma-separated extra legs (hotspot, train, replay) or 'none'")
+    ap.add_argument("--train-steps", type=int, default=5)
+    ap.add_argument("--replay-passes", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
@@ -52,8 +66,10 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}), flush=True)
 
 
+# ---------------------------------------------------------------- algorithmic work
+
 def gemm_algorithmic(P, L, d, f):
-    """Algorithmic FLOPs and HBM bytes of the two grouped GEMMs for P local pairs."""
+    """Algorithmic FLOPs and HBM bytes of the two forward grouped GEMMs for P local pairs."""
     g1_flops = 2.0 * P * d * (2 * f)
     g2_flops = 2.0 * P * f * d
     g1_bytes = (L * 2 * f * d + L * (2 * f // 128) * (d // 128) * 4     # W13 codes + scales
@@ -63,6 +79,13 @@ def gemm_algorithmic(P, L, d, f):
                 + P * f + P * (f // 128) * 4
                 + P * d * 2)                                             # Y bf16
     return g1_flops, g1_bytes, g2_flops, g2_bytes
+
+
+def train_gemm_flops(P, d, f):
+    """FLOPs of the six grouped GEMMs of a training step (P local pairs)."""
+    return {"gemm1": 4.0 * P * d * f, "gemm2": 2.0 * P * d * f,
+            "dgrad2": 2.0 * P * d * f, "dgrad1": 4.0 * P * d * f,
+            "wgrad2": 2.0 * P * d * f, "wgrad13": 4.0 * P * d * f}
 
 
 def measured_traffic(workload):
@@ -76,12 +99,200 @@ def measured_traffic(workload):
     rec = json.load(open(path))
     src = os.path.join(here, "moe_expert_layer_r3_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.hpp"):
+    for f in rec.get("sources", ["gemm.hip", "common.hpp"]):
         h.update(open(os.path.join(src, f), "rb").read())
     if h.hexdigest() != rec["source_sha256"]:
         return None
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
+
+def stage_events(names, steps):
+    return {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(steps)] for n in names}
+
+
+def mean_ms(ev):
+    return {n: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for n, pairs in ev.items()}
+
+
+def free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- forward leg
+
+def forward_leg(wl, steps, warmup, dev):
+    from moe_expert_layer_r3_amd import synth
+    from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights, weight_buffers
+
+    lg = synth.logits(wl)
+    x = synth.x(wl)
+    W13 = synth.weights(wl, "w13")
+    W2 = synth.weights(wl, "w2")
+    lg_d = torch.from_numpy(lg).to(dev)
+    x_d = x.to(dev)
+    W13_d, W2_d = W13.to(dev), W2.to(dev)
+
+    # weight quantisation (once per weight version), timed on its own
+    wts = weight_buffers(wl.L, wl.d, wl.f, dev)
+    quantize_weights(W13_d, W2_d, out=wts)
+    torch.cuda.synchronize()
+    qe0, qe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qe0.record()
+    for _ in range(3):
+        quantize_weights(W13_d, W2_d, out=wts)
+    qe1.record()
+    torch.cuda.synchronize()
+    wquant_ms = qe0.elapsed_time(qe1) / 3
+    del W13_d, W2_d
+    free()
+
+    plan = ForwardPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev)
+    for _ in range(warmup):
+        plan.forward(x_d, lg_d, wts)
+    ev = stage_events(plan.STAGES, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        plan.forward(x_d, lg_d, wts, events={n: ev[n][s] for n in plan.STAGES})
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    kern = mean_ms(ev)
+    counts = plan.counts.cpu().numpy()
+    P = int(counts.sum())
+    g1f, g1b, g2f, g2b = gemm_algorithmic(P, wl.L, wl.d, wl.f)
+    g1_s, g2_s = kern["gemm1"] * 1e-3, kern["gemm2"] * 1e-3
+    res = {
+        "tokens_per_s": wl.T / (ms * 1e-3),
+        "ms_per_step": ms,
+        "kernel_ms": kern,
+        "weight_quant_ms": wquant_ms,
+        "local_pairs": P,
+        "expert_counts": {"max": int(counts.max()), "mean": float(counts.mean()), "min": int(counts.min())},
+        "gemm1": {"tflops": g1f / g1_s / 1e12, "gbs": g1b / g1_s / 1e9, "bytes": g1b, "flops": g1f},
+        "gemm2": {"tflops": g2f / g2_s / 1e12, "gbs": g2b / g2_s / 1e9, "bytes": g2b, "flops": g2f},
+        "gemm_tflops": (g1f + g2f) / (g1_s + g2_s) / 1e12,
+    }
+    res["gemm_mfma_frac"] = res["gemm_tflops"] / FP8_PEAK_TFLOPS
+    del plan, wts, lg_d, x_d
+    free()
+    return res, (lg, x, W13, W2)
+
+
+# ---------------------------------------------------------------- training leg
+
+def train_leg(steps, warmup, dev):
+    from moe_expert_layer_r3_amd import synth
+    from moe_expert_layer_r3_amd.layer import TrainPlan, quantize_weights, weight_buffers
+
+    wl = synth.WORKLOADS["train"]
+    lg_d = torch.from_numpy(synth.logits(wl)).to(dev)
+    x_d = synth.x(wl).to(dev)
+    dy_d = synth.dy(wl).to(dev)
+    W13_d = synth.weights(wl, "w13").to(dev)
+    W2_d = synth.weights(wl, "w2").to(dev)
+    wts = weight_buffers(wl.L, wl.d, wl.f, dev, transpose=True)
+    plan = TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev)
+
+    def step(events=None):
+        if events is not None:
+            events["weight_quant"][0].record()
+        quantize_weights(W13_d, W2_d, transpose=True, out=wts)
+        if events is not None:
+            events["weight_quant"][1].record()
+        plan.forward(x_d, lg_d, wts, events=events)
+        plan.backward(x_d, dy_d, wts, events=events)
+
+    for _ in range(warmup):
+        step()
+    names = ("weight_quant",) + plan.STAGES + plan.BWD_STAGES
+    ev = stage_events(names, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step({n: ev[n][s] for n in names})
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    kern = mean_ms(ev)
+    P = int(plan.counts.sum().item())
+    fl = train_gemm_flops(P, wl.d, wl.f)
+    gemm_ms = sum(kern[n] for n in fl)
+    per = {n: {"ms": kern[n], "tflops": fl[n] / (kern[n] * 1e-3) / 1e12,
+               "mfma_frac": fl[n] / (kern[n] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS} for n in fl}
+    top = max(fl, key=lambda n: kern[n])
+    res = {
+        "workload": f"train: T={wl.T}, d={wl.d}, f={wl.f}, {wl.L} of {wl.E} experts local, top-{wl.k}, "
+                    "forward + backward, weights re-quantised each step",
+        "tokens_per_s": wl.T / (ms * 1e-3),
+        "ms_per_step": ms,
+        "ms_per_step_excl_weight_quant": ms - kern["weight_quant"],
+        "local_pairs": P,
+        "kernel_ms": kern,
+        "gemms": per,
+        "gemm_tflops": sum(fl.values()) / (gemm_ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "kernel": top, "achieved": per[top]["tflops"], "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": per[top]["mfma_frac"], "traffic": None},
+    }
+    res["gemm_mfma_frac"] = res["gemm_tflops"] / FP8_PEAK_TFLOPS
+    del plan, wts, lg_d, x_d, dy_d, W13_d, W2_d
+    free()
+    return res
+
+
+# ---------------------------------------------------------------- replay leg
+
+def replay_leg(passes, dev):
+    from moe_expert_layer_r3_amd import synth
+    from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights, weight_buffers
+
+    wl = synth.WORKLOADS["replay"]
+    rec_d = torch.from_numpy(synth.replay_record(wl)).to(dev)
+    nchunk = wl.seq_len // wl.T
+    layers = []
+    for l in range(wl.n_layers):
+        wts = weight_buffers(wl.L, wl.d, wl.f, dev)
+        quantize_weights(synth.weights(wl, "w13", layer=l).to(dev), synth.weights(wl, "w2", layer=l).to(dev),
+                         out=wts)
+        xs = [synth.x(wl, layer=l, t0=c * wl.T).to(dev) for c in range(nchunk)]
+        lgs = [torch.from_numpy(synth.logits(wl, layer=l, t0=c * wl.T)).to(dev) for c in range(nchunk)]
+        layers.append((wts, xs, lgs))
+        free()
+    plan = ForwardPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev)
+
+    def one_pass(ev=None, i=0):
+        for l, (wts, xs, lgs) in enumerate(layers):
+            for c in range(nchunk):
+                events = None if ev is None else {n: ev[n][i * wl.n_layers * nchunk + l * nchunk + c]
+                                                  for n in plan.STAGES}
+                plan.forward(xs[c], lgs[c], wts, replay=(rec_d, l, c * wl.T), events=events)
+
+    one_pass()
+    ev = stage_events(plan.STAGES, passes * wl.n_layers * nchunk)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(passes):
+        one_pass(ev, i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / passes
+    flags = int(plan.status.item())
+    res = {
+        "workload": f"replay: record [{wl.n_layers}, {wl.k}, {wl.seq_len}] Zipf({wl.rec_zipf}) ids, "
+                    f"{wl.T}-token chunks, d={wl.d}, f={wl.f}, {wl.L} of {wl.E} experts local, forward",
+        "layer_tokens_per_s": wl.n_layers * wl.seq_len / (ms * 1e-3),
+        "ms_per_pass": ms,
+        "kernel_ms_per_chunk": mean_ms(ev),
+        "status_flags": flags,
+    }
+    del plan, layers, rec_d
+    free()
+    return res
+
+
+# ---------------------------------------------------------------- host baseline
 
 def cpu_baseline(wl, lg, x_bf16, W13, W2):
     """The oracle on the host: routing + permutation for all tokens, expert work
@@ -132,64 +343,20 @@ def main():
               "the expert-parallel exchange across GPUs is not part of it", file=sys.stderr)
         sys.exit(2)
     from moe_expert_layer_r3_amd import synth
-    from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights
 
-    wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    lg = synth.logits(wl)
-    x = synth.x(wl)
-    W13 = synth.weights(wl, "w13")
-    W2 = synth.weights(wl, "w2")
-    lg_d = torch.from_numpy(lg).to(dev)
-    x_d = x.to(dev)
-    W13_d, W2_d = W13.to(dev), W2.to(dev)
-
-    # weight quantisation (once per weight version), timed on its own
-    wts = quantize_weights(W13_d, W2_d)
-    torch.cuda.synchronize()
-    qe0, qe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    qe0.record()
-    for _ in range(3):
-        wts = quantize_weights(W13_d, W2_d)
-    qe1.record()
-    torch.cuda.synchronize()
-    wquant_ms = qe0.elapsed_time(qe1) / 3
-    del W13_d, W2_d
-    torch.cuda.empty_cache()
-
-    plan = ForwardPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev)
-    for _ in range(args.warmup):
-        plan.forward(x_d, lg_d, wts)
-    torch.cuda.synchronize()
-
-    names = ["route", "permute", "gemm1", "gemm2", "combine"]
-    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for n in names}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        plan.forward(x_d, lg_d, wts, events={n: ev[n][s] for n in names})
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-    kern_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
-
-    counts = plan.counts.cpu().numpy()
-    P = int(counts.sum())
-    g1f, g1b, g2f, g2b = gemm_algorithmic(P, wl.L, wl.d, wl.f)
-    g1_s, g2_s = kern_ms["gemm1"] * 1e-3, kern_ms["gemm2"] * 1e-3
-    ach_gbs = g1b / g1_s / 1e9
-    gemm_tflops = (g1f + g2f) / (g1_s + g2_s) / 1e12
-
+    wl = synth.WORKLOADS[args.workload]
+    head, inputs = forward_leg(wl, args.steps, args.warmup, dev)
+    g1 = head["gemm1"]
     out = {
-        "metric": "MoE-layer tokens/s + FP8 grouped-GEMM TFLOP/s (% of MFMA peak)",
-        "value": wl.T / (ms * 1e-3),
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -197,18 +364,33 @@ def main():
         "data": "synthetic (seeded normals; random-init N(0,0.02) expert weights)",
         "config": {"workload": f"{wl.name}: one EP=8 share of a 256-expert top-8 MoE layer forward",
                    "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "local_experts": wl.L, "top_k": wl.k,
-                   "local_pairs": P},
+                   "local_pairs": head["local_pairs"]},
         "roofline": {"bound": "hbm", "kernel": "grouped GEMM1 + SwiGLU + quant (gemm_fp8_kernel<256,1>)",
-                     "achieved": ach_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach_gbs / HBM_PEAK_GBS,
+                     "achieved": g1["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": g1["gbs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic(wl.name)},
-        "gemm_tflops": gemm_tflops,
-        "gemm_mfma_frac": gemm_tflops / FP8_PEAK_TFLOPS,
-        "kernel_ms": kern_ms,
-        "weight_quant_ms": wquant_ms,
-        "expert_counts": {"max": int(counts.max()), "mean": float(counts.mean()), "min": int(counts.min())},
+        "gemm_tflops": head["gemm_tflops"],
+        "gemm_mfma_frac": head["gemm_mfma_frac"],
+        "kernel_ms": head["kernel_ms"],
+        "weight_quant_ms": head["weight_quant_ms"],
+        "expert_counts": head["expert_counts"],
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, lg, x, W13, W2)
+        out["cpu_baseline"] = cpu_baseline(wl, *inputs)
+    del inputs
+    legs = [] if args.legs == "none" else [s for s in args.legs.split(",") if s]
+    out["legs"] = {}
+    for leg in legs:
+        if leg == "hotspot" and args.workload != "hotspot":
+            r, _ = forward_leg(synth.WORKLOADS["hotspot"], args.steps, args.warmup, dev)
+            r["workload"] = "hotspot: ep8 shape, logits biased -1.2 ln(e+1) (expert 0 hottest), forward"
+            out["legs"]["hotspot"] = r
+        elif leg == "train":
+            out["legs"]["train"] = train_leg(args.train_steps, 2, dev)
+        elif leg == "replay":
+            out["legs"]["replay"] = replay_leg(args.replay_passes, dev)
+        else:
+            raise SystemExit(f"unknown leg {leg}")
+        print(f"# leg {leg} done", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 

@@ -12,17 +12,32 @@ from . import ops
 from .ops import _call, _p, _stream
 
 
-def quantize_weights(W13, W2, transpose=False):
-    """bf16 W13 [L, 2f, d], W2 [L, d, f] -> dict of FP8 codes and scales (and the
-    transposed copies used by the dgrad GEMMs when ``transpose``)."""
-    out = {}
-    r13 = ops.quant_fp8(W13, tile=ops.TILE_128x128, transpose=transpose)
-    r2 = ops.quant_fp8(W2, tile=ops.TILE_128x128, transpose=transpose)
-    out["w13q"], out["w13s"] = r13[0], r13[1]
-    out["w2q"], out["w2s"] = r2[0], r2[1]
+def weight_buffers(L, d, f, device="cuda", transpose=False):
+    """Preallocated FP8 weight codes and scales for quantize_weights(out=...)."""
+    u8, f32 = torch.uint8, torch.float32
+    e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)
+    out = dict(w13q=e((L, 2 * f, d), u8), w13s=e((L, 2 * f // 128, d // 128), f32),
+               w2q=e((L, d, f), u8), w2s=e((L, d // 128, f // 128), f32))
     if transpose:
-        out["w13qT"], out["w13sT"] = r13[2], r13[3]
-        out["w2qT"], out["w2sT"] = r2[2], r2[3]
+        out.update(w13qT=e((L, d, 2 * f), u8), w13sT=e((L, d // 128, 2 * f // 128), f32),
+                   w2qT=e((L, f, d), u8), w2sT=e((L, f // 128, d // 128), f32))
+    return out
+
+
+def quantize_weights(W13, W2, transpose=False, out=None):
+    """bf16 W13 [L, 2f, d], W2 [L, d, f] -> dict of FP8 codes and scales (and the
+    transposed copies used by the dgrad GEMMs when ``transpose``), 128x128 tiles.
+    ``out`` (from weight_buffers) receives the result without allocating."""
+    L, f2, d = W13.shape
+    if out is None:
+        out = weight_buffers(L, d, f2 // 2, W13.device, transpose)
+    for W, q, s in ((W13, "w13q", "w13s"), (W2, "w2q", "w2s")):
+        if W.dtype != torch.bfloat16 or not W.is_contiguous():
+            raise ValueError("weights must be contiguous bf16")
+        _, rows, cols = W.shape
+        qT, sT = (out[q + "T"], out[s + "T"]) if transpose else (None, None)
+        _call("moe_quant_fp8", _p(W), ops.SRC_BF16, L, rows, cols, cols, ops.TILE_128x128, _p(out[q]), _p(out[s]),
+              _p(qT), _p(sT), _stream())
     return out
 
 
@@ -79,6 +94,8 @@ class ForwardPlan:
     def combine(self):
         _call("moe_unpermute_combine", _p(self.Y), _p(self.pair_row), _p(self.w), self.T, self.k, self.d,
               self.rcap, _p(self.y), _stream())
+
+    STAGES = ("route", "permute", "gemm1", "gemm2", "combine")
 
     def forward(self, x, logits, wts, replay=None, events=None):
         """One forward pass.  replay = (rec, layer, s0) replays recorded ids.
@@ -140,6 +157,8 @@ class TrainPlan(ForwardPlan):
     def combine_bwd(self, dy):
         _call("moe_combine_backward", _p(dy), _p(self.Y), _p(self.pair_row), _p(self.w), self.T, self.k, self.d,
               self.rcap, _p(self.dyq), _p(self.dyq_s), _p(self.d_gate), _stream())
+
+    def dy_quant_t(self, dy):
         _call("moe_quant_fp8_rows_t", _p(dy), _p(self.w), _p(self.row_pair), _p(self.offsets), self.L, self.rcap,
               self.k, self.d, _p(self.dyqT), _p(self.dyqT_s), _stream())
 
@@ -158,20 +177,29 @@ class TrainPlan(ForwardPlan):
         _call("moe_grouped_gemm_fp8", _p(self.sb["dgu_q"]), _p(self.sb["dgu_s"]), _p(wts["w13qT"]),
               _p(wts["w13sT"]), _p(self.counts), _p(self.offsets), self.L, self.rcap, self.d, 2 * self.f,
               ops.EPI_STORE_BF16, None, _p(self.dX), None, None, None, None, None, _stream())
+
+    def unpermute(self):
         _call("moe_unpermute_combine", _p(self.dX), _p(self.pair_row), None, self.T, self.k, self.d, self.rcap,
               _p(self.dx), _stream())
 
-    def wgrad(self, x):
+    def x_quant_t(self, x):
         _call("moe_quant_fp8_rows_t", _p(x), None, _p(self.row_pair), _p(self.offsets), self.L, self.rcap,
               self.k, self.d, _p(self.xqT), _p(self.xqT_s), _stream())
+
+    def wgrad2(self):
         _call("moe_grouped_gemm_fp8_wgrad", _p(self.dyqT), _p(self.dyqT_s), _p(self.sb["h_qT"]),
               _p(self.sb["h_sT"]), _p(self.offsets), self.L, self.rcap, self.d, self.f, _p(self.dW2), _stream())
+
+    def wgrad13(self):
         _call("moe_grouped_gemm_fp8_wgrad", _p(self.sb["dgu_qT"]), _p(self.sb["dgu_sT"]), _p(self.xqT),
               _p(self.xqT_s), _p(self.offsets), self.L, self.rcap, 2 * self.f, self.d, _p(self.dW13), _stream())
 
     def gate_bwd(self):
         _call("moe_gate_backward", _p(self.d_gate), _p(self.w), _p(self.ids), self.T, self.k, self.E,
               _p(self.d_logits), _stream())
+
+    BWD_STAGES = ("combine_bwd", "dy_quant_t", "dgrad2", "swiglu_bwd", "dgrad1", "unpermute", "x_quant_t",
+              "wgrad2", "wgrad13", "gate_bwd")
 
     def backward(self, x, dy, wts, events=None):
         """Backward of the last ``forward`` for upstream gradient dy [T, d] bf16;
@@ -184,9 +212,13 @@ class TrainPlan(ForwardPlan):
             else:
                 fn(*a)
         rec("combine_bwd", self.combine_bwd, dy)
+        rec("dy_quant_t", self.dy_quant_t, dy)
         rec("dgrad2", self.dgrad2, wts)
         rec("swiglu_bwd", self.swiglu_bwd)
         rec("dgrad1", self.dgrad1, wts)
-        rec("wgrad", self.wgrad, x)
+        rec("unpermute", self.unpermute)
+        rec("x_quant_t", self.x_quant_t, x)
+        rec("wgrad2", self.wgrad2)
+        rec("wgrad13", self.wgrad13)
         rec("gate_bwd", self.gate_bwd)
         return self.dx, self.dW13, self.dW2, self.d_logits

@@ -149,14 +149,18 @@ def replay_record(w: Workload, seq_len=None):
     S = w.seq_len if seq_len is None else seq_len
     rec = np.empty((w.n_layers, w.k, S), dtype=np.int32)
     base = -w.rec_zipf * np.log(np.arange(1, w.E + 1, dtype=np.float64))
-    for l in range(w.n_layers):
-        for b in range((S + ROW_BLOCK - 1) // ROW_BLOCK):
-            r0, r1 = b * ROW_BLOCK, min(S, (b + 1) * ROW_BLOCK)
-            u = rng(w.cfg, TID_REC, l, b).random((r1 - r0, w.E))
-            pert = base[None, :] - np.log(-np.log(np.maximum(u, 1e-300)))
-            part = np.argpartition(-pert, w.k - 1, axis=1)[:, :w.k]
-            o = np.argsort(-np.take_along_axis(pert, part, axis=1), axis=1, kind="stable")
-            rec[l, :, r0:r1] = np.take_along_axis(part, o, axis=1).T
+
+    def blk(lb):
+        l, b = lb
+        r0, r1 = b * ROW_BLOCK, min(S, (b + 1) * ROW_BLOCK)
+        u = rng(w.cfg, TID_REC, l, b).random((r1 - r0, w.E))
+        pert = base[None, :] - np.log(-np.log(np.maximum(u, 1e-300)))
+        part = np.argpartition(-pert, w.k - 1, axis=1)[:, :w.k]
+        o = np.argsort(-np.take_along_axis(pert, part, axis=1), axis=1, kind="stable")
+        rec[l, :, r0:r1] = np.take_along_axis(part, o, axis=1).T
+    jobs = [(l, b) for l in range(w.n_layers) for b in range((S + ROW_BLOCK - 1) // ROW_BLOCK)]
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(blk, jobs))
     return rec
 
 
