@@ -21,7 +21,8 @@ In the FP8 form every GEMM operand is re-quantised along that GEMM's contraction
 axis: 1x128 along features for the dgrad products, 128x1 along tokens for the
 wgrad products.
 
-Rounding points (one reading, listed in the design doc): G, U and h are fp32, h is
+Rounding points (one reading of the pages, which fix no precision): every GEMM
+result is first an fp32 accumulator, so G, U, h and dH are fp32, and h is
 quantised from fp32; Y is bf16; y = bf16 of the sum; dY_r is one fp32 multiply;
 G and U are saved in bf16 and the backward works from those; dGU and the
 recomputed h are fp32 before quantisation; dX, dx, dW13, dW2 are bf16;
@@ -173,7 +174,7 @@ def backward(fw, dy, ids, w, E, wq, exact=False):
     d_gate[t_r, j_r] = B.r32(np.sum(dy[t_r] * fw["Y"][real], axis=1))
 
     # dgrad through W2, then dSwiGLU from the saved (bf16) G, U
-    dH = B.dgrad(B.act(dYp), wq[1], counts, offsets)
+    dH = B.r32(B.dgrad(B.act(dYp), wq[1], counts, offsets))
     Gs, Us = B.r16(fw["G"]), B.r16(fw["U"])
     sg = sigmoid(Gs)
     dG = dH * Us * sg * (1.0 + Gs * (1.0 - sg))
