@@ -126,8 +126,9 @@ int moe_permute_workspace(int64_t T, int32_t k, int32_t L, size_t* bytes);
  * for distinct ids per token.
  * Optional fused row gather (x != NULL): x [T, d] bf16.  For every real row r:
  *   x_perm[r, :] = x[t(r), :]                        (if x_perm != NULL, bf16)
- *   xq[r, :], xq_s[r, :] = 1x128 FP8 quantisation of x[t(r), :]   (if xq != NULL;
- *                          xq [row_cap, d] u8, xq_s [row_cap, d/128] fp32)
+ *   xq[r, :], xq_s[:, r] = 1x128 FP8 quantisation of x[t(r), :]   (if xq != NULL;
+ *                          xq [row_cap, d] u8, xq_s [d/128, row_cap] fp32: scales
+ *                          are stored K-block-major, the layout the GEMM reads)
  * Padding rows of x_perm / xq / xq_s are not written.
  * ws: device workspace of at least moe_permute_workspace() bytes.            */
 int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L,
@@ -161,7 +162,8 @@ int moe_quant_fp8(const void* src, int32_t src_type, int64_t groups, int64_t row
  * pair p = row_pair[r] (w == NULL: v = src[p / k, c]); padding rows are 0.
  * Tiles are the 128-row blocks [128b, 128b+128) for 128b < offsets[L] (every
  * block lies inside one expert because segments are 128-aligned).
- *   src [T, cols] bf16;  qT [cols, row_cap] u8;  sT [cols, row_cap/128] fp32.
+ *   src [T, cols] bf16;  qT [cols, row_cap] u8;  sT [row_cap/128, cols] fp32
+ *   (token-block-major scales, the layout the wgrad GEMM reads).
  * Columns at and past offsets[L] are left unchanged.                          */
 int moe_quant_fp8_rows_t(const uint16_t* src, const float* w, const int32_t* row_pair,
                          const int32_t* offsets, int32_t L, int64_t row_cap, int32_t k,
@@ -172,7 +174,7 @@ int moe_quant_fp8_rows_t(const uint16_t* src, const float* w, const int32_t* row
 enum {
     MOE_EPI_STORE_BF16 = 0,      /* out  = bf16 [row_cap, N]                             */
     MOE_EPI_SWIGLU_Q8 = 1,       /* N = 2f: h = silu(G)*U (G = cols [0,f), U = [f,2f));
-                                    out = hq u8 [row_cap, f], out_s = [row_cap, f/128]   */
+                                    out = hq u8 [row_cap, f], out_s = [f/128, row_cap]   */
     MOE_EPI_SWIGLU_Q8_SAVE = 2,  /* as SWIGLU_Q8, and out2 = bf16 [G, U] [row_cap, 2f]   */
     MOE_EPI_STORE_F32 = 3,       /* out  = fp32 accumulators [row_cap, N] (inspection)  */
     MOE_EPI_SWIGLU_F32 = 4       /* out  = fp32 h [row_cap, f] before quantisation
@@ -182,9 +184,10 @@ enum {
 /* Per-expert GEMM over the expert-grouped rows: for expert e, real rows
  * r in [offsets[e], offsets[e] + counts[e]):
  *     acc[r, n] = sum over 128-blocks c of K:
- *                 a_s[r, c] * b_s[e, n/128, c] * sum_i dec(a[r, 128c+i]) * dec(b[e, n, 128c+i])
+ *                 a_s[c, r] * b_s[e, n/128, c] * sum_i dec(a[r, 128c+i]) * dec(b[e, n, 128c+i])
  * accumulated in fp32, then passed through the epilogue.
- *   a [row_cap, K] e4m3, a_s [row_cap, K/128];  b [L, N, K] e4m3 (weights [out, in];
+ *   a [row_cap, K] e4m3, a_s [K/128, row_cap] (K-block-major: the 128 rows of a
+ *   tile share contiguous scales per K block); b [L, N, K] e4m3 (weights [out, in];
  *   the dgrad products pass the transposed weights from moe_quant_fp8's qT),
  *   b_s [L, N/128, K/128].  K, N multiples of 128.  Padding rows of the outputs
  *   are not written.  Rows past row_cap are never touched.                   */
@@ -197,9 +200,9 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* b, c
 
 /* Weight-gradient grouped GEMM: for every local expert e,
  *     dW[e][m, n] = sum over the 128-row token blocks b of e's padded segment:
- *                   aT_s[m, b] * bT_s[n, b] * sum_{r in b} dec(aT[m, r]) * dec(bT[n, r])
+ *                   aT_s[b, m] * bT_s[b, n] * sum_{r in b} dec(aT[m, r]) * dec(bT[n, r])
  * accumulated in fp32 and stored as bf16.
- *   aT [M, row_cap] e4m3, aT_s [M, row_cap/128]; bT [N, row_cap], bT_s [N, row_cap/128]
+ *   aT [M, row_cap] e4m3, aT_s [row_cap/128, M]; bT [N, row_cap], bT_s [row_cap/128, N]
  *   (from moe_quant_fp8_rows_t or moe_swiglu_backward); dW [L, M, N] bf16.
  *   An expert with no rows gets dW[e] = 0.  M, N multiples of 128.           */
 int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8_t* bT,
@@ -216,9 +219,10 @@ int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8
  * bf16 [G, U] (MOE_EPI_SWIGLU_Q8_SAVE's out2):
  *     dG = dH * U * s * (1 + G * (1 - s)),  dU = dH * G * s,  H = G * s * U
  * Outputs (quantised as in moe_quant_fp8):
- *   dgu_q [row_cap, 2f] u8 + dgu_s [row_cap, 2f/128]   1x128 tiles of [dG, dU]
- *   dgu_qT [2f, row_cap] u8 + dgu_sT [2f, row_cap/128] 128x1 tiles, transposed
- *   h_qT [f, row_cap] u8 + h_sT [f, row_cap/128]       128x1 tiles of H, transposed
+ *   dgu_q [row_cap, 2f] u8 + dgu_s [2f/128, row_cap]   1x128 tiles of [dG, dU]
+ *   dgu_qT [2f, row_cap] u8 + dgu_sT [row_cap/128, 2f] 128x1 tiles, transposed
+ *   h_qT [f, row_cap] u8 + h_sT [row_cap/128, f]       128x1 tiles of H, transposed
+ *   (scales in the layouts the GEMMs read: K-block-major, token-block-major)
  *   dgu_f32 [row_cap, 2f], h_f32 [row_cap, f]          optional (NULL = skip):
  *                                                      the fp32 values quantised
  * Padding rows (row_pair < 0) are 0 in the 128x1 tiles and are not written in
@@ -243,7 +247,7 @@ int moe_unpermute_combine(const uint16_t* y_perm, const int32_t* pair_row, const
 
 /* Combine backward: for every local pair (t, j) held by row r = pair_row[t, j]:
  *     dY[r, :]     = fp32(w[t, j] * dy[t, :])  -> 1x128 e4m3 (if dyq != NULL):
- *                    dyq [row_cap, d] u8, dyq_s [row_cap, d/128] fp32
+ *                    dyq [row_cap, d] u8, dyq_s [d/128, row_cap] fp32 (K-block-major)
  *     d_gate[t, j] = sum_n dy[t, n] * y_perm[r, n]   (fp32; 0 for non-local slots)
  *   dy [T, d] bf16, y_perm [row_cap, d] bf16 (the forward's expert outputs),
  *   pair_row [T, k], w [T, k] fp32, d_gate [T, k] fp32.

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ pair_row,
                                                              const float* __restrict__ w, int k, int d,
                                                              uint8_t* __restrict__ dyq, float* __restrict__ dyq_s,
-                                                             float* __restrict__ d_gate) {
+                                                             float* __restrict__ d_gate, int64_t row_cap) {
     __shared__ float part[CBLOCK / 64][CMAXK];
     const int64_t t = blockIdx.x;
     const int sub = threadIdx.x & 15, grp = threadIdx.x >> 4;  // 8 groups of 16 lanes
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
                 o.y = cvt_e4m3x4((wj * v[4]) * ts.inv, (wj * v[5]) * ts.inv, (wj * v[6]) * ts.inv,
                                  (wj * v[7]) * ts.inv);
                 *reinterpret_cast<uint2*>(dyq + r * d + col) = o;
-                if (sub == 0) dyq_s[r * ntile + tile] = ts.s;
+                if (sub == 0) dyq_s[tile * row_cap + r] = ts.s;  // K-block-major scales
             }
         }
     }
@@ -152,7 +152,7 @@ extern "C" int moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, 
     MOE_REQUIRE(dy && y_perm && pair_row && w && d_gate, MOE_ERR_NULL, "combine_backward: NULL argument");
     MOE_REQUIRE(!dyq == !dyq_s, MOE_ERR_NULL, "combine_backward: dyq and dyq_s go together");
     combine_bwd_kernel<<<dim3((unsigned)T), dim3(CBLOCK), 0, stream>>>(dy, y_perm, pair_row, w, k, d, dyq, dyq_s,
-                                                                       d_gate);
+                                                                       d_gate, row_cap);
     MOE_LAUNCH_CHECK("combine_bwd_kernel");
     return MOE_OK;
 }

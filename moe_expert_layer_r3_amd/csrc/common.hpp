@@ -80,6 +80,14 @@ __device__ __forceinline__ TileScale tile_scale(float amax) {
     return t;
 }
 
+// ---------------------------------------------------------------- SwiGLU
+// sigmoid and silu with the hardware exp2 and reciprocal (about 1 ulp each);
+// exp2 overflows to inf for x below about -88, which gives sigmoid = 0
+__device__ __forceinline__ float sigmoid_fast(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+__device__ __forceinline__ float silu(float x) { return x * sigmoid_fast(x); }
+
 // ---------------------------------------------------------------- wave reductions
 // xor-butterfly max over groups of `width` lanes (width a power of two <= 64)
 template <int WIDTH>

@@ -33,6 +33,10 @@ constexpr int GTHREADS = 512;
 constexpr int GWAVES = GTHREADS / 64;
 constexpr int GMAXL = 1024;
 constexpr int GMAXKB = 256;  // K <= 32768
+#ifndef MOE_GEMM_GROUP_M
+#define MOE_GEMM_GROUP_M 8
+#endif
+constexpr int GROUP_M = MOE_GEMM_GROUP_M;  // m-tiles per L2 super-tile
 
 struct GemmArgs {
     const uint8_t* a;
@@ -75,6 +79,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     constexpr int ASEG = GBM / 8 / GWAVES;  // 1 KB A segments per wave
     constexpr int BSEG = BN / 8 / GWAVES;   // 1 KB B segments per wave
     constexpr int NLD = ASEG + BSEG + 1;    // DMA instructions per wave per stage
+    // Waiting for stage kb allows NLD younger loads (stage kb+1's DMA).  The
+    // previous epilogue's global stores may also be outstanding; loads
+    // complete in order, so a count of NLD still implies stage kb landed.
     static_assert(!is_swiglu(EPI) || BN == 256, "SwiGLU tiles pair 128 G with 128 U columns");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
@@ -141,9 +148,35 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     const uint32_t a_rd1 = (wm * 64 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
     const uint32_t b_rd0 = SM::A_BYTES + (wn * WN + l15) * 128 + ((c0 ^ l7) << 4);
     const uint32_t b_rd1 = SM::A_BYTES + (wn * WN + l15) * 128 + (((c0 + 4) ^ l7) << 4);
-    const uint32_t s_rd = SM::A_BYTES + SM::B_BYTES + (wm * 64 + (lane >> 4) * 4) * 4;
+    // A scales of a stage: 128 floats stored so that the 16 bytes at slot
+    // wm*64 + 4*l15 hold the scales of rows wm*64 + mi*16 + l15, mi = 0..3 (the
+    // rows of this lane's outputs), see the scale DMA below
+    const uint32_t s_rd = SM::A_BYTES + SM::B_BYTES + (wm * 64 + l15 * 4) * 4;
+    // the same offsets per stage, as full LDS addresses: with the stage a
+    // compile-time constant in the (3x unrolled) K loop, every fragment read is
+    // one ds_read with an immediate offset and no address arithmetic
+    uint32_t rA0[3], rA1[3], rB0[3], rB1[3], rS[3];
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+        const uint32_t b = sbase + (uint32_t)(st * SM::STAGE);
+        rA0[st] = b + a_rd0;
+        rA1[st] = b + a_rd1;
+        rB0[st] = b + b_rd0;
+        rB1[st] = b + b_rd1;
+        rS[st] = b + s_rd;
+    }
 
-    for (int t = lb; t < total; t += G) {
+    // ---- per-tile parameters (all wave-uniform)
+    struct Tile {
+        int64_t row0, real_end;        // first row of the tile, end of the expert's real rows
+        int nt, n0;                    // n-tile and its first output column (SwiGLU: first h column is nt*128)
+        const uint8_t* a_base;         // this wave's first A row, K block 0
+        const uint8_t* b_base;         // this wave's first B row, K block 0
+        const float* s_base;           // the tile's A scales
+        const float* bs_lo;            // B scales of this wave's column blocks, K block 0
+        const float* bs_hi;
+    };
+    auto tile_at = [&](int t) {
         int lo = 0, hi = L;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -154,265 +187,337 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         const int tb1 = __builtin_amdgcn_readfirstlane(tile_base[e + 1]);
         const int mt_e = (tb1 - tb0) / NT;
         const int local = t - tb0;
-        const int nt = local / mt_e, mt = local - nt * mt_e;
-        const int64_t row0 = (int64_t)g.offsets[e] + (int64_t)mt * GBM;
-        const int64_t real_end = (int64_t)g.offsets[e] + g.counts[e];
-        const int n0 = nt * BN;  // STORE: first output column; SwiGLU: nt*128 is the first h column
-
-        const uint8_t* Ag = g.a + row0 * K;
-        const float* Asg = g.a_s + row0 * nkb;
-        const uint8_t* Bg = g.b + (int64_t)e * N * K;
-
-        // B scale rows (128-column blocks) of this wave: for SwiGLU the G block
-        // (n-subtiles 0, 1) and the U block (2, 3); for stores one block holds
-        // all of the wave's columns.  They are staged in LDS for the tile so
-        // the K loop reads them together with the operand fragments.
-        const float* bs_base = g.b_s + (int64_t)e * (N / 128) * nkb;
-        int blk0, blk1;
-        if constexpr (is_swiglu(EPI)) {
-            blk0 = nt;              // G columns
-            blk1 = f / 128 + nt;    // U columns
-        } else {
-            blk0 = n0 / 128;        // columns [n0, n0 + 128)
-            blk1 = blk0 + (BN > 128 ? 1 : 0);
-        }
-        for (int i = tid; i < 2 * nkb; i += GTHREADS) {
-            const int kb = i >> 1, which = i & 1;
-            bscale[kb][which] = bs_base[(int64_t)(which ? blk1 : blk0) * nkb + kb];
-        }
-        const uint32_t bs_rd = lds_addr(&bscale[0][0]);
-        // STORE: waves wn = 0, 1 use block blk0, wn = 2, 3 block blk1
-        const bool second_blk = !is_swiglu(EPI) && BN > 128 && wn >= 2;
-
-        // DMA sources.  Segment q (1 KB) holds tile rows 8q .. 8q+7; lane l moves
-        // LDS chunk (l & 7) of row 8q + l/8, i.e. global chunk (l & 7) ^ (row & 7)
-        // (the XOR swizzle is its own inverse; rows 8 apart share it).
-        const int ra = wave * (ASEG * 8) + (lane >> 3);
-        const uint8_t* a_src = Ag + (int64_t)ra * K + (((lane & 7) ^ (ra & 7)) << 4);
-        const int rb = wave * (BSEG * 8) + (lane >> 3);
-        int brow0;
+        // super-tiles of up to GROUP_M m-tiles x all n-tiles, m fastest inside:
+        // the 32 consecutive tiles an XCD runs at a time share few A and B tiles
+        const int grp = local / (GROUP_M * NT);
+        const int gm = min(GROUP_M, mt_e - grp * GROUP_M);
+        const int in = local - grp * GROUP_M * NT;
+        const int nt = in / gm, mt = grp * GROUP_M + (in - (in / gm) * gm);
+        Tile ti;
+        ti.row0 = (int64_t)g.offsets[e] + (int64_t)mt * GBM;
+        ti.real_end = (int64_t)g.offsets[e] + g.counts[e];
+        ti.nt = nt;
+        ti.n0 = nt * BN;
+        ti.a_base = g.a + (ti.row0 + wave * ASEG * 8) * K;
+        int brow_w;  // first B row of this wave's DMA segments
         if constexpr (is_swiglu(EPI)) {
             // LDS B rows in 32-row blocks: block 2w' holds G columns nt*128 +
             // 32w' + [0, 32), block 2w'+1 the U columns of the same h columns;
             // wave w fills block w
-            brow0 = ((wave & 1) ? f : 0) + nt * 128 + (wave >> 1) * 32 + (lane >> 3);
+            brow_w = ((wave & 1) ? f : 0) + nt * 128 + (wave >> 1) * 32;
         } else {
-            brow0 = n0 + rb;
+            brow_w = ti.n0 + wave * BSEG * 8;
         }
-        const uint8_t* b_src = Bg + (int64_t)brow0 * K + (((lane & 7) ^ (rb & 7)) << 4);
-        const float* s_src = Asg + (int64_t)(wave * 16 + (lane & 15)) * nkb;
-        const int64_t K8 = (int64_t)8 * K;
+        ti.b_base = g.b + ((int64_t)e * N + brow_w) * K;
+        ti.s_base = g.a_s + ti.row0;  // K-block-major: block kb's scales at kb * row_cap
+        // B scale rows (128-column blocks): for SwiGLU the G block (n-subtiles
+        // 0, 1) and the U block (2, 3); for stores waves wn = 0, 1 use the first
+        // block of the tile and wn = 2, 3 the second
+        const float* bsx = g.b_s + (int64_t)e * (N / 128) * nkb;
+        int blk0, blk1;
+        if constexpr (is_swiglu(EPI)) {
+            blk0 = nt;
+            blk1 = f / 128 + nt;
+        } else {
+            blk0 = ti.n0 / 128;
+            blk1 = blk0 + (BN > 128 ? 1 : 0);
+        }
+        ti.bs_lo = bsx + (int64_t)blk0 * nkb;
+        ti.bs_hi = bsx + (int64_t)blk1 * nkb;
+        return ti;
+    };
+    // B scales of a tile's two column blocks for every K block, staged in LDS
+    // (read by the K loop together with the operand fragments)
+    auto stage_bscale = [&](const Tile& ti) {
+        for (int i = tid; i < 2 * nkb; i += GTHREADS) {
+            const int kb = i >> 1, which = i & 1;
+            bscale[kb][which] = (which ? ti.bs_hi : ti.bs_lo)[kb];
+        }
+    };
+    const uint32_t bs_rd = lds_addr(&bscale[0][0]);
+    const bool second_blk = !is_swiglu(EPI) && BN > 128 && wn >= 2;
 
-        auto issue = [&](int stage, int kb) {
-            const uint32_t sA = sbase + (uint32_t)(stage * SM::STAGE);
-            const uint32_t sB = sA + SM::A_BYTES;
-            const uint32_t sS = sB + SM::B_BYTES;
-            const int kofs = kb * GBK;
+    // DMA lane offsets.  Segment q (1 KB) holds tile rows 8q .. 8q+7; lane l
+    // moves LDS chunk (l & 7) of row 8q + l/8, i.e. global chunk (l & 7) ^ (row
+    // & 7) (the XOR swizzle is its own inverse; rows 8 apart share it).  Every
+    // source is a wave-uniform base (SGPRs) plus a 32-bit per-lane offset.
+    const int lr = lane >> 3;  // row within a segment; every segment starts at a multiple of 8
+    const uint32_t chunk = (uint32_t)(((lane & 7) ^ lr) << 4);
+    uint32_t a_off[ASEG], b_off[BSEG];
 #pragma unroll
-            for (int i = 0; i < ASEG; ++i) dma16(a_src + i * K8 + kofs, sA + (wave * ASEG + i) * 1024);
+    for (int i = 0; i < ASEG; ++i) a_off[i] = (uint32_t)((8 * i + lr) * K) + chunk;
 #pragma unroll
-            for (int i = 0; i < BSEG; ++i) dma16(b_src + i * K8 + kofs, sB + (wave * BSEG + i) * 1024);
-            if (lane < 16) dma4(s_src + kb, sS + wave * 64);  // 16 rows' A scales per wave
-        };
+    for (int i = 0; i < BSEG; ++i) b_off[i] = (uint32_t)((8 * i + lr) * K) + chunk;
+    // A scales (stored K-block-major, so a block's 128 row scales are 512
+    // contiguous bytes): lane l < 16 of wave w fills scale slot w*16 + l, i.e.
+    // row (w/4)*64 + (l%4)*16 + (w%4)*4 + l/4 (the layout the fragment reads
+    // expect); one wave's 16 rows lie within 256 bytes
+    const uint32_t s_off = (uint32_t)(((wave >> 2) * 64 + (lane & 3) * 16 + (wave & 3) * 4 + ((lane & 15) >> 2)) * 4);
 
+    auto issue = [&](auto stage_c, int kb, const Tile& ti) {
+        constexpr int stage = decltype(stage_c)::value;
+        const uint32_t sA = sbase + (uint32_t)(stage * SM::STAGE);
+        const uint32_t sB = sA + SM::A_BYTES;
+        const uint32_t sS = sB + SM::B_BYTES;
+        const int kofs = kb * GBK;
+#pragma unroll
+        for (int i = 0; i < ASEG; ++i) dma16s(ti.a_base + kofs, a_off[i], sA + (wave * ASEG + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < BSEG; ++i) dma16s(ti.b_base + kofs, b_off[i], sB + (wave * BSEG + i) * 1024);
+        if (lane < 16) dma4s(ti.s_base + (int64_t)kb * g.row_cap, s_off, sS + wave * 64);  // 16 rows' A scales
+    };
+    // barrier for LDS data only (s_waitcnt lgkmcnt(0) + s_barrier): unlike
+    // __syncthreads it does not wait for the next tile's operand DMA in flight
+    auto lds_barrier = [&]() {
+        wait_lgkm0();
+        phase_barrier();
+    };
+
+    const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+    int t = lb;
+    Tile cur;
+    if (t < total) {
+        cur = tile_at(t);
+        stage_bscale(cur);
+        lds_barrier();
+        issue(std::integral_constant<int, 0>{}, 0, cur);
+        if (nkb > 1) issue(std::integral_constant<int, 1>{}, 1, cur);
+    }
+    for (; t < total; t += G) {
         v4f acc[4][NI];
+        v8i af[4], bfr[NI];   // fragments of one K block
+        float sc0[4], sc1[4]; // sA * sB of that block per m-subtile (sc1: the U half of a SwiGLU tile)
+        v4f ring[4];          // raw MFMA partials awaiting their rescale (4 in flight)
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = zero4;
+            ring[mi] = zero4;
+            sc0[mi] = sc1[mi] = 0.f;
+        }
 
-        __syncthreads();  // the previous tile's epilogue is done with smem
-        issue(0, 0);
-        if (nkb > 1) issue(1, 1);
-        for (int kb = 0; kb < nkb; ++kb) {
-            if (kb + 1 < nkb) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();  // stage kb landed for all waves; stage kb-1 no longer read
-            if (kb + 2 < nkb) issue((kb + 2) % 3, kb + 2);
-            const uint32_t base = opaque(sbase + (uint32_t)((kb % 3) * SM::STAGE));
+        // rescale-accumulate of the last n-subtile's partials, left in the ring
+        // by the previous compute
+        auto flush = [&]() {
+            constexpr bool second = is_swiglu(EPI) && (NI - 1) >= NI / 2;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) acc[mi][NI - 1] += ring[mi] * (second ? sc1[mi] : sc0[mi]);
+        };
+        // operand fragments and scales of K block kb from its LDS stage (the
+        // stage was published by the preceding barrier); the pending rescale
+        // of the previous block runs while the reads are in flight
+        auto load = [&](auto stage_c, int kb) {
+            constexpr int st = decltype(stage_c)::value;
+            // opaque: the reads may not be hoisted above the barrier that
+            // published the stage
+            const uint32_t pa0 = opaque(rA0[st]), pa1 = opaque(rA1[st]);
+            const uint32_t pb0 = opaque(rB0[st]), pb1 = opaque(rB1[st]), ps = opaque(rS[st]);
             const uint32_t bsa = opaque(bs_rd + kb * 8);
-
-            u32x4 alo[4], ahi[4], sa4[4], blo[2], bhi[2];
             const v2u sbv = lds8<0>(bsa);
-            blo[0] = lds16<0>(base + b_rd0);
-            bhi[0] = lds16<0>(base + b_rd1);
+            const u32x4 sa4 = lds16<0>(ps);
             static_for<0, 4>([&](auto ic) {
                 constexpr int mi = decltype(ic)::value;
-                alo[mi] = lds16<mi * 2048>(base + a_rd0);
-                ahi[mi] = lds16<mi * 2048>(base + a_rd1);
-                sa4[mi] = lds16<mi * 64>(base + s_rd);
+                af[mi] = join8(lds16<mi * 2048>(pa0), lds16<mi * 2048>(pa1));
             });
-            v8i af[4];
-            v4f sc0[4], sc1[4];
-            v4f pt[2][4];
+            static_for<0, NI>([&](auto nc) {
+                constexpr int ni = decltype(nc)::value;
+                bfr[ni] = join8(lds16<ni * 2048>(pb0), lds16<ni * 2048>(pb1));
+            });
+            flush();
             // element values go through plain integers: __builtin_bit_cast of an
             // ext_vector element lvalue reads element 0 with this compiler
             const uint32_t sbx = sbv.x, sby = sbv.y;
             const float sb0 = __uint_as_float(second_blk ? sby : sbx);
             const float sb1 = __uint_as_float(sby);
-            const v8i bf0 = join8(blo[0], bhi[0]);
+            const uint32_t sav[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
-                af[mi] = join8(alo[mi], ahi[mi]);
-                const v4f sa = __builtin_bit_cast(v4f, sa4[mi]);
+                const float sa = __uint_as_float(sav[mi]);
                 sc0[mi] = sa * sb0;
                 if constexpr (is_swiglu(EPI)) sc1[mi] = sa * sb1;
-                pt[0][mi] = mfma16x16x128(af[mi], bf0);
             }
-            // software pipeline over n-subtiles: the MFMAs of subtile ni run
-            // while the rescale-accumulate of subtile ni-1 retires on the VALU
-            static_for<0, NI + 1>([&](auto nc) {
-                constexpr int ni = decltype(nc)::value;
-                if constexpr (ni < NI) {
-                    if constexpr (ni + 1 < NI) {
-                        blo[(ni + 1) & 1] = lds16<(ni + 1) * 2048>(base + b_rd0);
-                        bhi[(ni + 1) & 1] = lds16<(ni + 1) * 2048>(base + b_rd1);
-                    }
-                    if constexpr (ni > 0) {
-                        const v8i bf = join8(blo[ni & 1], bhi[ni & 1]);
-#pragma unroll
-                        for (int mi = 0; mi < 4; ++mi) pt[ni & 1][mi] = mfma16x16x128(af[mi], bf);
-                    }
-                }
-                if constexpr (ni > 0) {
+            wait_lgkm0();  // this wave's reads of the stage are complete before the next barrier
+        };
+        // the 4*NI MFMAs of the loaded block in (n-subtile, m-subtile) order,
+        // weights as the first operand so that a lane's four outputs are four
+        // consecutive columns of one row; MFMA j reuses the ring slot of MFMA
+        // j-4 right after that partial's rescale, so four MFMAs are in flight
+        // between a result and its use.  The last n-subtile's partials stay
+        // in the ring for the next flush.
+        auto compute = [&]() {
+            static_for<0, 4 * NI>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                constexpr int ni = j / 4, mi = j % 4;
+                if constexpr (j >= 4) {
                     constexpr int pn = ni - 1;
                     constexpr bool second = is_swiglu(EPI) && pn >= NI / 2;
-#pragma unroll
-                    for (int mi = 0; mi < 4; ++mi) acc[mi][pn] += pt[pn & 1][mi] * (second ? sc1[mi] : sc0[mi]);
+                    acc[mi][pn] += ring[mi] * (second ? sc1[mi] : sc0[mi]);
                 }
+                ring[mi] = mfma16x16x128(bfr[ni], af[mi]);
+                // keep this order: the scheduler would otherwise issue every
+                // MFMA first, holding all partials live at once
+                __builtin_amdgcn_sched_barrier(0);
             });
+        };
+
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        // Ping-pong over the two wave groups (waves 0-3 and 4-7, one of each
+        // per SIMD): in every phase one group issues MFMAs while the other
+        // reads its fragments from LDS.  A K block takes two phases; both
+        // groups pass the same barriers in the same order.
+        //   phase A (block kb): every wave has waited for its DMA of stage kb;
+        //     DMA of kb + 2 goes out (into the stage both groups finished with);
+        //     group 0 loads kb, group 1 multiplies kb - 1
+        //   phase B: group 0 multiplies kb, group 1 loads kb
+        // Stages 0 and 1 of the tile were issued before the previous epilogue.
+        auto step0 = [&](auto st_c, int kb) {  // group 0: load kb, then multiply it
+            constexpr int st = decltype(st_c)::value;
+            if (kb + 1 < nkb) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+            phase_barrier();
+            if (kb + 2 < nkb) issue(std::integral_constant<int, (st + 2) % 3>{}, kb + 2, cur);
+            load(st_c, kb);
+            phase_barrier();
+            compute();
+        };
+        auto step1 = [&](auto st_c, int kb) {  // group 1: multiply kb - 1, then load kb
+            constexpr int st = decltype(st_c)::value;
+            if (kb + 1 < nkb) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+            phase_barrier();
+            if (kb + 2 < nkb) issue(std::integral_constant<int, (st + 2) % 3>{}, kb + 2, cur);
+            compute();
+            phase_barrier();
+            load(st_c, kb);
+        };
+        if (wave < 4) {
+            for (int kb = 0; kb < nkb; kb += 3) {
+                step0(S0{}, kb);
+                if (kb + 1 < nkb) step0(S1{}, kb + 1);
+                if (kb + 2 < nkb) step0(S2{}, kb + 2);
+            }
+        } else {
+            // block 0 peeled: nothing to multiply yet (and the fragments are
+            // never read before this group's first load)
+            if (nkb > 1) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+            phase_barrier();
+            if (nkb > 2) issue(S2{}, 2, cur);
+            phase_barrier();
+            load(S0{}, 0);
+            for (int kb = 1; kb < nkb; kb += 3) {
+                step1(S1{}, kb);
+                if (kb + 1 < nkb) step1(S2{}, kb + 1);
+                if (kb + 2 < nkb) step1(S0{}, kb + 2);
+            }
+            compute();
         }
-        __syncthreads();  // every wave is done reading the operand stages
+        flush();
+        // every wave is done reading the stages and this tile's B scales: the
+        // next tile's first two stages and its B scales go out now, so their
+        // latency overlaps this tile's epilogue (which writes from registers
+        // and touches no stage)
+        lds_barrier();
+        const Tile ep = cur;
+        if (t + G < total) {
+            cur = tile_at(t + G);
+            stage_bscale(cur);
+            issue(S0{}, 0, cur);
+            if (nkb > 1) issue(S1{}, 1, cur);
+        }
 
         // ---------------------------------------------------------- epilogues
-        // lane's rows: wm*64 + mi*16 + (lane>>4)*4 + i ; columns within the
-        // tile: wn*WN + ni*16 + (lane & 15)
-        const int rbase = wm * 64 + (lane >> 4) * 4;
-        const int cl = lane & 15;
+        // lane's outputs: row wm*64 + mi*16 + l15 of the tile, columns
+        // wn*WN + ni*16 + 4*lg + v (v = 0..3) within the tile; written straight
+        // from registers (each row's 4 lanes cover 16 contiguous columns)
+        const int lg = lane >> 4;
         if constexpr (EPI == MOE_EPI_STORE_F32) {
             float* out = static_cast<float*>(g.out);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t r = row0 + rbase + mi * 16 + i;
-                    if (r >= real_end) continue;
-#pragma unroll
-                    for (int ni = 0; ni < NI; ++ni) out[r * N + n0 + wn * WN + ni * 16 + cl] = acc[mi][ni][i];
-                }
-        } else if constexpr (EPI == MOE_EPI_STORE_BF16) {
-            constexpr int LDR = BN * 2 + 16;  // staged row stride (bytes)
-            static_assert(GBM * LDR <= SM::TOTAL, "staging fits");
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < 4; ++mi) {
+                const int64_t r = ep.row0 + wm * 64 + mi * 16 + l15;
+                if (r >= ep.real_end) continue;
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = rbase + mi * 16 + i;
-                        const int c = wn * WN + ni * 16 + cl;
-                        *reinterpret_cast<uint16_t*>(smem + r * LDR + c * 2) = (uint16_t)f32_to_bf16(acc[mi][ni][i]);
-                    }
-            __syncthreads();
+                    *reinterpret_cast<v4f*>(out + r * N + ep.n0 + wn * WN + ni * 16 + 4 * lg) = acc[mi][ni];
+            }
+        } else if constexpr (EPI == MOE_EPI_STORE_BF16) {
             uint16_t* out = static_cast<uint16_t*>(g.out);
-            constexpr int CPR = BN / 8;  // 16-byte chunks per row
-            for (int idx = tid; idx < GBM * CPR; idx += GTHREADS) {
-                const int r = idx / CPR, ch = idx - r * CPR;
-                if (row0 + r >= real_end) continue;
-                const uint4 v = *reinterpret_cast<const uint4*>(smem + r * LDR + ch * 16);
-                *reinterpret_cast<uint4*>(out + (row0 + r) * N + n0 + ch * 8) = v;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const int64_t r = ep.row0 + wm * 64 + mi * 16 + l15;
+                if (r >= ep.real_end) continue;
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) {
+                    const v4f a = acc[mi][ni];
+                    *reinterpret_cast<v2u*>(out + r * N + ep.n0 + wn * WN + ni * 16 + 4 * lg) =
+                        v2u{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w)};
+                }
             }
         } else if constexpr (is_swiglu(EPI)) {
-            // n-subtiles 0, 1 are G and 2, 3 the U of the same h columns
-            // hcol = wn*32 + ni*16 + cl within this tile's 128 h columns
-            float h[4][2][4];
+            // n-subtiles 0, 1 are G and 2, 3 the U of the same h columns:
+            // h column wn*32 + ni*16 + 4*lg + v of this tile's 128
+            const int hcol0 = ep.nt * 128;
+            v4f h[4][2];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float gv = acc[mi][ni][i], uv = acc[mi][ni + 2][i];
-                        h[mi][ni][i] = gv / (1.0f + expf(-gv)) * uv;
-                    }
-            const int hcol0 = nt * 128;
+                    for (int v = 0; v < 4; ++v) h[mi][ni][v] = silu(acc[mi][ni][v]) * acc[mi][ni + 2][v];
             if constexpr (EPI == MOE_EPI_SWIGLU_F32) {
                 float* out = static_cast<float*>(g.out);
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
+                for (int mi = 0; mi < 4; ++mi) {
+                    const int64_t r = ep.row0 + wm * 64 + mi * 16 + l15;
+                    if (r >= ep.real_end) continue;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t r = row0 + rbase + mi * 16 + i;
-                        if (r >= real_end) continue;
-#pragma unroll
-                        for (int ni = 0; ni < 2; ++ni) out[r * f + hcol0 + wn * 32 + ni * 16 + cl] = h[mi][ni][i];
-                    }
+                    for (int ni = 0; ni < 2; ++ni)
+                        *reinterpret_cast<v4f*>(out + r * f + hcol0 + wn * 32 + ni * 16 + 4 * lg) = h[mi][ni];
+                }
             } else {
-                // per-row amax over this wave's 32 h columns, then across the 4 N waves
+                // row amax over this wave's 32 h columns (8 in-lane, then the 4
+                // lane groups of the row), then across the 4 N waves via LDS
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
+                for (int mi = 0; mi < 4; ++mi) {
+                    float m = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float m = fmaxf(fabsf(h[mi][0][i]), fabsf(h[mi][1][i]));
-                        m = group_max<16>(m);
-                        if (cl == 0) rowmax[wn][rbase + mi * 16 + i] = m;
-                    }
-                __syncthreads();
-                constexpr int LDQ = 128 + 16;  // byte tile row stride
-                uint8_t* qt = smem;
+                    for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = rbase + mi * 16 + i;
-                        const float am = fmaxf(fmaxf(rowmax[0][r], rowmax[1][r]), fmaxf(rowmax[2][r], rowmax[3][r]));
-                        const TileScale ts = tile_scale(am);
-                        if (cl == 0 && wn == 0 && row0 + r < real_end) g.out_s[(row0 + r) * (f / 128) + nt] = ts.s;
-                        const int w2 = cvt_e4m3x2(h[mi][0][i] * ts.inv, h[mi][1][i] * ts.inv);
-                        qt[r * LDQ + wn * 32 + cl] = (uint8_t)(w2 & 0xFF);
-                        qt[r * LDQ + wn * 32 + 16 + cl] = (uint8_t)((w2 >> 8) & 0xFF);
-                    }
-                if constexpr (EPI == MOE_EPI_SWIGLU_Q8_SAVE) {
-                    // G and U as bf16, staged after the byte tile
-                    constexpr int LDG = 256 * 2 + 16;
-                    uint8_t* gt = smem + GBM * LDQ;
-                    static_assert(GBM * LDQ + GBM * LDG <= SM::TOTAL, "staging fits");
-#pragma unroll
-                    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int r = rbase + mi * 16 + i;
-                                const int c = wn * 32 + ni * 16 + cl;
-                                *reinterpret_cast<uint16_t*>(gt + r * LDG + c * 2) =
-                                    (uint16_t)f32_to_bf16(acc[mi][ni][i]);
-                                *reinterpret_cast<uint16_t*>(gt + r * LDG + 256 + c * 2) =
-                                    (uint16_t)f32_to_bf16(acc[mi][ni + 2][i]);
-                            }
+                        for (int v = 0; v < 4; ++v) m = fmaxf(m, fabsf(h[mi][ni][v]));
+                    m = fmaxf(m, __shfl_xor(m, 16));
+                    m = fmaxf(m, __shfl_xor(m, 32));
+                    if (lg == 0) rowmax[wn][wm * 64 + mi * 16 + l15] = m;
                 }
-                __syncthreads();
+                lds_barrier();
                 uint8_t* out = static_cast<uint8_t*>(g.out);
-                for (int idx = tid; idx < GBM * 8; idx += GTHREADS) {
-                    const int r = idx >> 3, ch = idx & 7;
-                    if (row0 + r >= real_end) continue;
-                    const uint4 v = *reinterpret_cast<const uint4*>(qt + r * LDQ + ch * 16);
-                    *reinterpret_cast<uint4*>(out + (row0 + r) * f + hcol0 + ch * 16) = v;
-                }
-                if constexpr (EPI == MOE_EPI_SWIGLU_Q8_SAVE) {
-                    constexpr int LDG = 256 * 2 + 16;
-                    const uint8_t* gt = smem + GBM * LDQ;
-                    uint16_t* out2 = static_cast<uint16_t*>(g.out2);
-                    for (int idx = tid; idx < GBM * 32; idx += GTHREADS) {
-                        const int r = idx >> 5, ch = idx & 31;  // 16 chunks of G then 16 of U
-                        if (row0 + r >= real_end) continue;
-                        const uint4 v = *reinterpret_cast<const uint4*>(gt + r * LDG + ch * 16);
-                        const int col = (ch < 16 ? 0 : f) + hcol0 + (ch & 15) * 8;
-                        *reinterpret_cast<uint4*>(out2 + (row0 + r) * N + col) = v;
+                uint16_t* out2 = static_cast<uint16_t*>(g.out2);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    const int rt = wm * 64 + mi * 16 + l15;
+                    const int64_t r = ep.row0 + rt;
+                    const float am = fmaxf(fmaxf(rowmax[0][rt], rowmax[1][rt]), fmaxf(rowmax[2][rt], rowmax[3][rt]));
+                    if (r >= ep.real_end) continue;
+                    const TileScale ts = tile_scale(am);
+                    if (lg == 0 && wn == 0) g.out_s[(int64_t)ep.nt * g.row_cap + r] = ts.s;
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        const int hc = hcol0 + wn * 32 + ni * 16 + 4 * lg;
+                        const v4f hv = h[mi][ni];
+                        *reinterpret_cast<uint32_t*>(out + r * f + hc) =
+                            cvt_e4m3x4(hv.x * ts.inv, hv.y * ts.inv, hv.z * ts.inv, hv.w * ts.inv);
+                        if constexpr (EPI == MOE_EPI_SWIGLU_Q8_SAVE) {
+                            // G and U as bf16 for the backward
+                            const v4f gv = acc[mi][ni], uv = acc[mi][ni + 2];
+                            *reinterpret_cast<v2u*>(out2 + r * N + hc) = v2u{pack_bf16x2(gv.x, gv.y), pack_bf16x2(gv.z, gv.w)};
+                            *reinterpret_cast<v2u*>(out2 + r * N + f + hc) = v2u{pack_bf16x2(uv.x, uv.y), pack_bf16x2(uv.z, uv.w)};
+                        }
                     }
                 }
             }
         }
-        // the next tile's first __syncthreads protects smem reuse
+        // the next tile's B scales (and this tile's row maxima) are settled
+        // before any wave reads them
+        lds_barrier();
     }
 }
 

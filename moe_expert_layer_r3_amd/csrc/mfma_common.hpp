@@ -27,12 +27,27 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
     asm volatile("global_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds) : "memory");
 }
 
+// The same transfers with a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset: the base advances by scalar adds along K, so no
+// per-lane 64-bit address arithmetic is needed in the loop.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("global_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
 // s_waitcnt immediate waiting for vmcnt <= N only (gfx9 encoding: vmcnt[3:0],
 // expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt immediate waiting for lgkmcnt == 0 only (LDS reads of this wave)
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
 typedef const __attribute__((address_space(3))) u32x4* lds_u32x4_ptr;
@@ -52,6 +67,15 @@ __device__ __forceinline__ v2u lds8(uint32_t addr) {
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm volatile("" : "+v"(v));
     return v;
+}
+
+// Workgroup barrier that the instruction scheduler may not move any
+// instruction across: phases separated by it (MFMA work on one side, LDS reads
+// on the other) stay where the source puts them.
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ v8i join8(u32x4 lo, u32x4 hi) {

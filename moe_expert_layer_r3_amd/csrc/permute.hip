@@ -155,7 +155,8 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
 __global__ __launch_bounds__(256) void gather_quant_kernel(const uint16_t* __restrict__ x, int64_t T, int d, int k,
                                                            const int32_t* __restrict__ pair_row,
                                                            uint16_t* __restrict__ x_perm,
-                                                           uint8_t* __restrict__ xq, float* __restrict__ xq_s) {
+                                                           uint8_t* __restrict__ xq, float* __restrict__ xq_s,
+                                                           int64_t row_cap) {
     const int ntile = d >> 7;
     const int64_t item = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
     const int sub = threadIdx.x & 15;
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(256) void gather_quant_kernel(const uint16_t* __res
         if (x_perm) *reinterpret_cast<uint4*>(x_perm + r * d + col) = raw;
         if (xq) {
             *reinterpret_cast<uint2*>(xq + r * d + col) = packed;
-            if (sub == 0) xq_s[r * ntile + tile] = s;
+            if (sub == 0) xq_s[tile * row_cap + r] = s;  // K-block-major scales
         }
     }
 }
@@ -253,7 +254,7 @@ extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0,
         const int64_t items = T * (d / 128);
         const int64_t threads = items * 16;
         gather_quant_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
-            x, T, d, k, pair_row, x_perm, xq, xq_s);
+            x, T, d, k, pair_row, x_perm, xq, xq_s, row_cap);
         MOE_LAUNCH_CHECK("gather_quant_kernel");
     }
     return MOE_OK;

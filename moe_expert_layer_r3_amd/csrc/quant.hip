@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void quant_rows_t_kernel(const uint16_t* __res
         for (int rr = 0; rr < 16; ++rr) m = fmaxf(m, cmax[rr][c8 + i]);
         TileScale ts = tile_scale(m);
         inv[i] = ts.inv;
-        if (r0 == 0) sT[(cc * 128 + c8 + i) * (row_cap >> 7) + b] = ts.s;
+        if (r0 == 0) sT[b * cols + cc * 128 + c8 + i] = ts.s;  // token-block-major scales
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {

@@ -5,7 +5,7 @@
 //
 // For a row r of the expert-grouped layout and a column c < f, from the GEMM
 // result dH (fp32) and the saved bf16 pre-activations G = GU[:, :f], U = GU[:, f:]:
-//     s  = 1 / (1 + exp(-G))
+//     s  = 1 / (1 + exp(-G))      (hardware exp2 and reciprocal, about 1 ulp)
 //     dG = dH * U * s * (1 + G * (1 - s))      (derivative of silu(G) * U in G)
 //     dU = dH * G * s                          (silu(G) = G * s)
 //     H  = G * s * U                           (the activation, recomputed)
@@ -52,7 +52,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
     const int f = a.f;
     const int64_t F2 = 2 * (int64_t)f;
     const int64_t col = cb * 128 + c8;  // column of f
-    const int64_t nblk = a.row_cap >> 7;
 
     float dg[8][8], du[8][8], hh[8][8];
     bool real[8];
@@ -76,7 +75,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
             for (int i = 0; i < 8; ++i) {
                 const float g = (i & 1) ? bf16_hi(gw[i >> 1]) : bf16_lo(gw[i >> 1]);
                 const float u = (i & 1) ? bf16_hi(uw[i >> 1]) : bf16_lo(uw[i >> 1]);
-                const float s = 1.0f / (1.0f + expf(-g));
+                const float s = sigmoid_fast(g);
                 const float gs = g * s;
                 dg[j][i] = dh[i] * u * s * (1.0f + g * (1.0f - s));
                 du[j][i] = dh[i] * gs;
@@ -116,8 +115,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
         *reinterpret_cast<uint2*>(a.dgu_q + r * F2 + col) = qg;
         *reinterpret_cast<uint2*>(a.dgu_q + r * F2 + f + col) = qu;
         if ((tid & 15) == 0) {
-            a.dgu_s[r * (F2 >> 7) + cb] = tg.s;
-            a.dgu_s[r * (F2 >> 7) + (f >> 7) + cb] = tu.s;
+            a.dgu_s[cb * a.row_cap + r] = tg.s;  // K-block-major scales
+            a.dgu_s[((f >> 7) + cb) * a.row_cap + r] = tu.s;
         }
         if (a.dgu_f32) {
             float4* pg = reinterpret_cast<float4*>(a.dgu_f32 + r * F2 + col);
@@ -151,10 +150,11 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
             const TileScale ts = tile_scale(m);
             inv[q][i] = ts.inv;
             if (r0 == 0) {
-                // transposed scale rows: dG at c, dU at f + c, H at c
+                // scales of the transposed tiles, token-block-major: dG at
+                // column c, dU at f + c (of 2f), H at c (of f)
                 float* sT = q == 2 ? a.h_sT : a.dgu_sT;
                 const int64_t c = (q == 1 ? f : 0) + col + i;
-                sT[c * nblk + b] = ts.s;
+                sT[b * (q == 2 ? (int64_t)f : F2) + c] = ts.s;
             }
         }
 #pragma unroll

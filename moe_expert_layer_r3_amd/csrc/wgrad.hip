@@ -62,7 +62,6 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int64_t rcap = g.row_cap;
-    const int64_t nblk_all = rcap / WBK;  // scale columns per row
     const int MT = g.M / WBM, NT = g.N / BN;
     const int total = g.L * MT * NT;
     const int G = gridDim.x;
@@ -94,8 +93,10 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         const int rb = wave * (BSEG * 8) + (lane >> 3);
         const uint8_t* b_src =
             g.bT + ((int64_t)nt * BN + rb) * rcap + lo + (((lane & 7) ^ (rb & 7)) << 4);
-        const float* sa_src = g.aT_s + ((int64_t)mt * WBM + wave * 16 + (lane & 15)) * nblk_all + kb0;
-        const float* sb_src = g.bT_s + ((int64_t)nt * BN + wave * BROWS + (lane & (BROWS - 1))) * nblk_all + kb0;
+        // scales are token-block-major ([row_cap/128, M] and [row_cap/128, N]):
+        // the rows of one token block are contiguous
+        const float* sa_src = g.aT_s + kb0 * g.M + (int64_t)mt * WBM + wave * 16 + (lane & 15);
+        const float* sb_src = g.bT_s + kb0 * g.N + (int64_t)nt * BN + wave * BROWS + (lane & (BROWS - 1));
         const int64_t R8 = 8 * rcap;
 
         auto issue = [&](int stage, int kb) {
@@ -108,8 +109,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
             for (int i = 0; i < ASEG; ++i) dma16(a_src + i * R8 + kofs, sA + (wave * ASEG + i) * 1024);
 #pragma unroll
             for (int i = 0; i < BSEG; ++i) dma16(b_src + i * R8 + kofs, sB + (wave * BSEG + i) * 1024);
-            if (lane < 16) dma4(sa_src + kb, sSA + wave * 64);   // 16 A rows per wave
-            if (lane < BROWS) dma4(sb_src + kb, sSB + wave * BROWS * 4);
+            if (lane < 16) dma4(sa_src + (int64_t)kb * g.M, sSA + wave * 64);  // 16 A rows per wave
+            if (lane < BROWS) dma4(sb_src + (int64_t)kb * g.N, sSB + wave * BROWS * 4);
         };
 
         v4f acc[4][NI];

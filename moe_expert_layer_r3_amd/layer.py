@@ -59,9 +59,9 @@ class ForwardPlan:
         self.ws = torch.empty(ops.permute_workspace(T, k, L), dtype=u8, device=dv)
         self.status = torch.zeros(1, dtype=i32, device=dv)
         self.xq = torch.empty((R, d), dtype=u8, device=dv)
-        self.xq_s = torch.empty((R, d // 128), dtype=f32, device=dv)
+        self.xq_s = torch.empty((d // 128, R), dtype=f32, device=dv)  # activation scales: K-block-major
         self.hq = torch.empty((R, f), dtype=u8, device=dv)
-        self.hq_s = torch.empty((R, f // 128), dtype=f32, device=dv)
+        self.hq_s = torch.empty((f // 128, R), dtype=f32, device=dv)
         self.gu = torch.empty((R, 2 * f), dtype=b16, device=dv) if save_gu else None
         self.Y = torch.empty((R, d), dtype=b16, device=dv)
         self.y = torch.empty((T, d), dtype=b16, device=dv)
@@ -135,21 +135,21 @@ class TrainPlan(ForwardPlan):
         f32, u8, b16 = torch.float32, torch.uint8, torch.bfloat16
         R = self.rcap
         self.dyq = torch.empty((R, d), dtype=u8, device=dv)
-        self.dyq_s = torch.empty((R, d // 128), dtype=f32, device=dv)
+        self.dyq_s = torch.empty((d // 128, R), dtype=f32, device=dv)
         self.d_gate = torch.empty((T, k), dtype=f32, device=dv)
         self.dyqT = torch.empty((d, R), dtype=u8, device=dv)
-        self.dyqT_s = torch.empty((d, R // 128), dtype=f32, device=dv)
+        self.dyqT_s = torch.empty((R // 128, d), dtype=f32, device=dv)  # token-block-major
         self.dH = torch.empty((R, f), dtype=f32, device=dv)
         self.sb = dict(dgu_q=torch.empty((R, 2 * f), dtype=u8, device=dv),
-                       dgu_s=torch.empty((R, 2 * f // 128), dtype=f32, device=dv),
+                       dgu_s=torch.empty((2 * f // 128, R), dtype=f32, device=dv),
                        dgu_qT=torch.empty((2 * f, R), dtype=u8, device=dv),
-                       dgu_sT=torch.empty((2 * f, R // 128), dtype=f32, device=dv),
+                       dgu_sT=torch.empty((R // 128, 2 * f), dtype=f32, device=dv),
                        h_qT=torch.empty((f, R), dtype=u8, device=dv),
-                       h_sT=torch.empty((f, R // 128), dtype=f32, device=dv))
+                       h_sT=torch.empty((R // 128, f), dtype=f32, device=dv))
         self.dX = torch.empty((R, d), dtype=b16, device=dv)
         self.dx = torch.empty((T, d), dtype=b16, device=dv)
         self.xqT = torch.empty((d, R), dtype=u8, device=dv)
-        self.xqT_s = torch.empty((d, R // 128), dtype=f32, device=dv)
+        self.xqT_s = torch.empty((R // 128, d), dtype=f32, device=dv)
         self.dW2 = torch.empty((L, d, f), dtype=b16, device=dv)
         self.dW13 = torch.empty((L, 2 * f, d), dtype=b16, device=dv)
         self.d_logits = torch.empty((T, E), dtype=f32, device=dv)

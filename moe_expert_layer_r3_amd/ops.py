@@ -189,7 +189,7 @@ def permute(ids, e0, L, rcap=None, x=None, x_perm=False, quant=True, status=None
             xp = torch.empty((rcap, d), dtype=torch.bfloat16, device=dev)
         if quant:
             xq = torch.empty((rcap, d), dtype=torch.uint8, device=dev)
-            xs = torch.empty((rcap, d // 128), dtype=torch.float32, device=dev)
+            xs = torch.empty((d // 128, rcap), dtype=torch.float32, device=dev)  # K-block-major
     _call("moe_permute", _p(ids), T, k, e0, L, rcap, _p(counts), _p(offsets), _p(row_pair), _p(pair_row),
           _p(x), d, _p(xp), _p(xq), _p(xs), _p(ws), ws.numel(), _p(status), _stream(dev))
     out.update(x_perm=xp, xq=xq, xq_s=xs)
@@ -236,7 +236,7 @@ def quant_rows_t(src, w, row_pair, offsets, L, rcap, k):
     cols = src.shape[1]
     dev = _dev(src)
     qT = torch.empty((cols, rcap), dtype=torch.uint8, device=dev)
-    sT = torch.empty((cols, rcap // 128), dtype=torch.float32, device=dev)
+    sT = torch.empty((rcap // 128, cols), dtype=torch.float32, device=dev)  # token-block-major
     _call("moe_quant_fp8_rows_t", _p(src), _p(w), _p(row_pair), _p(offsets), L, rcap, k, cols, _p(qT), _p(sT),
           _stream(dev))
     return qT, sT
@@ -264,7 +264,7 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
         res = out
     elif epilogue in (EPI_SWIGLU_Q8, EPI_SWIGLU_Q8_SAVE):
         out = torch.empty((rcap, f), dtype=torch.uint8, device=dev)
-        out_s = torch.empty((rcap, f // 128), dtype=torch.float32, device=dev)
+        out_s = torch.empty((f // 128, rcap), dtype=torch.float32, device=dev)  # K-block-major
         res = (out, out_s)
         if epilogue == EPI_SWIGLU_Q8_SAVE:
             out2 = torch.empty((rcap, N), dtype=torch.bfloat16, device=dev)
@@ -300,9 +300,9 @@ def swiglu_backward(dH, gu, row_pair, offsets, L, rcap, inspect=False, out=None)
     f = dH.shape[1]
     dev = _dev(dH)
     o = {} if out is None else dict(out)
-    shapes = dict(dgu_q=((rcap, 2 * f), torch.uint8), dgu_s=((rcap, 2 * f // 128), torch.float32),
-                  dgu_qT=((2 * f, rcap), torch.uint8), dgu_sT=((2 * f, rcap // 128), torch.float32),
-                  h_qT=((f, rcap), torch.uint8), h_sT=((f, rcap // 128), torch.float32))
+    shapes = dict(dgu_q=((rcap, 2 * f), torch.uint8), dgu_s=((2 * f // 128, rcap), torch.float32),
+                  dgu_qT=((2 * f, rcap), torch.uint8), dgu_sT=((rcap // 128, 2 * f), torch.float32),
+                  h_qT=((f, rcap), torch.uint8), h_sT=((rcap // 128, f), torch.float32))
     if inspect:
         shapes.update(dgu=((rcap, 2 * f), torch.float32), h=((rcap, f), torch.float32))
     for name, (shape, dt) in shapes.items():
@@ -333,7 +333,7 @@ def combine_backward(dy, y_perm, pair_row, w, rcap=None, quant=True):
     rcap = y_perm.shape[0] if rcap is None else rcap
     dev = _dev(dy)
     dyq = torch.empty((rcap, d), dtype=torch.uint8, device=dev) if quant else None
-    dys = torch.empty((rcap, d // 128), dtype=torch.float32, device=dev) if quant else None
+    dys = torch.empty((d // 128, rcap), dtype=torch.float32, device=dev) if quant else None
     d_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
     _call("moe_combine_backward", _p(dy), _p(y_perm), _p(pair_row), _p(w), T, k, d, rcap, _p(dyq), _p(dys),
           _p(d_gate), _stream(dev))

@@ -62,7 +62,7 @@ def test_quant_rows_t(weighted):
     v[real] = src[p // k] if w is None else of32(w.reshape(-1)[p][:, None].astype(np.float64) * src[p // k])
     rq, rs = OQ.quant_128x1_t(v, real)
     assert np.array_equal(npi(qT)[:, :n], rq)
-    assert np.array_equal(npi(sT)[:, :n // 128].astype(np.float64), rs)
+    assert np.array_equal(npi(sT)[:n // 128].T.astype(np.float64), rs)
 
 
 # ------------------------------------------------------------------ combine backward
@@ -86,7 +86,7 @@ def test_combine_backward():
     t, j = rp[real] // k, rp[real] % k
     rq, rs = OQ.quant_1x128(of32(w[t, j][:, None] * dy[t]))
     assert np.array_equal(npi(dyq)[rows], rq)
-    assert np.array_equal(npi(dys)[rows].astype(np.float64), rs)
+    assert np.array_equal(npi(dys).T[rows].astype(np.float64), rs)
     g = np64(d_gate)
     loc = pr >= 0
     ref = np.zeros((T, k))
@@ -139,17 +139,17 @@ def test_swiglu_backward(counts, f):
     h[~real] = 0.0
     q1, s1 = OQ.quant_1x128(dgu[rows])
     assert np.array_equal(npi(o["dgu_q"])[rows], q1)
-    assert np.array_equal(npi(o["dgu_s"])[rows].astype(np.float64), s1)
+    assert np.array_equal(npi(o["dgu_s"]).T[rows].astype(np.float64), s1)
     qt, st = OQ.quant_128x1_t(dgu, real)
     assert np.array_equal(npi(o["dgu_qT"])[:, :n], qt)
-    assert np.array_equal(npi(o["dgu_sT"])[:, :n // 128].astype(np.float64), st)
+    assert np.array_equal(npi(o["dgu_sT"])[:n // 128].T.astype(np.float64), st)
     qh, sh = OQ.quant_128x1_t(h, real)
     assert np.array_equal(npi(o["h_qT"])[:, :n], qh)
-    assert np.array_equal(npi(o["h_sT"])[:, :n // 128].astype(np.float64), sh)
+    assert np.array_equal(npi(o["h_sT"])[:n // 128].T.astype(np.float64), sh)
     # the production call (no inspection outputs) writes the same bytes
     o2 = ops.swiglu_backward(gpu(dH), bf16_tensor(GU), res["row_pair"], res["offsets"], len(counts), rcap)
-    for key in ("dgu_q", "dgu_s"):
-        assert np.array_equal(npi(o2[key])[rows], npi(o[key])[rows])
+    assert np.array_equal(npi(o2["dgu_q"])[rows], npi(o["dgu_q"])[rows])
+    assert np.array_equal(npi(o2["dgu_s"]).T[rows], npi(o["dgu_s"]).T[rows])
     for key in ("dgu_qT", "h_qT"):
         assert np.array_equal(npi(o2[key])[:, :n], npi(o[key])[:, :n])
 
@@ -170,7 +170,8 @@ def test_gemm_dgrad(counts, K, N):
     W[0, :128] *= 30.0
     wq, ws, wqT, wsT = ops.quant_fp8(bf16_tensor(W), tile=ops.TILE_128x128, transpose=True)
     say(f"gemm dgrad counts={counts} K={K} N={N}")
-    acc = ops.grouped_gemm(aq, as_, wqT, wsT, res["counts"], res["offsets"], ops.EPI_STORE_F32)
+    # the GEMM reads activation scales K-block-major
+    acc = ops.grouped_gemm(aq, as_.t().contiguous(), wqT, wsT, res["counts"], res["offsets"], ops.EPI_STORE_F32)
     c, o = npi(res["counts"]), npi(res["offsets"])
     ref = OG.grouped_dgrad(npi(aq), npi(as_), c, o, npi(wq), npi(ws))
     rows = np.concatenate([np.arange(o[e], o[e] + c[e]) for e in range(L)]).astype(np.int64)
@@ -210,12 +211,13 @@ def test_wgrad(counts, M, N):
     B = rng.standard_normal((n, N))
     qa, sa = OQ.quant_128x1_t(A, real)
     qb, sb = OQ.quant_128x1_t(B, real)
-    # rows past offsets[L] hold NaN codes and scales: the kernel must not read them
+    # rows past offsets[L] hold NaN codes and scales: the kernel must not read
+    # them; scales go in token-block-major, the layout the kernel reads
     def upload(q, s):
         qf = np.full((q.shape[0], rcap), 0x7F, dtype=np.uint8)
-        sf = np.full((q.shape[0], rcap // 128), np.nan, dtype=np.float32)
+        sf = np.full((rcap // 128, q.shape[0]), np.nan, dtype=np.float32)
         qf[:, :n] = q
-        sf[:, :n // 128] = s
+        sf[:n // 128] = s.T
         return gpu(qf), gpu(sf)
     aT, aT_s = upload(qa, sa)
     bT, bT_s = upload(qb, sb)
@@ -315,7 +317,7 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
         t, j = rp[rows] // k, rp[rows] % k
         dys = _rows(dy, t)
         # combine backward: dY = fp32(w * dy), 1x128
-        dyq, dyq_s = _rows(plan.dyq, rows), _rows(plan.dyq_s, rows)
+        dyq, dyq_s = _rows(plan.dyq, rows), _rows(plan.dyq_s.t(), rows)
         rq, rs = OQ.quant_1x128(of32(w[t, j][:, None] * dys))
         assert np.array_equal(dyq, rq) and np.array_equal(dyq_s, rs)
         # dgrad through W2 (transposed copy [f, d]), fp32 accumulators
@@ -327,7 +329,7 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
         ref_dgu, ref_h = _swiglu_ref(dH, gu[:, :f], gu[:, f:])
         dgu32 = _rows(ins["dgu"], rows)
         assert _tile_close(dgu32, ref_dgu) and _tile_close(_rows(ins["h"], rows), ref_h)
-        dgu_q, dgu_s = _rows(plan.sb["dgu_q"], rows), _rows(plan.sb["dgu_s"], rows)
+        dgu_q, dgu_s = _rows(plan.sb["dgu_q"], rows), _rows(plan.sb["dgu_s"].t(), rows)
         q1, s1 = OQ.quant_1x128(dgu32)
         assert np.array_equal(dgu_q, q1) and np.array_equal(dgu_s, s1)
         # dgrad through W13 (transposed copy [d, 2f]), bf16
@@ -355,29 +357,29 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
     Xp[rr] = _sub(x, rp[rr] // k, md)
     qx, sx = OQ.quant_128x1_t(Xp, real)
     assert np.array_equal(_cols(plan.xqT, md, 0, n), qx)
-    assert np.array_equal(_cols(plan.xqT_s, md, 0, n // 128), sx)
+    assert np.array_equal(_cols(plan.xqT_s.t(), md, 0, n // 128), sx)
     dYp = np.zeros((n, len(md)))
     dYp[rr] = of32(w[rp[rr] // k, rp[rr] % k][:, None] * _sub(dy, rp[rr] // k, md))
     qy, sy = OQ.quant_128x1_t(dYp, real)
     assert np.array_equal(_cols(plan.dyqT, md, 0, n), qy)
-    assert np.array_equal(_cols(plan.dyqT_s, md, 0, n // 128), sy)
+    assert np.array_equal(_cols(plan.dyqT_s.t(), md, 0, n // 128), sy)
     h32 = np.zeros((n, len(mf)))
     h32[rr] = _sub(ins["h"], rr, mf)
     qh, sh = OQ.quant_128x1_t(h32, real)
     assert np.array_equal(_cols(plan.sb["h_qT"], mf, 0, n), qh)
-    assert np.array_equal(_cols(plan.sb["h_sT"], mf, 0, n // 128), sh)
+    assert np.array_equal(_cols(plan.sb["h_sT"].t(), mf, 0, n // 128), sh)
     g32 = np.zeros((n, len(m2f)))
     g32[rr] = _sub(ins["dgu"], rr, m2f)
     qg, sg = OQ.quant_128x1_t(g32, real)
     assert np.array_equal(_cols(plan.sb["dgu_qT"], m2f, 0, n), qg)
-    assert np.array_equal(_cols(plan.sb["dgu_sT"], m2f, 0, n // 128), sg)
+    assert np.array_equal(_cols(plan.sb["dgu_sT"].t(), m2f, 0, n // 128), sg)
     # wgrad products, per expert, over the expert's padded segment
     for e in experts:
         lo, hi = int(o[e]), int(o[e + 1])
         seg_c, seg_o = np.array([c[e]]), np.array([0, hi - lo])
         b0, b1 = lo // 128, hi // 128
-        def op(qt, st, feats):
-            return _cols(qt, feats, lo, hi), _cols(st, feats, b0, b1)
+        def op(qt, st, feats):  # st token-block-major
+            return _cols(qt, feats, lo, hi), _cols(st.t(), feats, b0, b1)
         a2, as2 = op(plan.dyqT, plan.dyqT_s, md)
         b2, bs2 = op(plan.sb["h_qT"], plan.sb["h_sT"], np.arange(f))
         ref2 = OG.grouped_wgrad(a2, as2, b2, bs2, seg_c, seg_o)

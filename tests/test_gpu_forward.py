@@ -166,7 +166,7 @@ def _check_permute(ids, e0, L, x=None):
         real = rp >= 0
         xq, xs = OQ.quant_1x128(x)
         assert np.array_equal(npi(res["xq"])[:n][real], xq[rp[real] // k])
-        assert np.array_equal(npi(res["xq_s"])[:n][real].astype(np.float64), xs[rp[real] // k])
+        assert np.array_equal(npi(res["xq_s"]).T[:n][real].astype(np.float64), xs[rp[real] // k])
         assert np.array_equal(np64(res["x_perm"])[:n][real], x[rp[real] // k])
     return res
 
@@ -233,7 +233,7 @@ def test_gemm_store(counts, K, N):
     acc = ops.grouped_gemm(res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"], ops.EPI_STORE_F32)
     y = ops.grouped_gemm(res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"], ops.EPI_STORE_BF16)
     c, o = npi(res["counts"]), npi(res["offsets"])
-    ref = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]), c, o, npi(wq), npi(ws))
+    ref = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, npi(wq), npi(ws))
     rows = _real_rows(res)
     assert rel_fro(np64(acc)[rows], ref[rows]) <= ACC_TOL
     assert rel_fro(np64(y)[rows], obf16(ref[rows])) <= TOL
@@ -248,7 +248,7 @@ def test_gemm_swiglu(counts, K, f):
     hq, hs = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8)
     hq2, hs2, gu = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8_SAVE)
     c, o = npi(res["counts"]), npi(res["offsets"])
-    GU = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]), c, o, npi(wq), npi(ws))
+    GU = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, npi(wq), npi(ws))
     G, U = of32(GU[:, :f]), of32(GU[:, f:])
     h_ref = OL.silu(G) * U
     rows = _real_rows(res)
@@ -256,8 +256,8 @@ def test_gemm_swiglu(counts, K, f):
     # the fused quantiser, bit-exact on the GPU's own fp32 h
     qref, sref = OQ.quant_1x128(np64(h32)[rows])
     assert np.array_equal(npi(hq)[rows], qref)
-    assert np.array_equal(npi(hs)[rows].astype(np.float64), sref)
-    assert np.array_equal(npi(hq2)[rows], npi(hq)[rows]) and np.array_equal(npi(hs2)[rows], npi(hs)[rows])
+    assert np.array_equal(npi(hs).T[rows].astype(np.float64), sref)
+    assert np.array_equal(npi(hq2)[rows], npi(hq)[rows]) and np.array_equal(npi(hs2).T[rows], npi(hs).T[rows])
     assert rel_fro(np64(gu)[rows], obf16(GU[rows])) <= TOL
 
 
@@ -348,7 +348,7 @@ def test_layer_ep8_full_size_sampled():
         GU = OG.blockscaled_matmul(xq, xsc, rq[0], OG.expand_weight_scales(rs[0]))
         h = OL.silu(of32(GU[:, :wl.f])) * of32(GU[:, wl.f:])
         hq_g = npi(out["hq"])[rows]
-        hs_g = npi(out["hs"])[rows].astype(np.float64)
+        hs_g = npi(out["hs"]).T[rows].astype(np.float64)
         deq_g = OQ.dequant_1x128(hq_g, hs_g)
         assert rel_fro(deq_g, h) <= 0.05            # FP8 of h itself: a few percent
         Yref = obf16(OG.blockscaled_matmul(hq_g, hs_g, rq2[0], OG.expand_weight_scales(rs2[0])))
