@@ -158,13 +158,16 @@ int moe_quant_fp8(const void* src, int32_t src_type, int64_t groups, int64_t row
 
 /* 128x1 quantisation along rows of the expert-grouped layout, transposed output,
  * for the wgrad GEMMs (operands re-quantised along their contraction axis, the
- * token axis).  Source row r is  v[r, c] = fp32(w[p] * src[p / k, c])  for the
+ * token axis).  Transposed outputs here and in moe_swiglu_backward are tiled by
+ * token block ("block-transposed"): qT[b][c][i] holds row 128b + i, column c,
+ * i.e. [row_cap/128, cols, 128] bytes, so that 128 columns of one token block
+ * are one contiguous 16 KB piece.  Source row r is  v[r, c] = fp32(w[p] * src[p / k, c])  for the
  * pair p = row_pair[r] (w == NULL: v = src[p / k, c]); padding rows are 0.
  * Tiles are the 128-row blocks [128b, 128b+128) for 128b < offsets[L] (every
  * block lies inside one expert because segments are 128-aligned).
- *   src [T, cols] bf16;  qT [cols, row_cap] u8;  sT [row_cap/128, cols] fp32
- *   (token-block-major scales, the layout the wgrad GEMM reads).
- * Columns at and past offsets[L] are left unchanged.                          */
+ *   src [T, cols] bf16;  qT [row_cap/128, cols, 128] u8 (block-transposed);
+ *   sT [row_cap/128, cols] fp32 (token-block-major scales, the layout the wgrad
+ *   GEMM reads).  Token blocks at and past offsets[L]/128 are left unchanged. */
 int moe_quant_fp8_rows_t(const uint16_t* src, const float* w, const int32_t* row_pair,
                          const int32_t* offsets, int32_t L, int64_t row_cap, int32_t k,
                          int64_t cols, uint8_t* qT, float* sT, hipStream_t stream);
@@ -200,10 +203,11 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* b, c
 
 /* Weight-gradient grouped GEMM: for every local expert e,
  *     dW[e][m, n] = sum over the 128-row token blocks b of e's padded segment:
- *                   aT_s[b, m] * bT_s[b, n] * sum_{r in b} dec(aT[m, r]) * dec(bT[n, r])
+ *                   aT_s[b, m] * bT_s[b, n] * sum_i dec(aT[b][m][i]) * dec(bT[b][n][i])
  * accumulated in fp32 and stored as bf16.
- *   aT [M, row_cap] e4m3, aT_s [row_cap/128, M]; bT [N, row_cap], bT_s [row_cap/128, N]
- *   (from moe_quant_fp8_rows_t or moe_swiglu_backward); dW [L, M, N] bf16.
+ *   aT [row_cap/128, M, 128] e4m3 (block-transposed), aT_s [row_cap/128, M];
+ *   bT [row_cap/128, N, 128], bT_s [row_cap/128, N] (from moe_quant_fp8_rows_t
+ *   or moe_swiglu_backward); dW [L, M, N] bf16.  row_cap < 2^31.
  *   An expert with no rows gets dW[e] = 0.  M, N multiples of 128.           */
 int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8_t* bT,
                                const float* bT_s, const int32_t* offsets, int32_t L,
@@ -220,8 +224,11 @@ int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8
  *     dG = dH * U * s * (1 + G * (1 - s)),  dU = dH * G * s,  H = G * s * U
  * Outputs (quantised as in moe_quant_fp8):
  *   dgu_q [row_cap, 2f] u8 + dgu_s [2f/128, row_cap]   1x128 tiles of [dG, dU]
- *   dgu_qT [2f, row_cap] u8 + dgu_sT [row_cap/128, 2f] 128x1 tiles, transposed
- *   h_qT [f, row_cap] u8 + h_sT [row_cap/128, f]       128x1 tiles of H, transposed
+ *   dgu_qT [row_cap/128, 2f, 128] u8 + dgu_sT [row_cap/128, 2f]
+ *                                  128x1 tiles of [dG, dU], block-transposed
+ *   h_qT [row_cap/128, f, 128] u8 + h_sT [row_cap/128, f]
+ *                                  128x1 tiles of H, block-transposed
+ *   (block-transposed as in moe_quant_fp8_rows_t)
  *   (scales in the layouts the GEMMs read: K-block-major, token-block-major)
  *   dgu_f32 [row_cap, 2f], h_f32 [row_cap, f]          optional (NULL = skip):
  *                                                      the fp32 values quantised

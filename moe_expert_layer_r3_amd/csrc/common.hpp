@@ -44,6 +44,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
+// The same rounding (nearest even) in one instruction: gfx950's
+// v_cvt_pk_bf16_f32, reached through a __bf16 vector conversion.  Only NaN
+// payloads may differ from f32_to_bf16.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
 
 // ---------------------------------------------------------------- e4m3
 constexpr float E4M3_MAX = 448.0f;

@@ -68,6 +68,10 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm volatile("" : "+v"(v));
     return v;
 }
+// The same fence applied to a variable in place: later reads of `v` depend on
+// this point, and no register copy is made (the copy opaque() needs costs a
+// v_mov per address per use).
+__device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 // Workgroup barrier that the instruction scheduler may not move any
 // instruction across: phases separated by it (MFMA work on one side, LDS reads
@@ -92,6 +96,20 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Cross-lane exchanges of gfx950 (no LDS): swap32 trades lanes 32..63 of `a`
+// with lanes 0..31 of `b`; swap16 trades the odd 16-lane rows of `a` with the
+// even rows of `b` (rows 1, 3 <-> 0, 2).
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
 }
 
 __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b) {

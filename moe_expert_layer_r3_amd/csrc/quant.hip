@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void quant_rows_t_kernel(const uint16_t* __res
     for (int idx = tid; idx < 128 * 8; idx += 256) {
         const int c = idx >> 3, part = (idx & 7) * 16;
         uint4 val = *reinterpret_cast<const uint4*>(&tile_t[c][part]);
-        *reinterpret_cast<uint4*>(qT + (cc * 128 + c) * row_cap + b * 128 + part) = val;
+        *reinterpret_cast<uint4*>(qT + ((b * cols + cc * 128 + c) << 7) + part) = val;
     }
 }
 

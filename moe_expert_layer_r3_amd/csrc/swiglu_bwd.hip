@@ -179,8 +179,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
         const int q = idx >> 10, c = (idx >> 3) & 127, part = (idx & 7) * 16;
         const uint4 val = *reinterpret_cast<const uint4*>(&tile_t[q][c][part]);
         uint8_t* dst = q == 2 ? a.h_qT : a.dgu_qT;
-        const int64_t crow = (q == 1 ? f : 0) + cb * 128 + c;
-        *reinterpret_cast<uint4*>(dst + crow * a.row_cap + b * 128 + part) = val;
+        const int64_t crow = (q == 1 ? f : 0) + cb * 128 + c, C = q == 2 ? (int64_t)f : F2;
+        *reinterpret_cast<uint4*>(dst + ((b * C + crow) << 7) + part) = val;
     }
 }
 

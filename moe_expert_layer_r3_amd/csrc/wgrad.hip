@@ -5,27 +5,44 @@
 // For every local expert e and its padded row segment [offsets[e], offsets[e+1]):
 //   dW[e][m, n] = sum over 128-row token blocks b of the segment of
 //                 aT_s[b, m] * bT_s[b, n] * (aT[m, 128b:128b+128] . bT[n, 128b:128b+128])
-// aT [M, row_cap] and bT [N, row_cap] are both K(=token)-contiguous, the layout
-// the MFMA wants; scales are one per (row, token block) for both operands and
-// stored token-block-major, so one block's scales of a tile are contiguous.
+// aT and bT are the operands transposed and tiled by token block: aT[b][m][i]
+// is token 128b + i of row m ([row_cap/128, M, 128] bytes), so one K step of a
+// 128-row tile is a single contiguous 16 KB piece (with a plain [M, row_cap]
+// layout the 128 rows sit a power-of-two multiple apart and thrash the L2's
+// sets).  Scales are one per (row, token block) for both operands, stored
+// token-block-major, so one block's scales of a tile are contiguous too.
 //
-// Same machinery as the forward grouped GEMM (8 waves in two ping-pong groups,
-// 128 x 128 tile, three-stage LDS DMA ring, conflict-free fragment
-// layout, weights-first MFMA operand order, register-direct epilogue with the
-// next tile's first stages already in flight); differences: the contraction
-// runs over one expert's row segment (variable length, known only on the
-// device, possibly empty), both operands carry per-row scales (the factor of
-// a partial is sA[row] * sB[column], formed as the partial is added), and the
-// tile list is the dense (expert, m-tile, n-tile) grid, so experts without
-// rows get dW = 0.
+// Shape of the problem: an expert's segment is short (a few hundred tokens,
+// a handful of K steps) while its output M x N is large, so a tile does little
+// MFMA work per byte of bf16 it writes, and the operand stream is bounded by
+// the requests a CU can keep in flight to L2 (bytes per step / latency), not
+// by bandwidth.  The kernel is built around that:
+//   * 128 x 256 tiles where N allows (48 KB of operands per K step for 16
+//     MFMAs per wave; 128 x 128 needs 32 KB for 8);
+//   * each workgroup runs ONE stream of K steps over all of its tiles; the
+//     three-stage LDS DMA ring runs two steps ahead across tile boundaries, so
+//     a new tile never starts on an empty pipeline;
+//   * a finished tile is stored straight from registers while the next
+//     tile's loads are in flight.  Two cross-lane swaps first regroup each
+//     row's columns so that a lane holds 8 consecutive bf16 and every 16-byte
+//     store fills whole 64-byte segments (the MFMA layout would give 32-byte
+//     pieces, twice the write requests).  Stores and loads share the wave's
+//     vector-memory counter, so every wait counts the stores issued after the
+//     awaited stage and never drains them;
+//   * tiles of experts without rows are not in the stream: their dW = 0 is
+//     written by a plain fill after it.
+// The K step itself is the forward grouped GEMM's: 8 waves in two ping-pong
+// groups (one of each per SIMD), conflict-free swizzled fragments,
+// weights-first MFMA operand order; both operands carry per-row scales, so the
+// factor of a partial is sA[row] * sB[column], formed as the partial is added.
 #include "mfma_common.hpp"
 
 namespace moe {
 
-constexpr int WBM = 128;
-constexpr int WBK = 128;
+constexpr int WBM = 128;  // tile rows (M); tile columns BN = 256 or 128
+constexpr int WBK = 128;  // tokens per K step (one quantisation block)
 constexpr int WTHREADS = 512;
-constexpr int WWAVES = WTHREADS / 64;
+constexpr int WMAXL = 1024;
 
 struct WgradArgs {
     const uint8_t* aT;
@@ -47,39 +64,84 @@ struct WgradSmem {
     static constexpr int SA_BYTES = WBM * 4;
     static constexpr int SB_BYTES = BN * 4;
     static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-    static constexpr int TOTAL = 3 * STAGE;
+    static constexpr int TAB = 3 * STAGE;  // experts with rows: count, packed id|nkb, lo
+    static constexpr int TOTAL = TAB + (1 + 2 * WMAXL) * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS");
 };
+
+// vmcnt wait for a count known only at run time; n is one of the few sums of
+// NLD (a stage's loads) and NST (a tile's stores) the loop produces.
+template <int NLD, int NST>
+__device__ __forceinline__ void wait_younger(int n) {
+    if (n == NLD) wait_vmcnt<NLD>();
+    else if (n == NLD + NST) wait_vmcnt<NLD + NST>();
+    else if (n == NLD + 2 * NST) wait_vmcnt<NLD + 2 * NST>();
+    else if (n == NST) wait_vmcnt<NST>();
+    else if (n == 2 * NST) wait_vmcnt<2 * NST>();
+    else wait_vmcnt<0>();
+}
 
 template <int BN>
 __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     using SM = WgradSmem<BN>;
-    constexpr int WN = BN / 4;              // wave tile columns
-    constexpr int NI = WN / 16;             // n-subtiles per wave
-    constexpr int ASEG = WBM / 8 / WWAVES;  // 1 KB A segments per wave (2)
-    constexpr int BSEG = BN / 8 / WWAVES;   // 1 KB B segments per wave (4 or 2)
-    constexpr int BROWS = BN / WWAVES;      // B rows (and B scales) loaded per wave
-    constexpr int NLD = ASEG + BSEG + 2;    // DMA instructions per wave per stage (+ A and B scales)
+    constexpr int WN = BN / 4;             // wave tile columns
+    constexpr int NI = WN / 16;            // n-subtiles per wave
+    constexpr int ASEG = WBM / 64;         // 1 KB A segments (8 rows) per wave per stage
+    constexpr int BSEG = BN / 64;          // 1 KB B segments per wave per stage
+    constexpr int SROWS = BN / 8;          // B scales loaded per wave
+    constexpr int NLD = ASEG + BSEG + 2;   // DMA instructions per wave per stage (+ A and B scales)
+    constexpr int NST = 2 * NI;            // 16-byte stores per wave per tile
+    static_assert(SROWS <= 64 && NLD + 2 * NST < 64, "DMA lanes, vmcnt range");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
+    int* const tab = reinterpret_cast<int*>(smem + SM::TAB);
+    int* const tab_x = tab + 1;           // e | nkb << 10
+    int* const tab_lo = tab + 1 + WMAXL;  // first row of the segment
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int64_t rcap = g.row_cap;
     const int M = g.M, N = g.N;
-    const int MT = M / WBM, NT = N / BN;
-    const int total = g.L * MT * NT;
+    const int MT = M / WBM, NT = N / BN, TPE = MT * NT;
     const int G = gridDim.x;
     const int lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
+    // experts with at least one token block, in order
+    if (wave == 0) {
+        int cnt = 0;
+        for (int c = 0; c < g.L; c += 64) {
+            const int e = c + lane;
+            int64_t lo = 0, hi = 0;
+            if (e < g.L) {
+                lo = g.offsets[e];
+                hi = g.offsets[e + 1];
+                lo = lo < 0 ? 0 : (lo > rcap ? rcap : lo);
+                hi = hi > rcap ? rcap : hi;
+            }
+            const int nkb = hi > lo ? (int)((hi - lo) / WBK) : 0;
+            const uint64_t m = __ballot(nkb > 0);
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (nkb > 0) {
+                tab_x[cnt + below] = e | (nkb << 10);
+                tab_lo[cnt + below] = (int)lo;
+            }
+            cnt += __popcll(m);
+        }
+        if (lane == 0) tab[0] = cnt;
+    }
+    __syncthreads();
+    const int Lne = __builtin_amdgcn_readfirstlane(tab[0]);
+    const int total = Lne * TPE;  // tiles with K work, expert-major, then n-tile, m-tile fastest
+
     // fragment read offsets (lane l: row l & 15 of a fragment, K chunks g and
     // g + 4 of the 128-byte block, g = l >> 4; swizzled chunk c ^ (row & 7))
-    const int l15 = lane & 15, l7 = lane & 7, c0 = lane >> 4, lg = lane >> 4;
-    const uint32_t a_rd0 = (wm * 64 + l15) * 128 + ((c0 ^ l7) << 4);
-    const uint32_t a_rd1 = (wm * 64 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
-    const uint32_t b_rd0 = SM::A_BYTES + (wn * WN + l15) * 128 + ((c0 ^ l7) << 4);
-    const uint32_t b_rd1 = SM::A_BYTES + (wn * WN + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    const int l15 = lane & 15, l7 = lane & 7, lg = lane >> 4;
+    const uint32_t a_rd0 = (wm * 64 + l15) * 128 + ((lg ^ l7) << 4);
+    const uint32_t a_rd1 = (wm * 64 + l15) * 128 + (((lg + 4) ^ l7) << 4);
+    const uint32_t b_rd0 = SM::A_BYTES + (wn * WN + l15) * 128 + ((lg ^ l7) << 4);
+    const uint32_t b_rd1 = SM::A_BYTES + (wn * WN + l15) * 128 + (((lg + 4) ^ l7) << 4);
     // A scales: the 16 bytes at slot wm*64 + 4*l15 hold rows wm*64 + mi*16 + l15
     // (mi = 0..3); B scales: natural order, 4 consecutive columns per read
     const uint32_t sa_rd = SM::A_BYTES + SM::B_BYTES + (wm * 64 + l15 * 4) * 4;
@@ -95,193 +157,301 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         rSA[st] = b + sa_rd;
         rSB[st] = b + sb_rd;
     }
+    // output: byte offset in the tile of this lane's first 16 bytes of row
+    // wm*64 + mi*16 + l15 after the regrouping in finish() (columns wn*WN + 8*lg
+    // .. +7; the next 16 bytes of the lane, if any, are 64 bytes further)
+    uint32_t o_off[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) o_off[mi] = (uint32_t)(((wm * 64 + mi * 16 + l15) * N + wn * WN) * 2 + 16 * lg);
 
-    struct Tile {
-        int e, mt, nt, nkb;
-        const uint8_t* a_base;   // this wave's first A row at the segment start
-        const uint8_t* b_base;
-        const float* sa_base;    // the tile's A scales, first token block of the segment
-        const float* sb_base;    // this wave's B scales, first token block
-    };
-    auto tile_at = [&](int t) {
-        Tile ti;
-        ti.e = t / (MT * NT);
-        const int rem = t - ti.e * MT * NT;
-        ti.nt = rem / MT;  // m fastest: consecutive tiles share the B operand
-        ti.mt = rem - ti.nt * MT;
-        int64_t lo = g.offsets[ti.e], hi = g.offsets[ti.e + 1];
-        if (lo > rcap) lo = rcap;
-        if (hi > rcap) hi = rcap;
-        ti.nkb = __builtin_amdgcn_readfirstlane(hi > lo ? (int)((hi - lo) / WBK) : 0);
-        const int64_t kb0 = lo / WBK;
-        ti.a_base = g.aT + ((int64_t)ti.mt * WBM + wave * ASEG * 8) * rcap + lo;
-        ti.b_base = g.bT + ((int64_t)ti.nt * BN + wave * BSEG * 8) * rcap + lo;
-        ti.sa_base = g.aT_s + kb0 * M + (int64_t)ti.mt * WBM;
-        ti.sb_base = g.bT_s + kb0 * N + (int64_t)ti.nt * BN + wave * BROWS;
-        return ti;
-    };
-
-    // DMA lane offsets (swizzled chunk of row 8q + l/8 of each 1 KB segment)
+    // DMA lane offset: swizzled chunk of row l/8 of a contiguous 1 KB segment
+    // (8 rows of one token block); both operands share it
     const int lr = lane >> 3;
-    const uint32_t chunk = (uint32_t)(((lane & 7) ^ lr) << 4);
-    uint32_t a_off[ASEG], b_off[BSEG];
-#pragma unroll
-    for (int i = 0; i < ASEG; ++i) a_off[i] = (uint32_t)((8 * i + lr) * rcap) + chunk;
-#pragma unroll
-    for (int i = 0; i < BSEG; ++i) b_off[i] = (uint32_t)((8 * i + lr) * rcap) + chunk;
+    const uint32_t seg_off = (uint32_t)(lr * WBK + (((lane & 7) ^ lr) << 4));
     // lane l < 16 of wave w fills A scale slot w*16 + l: row (w/4)*64 + (l%4)*16
     // + (w%4)*4 + l/4 (the slot layout above)
     const uint32_t sa_off = (uint32_t)(((wave >> 2) * 64 + (lane & 3) * 16 + (wave & 3) * 4 + ((lane & 15) >> 2)) * 4);
-    const uint32_t sb_off = (uint32_t)((lane & (BROWS - 1)) * 4);
+    const uint32_t sb_off = (uint32_t)((lane & (SROWS - 1)) * 4);
 
-    auto issue = [&](auto stage_c, int kb, const Tile& ti) {
+    // A tile is (j, nt, mt): the j-th expert with rows, n-tile, m-tile (m
+    // fastest: neighbours share B).  Workgroup lb takes tiles lb, lb + G, ...;
+    // the step G is split into carries so that no division runs per tile.
+    struct Pos {
+        int j, nt, mt;
+    };
+    const int Gj = G / TPE, Gr = G - Gj * TPE, Gnt = Gr / MT, Gmt = Gr - Gnt * MT;
+    auto step_pos = [&](Pos& p) {
+        p.mt += Gmt;
+        int c = p.mt >= MT ? 1 : 0;
+        p.mt -= c * MT;
+        p.nt += Gnt + c;
+        c = p.nt >= NT ? 1 : 0;
+        p.nt -= c * NT;
+        p.j += Gj + c;
+    };
+    Pos p0;
+    p0.j = lb / TPE;
+    p0.nt = (lb - p0.j * TPE) / MT;
+    p0.mt = lb - p0.j * TPE - p0.nt * MT;
+    auto nkb_of = [&](const Pos& p) -> int {
+        return p.j < Lne ? (__builtin_amdgcn_readfirstlane(tab_x[p.j]) >> 10) : 0;
+    };
+    struct Src {
+        const uint8_t* a;  // this wave's first A row at the segment start
+        const uint8_t* b;
+        const float* sa;   // the tile's A scales, first token block of the segment
+        const float* sb;   // this wave's B scales, first token block
+    };
+    auto src_of = [&](const Pos& p) {
+        const int nt = p.nt, mt = p.mt;
+        const int64_t lo = __builtin_amdgcn_readfirstlane(tab_lo[p.j]);
+        Src s;
+        s.a = g.aT + ((lo / WBK) * M + (int64_t)mt * WBM + wave * ASEG * 8) * WBK;
+        s.b = g.bT + ((lo / WBK) * N + (int64_t)nt * BN + wave * BSEG * 8) * WBK;
+        s.sa = g.aT_s + (lo / WBK) * M + (int64_t)mt * WBM;
+        s.sb = g.bT_s + (lo / WBK) * N + (int64_t)nt * BN + wave * SROWS;
+        return s;
+    };
+    auto dst_of = [&](const Pos& p) -> uint16_t* {
+        const int e = __builtin_amdgcn_readfirstlane(tab_x[p.j]) & 1023;
+        return g.dW + (int64_t)e * M * N + (int64_t)p.mt * WBM * N + (int64_t)p.nt * BN;
+    };
+
+    auto issue = [&](auto stage_c, int kb, const Src& s) {
         constexpr int stage = decltype(stage_c)::value;
         const uint32_t sA = sbase + (uint32_t)(stage * SM::STAGE);
         const uint32_t sB = sA + SM::A_BYTES;
         const uint32_t sSA = sB + SM::B_BYTES;
         const uint32_t sSB = sSA + SM::SA_BYTES;
-        const int64_t kofs = (int64_t)kb * WBK;
+        const uint8_t* a = s.a + (int64_t)kb * M * WBK;
+        const uint8_t* b = s.b + (int64_t)kb * N * WBK;
 #pragma unroll
-        for (int i = 0; i < ASEG; ++i) dma16s(ti.a_base + kofs, a_off[i], sA + (wave * ASEG + i) * 1024);
+        for (int i = 0; i < ASEG; ++i) dma16s(a + i * 1024, seg_off, sA + (wave * ASEG + i) * 1024);
 #pragma unroll
-        for (int i = 0; i < BSEG; ++i) dma16s(ti.b_base + kofs, b_off[i], sB + (wave * BSEG + i) * 1024);
-        if (lane < 16) dma4s(ti.sa_base + (int64_t)kb * M, sa_off, sSA + wave * 64);
-        if (lane < BROWS) dma4s(ti.sb_base + (int64_t)kb * N, sb_off, sSB + wave * BROWS * 4);
+        for (int i = 0; i < BSEG; ++i) dma16s(b + i * 1024, seg_off, sB + (wave * BSEG + i) * 1024);
+        if (lane < 16) dma4s(s.sa + (int64_t)kb * M, sa_off, sSA + wave * 64);
+        if (lane < SROWS) dma4s(s.sb + (int64_t)kb * N, sb_off, sSB + wave * SROWS * 4);
     };
-    auto lds_barrier = [&]() {
-        wait_lgkm0();
-        phase_barrier();
+
+    // issue cursor: the K step two ahead of the one being waited for
+    Pos ip = p0;
+    int i_kb = 0, i_nkb = nkb_of(ip);
+    Src isrc{};
+    if (ip.j < Lne) isrc = src_of(ip);
+    auto issue_next = [&](auto stage_c) -> bool {
+        if (ip.j >= Lne) return false;
+        issue(stage_c, i_kb, isrc);
+        if (++i_kb == i_nkb) {
+            step_pos(ip);
+            i_kb = 0;
+            i_nkb = nkb_of(ip);
+            if (ip.j < Lne) isrc = src_of(ip);
+        }
+        return true;
     };
 
     const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    int t = lb;
-    Tile cur;
-    if (t < total) {
-        cur = tile_at(t);
-        if (cur.nkb > 0) issue(S0{}, 0, cur);
-        if (cur.nkb > 1) issue(S1{}, 1, cur);
-    }
-    for (; t < total; t += G) {
-        const int nkb = cur.nkb;
-        v4f acc[4][NI];
-        v8i af[4], bfr[NI];
-        float sa[4];          // A scales of the loaded block (rows of this lane)
-        v4f sb[NI];           // B scales of the loaded block (4 columns per n-subtile)
-        v4f ring[4];          // raw partials awaiting their rescale
+    v4f acc[4][NI];
+    v8i af[4], bfr[NI];
+    float sa[4];  // A scales of the loaded block (rows of this lane)
+    v4f sb[NI];   // B scales of the loaded block (4 columns per n-subtile)
+    v4f ring[4];  // raw partials awaiting their rescale
+    auto clear = [&]() {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = zero4;
             ring[mi] = zero4;
-            sa[mi] = 0.f;
         }
+    };
+    clear();
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) sb[ni] = zero4;
+    for (int mi = 0; mi < 4; ++mi) sa[mi] = 0.f;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) sb[ni] = zero4;
 
-        auto flush = [&]() {
+    auto flush = [&]() {
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi][NI - 1] += ring[mi] * (sa[mi] * sb[NI - 1]);
-        };
-        auto load = [&](auto stage_c) {
-            constexpr int st = decltype(stage_c)::value;
-            const uint32_t pa0 = opaque(rA0[st]), pa1 = opaque(rA1[st]);
-            const uint32_t pb0 = opaque(rB0[st]), pb1 = opaque(rB1[st]);
-            const uint32_t psa = opaque(rSA[st]), psb = opaque(rSB[st]);
-            const u32x4 sa4 = lds16<0>(psa);
-            u32x4 sbn[NI];
-            static_for<0, NI>([&](auto nc) {
-                constexpr int ni = decltype(nc)::value;
-                sbn[ni] = lds16<ni * 64>(psb);
-            });
-            static_for<0, 4>([&](auto ic) {
-                constexpr int mi = decltype(ic)::value;
-                af[mi] = join8(lds16<mi * 2048>(pa0), lds16<mi * 2048>(pa1));
-            });
-            static_for<0, NI>([&](auto nc) {
-                constexpr int ni = decltype(nc)::value;
-                bfr[ni] = join8(lds16<ni * 2048>(pb0), lds16<ni * 2048>(pb1));
-            });
-            flush();  // with the previous block's scales
-            const uint32_t sav[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+        for (int mi = 0; mi < 4; ++mi) acc[mi][NI - 1] += ring[mi] * (sa[mi] * sb[NI - 1]);
+    };
+    auto load = [&](auto stage_c) {
+        constexpr int st = decltype(stage_c)::value;
+        pin(rA0[st]);
+        pin(rA1[st]);
+        pin(rB0[st]);
+        pin(rB1[st]);
+        pin(rSA[st]);
+        pin(rSB[st]);
+        const uint32_t pa0 = rA0[st], pa1 = rA1[st], pb0 = rB0[st], pb1 = rB1[st];
+        const uint32_t psa = rSA[st], psb = rSB[st];
+        const u32x4 sa4 = lds16<0>(psa);
+        u32x4 sbn[NI];
+        static_for<0, NI>([&](auto nc) {
+            constexpr int ni = decltype(nc)::value;
+            sbn[ni] = lds16<ni * 64>(psb);
+        });
+        static_for<0, 4>([&](auto ic) {
+            constexpr int mi = decltype(ic)::value;
+            af[mi] = join8(lds16<mi * 2048>(pa0), lds16<mi * 2048>(pa1));
+        });
+        static_for<0, NI>([&](auto nc) {
+            constexpr int ni = decltype(nc)::value;
+            bfr[ni] = join8(lds16<ni * 2048>(pb0), lds16<ni * 2048>(pb1));
+        });
+        flush();  // with the previous block's scales
+        const uint32_t sav[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) sa[mi] = __uint_as_float(sav[mi]);
+        for (int mi = 0; mi < 4; ++mi) sa[mi] = __uint_as_float(sav[mi]);
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) sb[ni] = __builtin_bit_cast(v4f, sbn[ni]);
-            wait_lgkm0();
+        for (int ni = 0; ni < NI; ++ni) sb[ni] = __builtin_bit_cast(v4f, sbn[ni]);
+        wait_lgkm0();
+    };
+    auto compute = [&]() {
+        static_for<0, 4 * NI>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int ni = j / 4, mi = j % 4;
+            if constexpr (j >= 4) acc[mi][ni - 1] += ring[mi] * (sa[mi] * sb[ni - 1]);
+            ring[mi] = mfma16x16x128(bfr[ni], af[mi]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // finished tile: bf16 straight from the accumulators, then they restart.
+    // Lane (l15, lg) holds columns 16c + 4lg .. +3 of n-subtile c: 4-column
+    // chunk q = 4c + lg of the wave's row.  Exchanging the chunk-slot bit c0
+    // with lane-group bit 1 (swap32) and then with lane-group bit 0 (swap16)
+    // leaves slot 2h + s holding chunk 8h + 2lg + s: 8 consecutive columns per
+    // lane for each h.
+    auto finish = [&](uint16_t* dst) {
+        flush();
+        uint8_t* d = reinterpret_cast<uint8_t*>(dst);
+        static_for<0, 4>([&](auto ic) {
+            constexpr int mi = decltype(ic)::value;
+            uint32_t x[NI], y[NI];  // columns (0, 1) and (2, 3) of each chunk, packed bf16
+#pragma unroll
+            for (int c = 0; c < NI; ++c) {
+                const v4f a = acc[mi][c];
+                x[c] = cvt_bf16x2(a.x, a.y);
+                y[c] = cvt_bf16x2(a.z, a.w);
+            }
+#pragma unroll
+            for (int c = 0; c < NI; c += 2) {
+                swap32(x[c], x[c + 1]);
+                swap32(y[c], y[c + 1]);
+                swap16(x[c], x[c + 1]);
+                swap16(y[c], y[c + 1]);
+            }
+#pragma unroll
+            for (int h = 0; h < NI / 2; ++h)
+                *reinterpret_cast<u32x4*>(d + o_off[mi] + h * 64) = u32x4{x[2 * h], y[2 * h], x[2 * h + 1], y[2 * h + 1]};
+        });
+        clear();
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    if (lb < total) {
+        issue_next(S0{});
+        // vector-memory ops issued after the stage the next step waits for:
+        // stores two steps back, the next stage's loads, stores one step back
+        int yng = issue_next(S1{}) ? NLD : 0;
+        int ns1 = 0;  // NST if the previous step issued stores
+        auto wait_stage = [&]() {
+            if (yng == NLD) wait_vmcnt<NLD>();  // no stores in flight: the common case
+            else wait_younger<NLD, NST>(yng);
         };
-        auto compute = [&]() {
-            static_for<0, 4 * NI>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                constexpr int ni = j / 4, mi = j % 4;
-                if constexpr (j >= 4) acc[mi][ni - 1] += ring[mi] * (sa[mi] * sb[ni - 1]);
-                ring[mi] = mfma16x16x128(bfr[ni], af[mi]);
-                __builtin_amdgcn_sched_barrier(0);
-            });
+        auto account = [&](bool iss, bool sto) {
+            yng = ns1 + (iss ? NLD : 0) + (sto ? NST : 0);
+            ns1 = sto ? NST : 0;
         };
-        auto step0 = [&](auto st_c, int kb) {
-            constexpr int st = decltype(st_c)::value;
-            if (kb + 1 < nkb) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
-            phase_barrier();
-            if (kb + 2 < nkb) issue(std::integral_constant<int, (st + 2) % 3>{}, kb + 2, cur);
-            load(st_c);
-            phase_barrier();
-            compute();
-        };
-        auto step1 = [&](auto st_c, int kb) {
-            constexpr int st = decltype(st_c)::value;
-            if (kb + 1 < nkb) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
-            phase_barrier();
-            if (kb + 2 < nkb) issue(std::integral_constant<int, (st + 2) % 3>{}, kb + 2, cur);
-            compute();
-            phase_barrier();
-            load(st_c);
-        };
-        if (nkb > 0) {
-            if (wave < 4) {
-                for (int kb = 0; kb < nkb; kb += 3) {
-                    step0(S0{}, kb);
-                    if (kb + 1 < nkb) step0(S1{}, kb + 1);
-                    if (kb + 2 < nkb) step0(S2{}, kb + 2);
-                }
-            } else {
-                if (nkb > 1) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+        Pos cp = p0;  // tile of the block being computed
+        int c_kb = 0, c_nkb = nkb_of(cp);
+
+        if (wave < 4) {
+            // group 0: wait, issue, load, | compute (and store a finished tile)
+            auto step = [&](auto st_c) -> bool {
+                constexpr int st = decltype(st_c)::value;
+                wait_stage();
                 phase_barrier();
-                if (nkb > 2) issue(S2{}, 2, cur);
+                const bool iss = issue_next(std::integral_constant<int, (st + 2) % 3>{});
+                load(st_c);
                 phase_barrier();
-                load(S0{});
-                for (int kb = 1; kb < nkb; kb += 3) {
-                    step1(S1{}, kb);
-                    if (kb + 1 < nkb) step1(S2{}, kb + 1);
-                    if (kb + 2 < nkb) step1(S0{}, kb + 2);
-                }
                 compute();
+                const bool sto = ++c_kb == c_nkb;
+                account(iss, sto);
+                if (sto) {
+                    finish(dst_of(cp));
+                    step_pos(cp);
+                    c_kb = 0;
+                    if (cp.j >= Lne) return false;
+                    c_nkb = nkb_of(cp);
+                }
+                return true;
+            };
+            // one exit: the live-out fragments and accumulators keep their
+            // registers (break exits after every step made the allocator spill)
+            bool more = true;
+            while (more) {
+                more = step(S0{});
+                if (more) more = step(S1{});
+                if (more) more = step(S2{});
             }
-            flush();
-        }
-        // stages free: the next tile's first two stages go out before this
-        // tile's epilogue
-        lds_barrier();
-        const Tile ep = cur;
-        if (t + G < total) {
-            cur = tile_at(t + G);
-            if (cur.nkb > 0) issue(S0{}, 0, cur);
-            if (cur.nkb > 1) issue(S1{}, 1, cur);
-        }
-        // bf16 store straight from registers: row wm*64 + mi*16 + l15, columns
-        // wn*WN + ni*16 + 4*lg + v of the tile
-        uint16_t* out = g.dW + (int64_t)ep.e * M * N + (int64_t)ep.mt * WBM * N + (int64_t)ep.nt * BN;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int64_t r = wm * 64 + mi * 16 + l15;
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                const v4f a = acc[mi][ni];
-                *reinterpret_cast<v2u*>(out + r * N + wn * WN + ni * 16 + 4 * lg) =
-                    v2u{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w)};
+        } else {
+            // group 1, half a step behind: wait, issue, compute the previous
+            // block (and store a finished tile), | load
+            Pos lp = p0;  // tile of the block being loaded
+            int l_kb = 0, l_nkb = c_nkb;
+            auto step = [&](auto st_c, bool prev) -> bool {
+                constexpr int st = decltype(st_c)::value;
+                wait_stage();
+                phase_barrier();
+                const bool iss = issue_next(std::integral_constant<int, (st + 2) % 3>{});
+                bool sto = false;
+                if (prev) {
+                    compute();
+                    sto = ++c_kb == c_nkb;
+                    if (sto) {
+                        finish(dst_of(cp));
+                        step_pos(cp);
+                        c_kb = 0;
+                        c_nkb = nkb_of(cp);
+                    }
+                }
+                account(iss, sto);
+                phase_barrier();
+                load(st_c);
+                if (++l_kb == l_nkb) {
+                    step_pos(lp);
+                    l_kb = 0;
+                    if (lp.j >= Lne) return false;
+                    l_nkb = nkb_of(lp);
+                }
+                return true;
+            };
+            bool more = step(S0{}, false);
+            while (more) {
+                more = step(S1{}, true);
+                if (more) more = step(S2{}, true);
+                if (more) more = step(S0{}, true);
             }
+            compute();  // the last block, loaded by the last step
+            finish(dst_of(cp));
+        }
+    }
+
+    // experts without rows: dW = 0
+    {
+        const int64_t chunks = (int64_t)M * N / 8;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        int j = 0;
+        for (int e = 0; e < g.L; ++e) {
+            if (j < Lne && (__builtin_amdgcn_readfirstlane(tab_x[j]) & 1023) == e) {
+                ++j;
+                continue;
+            }
+            uint16_t* d = g.dW + (int64_t)e * M * N;
+            for (int64_t c = (int64_t)blockIdx.x * WTHREADS + tid; c < chunks; c += (int64_t)G * WTHREADS)
+                *reinterpret_cast<u32x4*>(d + c * 8) = z;
         }
     }
 }
@@ -293,10 +463,10 @@ using namespace moe;
 extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8_t* bT,
                                           const float* bT_s, const int32_t* offsets, int32_t L, int64_t row_cap,
                                           int32_t M, int32_t N, uint16_t* dW, hipStream_t stream) {
-    MOE_REQUIRE(L >= 1 && L <= 1024, MOE_ERR_SHAPE, "grouped_gemm_wgrad: L=%d outside [1, 1024]", L);
-    // lane offsets into the operand rows are 32-bit: 16 rows of row_cap bytes must fit
-    MOE_REQUIRE(row_cap >= 0 && row_cap % WBK == 0 && row_cap < ((int64_t)1 << 28), MOE_ERR_SHAPE,
-                "grouped_gemm_wgrad: row_cap=%lld must be a multiple of 128 below 2^28", (long long)row_cap);
+    MOE_REQUIRE(L >= 1 && L <= WMAXL, MOE_ERR_SHAPE, "grouped_gemm_wgrad: L=%d outside [1, %d]", L, WMAXL);
+    // segment starts are kept as 32-bit values on the device
+    MOE_REQUIRE(row_cap >= 0 && row_cap % WBK == 0 && row_cap < ((int64_t)1 << 31), MOE_ERR_SHAPE,
+                "grouped_gemm_wgrad: row_cap=%lld must be a multiple of 128 below 2^31", (long long)row_cap);
     MOE_REQUIRE(M > 0 && M % WBM == 0 && N > 0 && N % 128 == 0, MOE_ERR_SHAPE,
                 "grouped_gemm_wgrad: M=%d and N=%d must be multiples of 128", M, N);
     MOE_REQUIRE((int64_t)L * (M / WBM) * (N / 128) < ((int64_t)1 << 31), MOE_ERR_SHAPE,
@@ -304,10 +474,10 @@ extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, 
     MOE_REQUIRE(aT && aT_s && bT && bT_s && offsets && dW, MOE_ERR_NULL, "grouped_gemm_wgrad: NULL argument");
     WgradArgs a{aT, aT_s, bT, bT_s, offsets, L, row_cap, M, N, dW};
     const int grid = (num_cus() + 7) / 8 * 8;  // persistent, one block per CU
-    // 128 x 128 tiles only: with both operands scaled per row, a 128 x 256
-    // tile needs more than 256 VGPRs and spills inside the K loop, which costs
-    // more than the extra A traffic of the narrower tile (measured 1.75x slower)
-    wgrad_fp8_kernel<128><<<dim3(grid), dim3(WTHREADS), 0, stream>>>(a);
+    if (N % 256 == 0)
+        wgrad_fp8_kernel<256><<<dim3(grid), dim3(WTHREADS), 0, stream>>>(a);
+    else
+        wgrad_fp8_kernel<128><<<dim3(grid), dim3(WTHREADS), 0, stream>>>(a);
     MOE_LAUNCH_CHECK("wgrad_fp8_kernel");
     return MOE_OK;
 }

@@ -137,18 +137,18 @@ class TrainPlan(ForwardPlan):
         self.dyq = torch.empty((R, d), dtype=u8, device=dv)
         self.dyq_s = torch.empty((d // 128, R), dtype=f32, device=dv)
         self.d_gate = torch.empty((T, k), dtype=f32, device=dv)
-        self.dyqT = torch.empty((d, R), dtype=u8, device=dv)
+        self.dyqT = torch.empty((R // 128, d, 128), dtype=u8, device=dv)  # block-transposed
         self.dyqT_s = torch.empty((R // 128, d), dtype=f32, device=dv)  # token-block-major
         self.dH = torch.empty((R, f), dtype=f32, device=dv)
         self.sb = dict(dgu_q=torch.empty((R, 2 * f), dtype=u8, device=dv),
                        dgu_s=torch.empty((2 * f // 128, R), dtype=f32, device=dv),
-                       dgu_qT=torch.empty((2 * f, R), dtype=u8, device=dv),
+                       dgu_qT=torch.empty((R // 128, 2 * f, 128), dtype=u8, device=dv),
                        dgu_sT=torch.empty((R // 128, 2 * f), dtype=f32, device=dv),
-                       h_qT=torch.empty((f, R), dtype=u8, device=dv),
+                       h_qT=torch.empty((R // 128, f, 128), dtype=u8, device=dv),
                        h_sT=torch.empty((R // 128, f), dtype=f32, device=dv))
         self.dX = torch.empty((R, d), dtype=b16, device=dv)
         self.dx = torch.empty((T, d), dtype=b16, device=dv)
-        self.xqT = torch.empty((d, R), dtype=u8, device=dv)
+        self.xqT = torch.empty((R // 128, d, 128), dtype=u8, device=dv)
         self.xqT_s = torch.empty((R // 128, d), dtype=f32, device=dv)
         self.dW2 = torch.empty((L, d, f), dtype=b16, device=dv)
         self.dW13 = torch.empty((L, 2 * f, d), dtype=b16, device=dv)

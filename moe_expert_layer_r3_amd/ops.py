@@ -8,6 +8,7 @@ fails loudly if the library has not been built; there is no fallback path."""
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -229,13 +230,26 @@ def quant_fp8(src, tile=TILE_1x128, groups=1, transpose=False):
     return q, s
 
 
+def untile_t(qT):
+    """[cols, rcap] view (a copy) of a block-transposed operand [rcap/128, cols, 128]."""
+    nb, cols, _ = qT.shape
+    return qT.permute(1, 0, 2).reshape(cols, nb * 128)
+
+
+def tile_t(q):
+    """Block-transposed layout [rcap/128, cols, 128] of a numpy [cols, rcap] array."""
+    cols, r = q.shape
+    return np.ascontiguousarray(q.reshape(cols, r // 128, 128).transpose(1, 0, 2))
+
+
 def quant_rows_t(src, w, row_pair, offsets, L, rcap, k):
     """128x1 quantisation along the expert-grouped rows (gathered from src [T, cols]
-    via row_pair, optionally scaled by w), transposed: (qT [cols, rcap], sT [cols, rcap/128])."""
+    via row_pair, optionally scaled by w), transposed: (qT [rcap/128, cols, 128]
+    block-transposed, sT [rcap/128, cols])."""
     _contig(src, torch.bfloat16, "src")
     cols = src.shape[1]
     dev = _dev(src)
-    qT = torch.empty((cols, rcap), dtype=torch.uint8, device=dev)
+    qT = torch.empty((rcap // 128, cols, 128), dtype=torch.uint8, device=dev)
     sT = torch.empty((rcap // 128, cols), dtype=torch.float32, device=dev)  # token-block-major
     _call("moe_quant_fp8_rows_t", _p(src), _p(w), _p(row_pair), _p(offsets), L, rcap, k, cols, _p(qT), _p(sT),
           _stream(dev))
@@ -280,8 +294,9 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
 
 
 def grouped_gemm_wgrad(aT, aT_s, bT, bT_s, offsets, L, rcap, out=None):
-    """dW [L, M, N] bf16 from the 128x1-quantised transposed operands aT [M, rcap], bT [N, rcap]."""
-    M, N = aT.shape[0], bT.shape[0]
+    """dW [L, M, N] bf16 from the 128x1-quantised block-transposed operands
+    aT [rcap/128, M, 128], bT [rcap/128, N, 128]."""
+    M, N = aT.shape[1], bT.shape[1]
     dW = torch.empty((L, M, N), dtype=torch.bfloat16, device=_dev(aT)) if out is None else out
     _call("moe_grouped_gemm_fp8_wgrad", _p(aT), _p(aT_s), _p(bT), _p(bT_s), _p(offsets), L, rcap, M, N, _p(dW),
           _stream(aT.device))
@@ -292,7 +307,7 @@ def swiglu_backward(dH, gu, row_pair, offsets, L, rcap, inspect=False, out=None)
     """Backward through SwiGLU + FP8 re-quantisation of its results.
 
     dH [rcap, f] fp32, gu [rcap, 2f] bf16 (saved G, U).  Returns a dict with
-    dgu_q, dgu_s (1x128), dgu_qT, dgu_sT (128x1, transposed), h_qT, h_sT and, when
+    dgu_q, dgu_s (1x128), dgu_qT, dgu_sT (128x1, block-transposed), h_qT, h_sT and, when
     inspect, the fp32 dgu and h that were quantised.  ``out`` may hold
     preallocated tensors under the same names."""
     _contig(dH, torch.float32, "dH")
@@ -301,8 +316,8 @@ def swiglu_backward(dH, gu, row_pair, offsets, L, rcap, inspect=False, out=None)
     dev = _dev(dH)
     o = {} if out is None else dict(out)
     shapes = dict(dgu_q=((rcap, 2 * f), torch.uint8), dgu_s=((2 * f // 128, rcap), torch.float32),
-                  dgu_qT=((2 * f, rcap), torch.uint8), dgu_sT=((rcap // 128, 2 * f), torch.float32),
-                  h_qT=((f, rcap), torch.uint8), h_sT=((rcap // 128, f), torch.float32))
+                  dgu_qT=((rcap // 128, 2 * f, 128), torch.uint8), dgu_sT=((rcap // 128, 2 * f), torch.float32),
+                  h_qT=((rcap // 128, f, 128), torch.uint8), h_sT=((rcap // 128, f), torch.float32))
     if inspect:
         shapes.update(dgu=((rcap, 2 * f), torch.float32), h=((rcap, f), torch.float32))
     for name, (shape, dt) in shapes.items():

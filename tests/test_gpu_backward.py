@@ -61,7 +61,7 @@ def test_quant_rows_t(weighted):
     p = rp[real]
     v[real] = src[p // k] if w is None else of32(w.reshape(-1)[p][:, None].astype(np.float64) * src[p // k])
     rq, rs = OQ.quant_128x1_t(v, real)
-    assert np.array_equal(npi(qT)[:, :n], rq)
+    assert np.array_equal(npi(ops.untile_t(qT))[:, :n], rq)
     assert np.array_equal(npi(sT)[:n // 128].T.astype(np.float64), rs)
 
 
@@ -141,17 +141,17 @@ def test_swiglu_backward(counts, f):
     assert np.array_equal(npi(o["dgu_q"])[rows], q1)
     assert np.array_equal(npi(o["dgu_s"]).T[rows].astype(np.float64), s1)
     qt, st = OQ.quant_128x1_t(dgu, real)
-    assert np.array_equal(npi(o["dgu_qT"])[:, :n], qt)
+    assert np.array_equal(npi(ops.untile_t(o["dgu_qT"]))[:, :n], qt)
     assert np.array_equal(npi(o["dgu_sT"])[:n // 128].T.astype(np.float64), st)
     qh, sh = OQ.quant_128x1_t(h, real)
-    assert np.array_equal(npi(o["h_qT"])[:, :n], qh)
+    assert np.array_equal(npi(ops.untile_t(o["h_qT"]))[:, :n], qh)
     assert np.array_equal(npi(o["h_sT"])[:n // 128].T.astype(np.float64), sh)
     # the production call (no inspection outputs) writes the same bytes
     o2 = ops.swiglu_backward(gpu(dH), bf16_tensor(GU), res["row_pair"], res["offsets"], len(counts), rcap)
     assert np.array_equal(npi(o2["dgu_q"])[rows], npi(o["dgu_q"])[rows])
     assert np.array_equal(npi(o2["dgu_s"]).T[rows], npi(o["dgu_s"]).T[rows])
     for key in ("dgu_qT", "h_qT"):
-        assert np.array_equal(npi(o2[key])[:, :n], npi(o[key])[:, :n])
+        assert np.array_equal(npi(o2[key])[:n // 128], npi(o[key])[:n // 128])
 
 
 # ------------------------------------------------------------------ dgrad GEMM (transposed weights)
@@ -198,10 +198,14 @@ def _wgrad_check(got, ref, absum):
         raise AssertionError(f"element {i}: got {got[i]!r} ref {ref[i]!r} |terms| {absum[i]!r}")
 
 
+# the last case puts several tiles (of 1-, 2- and 3-block experts, with empty
+# experts between them) into each workgroup's stream of K steps
 @pytest.mark.parametrize("counts,M,N", [([0, 1, 130, 300], 256, 512), ([128, 256, 0, 5], 128, 128),
-                                        ([1500], 384, 256), ([0, 0], 128, 256)])
+                                        ([1500], 384, 256), ([0, 0], 128, 256),
+                                        ([(i * 37) % 300 if i % 7 else 0 for i in range(40)], 512, 1024)])
 def test_wgrad(counts, M, N):
-    k, E, e0 = 2, 16, 0
+    k = 2 if len(counts) <= 8 else 8
+    E, e0 = max(16, len(counts) + k), 0
     ids, res, rp, rng = _perm(counts, k, E, e0, seed=M + N + len(counts))
     L = len(counts)
     rcap = res["row_cap"]
@@ -218,7 +222,7 @@ def test_wgrad(counts, M, N):
         sf = np.full((rcap // 128, q.shape[0]), np.nan, dtype=np.float32)
         qf[:, :n] = q
         sf[:n // 128] = s.T
-        return gpu(qf), gpu(sf)
+        return gpu(ops.tile_t(qf)), gpu(sf)
     aT, aT_s = upload(qa, sa)
     bT, bT_s = upload(qb, sb)
     say(f"wgrad counts={counts} M={M} N={N}")
@@ -269,8 +273,13 @@ def _rows(t, rows):
 
 
 def _cols(t, cols, c0=None, c1=None):
-    """t[cols, c0:c1] (rows of a transposed operand, a column range) as numpy."""
-    sub = t[torch.as_tensor(np.asarray(cols, dtype=np.int64), device=t.device)][:, c0:c1]
+    """t[cols, c0:c1] (rows of a transposed operand, a column range) as numpy;
+    a block-transposed operand [rcap/128, cols, 128] is read as [cols, rcap]."""
+    idx = torch.as_tensor(np.asarray(cols, dtype=np.int64), device=t.device)
+    if t.dim() == 3:
+        sub = t[:, idx].permute(1, 0, 2).reshape(len(idx), -1)[:, c0:c1]
+    else:
+        sub = t[idx][:, c0:c1]
     return np64(sub) if sub.is_floating_point() else npi(sub)
 
 
@@ -308,8 +317,8 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
     realrows = np.flatnonzero(real)
     assert torch.equal(ins["dgu_q"][:n][torch.as_tensor(realrows, device=DEV)],
                        plan.sb["dgu_q"][:n][torch.as_tensor(realrows, device=DEV)])
-    assert torch.equal(ins["dgu_qT"][:, :n], plan.sb["dgu_qT"][:, :n])
-    assert torch.equal(ins["h_qT"][:, :n], plan.sb["h_qT"][:, :n])
+    assert torch.equal(ins["dgu_qT"][:n // 128], plan.sb["dgu_qT"][:n // 128])
+    assert torch.equal(ins["h_qT"][:n // 128], plan.sb["h_qT"][:n // 128])
     for e in experts:
         if c[e] == 0:
             continue
