@@ -2,22 +2,28 @@
 // Expert Parallelism" and "Expert Parallel"): the per-layer dispatch becomes a
 // local, stable, expert-grouped permutation of the (token, slot) pairs.
 //
-//   1. hist    : per chunk of CHUNK pairs, count local pairs per expert (LDS)
-//   2. scan    : per expert, exclusive scan of the chunk counts; counts; the
+//   1. hist    : per chunk of PCHUNK pairs, count local pairs per expert (LDS)
+//   2. scan    : per expert, exclusive scan of the chunk counts (one wave per
+//                expert, shuffle prefix over 64 chunks at a time); counts; the
 //                128-aligned offsets; padding rows of row_pair = -1
 //   3. scatter : per chunk, rank every pair among the earlier pairs of its
 //                expert (wave ballots, in pair order) and write row_pair /
-//                pair_row -- deterministic, no order-dependent atomics
-//   4. gather  : token-major: each token row of x is read once, quantised to
+//                pair_row -- deterministic, no order-dependent atomics; the
+//                per-expert row bases of the chunk are staged in LDS first
+//   4. gather  : one workgroup per token: its local rows are read once as
+//                uniform values, the row of x is read once, quantised to
 //                1x128 e4m3 once, and written to each of its local rows.
+// Chunks are small (1024 pairs) so that even a few thousand tokens spread the
+// index work over many workgroups; every step is latency-bound, not
+// bandwidth-bound.
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int PCHUNK = 4096;       // pairs per chunk (one block)
+constexpr int PCHUNK = 1024;       // pairs per chunk (one block)
 constexpr int PBLOCK = 256;        // threads per block in hist / scatter
 constexpr int PWAVES = PBLOCK / 64;
-constexpr int PER_WAVE = PCHUNK / PWAVES;  // 1024 consecutive pairs per wave
+constexpr int PER_WAVE = PCHUNK / PWAVES;  // 256 consecutive pairs per wave
 constexpr int MAXL = 1024;
 
 __global__ __launch_bounds__(PBLOCK) void perm_hist_kernel(const int32_t* __restrict__ ids, int64_t P, int e0,
@@ -37,41 +43,64 @@ __global__ __launch_bounds__(PBLOCK) void perm_hist_kernel(const int32_t* __rest
     for (int e = threadIdx.x; e < L; e += PBLOCK) chunk_counts[(int64_t)blockIdx.x * L + e] = cnt[e];
 }
 
-// Single block of 1024 threads; thread e owns expert e.
+// Single block of 1024 threads (16 waves).  Wave w handles experts w, w + 16,
+// ... for the chunk prefixes and the padding rows; thread e owns expert e for
+// the scan over experts (wave shuffles, one LDS round for the wave totals).
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunk, int L,
                                                          int64_t row_cap, int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ row_pair,
                                                          int32_t* __restrict__ status) {
-    __shared__ int64_t part[1024];
-    const int e = threadIdx.x;
-    int run = 0;
-    if (e < L) {
-        for (int c = 0; c < nchunk; ++c) {
-            int v = chunk_counts[(int64_t)c * L + e];
-            chunk_counts[(int64_t)c * L + e] = run;
-            run += v;
+    __shared__ int tot[MAXL];
+    __shared__ int64_t wsum[16];
+    __shared__ int64_t ends[MAXL];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // exclusive prefix of each expert's chunk counts, in place
+    for (int e = wave; e < L; e += 16) {
+        int carry = 0;
+        for (int c0 = 0; c0 < nchunk; c0 += 64) {
+            const int c = c0 + lane;
+            const int v = c < nchunk ? chunk_counts[(int64_t)c * L + e] : 0;
+            int x = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o);
+                if (lane >= o) x += y;
+            }
+            if (c < nchunk) chunk_counts[(int64_t)c * L + e] = carry + x - v;
+            carry += __shfl(x, 63);
         }
+        if (lane == 0) tot[e] = carry;
     }
-    const int64_t padded = e < L ? ((int64_t)run + MOE_ROW_ALIGN - 1) / MOE_ROW_ALIGN * MOE_ROW_ALIGN : 0;
-    // inclusive scan of padded sizes over the block (Hillis-Steele in LDS)
-    part[e] = padded;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        int64_t add = e >= off ? part[e - off] : 0;
-        __syncthreads();
-        part[e] += add;
-        __syncthreads();
+    // inclusive scan of the 128-aligned segment sizes over experts
+    const int e = threadIdx.x;
+    const int run = e < L ? tot[e] : 0;
+    const int64_t padded = ((int64_t)run + MOE_ROW_ALIGN - 1) / MOE_ROW_ALIGN * MOE_ROW_ALIGN;
+    int64_t x = padded;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
     }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) x += wsum[w];
     if (e < L) {
-        const int64_t end = part[e];
-        const int64_t start = end - padded;
+        ends[e] = x;
         counts[e] = run;
-        offsets[e + 1] = (int32_t)(end > 0x7FFFFFFF ? 0x7FFFFFFF : end);
+        offsets[e + 1] = (int32_t)(x > 0x7FFFFFFF ? 0x7FFFFFFF : x);
         if (e == 0) offsets[0] = 0;
-        for (int64_t r = start + run; r < end; ++r)
+        if (e == L - 1 && x > row_cap && status) atomicOr(status, MOE_FLAG_ROW_CAP);
+    }
+    __syncthreads();
+    // padding rows of each segment (fewer than 128): row_pair = -1
+    for (int e2 = wave; e2 < L; e2 += 16) {
+        const int64_t end = ends[e2];
+        const int c = tot[e2];
+        const int64_t start = end - ((int64_t)c + MOE_ROW_ALIGN - 1) / MOE_ROW_ALIGN * MOE_ROW_ALIGN;
+        for (int64_t r = start + c + lane; r < end; r += 64)
             if (r < row_cap) row_pair[r] = -1;
-        if (e == L - 1 && end > row_cap && status) atomicOr(status, MOE_FLAG_ROW_CAP);
     }
 }
 
@@ -81,23 +110,35 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
                                                               const int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ row_pair,
                                                               int32_t* __restrict__ pair_row) {
-    // run[w][e]: pairs of expert e seen so far by wave w (first pass: totals)
+    // run[w][e]: pairs of expert e seen so far by wave w (first pass: totals);
+    // base[e]: first row of this chunk's pairs of expert e
     __shared__ int run[PWAVES][MAXL];
+    __shared__ int64_t base[MAXL];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int e = threadIdx.x; e < L; e += PBLOCK)
+    for (int e = threadIdx.x; e < L; e += PBLOCK) {
         for (int w = 0; w < PWAVES; ++w) run[w][e] = 0;
+        base[e] = (int64_t)offsets[e] + chunk_base[(int64_t)blockIdx.x * L + e];
+    }
     __syncthreads();
     const int64_t wbase = (int64_t)blockIdx.x * PCHUNK + (int64_t)wave * PER_WAVE;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-    // pass 1: per-wave totals per expert
+    // the wave's local expert ids, loaded once for both passes
+    int les[PER_WAVE / 64];
+#pragma unroll
     for (int it = 0; it < PER_WAVE / 64; ++it) {
-        int64_t p = wbase + it * 64 + lane;
+        const int64_t p = wbase + it * 64 + lane;
         int le = -1;
         if (p < P) {
             le = ids[p] - e0;
             if (le < 0 || le >= L) le = -1;
         }
+        les[it] = le;
+    }
+    // pass 1: per-wave totals per expert
+#pragma unroll
+    for (int it = 0; it < PER_WAVE / 64; ++it) {
+        const int le = les[it];
         uint64_t active = __ballot(le >= 0);
         while (active) {
             int leader = __ffsll((unsigned long long)active) - 1;
@@ -119,13 +160,10 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
     }
     __syncthreads();
     // pass 2: ranks in pair order, write rows
+#pragma unroll
     for (int it = 0; it < PER_WAVE / 64; ++it) {
-        int64_t p = wbase + it * 64 + lane;
-        int le = -1;
-        if (p < P) {
-            le = ids[p] - e0;
-            if (le < 0 || le >= L) le = -1;
-        }
+        const int64_t p = wbase + it * 64 + lane;
+        const int le = les[it];
         int64_t row = -1;
         uint64_t active = __ballot(le >= 0);
         while (active) {
@@ -133,10 +171,7 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
             int e = __shfl(le, leader);
             uint64_t m = __ballot(le == e) & active;
             int before = run[wave][e];
-            if (le == e) {
-                row = (int64_t)offsets[e] + chunk_base[(int64_t)blockIdx.x * L + e] + before +
-                      __popcll(m & lt_mask);
-            }
+            if (le == e) row = base[e] + before + __popcll(m & lt_mask);
             __builtin_amdgcn_wave_barrier();
             if (lane == leader) run[wave][e] = before + __popcll(m);
             __builtin_amdgcn_wave_barrier();
@@ -150,50 +185,71 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
     }
 }
 
-// Token-major gather with fused 1x128 quantisation.  A work item is one
-// 128-wide tile of one token row, handled by 16 lanes of 8 bf16 values each.
-__global__ __launch_bounds__(256) void gather_quant_kernel(const uint16_t* __restrict__ x, int64_t T, int d, int k,
-                                                           const int32_t* __restrict__ pair_row,
-                                                           uint16_t* __restrict__ x_perm,
-                                                           uint8_t* __restrict__ xq, float* __restrict__ xq_s,
-                                                           int64_t row_cap) {
-    const int ntile = d >> 7;
-    const int64_t item = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
-    const int sub = threadIdx.x & 15;
-    const bool live = item < T * ntile;
-    const int64_t t = live ? item / ntile : 0;
-    const int tile = live ? (int)(item - t * ntile) : 0;
-    bool any_local = false;
-    if (live)
-        for (int j = 0; j < k; ++j) any_local |= pair_row[t * k + j] >= 0;
-    // all 16 lanes of an item agree; items never straddle a group of 16 lanes
-    if (!any_local) return;
-    const int64_t col = (int64_t)tile * 128 + sub * 8;
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + t * d + col);
-    float v[8];
-    v[0] = bf16_lo(raw.x); v[1] = bf16_hi(raw.x);
-    v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);
-    v[4] = bf16_lo(raw.z); v[5] = bf16_hi(raw.z);
-    v[6] = bf16_lo(raw.w); v[7] = bf16_hi(raw.w);
-    uint2 packed = make_uint2(0, 0);
-    float s = 0.f;
-    if (xq) {
-        float am = 0.f;
+// Token-major gather with fused 1x128 quantisation: one workgroup per token.
+// The token's k local rows are uniform (scalar loads, k <= 16); each 16-lane
+// group covers one 128-column tile with 8 bf16 per lane, so the tile's amax is
+// a 16-lane reduction.  The row's loads are issued together (up to GQ_LOADS
+// passes of 256 lanes x 8 columns) before any store.
+constexpr int GQ_THREADS = 256;
+constexpr int GQ_LOADS = 4;
+
+__global__ __launch_bounds__(GQ_THREADS) void gather_quant_kernel(const uint16_t* __restrict__ x, int64_t T,
+                                                                  int d, int k,
+                                                                  const int32_t* __restrict__ pair_row,
+                                                                  uint16_t* __restrict__ x_perm,
+                                                                  uint8_t* __restrict__ xq,
+                                                                  float* __restrict__ xq_s, int64_t row_cap) {
+    const int64_t t = blockIdx.x;
+    int r[16];
+    bool any = false;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
-        am = group_max<16>(am);
-        TileScale ts = tile_scale(am);
-        s = ts.s;
-        packed.x = cvt_e4m3x4(v[0] * ts.inv, v[1] * ts.inv, v[2] * ts.inv, v[3] * ts.inv);
-        packed.y = cvt_e4m3x4(v[4] * ts.inv, v[5] * ts.inv, v[6] * ts.inv, v[7] * ts.inv);
+    for (int j = 0; j < 16; ++j) {
+        r[j] = j < k ? pair_row[t * k + j] : -1;
+        any |= r[j] >= 0;
     }
-    for (int j = 0; j < k; ++j) {
-        const int64_t r = pair_row[t * k + j];
-        if (r < 0) continue;
-        if (x_perm) *reinterpret_cast<uint4*>(x_perm + r * d + col) = raw;
-        if (xq) {
-            *reinterpret_cast<uint2*>(xq + r * d + col) = packed;
-            if (sub == 0) xq_s[tile * row_cap + r] = s;  // K-block-major scales
+    if (!any) return;
+    const int sub = threadIdx.x & 15;
+    const uint16_t* xr = x + t * d;
+    for (int c0 = 0; c0 < d; c0 += GQ_LOADS * GQ_THREADS * 8) {
+        uint4 raw[GQ_LOADS];
+#pragma unroll
+        for (int i = 0; i < GQ_LOADS; ++i) {
+            const int col = c0 + (i * GQ_THREADS + threadIdx.x) * 8;
+            if (col < d) raw[i] = *reinterpret_cast<const uint4*>(xr + col);
+        }
+#pragma unroll
+        for (int i = 0; i < GQ_LOADS; ++i) {
+            const int col = c0 + (i * GQ_THREADS + threadIdx.x) * 8;
+            // d % 128 == 0: a 16-lane group is entirely in or out of range
+            if (col >= d) continue;
+            const int tile = col >> 7;
+            uint2 packed = make_uint2(0, 0);
+            float s = 0.f;
+            if (xq) {
+                float v[8];
+                v[0] = bf16_lo(raw[i].x); v[1] = bf16_hi(raw[i].x);
+                v[2] = bf16_lo(raw[i].y); v[3] = bf16_hi(raw[i].y);
+                v[4] = bf16_lo(raw[i].z); v[5] = bf16_hi(raw[i].z);
+                v[6] = bf16_lo(raw[i].w); v[7] = bf16_hi(raw[i].w);
+                float am = 0.f;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(v[q]));
+                am = group_max<16>(am);
+                const TileScale ts = tile_scale(am);
+                s = ts.s;
+                packed.x = cvt_e4m3x4(v[0] * ts.inv, v[1] * ts.inv, v[2] * ts.inv, v[3] * ts.inv);
+                packed.y = cvt_e4m3x4(v[4] * ts.inv, v[5] * ts.inv, v[6] * ts.inv, v[7] * ts.inv);
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (j >= k || r[j] < 0) continue;
+                const int64_t row = r[j];
+                if (x_perm) *reinterpret_cast<uint4*>(x_perm + row * d + col) = raw[i];
+                if (xq) {
+                    *reinterpret_cast<uint2*>(xq + row * d + col) = packed;
+                    if (sub == 0) xq_s[tile * row_cap + row] = s;  // K-block-major scales
+                }
+            }
         }
     }
 }
@@ -251,10 +307,8 @@ extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0,
         MOE_LAUNCH_CHECK("perm_scatter_kernel");
     }
     if (x && T > 0) {
-        const int64_t items = T * (d / 128);
-        const int64_t threads = items * 16;
-        gather_quant_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
-            x, T, d, k, pair_row, x_perm, xq, xq_s, row_cap);
+        gather_quant_kernel<<<dim3((unsigned)T), dim3(GQ_THREADS), 0, stream>>>(x, T, d, k, pair_row, x_perm, xq,
+                                                                               xq_s, row_cap);
         MOE_LAUNCH_CHECK("gather_quant_kernel");
     }
     return MOE_OK;
