@@ -88,6 +88,32 @@ def train_gemm_flops(P, d, f):
             "wgrad2": 2.0 * P * d * f, "wgrad13": 4.0 * P * d * f}
 
 
+def train_gemm_bytes(P, R, L, d, f):
+    """Algorithmic HBM bytes of the six grouped GEMMs of a training step: P local
+    pairs, R expert-grouped rows (segments padded to 128, the wgrad contraction).
+    FP8 operands count 1 byte per element plus fp32 scales per 128 elements."""
+    q = lambda n: n + n // 128 * 4                 # FP8 codes + 1x128 / 128x1 scales
+    w = lambda n: n + n // (128 * 128) * 4         # FP8 codes + 128x128 scales
+    return {"gemm1": w(L * 2 * f * d) + q(P * d) + q(P * f) + P * 2 * f * 2,   # + saved bf16 [G, U]
+            "gemm2": w(L * d * f) + q(P * f) + P * d * 2,
+            "dgrad2": q(P * d) + w(L * d * f) + P * f * 4,                     # dH fp32
+            "dgrad1": q(P * 2 * f) + w(L * 2 * f * d) + P * d * 2,             # dX bf16
+            "wgrad2": q(R * d) + q(R * f) + L * d * f * 2,                     # dW2 bf16
+            "wgrad13": q(R * 2 * f) + q(R * d) + L * 2 * f * d * 2}            # dW13 bf16
+
+
+def roofline_of(flops, nbytes, ms):
+    """Roofline entry of one kernel: bound by whichever floor (MFMA or HBM) is longer."""
+    t_mfma = flops / (FP8_PEAK_TFLOPS * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t = ms * 1e-3
+    if t_hbm >= t_mfma:
+        return {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": t_hbm / t}
+    return {"bound": "mfma", "achieved": flops / t / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": t_mfma / t}
+
+
 def measured_traffic(workload):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary, or None when the kernel source changed since then."""
@@ -218,10 +244,14 @@ def train_leg(steps, warmup, dev):
     ms = (t1 - t0) * 1e3 / steps
     kern = mean_ms(ev)
     P = int(plan.counts.sum().item())
+    R = int(plan.offsets[-1].item())
     fl = train_gemm_flops(P, wl.d, wl.f)
+    by = train_gemm_bytes(P, R, wl.L, wl.d, wl.f)
     gemm_ms = sum(kern[n] for n in fl)
     per = {n: {"ms": kern[n], "tflops": fl[n] / (kern[n] * 1e-3) / 1e12,
-               "mfma_frac": fl[n] / (kern[n] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS} for n in fl}
+               "mfma_frac": fl[n] / (kern[n] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+               "gbs": by[n] / (kern[n] * 1e-3) / 1e9, "flops": fl[n], "bytes": by[n],
+               "roofline": roofline_of(fl[n], by[n], kern[n])} for n in fl}
     top = max(fl, key=lambda n: kern[n])
     res = {
         "workload": f"train: T={wl.T}, d={wl.d}, f={wl.f}, {wl.L} of {wl.E} experts local, top-{wl.k}, "
@@ -233,8 +263,7 @@ def train_leg(steps, warmup, dev):
         "kernel_ms": kern,
         "gemms": per,
         "gemm_tflops": sum(fl.values()) / (gemm_ms * 1e-3) / 1e12,
-        "roofline": {"bound": "mfma", "kernel": top, "achieved": per[top]["tflops"], "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": per[top]["mfma_frac"], "traffic": None},
+        "roofline": dict(kernel=top, **per[top]["roofline"], traffic=None),
     }
     res["gemm_mfma_frac"] = res["gemm_tflops"] / FP8_PEAK_TFLOPS
     del plan, wts, lg_d, x_d, dy_d, W13_d, W2_d
