@@ -22,7 +22,14 @@
 //   * persistent blocks walk an expert-major tile list built on the device from
 //     counts/offsets (no host sync); consecutive tiles share a weight tile and
 //     are mapped to the same XCD so that weight tile is fetched into one L2.
-//   * epilogues stage through LDS for coalesced 16-byte stores.
+//   * tiles that run side by side on an XCD and share an operand (the two
+//     m-tiles of one weight tile, the n-tiles of one A tile) start their K loop
+//     at different K blocks (a rotation of 2 per odd m-tile and 2 per n-tile
+//     modulo 4): a neighbour's request for a line then finds it already in L2
+//     instead of waiting on the same miss while holding a request slot
+//     (measured: GEMM1 at 256 rows per expert 346 -> 313 us).  Only the order
+//     of the fp32 block sums changes.
+//   * epilogues write straight from registers.
 #include "mfma_common.hpp"
 
 namespace moe {
@@ -175,6 +182,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         const float* s_base;           // the tile's A scales
         const float* bs_lo;            // B scales of this wave's column blocks, K block 0
         const float* bs_hi;
+        int rot;                       // first K block of the tile's loop (rotated order)
     };
     auto tile_at = [&](int t) {
         int lo = 0, hi = L;
@@ -224,6 +232,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         }
         ti.bs_lo = bsx + (int64_t)blk0 * nkb;
         ti.bs_hi = bsx + (int64_t)blk1 * nkb;
+        ti.rot = ((mt & 1) * 2 + (nt & 3) * 2) % nkb;
         return ti;
     };
     // B scales of a tile's two column blocks for every K block, staged in LDS
@@ -259,12 +268,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         const uint32_t sA = sbase + (uint32_t)(stage * SM::STAGE);
         const uint32_t sB = sA + SM::A_BYTES;
         const uint32_t sS = sB + SM::B_BYTES;
-        const int kofs = kb * GBK;
+        int kr = kb + ti.rot;  // K block in memory order
+        if (kr >= nkb) kr -= nkb;
+        const int kofs = kr * GBK;
 #pragma unroll
         for (int i = 0; i < ASEG; ++i) dma16s(ti.a_base + kofs, a_off[i], sA + (wave * ASEG + i) * 1024);
 #pragma unroll
         for (int i = 0; i < BSEG; ++i) dma16s(ti.b_base + kofs, b_off[i], sB + (wave * BSEG + i) * 1024);
-        if (lane < 16) dma4s(ti.s_base + (int64_t)kb * g.row_cap, s_off, sS + wave * 64);  // 16 rows' A scales
+        if (lane < 16) dma4s(ti.s_base + (int64_t)kr * g.row_cap, s_off, sS + wave * 64);  // 16 rows' A scales
     };
     // barrier for LDS data only (s_waitcnt lgkmcnt(0) + s_barrier): unlike
     // __syncthreads it does not wait for the next tile's operand DMA in flight
@@ -312,7 +323,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
             // published the stage
             const uint32_t pa0 = opaque(rA0[st]), pa1 = opaque(rA1[st]);
             const uint32_t pb0 = opaque(rB0[st]), pb1 = opaque(rB1[st]), ps = opaque(rS[st]);
-            const uint32_t bsa = opaque(bs_rd + kb * 8);
+            int kr = kb + cur.rot;
+            if (kr >= nkb) kr -= nkb;
+            const uint32_t bsa = opaque(bs_rd + kr * 8);
             const v2u sbv = lds8<0>(bsa);
             const u32x4 sa4 = lds16<0>(ps);
             static_for<0, 4>([&](auto ic) {
