@@ -46,129 +46,155 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
     if (sub == 0) s[r * ntile + tile] = ts.s;
 }
 
-// 128x128: one block of 256 threads per tile.  Thread i covers columns
-// (i%16)*8 .. +7 of rows i/16 + 16*j, j = 0..7.  The optional transposed copy
-// goes through an LDS byte tile.
+// 128x128: one block of 256 threads per tile.  Thread (wave w, lane l) covers
+// rows 8*rq .. 8*rq + 7 of the tile, rq = 4w + l/16, and columns 8*cg .. +7,
+// cg = l % 16 (16 lanes read a row's 256 bytes).  The optional transposed copy
+// goes through an LDS tile: a column's codes for the thread's 8 consecutive
+// rows are one 8-byte word.
 template <bool F32>
 __global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restrict__ src, int64_t rows,
                                                             int64_t cols, int64_t ld, uint8_t* __restrict__ q,
                                                             float* __restrict__ s, uint8_t* __restrict__ qT,
                                                             float* __restrict__ sT) {
     __shared__ float wmax[4];
-    __shared__ __attribute__((aligned(16))) uint8_t tile_t[128][128 + 16];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_t[128][128 + 8];
     const int64_t rb_n = rows >> 7, cb_n = cols >> 7;
     const int64_t g = blockIdx.z;
     const int64_t rb = blockIdx.y, cb = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int c8 = (tid & 15) * 8, r0 = tid >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = lane & 15, rq = wave * 4 + (lane >> 4);
+    const int c8 = cg * 8;
     const int64_t gbase = g * rows * ld;
     float v[8][8];
-    float am = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int64_t r = rb * 128 + r0 + 16 * j;
+        const int64_t r = rb * 128 + rq * 8 + j;
         load8<F32>(src, gbase + r * ld + cb * 128 + c8, v[j]);
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[j][i]));
-    }
     am = group_max<64>(am);
-    if ((tid & 63) == 0) wmax[tid >> 6] = am;
+    if (lane == 0) wmax[wave] = am;
     __syncthreads();
     am = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    TileScale ts = tile_scale(am);
+    const TileScale ts = tile_scale(am);
     const int64_t qbase = g * rows * cols;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int r = r0 + 16 * j;
         uint2 out;
         out.x = cvt_e4m3x4(v[j][0] * ts.inv, v[j][1] * ts.inv, v[j][2] * ts.inv, v[j][3] * ts.inv);
         out.y = cvt_e4m3x4(v[j][4] * ts.inv, v[j][5] * ts.inv, v[j][6] * ts.inv, v[j][7] * ts.inv);
-        *reinterpret_cast<uint2*>(q + qbase + (rb * 128 + r) * cols + cb * 128 + c8) = out;
-        if (qT) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) tile_t[c8 + i][r] = (uint8_t)(((i < 4 ? out.x : out.y) >> (8 * (i & 3))) & 0xFF);
-        }
+        *reinterpret_cast<uint2*>(q + qbase + (rb * 128 + rq * 8 + j) * cols + cb * 128 + c8) = out;
     }
     if (tid == 0) {
         s[(g * rb_n + rb) * cb_n + cb] = ts.s;
         if (sT) sT[(g * cb_n + cb) * rb_n + rb] = ts.s;
     }
     if (qT) {
+        // column c8 + i, rows 8rq .. 8rq + 7 (the same rounding as above)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t lo = cvt_e4m3x4(v[0][i] * ts.inv, v[1][i] * ts.inv, v[2][i] * ts.inv, v[3][i] * ts.inv);
+            const uint32_t hi = cvt_e4m3x4(v[4][i] * ts.inv, v[5][i] * ts.inv, v[6][i] * ts.inv, v[7][i] * ts.inv);
+            *reinterpret_cast<uint2*>(&tile_t[c8 + i][rq * 8]) = make_uint2(lo, hi);
+        }
         __syncthreads();
         // qT[g][c][r]: 128 rows of the transposed tile, 16 bytes per thread per step
         for (int idx = tid; idx < 128 * 8; idx += 256) {
             const int c = idx >> 3, part = (idx & 7) * 16;
-            uint4 val = *reinterpret_cast<const uint4*>(&tile_t[c][part]);
+            const uint4 val = *reinterpret_cast<const uint4*>(&tile_t[c][part]);
             *reinterpret_cast<uint4*>(qT + qbase + (cb * 128 + c) * rows + rb * 128 + part) = val;
         }
     }
 }
 
 // 128x1 along rows of the expert-grouped layout with the row gather fused,
-// transposed output.  Block (column chunk cc of 128, row block b of 128).
-// Thread i covers columns (i%16)*8 .. +7 of rows i/16 + 16*j, j = 0..7.
+// block-transposed output.  Block (column chunk cc of 128, row block b of 128),
+// 256 threads.  Thread (wave w, lane l) owns rows 8*rq .. 8*rq + 7 of the block,
+// rq = 4w + l/16, and columns 8*cg .. 8*cg + 7, cg = l % 16:
+//   * the 16 lanes of one row read its 256 contiguous bytes, and the thread's
+//     8 row ids are one 32-byte load, all issued before any use;
+//   * a column's maximum is the thread's 8 rows, then the wave's 4 row octets
+//     (lanes 16 apart), then the 4 waves through a small LDS array;
+//   * a column's codes for the thread's 8 consecutive rows are one 8-byte word
+//     of the transposed LDS tile, which leaves as 16-byte stores of full
+//     128-byte columns.
 __global__ __launch_bounds__(256) void quant_rows_t_kernel(const uint16_t* __restrict__ src,
                                                            const float* __restrict__ w,
                                                            const int32_t* __restrict__ row_pair,
                                                            const int32_t* __restrict__ offsets, int L,
                                                            int64_t row_cap, int k, int64_t cols,
                                                            uint8_t* __restrict__ qT, float* __restrict__ sT) {
-    __shared__ float cmax[16][128];
-    __shared__ __attribute__((aligned(16))) uint8_t tile_t[128][128 + 16];
+    __shared__ __attribute__((aligned(16))) float cmax[4][128];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_t[128][128 + 8];
     const int64_t b = blockIdx.y, cc = blockIdx.x;
     int64_t total = offsets[L];
     if (total > row_cap) total = row_cap;
     if (b * 128 >= total) return;  // whole block leaves together
-    const int tid = threadIdx.x;
-    const int c8 = (tid & 15) * 8, r0 = tid >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = lane & 15, rq = wave * 4 + (lane >> 4);
+    const int c8 = cg * 8;
+    const int4* rp = reinterpret_cast<const int4*>(row_pair + b * 128 + rq * 8);
+    const int4 pa = rp[0], pb = rp[1];
+    const int p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    float wp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wp[j] = (w && p[j] >= 0) ? w[p[j]] : 1.f;
     float v[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (p[j] >= 0) {
+            load8<false>(src, (int64_t)(p[j] / k) * cols + cc * 128 + c8, v[j]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
+        }
+    }
     float am[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) am[i] = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int64_t r = b * 128 + r0 + 16 * j;
-        const int p = row_pair[r];
-        if (p >= 0) {
-            const int64_t t = p / k;
-            load8<false>(src, t * cols + cc * 128 + c8, v[j]);
-            if (w) {
-                const float wp = w[p];
+        if (w) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[j][i] = wp * v[j][i];
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
+            for (int i = 0; i < 8; ++i) v[j][i] = wp[j] * v[j][i];
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) am[i] = fmaxf(am[i], fabsf(v[j][i]));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) cmax[r0][c8 + i] = am[i];
+    for (int i = 0; i < 8; ++i) {
+        am[i] = fmaxf(am[i], __shfl_xor(am[i], 16));
+        am[i] = fmaxf(am[i], __shfl_xor(am[i], 32));
+    }
+    if (lane < 16) {
+        *reinterpret_cast<float4*>(&cmax[wave][c8]) = make_float4(am[0], am[1], am[2], am[3]);
+        *reinterpret_cast<float4*>(&cmax[wave][c8 + 4]) = make_float4(am[4], am[5], am[6], am[7]);
+    }
     __syncthreads();
     float inv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float m = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) m = fmaxf(m, cmax[rr][c8 + i]);
-        TileScale ts = tile_scale(m);
+        const float m = fmaxf(fmaxf(cmax[0][c8 + i], cmax[1][c8 + i]), fmaxf(cmax[2][c8 + i], cmax[3][c8 + i]));
+        const TileScale ts = tile_scale(m);
         inv[i] = ts.inv;
-        if (r0 == 0) sT[b * cols + cc * 128 + c8 + i] = ts.s;  // token-block-major scales
+        if (wave == 0 && lane < 16) sT[b * cols + cc * 128 + c8 + i] = ts.s;  // token-block-major scales
     }
+    // column c8 + i, rows 8rq .. 8rq + 7: bytes 0..7 of one word
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = r0 + 16 * j;
-        uint32_t lo = cvt_e4m3x4(v[j][0] * inv[0], v[j][1] * inv[1], v[j][2] * inv[2], v[j][3] * inv[3]);
-        uint32_t hi = cvt_e4m3x4(v[j][4] * inv[4], v[j][5] * inv[5], v[j][6] * inv[6], v[j][7] * inv[7]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) tile_t[c8 + i][r] = (uint8_t)(((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFF);
+    for (int i = 0; i < 8; ++i) {
+        const float x = inv[i];
+        const uint32_t lo = cvt_e4m3x4(v[0][i] * x, v[1][i] * x, v[2][i] * x, v[3][i] * x);
+        const uint32_t hi = cvt_e4m3x4(v[4][i] * x, v[5][i] * x, v[6][i] * x, v[7][i] * x);
+        *reinterpret_cast<uint2*>(&tile_t[c8 + i][rq * 8]) = make_uint2(lo, hi);
     }
     __syncthreads();
     for (int idx = tid; idx < 128 * 8; idx += 256) {
         const int c = idx >> 3, part = (idx & 7) * 16;
-        uint4 val = *reinterpret_cast<const uint4*>(&tile_t[c][part]);
+        const uint4 val = *reinterpret_cast<const uint4*>(&tile_t[c][part]);
         *reinterpret_cast<uint4*>(qT + ((b * cols + cc * 128 + c) << 7) + part) = val;
     }
 }

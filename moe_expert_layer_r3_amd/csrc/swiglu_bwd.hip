@@ -36,33 +36,38 @@ struct SwigluBwdArgs {
     float* h_f32;
 };
 
-// One block per (128-row block, 128-column block of f); 256 threads.  Thread i
-// covers columns (i%16)*8 .. +7 of rows i/16 + 16*j, j = 0..7, for all three
-// results.  Column maxima meet in LDS; the transposed codes go through LDS
-// byte tiles so that every global store is a 16-byte chunk of a 128-byte run.
+// One block per (128-row block, 128-column block of f); 256 threads.  Thread
+// (wave w, lane l) covers rows 8*rq .. 8*rq + 7 of the block, rq = 4w + l/16,
+// and columns 8*cg .. +7 of the f-block, cg = l % 16, for all three results:
+//   * the 16 lanes of a row share its 1x128 tiles (a 16-lane max);
+//   * a column's maximum over the block's 128 rows is the thread's 8 rows, the
+//     wave's 4 row octets (lanes 16 apart), then the 4 waves through a small
+//     LDS array;
+//   * a column's codes for the thread's 8 consecutive rows are one 8-byte word
+//     of the transposed LDS tile, which leaves as 16-byte stores of full
+//     128-byte columns.
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
-    __shared__ float cmax[3][16][128];
-    __shared__ __attribute__((aligned(16))) uint8_t tile_t[3][128][128 + 16];
+    __shared__ __attribute__((aligned(16))) float cmax[3][4][128];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_t[3][128][128 + 8];
     const int64_t b = blockIdx.x, cb = blockIdx.y;
     int64_t total = a.offsets[a.L];
     if (total > a.row_cap) total = a.row_cap;
     if (b * 128 >= total) return;  // whole block leaves together
-    const int tid = threadIdx.x;
-    const int c8 = (tid & 15) * 8, r0 = tid >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = lane & 15, rq = wave * 4 + (lane >> 4);
+    const int c8 = cg * 8;
     const int f = a.f;
     const int64_t F2 = 2 * (int64_t)f;
     const int64_t col = cb * 128 + c8;  // column of f
+    const int64_t r0 = b * 128 + rq * 8;
+    const int4* rp = reinterpret_cast<const int4*>(a.row_pair + r0);
+    const int4 pa = rp[0], pb = rp[1];
+    const bool real[8] = {pa.x >= 0, pa.y >= 0, pa.z >= 0, pa.w >= 0, pb.x >= 0, pb.y >= 0, pb.z >= 0, pb.w >= 0};
 
     float dg[8][8], du[8][8], hh[8][8];
-    bool real[8];
-    float am[3][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am[0][i] = am[1][i] = am[2][i] = 0.f;
-
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int64_t r = b * 128 + r0 + 16 * j;
-        real[j] = a.row_pair[r] >= 0;
+        const int64_t r = r0 + j;
         if (real[j]) {
             const float4* hp = reinterpret_cast<const float4*>(a.dH + r * f + col);
             const float4 h0 = hp[0], h1 = hp[1];
@@ -85,18 +90,12 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) dg[j][i] = du[j][i] = hh[j][i] = 0.f;
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            am[0][i] = fmaxf(am[0][i], fabsf(dg[j][i]));
-            am[1][i] = fmaxf(am[1][i], fabsf(du[j][i]));
-            am[2][i] = fmaxf(am[2][i], fabsf(hh[j][i]));
-        }
     }
 
     // row-major outputs: 1x128 [dG, dU] (the 16 lanes of a row share the tile)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int64_t r = b * 128 + r0 + 16 * j;
+        const int64_t r = r0 + j;
         float mg = 0.f, mu = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -114,7 +113,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
         qu.y = cvt_e4m3x4(du[j][4] * tu.inv, du[j][5] * tu.inv, du[j][6] * tu.inv, du[j][7] * tu.inv);
         *reinterpret_cast<uint2*>(a.dgu_q + r * F2 + col) = qg;
         *reinterpret_cast<uint2*>(a.dgu_q + r * F2 + f + col) = qu;
-        if ((tid & 15) == 0) {
+        if (cg == 0) {
             a.dgu_s[cb * a.row_cap + r] = tg.s;  // K-block-major scales
             a.dgu_s[((f >> 7) + cb) * a.row_cap + r] = tu.s;
         }
@@ -135,45 +134,45 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
 
     // 128x1 tiles: column maxima over the block's 128 rows
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cmax[q][r0][c8 + i] = am[q][i];
-    __syncthreads();
-    float inv[3][8];
-#pragma unroll
-    for (int q = 0; q < 3; ++q)
+    for (int q = 0; q < 3; ++q) {
+        float am[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float m = 0.f;
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) m = fmaxf(m, cmax[q][rr][c8 + i]);
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(q == 0 ? dg[j][i] : q == 1 ? du[j][i] : hh[j][i]));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            am[i] = fmaxf(m, __shfl_xor(m, 32));
+        }
+        if (lane < 16) {
+            *reinterpret_cast<float4*>(&cmax[q][wave][c8]) = make_float4(am[0], am[1], am[2], am[3]);
+            *reinterpret_cast<float4*>(&cmax[q][wave][c8 + 4]) = make_float4(am[4], am[5], am[6], am[7]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float m = fmaxf(fmaxf(cmax[q][0][c8 + i], cmax[q][1][c8 + i]),
+                                  fmaxf(cmax[q][2][c8 + i], cmax[q][3][c8 + i]));
             const TileScale ts = tile_scale(m);
-            inv[q][i] = ts.inv;
-            if (r0 == 0) {
+            if (wave == 0 && lane < 16) {
                 // scales of the transposed tiles, token-block-major: dG at
                 // column c, dU at f + c (of 2f), H at c (of f)
                 float* sT = q == 2 ? a.h_sT : a.dgu_sT;
                 const int64_t c = (q == 1 ? f : 0) + col + i;
                 sT[b * (q == 2 ? (int64_t)f : F2) + c] = ts.s;
             }
+            // column c8 + i, rows 8rq .. 8rq + 7: bytes 0..7 of one word
+            const float x = ts.inv;
+            float y[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] = (q == 0 ? dg[j][i] : q == 1 ? du[j][i] : hh[j][i]) * x;
+            const uint32_t lo = cvt_e4m3x4(y[0], y[1], y[2], y[3]);
+            const uint32_t hi = cvt_e4m3x4(y[4], y[5], y[6], y[7]);
+            *reinterpret_cast<uint2*>(&tile_t[q][c8 + i][rq * 8]) = make_uint2(lo, hi);
         }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = r0 + 16 * j;
-        const uint32_t w[6] = {
-            cvt_e4m3x4(dg[j][0] * inv[0][0], dg[j][1] * inv[0][1], dg[j][2] * inv[0][2], dg[j][3] * inv[0][3]),
-            cvt_e4m3x4(dg[j][4] * inv[0][4], dg[j][5] * inv[0][5], dg[j][6] * inv[0][6], dg[j][7] * inv[0][7]),
-            cvt_e4m3x4(du[j][0] * inv[1][0], du[j][1] * inv[1][1], du[j][2] * inv[1][2], du[j][3] * inv[1][3]),
-            cvt_e4m3x4(du[j][4] * inv[1][4], du[j][5] * inv[1][5], du[j][6] * inv[1][6], du[j][7] * inv[1][7]),
-            cvt_e4m3x4(hh[j][0] * inv[2][0], hh[j][1] * inv[2][1], hh[j][2] * inv[2][2], hh[j][3] * inv[2][3]),
-            cvt_e4m3x4(hh[j][4] * inv[2][4], hh[j][5] * inv[2][5], hh[j][6] * inv[2][6], hh[j][7] * inv[2][7]),
-        };
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                tile_t[q][c8 + i][r] = (uint8_t)((w[2 * q + (i >> 2)] >> (8 * (i & 3))) & 0xFF);
-    }
     __syncthreads();
     for (int idx = tid; idx < 3 * 128 * 8; idx += 256) {
         const int q = idx >> 10, c = (idx >> 3) & 127, part = (idx & 7) * 16;
