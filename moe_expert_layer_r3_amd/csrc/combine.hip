@@ -8,8 +8,12 @@ namespace moe {
 constexpr int CMAXK = 16;
 constexpr int CBLOCK = 128;
 
-// One block per token; each thread owns 8-element chunks of the output row.
-// Local slots are summed in ascending order in fp32.
+// One block per token; each thread owns up to CPT 8-element chunks of the
+// output row (chunks t, t + CBLOCK, ...).  Local slots are summed in ascending
+// order in fp32.  For each local slot (a uniform branch) the thread's chunk
+// loads are all issued before the first is used, so a token costs about one
+// memory latency per local slot rather than one per chunk and slot.
+constexpr int CPT = 8;
 __global__ __launch_bounds__(CBLOCK) void combine_kernel(const uint16_t* __restrict__ y_perm,
                                                          const int32_t* __restrict__ pair_row,
                                                          const float* __restrict__ w, int k, int d,
@@ -23,38 +27,56 @@ __global__ __launch_bounds__(CBLOCK) void combine_kernel(const uint16_t* __restr
         ws[j] = (j < k && w) ? w[t * k + j] : 1.f;
     }
     const int nchunk = d >> 3;
-    for (int c = threadIdx.x; c < nchunk; c += CBLOCK) {
-        float acc[8];
+    for (int c0 = 0; c0 < nchunk; c0 += CBLOCK * CPT) {
+        float acc[CPT][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int q = 0; q < CPT; ++q)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
 #pragma unroll
         for (int j = 0; j < CMAXK; ++j) {
-            if (rows[j] >= 0) {
-                const uint4 v = *reinterpret_cast<const uint4*>(y_perm + (int64_t)rows[j] * d + c * 8);
-                const float wj = ws[j];
-                acc[0] = fmaf(wj, bf16_lo(v.x), acc[0]);
-                acc[1] = fmaf(wj, bf16_hi(v.x), acc[1]);
-                acc[2] = fmaf(wj, bf16_lo(v.y), acc[2]);
-                acc[3] = fmaf(wj, bf16_hi(v.y), acc[3]);
-                acc[4] = fmaf(wj, bf16_lo(v.z), acc[4]);
-                acc[5] = fmaf(wj, bf16_hi(v.z), acc[5]);
-                acc[6] = fmaf(wj, bf16_lo(v.w), acc[6]);
-                acc[7] = fmaf(wj, bf16_hi(v.w), acc[7]);
+            if (rows[j] < 0) continue;
+            const uint16_t* src = y_perm + (int64_t)rows[j] * d;
+            uint4 v[CPT];
+#pragma unroll
+            for (int q = 0; q < CPT; ++q) {
+                const int c = c0 + q * CBLOCK + threadIdx.x;
+                if (c < nchunk) v[q] = *reinterpret_cast<const uint4*>(src + c * 8);
+            }
+            const float wj = ws[j];
+#pragma unroll
+            for (int q = 0; q < CPT; ++q) {
+                acc[q][0] = fmaf(wj, bf16_lo(v[q].x), acc[q][0]);
+                acc[q][1] = fmaf(wj, bf16_hi(v[q].x), acc[q][1]);
+                acc[q][2] = fmaf(wj, bf16_lo(v[q].y), acc[q][2]);
+                acc[q][3] = fmaf(wj, bf16_hi(v[q].y), acc[q][3]);
+                acc[q][4] = fmaf(wj, bf16_lo(v[q].z), acc[q][4]);
+                acc[q][5] = fmaf(wj, bf16_hi(v[q].z), acc[q][5]);
+                acc[q][6] = fmaf(wj, bf16_lo(v[q].w), acc[q][6]);
+                acc[q][7] = fmaf(wj, bf16_hi(v[q].w), acc[q][7]);
             }
         }
-        uint4 o;
-        o.x = pack_bf16x2(acc[0], acc[1]);
-        o.y = pack_bf16x2(acc[2], acc[3]);
-        o.z = pack_bf16x2(acc[4], acc[5]);
-        o.w = pack_bf16x2(acc[6], acc[7]);
-        *reinterpret_cast<uint4*>(y + t * d + c * 8) = o;
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            const int c = c0 + q * CBLOCK + threadIdx.x;
+            if (c >= nchunk) continue;
+            uint4 o;
+            o.x = cvt_bf16x2(acc[q][0], acc[q][1]);
+            o.y = cvt_bf16x2(acc[q][2], acc[q][3]);
+            o.z = cvt_bf16x2(acc[q][4], acc[q][5]);
+            o.w = cvt_bf16x2(acc[q][6], acc[q][7]);
+            *reinterpret_cast<uint4*>(y + t * d + c * 8) = o;
+        }
     }
 }
 
-// One block per token.  Work unit: one 128-wide tile, 16 lanes x 8 values.
-// For every local slot j: dY = fp32(w_j * dy) quantised 1x128 (the tile amax of
-// the rounded products is fp32(|w_j| * amax|dy|) because rounding is
-// monotonic), and the partial dot <dy, Y_r> for d_gate.
+// One block per token.  Work unit: one 128-wide tile, 16 lanes x 8 values; the
+// 8 lane groups take tiles g, g + 8, ..., TPG at a time.  For every local slot
+// j: dY = fp32(w_j * dy) quantised 1x128 (the tile amax of the rounded
+// products is fp32(|w_j| * amax|dy|) because rounding is monotonic), and the
+// partial dot <dy, Y_r> for d_gate.  Per local slot (a uniform branch) the
+// group's Y tile loads are issued together before any is used.
+constexpr int TPG = 7;
 __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __restrict__ dy,
                                                              const uint16_t* __restrict__ y_perm,
                                                              const int32_t* __restrict__ pair_row,
@@ -64,58 +86,71 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
     __shared__ float part[CBLOCK / 64][CMAXK];
     const int64_t t = blockIdx.x;
     const int sub = threadIdx.x & 15, grp = threadIdx.x >> 4;  // 8 groups of 16 lanes
-    const int ntile = d >> 7;
-    int rows[CMAXK];
-    float ws[CMAXK], dot[CMAXK];
-#pragma unroll
-    for (int j = 0; j < CMAXK; ++j) {
-        rows[j] = j < k ? pair_row[t * k + j] : -1;
-        ws[j] = j < k ? w[t * k + j] : 0.f;
-        dot[j] = 0.f;
-    }
-    for (int tile = grp; tile < ntile; tile += CBLOCK / 16) {
-        const int64_t col = (int64_t)tile * 128 + sub * 8;
-        const uint4 raw = *reinterpret_cast<const uint4*>(dy + t * d + col);
-        float v[8];
-        v[0] = bf16_lo(raw.x); v[1] = bf16_hi(raw.x);
-        v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);
-        v[4] = bf16_lo(raw.z); v[5] = bf16_hi(raw.z);
-        v[6] = bf16_lo(raw.w); v[7] = bf16_hi(raw.w);
-        float am = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
-        am = group_max<16>(am);
-#pragma unroll
-        for (int j = 0; j < CMAXK; ++j) {
-            if (rows[j] < 0) continue;
-            const int64_t r = rows[j];
-            const float wj = ws[j];
-            const uint4 yr = *reinterpret_cast<const uint4*>(y_perm + r * d + col);
-            dot[j] = fmaf(v[0], bf16_lo(yr.x), dot[j]);
-            dot[j] = fmaf(v[1], bf16_hi(yr.x), dot[j]);
-            dot[j] = fmaf(v[2], bf16_lo(yr.y), dot[j]);
-            dot[j] = fmaf(v[3], bf16_hi(yr.y), dot[j]);
-            dot[j] = fmaf(v[4], bf16_lo(yr.z), dot[j]);
-            dot[j] = fmaf(v[5], bf16_hi(yr.z), dot[j]);
-            dot[j] = fmaf(v[6], bf16_lo(yr.w), dot[j]);
-            dot[j] = fmaf(v[7], bf16_hi(yr.w), dot[j]);
-            if (dyq) {
-                TileScale ts = tile_scale(fabsf(wj) * am);
-                uint2 o;
-                o.x = cvt_e4m3x4((wj * v[0]) * ts.inv, (wj * v[1]) * ts.inv, (wj * v[2]) * ts.inv,
-                                 (wj * v[3]) * ts.inv);
-                o.y = cvt_e4m3x4((wj * v[4]) * ts.inv, (wj * v[5]) * ts.inv, (wj * v[6]) * ts.inv,
-                                 (wj * v[7]) * ts.inv);
-                *reinterpret_cast<uint2*>(dyq + r * d + col) = o;
-                if (sub == 0) dyq_s[tile * row_cap + r] = ts.s;  // K-block-major scales
-            }
-        }
-    }
     const int wave = threadIdx.x >> 6;
+    const int ntile = d >> 7;
+    for (int t0 = 0; t0 < ntile; t0 += (CBLOCK / 16) * TPG) {
+        float v[TPG][8], am[TPG];
 #pragma unroll
-    for (int j = 0; j < CMAXK; ++j) {
-        float s = group_sum<64>(dot[j]);
-        if ((threadIdx.x & 63) == 0) part[wave][j] = s;
+        for (int q = 0; q < TPG; ++q) {
+            const int tile = t0 + q * (CBLOCK / 16) + grp;
+            uint4 raw = make_uint4(0, 0, 0, 0);
+            if (tile < ntile) raw = *reinterpret_cast<const uint4*>(dy + t * d + (int64_t)tile * 128 + sub * 8);
+            v[q][0] = bf16_lo(raw.x); v[q][1] = bf16_hi(raw.x);
+            v[q][2] = bf16_lo(raw.y); v[q][3] = bf16_hi(raw.y);
+            v[q][4] = bf16_lo(raw.z); v[q][5] = bf16_hi(raw.z);
+            v[q][6] = bf16_lo(raw.w); v[q][7] = bf16_hi(raw.w);
+        }
+#pragma unroll
+        for (int q = 0; q < TPG; ++q) {
+            float m = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[q][i]));
+            am[q] = group_max<16>(m);
+        }
+        // one body for all slots (kept rolled: the quantiser makes it long)
+#pragma unroll 1
+        for (int j = 0; j < k; ++j) {
+            const int64_t r = pair_row[t * k + j];  // uniform
+            float dot = 0.f;
+            if (r >= 0) {
+                const float wj = w[t * k + j];
+                uint4 ys[TPG];
+#pragma unroll
+                for (int q = 0; q < TPG; ++q) {
+                    const int tile = t0 + q * (CBLOCK / 16) + grp;
+                    if (tile < ntile)
+                        ys[q] = *reinterpret_cast<const uint4*>(y_perm + r * d + (int64_t)tile * 128 + sub * 8);
+                }
+#pragma unroll
+                for (int q = 0; q < TPG; ++q) {
+                    const int tile = t0 + q * (CBLOCK / 16) + grp;
+                    if (tile >= ntile) continue;
+                    const int64_t col = (int64_t)tile * 128 + sub * 8;
+                    const uint4 yr = ys[q];
+                    dot = fmaf(v[q][0], bf16_lo(yr.x), dot);
+                    dot = fmaf(v[q][1], bf16_hi(yr.x), dot);
+                    dot = fmaf(v[q][2], bf16_lo(yr.y), dot);
+                    dot = fmaf(v[q][3], bf16_hi(yr.y), dot);
+                    dot = fmaf(v[q][4], bf16_lo(yr.z), dot);
+                    dot = fmaf(v[q][5], bf16_hi(yr.z), dot);
+                    dot = fmaf(v[q][6], bf16_lo(yr.w), dot);
+                    dot = fmaf(v[q][7], bf16_hi(yr.w), dot);
+                    if (dyq) {
+                        const TileScale ts = tile_scale(fabsf(wj) * am[q]);
+                        uint2 o;
+                        o.x = cvt_e4m3x4((wj * v[q][0]) * ts.inv, (wj * v[q][1]) * ts.inv, (wj * v[q][2]) * ts.inv,
+                                         (wj * v[q][3]) * ts.inv);
+                        o.y = cvt_e4m3x4((wj * v[q][4]) * ts.inv, (wj * v[q][5]) * ts.inv, (wj * v[q][6]) * ts.inv,
+                                         (wj * v[q][7]) * ts.inv);
+                        *reinterpret_cast<uint2*>(dyq + r * d + col) = o;
+                        if (sub == 0) dyq_s[tile * row_cap + r] = ts.s;  // K-block-major scales
+                    }
+                }
+            }
+            // this pass's partial of <dy, Y_r>, summed over the block's lanes
+            const float s = group_sum<64>(dot);
+            if ((threadIdx.x & 63) == 0) part[wave][j] = (t0 == 0 ? 0.f : part[wave][j]) + s;
+        }
     }
     __syncthreads();
     if (threadIdx.x < k) {
