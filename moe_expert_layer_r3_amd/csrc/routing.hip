@@ -73,6 +73,69 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     }
 }
 
+// Sixteen lanes per token row, for E <= 16 * VPL <= 256: lane l of a group
+// holds logits VPL*l .. VPL*l + VPL - 1 (a contiguous run), and k rounds of a
+// 16-lane arg-max under the same key (value desc, id asc) pick the slots in
+// order; a round is VPL local compares and four shuffles instead of six.
+template <int VPL>
+__global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                     int k, int32_t* __restrict__ ids, float* __restrict__ w,
+                                                     int32_t* __restrict__ rec, int64_t rec_stride, int64_t s0) {
+    const int lane = threadIdx.x & 15;
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4);
+    // every lane takes part in the shuffles; rows past T compute on row 0 and store nothing
+    const bool live = row < T;
+    const float* src = logits + (live ? row : 0) * E;
+    float v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int e = lane * VPL + i;
+        v[i] = e < E ? src[e] : -INFINITY;
+    }
+    uint32_t taken = 0;
+    float my_val = 0.f;
+    int my_id = 0;
+    for (int s = 0; s < k; ++s) {
+        // lane-local best among untaken values; ids grow with i, so '>' keeps the lower id
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int e = lane * VPL + i;
+            const bool ok = e < E && !((taken >> i) & 1u);
+            if (ok && (bi == 0x7FFFFFFF || v[i] > bv)) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) {
+            const float ov = __shfl_xor(bv, m, 16);
+            const int oi = __shfl_xor(bi, m, 16);
+            const bool take = (oi != 0x7FFFFFFF) && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
+            if (take) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if (bi / VPL == lane) taken |= 1u << (bi % VPL);
+        if (lane == s) {
+            my_val = bv;
+            my_id = bi;
+        }
+    }
+    // softmax over the selection; slot 0 holds the max
+    const float m = __shfl(my_val, 0, 16);
+    const float ex = lane < k ? expf(my_val - m) : 0.f;
+    float sum = 0.f;
+    for (int j = 0; j < k; ++j) sum += __shfl(ex, j, 16);  // ascending slot order
+    if (live && lane < k) {
+        ids[row * k + lane] = my_id;
+        w[row * k + lane] = ex / sum;
+        if (rec) rec[(int64_t)lane * rec_stride + s0 + row] = my_id;
+    }
+}
+
 // One thread per token: read the k recorded ids (coalesced along the sequence
 // for each slot), validate, gather the k logits, softmax.
 __global__ __launch_bounds__(256) void replay_kernel(const int32_t* __restrict__ rec, int k, int64_t S,
@@ -149,6 +212,22 @@ using namespace moe;
 static int launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w,
                        int32_t* rec, int64_t rec_stride, int64_t s0, hipStream_t stream) {
     if (T == 0) return MOE_OK;
+    if (E <= 256) {
+        dim3 grid16((unsigned)((T + 15) / 16)), block16(256);
+        const int vpl = (E + 15) / 16;
+        if (vpl <= 1)
+            topk16_kernel<1><<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+        else if (vpl <= 2)
+            topk16_kernel<2><<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+        else if (vpl <= 4)
+            topk16_kernel<4><<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+        else if (vpl <= 8)
+            topk16_kernel<8><<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+        else
+            topk16_kernel<16><<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+        MOE_LAUNCH_CHECK("topk16_kernel");
+        return MOE_OK;
+    }
     const int waves_per_block = 4;
     dim3 grid((unsigned)((T + waves_per_block - 1) / waves_per_block)), block(64 * waves_per_block);
     int vpl = (E + 63) / 64;
