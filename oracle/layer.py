@@ -73,6 +73,17 @@ class _FP8:
         return gemm.grouped_wgrad(at[0], at[1], bt[0], bt[1], counts, offsets)
 
 
+class _FP8Pow2(_FP8):
+    """The same chain with power-of-two (UE8M0) tile scales everywhere."""
+
+    @staticmethod
+    def weights(W13, W2):
+        return blockfp8.quant_128x128(W13, pow2=True), blockfp8.quant_128x128(W2, pow2=True)
+
+    act = staticmethod(lambda v: blockfp8.quant_1x128(v, pow2=True))
+    act_t = staticmethod(lambda v, real: blockfp8.quant_128x1_t(v, real, pow2=True))
+
+
 class _Exact:
     """Unquantised fp64 chain (for the autograd pin)."""
     r32 = staticmethod(lambda v: np.asarray(v, dtype=np.float64))
@@ -119,15 +130,21 @@ class _Exact:
         return out
 
 
-def quantize_weights(W13, W2):
-    """128x128 FP8 weights: ((W13q, W13s), (W2q, W2s))."""
-    return _FP8.weights(W13, W2)
+def _chain(exact, pow2):
+    return _Exact if exact else (_FP8Pow2 if pow2 else _FP8)
 
 
-def forward(x, ids, w, e0, L, wq, exact=False):
+def quantize_weights(W13, W2, pow2=False):
+    """128x128 FP8 weights: ((W13q, W13s), (W2q, W2s)); pow2 for power-of-two scales."""
+    return _chain(False, pow2).weights(W13, W2)
+
+
+def forward(x, ids, w, e0, L, wq, exact=False, pow2=False):
     """x [T, d] bf16 values, ids [T, k], gates w [T, k]; wq from quantize_weights
-    (or the fp64 weights when exact).  Returns a dict of every intermediate."""
-    B = _Exact if exact else _FP8
+    (or the fp64 weights when exact).  pow2: every activation tile scale is a
+    power of two (the weights must be quantised the same way).  Returns a dict
+    of every intermediate."""
+    B = _chain(exact, pow2)
     x = np.asarray(x, dtype=np.float64)
     T, k = np.asarray(ids).shape
     counts, offsets, row_pair, pair_row = dispatch.permute_index(ids, e0, L)
@@ -154,9 +171,9 @@ def _combine_exact(Y, pair_row, w):
     return y
 
 
-def backward(fw, dy, ids, w, E, wq, exact=False):
+def backward(fw, dy, ids, w, E, wq, exact=False, pow2=False):
     """Training backward of ``forward``'s result ``fw`` for upstream gradient dy [T, d]."""
-    B = _Exact if exact else _FP8
+    B = _chain(exact, pow2)
     dy = np.asarray(dy, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
     k = fw["k"]
