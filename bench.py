@@ -10,9 +10,12 @@ already resident in HBM when timing starts.
 
 Further legs, reported as sub-objects of the same JSON line:
   hotspot  the same forward with Zipf-skewed routing (unequal expert loads)
+  pow2     the headline forward with power-of-two (UE8M0) tile scales, which
+           the block-scaled MFMA applies itself (no VALU rescale)
   train    forward + backward at T=16384 (dgrad and wgrad GEMMs on FP8 operands
            re-quantised along their contraction axis), weights re-quantised
            every step (the step time is also given without that part)
+  train_pow2  the same step with power-of-two tile scales throughout
   replay   Router Replay of a recorded [4, 8, 131072] id tensor: every layer's
            131072 tokens in 16384-token chunks, each layer with its own weights
 
@@ -43,8 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ep8", choices=["ep8", "hotspot"],
                     help="workload of the headline forward step")
-    ap.add_argument("--legs", default="hotspot,train,replay",
-                    help="comma-separated extra legs (hotspot, train, replay) or 'none'")
+    ap.add_argument("--legs", default="hotspot,pow2,train,train_pow2,replay",
+                    help="comma-separated extra legs (hotspot, pow2, train, train_pow2, replay) or 'none'")
     ap.add_argument("--train-steps", type=int, default=5)
     ap.add_argument("--replay-passes", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -148,7 +151,7 @@ def free():
 
 # ---------------------------------------------------------------- forward leg
 
-def forward_leg(wl, steps, warmup, dev):
+def forward_leg(wl, steps, warmup, dev, pow2=False):
     from moe_expert_layer_r3_amd import synth
     from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights, weight_buffers
 
@@ -162,19 +165,19 @@ def forward_leg(wl, steps, warmup, dev):
 
     # weight quantisation (once per weight version), timed on its own
     wts = weight_buffers(wl.L, wl.d, wl.f, dev)
-    quantize_weights(W13_d, W2_d, out=wts)
+    quantize_weights(W13_d, W2_d, out=wts, pow2=pow2)
     torch.cuda.synchronize()
     qe0, qe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     qe0.record()
     for _ in range(3):
-        quantize_weights(W13_d, W2_d, out=wts)
+        quantize_weights(W13_d, W2_d, out=wts, pow2=pow2)
     qe1.record()
     torch.cuda.synchronize()
     wquant_ms = qe0.elapsed_time(qe1) / 3
     del W13_d, W2_d
     free()
 
-    plan = ForwardPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev)
+    plan = ForwardPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev, pow2=pow2)
     for _ in range(warmup):
         plan.forward(x_d, lg_d, wts)
     ev = stage_events(plan.STAGES, steps)
@@ -209,7 +212,7 @@ def forward_leg(wl, steps, warmup, dev):
 
 # ---------------------------------------------------------------- training leg
 
-def train_leg(steps, warmup, dev):
+def train_leg(steps, warmup, dev, pow2=False):
     from moe_expert_layer_r3_amd import synth
     from moe_expert_layer_r3_amd.layer import TrainPlan, quantize_weights, weight_buffers
 
@@ -220,12 +223,12 @@ def train_leg(steps, warmup, dev):
     W13_d = synth.weights(wl, "w13").to(dev)
     W2_d = synth.weights(wl, "w2").to(dev)
     wts = weight_buffers(wl.L, wl.d, wl.f, dev, transpose=True)
-    plan = TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev)
+    plan = TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev, pow2=pow2)
 
     def step(events=None):
         if events is not None:
             events["weight_quant"][0].record()
-        quantize_weights(W13_d, W2_d, transpose=True, out=wts)
+        quantize_weights(W13_d, W2_d, transpose=True, out=wts, pow2=pow2)
         if events is not None:
             events["weight_quant"][1].record()
         plan.forward(x_d, lg_d, wts, events=events)
@@ -255,7 +258,8 @@ def train_leg(steps, warmup, dev):
     top = max(fl, key=lambda n: kern[n])
     res = {
         "workload": f"train: T={wl.T}, d={wl.d}, f={wl.f}, {wl.L} of {wl.E} experts local, top-{wl.k}, "
-                    "forward + backward, weights re-quantised each step",
+                    "forward + backward, weights re-quantised each step"
+                    + (", power-of-two (UE8M0) tile scales" if pow2 else ""),
         "tokens_per_s": wl.T / (ms * 1e-3),
         "ms_per_step": ms,
         "ms_per_step_excl_weight_quant": ms - kern["weight_quant"],
@@ -394,7 +398,7 @@ def main():
         "config": {"workload": f"{wl.name}: one EP=8 share of a 256-expert top-8 MoE layer forward",
                    "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "local_experts": wl.L, "top_k": wl.k,
                    "local_pairs": head["local_pairs"]},
-        "roofline": {"bound": "hbm", "kernel": "grouped GEMM1 + SwiGLU + quant (gemm_fp8_kernel<256,1>)",
+        "roofline": {"bound": "hbm", "kernel": "grouped GEMM1 + SwiGLU + quant (gemm_fp8_kernel<256,1,false>)",
                      "achieved": g1["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": g1["gbs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic(wl.name)},
         "gemm_tflops": head["gemm_tflops"],
@@ -413,8 +417,15 @@ def main():
             r, _ = forward_leg(synth.WORKLOADS["hotspot"], args.steps, args.warmup, dev)
             r["workload"] = "hotspot: ep8 shape, logits biased -1.2 ln(e+1) (expert 0 hottest), forward"
             out["legs"]["hotspot"] = r
+        elif leg == "pow2":
+            r, _ = forward_leg(wl, args.steps, args.warmup, dev, pow2=True)
+            r["workload"] = (f"{wl.name} forward with power-of-two (UE8M0) tile scales applied by the "
+                             "block-scaled MFMA (a variant; the headline uses fp32 scales)")
+            out["legs"]["pow2"] = r
         elif leg == "train":
             out["legs"]["train"] = train_leg(args.train_steps, 2, dev)
+        elif leg == "train_pow2":
+            out["legs"]["train_pow2"] = train_leg(args.train_steps, 2, dev, pow2=True)
         elif leg == "replay":
             out["legs"]["replay"] = replay_leg(args.replay_passes, dev)
         else:

@@ -130,17 +130,26 @@ int moe_permute_workspace(int64_t T, int32_t k, int32_t L, size_t* bytes);
  *                          xq [row_cap, d] u8, xq_s [d/128, row_cap] fp32: scales
  *                          are stored K-block-major, the layout the GEMM reads)
  * Padding rows of x_perm / xq / xq_s are not written.
+ * quant_flags: 0, or MOE_SCALE_POW2 for power-of-two xq_s scales (below).
  * ws: device workspace of at least moe_permute_workspace() bytes.            */
 int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L,
                 int64_t row_cap, int32_t* counts, int32_t* offsets,
                 int32_t* row_pair, int32_t* pair_row,
                 const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq, float* xq_s,
-                void* ws, size_t ws_bytes, int32_t* dev_status, hipStream_t stream);
+                int32_t quant_flags, void* ws, size_t ws_bytes, int32_t* dev_status,
+                hipStream_t stream);
 
 /* ---- block-scaled FP8 quantisation [FP8] -------------------------------- */
 
 enum { MOE_TILE_1x128 = 0, MOE_TILE_128x128 = 1 };
 enum { MOE_SRC_BF16 = 0, MOE_SRC_F32 = 1 };
+/* OR'ed into moe_quant_fp8's tile, moe_permute's quant_flags and
+ * moe_grouped_gemm_fp8's epilogue: power-of-two (UE8M0) scales.  The scale of
+ * a tile with a = max(max|v|, 2^-40) is s = 2^e, e the least integer with
+ * a <= 448 * 2^e, and inv = 2^-e (both exact), in place of s = a/448.  The
+ * scales stay fp32 values in the same layouts; the GEMM then applies them as
+ * E8M0 exponents inside the matrix instruction.                              */
+enum { MOE_SCALE_POW2 = 0x100 };
 
 /* Quantise src viewed as `groups` matrices of [rows, cols] (row stride ld
  * elements, group stride rows*ld) to OCP e4m3 with one fp32 scale per tile:
@@ -167,10 +176,12 @@ int moe_quant_fp8(const void* src, int32_t src_type, int64_t groups, int64_t row
  * block lies inside one expert because segments are 128-aligned).
  *   src [T, cols] bf16;  qT [row_cap/128, cols, 128] u8 (block-transposed);
  *   sT [row_cap/128, cols] fp32 (token-block-major scales, the layout the wgrad
- *   GEMM reads).  Token blocks at and past offsets[L]/128 are left unchanged. */
+ *   GEMM reads).  Token blocks at and past offsets[L]/128 are left unchanged.
+ * flags: 0, or MOE_SCALE_POW2 for power-of-two scales.                       */
 int moe_quant_fp8_rows_t(const uint16_t* src, const float* w, const int32_t* row_pair,
                          const int32_t* offsets, int32_t L, int64_t row_cap, int32_t k,
-                         int64_t cols, uint8_t* qT, float* sT, hipStream_t stream);
+                         int64_t cols, uint8_t* qT, float* sT, int32_t flags,
+                         hipStream_t stream);
 
 /* ---- grouped GEMM [FP8] ------------------------------------------------- */
 
@@ -193,7 +204,11 @@ enum {
  *   tile share contiguous scales per K block); b [L, N, K] e4m3 (weights [out, in];
  *   the dgrad products pass the transposed weights from moe_quant_fp8's qT),
  *   b_s [L, N/128, K/128].  K, N multiples of 128.  Padding rows of the outputs
- *   are not written.  Rows past row_cap are never touched.                   */
+ *   are not written.  Rows past row_cap are never touched.
+ * epilogue | MOE_SCALE_POW2: every a_s and b_s value must be a power of two in
+ *   [2^-126, 2^127] (as the MOE_SCALE_POW2 quantisers write them); the matrix
+ *   instruction applies them as E8M0 exponents (any mantissa bits are
+ *   ignored), and the SwiGLU epilogues quantise h with power-of-two scales.  */
 int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* b, const float* b_s,
                          const int32_t* counts, const int32_t* offsets, int32_t L,
                          int64_t row_cap, int32_t N, int32_t K, int32_t epilogue,
@@ -208,11 +223,13 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* b, c
  *   aT [row_cap/128, M, 128] e4m3 (block-transposed), aT_s [row_cap/128, M];
  *   bT [row_cap/128, N, 128], bT_s [row_cap/128, N] (from moe_quant_fp8_rows_t
  *   or moe_swiglu_backward); dW [L, M, N] bf16.  row_cap < 2^31.
- *   An expert with no rows gets dW[e] = 0.  M, N multiples of 128.           */
+ *   An expert with no rows gets dW[e] = 0.  M, N multiples of 128.
+ * flags MOE_SCALE_POW2: every aT_s and bT_s value is a power of two in
+ *   [2^-126, 2^127], applied by the matrix instruction as E8M0 exponents.     */
 int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8_t* bT,
                                const float* bT_s, const int32_t* offsets, int32_t L,
                                int64_t row_cap, int32_t M, int32_t N, uint16_t* dW,
-                               hipStream_t stream);
+                               int32_t flags, hipStream_t stream);
 
 /* ---- SwiGLU backward [FP8] --------------------------------------------- */
 
@@ -234,12 +251,13 @@ int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8
  *                                                      the fp32 values quantised
  * Padding rows (row_pair < 0) are 0 in the 128x1 tiles and are not written in
  * the row-major outputs; rows at and past offsets[L] are not touched at all.
- *   dH [row_cap, f] fp32, gu [row_cap, 2f] bf16, row_pair [row_cap]; f % 128 == 0. */
+ *   dH [row_cap, f] fp32, gu [row_cap, 2f] bf16, row_pair [row_cap]; f % 128 == 0.
+ * flags: 0, or MOE_SCALE_POW2 for power-of-two scales on every output.        */
 int moe_swiglu_backward(const float* dH, const uint16_t* gu, const int32_t* row_pair,
                         const int32_t* offsets, int32_t L, int64_t row_cap, int32_t f,
                         uint8_t* dgu_q, float* dgu_s, uint8_t* dgu_qT, float* dgu_sT,
                         uint8_t* h_qT, float* h_sT, float* dgu_f32, float* h_f32,
-                        hipStream_t stream);
+                        int32_t flags, hipStream_t stream);
 
 /* ---- combine [EP] ------------------------------------------------------- */
 
@@ -258,10 +276,12 @@ int moe_unpermute_combine(const uint16_t* y_perm, const int32_t* pair_row, const
  *     d_gate[t, j] = sum_n dy[t, n] * y_perm[r, n]   (fp32; 0 for non-local slots)
  *   dy [T, d] bf16, y_perm [row_cap, d] bf16 (the forward's expert outputs),
  *   pair_row [T, k], w [T, k] fp32, d_gate [T, k] fp32.
- * The 128x1 transposed copy of dY for wgrad comes from moe_quant_fp8_rows_t.   */
+ * The 128x1 transposed copy of dY for wgrad comes from moe_quant_fp8_rows_t.
+ * flags: 0, or MOE_SCALE_POW2 for power-of-two dyq_s scales.                  */
 int moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, const int32_t* pair_row,
                          const float* w, int64_t T, int32_t k, int32_t d, int64_t row_cap,
-                         uint8_t* dyq, float* dyq_s, float* d_gate, hipStream_t stream);
+                         uint8_t* dyq, float* dyq_s, float* d_gate, int32_t flags,
+                         hipStream_t stream);
 
 /* Backward of the softmax over the selected logits (complete when every expert
  * is local; under expert parallelism d_gate must first be summed over GPUs):

@@ -77,6 +77,7 @@ __global__ __launch_bounds__(CBLOCK) void combine_kernel(const uint16_t* __restr
 // partial dot <dy, Y_r> for d_gate.  Per local slot (a uniform branch) the
 // group's Y tile loads are issued together before any is used.
 constexpr int TPG = 7;
+template <bool P2>
 __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __restrict__ dy,
                                                              const uint16_t* __restrict__ y_perm,
                                                              const int32_t* __restrict__ pair_row,
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
                     dot = fmaf(v[q][6], bf16_lo(yr.w), dot);
                     dot = fmaf(v[q][7], bf16_hi(yr.w), dot);
                     if (dyq) {
-                        const TileScale ts = tile_scale(fabsf(wj) * am[q]);
+                        const TileScale ts = tile_scale_t<P2>(fabsf(wj) * am[q]);
                         uint2 o;
                         o.x = cvt_e4m3x4((wj * v[q][0]) * ts.inv, (wj * v[q][1]) * ts.inv, (wj * v[q][2]) * ts.inv,
                                          (wj * v[q][3]) * ts.inv);
@@ -179,15 +180,18 @@ extern "C" int moe_unpermute_combine(const uint16_t* y_perm, const int32_t* pair
 
 extern "C" int moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, const int32_t* pair_row,
                                     const float* w, int64_t T, int32_t k, int32_t d, int64_t row_cap, uint8_t* dyq,
-                                    float* dyq_s, float* d_gate, hipStream_t stream) {
+                                    float* dyq_s, float* d_gate, int32_t flags, hipStream_t stream) {
+    MOE_REQUIRE(flags == 0 || flags == MOE_SCALE_POW2, MOE_ERR_UNSUPPORTED, "combine_backward: unknown flags 0x%x", flags);
     MOE_REQUIRE(T >= 0 && T <= 0x7FFFFFFF && k >= 1 && k <= CMAXK, MOE_ERR_SHAPE, "combine_backward: bad T/k");
     MOE_REQUIRE(d > 0 && d % 128 == 0, MOE_ERR_SHAPE, "combine_backward: d=%d must be a multiple of 128", d);
     MOE_REQUIRE(row_cap >= 0, MOE_ERR_SHAPE, "combine_backward: bad row_cap");
     if (T == 0) return MOE_OK;
     MOE_REQUIRE(dy && y_perm && pair_row && w && d_gate, MOE_ERR_NULL, "combine_backward: NULL argument");
     MOE_REQUIRE(!dyq == !dyq_s, MOE_ERR_NULL, "combine_backward: dyq and dyq_s go together");
-    combine_bwd_kernel<<<dim3((unsigned)T), dim3(CBLOCK), 0, stream>>>(dy, y_perm, pair_row, w, k, d, dyq, dyq_s,
-                                                                       d_gate, row_cap);
+    auto go = [&](auto kern) {
+        kern<<<dim3((unsigned)T), dim3(CBLOCK), 0, stream>>>(dy, y_perm, pair_row, w, k, d, dyq, dyq_s, d_gate, row_cap);
+    };
+    flags ? go(combine_bwd_kernel<true>) : go(combine_bwd_kernel<false>);
     MOE_LAUNCH_CHECK("combine_bwd_kernel");
     return MOE_OK;
 }

@@ -88,6 +88,28 @@ __device__ __forceinline__ TileScale tile_scale(float amax) {
     return t;
 }
 
+// Power-of-two (UE8M0) variant: s = 2^e with e the smallest integer such that
+// a <= 448 * 2^e.  Writing a = m * 2^E with m in [0.5, 1) (a >= 2^-40 is a
+// normal float: E = biased exponent - 126, m <= 0.875 exactly when the
+// mantissa field is <= 0x600000) and 448 = 0.875 * 2^9 gives e = E - 9 when
+// m <= 0.875, else E - 8.  s and inv = 2^-e are built from their bits (exact).
+__device__ __forceinline__ TileScale tile_scale_pow2(float amax) {
+    const uint32_t u = __float_as_uint(fmaxf(amax, QUANT_EPS));
+    const int E = (int)((u >> 23) & 0xFFu) - 126;
+    const int e = (u & 0x7FFFFFu) <= 0x600000u ? E - 9 : E - 8;
+    TileScale t;
+    t.s = __uint_as_float((uint32_t)(e + 127) << 23);
+    t.inv = __uint_as_float((uint32_t)(127 - e) << 23);
+    return t;
+}
+template <bool POW2>
+__device__ __forceinline__ TileScale tile_scale_t(float amax) {
+    if constexpr (POW2) return tile_scale_pow2(amax);
+    else return tile_scale(amax);
+}
+// E8M0 code of a power-of-two fp32 scale (its biased exponent field)
+__device__ __forceinline__ int e8m0_of(float pow2) { return (int)((__float_as_uint(pow2) >> 23) & 0xFFu); }
+
 // ---------------------------------------------------------------- SwiGLU
 // sigmoid and silu with the hardware exp2 and reciprocal (about 1 ulp each);
 // exp2 overflows to inf for x below about -88, which gives sigmoid = 0

@@ -30,6 +30,11 @@
 //     (measured: GEMM1 at 256 rows per expert 346 -> 313 us).  Only the order
 //     of the fp32 block sums changes.
 //   * epilogues write straight from registers.
+//   * power-of-two scales (P2): every scale is 2^e, so sA*sB needs no fp32
+//     multiply: the MFMA takes the two E8M0 exponents (one per operand row)
+//     and accumulates the scaled block product into the fp32 accumulator
+//     itself.  No partial waits for a VALU rescale, and the ring of raw
+//     partials is gone.
 #include "mfma_common.hpp"
 
 namespace moe {
@@ -78,7 +83,7 @@ struct GemmSmem {
     static constexpr int TOTAL = NSTAGE * STAGE;
 };
 
-template <int BN, int EPI>
+template <int BN, int EPI, bool P2>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     using SM = GemmSmem<BN>;
     constexpr int WN = BN / 4;        // wave tile columns
@@ -299,6 +304,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         v8i af[4], bfr[NI];   // fragments of one K block
         float sc0[4], sc1[4]; // sA * sB of that block per m-subtile (sc1: the U half of a SwiGLU tile)
         v4f ring[4];          // raw MFMA partials awaiting their rescale (4 in flight)
+        int ea[4], eb0 = 127, eb1 = 127;  // P2: E8M0 codes of sA per m-subtile and of sB
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -310,6 +316,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         // rescale-accumulate of the last n-subtile's partials, left in the ring
         // by the previous compute
         auto flush = [&]() {
+            if constexpr (P2) return;
             constexpr bool second = is_swiglu(EPI) && (NI - 1) >= NI / 2;
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) acc[mi][NI - 1] += ring[mi] * (second ? sc1[mi] : sc0[mi]);
@@ -340,14 +347,22 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
             // element values go through plain integers: __builtin_bit_cast of an
             // ext_vector element lvalue reads element 0 with this compiler
             const uint32_t sbx = sbv.x, sby = sbv.y;
-            const float sb0 = __uint_as_float(second_blk ? sby : sbx);
-            const float sb1 = __uint_as_float(sby);
             const uint32_t sav[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+            if constexpr (P2) {
+                // positive powers of two: the E8M0 code is the exponent field
+                eb0 = (int)((second_blk ? sby : sbx) >> 23);
+                eb1 = (int)(sby >> 23);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const float sa = __uint_as_float(sav[mi]);
-                sc0[mi] = sa * sb0;
-                if constexpr (is_swiglu(EPI)) sc1[mi] = sa * sb1;
+                for (int mi = 0; mi < 4; ++mi) ea[mi] = (int)(sav[mi] >> 23);
+            } else {
+                const float sb0 = __uint_as_float(second_blk ? sby : sbx);
+                const float sb1 = __uint_as_float(sby);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    const float sa = __uint_as_float(sav[mi]);
+                    sc0[mi] = sa * sb0;
+                    if constexpr (is_swiglu(EPI)) sc1[mi] = sa * sb1;
+                }
             }
             wait_lgkm0();  // this wave's reads of the stage are complete before the next barrier
         };
@@ -358,6 +373,15 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         // between a result and its use.  The last n-subtile's partials stay
         // in the ring for the next flush.
         auto compute = [&]() {
+            if constexpr (P2) {
+                static_for<0, 4 * NI>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    constexpr int ni = j / 4, mi = j % 4;
+                    constexpr bool second = is_swiglu(EPI) && ni >= NI / 2;
+                    acc[mi][ni] = mfma16x16x128_e8m0(bfr[ni], af[mi], acc[mi][ni], second ? eb1 : eb0, ea[mi]);
+                });
+                return;
+            }
             static_for<0, 4 * NI>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 constexpr int ni = j / 4, mi = j % 4;
@@ -510,7 +534,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
                     const int64_t r = ep.row0 + rt;
                     const float am = fmaxf(fmaxf(rowmax[0][rt], rowmax[1][rt]), fmaxf(rowmax[2][rt], rowmax[3][rt]));
                     if (r >= ep.real_end) continue;
-                    const TileScale ts = tile_scale(am);
+                    const TileScale ts = tile_scale_t<P2>(am);
                     if (lg == 0 && wn == 0) g.out_s[(int64_t)ep.nt * g.row_cap + r] = ts.s;
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni) {
@@ -535,10 +559,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 }
 
 template <int BN, int EPI>
-static int launch_gemm(const GemmArgs& a, hipStream_t stream) {
+static int launch_gemm(const GemmArgs& a, bool p2, hipStream_t stream) {
     const int ncu = num_cus();
     const int grid = (ncu + 7) / 8 * 8;  // one 512-thread block per CU (LDS bound), persistent
-    gemm_fp8_kernel<BN, EPI><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+    if (p2)
+        gemm_fp8_kernel<BN, EPI, true><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+    else
+        gemm_fp8_kernel<BN, EPI, false><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
     MOE_LAUNCH_CHECK("gemm_fp8_kernel");
     return MOE_OK;
 }
@@ -552,6 +579,8 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
                                     int32_t N, int32_t K, int32_t epilogue, const uint16_t* epi_in, void* out,
                                     float* out_s, void* out2, float* out2_s, void* out3, float* out3_s,
                                     hipStream_t stream) {
+    const bool p2 = (epilogue & MOE_SCALE_POW2) != 0;
+    epilogue &= ~MOE_SCALE_POW2;
     MOE_REQUIRE(L >= 1 && L <= GMAXL, MOE_ERR_SHAPE, "grouped_gemm: L=%d outside [1, 1024]", L);
     MOE_REQUIRE(row_cap >= 0 && row_cap % GBM == 0 && row_cap <= 0x7FFFFFFF, MOE_ERR_SHAPE,
                 "grouped_gemm: row_cap=%lld must be a multiple of 128", (long long)row_cap);
@@ -573,17 +602,17 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
     const bool wide = N % 256 == 0;
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
-            return wide ? launch_gemm<256, MOE_EPI_STORE_BF16>(ga, stream)
-                        : launch_gemm<128, MOE_EPI_STORE_BF16>(ga, stream);
+            return wide ? launch_gemm<256, MOE_EPI_STORE_BF16>(ga, p2, stream)
+                        : launch_gemm<128, MOE_EPI_STORE_BF16>(ga, p2, stream);
         case MOE_EPI_STORE_F32:
-            return wide ? launch_gemm<256, MOE_EPI_STORE_F32>(ga, stream)
-                        : launch_gemm<128, MOE_EPI_STORE_F32>(ga, stream);
+            return wide ? launch_gemm<256, MOE_EPI_STORE_F32>(ga, p2, stream)
+                        : launch_gemm<128, MOE_EPI_STORE_F32>(ga, p2, stream);
         case MOE_EPI_SWIGLU_Q8:
-            return launch_gemm<256, MOE_EPI_SWIGLU_Q8>(ga, stream);
+            return launch_gemm<256, MOE_EPI_SWIGLU_Q8>(ga, p2, stream);
         case MOE_EPI_SWIGLU_Q8_SAVE:
-            return launch_gemm<256, MOE_EPI_SWIGLU_Q8_SAVE>(ga, stream);
+            return launch_gemm<256, MOE_EPI_SWIGLU_Q8_SAVE>(ga, p2, stream);
         case MOE_EPI_SWIGLU_F32:
-            return launch_gemm<256, MOE_EPI_SWIGLU_F32>(ga, stream);
+            return launch_gemm<256, MOE_EPI_SWIGLU_F32>(ga, p2, stream);
     }
     return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm: epilogue %d", epilogue);
 }

@@ -52,6 +52,7 @@ __device__ __forceinline__ void wait_lgkm0() {
 
 typedef const __attribute__((address_space(3))) u32x4* lds_u32x4_ptr;
 typedef const __attribute__((address_space(3))) v2u* lds_v2u_ptr;
+typedef const __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
 
 // Plain LDS loads (the compiler tracks their lgkmcnt).  `base` comes out of an
 // opaque move placed after the stage's barrier, so no read can be hoisted
@@ -63,6 +64,10 @@ __device__ __forceinline__ u32x4 lds16(uint32_t addr) {
 template <int OFF>
 __device__ __forceinline__ v2u lds8(uint32_t addr) {
     return *(lds_v2u_ptr)(uintptr_t)(addr + OFF);
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t lds4(uint32_t addr) {
+    return *(lds_u32_ptr)(uintptr_t)(addr + OFF);
 }
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm volatile("" : "+v"(v));
@@ -117,6 +122,12 @@ __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b) {
     // E8M0 127 = 2^0: the hardware block scales are 1, the fp32 scales are
     // applied by the caller
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
+}
+// c + (2^(ea-127) 2^(eb-127)) * (a . b) with the E8M0 block scales applied by
+// the matrix core: ea scales row (lane % 16) of a, eb row (lane % 16) of b
+// (each lane passes the scale of the row whose K chunk it holds)
+__device__ __forceinline__ v4f mfma16x16x128_e8m0(const v8i& a, const v8i& b, const v4f& c, int ea, int eb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
 
 }  // namespace moe

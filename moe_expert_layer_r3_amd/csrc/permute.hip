@@ -193,6 +193,7 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
 constexpr int GQ_THREADS = 256;
 constexpr int GQ_LOADS = 4;
 
+template <bool P2>
 __global__ __launch_bounds__(GQ_THREADS) void gather_quant_kernel(const uint16_t* __restrict__ x, int64_t T,
                                                                   int d, int k,
                                                                   const int32_t* __restrict__ pair_row,
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(GQ_THREADS) void gather_quant_kernel(const uint16_t
 #pragma unroll
                 for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(v[q]));
                 am = group_max<16>(am);
-                const TileScale ts = tile_scale(am);
+                const TileScale ts = tile_scale_t<P2>(am);
                 s = ts.s;
                 packed.x = cvt_e4m3x4(v[0] * ts.inv, v[1] * ts.inv, v[2] * ts.inv, v[3] * ts.inv);
                 packed.y = cvt_e4m3x4(v[4] * ts.inv, v[5] * ts.inv, v[6] * ts.inv, v[7] * ts.inv);
@@ -271,8 +272,9 @@ extern "C" int moe_permute_workspace(int64_t T, int32_t k, int32_t L, size_t* by
 
 extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L, int64_t row_cap,
                            int32_t* counts, int32_t* offsets, int32_t* row_pair, int32_t* pair_row,
-                           const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq, float* xq_s, void* ws,
-                           size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
+                           const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq, float* xq_s,
+                           int32_t quant_flags, void* ws, size_t ws_bytes, int32_t* dev_status,
+                           hipStream_t stream) {
     MOE_REQUIRE(T >= 0 && T <= ((int64_t)1 << 31) / 16, MOE_ERR_SHAPE, "permute: bad T=%lld", (long long)T);
     MOE_REQUIRE(k >= 1 && k <= 16, MOE_ERR_SHAPE, "permute: k=%d outside [1, 16]", k);
     MOE_REQUIRE(L >= 1 && L <= MAXL && e0 >= 0, MOE_ERR_SHAPE, "permute: L=%d outside [1, 1024] or e0<0", L);
@@ -280,6 +282,8 @@ extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0,
                 "permute: row_cap=%lld must be a multiple of 128 below 2^31", (long long)row_cap);
     MOE_REQUIRE(counts && offsets && (T == 0 || (ids && pair_row)) && (row_cap == 0 || row_pair), MOE_ERR_NULL,
                 "permute: NULL ids/counts/offsets/row_pair/pair_row");
+    MOE_REQUIRE(quant_flags == 0 || quant_flags == MOE_SCALE_POW2, MOE_ERR_UNSUPPORTED,
+                "permute: unknown quant_flags 0x%x", quant_flags);
     if (x) {
         MOE_REQUIRE(d > 0 && d % 128 == 0, MOE_ERR_SHAPE, "permute: d=%d must be a positive multiple of 128", d);
         MOE_REQUIRE(x_perm || xq, MOE_ERR_NULL, "permute: x given but neither x_perm nor xq");
@@ -307,8 +311,10 @@ extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0,
         MOE_LAUNCH_CHECK("perm_scatter_kernel");
     }
     if (x && T > 0) {
-        gather_quant_kernel<<<dim3((unsigned)T), dim3(GQ_THREADS), 0, stream>>>(x, T, d, k, pair_row, x_perm, xq,
-                                                                               xq_s, row_cap);
+        auto go = [&](auto kern) {
+            kern<<<dim3((unsigned)T), dim3(GQ_THREADS), 0, stream>>>(x, T, d, k, pair_row, x_perm, xq, xq_s, row_cap);
+        };
+        quant_flags ? go(gather_quant_kernel<true>) : go(gather_quant_kernel<false>);
         MOE_LAUNCH_CHECK("gather_quant_kernel");
     }
     return MOE_OK;

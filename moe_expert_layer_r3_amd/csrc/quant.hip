@@ -1,6 +1,8 @@
 // Block-scaled FP8 e4m3 quantisation ("RL at 1T scale", section "FP8 Training":
 // DeepSeek-V3 style block scaling).  Per tile: a = max(max|v|, 2^-40),
 // inv = 448/a, s = a/448 (fp32, correctly rounded), q = e4m3_rne_sat(fp32(v*inv)).
+// With P2 the scale is the power of two s = 2^e, e the least integer with
+// a <= 448 * 2^e (a UE8M0 code), and inv = 2^-e exactly.
 #include "common.hpp"
 
 namespace moe {
@@ -22,7 +24,7 @@ __device__ __forceinline__ void load8(const void* src, int64_t idx, float v[8]) 
 }
 
 // 1x128: a work item is one 128-wide tile of one row, 16 lanes x 8 values.
-template <bool F32>
+template <bool F32, bool P2>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ src, int64_t nrows, int64_t cols,
                                                           int64_t ld, uint8_t* __restrict__ q,
                                                           float* __restrict__ s) {
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
     am = group_max<16>(am);
-    TileScale ts = tile_scale(am);
+    TileScale ts = tile_scale_t<P2>(am);
     uint2 out;
     out.x = cvt_e4m3x4(v[0] * ts.inv, v[1] * ts.inv, v[2] * ts.inv, v[3] * ts.inv);
     out.y = cvt_e4m3x4(v[4] * ts.inv, v[5] * ts.inv, v[6] * ts.inv, v[7] * ts.inv);
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
 // cg = l % 16 (16 lanes read a row's 256 bytes).  The optional transposed copy
 // goes through an LDS tile: a column's codes for the thread's 8 consecutive
 // rows are one 8-byte word.
-template <bool F32>
+template <bool F32, bool P2>
 __global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restrict__ src, int64_t rows,
                                                             int64_t cols, int64_t ld, uint8_t* __restrict__ q,
                                                             float* __restrict__ s, uint8_t* __restrict__ qT,
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restri
     if (lane == 0) wmax[wave] = am;
     __syncthreads();
     am = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const TileScale ts = tile_scale(am);
+    const TileScale ts = tile_scale_t<P2>(am);
     const int64_t qbase = g * rows * cols;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -122,6 +124,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restri
 //   * a column's codes for the thread's 8 consecutive rows are one 8-byte word
 //     of the transposed LDS tile, which leaves as 16-byte stores of full
 //     128-byte columns.
+template <bool P2>
 __global__ __launch_bounds__(256) void quant_rows_t_kernel(const uint16_t* __restrict__ src,
                                                            const float* __restrict__ w,
                                                            const int32_t* __restrict__ row_pair,
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(256) void quant_rows_t_kernel(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float m = fmaxf(fmaxf(cmax[0][c8 + i], cmax[1][c8 + i]), fmaxf(cmax[2][c8 + i], cmax[3][c8 + i]));
-        const TileScale ts = tile_scale(m);
+        const TileScale ts = tile_scale_t<P2>(m);
         inv[i] = ts.inv;
         if (wave == 0 && lane < 16) sT[b * cols + cc * 128 + c8 + i] = ts.s;  // token-block-major scales
     }
@@ -208,6 +211,8 @@ extern "C" int moe_quant_fp8(const void* src, int32_t src_type, int64_t groups, 
                              hipStream_t stream) {
     MOE_REQUIRE(src_type == MOE_SRC_BF16 || src_type == MOE_SRC_F32, MOE_ERR_UNSUPPORTED,
                 "quant_fp8: unknown src_type %d", src_type);
+    const bool p2 = (tile & MOE_SCALE_POW2) != 0;
+    tile &= ~MOE_SCALE_POW2;
     MOE_REQUIRE(tile == MOE_TILE_1x128 || tile == MOE_TILE_128x128, MOE_ERR_UNSUPPORTED,
                 "quant_fp8: unknown tile %d", tile);
     MOE_REQUIRE(groups >= 0 && rows >= 0 && cols >= 0 && cols % 128 == 0, MOE_ERR_SHAPE,
@@ -227,18 +232,20 @@ extern "C" int moe_quant_fp8(const void* src, int32_t src_type, int64_t groups, 
         const int64_t nrows = groups * rows;
         const int64_t threads = nrows * (cols / 128) * 16;
         dim3 grid((unsigned)((threads + 255) / 256));
+        auto go = [&](auto kern) { kern<<<grid, 256, 0, stream>>>(src, nrows, cols, ld, q, scales); };
         if (f32)
-            quant_1x128_kernel<true><<<grid, 256, 0, stream>>>(src, nrows, cols, ld, q, scales);
+            p2 ? go(quant_1x128_kernel<true, true>) : go(quant_1x128_kernel<true, false>);
         else
-            quant_1x128_kernel<false><<<grid, 256, 0, stream>>>(src, nrows, cols, ld, q, scales);
+            p2 ? go(quant_1x128_kernel<false, true>) : go(quant_1x128_kernel<false, false>);
         MOE_LAUNCH_CHECK("quant_1x128_kernel");
     } else {
         MOE_REQUIRE(rows / 128 <= 65535 && groups <= 65535, MOE_ERR_SHAPE, "quant_fp8: too many 128x128 tiles");
         dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128), (unsigned)groups);
+        auto go = [&](auto kern) { kern<<<grid, 256, 0, stream>>>(src, rows, cols, ld, q, scales, qT, scalesT); };
         if (f32)
-            quant_128x128_kernel<true><<<grid, 256, 0, stream>>>(src, rows, cols, ld, q, scales, qT, scalesT);
+            p2 ? go(quant_128x128_kernel<true, true>) : go(quant_128x128_kernel<true, false>);
         else
-            quant_128x128_kernel<false><<<grid, 256, 0, stream>>>(src, rows, cols, ld, q, scales, qT, scalesT);
+            p2 ? go(quant_128x128_kernel<false, true>) : go(quant_128x128_kernel<false, false>);
         MOE_LAUNCH_CHECK("quant_128x128_kernel");
     }
     return MOE_OK;
@@ -246,7 +253,8 @@ extern "C" int moe_quant_fp8(const void* src, int32_t src_type, int64_t groups, 
 
 extern "C" int moe_quant_fp8_rows_t(const uint16_t* src, const float* w, const int32_t* row_pair,
                                     const int32_t* offsets, int32_t L, int64_t row_cap, int32_t k, int64_t cols,
-                                    uint8_t* qT, float* sT, hipStream_t stream) {
+                                    uint8_t* qT, float* sT, int32_t flags, hipStream_t stream) {
+    MOE_REQUIRE(flags == 0 || flags == MOE_SCALE_POW2, MOE_ERR_UNSUPPORTED, "quant_fp8_rows_t: unknown flags 0x%x", flags);
     MOE_REQUIRE(L >= 1 && L <= 1024 && k >= 1 && k <= 16, MOE_ERR_SHAPE, "quant_fp8_rows_t: bad L/k");
     MOE_REQUIRE(row_cap >= 0 && row_cap % 128 == 0 && row_cap <= 0x7FFFFFFF, MOE_ERR_SHAPE,
                 "quant_fp8_rows_t: row_cap=%lld must be a multiple of 128", (long long)row_cap);
@@ -256,7 +264,8 @@ extern "C" int moe_quant_fp8_rows_t(const uint16_t* src, const float* w, const i
     MOE_REQUIRE(src && row_pair && offsets && qT && sT, MOE_ERR_NULL, "quant_fp8_rows_t: NULL argument");
     MOE_REQUIRE(row_cap / 128 <= 65535, MOE_ERR_SHAPE, "quant_fp8_rows_t: row_cap too large");
     dim3 grid((unsigned)(cols / 128), (unsigned)(row_cap / 128));
-    quant_rows_t_kernel<<<grid, 256, 0, stream>>>(src, w, row_pair, offsets, L, row_cap, k, cols, qT, sT);
+    auto go = [&](auto kern) { kern<<<grid, 256, 0, stream>>>(src, w, row_pair, offsets, L, row_cap, k, cols, qT, sT); };
+    flags ? go(quant_rows_t_kernel<true>) : go(quant_rows_t_kernel<false>);
     MOE_LAUNCH_CHECK("quant_rows_t_kernel");
     return MOE_OK;
 }

@@ -46,6 +46,7 @@ struct SwigluBwdArgs {
 //   * a column's codes for the thread's 8 consecutive rows are one 8-byte word
 //     of the transposed LDS tile, which leaves as 16-byte stores of full
 //     128-byte columns.
+template <bool P2>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
     __shared__ __attribute__((aligned(16))) float cmax[3][4][128];
     __shared__ __attribute__((aligned(16))) uint8_t tile_t[3][128][128 + 8];
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
         mg = group_max<16>(mg);
         mu = group_max<16>(mu);
         if (!real[j]) continue;
-        const TileScale tg = tile_scale(mg), tu = tile_scale(mu);
+        const TileScale tg = tile_scale_t<P2>(mg), tu = tile_scale_t<P2>(mu);
         uint2 qg, qu;
         qg.x = cvt_e4m3x4(dg[j][0] * tg.inv, dg[j][1] * tg.inv, dg[j][2] * tg.inv, dg[j][3] * tg.inv);
         qg.y = cvt_e4m3x4(dg[j][4] * tg.inv, dg[j][5] * tg.inv, dg[j][6] * tg.inv, dg[j][7] * tg.inv);
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
         for (int i = 0; i < 8; ++i) {
             const float m = fmaxf(fmaxf(cmax[q][0][c8 + i], cmax[q][1][c8 + i]),
                                   fmaxf(cmax[q][2][c8 + i], cmax[q][3][c8 + i]));
-            const TileScale ts = tile_scale(m);
+            const TileScale ts = tile_scale_t<P2>(m);
             if (wave == 0 && lane < 16) {
                 // scales of the transposed tiles, token-block-major: dG at
                 // column c, dU at f + c (of 2f), H at c (of f)
@@ -190,7 +191,8 @@ using namespace moe;
 extern "C" int moe_swiglu_backward(const float* dH, const uint16_t* gu, const int32_t* row_pair,
                                    const int32_t* offsets, int32_t L, int64_t row_cap, int32_t f,
                                    uint8_t* dgu_q, float* dgu_s, uint8_t* dgu_qT, float* dgu_sT, uint8_t* h_qT,
-                                   float* h_sT, float* dgu_f32, float* h_f32, hipStream_t stream) {
+                                   float* h_sT, float* dgu_f32, float* h_f32, int32_t flags, hipStream_t stream) {
+    MOE_REQUIRE(flags == 0 || flags == MOE_SCALE_POW2, MOE_ERR_UNSUPPORTED, "swiglu_backward: unknown flags 0x%x", flags);
     MOE_REQUIRE(L >= 1 && L <= 1024, MOE_ERR_SHAPE, "swiglu_backward: L=%d outside [1, 1024]", L);
     MOE_REQUIRE(row_cap >= 0 && row_cap % 128 == 0 && row_cap <= 0x7FFFFFFF, MOE_ERR_SHAPE,
                 "swiglu_backward: row_cap=%lld must be a multiple of 128", (long long)row_cap);
@@ -202,7 +204,10 @@ extern "C" int moe_swiglu_backward(const float* dH, const uint16_t* gu, const in
     SwigluBwdArgs args{dH, gu, row_pair, offsets, L, row_cap, f, dgu_q, dgu_s, dgu_qT, dgu_sT,
                        h_qT, h_sT, dgu_f32, h_f32};
     const dim3 grid((unsigned)(row_cap / 128), (unsigned)(f / 128));
-    swiglu_bwd_kernel<<<grid, 256, 0, stream>>>(args);
+    if (flags)
+        swiglu_bwd_kernel<true><<<grid, 256, 0, stream>>>(args);
+    else
+        swiglu_bwd_kernel<false><<<grid, 256, 0, stream>>>(args);
     MOE_LAUNCH_CHECK("swiglu_bwd_kernel");
     return MOE_OK;
 }

@@ -35,6 +35,9 @@
 // groups (one of each per SIMD), conflict-free swizzled fragments,
 // weights-first MFMA operand order; both operands carry per-row scales, so the
 // factor of a partial is sA[row] * sB[column], formed as the partial is added.
+// With power-of-two scales (P2) that factor is exactly what the block-scaled
+// MFMA applies per operand row: each lane passes the E8M0 exponents of its A
+// row and its B row, and the MFMA accumulates in place (no rescale on the VALU).
 #include "mfma_common.hpp"
 
 namespace moe {
@@ -81,7 +84,7 @@ __device__ __forceinline__ void wait_younger(int n) {
     else wait_vmcnt<0>();
 }
 
-template <int BN>
+template <int BN, bool P2>
 __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     using SM = WgradSmem<BN>;
     constexpr int WN = BN / 4;             // wave tile columns
@@ -145,7 +148,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     // A scales: the 16 bytes at slot wm*64 + 4*l15 hold rows wm*64 + mi*16 + l15
     // (mi = 0..3); B scales: natural order, 4 consecutive columns per read
     const uint32_t sa_rd = SM::A_BYTES + SM::B_BYTES + (wm * 64 + l15 * 4) * 4;
-    const uint32_t sb_rd = SM::A_BYTES + SM::B_BYTES + SM::SA_BYTES + (wn * WN + 4 * lg) * 4;
+    // (P2: the scale of the B row whose K chunk the lane holds, column wn*WN + ni*16 + l15)
+    const uint32_t sb_rd = SM::A_BYTES + SM::B_BYTES + SM::SA_BYTES + (wn * WN + (P2 ? l15 : 4 * lg)) * 4;
     uint32_t rA0[3], rA1[3], rB0[3], rB1[3], rSA[3], rSB[3];
 #pragma unroll
     for (int st = 0; st < 3; ++st) {
@@ -256,6 +260,11 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     float sa[4];  // A scales of the loaded block (rows of this lane)
     v4f sb[NI];   // B scales of the loaded block (4 columns per n-subtile)
     v4f ring[4];  // raw partials awaiting their rescale
+    int ea[4], eb[NI];  // P2: E8M0 exponents of the lane's A rows and B rows
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) ea[mi] = 127;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) eb[ni] = 127;
     auto clear = [&]() {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
@@ -271,6 +280,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     for (int ni = 0; ni < NI; ++ni) sb[ni] = zero4;
 
     auto flush = [&]() {
+        if constexpr (P2) return;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) acc[mi][NI - 1] += ring[mi] * (sa[mi] * sb[NI - 1]);
     };
@@ -286,9 +296,13 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         const uint32_t psa = rSA[st], psb = rSB[st];
         const u32x4 sa4 = lds16<0>(psa);
         u32x4 sbn[NI];
+        uint32_t sb1[NI];
         static_for<0, NI>([&](auto nc) {
             constexpr int ni = decltype(nc)::value;
-            sbn[ni] = lds16<ni * 64>(psb);
+            if constexpr (P2)
+                sb1[ni] = lds4<ni * 64>(psb);
+            else
+                sbn[ni] = lds16<ni * 64>(psb);
         });
         static_for<0, 4>([&](auto ic) {
             constexpr int mi = decltype(ic)::value;
@@ -300,13 +314,29 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         });
         flush();  // with the previous block's scales
         const uint32_t sav[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+        if constexpr (P2) {
+            // positive powers of two: the E8M0 code is the exponent field
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) sa[mi] = __uint_as_float(sav[mi]);
+            for (int mi = 0; mi < 4; ++mi) ea[mi] = (int)(sav[mi] >> 23);
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) sb[ni] = __builtin_bit_cast(v4f, sbn[ni]);
+            for (int ni = 0; ni < NI; ++ni) eb[ni] = (int)(sb1[ni] >> 23);
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) sa[mi] = __uint_as_float(sav[mi]);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) sb[ni] = __builtin_bit_cast(v4f, sbn[ni]);
+        }
         wait_lgkm0();
     };
     auto compute = [&]() {
+        if constexpr (P2) {
+            static_for<0, 4 * NI>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                constexpr int ni = j / 4, mi = j % 4;
+                acc[mi][ni] = mfma16x16x128_e8m0(bfr[ni], af[mi], acc[mi][ni], eb[ni], ea[mi]);
+            });
+            return;
+        }
         static_for<0, 4 * NI>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             constexpr int ni = j / 4, mi = j % 4;
@@ -462,7 +492,9 @@ using namespace moe;
 
 extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8_t* bT,
                                           const float* bT_s, const int32_t* offsets, int32_t L, int64_t row_cap,
-                                          int32_t M, int32_t N, uint16_t* dW, hipStream_t stream) {
+                                          int32_t M, int32_t N, uint16_t* dW, int32_t flags, hipStream_t stream) {
+    MOE_REQUIRE(flags == 0 || flags == MOE_SCALE_POW2, MOE_ERR_UNSUPPORTED, "grouped_gemm_wgrad: unknown flags 0x%x",
+                flags);
     MOE_REQUIRE(L >= 1 && L <= WMAXL, MOE_ERR_SHAPE, "grouped_gemm_wgrad: L=%d outside [1, %d]", L, WMAXL);
     // segment starts are kept as 32-bit values on the device
     MOE_REQUIRE(row_cap >= 0 && row_cap % WBK == 0 && row_cap < ((int64_t)1 << 31), MOE_ERR_SHAPE,
@@ -474,10 +506,11 @@ extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, 
     MOE_REQUIRE(aT && aT_s && bT && bT_s && offsets && dW, MOE_ERR_NULL, "grouped_gemm_wgrad: NULL argument");
     WgradArgs a{aT, aT_s, bT, bT_s, offsets, L, row_cap, M, N, dW};
     const int grid = (num_cus() + 7) / 8 * 8;  // persistent, one block per CU
+    auto go = [&](auto kern) { kern<<<dim3(grid), dim3(WTHREADS), 0, stream>>>(a); };
     if (N % 256 == 0)
-        wgrad_fp8_kernel<256><<<dim3(grid), dim3(WTHREADS), 0, stream>>>(a);
+        flags ? go(wgrad_fp8_kernel<256, true>) : go(wgrad_fp8_kernel<256, false>);
     else
-        wgrad_fp8_kernel<128><<<dim3(grid), dim3(WTHREADS), 0, stream>>>(a);
+        flags ? go(wgrad_fp8_kernel<128, true>) : go(wgrad_fp8_kernel<128, false>);
     MOE_LAUNCH_CHECK("wgrad_fp8_kernel");
     return MOE_OK;
 }

@@ -24,9 +24,10 @@ def weight_buffers(L, d, f, device="cuda", transpose=False):
     return out
 
 
-def quantize_weights(W13, W2, transpose=False, out=None):
+def quantize_weights(W13, W2, transpose=False, out=None, pow2=False):
     """bf16 W13 [L, 2f, d], W2 [L, d, f] -> dict of FP8 codes and scales (and the
-    transposed copies used by the dgrad GEMMs when ``transpose``), 128x128 tiles.
+    transposed copies used by the dgrad GEMMs when ``transpose``), 128x128 tiles,
+    power-of-two scales when ``pow2``.
     ``out`` (from weight_buffers) receives the result without allocating."""
     L, f2, d = W13.shape
     if out is None:
@@ -36,16 +37,20 @@ def quantize_weights(W13, W2, transpose=False, out=None):
             raise ValueError("weights must be contiguous bf16")
         _, rows, cols = W.shape
         qT, sT = (out[q + "T"], out[s + "T"]) if transpose else (None, None)
-        _call("moe_quant_fp8", _p(W), ops.SRC_BF16, L, rows, cols, cols, ops.TILE_128x128, _p(out[q]), _p(out[s]),
+        tile = ops.TILE_128x128 | (ops.SCALE_POW2 if pow2 else 0)
+        _call("moe_quant_fp8", _p(W), ops.SRC_BF16, L, rows, cols, cols, tile, _p(out[q]), _p(out[s]),
               _p(qT), _p(sT), _stream())
     return out
 
 
 class ForwardPlan:
-    """Device buffers for one forward pass of T tokens."""
+    """Device buffers for one forward pass of T tokens.  pow2: power-of-two
+    (UE8M0) activation scales, applied by the MFMA; the weights must then come
+    from quantize_weights(..., pow2=True)."""
 
-    def __init__(self, T, d, f, E, L, k, e0=0, device="cuda", save_gu=False):
+    def __init__(self, T, d, f, E, L, k, e0=0, device="cuda", save_gu=False, pow2=False):
         self.T, self.d, self.f, self.E, self.L, self.k, self.e0 = T, d, f, E, L, k, e0
+        self.sflag = ops.SCALE_POW2 if pow2 else 0
         self.rcap = ops.row_cap(T, k, L)
         dv = device
         i32, f32, u8, b16 = torch.int32, torch.float32, torch.uint8, torch.bfloat16
@@ -78,17 +83,18 @@ class ForwardPlan:
     def permute(self, x):
         _call("moe_permute", _p(self.ids), self.T, self.k, self.e0, self.L, self.rcap, _p(self.counts),
               _p(self.offsets), _p(self.row_pair), _p(self.pair_row), _p(x), self.d, None, _p(self.xq),
-              _p(self.xq_s), _p(self.ws), self.ws.numel(), _p(self.status), _stream())
+              _p(self.xq_s), self.sflag, _p(self.ws), self.ws.numel(), _p(self.status), _stream())
 
     def gemm1(self, wts):
         epi = ops.EPI_SWIGLU_Q8_SAVE if self.gu is not None else ops.EPI_SWIGLU_Q8
         _call("moe_grouped_gemm_fp8", _p(self.xq), _p(self.xq_s), _p(wts["w13q"]), _p(wts["w13s"]),
-              _p(self.counts), _p(self.offsets), self.L, self.rcap, 2 * self.f, self.d, epi, None,
+              _p(self.counts), _p(self.offsets), self.L, self.rcap, 2 * self.f, self.d, epi | self.sflag, None,
               _p(self.hq), _p(self.hq_s), _p(self.gu), None, None, None, _stream())
 
     def gemm2(self, wts):
         _call("moe_grouped_gemm_fp8", _p(self.hq), _p(self.hq_s), _p(wts["w2q"]), _p(wts["w2s"]),
-              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.d, self.f, ops.EPI_STORE_BF16, None,
+              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.d, self.f, ops.EPI_STORE_BF16 | self.sflag,
+              None,
               _p(self.Y), None, None, None, None, None, _stream())
 
     def combine(self):
@@ -129,8 +135,8 @@ class TrainPlan(ForwardPlan):
       x 128x1 (transposed);  wgrad GEMMs dW2 = dY^T H, dW13 = [dG, dU]^T X
       softmax-over-selection backward -> d_logits."""
 
-    def __init__(self, T, d, f, E, L, k, e0=0, device="cuda"):
-        super().__init__(T, d, f, E, L, k, e0=e0, device=device, save_gu=True)
+    def __init__(self, T, d, f, E, L, k, e0=0, device="cuda", pow2=False):
+        super().__init__(T, d, f, E, L, k, e0=e0, device=device, save_gu=True, pow2=pow2)
         dv = device
         f32, u8, b16 = torch.float32, torch.uint8, torch.bfloat16
         R = self.rcap
@@ -156,27 +162,28 @@ class TrainPlan(ForwardPlan):
 
     def combine_bwd(self, dy):
         _call("moe_combine_backward", _p(dy), _p(self.Y), _p(self.pair_row), _p(self.w), self.T, self.k, self.d,
-              self.rcap, _p(self.dyq), _p(self.dyq_s), _p(self.d_gate), _stream())
+              self.rcap, _p(self.dyq), _p(self.dyq_s), _p(self.d_gate), self.sflag, _stream())
 
     def dy_quant_t(self, dy):
         _call("moe_quant_fp8_rows_t", _p(dy), _p(self.w), _p(self.row_pair), _p(self.offsets), self.L, self.rcap,
-              self.k, self.d, _p(self.dyqT), _p(self.dyqT_s), _stream())
+              self.k, self.d, _p(self.dyqT), _p(self.dyqT_s), self.sflag, _stream())
 
     def dgrad2(self, wts):
         _call("moe_grouped_gemm_fp8", _p(self.dyq), _p(self.dyq_s), _p(wts["w2qT"]), _p(wts["w2sT"]),
-              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.f, self.d, ops.EPI_STORE_F32, None,
+              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.f, self.d, ops.EPI_STORE_F32 | self.sflag,
+              None,
               _p(self.dH), None, None, None, None, None, _stream())
 
     def swiglu_bwd(self):
         s = self.sb
         _call("moe_swiglu_backward", _p(self.dH), _p(self.gu), _p(self.row_pair), _p(self.offsets), self.L,
               self.rcap, self.f, _p(s["dgu_q"]), _p(s["dgu_s"]), _p(s["dgu_qT"]), _p(s["dgu_sT"]),
-              _p(s["h_qT"]), _p(s["h_sT"]), None, None, _stream())
+              _p(s["h_qT"]), _p(s["h_sT"]), None, None, self.sflag, _stream())
 
     def dgrad1(self, wts):
         _call("moe_grouped_gemm_fp8", _p(self.sb["dgu_q"]), _p(self.sb["dgu_s"]), _p(wts["w13qT"]),
               _p(wts["w13sT"]), _p(self.counts), _p(self.offsets), self.L, self.rcap, self.d, 2 * self.f,
-              ops.EPI_STORE_BF16, None, _p(self.dX), None, None, None, None, None, _stream())
+              ops.EPI_STORE_BF16 | self.sflag, None, _p(self.dX), None, None, None, None, None, _stream())
 
     def unpermute(self):
         _call("moe_unpermute_combine", _p(self.dX), _p(self.pair_row), None, self.T, self.k, self.d, self.rcap,
@@ -184,15 +191,17 @@ class TrainPlan(ForwardPlan):
 
     def x_quant_t(self, x):
         _call("moe_quant_fp8_rows_t", _p(x), None, _p(self.row_pair), _p(self.offsets), self.L, self.rcap,
-              self.k, self.d, _p(self.xqT), _p(self.xqT_s), _stream())
+              self.k, self.d, _p(self.xqT), _p(self.xqT_s), self.sflag, _stream())
 
     def wgrad2(self):
         _call("moe_grouped_gemm_fp8_wgrad", _p(self.dyqT), _p(self.dyqT_s), _p(self.sb["h_qT"]),
-              _p(self.sb["h_sT"]), _p(self.offsets), self.L, self.rcap, self.d, self.f, _p(self.dW2), _stream())
+              _p(self.sb["h_sT"]), _p(self.offsets), self.L, self.rcap, self.d, self.f, _p(self.dW2), self.sflag,
+              _stream())
 
     def wgrad13(self):
         _call("moe_grouped_gemm_fp8_wgrad", _p(self.sb["dgu_qT"]), _p(self.sb["dgu_sT"]), _p(self.xqT),
-              _p(self.xqT_s), _p(self.offsets), self.L, self.rcap, 2 * self.f, self.d, _p(self.dW13), _stream())
+              _p(self.xqT_s), _p(self.offsets), self.L, self.rcap, 2 * self.f, self.d, _p(self.dW13), self.sflag,
+              _stream())
 
     def gate_bwd(self):
         _call("moe_gate_backward", _p(self.d_gate), _p(self.w), _p(self.ids), self.T, self.k, self.E,

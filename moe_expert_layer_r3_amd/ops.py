@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 EPI_STORE_BF16, EPI_SWIGLU_Q8, EPI_SWIGLU_Q8_SAVE, EPI_STORE_F32, EPI_SWIGLU_F32 = range(5)
 TILE_1x128, TILE_128x128 = 0, 1
+SCALE_POW2 = 0x100  # power-of-two (UE8M0) tile scales, OR'ed into tile / epilogue
 SRC_BF16, SRC_F32 = 0, 1
 FLAG_BAD_ID, FLAG_DUP_ID, FLAG_ROW_CAP = 1, 2, 4
 ROW_ALIGN = 128
@@ -42,16 +43,16 @@ _SIGS = {
     "moe_replay_load": (ctypes.c_int, [_P, _I32, _I32, _I64, _I32, _I64, _I64, _P, _I32, _P, _P, _P, _P]),
     "moe_permute_workspace": (ctypes.c_int, [_I64, _I32, _I32, ctypes.POINTER(_SZ)]),
     "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P,
-                                   _P, _I32, _P, _P, _P, _P, _SZ, _P, _P]),
+                                   _P, _I32, _P, _P, _P, _I32, _P, _SZ, _P, _P]),
     "moe_quant_fp8": (ctypes.c_int, [_P, _I32, _I64, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
-    "moe_quant_fp8_rows_t": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _P, _P, _P]),
+    "moe_quant_fp8_rows_t": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _P, _P, _I32, _P]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
                                             _P, _P, _P, _P, _P, _P, _P, _P]),
-    "moe_grouped_gemm_fp8_wgrad": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P]),
+    "moe_grouped_gemm_fp8_wgrad": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _I32, _P]),
     "moe_swiglu_backward": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
-                                           _P]),
+                                           _I32, _P]),
     "moe_unpermute_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I64, _P, _P]),
-    "moe_combine_backward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _I64, _P, _P, _P, _P]),
+    "moe_combine_backward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _I64, _P, _P, _P, _I32, _P]),
     "moe_gate_backward": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
 }
 
@@ -84,6 +85,10 @@ def _call(name, *args):
     rc = getattr(lib(), name)(*args)
     if rc != 0:
         raise MoeError(name, rc, last_error())
+
+
+def _flag(pow2):
+    return SCALE_POW2 if pow2 else 0
 
 
 def _p(t):
@@ -165,8 +170,9 @@ def permute_workspace(T, k, L):
     return n.value
 
 
-def permute(ids, e0, L, rcap=None, x=None, x_perm=False, quant=True, status=None, ws=None):
-    """Expert-grouped permutation (+ optional fused gather / 1x128 quant of x).
+def permute(ids, e0, L, rcap=None, x=None, x_perm=False, quant=True, status=None, ws=None, pow2=False):
+    """Expert-grouped permutation (+ optional fused gather / 1x128 quant of x,
+    with power-of-two scales when pow2).
 
     Returns a dict with counts, offsets, row_pair, pair_row, row_cap and, when x
     is given, x_perm (bf16) and/or xq (u8) + xq_s (fp32)."""
@@ -192,15 +198,17 @@ def permute(ids, e0, L, rcap=None, x=None, x_perm=False, quant=True, status=None
             xq = torch.empty((rcap, d), dtype=torch.uint8, device=dev)
             xs = torch.empty((d // 128, rcap), dtype=torch.float32, device=dev)  # K-block-major
     _call("moe_permute", _p(ids), T, k, e0, L, rcap, _p(counts), _p(offsets), _p(row_pair), _p(pair_row),
-          _p(x), d, _p(xp), _p(xq), _p(xs), _p(ws), ws.numel(), _p(status), _stream(dev))
+          _p(x), d, _p(xp), _p(xq), _p(xs), _flag(pow2), _p(ws), ws.numel(), _p(status),
+          _stream(dev))
     out.update(x_perm=xp, xq=xq, xq_s=xs)
     return out
 
 
 # ---------------------------------------------------------------- quantisation
 
-def quant_fp8(src, tile=TILE_1x128, groups=1, transpose=False):
-    """Quantise src ([rows, cols] or [groups, rows, cols], bf16 or fp32).
+def quant_fp8(src, tile=TILE_1x128, groups=1, transpose=False, pow2=False):
+    """Quantise src ([rows, cols] or [groups, rows, cols], bf16 or fp32), with
+    power-of-two scales when pow2.
 
     Returns (q, s) or, for 128x128 with transpose=True, (q, s, qT, sT)."""
     src_type = {torch.bfloat16: SRC_BF16, torch.float32: SRC_F32}[src.dtype]
@@ -221,7 +229,7 @@ def quant_fp8(src, tile=TILE_1x128, groups=1, transpose=False):
         s = torch.empty((groups, rows // 128, cols // 128), dtype=torch.float32, device=dev)
         qT = torch.empty((groups, cols, rows), dtype=torch.uint8, device=dev) if transpose else None
         sT = torch.empty((groups, cols // 128, rows // 128), dtype=torch.float32, device=dev) if transpose else None
-    _call("moe_quant_fp8", _p(src), src_type, groups, rows, cols, cols, tile, _p(q), _p(s), _p(qT), _p(sT),
+    _call("moe_quant_fp8", _p(src), src_type, groups, rows, cols, cols, tile | _flag(pow2), _p(q), _p(s), _p(qT), _p(sT),
           _stream(dev))
     if tile == TILE_128x128 and transpose:
         return q, s, qT, sT
@@ -242,7 +250,7 @@ def tile_t(q):
     return np.ascontiguousarray(q.reshape(cols, r // 128, 128).transpose(1, 0, 2))
 
 
-def quant_rows_t(src, w, row_pair, offsets, L, rcap, k):
+def quant_rows_t(src, w, row_pair, offsets, L, rcap, k, pow2=False):
     """128x1 quantisation along the expert-grouped rows (gathered from src [T, cols]
     via row_pair, optionally scaled by w), transposed: (qT [rcap/128, cols, 128]
     block-transposed, sT [rcap/128, cols])."""
@@ -252,16 +260,18 @@ def quant_rows_t(src, w, row_pair, offsets, L, rcap, k):
     qT = torch.empty((rcap // 128, cols, 128), dtype=torch.uint8, device=dev)
     sT = torch.empty((rcap // 128, cols), dtype=torch.float32, device=dev)  # token-block-major
     _call("moe_quant_fp8_rows_t", _p(src), _p(w), _p(row_pair), _p(offsets), L, rcap, k, cols, _p(qT), _p(sT),
-          _stream(dev))
+          _flag(pow2), _stream(dev))
     return qT, sT
 
 
 # ---------------------------------------------------------------- GEMMs
 
-def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_in=None, rcap=None):
+def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_in=None, rcap=None, pow2=False):
     """Per-expert blockwise-scaled FP8 GEMM over the expert-grouped rows.
 
-    a [rcap, K] u8, a_s [rcap, K/128]; b [L, N, K] u8, b_s [L, N/128, K/128].
+    a [rcap, K] u8, a_s [K/128, rcap]; b [L, N, K] u8, b_s [L, N/128, K/128].
+    pow2: every scale is a power of two, applied by the MFMA as E8M0 (the
+    SwiGLU epilogues then also quantise h with power-of-two scales).
     Returns the epilogue's outputs: STORE_BF16 -> y; STORE_F32 -> acc;
     SWIGLU_Q8 -> (hq, hq_s); SWIGLU_Q8_SAVE -> (hq, hq_s, gu);
     SWIGLU_F32 -> h."""
@@ -289,21 +299,22 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     else:
         raise ValueError(f"unknown epilogue {epilogue}")
     _call("moe_grouped_gemm_fp8", _p(a), _p(a_s), _p(b), _p(b_s), _p(counts), _p(offsets), L, rcap, N, K,
-          epilogue, _p(epi_in), _p(out), _p(out_s), _p(out2), _p(out2_s), _p(out3), _p(out3_s), _stream(dev))
+          epilogue | _flag(pow2), _p(epi_in), _p(out), _p(out_s), _p(out2), _p(out2_s), _p(out3), _p(out3_s),
+          _stream(dev))
     return res
 
 
-def grouped_gemm_wgrad(aT, aT_s, bT, bT_s, offsets, L, rcap, out=None):
+def grouped_gemm_wgrad(aT, aT_s, bT, bT_s, offsets, L, rcap, out=None, pow2=False):
     """dW [L, M, N] bf16 from the 128x1-quantised block-transposed operands
     aT [rcap/128, M, 128], bT [rcap/128, N, 128]."""
     M, N = aT.shape[1], bT.shape[1]
     dW = torch.empty((L, M, N), dtype=torch.bfloat16, device=_dev(aT)) if out is None else out
     _call("moe_grouped_gemm_fp8_wgrad", _p(aT), _p(aT_s), _p(bT), _p(bT_s), _p(offsets), L, rcap, M, N, _p(dW),
-          _stream(aT.device))
+          _flag(pow2), _stream(aT.device))
     return dW
 
 
-def swiglu_backward(dH, gu, row_pair, offsets, L, rcap, inspect=False, out=None):
+def swiglu_backward(dH, gu, row_pair, offsets, L, rcap, inspect=False, out=None, pow2=False):
     """Backward through SwiGLU + FP8 re-quantisation of its results.
 
     dH [rcap, f] fp32, gu [rcap, 2f] bf16 (saved G, U).  Returns a dict with
@@ -325,7 +336,7 @@ def swiglu_backward(dH, gu, row_pair, offsets, L, rcap, inspect=False, out=None)
             o[name] = torch.empty(shape, dtype=dt, device=dev)
     _call("moe_swiglu_backward", _p(dH), _p(gu), _p(row_pair), _p(offsets), L, rcap, f,
           _p(o["dgu_q"]), _p(o["dgu_s"]), _p(o["dgu_qT"]), _p(o["dgu_sT"]), _p(o["h_qT"]), _p(o["h_sT"]),
-          _p(o.get("dgu")), _p(o.get("h")), _stream(dev))
+          _p(o.get("dgu")), _p(o.get("h")), _flag(pow2), _stream(dev))
     return o
 
 
@@ -341,8 +352,8 @@ def combine(y_perm, pair_row, w, rcap=None):
     return y
 
 
-def combine_backward(dy, y_perm, pair_row, w, rcap=None, quant=True):
-    """(dYq [rcap, d] u8, dYq_s [rcap, d/128], d_gate [T, k] fp32)."""
+def combine_backward(dy, y_perm, pair_row, w, rcap=None, quant=True, pow2=False):
+    """(dYq [rcap, d] u8, dYq_s [d/128, rcap] (K-block-major), d_gate [T, k] fp32)."""
     T, k = pair_row.shape
     d = dy.shape[1]
     rcap = y_perm.shape[0] if rcap is None else rcap
@@ -351,5 +362,5 @@ def combine_backward(dy, y_perm, pair_row, w, rcap=None, quant=True):
     dys = torch.empty((d // 128, rcap), dtype=torch.float32, device=dev) if quant else None
     d_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
     _call("moe_combine_backward", _p(dy), _p(y_perm), _p(pair_row), _p(w), T, k, d, rcap, _p(dyq), _p(dys),
-          _p(d_gate), _stream(dev))
+          _p(d_gate), _flag(pow2), _stream(dev))
     return dyq, dys, d_gate

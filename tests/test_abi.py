@@ -78,7 +78,8 @@ def test_permute_validation():
     n = ctypes.c_size_t(0)
     assert ops.lib().moe_permute_workspace(8192, 8, 32, ctypes.byref(n)) == 0 and n.value > 0
     args = dict(ids=FAKE, T=100, k=2, e0=0, L=8, rcap=512, counts=FAKE, offsets=FAKE, row_pair=FAKE,
-                pair_row=FAKE, x=None, d=0, xp=None, xq=None, xs=None, ws=FAKE, wsb=1 << 20, st=None, s=None)
+                pair_row=FAKE, x=None, d=0, xp=None, xq=None, xs=None, qf=0, ws=FAKE, wsb=1 << 20, st=None,
+                s=None)
 
     def call(**kw):
         a = dict(args)
@@ -92,6 +93,7 @@ def test_permute_validation():
     assert call(x=FAKE, d=100, xq=FAKE, xs=FAKE) == -2
     assert call(x=FAKE, d=128) == -1              # x without an output
     assert call(xq=FAKE, xs=FAKE) == -1           # output without x
+    assert call(qf=1) == -3 and call(qf=0x101) == -3  # unknown quant flags
 
 
 def test_quant_validation():
@@ -102,9 +104,12 @@ def test_quant_validation():
     assert _rc(L, FAKE, 0, 1, 128, 128, 128, 0, FAKE, FAKE, FAKE, FAKE, None)[0] == -3  # qT for 1x128
     assert _rc(L, None, 0, 1, 128, 128, 128, 0, FAKE, FAKE, None, None, None)[0] == -1
     assert _rc(L, FAKE, 0, 1, 128, 128, 64, 0, FAKE, FAKE, None, None, None)[0] == -2   # ld < cols
+    assert _rc(L, FAKE, 0, 1, 128, 128, 128, 0x102, FAKE, FAKE, None, None, None)[0] == -3  # unknown tile
+    assert _rc(L, FAKE, 0, 1, 128, 128, 128, 0x200, FAKE, FAKE, None, None, None)[0] == -3  # unknown flag
     R = "moe_quant_fp8_rows_t"
-    assert _rc(R, FAKE, None, FAKE, FAKE, 8, 200, 2, 128, FAKE, FAKE, None)[0] == -2
-    assert _rc(R, FAKE, None, FAKE, FAKE, 8, 256, 2, 100, FAKE, FAKE, None)[0] == -2
+    assert _rc(R, FAKE, None, FAKE, FAKE, 8, 200, 2, 128, FAKE, FAKE, 0, None)[0] == -2
+    assert _rc(R, FAKE, None, FAKE, FAKE, 8, 256, 2, 100, FAKE, FAKE, 0, None)[0] == -2
+    assert _rc(R, FAKE, None, FAKE, FAKE, 8, 256, 2, 128, FAKE, FAKE, 1, None)[0] == -3   # unknown flags
 
 
 def test_gemm_validation():
@@ -123,6 +128,8 @@ def test_gemm_validation():
     assert call(a7=1000) == -2           # row_cap % 128
     assert call(a6=0) == -2
     assert call(a10=9) == -3             # unknown epilogue
+    assert call(a10=0x109) == -3 and call(a10=0x200) == -3  # unknown epilogue with / without POW2
+    assert call(a10=0x101) == -1         # SWIGLU_Q8 | POW2 without out_s
     assert call(a10=1) == -1             # SWIGLU_Q8 without out_s
     assert call(a10=1, a8=384, a13=FAKE) == -2    # SwiGLU needs N % 256
     assert call(a0=None) == -1
@@ -132,5 +139,23 @@ def test_combine_validation():
     assert _rc("moe_unpermute_combine", FAKE, FAKE, FAKE, 10, 17, 128, 256, FAKE, None)[0] == -2
     assert _rc("moe_unpermute_combine", FAKE, FAKE, FAKE, 10, 2, 100, 256, FAKE, None)[0] == -2
     assert _rc("moe_unpermute_combine", FAKE, None, FAKE, 10, 2, 128, 256, FAKE, None)[0] == -1
-    assert _rc("moe_combine_backward", FAKE, FAKE, FAKE, FAKE, 10, 2, 128, 256, FAKE, None, FAKE, None)[0] == -1
+    assert _rc("moe_combine_backward", FAKE, FAKE, FAKE, FAKE, 10, 2, 128, 256, FAKE, None, FAKE, 0, None)[0] == -1
+    assert _rc("moe_combine_backward", FAKE, FAKE, FAKE, FAKE, 10, 2, 128, 256, FAKE, FAKE, FAKE, 3, None)[0] == -3
     assert _rc("moe_gate_backward", FAKE, FAKE, FAKE, 10, 2, 2000, FAKE, None)[0] == -2
+
+
+def test_backward_validation():
+    W = "moe_grouped_gemm_fp8_wgrad"
+    assert _rc(W, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 1024, 256, 512, FAKE, 1, None)[0] == -3      # unknown flags
+    assert _rc(W, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 1024, 200, 512, FAKE, 0, None)[0] == -2      # M % 128
+    assert _rc(W, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 1000, 256, 512, FAKE, 0x100, None)[0] == -2  # row_cap % 128
+    assert _rc(W, FAKE, None, FAKE, FAKE, FAKE, 8, 1024, 256, 512, FAKE, 0x100, None)[0] == -1
+    S = "moe_swiglu_backward"
+    ok = [FAKE] * 4 + [8, 1024, 256] + [FAKE] * 6 + [None, None]
+    assert _rc(S, *ok, 0x200, None)[0] == -3                                                  # unknown flags
+    bad_f = list(ok)
+    bad_f[6] = 100
+    assert _rc(S, *bad_f, 0, None)[0] == -2                                                   # f % 128
+    no_h = list(ok)
+    no_h[11] = None
+    assert _rc(S, *no_h, 0x100, None)[0] == -1

@@ -43,31 +43,32 @@ def _bf16_rows(rng, T, cols):
 
 # ------------------------------------------------------------------ 128x1 quantisation
 
-@pytest.mark.parametrize("weighted", [True, False])
-def test_quant_rows_t(weighted):
+@pytest.mark.parametrize("weighted,pow2", [(True, False), (False, False), (True, True)])
+def test_quant_rows_t(weighted, pow2):
     counts, k, E, e0 = [0, 1, 130, 300, 128], 4, 40, 3
     ids, res, rp, rng = _perm(counts, k, E, e0, seed=21 + weighted)
     T, cols = ids.shape[0], 384
     src = _bf16_rows(rng, T, cols)
     src[7, :] = 0.0
     w = rng.random((T, k)).astype(np.float32) if weighted else None
-    say(f"quant_rows_t weighted={weighted} counts={counts}")
+    say(f"quant_rows_t weighted={weighted} pow2={pow2} counts={counts}")
     rcap = res["row_cap"]
     qT, sT = ops.quant_rows_t(bf16_tensor(src), None if w is None else gpu(w), res["row_pair"], res["offsets"],
-                              len(counts), rcap, k)
+                              len(counts), rcap, k, pow2=pow2)
     n = len(rp)
     real = rp >= 0
     v = np.zeros((n, cols))
     p = rp[real]
     v[real] = src[p // k] if w is None else of32(w.reshape(-1)[p][:, None].astype(np.float64) * src[p // k])
-    rq, rs = OQ.quant_128x1_t(v, real)
+    rq, rs = OQ.quant_128x1_t(v, real, pow2=pow2)
     assert np.array_equal(npi(ops.untile_t(qT))[:, :n], rq)
     assert np.array_equal(npi(sT)[:n // 128].T.astype(np.float64), rs)
 
 
 # ------------------------------------------------------------------ combine backward
 
-def test_combine_backward():
+@pytest.mark.parametrize("pow2", [False, True])
+def test_combine_backward(pow2):
     rng = np.random.default_rng(31)
     T, E, k, e0, L, d = 2000, 64, 6, 16, 16, 512
     lg = rng.standard_normal((T, E)).astype(np.float32)
@@ -76,15 +77,15 @@ def test_combine_backward():
     rcap = res["row_cap"]
     Y = obf16(rng.standard_normal((rcap, d)))
     dy = _bf16_rows(rng, T, d)
-    say("combine backward")
+    say(f"combine backward pow2={pow2}")
     dyq, dys, d_gate = ops.combine_backward(bf16_tensor(dy), bf16_tensor(Y), res["pair_row"],
-                                            gpu(w.astype(np.float32)))
+                                            gpu(w.astype(np.float32)), pow2=pow2)
     pr = npi(res["pair_row"])
     rp = npi(res["row_pair"])[:int(npi(res["offsets"])[-1])]
     real = rp >= 0
     rows = np.flatnonzero(real)
     t, j = rp[real] // k, rp[real] % k
-    rq, rs = OQ.quant_1x128(of32(w[t, j][:, None] * dy[t]))
+    rq, rs = OQ.quant_1x128(of32(w[t, j][:, None] * dy[t]), pow2=pow2)
     assert np.array_equal(npi(dyq)[rows], rq)
     assert np.array_equal(npi(dys).T[rows].astype(np.float64), rs)
     g = np64(d_gate)
@@ -114,8 +115,9 @@ def _tile_close(got, ref, width=128):
     return bool(np.all(err <= 1e-5 * (np.abs(r) + amax)))
 
 
-@pytest.mark.parametrize("counts,f", [([0, 1, 130, 300], 256), ([128, 5], 128), ([257, 0, 64], 384)])
-def test_swiglu_backward(counts, f):
+@pytest.mark.parametrize("counts,f,pow2", [([0, 1, 130, 300], 256, False), ([128, 5], 128, False),
+                                           ([257, 0, 64], 384, False), ([0, 1, 130, 300], 256, True)])
+def test_swiglu_backward(counts, f, pow2):
     k, E, e0 = 2, 16, 0
     ids, res, rp, rng = _perm(counts, k, E, e0, seed=41 + f)
     rcap = res["row_cap"]
@@ -126,9 +128,9 @@ def test_swiglu_backward(counts, f):
     dH[~np.concatenate([real, np.zeros(rcap - n, bool)])] = np.nan   # padding rows must never be read
     GU = obf16(rng.standard_normal((rcap, 2 * f)) * 3.0)
     GU[rows[:3], :4] = [[-100.0, 100.0, 0.0, -1.25]] * 3                 # sigmoid tails, exact zero, dG ~ 0
-    say(f"swiglu backward counts={counts} f={f}")
+    say(f"swiglu backward counts={counts} f={f} pow2={pow2}")
     o = ops.swiglu_backward(gpu(dH), bf16_tensor(GU), res["row_pair"], res["offsets"], len(counts), rcap,
-                            inspect=True)
+                            inspect=True, pow2=pow2)
     dgu = np64(o["dgu"])[:n]
     h = np64(o["h"])[:n]
     ref_dgu, ref_h = _swiglu_ref(dH[:n].astype(np.float64), GU[:n, :f], GU[:n, f:])
@@ -137,17 +139,18 @@ def test_swiglu_backward(counts, f):
     # fused quantisers, bit-exact on the GPU's own fp32 values
     dgu[~real] = 0.0
     h[~real] = 0.0
-    q1, s1 = OQ.quant_1x128(dgu[rows])
+    q1, s1 = OQ.quant_1x128(dgu[rows], pow2=pow2)
     assert np.array_equal(npi(o["dgu_q"])[rows], q1)
     assert np.array_equal(npi(o["dgu_s"]).T[rows].astype(np.float64), s1)
-    qt, st = OQ.quant_128x1_t(dgu, real)
+    qt, st = OQ.quant_128x1_t(dgu, real, pow2=pow2)
     assert np.array_equal(npi(ops.untile_t(o["dgu_qT"]))[:, :n], qt)
     assert np.array_equal(npi(o["dgu_sT"])[:n // 128].T.astype(np.float64), st)
-    qh, sh = OQ.quant_128x1_t(h, real)
+    qh, sh = OQ.quant_128x1_t(h, real, pow2=pow2)
     assert np.array_equal(npi(ops.untile_t(o["h_qT"]))[:, :n], qh)
     assert np.array_equal(npi(o["h_sT"])[:n // 128].T.astype(np.float64), sh)
     # the production call (no inspection outputs) writes the same bytes
-    o2 = ops.swiglu_backward(gpu(dH), bf16_tensor(GU), res["row_pair"], res["offsets"], len(counts), rcap)
+    o2 = ops.swiglu_backward(gpu(dH), bf16_tensor(GU), res["row_pair"], res["offsets"], len(counts), rcap,
+                             pow2=pow2)
     assert np.array_equal(npi(o2["dgu_q"])[rows], npi(o["dgu_q"])[rows])
     assert np.array_equal(npi(o2["dgu_s"]).T[rows], npi(o["dgu_s"]).T[rows])
     for key in ("dgu_qT", "h_qT"):
@@ -156,8 +159,9 @@ def test_swiglu_backward(counts, f):
 
 # ------------------------------------------------------------------ dgrad GEMM (transposed weights)
 
-@pytest.mark.parametrize("counts,K,N", [([0, 1, 130, 300], 256, 512), ([77, 128], 384, 256)])
-def test_gemm_dgrad(counts, K, N):
+@pytest.mark.parametrize("counts,K,N,pow2", [([0, 1, 130, 300], 256, 512, False), ([77, 128], 384, 256, False),
+                                             ([77, 128], 384, 256, True)])
+def test_gemm_dgrad(counts, K, N, pow2):
     """acc[r] = dY[r] @ W[e] for W [L, K, N] given in its forward [out=K, in=N]
     layout; the GEMM reads the transposed copy written by the 128x128 quantiser."""
     k, E, e0 = 4, 32, 0
@@ -165,13 +169,14 @@ def test_gemm_dgrad(counts, K, N):
     L = len(counts)
     rcap = res["row_cap"]
     A = obf16(rng.standard_normal((rcap, K)))
-    aq, as_ = ops.quant_fp8(bf16_tensor(A))
+    aq, as_ = ops.quant_fp8(bf16_tensor(A), pow2=pow2)
     W = obf16(rng.standard_normal((L, K, N)) * 0.02)
     W[0, :128] *= 30.0
-    wq, ws, wqT, wsT = ops.quant_fp8(bf16_tensor(W), tile=ops.TILE_128x128, transpose=True)
-    say(f"gemm dgrad counts={counts} K={K} N={N}")
+    wq, ws, wqT, wsT = ops.quant_fp8(bf16_tensor(W), tile=ops.TILE_128x128, transpose=True, pow2=pow2)
+    say(f"gemm dgrad counts={counts} K={K} N={N} pow2={pow2}")
     # the GEMM reads activation scales K-block-major
-    acc = ops.grouped_gemm(aq, as_.t().contiguous(), wqT, wsT, res["counts"], res["offsets"], ops.EPI_STORE_F32)
+    acc = ops.grouped_gemm(aq, as_.t().contiguous(), wqT, wsT, res["counts"], res["offsets"], ops.EPI_STORE_F32,
+                           pow2=pow2)
     c, o = npi(res["counts"]), npi(res["offsets"])
     ref = OG.grouped_dgrad(npi(aq), npi(as_), c, o, npi(wq), npi(ws))
     rows = np.concatenate([np.arange(o[e], o[e] + c[e]) for e in range(L)]).astype(np.int64)
@@ -200,10 +205,14 @@ def _wgrad_check(got, ref, absum):
 
 # the last case puts several tiles (of 1-, 2- and 3-block experts, with empty
 # experts between them) into each workgroup's stream of K steps
-@pytest.mark.parametrize("counts,M,N", [([0, 1, 130, 300], 256, 512), ([128, 256, 0, 5], 128, 128),
-                                        ([1500], 384, 256), ([0, 0], 128, 256),
-                                        ([(i * 37) % 300 if i % 7 else 0 for i in range(40)], 512, 1024)])
-def test_wgrad(counts, M, N):
+_MANY = [(i * 37) % 300 if i % 7 else 0 for i in range(40)]
+
+
+@pytest.mark.parametrize("counts,M,N,pow2", [([0, 1, 130, 300], 256, 512, False), ([128, 256, 0, 5], 128, 128, False),
+                                             ([1500], 384, 256, False), ([0, 0], 128, 256, False),
+                                             (_MANY, 512, 1024, False), ([0, 1, 130, 300], 256, 512, True),
+                                             ([128, 256, 0, 5], 128, 128, True), (_MANY, 512, 1024, True)])
+def test_wgrad(counts, M, N, pow2):
     k = 2 if len(counts) <= 8 else 8
     E, e0 = max(16, len(counts) + k), 0
     ids, res, rp, rng = _perm(counts, k, E, e0, seed=M + N + len(counts))
@@ -213,8 +222,8 @@ def test_wgrad(counts, M, N):
     real = rp >= 0
     A = rng.standard_normal((n, M)) * np.exp2(rng.integers(-4, 4, (1, M)))
     B = rng.standard_normal((n, N))
-    qa, sa = OQ.quant_128x1_t(A, real)
-    qb, sb = OQ.quant_128x1_t(B, real)
+    qa, sa = OQ.quant_128x1_t(A, real, pow2=pow2)
+    qb, sb = OQ.quant_128x1_t(B, real, pow2=pow2)
     # rows past offsets[L] hold NaN codes and scales: the kernel must not read
     # them; scales go in token-block-major, the layout the kernel reads
     def upload(q, s):
@@ -225,8 +234,8 @@ def test_wgrad(counts, M, N):
         return gpu(ops.tile_t(qf)), gpu(sf)
     aT, aT_s = upload(qa, sa)
     bT, bT_s = upload(qb, sb)
-    say(f"wgrad counts={counts} M={M} N={N}")
-    dW = ops.grouped_gemm_wgrad(aT, aT_s, bT, bT_s, res["offsets"], L, rcap)
+    say(f"wgrad counts={counts} M={M} N={N} pow2={pow2}")
+    dW = ops.grouped_gemm_wgrad(aT, aT_s, bT, bT_s, res["offsets"], L, rcap, pow2=pow2)
     c, o = npi(res["counts"]), npi(res["offsets"])
     ref = OG.grouped_wgrad(qa, sa, qb, sb, c, o)
     absum = OG.grouped_wgrad(_abs_codes(qa), sa, _abs_codes(qb), sb, c, o)
@@ -257,9 +266,9 @@ def test_gate_backward():
 
 # ------------------------------------------------------------------ whole layer
 
-def _train_gpu(wl, x, lg, W13, W2, dy):
-    plan = ML.TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, e0=wl.e0, device=DEV)
-    wts = ML.quantize_weights(W13, W2, transpose=True)
+def _train_gpu(wl, x, lg, W13, W2, dy, pow2=False):
+    plan = ML.TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, e0=wl.e0, device=DEV, pow2=pow2)
+    wts = ML.quantize_weights(W13, W2, transpose=True, pow2=pow2)
     plan.forward(x, lg, wts)
     plan.backward(x, dy, wts)
     torch.cuda.synchronize()
@@ -297,7 +306,7 @@ def _remap(pr):
     return rows, out
 
 
-def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None):
+def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None, pow2=False):
     """Stage-by-stage parity on the GPU's own upstream operands.
 
     rows_of(seg) picks the checked rows of an expert's segment (all by default);
@@ -313,7 +322,7 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
     rows_of = (lambda seg: seg) if rows_of is None else rows_of
     feat_of = (lambda m: np.arange(m)) if feat_of is None else feat_of
     # inspection rerun of the SwiGLU backward on the same inputs: same bytes
-    ins = ops.swiglu_backward(plan.dH, plan.gu, plan.row_pair, plan.offsets, L, plan.rcap, inspect=True)
+    ins = ops.swiglu_backward(plan.dH, plan.gu, plan.row_pair, plan.offsets, L, plan.rcap, inspect=True, pow2=pow2)
     realrows = np.flatnonzero(real)
     assert torch.equal(ins["dgu_q"][:n][torch.as_tensor(realrows, device=DEV)],
                        plan.sb["dgu_q"][:n][torch.as_tensor(realrows, device=DEV)])
@@ -327,7 +336,7 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
         dys = _rows(dy, t)
         # combine backward: dY = fp32(w * dy), 1x128
         dyq, dyq_s = _rows(plan.dyq, rows), _rows(plan.dyq_s.t(), rows)
-        rq, rs = OQ.quant_1x128(of32(w[t, j][:, None] * dys))
+        rq, rs = OQ.quant_1x128(of32(w[t, j][:, None] * dys), pow2=pow2)
         assert np.array_equal(dyq, rq) and np.array_equal(dyq_s, rs)
         # dgrad through W2 (transposed copy [f, d]), fp32 accumulators
         ref_dH = OG.blockscaled_matmul(dyq, dyq_s, npi(wts["w2qT"][e]), OG.expand_weight_scales(npi(wts["w2sT"][e])))
@@ -339,7 +348,7 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
         dgu32 = _rows(ins["dgu"], rows)
         assert _tile_close(dgu32, ref_dgu) and _tile_close(_rows(ins["h"], rows), ref_h)
         dgu_q, dgu_s = _rows(plan.sb["dgu_q"], rows), _rows(plan.sb["dgu_s"].t(), rows)
-        q1, s1 = OQ.quant_1x128(dgu32)
+        q1, s1 = OQ.quant_1x128(dgu32, pow2=pow2)
         assert np.array_equal(dgu_q, q1) and np.array_equal(dgu_s, s1)
         # dgrad through W13 (transposed copy [d, 2f]), bf16
         ref_dX = OG.blockscaled_matmul(dgu_q, dgu_s, npi(wts["w13qT"][e]),
@@ -364,22 +373,22 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
     rr = realrows
     Xp = np.zeros((n, len(md)))
     Xp[rr] = _sub(x, rp[rr] // k, md)
-    qx, sx = OQ.quant_128x1_t(Xp, real)
+    qx, sx = OQ.quant_128x1_t(Xp, real, pow2=pow2)
     assert np.array_equal(_cols(plan.xqT, md, 0, n), qx)
     assert np.array_equal(_cols(plan.xqT_s.t(), md, 0, n // 128), sx)
     dYp = np.zeros((n, len(md)))
     dYp[rr] = of32(w[rp[rr] // k, rp[rr] % k][:, None] * _sub(dy, rp[rr] // k, md))
-    qy, sy = OQ.quant_128x1_t(dYp, real)
+    qy, sy = OQ.quant_128x1_t(dYp, real, pow2=pow2)
     assert np.array_equal(_cols(plan.dyqT, md, 0, n), qy)
     assert np.array_equal(_cols(plan.dyqT_s.t(), md, 0, n // 128), sy)
     h32 = np.zeros((n, len(mf)))
     h32[rr] = _sub(ins["h"], rr, mf)
-    qh, sh = OQ.quant_128x1_t(h32, real)
+    qh, sh = OQ.quant_128x1_t(h32, real, pow2=pow2)
     assert np.array_equal(_cols(plan.sb["h_qT"], mf, 0, n), qh)
     assert np.array_equal(_cols(plan.sb["h_sT"].t(), mf, 0, n // 128), sh)
     g32 = np.zeros((n, len(m2f)))
     g32[rr] = _sub(ins["dgu"], rr, m2f)
-    qg, sg = OQ.quant_128x1_t(g32, real)
+    qg, sg = OQ.quant_128x1_t(g32, real, pow2=pow2)
     assert np.array_equal(_cols(plan.sb["dgu_qT"], m2f, 0, n), qg)
     assert np.array_equal(_cols(plan.sb["dgu_sT"].t(), m2f, 0, n // 128), sg)
     # wgrad products, per expert, over the expert's padded segment
@@ -401,25 +410,26 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
         _wgrad_check(_rows(plan.dW13[e], m2f)[None], ref13, abs13)
 
 
-def test_layer_tiny_train():
+@pytest.mark.parametrize("pow2", [False, True])
+def test_layer_tiny_train(pow2):
     wl = synth.WORKLOADS["tiny"]
     lg = synth.logits(wl)
     x = synth.x(wl)
     dy = synth.dy(wl)
     W13 = synth.weights(wl, "w13")
     W2 = synth.weights(wl, "w2")
-    say("tiny layer forward + backward T=128 d=128 f=256 E=8 k=2")
-    plan, wts = _train_gpu(wl, x.to(DEV), gpu(lg), W13.to(DEV), W2.to(DEV), dy.to(DEV))
-    wq = OL.quantize_weights(np64(W13), np64(W2))
+    say(f"tiny layer forward + backward T=128 d=128 f=256 E=8 k=2 pow2={pow2}")
+    plan, wts = _train_gpu(wl, x.to(DEV), gpu(lg), W13.to(DEV), W2.to(DEV), dy.to(DEV), pow2=pow2)
+    wq = OL.quantize_weights(np64(W13), np64(W2), pow2=pow2)
     assert np.array_equal(npi(wts["w13qT"]), np.swapaxes(wq[0][0], 1, 2))
     assert np.array_equal(npi(wts["w2qT"]), np.swapaxes(wq[1][0], 1, 2))
-    _check_stages(plan, wts, x.to(DEV), dy.to(DEV), wl)
+    _check_stages(plan, wts, x.to(DEV), dy.to(DEV), wl, pow2=pow2)
     # end to end against the oracle's own chain: the two chains take their FP8
     # decisions on values that differ by fp32 rounding, so an occasional code
     # lands one step apart; 1e-2 bounds that effect at this size.
     ids, w = OR.topk(lg, wl.k)
-    fw = OL.forward(np64(x), ids, w, 0, wl.L, wq)
-    bw = OL.backward(fw, np64(dy), ids, w, wl.E, wq)
+    fw = OL.forward(np64(x), ids, w, 0, wl.L, wq, pow2=pow2)
+    bw = OL.backward(fw, np64(dy), ids, w, wl.E, wq, pow2=pow2)
     for name, got, ref in (("dx", plan.dx, bw["dx"]), ("dW2", plan.dW2, bw["dW2"]),
                            ("dW13", plan.dW13, bw["dW13"]), ("d_logits", plan.d_logits, bw["d_logits"])):
         err = rel_fro(np64(got), ref)
@@ -427,7 +437,8 @@ def test_layer_tiny_train():
         assert err <= 1e-2, name
 
 
-def test_layer_train_full_size_sampled():
+@pytest.mark.parametrize("pow2", [False, True])
+def test_layer_train_full_size_sampled(pow2):
     """T=16384, d=7168, f=2048, 32 of 256 experts, top-8, forward + backward,
     launched as the benchmark launches it; stages checked on sampled rows."""
     wl = synth.WORKLOADS["train"]
@@ -437,8 +448,8 @@ def test_layer_train_full_size_sampled():
     dy = synth.dy(wl)
     W13 = synth.weights(wl, "w13")
     W2 = synth.weights(wl, "w2")
-    say("train: GPU forward + backward")
-    plan, wts = _train_gpu(wl, x.to(DEV), gpu(lg), W13.to(DEV), W2.to(DEV), dy.to(DEV))
+    say(f"train: GPU forward + backward pow2={pow2}")
+    plan, wts = _train_gpu(wl, x.to(DEV), gpu(lg), W13.to(DEV), W2.to(DEV), dy.to(DEV), pow2=pow2)
     ids, w = OR.topk(lg, wl.k)
     assert np.array_equal(npi(plan.ids), ids)
     c, o, rp, pr = OD.permute_index(ids, wl.e0, wl.L)
@@ -448,5 +459,5 @@ def test_layer_train_full_size_sampled():
     del W13, W2
     _check_stages(plan, wts, x.to(DEV), dy.to(DEV), wl,
                   rows_of=lambda seg: seg[:: max(1, len(seg) // 16)], experts=(0, 13, 31),
-                  feat_of=lambda m: np.arange(0, m, m // 32))
+                  feat_of=lambda m: np.arange(0, m, m // 32), pow2=pow2)
     say("train sampled parity ok")
