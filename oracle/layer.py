@@ -35,7 +35,7 @@ against torch fp64 autograd to pin the chain's formulas.
 
 import numpy as np
 
-from . import blockfp8, dispatch, gemm
+from . import blockfp8, dispatch, gemm, mxfp4
 from .numerics import bf16, f32
 from .routing import gate_backward
 
@@ -84,6 +84,25 @@ class _FP8Pow2(_FP8):
     act_t = staticmethod(lambda v, real: blockfp8.quant_128x1_t(v, real, pow2=True))
 
 
+class _MXFP4(_FP8Pow2):
+    """Forward with MXFP4 expert weights (E2M1 codes, one E8M0 scale per 32
+    values along K) and power-of-two 1x128 FP8 activations."""
+
+    @staticmethod
+    def weights(W13, W2):
+        return mxfp4.quant_mx(W13), mxfp4.quant_mx(W2)
+
+    @staticmethod
+    def fwd(a, wq, counts, offsets):
+        return mxfp4.grouped_forward(a[0], a[1], counts, offsets, wq[0], wq[1])
+
+    @staticmethod
+    def dgrad(a, wq, counts, offsets):
+        raise NotImplementedError("MXFP4 weights are defined for the forward products")
+
+    wgrad = dgrad
+
+
 class _Exact:
     """Unquantised fp64 chain (for the autograd pin)."""
     r32 = staticmethod(lambda v: np.asarray(v, dtype=np.float64))
@@ -130,21 +149,26 @@ class _Exact:
         return out
 
 
-def _chain(exact, pow2):
+def _chain(exact, pow2, mx=False):
+    if mx:
+        return _MXFP4
     return _Exact if exact else (_FP8Pow2 if pow2 else _FP8)
 
 
-def quantize_weights(W13, W2, pow2=False):
-    """128x128 FP8 weights: ((W13q, W13s), (W2q, W2s)); pow2 for power-of-two scales."""
-    return _chain(False, pow2).weights(W13, W2)
+def quantize_weights(W13, W2, pow2=False, mx=False):
+    """128x128 FP8 weights: ((W13q, W13s), (W2q, W2s)); pow2 for power-of-two
+    scales.  mx: MXFP4 weights ((codes, E8M0 scale codes) per matrix, codes
+    unpacked)."""
+    return _chain(False, pow2, mx).weights(W13, W2)
 
 
-def forward(x, ids, w, e0, L, wq, exact=False, pow2=False):
+def forward(x, ids, w, e0, L, wq, exact=False, pow2=False, mx=False):
     """x [T, d] bf16 values, ids [T, k], gates w [T, k]; wq from quantize_weights
     (or the fp64 weights when exact).  pow2: every activation tile scale is a
-    power of two (the weights must be quantised the same way).  Returns a dict
-    of every intermediate."""
-    B = _chain(exact, pow2)
+    power of two (the weights must be quantised the same way).  mx: MXFP4
+    weights with power-of-two FP8 activations.  Returns a dict of every
+    intermediate."""
+    B = _chain(exact, pow2, mx)
     x = np.asarray(x, dtype=np.float64)
     T, k = np.asarray(ids).shape
     counts, offsets, row_pair, pair_row = dispatch.permute_index(ids, e0, L)
