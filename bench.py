@@ -12,6 +12,8 @@ Further legs, reported as sub-objects of the same JSON line:
   hotspot  the same forward with Zipf-skewed routing (unequal expert loads)
   pow2     the headline forward with power-of-two (UE8M0) tile scales, which
            the block-scaled MFMA applies itself (no VALU rescale)
+  mxfp4    the headline forward with MXFP4 expert weights (4-bit E2M1, one
+           E8M0 scale per 32 values) and power-of-two FP8 activations
   train    forward + backward at T=16384 (dgrad and wgrad GEMMs on FP8 operands
            re-quantised along their contraction axis), weights re-quantised
            every step (the step time is also given without that part)
@@ -46,8 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ep8", choices=["ep8", "hotspot"],
                     help="workload of the headline forward step")
-    ap.add_argument("--legs", default="hotspot,pow2,train,train_pow2,replay",
-                    help="comma-separated extra legs (hotspot, pow2, train, train_pow2, replay) or 'none'")
+    ap.add_argument("--legs", default="hotspot,pow2,mxfp4,train,train_pow2,replay",
+                    help="comma-separated extra legs (hotspot, pow2, mxfp4, train, train_pow2, replay) or 'none'")
     ap.add_argument("--train-steps", type=int, default=5)
     ap.add_argument("--replay-passes", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -71,14 +73,17 @@ def copy_calibration():
 
 # ---------------------------------------------------------------- algorithmic work
 
-def gemm_algorithmic(P, L, d, f):
-    """Algorithmic FLOPs and HBM bytes of the two forward grouped GEMMs for P local pairs."""
+def gemm_algorithmic(P, L, d, f, mxfp4=False):
+    """Algorithmic FLOPs and HBM bytes of the two forward grouped GEMMs for P local
+    pairs.  mxfp4: weights are 4-bit codes plus one scale byte per 32 values."""
+    def wbytes(n, k):
+        return n * k // 2 + n * (k // 32) if mxfp4 else n * k + (n // 128) * (k // 128) * 4
     g1_flops = 2.0 * P * d * (2 * f)
     g2_flops = 2.0 * P * f * d
-    g1_bytes = (L * 2 * f * d + L * (2 * f // 128) * (d // 128) * 4     # W13 codes + scales
+    g1_bytes = (L * wbytes(2 * f, d)                                      # W13 codes + scales
                 + P * d + P * (d // 128) * 4                             # Xq + scales
                 + P * f + P * (f // 128) * 4)                            # hq + scales
-    g2_bytes = (L * d * f + L * (d // 128) * (f // 128) * 4
+    g2_bytes = (L * wbytes(d, f)
                 + P * f + P * (f // 128) * 4
                 + P * d * 2)                                             # Y bf16
     return g1_flops, g1_bytes, g2_flops, g2_bytes
@@ -151,7 +156,7 @@ def free():
 
 # ---------------------------------------------------------------- forward leg
 
-def forward_leg(wl, steps, warmup, dev, pow2=False):
+def forward_leg(wl, steps, warmup, dev, pow2=False, mxfp4=False):
     from moe_expert_layer_r3_amd import synth
     from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights, weight_buffers
 
@@ -164,20 +169,20 @@ def forward_leg(wl, steps, warmup, dev, pow2=False):
     W13_d, W2_d = W13.to(dev), W2.to(dev)
 
     # weight quantisation (once per weight version), timed on its own
-    wts = weight_buffers(wl.L, wl.d, wl.f, dev)
-    quantize_weights(W13_d, W2_d, out=wts, pow2=pow2)
+    wts = None if mxfp4 else weight_buffers(wl.L, wl.d, wl.f, dev)
+    wts = quantize_weights(W13_d, W2_d, out=wts, pow2=pow2, mxfp4=mxfp4)
     torch.cuda.synchronize()
     qe0, qe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     qe0.record()
     for _ in range(3):
-        quantize_weights(W13_d, W2_d, out=wts, pow2=pow2)
+        quantize_weights(W13_d, W2_d, out=wts, pow2=pow2, mxfp4=mxfp4)
     qe1.record()
     torch.cuda.synchronize()
     wquant_ms = qe0.elapsed_time(qe1) / 3
     del W13_d, W2_d
     free()
 
-    plan = ForwardPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev, pow2=pow2)
+    plan = ForwardPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev, pow2=pow2, mxfp4=mxfp4)
     for _ in range(warmup):
         plan.forward(x_d, lg_d, wts)
     ev = stage_events(plan.STAGES, steps)
@@ -191,7 +196,7 @@ def forward_leg(wl, steps, warmup, dev, pow2=False):
     kern = mean_ms(ev)
     counts = plan.counts.cpu().numpy()
     P = int(counts.sum())
-    g1f, g1b, g2f, g2b = gemm_algorithmic(P, wl.L, wl.d, wl.f)
+    g1f, g1b, g2f, g2b = gemm_algorithmic(P, wl.L, wl.d, wl.f, mxfp4=mxfp4)
     g1_s, g2_s = kern["gemm1"] * 1e-3, kern["gemm2"] * 1e-3
     res = {
         "tokens_per_s": wl.T / (ms * 1e-3),
@@ -422,6 +427,11 @@ def main():
             r["workload"] = (f"{wl.name} forward with power-of-two (UE8M0) tile scales applied by the "
                              "block-scaled MFMA (a variant; the headline uses fp32 scales)")
             out["legs"]["pow2"] = r
+        elif leg == "mxfp4":
+            r, _ = forward_leg(wl, args.steps, args.warmup, dev, mxfp4=True)
+            r["workload"] = (f"{wl.name} forward with MXFP4 expert weights (E2M1, E8M0 scale per 32 values) and "
+                             "power-of-two FP8 activations (a variant; the headline uses FP8 weights)")
+            out["legs"]["mxfp4"] = r
         elif leg == "train":
             out["legs"]["train"] = train_leg(args.train_steps, 2, dev)
         elif leg == "train_pow2":

@@ -150,6 +150,9 @@ enum { MOE_SRC_BF16 = 0, MOE_SRC_F32 = 1 };
  * scales stay fp32 values in the same layouts; the GEMM then applies them as
  * E8M0 exponents inside the matrix instruction.                              */
 enum { MOE_SCALE_POW2 = 0x100 };
+/* OR'ed (with MOE_SCALE_POW2) into moe_grouped_gemm_fp8's epilogue: the weights
+ * b are MXFP4 from moe_quant_mxfp4 instead of 128x128 FP8.                     */
+enum { MOE_WEIGHT_MXFP4 = 0x200 };
 
 /* Quantise src viewed as `groups` matrices of [rows, cols] (row stride ld
  * elements, group stride rows*ld) to OCP e4m3 with one fp32 scale per tile:
@@ -164,6 +167,23 @@ enum { MOE_SCALE_POW2 = 0x100 };
 int moe_quant_fp8(const void* src, int32_t src_type, int64_t groups, int64_t rows,
                   int64_t cols, int64_t ld, int32_t tile, uint8_t* q, float* scales,
                   uint8_t* qT, float* scalesT, hipStream_t stream);
+
+/* MXFP4 quantisation (OCP Microscaling v1.0 FP4) of bf16 weight rows along
+ * their columns (the consuming GEMM's K), for moe_grouped_gemm_fp8 with
+ * MOE_WEIGHT_MXFP4 ("RL at 1T scale", section on future work: 4-bit training
+ * and inference).  For every block of 32 consecutive columns of a row:
+ *     E = floor(log2(max|v|)) - 2 clamped to [-127, 127] (-127 for a zero block)
+ *     scales[r, c/32] = E + 127 (E8M0);  code = nearest E2M1 magnitude of
+ *     |v| * 2^-E (0, 0.5, 1, 1.5, 2, 3, 4, 6; ties to the even code; above 6
+ *     clamped to 6) with the sign bit of v
+ *   src: groups matrices [rows, cols] bf16, row stride ld (>= cols, multiple
+ *   of 8), group stride rows*ld;
+ *   q [groups*rows, cols/2] u8, element 2b of a row in the low nibble of byte b;
+ *   scales [groups, cols/128, rows, 4] u8 (K-block-major: the 4 scales of one
+ *   row and 128-column block are adjacent, and a block's rows follow each
+ *   other, the order the GEMM's K steps read).  cols % 128 == 0.            */
+int moe_quant_mxfp4(const uint16_t* src, int64_t groups, int64_t rows, int64_t cols, int64_t ld,
+                    uint8_t* q, uint8_t* scales, hipStream_t stream);
 
 /* 128x1 quantisation along rows of the expert-grouped layout, transposed output,
  * for the wgrad GEMMs (operands re-quantised along their contraction axis, the
@@ -208,7 +228,12 @@ enum {
  * epilogue | MOE_SCALE_POW2: every a_s and b_s value must be a power of two in
  *   [2^-126, 2^127] (as the MOE_SCALE_POW2 quantisers write them); the matrix
  *   instruction applies them as E8M0 exponents (any mantissa bits are
- *   ignored), and the SwiGLU epilogues quantise h with power-of-two scales.  */
+ *   ignored), and the SwiGLU epilogues quantise h with power-of-two scales.
+ * epilogue | MOE_SCALE_POW2 | MOE_WEIGHT_MXFP4: b is MXFP4, b [L, N, K/2]
+ *   packed E2M1 and b_s (passed as float*, read as bytes) [L, K/128, N, 4]
+ *   E8M0 codes, both from moe_quant_mxfp4 with groups = L, rows = N, cols = K:
+ *     acc[r, n] = sum_k a_s[k/128, r] dec8(a[r, k]) * 2^(b_s[e, k/128, n, (k/32)%4] - 127) dec4(b[e, n, k])
+ *   (the fp4 variant exists for the forward products; the other rules hold). */
 int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* b, const float* b_s,
                          const int32_t* counts, const int32_t* offsets, int32_t L,
                          int64_t row_cap, int32_t N, int32_t K, int32_t epilogue,

@@ -35,6 +35,10 @@
 //     and accumulates the scaled block product into the fp32 accumulator
 //     itself.  No partial waits for a VALU rescale, and the ring of raw
 //     partials is gone.
+//   * MXFP4 weights (WF4, with P2 activations): B rows are 64 bytes per K step
+//     (E2M1, two per byte) with one E8M0 scale per 32 values; a lane's B
+//     fragment is the 16 bytes of K block lane/16 and its scale byte, and the
+//     MFMA runs in the mixed fp4 x fp8 form.  Half the weight bytes per step.
 #include "mfma_common.hpp"
 
 namespace moe {
@@ -73,24 +77,27 @@ constexpr bool is_swiglu(int epi) {
     return epi == MOE_EPI_SWIGLU_Q8 || epi == MOE_EPI_SWIGLU_Q8_SAVE || epi == MOE_EPI_SWIGLU_F32;
 }
 
-template <int BN>
+template <int BN, bool WF4>
 struct GemmSmem {
     static constexpr int A_BYTES = GBM * GBK;
-    static constexpr int B_BYTES = BN * GBK;
+    static constexpr int B_BYTES = BN * (WF4 ? GBK / 2 : GBK);
     static constexpr int S_BYTES = GBM * 4;
-    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int BS_BYTES = WF4 ? BN * 4 : 0;  // E8M0 weight scales: 4 per row per K step
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES + BS_BYTES;
     static constexpr int NSTAGE = 3;
     static constexpr int TOTAL = NSTAGE * STAGE;
 };
 
-template <int BN, int EPI, bool P2>
+template <int BN, int EPI, bool P2, bool WF4>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
-    using SM = GemmSmem<BN>;
+    using SM = GemmSmem<BN, WF4>;
     constexpr int WN = BN / 4;        // wave tile columns
     constexpr int NI = WN / 16;       // n-subtiles per wave
     constexpr int ASEG = GBM / 8 / GWAVES;  // 1 KB A segments per wave
-    constexpr int BSEG = BN / 8 / GWAVES;   // 1 KB B segments per wave
-    constexpr int NLD = ASEG + BSEG + 1;    // DMA instructions per wave per stage
+    constexpr int BSEG = SM::B_BYTES / 1024 / GWAVES;  // 1 KB B segments per wave
+    constexpr int BROWS = BN / GWAVES;      // B rows each wave loads (8 per fp8 segment, 16 per fp4 one)
+    constexpr int NLD = ASEG + BSEG + 1 + (WF4 ? 1 : 0);  // DMA instructions per wave per stage
+    static_assert(!WF4 || P2, "MXFP4 weights take the hardware-scale path");
     // Waiting for stage kb allows NLD younger loads (stage kb+1's DMA).  The
     // previous epilogue's global stores may also be outstanding; loads
     // complete in order, so a count of NLD still implies stage kb landed.
@@ -158,8 +165,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     const int l15 = lane & 15, l7 = lane & 7, c0 = lane >> 4;
     const uint32_t a_rd0 = (wm * 64 + l15) * 128 + ((c0 ^ l7) << 4);
     const uint32_t a_rd1 = (wm * 64 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
-    const uint32_t b_rd0 = SM::A_BYTES + (wn * WN + l15) * 128 + ((c0 ^ l7) << 4);
+    // fp4 B rows are 64 bytes: 4 chunks, chunk c of row r stored at c ^ sw4(r)
+    // with sw4(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps the 16 rows of a
+    // fragment read on distinct banks; lane group g reads chunk g (K values
+    // [32g, 32g + 32)), the natural partner of the A chunks g and g + 4
+    const int sw4 = ((l15 >> 1) ^ (l15 >> 3)) & 3;
+    const uint32_t b_rd0 = WF4 ? SM::A_BYTES + (wn * WN + l15) * 64 + ((c0 ^ sw4) << 4)
+                               : SM::A_BYTES + (wn * WN + l15) * 128 + ((c0 ^ l7) << 4);
     const uint32_t b_rd1 = SM::A_BYTES + (wn * WN + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    // fp4 weight scales: 4 bytes per LDS B row (its four 32-blocks of the step)
+    const uint32_t bq_rd = SM::A_BYTES + SM::B_BYTES + SM::S_BYTES + (wn * WN + l15) * 4 + c0;
     // A scales of a stage: 128 floats stored so that the 16 bytes at slot
     // wm*64 + 4*l15 hold the scales of rows wm*64 + mi*16 + l15, mi = 0..3 (the
     // rows of this lane's outputs), see the scale DMA below
@@ -167,7 +182,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     // the same offsets per stage, as full LDS addresses: with the stage a
     // compile-time constant in the (3x unrolled) K loop, every fragment read is
     // one ds_read with an immediate offset and no address arithmetic
-    uint32_t rA0[3], rA1[3], rB0[3], rB1[3], rS[3];
+    uint32_t rA0[3], rA1[3], rB0[3], rB1[3], rS[3], rBS[3];
 #pragma unroll
     for (int st = 0; st < 3; ++st) {
         const uint32_t b = sbase + (uint32_t)(st * SM::STAGE);
@@ -175,6 +190,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         rA1[st] = b + a_rd1;
         rB0[st] = b + b_rd0;
         rB1[st] = b + b_rd1;
+        rBS[st] = b + bq_rd;
         rS[st] = b + s_rd;
     }
 
@@ -184,6 +200,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         int nt, n0;                    // n-tile and its first output column (SwiGLU: first h column is nt*128)
         const uint8_t* a_base;         // this wave's first A row, K block 0
         const uint8_t* b_base;         // this wave's first B row, K block 0
+        const uint8_t* bsm;            // fp4: this wave's first B row's E8M0 scales, K block 0
         const float* s_base;           // the tile's A scales
         const float* bs_lo;            // B scales of this wave's column blocks, K block 0
         const float* bs_hi;
@@ -219,9 +236,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
             // wave w fills block w
             brow_w = ((wave & 1) ? f : 0) + nt * 128 + (wave >> 1) * 32;
         } else {
-            brow_w = ti.n0 + wave * BSEG * 8;
+            brow_w = ti.n0 + wave * BROWS;
         }
-        ti.b_base = g.b + ((int64_t)e * N + brow_w) * K;
+        ti.b_base = g.b + ((int64_t)e * N + brow_w) * (WF4 ? K / 2 : K);
+        ti.bsm = reinterpret_cast<const uint8_t*>(g.b_s) + ((int64_t)e * nkb * N + brow_w) * 4;
         ti.s_base = g.a_s + ti.row0;  // K-block-major: block kb's scales at kb * row_cap
         // B scale rows (128-column blocks): for SwiGLU the G block (n-subtiles
         // 0, 1) and the U block (2, 3); for stores waves wn = 0, 1 use the first
@@ -243,6 +261,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     // B scales of a tile's two column blocks for every K block, staged in LDS
     // (read by the K loop together with the operand fragments)
     auto stage_bscale = [&](const Tile& ti) {
+        if constexpr (WF4) return;  // per-row scales travel with the operand stages
         for (int i = tid; i < 2 * nkb; i += GTHREADS) {
             const int kb = i >> 1, which = i & 1;
             bscale[kb][which] = (which ? ti.bs_hi : ti.bs_lo)[kb];
@@ -262,6 +281,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     for (int i = 0; i < ASEG; ++i) a_off[i] = (uint32_t)((8 * i + lr) * K) + chunk;
 #pragma unroll
     for (int i = 0; i < BSEG; ++i) b_off[i] = (uint32_t)((8 * i + lr) * K) + chunk;
+    if constexpr (WF4) {
+        // fp4 segment: 16 rows of 64 bytes; lane l moves LDS chunk (l & 3) of
+        // row l/4, i.e. global chunk (l & 3) ^ sw4(row) (segments start at
+        // multiples of 16 rows, so the row within the segment sets the swizzle)
+        const int r4 = lane >> 2;
+        const uint32_t ch4 = (uint32_t)(((lane & 3) ^ (((r4 >> 1) ^ (r4 >> 3)) & 3)) << 4);
+#pragma unroll
+        for (int i = 0; i < BSEG; ++i) b_off[i] = (uint32_t)((16 * i + r4) * (K / 2)) + ch4;
+    }
+    const uint32_t bs_off = (uint32_t)(lane * 4);  // fp4 scales: lane l < BROWS fetches row l's 4 bytes
     // A scales (stored K-block-major, so a block's 128 row scales are 512
     // contiguous bytes): lane l < 16 of wave w fills scale slot w*16 + l, i.e.
     // row (w/4)*64 + (l%4)*16 + (w%4)*4 + l/4 (the layout the fragment reads
@@ -278,8 +307,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         const int kofs = kr * GBK;
 #pragma unroll
         for (int i = 0; i < ASEG; ++i) dma16s(ti.a_base + kofs, a_off[i], sA + (wave * ASEG + i) * 1024);
+        const int kofs_b = WF4 ? kr * (GBK / 2) : kofs;
 #pragma unroll
-        for (int i = 0; i < BSEG; ++i) dma16s(ti.b_base + kofs, b_off[i], sB + (wave * BSEG + i) * 1024);
+        for (int i = 0; i < BSEG; ++i) dma16s(ti.b_base + kofs_b, b_off[i], sB + (wave * BSEG + i) * 1024);
+        if constexpr (WF4) {
+            if (lane < BROWS) dma4s(ti.bsm + (int64_t)kr * N * 4, bs_off, sS + SM::S_BYTES + wave * BROWS * 4);
+        }
         if (lane < 16) dma4s(ti.s_base + (int64_t)kr * g.row_cap, s_off, sS + wave * 64);  // 16 rows' A scales
     };
     // barrier for LDS data only (s_waitcnt lgkmcnt(0) + s_barrier): unlike
@@ -305,6 +338,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         float sc0[4], sc1[4]; // sA * sB of that block per m-subtile (sc1: the U half of a SwiGLU tile)
         v4f ring[4];          // raw MFMA partials awaiting their rescale (4 in flight)
         int ea[4], eb0 = 127, eb1 = 127;  // P2: E8M0 codes of sA per m-subtile and of sB
+        int eb4[NI];                      // WF4: E8M0 code of this lane's B row and K block per n-subtile
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -339,10 +373,20 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
                 constexpr int mi = decltype(ic)::value;
                 af[mi] = join8(lds16<mi * 2048>(pa0), lds16<mi * 2048>(pa1));
             });
-            static_for<0, NI>([&](auto nc) {
-                constexpr int ni = decltype(nc)::value;
-                bfr[ni] = join8(lds16<ni * 2048>(pb0), lds16<ni * 2048>(pb1));
-            });
+            if constexpr (WF4) {
+                const uint32_t pbs = opaque(rBS[st]);
+                const u32x4 z4 = {0u, 0u, 0u, 0u};
+                static_for<0, NI>([&](auto nc) {
+                    constexpr int ni = decltype(nc)::value;
+                    bfr[ni] = join8(lds16<ni * 1024>(pb0), z4);
+                    eb4[ni] = (int)lds1<ni * 64>(pbs);
+                });
+            } else {
+                static_for<0, NI>([&](auto nc) {
+                    constexpr int ni = decltype(nc)::value;
+                    bfr[ni] = join8(lds16<ni * 2048>(pb0), lds16<ni * 2048>(pb1));
+                });
+            }
             flush();
             // element values go through plain integers: __builtin_bit_cast of an
             // ext_vector element lvalue reads element 0 with this compiler
@@ -378,7 +422,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
                     constexpr int j = decltype(jc)::value;
                     constexpr int ni = j / 4, mi = j % 4;
                     constexpr bool second = is_swiglu(EPI) && ni >= NI / 2;
-                    acc[mi][ni] = mfma16x16x128_e8m0(bfr[ni], af[mi], acc[mi][ni], second ? eb1 : eb0, ea[mi]);
+                    if constexpr (WF4)
+                        acc[mi][ni] = mfma16x16x128_fp4_e8m0(bfr[ni], af[mi], acc[mi][ni], eb4[ni], ea[mi]);
+                    else
+                        acc[mi][ni] = mfma16x16x128_e8m0(bfr[ni], af[mi], acc[mi][ni], second ? eb1 : eb0, ea[mi]);
                 });
                 return;
             }
@@ -559,13 +606,15 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 }
 
 template <int BN, int EPI>
-static int launch_gemm(const GemmArgs& a, bool p2, hipStream_t stream) {
+static int launch_gemm(const GemmArgs& a, bool p2, bool wf4, hipStream_t stream) {
     const int ncu = num_cus();
     const int grid = (ncu + 7) / 8 * 8;  // one 512-thread block per CU (LDS bound), persistent
-    if (p2)
-        gemm_fp8_kernel<BN, EPI, true><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+    if (wf4)
+        gemm_fp8_kernel<BN, EPI, true, true><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+    else if (p2)
+        gemm_fp8_kernel<BN, EPI, true, false><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
     else
-        gemm_fp8_kernel<BN, EPI, false><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+        gemm_fp8_kernel<BN, EPI, false, false><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
     MOE_LAUNCH_CHECK("gemm_fp8_kernel");
     return MOE_OK;
 }
@@ -580,7 +629,9 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
                                     float* out_s, void* out2, float* out2_s, void* out3, float* out3_s,
                                     hipStream_t stream) {
     const bool p2 = (epilogue & MOE_SCALE_POW2) != 0;
-    epilogue &= ~MOE_SCALE_POW2;
+    const bool wf4 = (epilogue & MOE_WEIGHT_MXFP4) != 0;
+    epilogue &= ~(MOE_SCALE_POW2 | MOE_WEIGHT_MXFP4);
+    MOE_REQUIRE(!wf4 || p2, MOE_ERR_UNSUPPORTED, "grouped_gemm: MXFP4 weights need MOE_SCALE_POW2 activations");
     MOE_REQUIRE(L >= 1 && L <= GMAXL, MOE_ERR_SHAPE, "grouped_gemm: L=%d outside [1, 1024]", L);
     MOE_REQUIRE(row_cap >= 0 && row_cap % GBM == 0 && row_cap <= 0x7FFFFFFF, MOE_ERR_SHAPE,
                 "grouped_gemm: row_cap=%lld must be a multiple of 128", (long long)row_cap);
@@ -602,17 +653,17 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
     const bool wide = N % 256 == 0;
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
-            return wide ? launch_gemm<256, MOE_EPI_STORE_BF16>(ga, p2, stream)
-                        : launch_gemm<128, MOE_EPI_STORE_BF16>(ga, p2, stream);
+            return wide ? launch_gemm<256, MOE_EPI_STORE_BF16>(ga, p2, wf4, stream)
+                        : launch_gemm<128, MOE_EPI_STORE_BF16>(ga, p2, wf4, stream);
         case MOE_EPI_STORE_F32:
-            return wide ? launch_gemm<256, MOE_EPI_STORE_F32>(ga, p2, stream)
-                        : launch_gemm<128, MOE_EPI_STORE_F32>(ga, p2, stream);
+            return wide ? launch_gemm<256, MOE_EPI_STORE_F32>(ga, p2, wf4, stream)
+                        : launch_gemm<128, MOE_EPI_STORE_F32>(ga, p2, wf4, stream);
         case MOE_EPI_SWIGLU_Q8:
-            return launch_gemm<256, MOE_EPI_SWIGLU_Q8>(ga, p2, stream);
+            return launch_gemm<256, MOE_EPI_SWIGLU_Q8>(ga, p2, wf4, stream);
         case MOE_EPI_SWIGLU_Q8_SAVE:
-            return launch_gemm<256, MOE_EPI_SWIGLU_Q8_SAVE>(ga, p2, stream);
+            return launch_gemm<256, MOE_EPI_SWIGLU_Q8_SAVE>(ga, p2, wf4, stream);
         case MOE_EPI_SWIGLU_F32:
-            return launch_gemm<256, MOE_EPI_SWIGLU_F32>(ga, p2, stream);
+            return launch_gemm<256, MOE_EPI_SWIGLU_F32>(ga, p2, wf4, stream);
     }
     return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm: epilogue %d", epilogue);
 }

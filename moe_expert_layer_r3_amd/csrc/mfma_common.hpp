@@ -53,6 +53,7 @@ __device__ __forceinline__ void wait_lgkm0() {
 typedef const __attribute__((address_space(3))) u32x4* lds_u32x4_ptr;
 typedef const __attribute__((address_space(3))) v2u* lds_v2u_ptr;
 typedef const __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
+typedef const __attribute__((address_space(3))) uint8_t* lds_u8_ptr;
 
 // Plain LDS loads (the compiler tracks their lgkmcnt).  `base` comes out of an
 // opaque move placed after the stage's barrier, so no read can be hoisted
@@ -68,6 +69,10 @@ __device__ __forceinline__ v2u lds8(uint32_t addr) {
 template <int OFF>
 __device__ __forceinline__ uint32_t lds4(uint32_t addr) {
     return *(lds_u32_ptr)(uintptr_t)(addr + OFF);
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t lds1(uint32_t addr) {
+    return *(lds_u8_ptr)(uintptr_t)(addr + OFF);
 }
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm volatile("" : "+v"(v));
@@ -128,6 +133,15 @@ __device__ __forceinline__ v4f mfma16x16x128(const v8i& a, const v8i& b) {
 // (each lane passes the scale of the row whose K chunk it holds)
 __device__ __forceinline__ v4f mfma16x16x128_e8m0(const v8i& a, const v8i& b, const v4f& c, int ea, int eb) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+// the same with a as packed fp4 e2m1 (32 values in the low 16 bytes of the
+// lane's operand, element 2i in the low nibble of byte i) and b fp8 e4m3.
+// Lane group g = lane / 16 of a holds K values [32g, 32g + 32) of its row; the
+// fp8 operand's lane group g holds the 16-byte K chunks g and g + 4 (measured:
+// with that layout the K indices of the two operands pair in order), and each
+// lane's E8M0 scale covers exactly its own 32 values.
+__device__ __forceinline__ v4f mfma16x16x128_fp4_e8m0(const v8i& a, const v8i& b, const v4f& c, int ea, int eb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, ea, 0, eb);
 }
 
 }  // namespace moe

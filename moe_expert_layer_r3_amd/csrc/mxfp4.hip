@@ -1,0 +1,86 @@
+// MXFP4 quantisation of expert weights (OCP Microscaling v1.0 FP4: E2M1
+// elements, one E8M0 power-of-two scale per 32 consecutive values along K).
+// The pages name 4-bit training and inference as future work ("RL at 1T
+// scale", section on future work); MXFP4 is the 4-bit block format that
+// gfx950's block-scaled matrix instruction applies natively.
+//
+// Per block of 32 values V:  E = floor(log2(max|V|)) - 2, clamped to
+// [-127, 127] (-127 for an all-zero block; 2 is the exponent of E2M1's largest
+// normal 6 = 1.5 * 2^2), scale code E + 127, and each value's code is the
+// nearest E2M1 magnitude of |V_i| * 2^-E (ties to the even code, above 6
+// clamped to 6) with the sign bit of V_i.
+#include "common.hpp"
+
+namespace moe {
+
+// E2M1 code of x (|x| <= 8 after scaling): the count of rounding thresholds
+// below |x|.  The midpoints 0.25, 1.25, 2.5, 5 lie between an even and the next
+// odd code and round down (to the even code); 0.75, 1.75, 3.5 lie between an
+// odd and the next even code and round up.
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+    const float a = fabsf(x);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// One thread per 8 values (one 16-byte load); the 4 threads of a 32-block
+// agree on its maximum through two xor shuffles.  Every value is exact in
+// fp32 (bf16 source), the maximum's exponent field gives floor(log2), and
+// v * 2^-E is exact, so the codes match the definition bit for bit.
+// Scales are stored K-block-major per group, [groups, cols/128, rows, 4]: the
+// GEMM's K step reads 4 bytes for each of a tile's rows, and this way those
+// bytes are contiguous (a row-major [rows, cols/32] layout put every row's 4
+// bytes in a different cache line).
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                           int64_t nrows, int64_t cols, int64_t ld,
+                                                           uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+    const int64_t per_row = cols >> 3;
+    const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (item >= nrows * per_row) return;  // whole 4-thread groups leave together (per_row % 4 == 0)
+    const int64_t r = item / per_row, c8 = (item - r * per_row) * 8;
+    const uint4 raw = *reinterpret_cast<const uint4*>(src + r * ld + c8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_lo(w[i]);
+        v[2 * i + 1] = bf16_hi(w[i]);
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = group_max<4>(am);
+    const int ef = (int)((__float_as_uint(am) >> 23) & 0xFFu);  // 0 for zero and subnormal maxima
+    const int code = ef == 0 ? 0 : max(ef - 2, 0);                  // E + 127 with E = ef - 129 >= -127
+    const float inv = __uint_as_float((uint32_t)(254 - code) << 23); // 2^-E
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed |= e2m1_code(v[i] * inv) << (4 * i);
+    *reinterpret_cast<uint32_t*>(q + r * (cols >> 1) + (c8 >> 1)) = packed;
+    if ((c8 & 31) == 0) {
+        const int64_t g = r / rows, rr = r - g * rows;
+        s[((g * (cols >> 7) + (c8 >> 7)) * rows + rr) * 4 + ((c8 >> 5) & 3)] = (uint8_t)code;
+    }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_quant_mxfp4(const uint16_t* src, int64_t groups, int64_t rows, int64_t cols, int64_t ld,
+                               uint8_t* q, uint8_t* scales, hipStream_t stream) {
+    MOE_REQUIRE(groups >= 0 && rows >= 0 && cols >= 0 && cols % 128 == 0, MOE_ERR_SHAPE,
+                "quant_mxfp4: cols=%lld must be a multiple of 128", (long long)cols);
+    MOE_REQUIRE(ld >= cols && ld % 8 == 0, MOE_ERR_SHAPE, "quant_mxfp4: ld=%lld must be >= cols and a multiple of 8",
+                (long long)ld);
+    if (groups == 0 || rows == 0 || cols == 0) return MOE_OK;
+    MOE_REQUIRE(src && q && scales, MOE_ERR_NULL, "quant_mxfp4: NULL src/q/scales");
+    const int64_t nrows = groups * rows;
+    const int64_t threads = nrows * (cols / 8);
+    MOE_REQUIRE((threads + 255) / 256 <= 0x7FFFFFFF, MOE_ERR_SHAPE, "quant_mxfp4: too large");
+    quant_mxfp4_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(src, rows, nrows, cols,
+                                                                                       ld, q, scales);
+    MOE_LAUNCH_CHECK("quant_mxfp4_kernel");
+    return MOE_OK;
+}

@@ -24,12 +24,27 @@ def weight_buffers(L, d, f, device="cuda", transpose=False):
     return out
 
 
-def quantize_weights(W13, W2, transpose=False, out=None, pow2=False):
+def quantize_weights(W13, W2, transpose=False, out=None, pow2=False, mxfp4=False):
     """bf16 W13 [L, 2f, d], W2 [L, d, f] -> dict of FP8 codes and scales (and the
     transposed copies used by the dgrad GEMMs when ``transpose``), 128x128 tiles,
-    power-of-two scales when ``pow2``.
+    power-of-two scales when ``pow2``.  ``mxfp4``: MXFP4 weights instead (forward
+    GEMMs only): w13q [L, 2f, d/2] packed E2M1, w13s [L, d/128, 2f, 4] E8M0
+    codes (K-block-major), and alike for W2.
     ``out`` (from weight_buffers) receives the result without allocating."""
     L, f2, d = W13.shape
+    if mxfp4:
+        if transpose:
+            raise ValueError("MXFP4 weights are quantised for the forward products only")
+        e = lambda shape: torch.empty(shape, dtype=torch.uint8, device=W13.device)
+        if out is None:
+            out = dict(w13q=e((L, f2, d // 2)), w13s=e((L, d // 128, f2, 4)),
+                       w2q=e((L, d, f2 // 4)), w2s=e((L, f2 // 256, d, 4)))
+        for W, q, s in ((W13, "w13q", "w13s"), (W2, "w2q", "w2s")):
+            if W.dtype != torch.bfloat16 or not W.is_contiguous():
+                raise ValueError("weights must be contiguous bf16")
+            _call("moe_quant_mxfp4", _p(W), W.shape[0], W.shape[1], W.shape[2], W.shape[2], _p(out[q]), _p(out[s]),
+                  _stream())
+        return out
     if out is None:
         out = weight_buffers(L, d, f2 // 2, W13.device, transpose)
     for W, q, s in ((W13, "w13q", "w13s"), (W2, "w2q", "w2s")):
@@ -46,11 +61,13 @@ def quantize_weights(W13, W2, transpose=False, out=None, pow2=False):
 class ForwardPlan:
     """Device buffers for one forward pass of T tokens.  pow2: power-of-two
     (UE8M0) activation scales, applied by the MFMA; the weights must then come
-    from quantize_weights(..., pow2=True)."""
+    from quantize_weights(..., pow2=True).  mxfp4: MXFP4 weights (from
+    quantize_weights(..., mxfp4=True)) with power-of-two FP8 activations."""
 
-    def __init__(self, T, d, f, E, L, k, e0=0, device="cuda", save_gu=False, pow2=False):
+    def __init__(self, T, d, f, E, L, k, e0=0, device="cuda", save_gu=False, pow2=False, mxfp4=False):
         self.T, self.d, self.f, self.E, self.L, self.k, self.e0 = T, d, f, E, L, k, e0
-        self.sflag = ops.SCALE_POW2 if pow2 else 0
+        self.sflag = ops.SCALE_POW2 if (pow2 or mxfp4) else 0  # activation quantisers
+        self.gflag = self.sflag | (ops.WEIGHT_MXFP4 if mxfp4 else 0)  # forward GEMMs
         self.rcap = ops.row_cap(T, k, L)
         dv = device
         i32, f32, u8, b16 = torch.int32, torch.float32, torch.uint8, torch.bfloat16
@@ -88,12 +105,12 @@ class ForwardPlan:
     def gemm1(self, wts):
         epi = ops.EPI_SWIGLU_Q8_SAVE if self.gu is not None else ops.EPI_SWIGLU_Q8
         _call("moe_grouped_gemm_fp8", _p(self.xq), _p(self.xq_s), _p(wts["w13q"]), _p(wts["w13s"]),
-              _p(self.counts), _p(self.offsets), self.L, self.rcap, 2 * self.f, self.d, epi | self.sflag, None,
+              _p(self.counts), _p(self.offsets), self.L, self.rcap, 2 * self.f, self.d, epi | self.gflag, None,
               _p(self.hq), _p(self.hq_s), _p(self.gu), None, None, None, _stream())
 
     def gemm2(self, wts):
         _call("moe_grouped_gemm_fp8", _p(self.hq), _p(self.hq_s), _p(wts["w2q"]), _p(wts["w2s"]),
-              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.d, self.f, ops.EPI_STORE_BF16 | self.sflag,
+              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.d, self.f, ops.EPI_STORE_BF16 | self.gflag,
               None,
               _p(self.Y), None, None, None, None, None, _stream())
 

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 EPI_STORE_BF16, EPI_SWIGLU_Q8, EPI_SWIGLU_Q8_SAVE, EPI_STORE_F32, EPI_SWIGLU_F32 = range(5)
 TILE_1x128, TILE_128x128 = 0, 1
 SCALE_POW2 = 0x100  # power-of-two (UE8M0) tile scales, OR'ed into tile / epilogue
+WEIGHT_MXFP4 = 0x200  # MXFP4 weights, OR'ed (with SCALE_POW2) into a GEMM epilogue
 SRC_BF16, SRC_F32 = 0, 1
 FLAG_BAD_ID, FLAG_DUP_ID, FLAG_ROW_CAP = 1, 2, 4
 ROW_ALIGN = 128
@@ -45,6 +46,7 @@ _SIGS = {
     "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P,
                                    _P, _I32, _P, _P, _P, _I32, _P, _SZ, _P, _P]),
     "moe_quant_fp8": (ctypes.c_int, [_P, _I32, _I64, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
+    "moe_quant_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, _P]),
     "moe_quant_fp8_rows_t": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _P, _P, _I32, _P]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
                                             _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -238,6 +240,24 @@ def quant_fp8(src, tile=TILE_1x128, groups=1, transpose=False, pow2=False):
     return q, s
 
 
+def quant_mxfp4(src):
+    """MXFP4 of bf16 src [G, N, K] (or [N, K]) along K: (q [G, N, K/2] u8 packed,
+    scales [G, K/128, N, 4] u8 E8M0 codes, K-block-major)."""
+    _contig(src, torch.bfloat16, "src")
+    dev = _dev(src)
+    G, N, K = src.shape if src.dim() == 3 else (1,) + tuple(src.shape)
+    q = torch.empty(src.shape[:-1] + (K // 2,), dtype=torch.uint8, device=dev)
+    s = torch.empty((G, K // 128, N, 4), dtype=torch.uint8, device=dev)
+    _call("moe_quant_mxfp4", _p(src), G, N, K, K, _p(q), _p(s), _stream(dev))
+    return q, s
+
+
+def mx_scales_rows(s):
+    """[G, K/128, N, 4] K-block-major MXFP4 scales as numpy [G, N, K/32]."""
+    G, kb, N, _ = s.shape
+    return s.detach().cpu().numpy().transpose(0, 2, 1, 3).reshape(G, N, kb * 4)
+
+
 def untile_t(qT):
     """[cols, rcap] view (a copy) of a block-transposed operand [rcap/128, cols, 128]."""
     nb, cols, _ = qT.shape
@@ -266,17 +286,22 @@ def quant_rows_t(src, w, row_pair, offsets, L, rcap, k, pow2=False):
 
 # ---------------------------------------------------------------- GEMMs
 
-def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_in=None, rcap=None, pow2=False):
+def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_in=None, rcap=None, pow2=False,
+                 mxfp4=False):
     """Per-expert blockwise-scaled FP8 GEMM over the expert-grouped rows.
 
     a [rcap, K] u8, a_s [K/128, rcap]; b [L, N, K] u8, b_s [L, N/128, K/128].
     pow2: every scale is a power of two, applied by the MFMA as E8M0 (the
     SwiGLU epilogues then also quantise h with power-of-two scales).
+    mxfp4: b [L, N, K/2] and b_s [L, N, K/32] from quant_mxfp4 (implies pow2).
     Returns the epilogue's outputs: STORE_BF16 -> y; STORE_F32 -> acc;
     SWIGLU_Q8 -> (hq, hq_s); SWIGLU_Q8_SAVE -> (hq, hq_s, gu);
     SWIGLU_F32 -> h."""
     rcap = a.shape[0] if rcap is None else rcap
     L, N, K = b.shape
+    if mxfp4:
+        K *= 2
+        pow2 = True
     dev = _dev(a)
     f = N // 2
     out = out_s = out2 = out2_s = out3 = out3_s = None
@@ -299,7 +324,7 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     else:
         raise ValueError(f"unknown epilogue {epilogue}")
     _call("moe_grouped_gemm_fp8", _p(a), _p(a_s), _p(b), _p(b_s), _p(counts), _p(offsets), L, rcap, N, K,
-          epilogue | _flag(pow2), _p(epi_in), _p(out), _p(out_s), _p(out2), _p(out2_s), _p(out3), _p(out3_s),
+          epilogue | _flag(pow2) | (WEIGHT_MXFP4 if mxfp4 else 0), _p(epi_in), _p(out), _p(out_s), _p(out2), _p(out2_s), _p(out3), _p(out3_s),
           _stream(dev))
     return res
 

@@ -159,3 +159,17 @@ def test_backward_validation():
     no_h = list(ok)
     no_h[11] = None
     assert _rc(S, *no_h, 0x100, None)[0] == -1
+
+
+def test_mxfp4_validation():
+    Q = "moe_quant_mxfp4"
+    assert _rc(Q, FAKE, 1, 4, 96, 96, FAKE, FAKE, None)[0] == -2     # cols % 128
+    assert _rc(Q, FAKE, 1, 4, 128, 64, FAKE, FAKE, None)[0] == -2    # ld < cols
+    assert _rc(Q, None, 1, 4, 128, 128, FAKE, FAKE, None)[0] == -1
+    assert _rc(Q, FAKE, 0, 4, 128, 128, None, None, None)[0] == 0    # empty: nothing to do
+    G = "moe_grouped_gemm_fp8"
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 1024, 512, 256, 0, None, FAKE, None, None, None, None, None, None]
+    args[10] = 0x200                                                # MXFP4 without POW2
+    assert _rc(G, *args)[0] == -3
+    args[10] = 0x301                                                # SWIGLU_Q8 | POW2 | MXFP4 without out_s
+    assert _rc(G, *args)[0] == -1

@@ -1,0 +1,161 @@
+"""GPU parity of the MXFP4-weight forward (E2M1 codes with an E8M0 scale per 32
+values, FP8 activations with power-of-two 1x128 scales) against the oracle,
+through the C ABI.
+
+Codes and scale bytes are bit-exact; GEMM outputs hold the bounds of the FP8
+path (1e-4 on fp32 accumulators, 2e-3 relative Frobenius on bf16 outputs and
+the layer output) against the oracle's fp64 products over the same operands."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import blockfp8 as OQ
+from oracle import dispatch as OD
+from oracle import layer as OL
+from oracle import mxfp4 as MX
+from oracle import routing as OR
+from oracle.numerics import bf16 as obf16, f32 as of32
+from moe_expert_layer_r3_amd import ops, synth
+from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights
+from gpu_util import DEV, bf16_tensor, gpu, ids_for_counts, np64, npi, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+ACC_TOL = 1e-4
+
+
+def test_quant_mxfp4_bit_exact():
+    rng = np.random.default_rng(60)
+    w = rng.standard_normal((3, 70, 384)) * np.exp2(rng.integers(-30, 30, (3, 70, 1)))
+    w[0, 0, :32] = 0.0                                  # zero block
+    w[0, 1, :32] = 2.0 ** -133                          # subnormal block
+    w[0, 2, :32] = 0.5
+    w[0, 2, 7] = 6.0 * 2.0 ** -4                        # amax = 6 * 2^k: exact
+    w[0, 3, :32] = -0.25
+    w[0, 3, 9] = -7.5 * 2.0 ** 3                        # saturates
+    w[0, 4, 32:64] = -0.0
+    w[1, 5, :] = np.tile(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]), 48)  # ties at X = 1
+    w = obf16(w)
+    say("mxfp4 quant [3, 70, 384]")
+    q, s = ops.quant_mxfp4(bf16_tensor(w))
+    codes, sc = MX.quant_mx(w)
+    assert np.array_equal(ops.mx_scales_rows(s), sc)
+    assert np.array_equal(npi(q), MX.pack(codes))
+
+
+def _real_rows(res):
+    o, c = npi(res["offsets"]), npi(res["counts"])
+    return np.concatenate([np.arange(o[e], o[e] + c[e]) for e in range(len(c))]).astype(np.int64)
+
+
+def _problem(counts, K, N, seed, e0=0, E=64, k=8):
+    rng = np.random.default_rng(seed)
+    L = len(counts)
+    ids = ids_for_counts(counts, k=k, E=E, e0=e0, rng=rng)
+    x = obf16(rng.standard_normal((ids.shape[0], K)) * np.exp2(rng.integers(-6, 6, (ids.shape[0], 1))))
+    res = ops.permute(gpu(ids), e0, L, x=bf16_tensor(x), pow2=True)
+    W = obf16(rng.standard_normal((L, N, K)) * 0.02 * np.exp2(rng.integers(-3, 3, (L, N, 1))))
+    W[0, :64] *= 40.0
+    q, s = ops.quant_mxfp4(bf16_tensor(W))
+    return res, q, s
+
+
+def _ref(res, q, s):
+    c, o = npi(res["counts"]), npi(res["offsets"])
+    return MX.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, MX.unpack(npi(q)), ops.mx_scales_rows(s))
+
+
+@pytest.mark.parametrize("counts,K,N", [([0, 1, 130, 300], 256, 512), ([128, 256, 5, 0, 77, 129], 384, 256),
+                                        ([40], 128, 128), ([200, 3], 640, 384)])
+def test_gemm_store_mxfp4(counts, K, N):
+    res, q, s = _problem(counts, K, N, seed=K + N + 200)
+    say(f"mxfp4 gemm STORE counts={counts} K={K} N={N}")
+    args = (res["xq"], res["xq_s"], q, s, res["counts"], res["offsets"])
+    acc = ops.grouped_gemm(*args, ops.EPI_STORE_F32, mxfp4=True)
+    y = ops.grouped_gemm(*args, ops.EPI_STORE_BF16, mxfp4=True)
+    ref = _ref(res, q, s)
+    rows = _real_rows(res)
+    assert rel_fro(np64(acc)[rows], ref[rows]) <= ACC_TOL
+    assert rel_fro(np64(y)[rows], obf16(ref[rows])) <= TOL
+
+
+@pytest.mark.parametrize("counts,K,f", [([0, 1, 130, 300], 256, 256), ([129, 64], 384, 384), ([256], 128, 128)])
+def test_gemm_swiglu_mxfp4(counts, K, f):
+    res, q, s = _problem(counts, K, 2 * f, seed=K + f + 201)
+    say(f"mxfp4 gemm SWIGLU counts={counts} K={K} f={f}")
+    args = (res["xq"], res["xq_s"], q, s, res["counts"], res["offsets"])
+    h32 = ops.grouped_gemm(*args, ops.EPI_SWIGLU_F32, mxfp4=True)
+    hq, hs = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8, mxfp4=True)
+    GU = _ref(res, q, s)
+    h_ref = OL.silu(of32(GU[:, :f])) * of32(GU[:, f:])
+    rows = _real_rows(res)
+    assert rel_fro(np64(h32)[rows], h_ref[rows]) <= ACC_TOL
+    qref, sref = OQ.quant_1x128(np64(h32)[rows], pow2=True)
+    assert np.array_equal(npi(hq)[rows], qref)
+    assert np.array_equal(npi(hs).T[rows].astype(np.float64), sref)
+
+
+def _plan_forward(wl):
+    lg = synth.logits(wl)
+    x = synth.x(wl)
+    W13 = synth.weights(wl, "w13")
+    W2 = synth.weights(wl, "w2")
+    wts = quantize_weights(W13.to(DEV), W2.to(DEV), mxfp4=True)
+    plan = ForwardPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=DEV, mxfp4=True)
+    y = plan.forward(x.to(DEV), gpu(lg), wts)
+    torch.cuda.synchronize()
+    return lg, x, W13, W2, wts, plan, y
+
+
+def test_layer_tiny_forward_mxfp4():
+    wl = synth.WORKLOADS["tiny"]
+    say("mxfp4 tiny layer forward through ForwardPlan")
+    lg, x, W13, W2, wts, plan, y = _plan_forward(wl)
+    ids, w = OR.topk(lg, wl.k)
+    assert np.array_equal(npi(plan.ids), ids)
+    wq = OL.quantize_weights(np64(W13), np64(W2), mx=True)
+    assert np.array_equal(MX.unpack(npi(wts["w13q"])), wq[0][0])
+    assert np.array_equal(ops.mx_scales_rows(wts["w13s"]), wq[0][1])
+    assert np.array_equal(MX.unpack(npi(wts["w2q"])), wq[1][0])
+    assert np.array_equal(ops.mx_scales_rows(wts["w2s"]), wq[1][1])
+    fw = OL.forward(np64(x), ids, w, wl.e0, wl.L, wq, mx=True)
+    e = rel_fro(np64(y), fw["y"])
+    say("mxfp4 tiny layer rel err", e)
+    assert e <= TOL
+
+
+def test_layer_ep8_full_size_sampled_mxfp4():
+    """The EP=8 share (T=8192, d=7168, f=2048, 32 of 256 experts, top-8) with
+    MXFP4 weights through ForwardPlan, as the benchmark runs it; sampled rows
+    of two experts and of the combine against the oracle."""
+    wl = synth.WORKLOADS["ep8"]
+    say("mxfp4 ep8: GPU forward")
+    lg, x, W13, W2, wts, plan, y = _plan_forward(wl)
+    ids, w = OR.topk(lg, wl.k)
+    assert np.array_equal(npi(plan.ids), ids)
+    c, o, rp, pr = OD.permute_index(ids, wl.e0, wl.L)
+    assert np.array_equal(npi(plan.offsets), o)
+    xs_np = np64(x)
+    say("mxfp4 ep8: checking sampled rows")
+    for e in (0, 17):
+        c13, s13 = MX.quant_mx(np64(W13[e]))
+        assert np.array_equal(MX.unpack(npi(wts["w13q"][e])), c13)
+        assert np.array_equal(ops.mx_scales_rows(wts["w13s"][e:e + 1])[0], s13)
+        c2, s2 = MX.quant_mx(np64(W2[e]))
+        assert np.array_equal(MX.unpack(npi(wts["w2q"][e])), c2)
+        assert np.array_equal(ops.mx_scales_rows(wts["w2s"][e:e + 1])[0], s2)
+        rows = np.arange(o[e], o[e] + c[e])[:: max(1, c[e] // 24)]
+        xq, xsc = OQ.quant_1x128(xs_np[rp[rows] // wl.k], pow2=True)
+        assert np.array_equal(npi(plan.xq)[rows], xq)
+        GU = MX.matmul(xq, xsc, c13, s13)
+        h = OL.silu(of32(GU[:, :wl.f])) * of32(GU[:, wl.f:])
+        hq_g = npi(plan.hq)[rows]
+        hs_g = npi(plan.hq_s).T[rows].astype(np.float64)
+        assert rel_fro(OQ.dequant_1x128(hq_g, hs_g), h) <= 0.05
+        Yref = obf16(MX.matmul(hq_g, hs_g, c2, s2))
+        assert rel_fro(np64(plan.Y)[rows], Yref) <= TOL
+    toks = np.arange(0, wl.T, 97)
+    yref = OD.combine(np64(plan.Y), pr[toks], w[toks])
+    assert rel_fro(np64(y)[toks], yref) <= TOL
+    say("mxfp4 ep8 sampled parity ok")
