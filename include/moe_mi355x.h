@@ -178,10 +178,11 @@ int moe_quant_fp8(const void* src, int32_t src_type, int64_t groups, int64_t row
  *     clamped to 6) with the sign bit of v
  *   src: groups matrices [rows, cols] bf16, row stride ld (>= cols, multiple
  *   of 8), group stride rows*ld;
- *   q [groups*rows, cols/2] u8, element 2b of a row in the low nibble of byte b;
- *   scales [groups, cols/128, rows, 4] u8 (K-block-major: the 4 scales of one
- *   row and 128-column block are adjacent, and a block's rows follow each
- *   other, the order the GEMM's K steps read).  cols % 128 == 0.            */
+ *   q [groups, cols/128, rows, 64] u8: the 128 codes of one row and 128-column
+ *   block are 64 adjacent bytes (element 2b in the low nibble of byte b);
+ *   scales [groups, cols/128, rows, 4] u8.  Both are K-block-major: a block's
+ *   rows follow each other, the order the GEMM's K steps read.
+ *   cols % 128 == 0.                                                         */
 int moe_quant_mxfp4(const uint16_t* src, int64_t groups, int64_t rows, int64_t cols, int64_t ld,
                     uint8_t* q, uint8_t* scales, hipStream_t stream);
 
@@ -229,10 +230,11 @@ enum {
  *   [2^-126, 2^127] (as the MOE_SCALE_POW2 quantisers write them); the matrix
  *   instruction applies them as E8M0 exponents (any mantissa bits are
  *   ignored), and the SwiGLU epilogues quantise h with power-of-two scales.
- * epilogue | MOE_SCALE_POW2 | MOE_WEIGHT_MXFP4: b is MXFP4, b [L, N, K/2]
+ * epilogue | MOE_SCALE_POW2 | MOE_WEIGHT_MXFP4: b is MXFP4, b [L, K/128, N, 64]
  *   packed E2M1 and b_s (passed as float*, read as bytes) [L, K/128, N, 4]
  *   E8M0 codes, both from moe_quant_mxfp4 with groups = L, rows = N, cols = K:
- *     acc[r, n] = sum_k a_s[k/128, r] dec8(a[r, k]) * 2^(b_s[e, k/128, n, (k/32)%4] - 127) dec4(b[e, n, k])
+ *     acc[r, n] = sum_k a_s[k/128, r] dec8(a[r, k]) * 2^(b_s[e, k/128, n, (k/32)%4] - 127) dec4(W[e, n, k])
+ *   with W[e, n, k] the code in b[e, k/128, n, (k%128)/2] (low nibble for even k).
  *   (the fp4 variant exists for the forward products; the other rules hold). */
 int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* b, const float* b_s,
                          const int32_t* counts, const int32_t* offsets, int32_t L,

@@ -13,7 +13,7 @@
 //     per element per block; MFMAs of the next n-subtile run meanwhile.
 //   * operands stream global -> LDS directly (global_load_lds_dwordx4), three
 //     stages deep: K blocks kb+1 and kb+2 are in flight while kb is
-//     multiplied; one barrier per K block.  The LDS image of every 128-byte
+//     multiplied.  The LDS image of every 128-byte
 //     row is XOR swizzled in 16-byte chunks (chunk c of row r is stored at
 //     c ^ (r & 7)), and the four 16-lane groups of a fragment read take the
 //     consecutive chunks g and g + 4: measured on gfx950, this pattern reads
@@ -84,6 +84,9 @@ struct GemmSmem {
     static constexpr int S_BYTES = GBM * 4;
     static constexpr int BS_BYTES = WF4 ? BN * 4 : 0;  // E8M0 weight scales: 4 per row per K step
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES + BS_BYTES;
+    // three stages: the DMA runs two K steps ahead.  (A fourth stage fits
+    // with fp4 weights and was measured: no gain, the stream is bound by
+    // line requests per CU, not by latency.)
     static constexpr int NSTAGE = 3;
     static constexpr int TOTAL = NSTAGE * STAGE;
 };
@@ -182,9 +185,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     // the same offsets per stage, as full LDS addresses: with the stage a
     // compile-time constant in the (3x unrolled) K loop, every fragment read is
     // one ds_read with an immediate offset and no address arithmetic
-    uint32_t rA0[3], rA1[3], rB0[3], rB1[3], rS[3], rBS[3];
+    constexpr int NS = SM::NSTAGE;
+    uint32_t rA0[NS], rA1[NS], rB0[NS], rB1[NS], rS[NS], rBS[NS];
 #pragma unroll
-    for (int st = 0; st < 3; ++st) {
+    for (int st = 0; st < NS; ++st) {
         const uint32_t b = sbase + (uint32_t)(st * SM::STAGE);
         rA0[st] = b + a_rd0;
         rA1[st] = b + a_rd1;
@@ -238,7 +242,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         } else {
             brow_w = ti.n0 + wave * BROWS;
         }
-        ti.b_base = g.b + ((int64_t)e * N + brow_w) * (WF4 ? K / 2 : K);
+        // fp4 codes are K-block-major [L, K/128, N, 64]: the wave's rows of one K
+        // step are contiguous
+        ti.b_base = WF4 ? g.b + ((int64_t)e * nkb * N + brow_w) * 64 : g.b + ((int64_t)e * N + brow_w) * K;
         ti.bsm = reinterpret_cast<const uint8_t*>(g.b_s) + ((int64_t)e * nkb * N + brow_w) * 4;
         ti.s_base = g.a_s + ti.row0;  // K-block-major: block kb's scales at kb * row_cap
         // B scale rows (128-column blocks): for SwiGLU the G block (n-subtiles
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         const int r4 = lane >> 2;
         const uint32_t ch4 = (uint32_t)(((lane & 3) ^ (((r4 >> 1) ^ (r4 >> 3)) & 3)) << 4);
 #pragma unroll
-        for (int i = 0; i < BSEG; ++i) b_off[i] = (uint32_t)((16 * i + r4) * (K / 2)) + ch4;
+        for (int i = 0; i < BSEG; ++i) b_off[i] = (uint32_t)((16 * i + r4) * 64) + ch4;
     }
     const uint32_t bs_off = (uint32_t)(lane * 4);  // fp4 scales: lane l < BROWS fetches row l's 4 bytes
     // A scales (stored K-block-major, so a block's 128 row scales are 512
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         const int kofs = kr * GBK;
 #pragma unroll
         for (int i = 0; i < ASEG; ++i) dma16s(ti.a_base + kofs, a_off[i], sA + (wave * ASEG + i) * 1024);
-        const int kofs_b = WF4 ? kr * (GBK / 2) : kofs;
+        const int64_t kofs_b = WF4 ? (int64_t)kr * N * 64 : kofs;
 #pragma unroll
         for (int i = 0; i < BSEG; ++i) dma16s(ti.b_base + kofs_b, b_off[i], sB + (wave * BSEG + i) * 1024);
         if constexpr (WF4) {
@@ -323,14 +329,31 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     };
 
     const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+    // the first NS - 1 stages of a tile (all but one of the ring)
+    auto prologue = [&](const Tile& ti) {
+        static_for<0, NS - 1>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if (i < nkb) issue(std::integral_constant<int, i>{}, i, ti);
+        });
+    };
+    // wait until stage kb has landed: the stages after it that are already
+    // issued (up to NS - 2 of them) may stay in flight
+    auto wait_stage = [&](int kb) {
+        if constexpr (NS == 4) {
+            if (kb + 2 < nkb) wait_vmcnt<2 * NLD>();
+            else if (kb + 1 < nkb) wait_vmcnt<NLD>();
+            else wait_vmcnt<0>();
+        } else {
+            if (kb + 1 < nkb) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+        }
+    };
     int t = lb;
     Tile cur;
     if (t < total) {
         cur = tile_at(t);
         stage_bscale(cur);
         lds_barrier();
-        issue(std::integral_constant<int, 0>{}, 0, cur);
-        if (nkb > 1) issue(std::integral_constant<int, 1>{}, 1, cur);
+        prologue(cur);
     }
     for (; t < total; t += G) {
         v4f acc[4][NI];
@@ -445,68 +468,68 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
         };
 
         using S0 = std::integral_constant<int, 0>;
-        using S1 = std::integral_constant<int, 1>;
-        using S2 = std::integral_constant<int, 2>;
         // Ping-pong over the two wave groups (waves 0-3 and 4-7, one of each
         // per SIMD): in every phase one group issues MFMAs while the other
         // reads its fragments from LDS.  A K block takes two phases; both
         // groups pass the same barriers in the same order.
         //   phase A (block kb): every wave has waited for its DMA of stage kb;
-        //     DMA of kb + 2 goes out (into the stage both groups finished with);
-        //     group 0 loads kb, group 1 multiplies kb - 1
+        //     DMA of kb + NS - 1 goes out (into the stage both groups finished
+        //     with, the one of kb - 1); group 0 loads kb, group 1 multiplies kb - 1
         //   phase B: group 0 multiplies kb, group 1 loads kb
-        // Stages 0 and 1 of the tile were issued before the previous epilogue.
+        // Stages 0 .. NS - 2 of the tile were issued before the previous epilogue.
         auto step0 = [&](auto st_c, int kb) {  // group 0: load kb, then multiply it
             constexpr int st = decltype(st_c)::value;
-            if (kb + 1 < nkb) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+            wait_stage(kb);
             phase_barrier();
-            if (kb + 2 < nkb) issue(std::integral_constant<int, (st + 2) % 3>{}, kb + 2, cur);
+            if (kb + NS - 1 < nkb) issue(std::integral_constant<int, (st + NS - 1) % NS>{}, kb + NS - 1, cur);
             load(st_c, kb);
             phase_barrier();
             compute();
         };
         auto step1 = [&](auto st_c, int kb) {  // group 1: multiply kb - 1, then load kb
             constexpr int st = decltype(st_c)::value;
-            if (kb + 1 < nkb) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+            wait_stage(kb);
             phase_barrier();
-            if (kb + 2 < nkb) issue(std::integral_constant<int, (st + 2) % 3>{}, kb + 2, cur);
+            if (kb + NS - 1 < nkb) issue(std::integral_constant<int, (st + NS - 1) % NS>{}, kb + NS - 1, cur);
             compute();
             phase_barrier();
             load(st_c, kb);
         };
+        // unrolled by NS so that every stage index is a compile-time constant
         if (wave < 4) {
-            for (int kb = 0; kb < nkb; kb += 3) {
-                step0(S0{}, kb);
-                if (kb + 1 < nkb) step0(S1{}, kb + 1);
-                if (kb + 2 < nkb) step0(S2{}, kb + 2);
+            for (int kb0 = 0; kb0 < nkb; kb0 += NS) {
+                static_for<0, NS>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if (kb0 + i < nkb) step0(std::integral_constant<int, i>{}, kb0 + i);
+                });
             }
         } else {
             // block 0 peeled: nothing to multiply yet (and the fragments are
             // never read before this group's first load)
-            if (nkb > 1) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+            wait_stage(0);
             phase_barrier();
-            if (nkb > 2) issue(S2{}, 2, cur);
+            if (NS - 1 < nkb) issue(std::integral_constant<int, NS - 1>{}, NS - 1, cur);
             phase_barrier();
             load(S0{}, 0);
-            for (int kb = 1; kb < nkb; kb += 3) {
-                step1(S1{}, kb);
-                if (kb + 1 < nkb) step1(S2{}, kb + 1);
-                if (kb + 2 < nkb) step1(S0{}, kb + 2);
+            for (int kb0 = 1; kb0 < nkb; kb0 += NS) {
+                static_for<0, NS>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if (kb0 + i < nkb) step1(std::integral_constant<int, (1 + i) % NS>{}, kb0 + i);
+                });
             }
             compute();
         }
         flush();
         // every wave is done reading the stages and this tile's B scales: the
-        // next tile's first two stages and its B scales go out now, so their
-        // latency overlaps this tile's epilogue (which writes from registers
-        // and touches no stage)
+        // next tile's first NS - 1 stages and its B scales go out now, so
+        // their latency overlaps this tile's epilogue (which writes from
+        // registers and touches no stage)
         lds_barrier();
         const Tile ep = cur;
         if (t + G < total) {
             cur = tile_at(t + G);
             stage_bscale(cur);
-            issue(S0{}, 0, cur);
-            if (nkb > 1) issue(S1{}, 1, cur);
+            prologue(cur);
         }
 
         // ---------------------------------------------------------- epilogues

@@ -28,10 +28,11 @@ __device__ __forceinline__ uint32_t e2m1_code(float x) {
 // agree on its maximum through two xor shuffles.  Every value is exact in
 // fp32 (bf16 source), the maximum's exponent field gives floor(log2), and
 // v * 2^-E is exact, so the codes match the definition bit for bit.
-// Scales are stored K-block-major per group, [groups, cols/128, rows, 4]: the
-// GEMM's K step reads 4 bytes for each of a tile's rows, and this way those
-// bytes are contiguous (a row-major [rows, cols/32] layout put every row's 4
-// bytes in a different cache line).
+// Codes and scales are stored K-block-major per group, [groups, cols/128,
+// rows, 64] and [groups, cols/128, rows, 4]: a GEMM K step reads 64 code bytes
+// and 4 scale bytes of each of a tile's rows, and this way a K step of
+// consecutive rows is contiguous.  Row-major layouts cost one cache-line
+// request per row and K step for half a line of codes and 4 scale bytes.
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ src, int64_t rows,
                                                            int64_t nrows, int64_t cols, int64_t ld,
                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
@@ -57,11 +58,10 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) packed |= e2m1_code(v[i] * inv) << (4 * i);
-    *reinterpret_cast<uint32_t*>(q + r * (cols >> 1) + (c8 >> 1)) = packed;
-    if ((c8 & 31) == 0) {
-        const int64_t g = r / rows, rr = r - g * rows;
-        s[((g * (cols >> 7) + (c8 >> 7)) * rows + rr) * 4 + ((c8 >> 5) & 3)] = (uint8_t)code;
-    }
+    const int64_t g = r / rows, rr = r - g * rows;
+    const int64_t blk = (g * (cols >> 7) + (c8 >> 7)) * rows + rr;  // (group, K block, row)
+    *reinterpret_cast<uint32_t*>(q + blk * 64 + ((c8 & 127) >> 1)) = packed;
+    if ((c8 & 31) == 0) s[blk * 4 + ((c8 >> 5) & 3)] = (uint8_t)code;
 }
 
 }  // namespace moe

@@ -28,8 +28,8 @@ def quantize_weights(W13, W2, transpose=False, out=None, pow2=False, mxfp4=False
     """bf16 W13 [L, 2f, d], W2 [L, d, f] -> dict of FP8 codes and scales (and the
     transposed copies used by the dgrad GEMMs when ``transpose``), 128x128 tiles,
     power-of-two scales when ``pow2``.  ``mxfp4``: MXFP4 weights instead (forward
-    GEMMs only): w13q [L, 2f, d/2] packed E2M1, w13s [L, d/128, 2f, 4] E8M0
-    codes (K-block-major), and alike for W2.
+    GEMMs only): w13q [L, d/128, 2f, 64] packed E2M1, w13s [L, d/128, 2f, 4]
+    E8M0 codes (both K-block-major), and alike for W2.
     ``out`` (from weight_buffers) receives the result without allocating."""
     L, f2, d = W13.shape
     if mxfp4:
@@ -37,8 +37,8 @@ def quantize_weights(W13, W2, transpose=False, out=None, pow2=False, mxfp4=False
             raise ValueError("MXFP4 weights are quantised for the forward products only")
         e = lambda shape: torch.empty(shape, dtype=torch.uint8, device=W13.device)
         if out is None:
-            out = dict(w13q=e((L, f2, d // 2)), w13s=e((L, d // 128, f2, 4)),
-                       w2q=e((L, d, f2 // 4)), w2s=e((L, f2 // 256, d, 4)))
+            out = dict(w13q=e((L, d // 128, f2, 64)), w13s=e((L, d // 128, f2, 4)),
+                       w2q=e((L, f2 // 256, d, 64)), w2s=e((L, f2 // 256, d, 4)))
         for W, q, s in ((W13, "w13q", "w13s"), (W2, "w2q", "w2s")):
             if W.dtype != torch.bfloat16 or not W.is_contiguous():
                 raise ValueError("weights must be contiguous bf16")
@@ -139,6 +139,25 @@ class ForwardPlan:
         rec("gemm2", self.gemm2, wts)
         rec("combine", self.combine)
         return self.y
+
+
+    def capture(self, x, logits, wts, replay=None, warmup=1):
+        """Capture one ``forward`` over these exact buffers into a HIP graph
+        (torch.cuda.CUDAGraph).  Every stage is a kernel launch on the current
+        stream with no allocation, host synchronisation or memset, so the whole
+        pass is capturable; graph.replay() reruns it on whatever x, logits and
+        weights the buffers hold at that time, without per-launch host cost.
+        ``warmup`` eager passes run first on the capture's side stream."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                self.forward(x, logits, wts, replay=replay)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x, logits, wts, replay=replay)
+        return graph
 
 
 class TrainPlan(ForwardPlan):

@@ -241,12 +241,12 @@ def quant_fp8(src, tile=TILE_1x128, groups=1, transpose=False, pow2=False):
 
 
 def quant_mxfp4(src):
-    """MXFP4 of bf16 src [G, N, K] (or [N, K]) along K: (q [G, N, K/2] u8 packed,
-    scales [G, K/128, N, 4] u8 E8M0 codes, K-block-major)."""
+    """MXFP4 of bf16 src [G, N, K] (or [N, K]) along K: (q [G, K/128, N, 64] u8
+    packed E2M1, scales [G, K/128, N, 4] u8 E8M0 codes), both K-block-major."""
     _contig(src, torch.bfloat16, "src")
     dev = _dev(src)
     G, N, K = src.shape if src.dim() == 3 else (1,) + tuple(src.shape)
-    q = torch.empty(src.shape[:-1] + (K // 2,), dtype=torch.uint8, device=dev)
+    q = torch.empty((G, K // 128, N, 64), dtype=torch.uint8, device=dev)
     s = torch.empty((G, K // 128, N, 4), dtype=torch.uint8, device=dev)
     _call("moe_quant_mxfp4", _p(src), G, N, K, K, _p(q), _p(s), _stream(dev))
     return q, s
@@ -256,6 +256,12 @@ def mx_scales_rows(s):
     """[G, K/128, N, 4] K-block-major MXFP4 scales as numpy [G, N, K/32]."""
     G, kb, N, _ = s.shape
     return s.detach().cpu().numpy().transpose(0, 2, 1, 3).reshape(G, N, kb * 4)
+
+
+def mx_codes_rows(q):
+    """[G, K/128, N, 64] K-block-major packed MXFP4 codes as numpy [G, N, K/2]."""
+    G, kb, N, _ = q.shape
+    return q.detach().cpu().numpy().transpose(0, 2, 1, 3).reshape(G, N, kb * 64)
 
 
 def untile_t(qT):
@@ -293,15 +299,17 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     a [rcap, K] u8, a_s [K/128, rcap]; b [L, N, K] u8, b_s [L, N/128, K/128].
     pow2: every scale is a power of two, applied by the MFMA as E8M0 (the
     SwiGLU epilogues then also quantise h with power-of-two scales).
-    mxfp4: b [L, N, K/2] and b_s [L, N, K/32] from quant_mxfp4 (implies pow2).
+    mxfp4: b [L, K/128, N, 64] and b_s [L, K/128, N, 4] from quant_mxfp4 (implies pow2).
     Returns the epilogue's outputs: STORE_BF16 -> y; STORE_F32 -> acc;
     SWIGLU_Q8 -> (hq, hq_s); SWIGLU_Q8_SAVE -> (hq, hq_s, gu);
     SWIGLU_F32 -> h."""
     rcap = a.shape[0] if rcap is None else rcap
-    L, N, K = b.shape
     if mxfp4:
-        K *= 2
+        L, kb, N, _ = b.shape
+        K = kb * 128
         pow2 = True
+    else:
+        L, N, K = b.shape
     dev = _dev(a)
     f = N // 2
     out = out_s = out2 = out2_s = out3 = out3_s = None

@@ -358,3 +358,33 @@ def test_layer_ep8_full_size_sampled():
     yref = OD.combine(Yg, pr[toks], w[toks])
     assert rel_fro(np64(out["y"])[toks], yref) <= TOL
     say("ep8 sampled parity ok")
+
+
+def test_forward_graph_replay():
+    """The ep8 forward captured into a HIP graph: every replay, with new inputs
+    copied into the captured buffers and eager work and synchronisations in
+    between, writes exactly what the eager pass writes for the same inputs."""
+    from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights
+    wl = synth.WORKLOADS["ep8"]
+    say("graph: ep8 inputs")
+    W13 = synth.weights(wl, "w13").to(DEV)
+    W2 = synth.weights(wl, "w2").to(DEV)
+    wts = quantize_weights(W13, W2)
+    del W13, W2
+    plan = ForwardPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=DEV)
+    xs = [synth.x(wl, t0=i * 1024).to(DEV) for i in range(3)]
+    lgs = [torch.from_numpy(synth.logits(wl, t0=i * 1024)).to(DEV) for i in range(3)]
+    x_buf, lg_buf = xs[0].clone(), lgs[0].clone()
+    say("graph: capture")
+    graph = plan.capture(x_buf, lg_buf, wts)
+    for it in (1, 2, 0, 1):
+        ref = plan.forward(xs[it], lgs[it], wts).clone()        # eager, same buffers otherwise
+        ref_ids = plan.ids.clone()
+        torch.cuda.synchronize()
+        x_buf.copy_(xs[it])
+        lg_buf.copy_(lgs[it])
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"graph: replay with input set {it}")
+        assert torch.equal(plan.ids, ref_ids)
+        assert torch.equal(plan.y, ref)

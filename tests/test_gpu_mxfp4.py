@@ -41,7 +41,7 @@ def test_quant_mxfp4_bit_exact():
     q, s = ops.quant_mxfp4(bf16_tensor(w))
     codes, sc = MX.quant_mx(w)
     assert np.array_equal(ops.mx_scales_rows(s), sc)
-    assert np.array_equal(npi(q), MX.pack(codes))
+    assert np.array_equal(ops.mx_codes_rows(q), MX.pack(codes))
 
 
 def _real_rows(res):
@@ -63,7 +63,7 @@ def _problem(counts, K, N, seed, e0=0, E=64, k=8):
 
 def _ref(res, q, s):
     c, o = npi(res["counts"]), npi(res["offsets"])
-    return MX.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, MX.unpack(npi(q)), ops.mx_scales_rows(s))
+    return MX.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, MX.unpack(ops.mx_codes_rows(q)), ops.mx_scales_rows(s))
 
 
 @pytest.mark.parametrize("counts,K,N", [([0, 1, 130, 300], 256, 512), ([128, 256, 5, 0, 77, 129], 384, 256),
@@ -115,9 +115,9 @@ def test_layer_tiny_forward_mxfp4():
     ids, w = OR.topk(lg, wl.k)
     assert np.array_equal(npi(plan.ids), ids)
     wq = OL.quantize_weights(np64(W13), np64(W2), mx=True)
-    assert np.array_equal(MX.unpack(npi(wts["w13q"])), wq[0][0])
+    assert np.array_equal(MX.unpack(ops.mx_codes_rows(wts["w13q"])), wq[0][0])
     assert np.array_equal(ops.mx_scales_rows(wts["w13s"]), wq[0][1])
-    assert np.array_equal(MX.unpack(npi(wts["w2q"])), wq[1][0])
+    assert np.array_equal(MX.unpack(ops.mx_codes_rows(wts["w2q"])), wq[1][0])
     assert np.array_equal(ops.mx_scales_rows(wts["w2s"]), wq[1][1])
     fw = OL.forward(np64(x), ids, w, wl.e0, wl.L, wq, mx=True)
     e = rel_fro(np64(y), fw["y"])
@@ -140,10 +140,10 @@ def test_layer_ep8_full_size_sampled_mxfp4():
     say("mxfp4 ep8: checking sampled rows")
     for e in (0, 17):
         c13, s13 = MX.quant_mx(np64(W13[e]))
-        assert np.array_equal(MX.unpack(npi(wts["w13q"][e])), c13)
+        assert np.array_equal(MX.unpack(ops.mx_codes_rows(wts["w13q"][e:e + 1])[0]), c13)
         assert np.array_equal(ops.mx_scales_rows(wts["w13s"][e:e + 1])[0], s13)
         c2, s2 = MX.quant_mx(np64(W2[e]))
-        assert np.array_equal(MX.unpack(npi(wts["w2q"][e])), c2)
+        assert np.array_equal(MX.unpack(ops.mx_codes_rows(wts["w2q"][e:e + 1])[0]), c2)
         assert np.array_equal(ops.mx_scales_rows(wts["w2s"][e:e + 1])[0], s2)
         rows = np.arange(o[e], o[e] + c[e])[:: max(1, c[e] // 24)]
         xq, xsc = OQ.quant_1x128(xs_np[rp[rows] // wl.k], pow2=True)
