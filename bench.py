@@ -421,7 +421,7 @@ def main():
         "config": {"workload": f"{wl.name}: one EP=8 share of a 256-expert top-8 MoE layer forward",
                    "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "local_experts": wl.L, "top_k": wl.k,
                    "local_pairs": head["local_pairs"]},
-        "roofline": {"bound": "hbm", "kernel": "grouped GEMM1 + SwiGLU + quant (gemm_fp8_kernel<256,1,false>)",
+        "roofline": {"bound": "hbm", "kernel": "grouped GEMM1 + SwiGLU + quant (gemm_fp8_kernel<256,1,false,false>)",
                      "achieved": g1["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": g1["gbs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic(wl.name)},
         "gemm_tflops": head["gemm_tflops"],
