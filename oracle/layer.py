@@ -85,12 +85,18 @@ class _FP8Pow2(_FP8):
 
 
 class _MXFP4(_FP8Pow2):
-    """Forward with MXFP4 expert weights (E2M1 codes, one E8M0 scale per 32
-    values along K) and power-of-two 1x128 FP8 activations."""
+    """MXFP4 expert weights (E2M1 codes, one E8M0 scale per 32 values along the
+    contraction axis) with power-of-two FP8 activations and gradients.  Each
+    weight matrix is quantised twice, as MX blocks run along the contraction
+    axis of the product that reads them: W [N, K] along K for the forward, and
+    its transpose [K, N] along N for the dgrad product.  The weight-gradient
+    products read no weights and stay FP8 (128x1 power-of-two operands)."""
 
     @staticmethod
     def weights(W13, W2):
-        return mxfp4.quant_mx(W13), mxfp4.quant_mx(W2)
+        def both(W):
+            return mxfp4.quant_mx(W) + mxfp4.quant_mx(np.swapaxes(np.asarray(W, np.float64), -1, -2))
+        return both(W13), both(W2)
 
     @staticmethod
     def fwd(a, wq, counts, offsets):
@@ -98,9 +104,8 @@ class _MXFP4(_FP8Pow2):
 
     @staticmethod
     def dgrad(a, wq, counts, offsets):
-        raise NotImplementedError("MXFP4 weights are defined for the forward products")
-
-    wgrad = dgrad
+        # the transposed weights [K, N] play the forward weights' part
+        return mxfp4.grouped_forward(a[0], a[1], counts, offsets, wq[2], wq[3])
 
 
 class _Exact:
@@ -157,8 +162,8 @@ def _chain(exact, pow2, mx=False):
 
 def quantize_weights(W13, W2, pow2=False, mx=False):
     """128x128 FP8 weights: ((W13q, W13s), (W2q, W2s)); pow2 for power-of-two
-    scales.  mx: MXFP4 weights ((codes, E8M0 scale codes) per matrix, codes
-    unpacked)."""
+    scales.  mx: MXFP4 weights, per matrix (codes, E8M0 scale codes, codes of
+    the transpose, its scale codes), codes unpacked."""
     return _chain(False, pow2, mx).weights(W13, W2)
 
 
@@ -195,9 +200,10 @@ def _combine_exact(Y, pair_row, w):
     return y
 
 
-def backward(fw, dy, ids, w, E, wq, exact=False, pow2=False):
-    """Training backward of ``forward``'s result ``fw`` for upstream gradient dy [T, d]."""
-    B = _chain(exact, pow2)
+def backward(fw, dy, ids, w, E, wq, exact=False, pow2=False, mx=False):
+    """Training backward of ``forward``'s result ``fw`` for upstream gradient dy [T, d]
+    (mx: MXFP4 weights from quantize_weights(..., mx=True))."""
+    B = _chain(exact, pow2, mx)
     dy = np.asarray(dy, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
     k = fw["k"]

@@ -154,7 +154,7 @@ def test_forward_chain_matches_fp8_on_shared_grid():
     ids, w = topk(rng.standard_normal((T, E)).astype(np.float32), k)
     wmx = OL.quantize_weights(W13, W2, mx=True)
     wp2 = OL.quantize_weights(W13, W2, pow2=True)
-    assert np.array_equal(MX.dequant_mx(*wmx[0]), W13)
+    assert np.array_equal(MX.dequant_mx(*wmx[0][:2]), W13)
     assert np.array_equal(Q.dequant_128x128(*wp2[0]), W13)
     a = OL.forward(x, ids, w, 0, L, wmx, mx=True)
     b = OL.forward(x, ids, w, 0, L, wp2, pow2=True)
@@ -173,8 +173,40 @@ def test_forward_chain_close_to_exact():
     x = bf16(rng.standard_normal((T, d)))
     ids, w = topk(rng.standard_normal((T, E)).astype(np.float32), k)
     wmx = OL.quantize_weights(W13, W2, mx=True)
-    ew = max(np.linalg.norm(MX.dequant_mx(*q) - W) / np.linalg.norm(W) for q, W in zip(wmx, (W13, W2)))
+    ew = max(np.linalg.norm(MX.dequant_mx(*q[:2]) - W) / np.linalg.norm(W) for q, W in zip(wmx, (W13, W2)))
     ex = OL.forward(x, ids, w, 0, L, (W13, W2), exact=True)
     mx = OL.forward(x, ids, w, 0, L, wmx, mx=True)
     rel = np.linalg.norm(mx["y"] - ex["y"]) / np.linalg.norm(ex["y"])
     assert 0.05 < ew < 0.2 and ew < rel < 2.5 * ew, (ew, rel)
+
+
+def test_training_chain_matches_fp8_on_shared_grid():
+    """Weights on the E2M1 grid times one power of two per 128x128 tile, with a
+    6 in every 32-block along rows and along columns (the diagonals i = j mod
+    32): MX blocks in both directions and the power-of-two 128x128 FP8 tiles
+    all hold them exactly, so forward and backward of the MXFP4 chain (its
+    dgrad products reading the transposed quantisation) equal the power-of-two
+    FP8 chain's."""
+    rng = np.random.default_rng(8)
+    T, d, f, E, L, k = 64, 256, 128, 8, 8, 2
+
+    def grid_weights(rows, cols):
+        w = MX.E2M1_MAG[rng.integers(0, 8, (L, rows, cols))] * np.where(rng.random((L, rows, cols)) < 0.5, -1.0, 1.0)
+        i, j = np.meshgrid(np.arange(rows), np.arange(cols), indexing="ij")
+        w[:, (i % 32) == (j % 32)] = 6.0
+        kexp = rng.integers(-9, -5, (L, rows // 128, cols // 128))
+        return w * np.exp2(np.repeat(np.repeat(kexp, 128, axis=1), 128, axis=2))
+
+    W13, W2 = grid_weights(2 * f, d), grid_weights(d, f)
+    x = bf16(rng.standard_normal((T, d)))
+    dy = bf16(rng.standard_normal((T, d)))
+    ids, w = topk(rng.standard_normal((T, E)).astype(np.float32), k)
+    wmx = OL.quantize_weights(W13, W2, mx=True)
+    wp2 = OL.quantize_weights(W13, W2, pow2=True)
+    assert np.array_equal(MX.dequant_mx(*wmx[0][2:]), np.swapaxes(W13, 1, 2))
+    fa = OL.forward(x, ids, w, 0, L, wmx, mx=True)
+    fb = OL.forward(x, ids, w, 0, L, wp2, pow2=True)
+    ba = OL.backward(fa, dy, ids, w, E, wmx, mx=True)
+    bb = OL.backward(fb, dy, ids, w, E, wp2, pow2=True)
+    for key in ("dx", "dW13", "dW2", "d_logits"):
+        assert np.allclose(ba[key], bb[key], rtol=1e-12, atol=1e-12 * np.max(np.abs(bb[key]))), key
