@@ -22,6 +22,7 @@ Further legs, reported as sub-objects of the same JSON line:
            re-quantised along their contraction axis), weights re-quantised
            every step (the step time is also given without that part)
   train_pow2  the same step with power-of-two tile scales throughout
+  train_mxfp4  the same step with MXFP4 weights in the forward and dgrad GEMMs
   replay   Router Replay of a recorded [4, 8, 131072] id tensor: every layer's
            131072 tokens in 16384-token chunks, each layer with its own weights
 
@@ -52,8 +53,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ep8", choices=["ep8", "hotspot"],
                     help="workload of the headline forward step")
-    ap.add_argument("--legs", default="hotspot,pow2,mxfp4,train,train_pow2,replay",
-                    help="comma-separated extra legs (hotspot, pow2, mxfp4, train, train_pow2, replay) or 'none'")
+    ap.add_argument("--legs", default="hotspot,pow2,mxfp4,train,train_pow2,train_mxfp4,replay",
+                    help="comma-separated extra legs (hotspot, pow2, mxfp4, train, train_pow2, train_mxfp4, "
+                         "replay) or 'none'")
     ap.add_argument("--train-steps", type=int, default=5)
     ap.add_argument("--replay-passes", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,12 +102,16 @@ def train_gemm_flops(P, d, f):
             "wgrad2": 2.0 * P * d * f, "wgrad13": 4.0 * P * d * f}
 
 
-def train_gemm_bytes(P, R, L, d, f):
+def train_gemm_bytes(P, R, L, d, f, mxfp4=False):
     """Algorithmic HBM bytes of the six grouped GEMMs of a training step: P local
     pairs, R expert-grouped rows (segments padded to 128, the wgrad contraction).
-    FP8 operands count 1 byte per element plus fp32 scales per 128 elements."""
+    FP8 operands count 1 byte per element plus fp32 scales per 128 elements;
+    MXFP4 weights half a byte per element plus one scale byte per 32."""
     q = lambda n: n + n // 128 * 4                 # FP8 codes + 1x128 / 128x1 scales
-    w = lambda n: n + n // (128 * 128) * 4         # FP8 codes + 128x128 scales
+    if mxfp4:
+        w = lambda n: n // 2 + n // 32             # E2M1 codes + E8M0 scales
+    else:
+        w = lambda n: n + n // (128 * 128) * 4     # FP8 codes + 128x128 scales
     return {"gemm1": w(L * 2 * f * d) + q(P * d) + q(P * f) + P * 2 * f * 2,   # + saved bf16 [G, U]
             "gemm2": w(L * d * f) + q(P * f) + P * d * 2,
             "dgrad2": q(P * d) + w(L * d * f) + P * f * 4,                     # dH fp32
@@ -235,7 +241,7 @@ def forward_leg(wl, steps, warmup, dev, pow2=False, mxfp4=False):
 
 # ---------------------------------------------------------------- training leg
 
-def train_leg(steps, warmup, dev, pow2=False):
+def train_leg(steps, warmup, dev, pow2=False, mxfp4=False):
     from moe_expert_layer_r3_amd import synth
     from moe_expert_layer_r3_amd.layer import TrainPlan, quantize_weights, weight_buffers
 
@@ -245,13 +251,14 @@ def train_leg(steps, warmup, dev, pow2=False):
     dy_d = synth.dy(wl).to(dev)
     W13_d = synth.weights(wl, "w13").to(dev)
     W2_d = synth.weights(wl, "w2").to(dev)
-    wts = weight_buffers(wl.L, wl.d, wl.f, dev, transpose=True)
-    plan = TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev, pow2=pow2)
+    wts = None if mxfp4 else weight_buffers(wl.L, wl.d, wl.f, dev, transpose=True)
+    wts = quantize_weights(W13_d, W2_d, transpose=True, out=wts, pow2=pow2, mxfp4=mxfp4)
+    plan = TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev, pow2=pow2, mxfp4=mxfp4)
 
     def step(events=None):
         if events is not None:
             events["weight_quant"][0].record()
-        quantize_weights(W13_d, W2_d, transpose=True, out=wts, pow2=pow2)
+        quantize_weights(W13_d, W2_d, transpose=True, out=wts, pow2=pow2, mxfp4=mxfp4)
         if events is not None:
             events["weight_quant"][1].record()
         plan.forward(x_d, lg_d, wts, events=events)
@@ -272,7 +279,7 @@ def train_leg(steps, warmup, dev, pow2=False):
     P = int(plan.counts.sum().item())
     R = int(plan.offsets[-1].item())
     fl = train_gemm_flops(P, wl.d, wl.f)
-    by = train_gemm_bytes(P, R, wl.L, wl.d, wl.f)
+    by = train_gemm_bytes(P, R, wl.L, wl.d, wl.f, mxfp4=mxfp4)
     gemm_ms = sum(kern[n] for n in fl)
     per = {n: {"ms": kern[n], "tflops": fl[n] / (kern[n] * 1e-3) / 1e12,
                "mfma_frac": fl[n] / (kern[n] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
@@ -282,7 +289,8 @@ def train_leg(steps, warmup, dev, pow2=False):
     res = {
         "workload": f"train: T={wl.T}, d={wl.d}, f={wl.f}, {wl.L} of {wl.E} experts local, top-{wl.k}, "
                     "forward + backward, weights re-quantised each step"
-                    + (", power-of-two (UE8M0) tile scales" if pow2 else ""),
+                    + (", power-of-two (UE8M0) tile scales" if pow2 else "")
+                    + (", MXFP4 weights (forward and dgrad), FP8 power-of-two activations" if mxfp4 else ""),
         "tokens_per_s": wl.T / (ms * 1e-3),
         "ms_per_step": ms,
         "ms_per_step_excl_weight_quant": ms - kern["weight_quant"],
@@ -455,6 +463,8 @@ def main():
             out["legs"]["train"] = train_leg(args.train_steps, 2, dev)
         elif leg == "train_pow2":
             out["legs"]["train_pow2"] = train_leg(args.train_steps, 2, dev, pow2=True)
+        elif leg == "train_mxfp4":
+            out["legs"]["train_mxfp4"] = train_leg(args.train_steps, 2, dev, mxfp4=True)
         elif leg == "replay":
             out["legs"]["replay"] = replay_leg(args.replay_passes, dev)
         else:

@@ -182,9 +182,14 @@ int moe_quant_fp8(const void* src, int32_t src_type, int64_t groups, int64_t row
  *   block are 64 adjacent bytes (element 2b in the low nibble of byte b);
  *   scales [groups, cols/128, rows, 4] u8.  Both are K-block-major: a block's
  *   rows follow each other, the order the GEMM's K steps read.
- *   cols % 128 == 0.                                                         */
+ *   cols % 128 == 0.
+ * qT, scalesT (both or neither; rows % 128 == 0): also the MXFP4 of each
+ *   group's transpose [cols, rows], blocks of 32 consecutive rows, for the
+ *   dgrad products: qT [groups, rows/128, cols, 64], scalesT [groups, rows/128,
+ *   cols, 4] (the same layout with rows and cols exchanged); one pass reads
+ *   src once for both.                                                       */
 int moe_quant_mxfp4(const uint16_t* src, int64_t groups, int64_t rows, int64_t cols, int64_t ld,
-                    uint8_t* q, uint8_t* scales, hipStream_t stream);
+                    uint8_t* q, uint8_t* scales, uint8_t* qT, uint8_t* scalesT, hipStream_t stream);
 
 /* 128x1 quantisation along rows of the expert-grouped layout, transposed output,
  * for the wgrad GEMMs (operands re-quantised along their contraction axis, the

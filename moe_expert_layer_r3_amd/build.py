@@ -36,14 +36,20 @@ def build(verbose=False, save_temps=False):
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
-        if save_temps:
-            cmd.append("-save-temps=obj")
-        r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
+        r = subprocess.run([HIPCC, *FLAGS, "-c", src, "-o", obj], capture_output=True, text=True, cwd=BUILD)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
         if verbose and r.stderr.strip():
             print(r.stderr, file=sys.stderr)
+        if save_temps:
+            # inspection copies (assembly, register counts) from a separate
+            # compile: hipcc's -save-temps pipeline generates different code
+            # (measured: expf loses an FMA contraction), so the objects that are
+            # linked never come from it
+            temps = os.path.join(BUILD, "temps")
+            os.makedirs(temps, exist_ok=True)
+            subprocess.run([HIPCC, *FLAGS, "-c", src, "-o", os.path.join(temps, os.path.basename(obj)),
+                            "-save-temps=obj"], capture_output=True, text=True, cwd=temps)
         return obj
 
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:

@@ -33,17 +33,20 @@ def quantize_weights(W13, W2, transpose=False, out=None, pow2=False, mxfp4=False
     ``out`` (from weight_buffers) receives the result without allocating."""
     L, f2, d = W13.shape
     if mxfp4:
-        if transpose:
-            raise ValueError("MXFP4 weights are quantised for the forward products only")
         e = lambda shape: torch.empty(shape, dtype=torch.uint8, device=W13.device)
+        f = f2 // 2
         if out is None:
             out = dict(w13q=e((L, d // 128, f2, 64)), w13s=e((L, d // 128, f2, 4)),
-                       w2q=e((L, f2 // 256, d, 64)), w2s=e((L, f2 // 256, d, 4)))
+                       w2q=e((L, f // 128, d, 64)), w2s=e((L, f // 128, d, 4)))
+            if transpose:  # for the dgrad products: blocks along the other axis
+                out.update(w13qT=e((L, f2 // 128, d, 64)), w13sT=e((L, f2 // 128, d, 4)),
+                           w2qT=e((L, d // 128, f, 64)), w2sT=e((L, d // 128, f, 4)))
         for W, q, s in ((W13, "w13q", "w13s"), (W2, "w2q", "w2s")):
             if W.dtype != torch.bfloat16 or not W.is_contiguous():
                 raise ValueError("weights must be contiguous bf16")
+            qT, sT = (out[q + "T"], out[s + "T"]) if transpose else (None, None)
             _call("moe_quant_mxfp4", _p(W), W.shape[0], W.shape[1], W.shape[2], W.shape[2], _p(out[q]), _p(out[s]),
-                  _stream())
+                  _p(qT), _p(sT), _stream())
         return out
     if out is None:
         out = weight_buffers(L, d, f2 // 2, W13.device, transpose)
@@ -171,8 +174,8 @@ class TrainPlan(ForwardPlan):
       x 128x1 (transposed);  wgrad GEMMs dW2 = dY^T H, dW13 = [dG, dU]^T X
       softmax-over-selection backward -> d_logits."""
 
-    def __init__(self, T, d, f, E, L, k, e0=0, device="cuda", pow2=False):
-        super().__init__(T, d, f, E, L, k, e0=e0, device=device, save_gu=True, pow2=pow2)
+    def __init__(self, T, d, f, E, L, k, e0=0, device="cuda", pow2=False, mxfp4=False):
+        super().__init__(T, d, f, E, L, k, e0=e0, device=device, save_gu=True, pow2=pow2, mxfp4=mxfp4)
         dv = device
         f32, u8, b16 = torch.float32, torch.uint8, torch.bfloat16
         R = self.rcap
@@ -206,7 +209,7 @@ class TrainPlan(ForwardPlan):
 
     def dgrad2(self, wts):
         _call("moe_grouped_gemm_fp8", _p(self.dyq), _p(self.dyq_s), _p(wts["w2qT"]), _p(wts["w2sT"]),
-              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.f, self.d, ops.EPI_STORE_F32 | self.sflag,
+              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.f, self.d, ops.EPI_STORE_F32 | self.gflag,
               None,
               _p(self.dH), None, None, None, None, None, _stream())
 
@@ -219,7 +222,7 @@ class TrainPlan(ForwardPlan):
     def dgrad1(self, wts):
         _call("moe_grouped_gemm_fp8", _p(self.sb["dgu_q"]), _p(self.sb["dgu_s"]), _p(wts["w13qT"]),
               _p(wts["w13sT"]), _p(self.counts), _p(self.offsets), self.L, self.rcap, self.d, 2 * self.f,
-              ops.EPI_STORE_BF16 | self.sflag, None, _p(self.dX), None, None, None, None, None, _stream())
+              ops.EPI_STORE_BF16 | self.gflag, None, _p(self.dX), None, None, None, None, None, _stream())
 
     def unpermute(self):
         _call("moe_unpermute_combine", _p(self.dX), _p(self.pair_row), None, self.T, self.k, self.d, self.rcap,

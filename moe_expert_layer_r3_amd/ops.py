@@ -46,7 +46,7 @@ _SIGS = {
     "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P,
                                    _P, _I32, _P, _P, _P, _I32, _P, _SZ, _P, _P]),
     "moe_quant_fp8": (ctypes.c_int, [_P, _I32, _I64, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
-    "moe_quant_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, _P]),
+    "moe_quant_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "moe_quant_fp8_rows_t": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _P, _P, _I32, _P]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
                                             _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -240,16 +240,20 @@ def quant_fp8(src, tile=TILE_1x128, groups=1, transpose=False, pow2=False):
     return q, s
 
 
-def quant_mxfp4(src):
+def quant_mxfp4(src, transpose=False):
     """MXFP4 of bf16 src [G, N, K] (or [N, K]) along K: (q [G, K/128, N, 64] u8
-    packed E2M1, scales [G, K/128, N, 4] u8 E8M0 codes), both K-block-major."""
+    packed E2M1, scales [G, K/128, N, 4] u8 E8M0 codes), both K-block-major;
+    with transpose also the transpose's along N: qT [G, N/128, K, 64], sT
+    [G, N/128, K, 4]."""
     _contig(src, torch.bfloat16, "src")
     dev = _dev(src)
     G, N, K = src.shape if src.dim() == 3 else (1,) + tuple(src.shape)
     q = torch.empty((G, K // 128, N, 64), dtype=torch.uint8, device=dev)
     s = torch.empty((G, K // 128, N, 4), dtype=torch.uint8, device=dev)
-    _call("moe_quant_mxfp4", _p(src), G, N, K, K, _p(q), _p(s), _stream(dev))
-    return q, s
+    qT = torch.empty((G, N // 128, K, 64), dtype=torch.uint8, device=dev) if transpose else None
+    sT = torch.empty((G, N // 128, K, 4), dtype=torch.uint8, device=dev) if transpose else None
+    _call("moe_quant_mxfp4", _p(src), G, N, K, K, _p(q), _p(s), _p(qT), _p(sT), _stream(dev))
+    return (q, s, qT, sT) if transpose else (q, s)
 
 
 def mx_scales_rows(s):

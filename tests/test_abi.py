@@ -163,10 +163,12 @@ def test_backward_validation():
 
 def test_mxfp4_validation():
     Q = "moe_quant_mxfp4"
-    assert _rc(Q, FAKE, 1, 4, 96, 96, FAKE, FAKE, None)[0] == -2     # cols % 128
-    assert _rc(Q, FAKE, 1, 4, 128, 64, FAKE, FAKE, None)[0] == -2    # ld < cols
-    assert _rc(Q, None, 1, 4, 128, 128, FAKE, FAKE, None)[0] == -1
-    assert _rc(Q, FAKE, 0, 4, 128, 128, None, None, None)[0] == 0    # empty: nothing to do
+    assert _rc(Q, FAKE, 1, 4, 96, 96, FAKE, FAKE, None, None, None)[0] == -2     # cols % 128
+    assert _rc(Q, FAKE, 1, 4, 128, 64, FAKE, FAKE, None, None, None)[0] == -2    # ld < cols
+    assert _rc(Q, None, 1, 4, 128, 128, FAKE, FAKE, None, None, None)[0] == -1
+    assert _rc(Q, FAKE, 0, 4, 128, 128, None, None, None, None, None)[0] == 0    # empty: nothing to do
+    assert _rc(Q, FAKE, 1, 4, 128, 128, FAKE, FAKE, FAKE, None, None)[0] == -1   # qT without scalesT
+    assert _rc(Q, FAKE, 1, 100, 128, 128, FAKE, FAKE, FAKE, FAKE, None)[0] == -2  # transpose needs rows % 128
     G = "moe_grouped_gemm_fp8"
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 1024, 512, 256, 0, None, FAKE, None, None, None, None, None, None]
     args[10] = 0x200                                                # MXFP4 without POW2

@@ -159,3 +159,99 @@ def test_layer_ep8_full_size_sampled_mxfp4():
     yref = OD.combine(np64(plan.Y), pr[toks], w[toks])
     assert rel_fro(np64(y)[toks], yref) <= TOL
     say("mxfp4 ep8 sampled parity ok")
+
+
+# ------------------------------------------------------------------ training with MXFP4 weights
+
+def test_quant_mxfp4_transpose_bit_exact():
+    rng = np.random.default_rng(61)
+    w = rng.standard_normal((3, 256, 384)) * np.exp2(rng.integers(-20, 20, (3, 256, 1)))
+    w[0, :32, 5] = 0.0                                 # zero column block
+    w[1, 64:96, 7] = 2.0 ** -133                       # subnormal column block
+    w[2, 128:160, 9] = -7.5 * 2.0 ** 2                 # saturating column block
+    w = obf16(w)
+    say("mxfp4 quant with transpose [3, 256, 384]")
+    q, s, qT, sT = ops.quant_mxfp4(bf16_tensor(w), transpose=True)
+    q1, s1 = ops.quant_mxfp4(bf16_tensor(w))
+    assert torch.equal(q, q1) and torch.equal(s, s1)    # the fused pass writes the same forward codes
+    codes, sc = MX.quant_mx(np.swapaxes(w, 1, 2))
+    assert np.array_equal(ops.mx_scales_rows(sT), sc)
+    assert np.array_equal(ops.mx_codes_rows(qT), MX.pack(codes))
+
+
+@pytest.mark.parametrize("counts,K,N", [([0, 1, 130, 300], 256, 512), ([77, 128], 384, 256)])
+def test_gemm_dgrad_mxfp4(counts, K, N):
+    """acc[r] = dY[r] @ W[e] with W [L, K, N] in its forward [out, in] layout:
+    the GEMM reads the transposed MXFP4 copy (blocks along K)."""
+    rng = np.random.default_rng(K + N + 300)
+    L = len(counts)
+    ids = ids_for_counts(counts, k=4, E=32, e0=0, rng=rng)
+    res = ops.permute(gpu(ids), 0, L)
+    rcap = res["row_cap"]
+    A = obf16(rng.standard_normal((rcap, K)))
+    aq, as_ = ops.quant_fp8(bf16_tensor(A), pow2=True)
+    W = obf16(rng.standard_normal((L, K, N)) * 0.02)
+    W[0, :128] *= 30.0
+    _, _, qT, sT = ops.quant_mxfp4(bf16_tensor(W), transpose=True)
+    say(f"mxfp4 gemm dgrad counts={counts} K={K} N={N}")
+    acc = ops.grouped_gemm(aq, as_.t().contiguous(), qT, sT, res["counts"], res["offsets"], ops.EPI_STORE_F32,
+                           mxfp4=True)
+    c, o = npi(res["counts"]), npi(res["offsets"])
+    ref = MX.grouped_forward(npi(aq), npi(as_), c, o, MX.unpack(ops.mx_codes_rows(qT)), ops.mx_scales_rows(sT))
+    assert rel_fro(np64(acc)[_real_rows(res)], ref[_real_rows(res)]) <= ACC_TOL
+
+
+def _train(wl):
+    from moe_expert_layer_r3_amd.layer import TrainPlan
+    lg = synth.logits(wl)
+    x = synth.x(wl)
+    dy = synth.dy(wl)
+    W13 = synth.weights(wl, "w13")
+    W2 = synth.weights(wl, "w2")
+    wts = quantize_weights(W13.to(DEV), W2.to(DEV), transpose=True, mxfp4=True)
+    plan = TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, e0=wl.e0, device=DEV, mxfp4=True)
+    plan.forward(x.to(DEV), gpu(lg), wts)
+    plan.backward(x.to(DEV), dy.to(DEV), wts)
+    torch.cuda.synchronize()
+    return lg, x, dy, W13, W2, wts, plan
+
+
+def test_layer_tiny_train_mxfp4():
+    wl = synth.WORKLOADS["tiny"]
+    say("mxfp4 tiny layer forward + backward")
+    lg, x, dy, W13, W2, wts, plan = _train(wl)
+    ids, w = OR.topk(lg, wl.k)
+    wq = OL.quantize_weights(np64(W13), np64(W2), mx=True)
+    assert np.array_equal(MX.unpack(ops.mx_codes_rows(wts["w13qT"])), wq[0][2])
+    assert np.array_equal(ops.mx_scales_rows(wts["w2sT"]), wq[1][3])
+    fw = OL.forward(np64(x), ids, w, wl.e0, wl.L, wq, mx=True)
+    bw = OL.backward(fw, np64(dy), ids, w, wl.E, wq, mx=True)
+    # as for the FP8 chain: the two chains take their FP8 rounding decisions
+    # on values that differ by fp32 rounding, so 1e-2 bounds the end result
+    for name, got, ref in (("y", plan.y, fw["y"]), ("dx", plan.dx, bw["dx"]), ("dW2", plan.dW2, bw["dW2"]),
+                           ("dW13", plan.dW13, bw["dW13"]), ("d_logits", plan.d_logits, bw["d_logits"])):
+        err = rel_fro(np64(got), ref)
+        say(f"mxfp4 tiny chain {name}: rel err {err:.2e}")
+        assert err <= 1e-2, name
+
+
+def test_layer_train_full_size_sampled_mxfp4():
+    """T=16384 training step with MXFP4 weights through TrainPlan, as the
+    benchmark runs it: both dgrad products on sampled rows of two experts,
+    against the oracle over the GPU's own operands."""
+    wl = synth.WORKLOADS["train"]
+    say("mxfp4 train: GPU forward + backward")
+    lg, x, dy, W13, W2, wts, plan = _train(wl)
+    c, o = npi(plan.counts), npi(plan.offsets)
+    for e in (0, 21):
+        rows = np.arange(o[e], o[e] + c[e])[:: max(1, c[e] // 16)]
+        idx = torch.as_tensor(rows, device=DEV)
+        w2T = MX.unpack(ops.mx_codes_rows(wts["w2qT"][e:e + 1])[0]), ops.mx_scales_rows(wts["w2sT"][e:e + 1])[0]
+        c2, s2 = MX.quant_mx(np64(W2[e]).T)
+        assert np.array_equal(w2T[0], c2) and np.array_equal(w2T[1], s2)
+        dH = MX.matmul(npi(plan.dyq[idx]), np64(plan.dyq_s.t()[idx]), *w2T)
+        assert rel_fro(np64(plan.dH[idx]), dH) <= ACC_TOL
+        w13T = MX.unpack(ops.mx_codes_rows(wts["w13qT"][e:e + 1])[0]), ops.mx_scales_rows(wts["w13sT"][e:e + 1])[0]
+        dX = MX.matmul(npi(plan.sb["dgu_q"][idx]), np64(plan.sb["dgu_s"].t()[idx]), *w13T)
+        assert rel_fro(np64(plan.dX[idx]), obf16(dX)) <= TOL
+    say("mxfp4 train sampled dgrad parity ok")
