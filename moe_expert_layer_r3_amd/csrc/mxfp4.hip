@@ -13,15 +13,20 @@
 
 namespace moe {
 
-// E2M1 code of x (|x| <= 8 after scaling): the count of rounding thresholds
-// below |x|.  The midpoints 0.25, 1.25, 2.5, 5 lie between an even and the next
-// odd code and round down (to the even code); 0.75, 1.75, 3.5 lie between an
-// odd and the next even code and round up.
-__device__ __forceinline__ uint32_t e2m1_code(float x) {
-    const float a = fabsf(x);
-    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-    return c | ((__float_as_uint(x) >> 28) & 8u);
+// Eight already-scaled values (v * 2^-E, exact) to eight E2M1 codes, value i
+// in bits 4i .. 4i+3.  gfx950's v_cvt_scalef32_pk_fp4_f32 rounds x / s to the
+// nearest E2M1 value with ties to the even code, saturates at 6 and keeps the
+// sign (measured against that definition on a dense sweep of [-10, 10],
+// signed zeros included); with s = 1 it does only the rounding, so blocks
+// whose scale 2^-127 is not a normal float need no special case.  The first
+// operand of a pair goes to the low nibble; the last argument picks the byte.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float x[8]) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[0], x[1], 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[2], x[3], 1.0f, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[4], x[5], 1.0f, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[6], x[7], 1.0f, 3);
+    return r;
 }
 
 // One thread per 8 values (one 16-byte load); the 4 threads of a 32-block
@@ -55,9 +60,10 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
     const int ef = (int)((__float_as_uint(am) >> 23) & 0xFFu);  // 0 for zero and subnormal maxima
     const int code = ef == 0 ? 0 : max(ef - 2, 0);                  // E + 127 with E = ef - 129 >= -127
     const float inv = __uint_as_float((uint32_t)(254 - code) << 23); // 2^-E
-    uint32_t packed = 0;
+    float x[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= e2m1_code(v[i] * inv) << (4 * i);
+    for (int i = 0; i < 8; ++i) x[i] = v[i] * inv;
+    const uint32_t packed = e2m1_pack8(x);
     const int64_t g = r / rows, rr = r - g * rows;
     const int64_t blk = (g * (cols >> 7) + (c8 >> 7)) * rows + rr;  // (group, K block, row)
     *reinterpret_cast<uint32_t*>(q + blk * 64 + ((c8 & 127) >> 1)) = packed;
@@ -106,10 +112,10 @@ __global__ __launch_bounds__(256) void quant_mxfp4_both_kernel(const uint16_t* _
         const int ef = (int)((__float_as_uint(am) >> 23) & 0xFFu);
         const int code = ef == 0 ? 0 : max(ef - 2, 0);
         const float inv = __uint_as_float((uint32_t)(254 - code) << 23);
-        uint32_t packed = 0;
+        float x[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) packed |= e2m1_code(v[j][i] * inv) << (4 * i);
-        *reinterpret_cast<uint32_t*>(&rec[0][rq * 8 + j][cg * 4]) = packed;
+        for (int i = 0; i < 8; ++i) x[i] = v[j][i] * inv;
+        *reinterpret_cast<uint32_t*>(&rec[0][rq * 8 + j][cg * 4]) = e2m1_pack8(x);
         if ((cg & 3) == 0) srec[0][rq * 8 + j][cg >> 2] = (uint8_t)code;
     }
     // blocks along rows: column 8cg + i, rows 32*w .. +31
@@ -123,10 +129,10 @@ __global__ __launch_bounds__(256) void quant_mxfp4_both_kernel(const uint16_t* _
         const int ef = (int)((__float_as_uint(am) >> 23) & 0xFFu);
         const int code = ef == 0 ? 0 : max(ef - 2, 0);
         const float inv = __uint_as_float((uint32_t)(254 - code) << 23);
-        uint32_t packed = 0;
+        float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) packed |= e2m1_code(v[j][i] * inv) << (4 * j);
-        *reinterpret_cast<uint32_t*>(&rec[1][cg * 8 + i][rq * 4]) = packed;
+        for (int j = 0; j < 8; ++j) x[j] = v[j][i] * inv;
+        *reinterpret_cast<uint32_t*>(&rec[1][cg * 8 + i][rq * 4]) = e2m1_pack8(x);
         if ((lane >> 4) == 0) srec[1][cg * 8 + i][wave] = (uint8_t)code;
     }
     __syncthreads();
