@@ -388,3 +388,43 @@ def test_forward_graph_replay():
         say(f"graph: replay with input set {it}")
         assert torch.equal(plan.ids, ref_ids)
         assert torch.equal(plan.y, ref)
+
+
+def test_layer_hotspot_full_size_sampled():
+    """The skewed-routing workload (expert 0 receives 8054 of 8192 tokens, the
+    coldest local expert 156): experts of 63 and 2 M-tiles through the same
+    launch as the benchmark's hotspot leg; GEMM rows sampled from the hottest,
+    a middle and the coldest expert, across the whole segment."""
+    wl = synth.WORKLOADS["hotspot"]
+    say("hotspot: generating inputs")
+    lg = synth.logits(wl)
+    x = synth.x(wl)
+    W13 = synth.weights(wl, "w13")
+    W2 = synth.weights(wl, "w2")
+    say("hotspot: GPU forward")
+    out = _layer_forward_gpu(x.to(DEV), gpu(lg), W13.to(DEV), W2.to(DEV), wl.k, wl.e0, wl.L)
+    torch.cuda.synchronize()
+    ids, w = OR.topk(lg, wl.k)
+    assert np.array_equal(npi(out["ids"]), ids)
+    c, o, rp, pr = OD.permute_index(ids, wl.e0, wl.L)
+    res = out["res"]
+    assert np.array_equal(npi(res["counts"]), c) and np.array_equal(npi(res["offsets"]), o)
+    xs_np = np64(x)
+    for e in (0, int(np.argsort(c)[len(c) // 2]), int(np.argmin(c))):
+        say(f"hotspot: expert {e} ({c[e]} rows)")
+        rq, rs = OQ.quant_128x128(np64(W13[e:e + 1]))
+        rq2, rs2 = OQ.quant_128x128(np64(W2[e:e + 1]))
+        rows = np.arange(o[e], o[e] + c[e])[:: max(1, c[e] // 20)]
+        xq, xsc = OQ.quant_1x128(xs_np[rp[rows] // wl.k])
+        assert np.array_equal(npi(res["xq"])[rows], xq)
+        GU = OG.blockscaled_matmul(xq, xsc, rq[0], OG.expand_weight_scales(rs[0]))
+        h = OL.silu(of32(GU[:, :wl.f])) * of32(GU[:, wl.f:])
+        hq_g = npi(out["hq"])[rows]
+        hs_g = npi(out["hs"]).T[rows].astype(np.float64)
+        assert rel_fro(OQ.dequant_1x128(hq_g, hs_g), h) <= 0.05
+        Yref = obf16(OG.blockscaled_matmul(hq_g, hs_g, rq2[0], OG.expand_weight_scales(rs2[0])))
+        assert rel_fro(np64(out["Y"])[rows], Yref) <= TOL
+    toks = np.arange(0, wl.T, 61)
+    yref = OD.combine(np64(out["Y"]), pr[toks], w[toks])
+    assert rel_fro(np64(out["y"])[toks], yref) <= TOL
+    say("hotspot sampled parity ok")
