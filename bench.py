@@ -132,20 +132,32 @@ def roofline_of(flops, nbytes, ms):
             "frac": t_mfma / t}
 
 
+def code_sha256(paths):
+    """sha256 of the sources' code: comments and blank lines removed, each line
+    stripped, so that a comment edit does not orphan a profile while any
+    change to the code does."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for p in paths:
+        text = re.sub(r"/\*.*?\*/", "", open(p).read(), flags=re.S)
+        for line in text.splitlines():
+            line = re.sub(r"//.*", "", line).strip()
+            if line:
+                h.update(line.encode() + b"\n")
+    return h.hexdigest()
+
+
 def measured_traffic(workload):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None when the kernel source changed since then."""
-    import hashlib
+    WRITE_SIZE summary, or None when the kernel code changed since then."""
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"gemm1_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     src = os.path.join(here, "moe_expert_layer_r3_amd", "csrc")
-    h = hashlib.sha256()
-    for f in rec.get("sources", ["gemm.hip", "common.hpp"]):
-        h.update(open(os.path.join(src, f), "rb").read())
-    if h.hexdigest() != rec["source_sha256"]:
+    if code_sha256([os.path.join(src, f) for f in rec["sources"]]) != rec["code_sha256"]:
         return None
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
@@ -429,7 +441,7 @@ def main():
         "config": {"workload": f"{wl.name}: one EP=8 share of a 256-expert top-8 MoE layer forward",
                    "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "local_experts": wl.L, "top_k": wl.k,
                    "local_pairs": head["local_pairs"]},
-        "roofline": {"bound": "hbm", "kernel": "grouped GEMM1 + SwiGLU + quant (gemm_fp8_kernel<256,1,false,false>)",
+        "roofline": {"bound": "hbm", "kernel": "grouped GEMM1 + SwiGLU + quant (gemm_wide_kernel<1,false,false>, 256x256 tiles)",
                      "achieved": g1["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": g1["gbs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic(wl.name)},
         "gemm_tflops": head["gemm_tflops"],

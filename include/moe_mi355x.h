@@ -153,6 +153,11 @@ enum { MOE_SCALE_POW2 = 0x100 };
 /* OR'ed (with MOE_SCALE_POW2) into moe_grouped_gemm_fp8's epilogue: the weights
  * b are MXFP4 from moe_quant_mxfp4 instead of 128x128 FP8.                     */
 enum { MOE_WEIGHT_MXFP4 = 0x200 };
+/* OR'ed into moe_grouped_gemm_fp8's epilogue: compute with 128 x 256 block
+ * tiles instead of the default 256 x 256 ones (N % 256 == 0; with
+ * N % 256 != 0 the 128 x 128 tile is used either way).  The result is the same
+ * up to the order of the fp32 block sums.                                     */
+enum { MOE_GEMM_TILE128 = 0x400 };
 
 /* Quantise src viewed as `groups` matrices of [rows, cols] (row stride ld
  * elements, group stride rows*ld) to OCP e4m3 with one fp32 scale per tile:

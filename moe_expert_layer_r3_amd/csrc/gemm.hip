@@ -35,6 +35,8 @@
 //     and accumulates the scaled block product into the fp32 accumulator
 //     itself.  No partial waits for a VALU rescale, and the ring of raw
 //     partials is gone.
+//   * N % 256 == 0 runs the 256 x 256 variant of this product further below
+//     (gemm_wide_kernel) unless the caller asks for this 128 x 256 one.
 //   * MXFP4 weights (WF4, with P2 activations): B rows are 64 bytes per K step
 //     (E2M1, two per byte) with one E8M0 scale per 32 values; a lane's B
 //     fragment is the 16 bytes of K block lane/16 and its scale byte, and the
@@ -628,8 +630,540 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
     }
 }
 
+// ------------------------------------------------------------------ 256 x 256
+// The same product on 256 x 256 block tiles.  A K step then moves 64 KB of
+// operands for 16.8 MFLOP instead of 48 KB for 8.4 MFLOP: 1.5x fewer line
+// requests per MFMA, which is what bounds the 128-row tile (a CU keeps about
+// 120 line requests in flight).  Eight waves (two per SIMD) as 2 (M) x 4 (N),
+// each 128 x 64: its 128 accumulators leave no room for the ping-pong's
+// all-fragments-at-once phase, so a wave holds its four B fragments of the K
+// step and streams the eight A fragments, one 16-row subtile at a time, each
+// followed by its four MFMAs (and, with fp32 scales, their rescale).  The two
+// waves of a SIMD interleave on their own.  Two LDS stages (64 KB each) and
+// one barrier per K step, placed before the step's last subtile: it frees the
+// stage just read and publishes the next one, whose DMA was issued a step
+// earlier, so a single vmcnt(0) per step suffices and loads may be skipped
+// freely (A rows beyond the expert's padded segment are never fetched, and a
+// wave whose rows are all padding issues no MFMAs).
+constexpr int WBM = 256;
+constexpr int WBN = 256;
+
+template <bool WF4>
+struct WideSmem {
+    static constexpr int A_BYTES = WBM * GBK;
+    static constexpr int B_BYTES = WBN * (WF4 ? GBK / 2 : GBK);
+    static constexpr int S_BYTES = WBM * 4;
+    static constexpr int BS_BYTES = WF4 ? WBN * 4 : 0;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES + BS_BYTES;
+    static constexpr int TOTAL = 2 * STAGE;
+};
+
+template <int EPI, bool P2, bool WF4>
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
+    using SM = WideSmem<WF4>;
+    constexpr int MI = 8, NI = 4;  // 16 x 16 subtiles of a wave's 128 x 64
+    static_assert(!WF4 || P2, "MXFP4 weights take the hardware-scale path");
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
+    __shared__ int tile_base[GMAXL + 1];
+    __shared__ int scan_tmp[GTHREADS];
+    __shared__ float rowmax[4][WBM];
+    __shared__ __attribute__((aligned(8))) float bscale[GMAXKB][2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int L = g.L, N = g.N, K = g.K;
+    const int nkb = K / GBK;
+    const int NT = N / WBN;
+    const int f = N / 2;
+
+    // ---- tile list: per expert ceil(padded rows / 256) m-tiles x NT n-tiles
+    {
+        int loc[2];
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid * 2 + i;
+            int m = 0;
+            if (e < L) {
+                int64_t lo = g.offsets[e], hi = g.offsets[e + 1];
+                if (lo > g.row_cap) lo = g.row_cap;
+                if (hi > g.row_cap) hi = g.row_cap;
+                m = hi > lo ? (int)((hi - lo + WBM - 1) / WBM) : 0;
+            }
+            loc[i] = m;
+            sum += m;
+        }
+        scan_tmp[tid] = sum;
+        __syncthreads();
+        for (int off = 1; off < GTHREADS; off <<= 1) {
+            int add = tid >= off ? scan_tmp[tid - off] : 0;
+            __syncthreads();
+            scan_tmp[tid] += add;
+            __syncthreads();
+        }
+        int run = scan_tmp[tid] - sum;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid * 2 + i;
+            if (e < L) tile_base[e] = run * NT;
+            run += loc[i];
+        }
+        if (tid == 0) tile_base[L] = scan_tmp[GTHREADS - 1] * NT;
+        __syncthreads();
+    }
+    const int total = tile_base[L];
+    const int G = gridDim.x;
+    const int lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+
+    // fragment read offsets (stage-relative), as in the 128-row kernel with
+    // 128-row wave tiles: A row wm*128 + mi*16 + l15, B row wn*64 + ni*16 + l15
+    const int l15 = lane & 15, l7 = lane & 7, c0 = lane >> 4;
+    const uint32_t a_rd0 = (wm * 128 + l15) * 128 + ((c0 ^ l7) << 4);
+    const uint32_t a_rd1 = (wm * 128 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    const int sw4 = ((l15 >> 1) ^ (l15 >> 3)) & 3;
+    const uint32_t b_rd0 = WF4 ? SM::A_BYTES + (wn * 64 + l15) * 64 + ((c0 ^ sw4) << 4)
+                               : SM::A_BYTES + (wn * 64 + l15) * 128 + ((c0 ^ l7) << 4);
+    const uint32_t b_rd1 = SM::A_BYTES + (wn * 64 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    const uint32_t bq_rd = SM::A_BYTES + SM::B_BYTES + SM::S_BYTES + (wn * 64 + l15) * 4 + c0;
+    // A scales of a stage: slot wm*128 + l15*8 + mi holds row wm*128 + mi*16 +
+    // l15, so a lane's eight row scales are 32 contiguous bytes
+    const uint32_t s_rd = SM::A_BYTES + SM::B_BYTES + (wm * 128 + l15 * 8) * 4;
+
+    struct Tile {
+        int64_t row0, real_end, a_lim;  // first row, end of real rows, end of fetchable rows
+        int nt, n0;
+        const uint8_t* a_base;          // this wave's first A row, K block 0
+        const uint8_t* b_base;
+        const uint8_t* bsm;
+        const float* s_base;
+        const float* bs_lo;
+        const float* bs_hi;
+        int rot;
+        int na;                         // A DMA segments of this wave inside a_lim (0..4)
+        int nmi;                        // 16-row subtiles of this wave with real rows (0..8)
+    };
+    auto tile_at = [&](int t) {
+        int lo = 0, hi = L;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tile_base[mid] <= t) lo = mid; else hi = mid;
+        }
+        const int e = __builtin_amdgcn_readfirstlane(lo);
+        const int tb0 = __builtin_amdgcn_readfirstlane(tile_base[e]);
+        const int tb1 = __builtin_amdgcn_readfirstlane(tile_base[e + 1]);
+        const int mt_e = (tb1 - tb0) / NT;
+        const int local = t - tb0;
+        const int grp = local / (GROUP_M * NT);
+        const int gm = min(GROUP_M, mt_e - grp * GROUP_M);
+        const int in = local - grp * GROUP_M * NT;
+        const int nt = in / gm, mt = grp * GROUP_M + (in - (in / gm) * gm);
+        Tile ti;
+        ti.row0 = (int64_t)g.offsets[e] + (int64_t)mt * WBM;
+        ti.real_end = (int64_t)g.offsets[e] + g.counts[e];
+        int64_t lim = g.offsets[e + 1];
+        if (lim > g.row_cap) lim = g.row_cap;
+        ti.a_lim = lim;
+        if (ti.real_end > lim) ti.real_end = lim;
+        {
+            const int64_t left = lim - (ti.row0 + wave * 32);  // rows of this wave's DMA share inside the limit
+            ti.na = left <= 0 ? 0 : (left >= 32 ? 4 : (int)(left / 8));
+            const int64_t real = ti.real_end - (ti.row0 + wm * 128);
+            ti.nmi = real <= 0 ? 0 : (real >= 128 ? MI : (int)((real + 15) / 16));
+        }
+        ti.nt = nt;
+        ti.n0 = nt * WBN;
+        ti.a_base = g.a + (ti.row0 + wave * 32) * K;
+        int brow_w;
+        if constexpr (is_swiglu(EPI)) {
+            brow_w = ((wave & 1) ? f : 0) + nt * 128 + (wave >> 1) * 32;
+        } else {
+            brow_w = ti.n0 + wave * 32;
+        }
+        ti.b_base = WF4 ? g.b + ((int64_t)e * nkb * N + brow_w) * 64 : g.b + ((int64_t)e * N + brow_w) * K;
+        ti.bsm = reinterpret_cast<const uint8_t*>(g.b_s) + ((int64_t)e * nkb * N + brow_w) * 4;
+        ti.s_base = g.a_s + ti.row0;
+        const float* bsx = g.b_s + (int64_t)e * (N / 128) * nkb;
+        int blk0, blk1;
+        if constexpr (is_swiglu(EPI)) {
+            blk0 = nt;
+            blk1 = f / 128 + nt;
+        } else {
+            blk0 = ti.n0 / 128;
+            blk1 = blk0 + 1;
+        }
+        ti.bs_lo = bsx + (int64_t)blk0 * nkb;
+        ti.bs_hi = bsx + (int64_t)blk1 * nkb;
+        ti.rot = ((mt & 1) * 2 + (nt & 3) * 2) % nkb;
+        return ti;
+    };
+    auto stage_bscale = [&](const Tile& ti) {
+        if constexpr (WF4) return;
+        for (int i = tid; i < 2 * nkb; i += GTHREADS) {
+            const int kb = i >> 1, which = i & 1;
+            bscale[kb][which] = (which ? ti.bs_hi : ti.bs_lo)[kb];
+        }
+    };
+    const uint32_t bs_rd = lds_addr(&bscale[0][0]);
+    const bool second_blk = !is_swiglu(EPI) && wn >= 2;
+
+    // DMA lane offsets (1 KB segments of 8 fp8 rows / 16 fp4 rows, XOR
+    // swizzled chunks as in the 128-row kernel)
+    const int lr = lane >> 3;
+    const uint32_t chunk = (uint32_t)(((lane & 7) ^ lr) << 4);
+    const uint32_t a_off0 = (uint32_t)(lr * K) + chunk;  // segment i adds 8*i*K
+    uint32_t b_off0;
+    if constexpr (WF4) {
+        const int r4 = lane >> 2;
+        b_off0 = (uint32_t)(r4 * 64) + (uint32_t)(((lane & 3) ^ (((r4 >> 1) ^ (r4 >> 3)) & 3)) << 4);  // segment i adds 1024*i
+    } else {
+        b_off0 = a_off0;
+    }
+    const uint32_t bs_off = (uint32_t)(lane * 4);
+    // A scales: lane l < 32 of wave w fills slot 32w + l, i.e. row
+    // (w >> 2)*128 + (l & 7)*16 + 4*(w & 3) + (l >> 3)
+    const int s_row = (wave >> 2) * 128 + (lane & 7) * 16 + 4 * (wave & 3) + ((lane >> 3) & 3);
+    const uint32_t s_off = (uint32_t)(s_row * 4);
+
+    // B operand (and its scales) of K block kb into stage st
+    auto issue_b = [&](uint32_t sA, int kr, const Tile& ti) {
+        const uint32_t sB = sA + SM::A_BYTES;
+        if constexpr (WF4) {
+            const uint8_t* bb = ti.b_base + (int64_t)kr * N * 64;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) dma16s(bb, b_off0 + 1024 * i, sB + (wave * 2 + i) * 1024);
+            if (lane < 32)
+                dma4s(ti.bsm + (int64_t)kr * N * 4, bs_off, sB + SM::B_BYTES + SM::S_BYTES + wave * 128);
+        } else {
+            const uint8_t* bb = ti.b_base + kr * GBK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dma16s(bb, b_off0 + (uint32_t)(8 * i * K), sB + (wave * 4 + i) * 1024);
+        }
+    };
+    auto issue_a = [&](uint32_t sA, int kr, const Tile& ti) {
+        const uint8_t* ab = ti.a_base + kr * GBK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i < ti.na) dma16s(ab, a_off0 + (uint32_t)(8 * i * K), sA + (wave * 4 + i) * 1024);
+        if (lane < 32 && ti.row0 + s_row < ti.a_lim)
+            dma4s(ti.s_base + (int64_t)kr * g.row_cap, s_off, sA + SM::A_BYTES + SM::B_BYTES + wave * 128);
+    };
+    auto krot = [&](int kb, const Tile& ti) {
+        int kr = kb + ti.rot;
+        if (kr >= nkb) kr -= nkb;
+        return kr;
+    };
+    auto lds_barrier = [&]() {
+        wait_lgkm0();
+        phase_barrier();
+    };
+
+    const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+    int t = lb;
+    Tile cur;
+    if (t < total) {
+        cur = tile_at(t);
+        stage_bscale(cur);
+        issue_b(sbase, krot(0, cur), cur);
+        issue_a(sbase, krot(0, cur), cur);
+    }
+    for (; t < total; t += G) {
+        v4f acc[MI][NI];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = zero4;
+        const int nmi = cur.nmi;
+
+        // Operands of the current K step held in registers: B fragments (and
+        // fp4 scale codes), A and B scales, and the first A fragment.
+        v8i bfr[NI];
+        int eb4[NI];
+        uint32_t sav[8];
+        uint32_t sbx = 0, sby = 0;
+        v8i afc;
+        auto read_b = [&](auto nc, uint32_t pb0, uint32_t pb1, uint32_t pbs) {
+            constexpr int ni = decltype(nc)::value;
+            if constexpr (WF4) {
+                const u32x4 z4 = {0u, 0u, 0u, 0u};
+                bfr[ni] = join8(lds16<ni * 1024>(pb0), z4);
+                eb4[ni] = (int)lds1<ni * 64>(pbs);
+            } else {
+                bfr[ni] = join8(lds16<ni * 2048>(pb0), lds16<ni * 2048>(pb1));
+            }
+        };
+        auto read_scales = [&](uint32_t ps, uint32_t bsa) {
+            const v2u sbv = lds8<0>(bsa);
+            const u32x4 lo = lds16<0>(ps), hi = lds16<16>(ps);
+            sbx = sbv.x;
+            sby = sbv.y;
+            sav[0] = lo.x; sav[1] = lo.y; sav[2] = lo.z; sav[3] = lo.w;
+            sav[4] = hi.x; sav[5] = hi.y; sav[6] = hi.z; sav[7] = hi.w;
+        };
+        auto read_a = [&](auto mc, uint32_t pa0, uint32_t pa1) {
+            constexpr int mi = decltype(mc)::value;
+            return join8(lds16<mi * 2048>(pa0), lds16<mi * 2048>(pa1));
+        };
+        // every operand of a step, from the stage at LDS address sX
+        auto read_step = [&](uint32_t sX, int kr) {
+            uint32_t pb0 = sX + b_rd0, pb1 = sX + b_rd1, pbs = sX + bq_rd, ps = sX + s_rd;
+            uint32_t pa0 = sX + a_rd0, pa1 = sX + a_rd1, bsa = bs_rd + kr * 8;
+            pin(pb0); pin(pb1); pin(pbs); pin(ps); pin(pa0); pin(pa1); pin(bsa);
+            static_for<0, NI>([&](auto nc) { read_b(nc, pb0, pb1, pbs); });
+            read_scales(ps, bsa);
+            afc = read_a(std::integral_constant<int, 0>{}, pa0, pa1);
+        };
+        // four MFMAs of 16-row subtile mi on fragment af; with fp32 scales
+        // their fresh partials are rescaled into the accumulators
+        auto subtile = [&](auto mc, const v8i& af) {
+            constexpr int mi = decltype(mc)::value;
+            if constexpr (P2) {
+                const int ea = (int)(sav[mi] >> 23);
+                const int eb0 = (int)((second_blk ? sby : sbx) >> 23), eb1 = (int)(sby >> 23);
+                static_for<0, NI>([&](auto nc) {
+                    constexpr int ni = decltype(nc)::value;
+                    constexpr bool second = is_swiglu(EPI) && ni >= NI / 2;
+                    if constexpr (WF4)
+                        acc[mi][ni] = mfma16x16x128_fp4_e8m0(bfr[ni], af, acc[mi][ni], eb4[ni], ea);
+                    else
+                        acc[mi][ni] = mfma16x16x128_e8m0(bfr[ni], af, acc[mi][ni], second ? eb1 : eb0, ea);
+                });
+            } else {
+                const float sa = __uint_as_float(sav[mi]);
+                const float s0 = sa * __uint_as_float(second_blk ? sby : sbx);
+                const float s1 = sa * __uint_as_float(sby);
+                v4f p[NI];
+                static_for<0, NI>([&](auto nc) {
+                    constexpr int ni = decltype(nc)::value;
+                    p[ni] = mfma16x16x128(bfr[ni], af);
+                });
+                static_for<0, NI>([&](auto nc) {
+                    constexpr int ni = decltype(nc)::value;
+                    constexpr bool second = is_swiglu(EPI) && ni >= NI / 2;
+                    acc[mi][ni] += p[ni] * (second ? s1 : s0);
+                });
+            }
+        };
+
+        // One K step from stage st.  Subtiles 0-6 run straight-line code (the
+        // compiler counts the outstanding LDS reads exactly; scheduling
+        // barriers keep the order, since hoisted, the eight A fragments would
+        // not fit next to the accumulators), each reading the next subtile's
+        // A fragment while it multiplies.  Then every LDS read of stage st is
+        // done, and once this wave's DMA of step kb + 1 has landed one
+        // barrier both frees stage st and publishes stage st ^ 1: the DMA of
+        // step kb + 2 goes out, and the last subtile's MFMAs run while the
+        // next step's B fragments, scales and first A fragment are read (each
+        // B fragment right after the MFMA that last uses the old one).  A
+        // wave whose 128 rows are all padding skips the MFMAs and reads; a
+        // partly filled one runs all subtiles (a second, guarded copy of this
+        // code costs the register allocation hundreds of spills).
+        auto kstep = [&](auto st_c, int kb) {
+            constexpr int st = decltype(st_c)::value;
+            const uint32_t sA = sbase + (uint32_t)(st * SM::STAGE);
+            const uint32_t sN = sbase + (uint32_t)((st ^ 1) * SM::STAGE);
+            if (nmi > 0) {
+                uint32_t pa0 = sA + a_rd0, pa1 = sA + a_rd1;
+                pin(pa0); pin(pa1);
+                static_for<0, MI - 1>([&](auto mc) {
+                    constexpr int mi = decltype(mc)::value;
+                    const v8i afn = read_a(std::integral_constant<int, mi + 1>{}, pa0, pa1);
+                    subtile(mc, afc);
+                    __builtin_amdgcn_sched_barrier(0);
+                    afc = afn;
+                });
+            }
+            wait_vmcnt<0>();
+            lds_barrier();
+            if (kb + 2 < nkb) {
+                const int kr2 = krot(kb + 2, cur);
+                issue_b(sA, kr2, cur);
+                issue_a(sA, kr2, cur);
+            }
+            if (nmi > 0) {
+                // reads of the step after the tile's last one fetch unused
+                // values (krot keeps the B-scale index in range)
+                uint32_t pb0 = sN + b_rd0, pb1 = sN + b_rd1, pbs = sN + bq_rd;
+                pin(pb0); pin(pb1); pin(pbs);
+                constexpr int mi = MI - 1;
+                if constexpr (P2) {
+                    const int ea = (int)(sav[mi] >> 23);
+                    const int eb0 = (int)((second_blk ? sby : sbx) >> 23), eb1 = (int)(sby >> 23);
+                    static_for<0, NI>([&](auto nc) {
+                        constexpr int ni = decltype(nc)::value;
+                        constexpr bool second = is_swiglu(EPI) && ni >= NI / 2;
+                        if constexpr (WF4)
+                            acc[mi][ni] = mfma16x16x128_fp4_e8m0(bfr[ni], afc, acc[mi][ni], eb4[ni], ea);
+                        else
+                            acc[mi][ni] = mfma16x16x128_e8m0(bfr[ni], afc, acc[mi][ni], second ? eb1 : eb0, ea);
+                        read_b(nc, pb0, pb1, pbs);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                } else {
+                    const float sa = __uint_as_float(sav[mi]);
+                    const float s0 = sa * __uint_as_float(second_blk ? sby : sbx);
+                    const float s1 = sa * __uint_as_float(sby);
+                    v4f p[NI];
+                    static_for<0, NI>([&](auto nc) {
+                        constexpr int ni = decltype(nc)::value;
+                        p[ni] = mfma16x16x128(bfr[ni], afc);
+                        read_b(nc, pb0, pb1, pbs);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                    static_for<0, NI>([&](auto nc) {
+                        constexpr int ni = decltype(nc)::value;
+                        constexpr bool second = is_swiglu(EPI) && ni >= NI / 2;
+                        acc[mi][ni] += p[ni] * (second ? s1 : s0);
+                    });
+                }
+                uint32_t ps = sN + s_rd, pa0 = sN + a_rd0, pa1 = sN + a_rd1, bsa = bs_rd + krot(kb + 1, cur) * 8;
+                pin(ps); pin(pa0); pin(pa1); pin(bsa);
+                read_scales(ps, bsa);
+                afc = read_a(std::integral_constant<int, 0>{}, pa0, pa1);
+            }
+        };
+
+        // stage 0 (step 0) has landed: step 1 goes out, step 0's operands are read
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (nkb > 1) {
+            const int kr1 = krot(1, cur);
+            issue_b(sbase + SM::STAGE, kr1, cur);
+            issue_a(sbase + SM::STAGE, kr1, cur);
+        }
+        if (nmi > 0) read_step(sbase, krot(0, cur));
+        for (int kb0 = 0; kb0 < nkb; kb0 += 2) {
+            kstep(std::integral_constant<int, 0>{}, kb0);
+            if (kb0 + 1 < nkb) kstep(std::integral_constant<int, 1>{}, kb0 + 1);
+        }
+        // all stages and this tile's B scales are free: the next tile's first
+        // step goes out now and overlaps the epilogue
+        const Tile ep = cur;
+        if (t + G < total) {
+            cur = tile_at(t + G);
+            stage_bscale(cur);
+            issue_b(sbase, krot(0, cur), cur);
+            issue_a(sbase, krot(0, cur), cur);
+        }
+
+        const int lg = lane >> 4;
+        if constexpr (EPI == MOE_EPI_STORE_F32) {
+            float* out = static_cast<float*>(g.out);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const int64_t r = ep.row0 + wm * 128 + mi * 16 + l15;
+                if (r >= ep.real_end) continue;
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+                    *reinterpret_cast<v4f*>(out + r * N + ep.n0 + wn * 64 + ni * 16 + 4 * lg) = acc[mi][ni];
+            }
+        } else if constexpr (EPI == MOE_EPI_STORE_BF16) {
+            uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const int64_t r = ep.row0 + wm * 128 + mi * 16 + l15;
+                if (r >= ep.real_end) continue;
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) {
+                    const v4f a = acc[mi][ni];
+                    *reinterpret_cast<v2u*>(out + r * N + ep.n0 + wn * 64 + ni * 16 + 4 * lg) =
+                        v2u{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w)};
+                }
+            }
+        } else if constexpr (is_swiglu(EPI)) {
+            const int hcol0 = ep.nt * 128;
+            if constexpr (EPI == MOE_EPI_SWIGLU_F32) {
+                float* out = static_cast<float*>(g.out);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    const int64_t r = ep.row0 + wm * 128 + mi * 16 + l15;
+                    if (r >= ep.real_end) continue;
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        v4f h;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) h[v] = silu(acc[mi][ni][v]) * acc[mi][ni + 2][v];
+                        *reinterpret_cast<v4f*>(out + r * f + hcol0 + wn * 32 + ni * 16 + 4 * lg) = h;
+                    }
+                }
+            } else {
+                // h overwrites the U accumulators once G and U are saved; the
+                // row amax goes across the 4 N waves through LDS
+                uint16_t* out2 = static_cast<uint16_t*>(g.out2);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    const int64_t r = ep.row0 + wm * 128 + mi * 16 + l15;
+                    float m = 0.f;
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        const v4f gv = acc[mi][ni], uv = acc[mi][ni + 2];
+                        if constexpr (EPI == MOE_EPI_SWIGLU_Q8_SAVE) {
+                            if (r < ep.real_end) {
+                                const int hc = hcol0 + wn * 32 + ni * 16 + 4 * lg;
+                                *reinterpret_cast<v2u*>(out2 + r * N + hc) =
+                                    v2u{pack_bf16x2(gv.x, gv.y), pack_bf16x2(gv.z, gv.w)};
+                                *reinterpret_cast<v2u*>(out2 + r * N + f + hc) =
+                                    v2u{pack_bf16x2(uv.x, uv.y), pack_bf16x2(uv.z, uv.w)};
+                            }
+                        }
+                        v4f h;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            h[v] = silu(gv[v]) * uv[v];
+                            m = fmaxf(m, fabsf(h[v]));
+                        }
+                        acc[mi][ni + 2] = h;
+                    }
+                    m = fmaxf(m, __shfl_xor(m, 16));
+                    m = fmaxf(m, __shfl_xor(m, 32));
+                    if (lg == 0) rowmax[wn][wm * 128 + mi * 16 + l15] = m;
+                }
+                lds_barrier();
+                uint8_t* out = static_cast<uint8_t*>(g.out);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    const int rt = wm * 128 + mi * 16 + l15;
+                    const int64_t r = ep.row0 + rt;
+                    if (r >= ep.real_end) continue;
+                    const float am = fmaxf(fmaxf(rowmax[0][rt], rowmax[1][rt]), fmaxf(rowmax[2][rt], rowmax[3][rt]));
+                    const TileScale ts = tile_scale_t<P2>(am);
+                    if (lg == 0 && wn == 0) g.out_s[(int64_t)ep.nt * g.row_cap + r] = ts.s;
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        const int hc = hcol0 + wn * 32 + ni * 16 + 4 * lg;
+                        const v4f hv = acc[mi][ni + 2];
+                        *reinterpret_cast<uint32_t*>(out + r * f + hc) =
+                            cvt_e4m3x4(hv.x * ts.inv, hv.y * ts.inv, hv.z * ts.inv, hv.w * ts.inv);
+                    }
+                }
+            }
+        }
+        // row maxima read and the next tile's B scales written before reuse
+        lds_barrier();
+    }
+}
+
+template <int EPI>
+static int launch_wide(const GemmArgs& a, bool p2, bool wf4, hipStream_t stream) {
+    const int ncu = num_cus();
+    const int grid = (ncu + 7) / 8 * 8;
+    if (wf4)
+        gemm_wide_kernel<EPI, true, true><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+    else if (p2)
+        gemm_wide_kernel<EPI, true, false><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+    else
+        gemm_wide_kernel<EPI, false, false><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+    MOE_LAUNCH_CHECK("gemm_wide_kernel");
+    return MOE_OK;
+}
+
 template <int BN, int EPI>
-static int launch_gemm(const GemmArgs& a, bool p2, bool wf4, hipStream_t stream) {
+static int launch_gemm(const GemmArgs& a, bool p2, bool wf4, bool wide, hipStream_t stream) {
+    if constexpr (BN == 256) {
+        if (wide) return launch_wide<EPI>(a, p2, wf4, stream);
+    }
     const int ncu = num_cus();
     const int grid = (ncu + 7) / 8 * 8;  // one 512-thread block per CU (LDS bound), persistent
     if (wf4)
@@ -653,7 +1187,8 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
                                     hipStream_t stream) {
     const bool p2 = (epilogue & MOE_SCALE_POW2) != 0;
     const bool wf4 = (epilogue & MOE_WEIGHT_MXFP4) != 0;
-    epilogue &= ~(MOE_SCALE_POW2 | MOE_WEIGHT_MXFP4);
+    const bool tile128 = (epilogue & MOE_GEMM_TILE128) != 0;
+    epilogue &= ~(MOE_SCALE_POW2 | MOE_WEIGHT_MXFP4 | MOE_GEMM_TILE128);
     MOE_REQUIRE(!wf4 || p2, MOE_ERR_UNSUPPORTED, "grouped_gemm: MXFP4 weights need MOE_SCALE_POW2 activations");
     MOE_REQUIRE(L >= 1 && L <= GMAXL, MOE_ERR_SHAPE, "grouped_gemm: L=%d outside [1, 1024]", L);
     MOE_REQUIRE(row_cap >= 0 && row_cap % GBM == 0 && row_cap <= 0x7FFFFFFF, MOE_ERR_SHAPE,
@@ -676,17 +1211,17 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
     const bool wide = N % 256 == 0;
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
-            return wide ? launch_gemm<256, MOE_EPI_STORE_BF16>(ga, p2, wf4, stream)
-                        : launch_gemm<128, MOE_EPI_STORE_BF16>(ga, p2, wf4, stream);
+            return wide ? launch_gemm<256, MOE_EPI_STORE_BF16>(ga, p2, wf4, !tile128, stream)
+                        : launch_gemm<128, MOE_EPI_STORE_BF16>(ga, p2, wf4, !tile128, stream);
         case MOE_EPI_STORE_F32:
-            return wide ? launch_gemm<256, MOE_EPI_STORE_F32>(ga, p2, wf4, stream)
-                        : launch_gemm<128, MOE_EPI_STORE_F32>(ga, p2, wf4, stream);
+            return wide ? launch_gemm<256, MOE_EPI_STORE_F32>(ga, p2, wf4, !tile128, stream)
+                        : launch_gemm<128, MOE_EPI_STORE_F32>(ga, p2, wf4, !tile128, stream);
         case MOE_EPI_SWIGLU_Q8:
-            return launch_gemm<256, MOE_EPI_SWIGLU_Q8>(ga, p2, wf4, stream);
+            return launch_gemm<256, MOE_EPI_SWIGLU_Q8>(ga, p2, wf4, !tile128, stream);
         case MOE_EPI_SWIGLU_Q8_SAVE:
-            return launch_gemm<256, MOE_EPI_SWIGLU_Q8_SAVE>(ga, p2, wf4, stream);
+            return launch_gemm<256, MOE_EPI_SWIGLU_Q8_SAVE>(ga, p2, wf4, !tile128, stream);
         case MOE_EPI_SWIGLU_F32:
-            return launch_gemm<256, MOE_EPI_SWIGLU_F32>(ga, p2, wf4, stream);
+            return launch_gemm<256, MOE_EPI_SWIGLU_F32>(ga, p2, wf4, !tile128, stream);
     }
     return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm: epilogue %d", epilogue);
 }

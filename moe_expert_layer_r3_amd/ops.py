@@ -18,6 +18,7 @@ EPI_STORE_BF16, EPI_SWIGLU_Q8, EPI_SWIGLU_Q8_SAVE, EPI_STORE_F32, EPI_SWIGLU_F32
 TILE_1x128, TILE_128x128 = 0, 1
 SCALE_POW2 = 0x100  # power-of-two (UE8M0) tile scales, OR'ed into tile / epilogue
 WEIGHT_MXFP4 = 0x200  # MXFP4 weights, OR'ed (with SCALE_POW2) into a GEMM epilogue
+GEMM_TILE128 = 0x400  # 128 x 256 GEMM tiles instead of 256 x 256, OR'ed into a GEMM epilogue
 SRC_BF16, SRC_F32 = 0, 1
 FLAG_BAD_ID, FLAG_DUP_ID, FLAG_ROW_CAP = 1, 2, 4
 ROW_ALIGN = 128
@@ -297,13 +298,14 @@ def quant_rows_t(src, w, row_pair, offsets, L, rcap, k, pow2=False):
 # ---------------------------------------------------------------- GEMMs
 
 def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_in=None, rcap=None, pow2=False,
-                 mxfp4=False):
+                 mxfp4=False, tile128=False):
     """Per-expert blockwise-scaled FP8 GEMM over the expert-grouped rows.
 
     a [rcap, K] u8, a_s [K/128, rcap]; b [L, N, K] u8, b_s [L, N/128, K/128].
     pow2: every scale is a power of two, applied by the MFMA as E8M0 (the
     SwiGLU epilogues then also quantise h with power-of-two scales).
     mxfp4: b [L, K/128, N, 64] and b_s [L, K/128, N, 4] from quant_mxfp4 (implies pow2).
+    tile128: 128 x 256 block tiles instead of 256 x 256 (N % 256 == 0).
     Returns the epilogue's outputs: STORE_BF16 -> y; STORE_F32 -> acc;
     SWIGLU_Q8 -> (hq, hq_s); SWIGLU_Q8_SAVE -> (hq, hq_s, gu);
     SWIGLU_F32 -> h."""
@@ -336,7 +338,7 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     else:
         raise ValueError(f"unknown epilogue {epilogue}")
     _call("moe_grouped_gemm_fp8", _p(a), _p(a_s), _p(b), _p(b_s), _p(counts), _p(offsets), L, rcap, N, K,
-          epilogue | _flag(pow2) | (WEIGHT_MXFP4 if mxfp4 else 0), _p(epi_in), _p(out), _p(out_s), _p(out2), _p(out2_s), _p(out3), _p(out3_s),
+          epilogue | _flag(pow2) | (WEIGHT_MXFP4 if mxfp4 else 0) | (GEMM_TILE128 if tile128 else 0), _p(epi_in), _p(out), _p(out_s), _p(out2), _p(out2_s), _p(out3), _p(out3_s),
           _stream(dev))
     return res
 

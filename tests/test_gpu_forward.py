@@ -225,13 +225,19 @@ def _real_rows(res):
     return np.concatenate([np.arange(o[e], o[e] + c[e]) for e in range(len(c))]).astype(np.int64)
 
 
+# tile128: the 128 x 256 kernel instead of the default 256 x 256 one (the cases
+# cover 256-row tiles that reach past their expert's segment, tiles whose
+# second half is padding, and experts with several 256-row tiles)
+@pytest.mark.parametrize("tile128", [False, True])
 @pytest.mark.parametrize("counts,K,N", [([0, 1, 130, 300], 256, 512), ([128, 256, 5, 0, 77, 129], 384, 256),
-                                        ([40], 128, 128), ([200, 3], 640, 384)])
-def test_gemm_store(counts, K, N):
+                                        ([40], 128, 128), ([200, 3], 640, 384), ([1100, 700, 3], 256, 256)])
+def test_gemm_store(counts, K, N, tile128):
     res, wq, ws, L = _gemm_problem(counts, K, N, seed=K + N)
-    say(f"gemm STORE counts={counts} K={K} N={N}")
-    acc = ops.grouped_gemm(res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"], ops.EPI_STORE_F32)
-    y = ops.grouped_gemm(res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"], ops.EPI_STORE_BF16)
+    say(f"gemm STORE counts={counts} K={K} N={N} tile128={tile128}")
+    acc = ops.grouped_gemm(res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"], ops.EPI_STORE_F32,
+                           tile128=tile128)
+    y = ops.grouped_gemm(res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"], ops.EPI_STORE_BF16,
+                         tile128=tile128)
     c, o = npi(res["counts"]), npi(res["offsets"])
     ref = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, npi(wq), npi(ws))
     rows = _real_rows(res)
@@ -239,14 +245,16 @@ def test_gemm_store(counts, K, N):
     assert rel_fro(np64(y)[rows], obf16(ref[rows])) <= TOL
 
 
-@pytest.mark.parametrize("counts,K,f", [([0, 1, 130, 300], 256, 256), ([129, 64], 384, 384), ([256], 128, 128)])
-def test_gemm_swiglu(counts, K, f):
+@pytest.mark.parametrize("tile128", [False, True])
+@pytest.mark.parametrize("counts,K,f", [([0, 1, 130, 300], 256, 256), ([129, 64], 384, 384), ([256], 128, 128),
+                                        ([700, 257], 256, 128)])
+def test_gemm_swiglu(counts, K, f, tile128):
     res, wq, ws, L = _gemm_problem(counts, K, 2 * f, seed=K + f + 1)
-    say(f"gemm SWIGLU counts={counts} K={K} f={f}")
+    say(f"gemm SWIGLU counts={counts} K={K} f={f} tile128={tile128}")
     args = (res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"])
-    h32 = ops.grouped_gemm(*args, ops.EPI_SWIGLU_F32)
-    hq, hs = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8)
-    hq2, hs2, gu = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8_SAVE)
+    h32 = ops.grouped_gemm(*args, ops.EPI_SWIGLU_F32, tile128=tile128)
+    hq, hs = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8, tile128=tile128)
+    hq2, hs2, gu = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8_SAVE, tile128=tile128)
     c, o = npi(res["counts"]), npi(res["offsets"])
     GU = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, npi(wq), npi(ws))
     G, U = of32(GU[:, :f]), of32(GU[:, f:])

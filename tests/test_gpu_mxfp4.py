@@ -66,27 +66,29 @@ def _ref(res, q, s):
     return MX.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, MX.unpack(ops.mx_codes_rows(q)), ops.mx_scales_rows(s))
 
 
+@pytest.mark.parametrize("tile128", [False, True])
 @pytest.mark.parametrize("counts,K,N", [([0, 1, 130, 300], 256, 512), ([128, 256, 5, 0, 77, 129], 384, 256),
                                         ([40], 128, 128), ([200, 3], 640, 384)])
-def test_gemm_store_mxfp4(counts, K, N):
+def test_gemm_store_mxfp4(counts, K, N, tile128):
     res, q, s = _problem(counts, K, N, seed=K + N + 200)
-    say(f"mxfp4 gemm STORE counts={counts} K={K} N={N}")
+    say(f"mxfp4 gemm STORE counts={counts} K={K} N={N} tile128={tile128}")
     args = (res["xq"], res["xq_s"], q, s, res["counts"], res["offsets"])
-    acc = ops.grouped_gemm(*args, ops.EPI_STORE_F32, mxfp4=True)
-    y = ops.grouped_gemm(*args, ops.EPI_STORE_BF16, mxfp4=True)
+    acc = ops.grouped_gemm(*args, ops.EPI_STORE_F32, mxfp4=True, tile128=tile128)
+    y = ops.grouped_gemm(*args, ops.EPI_STORE_BF16, mxfp4=True, tile128=tile128)
     ref = _ref(res, q, s)
     rows = _real_rows(res)
     assert rel_fro(np64(acc)[rows], ref[rows]) <= ACC_TOL
     assert rel_fro(np64(y)[rows], obf16(ref[rows])) <= TOL
 
 
+@pytest.mark.parametrize("tile128", [False, True])
 @pytest.mark.parametrize("counts,K,f", [([0, 1, 130, 300], 256, 256), ([129, 64], 384, 384), ([256], 128, 128)])
-def test_gemm_swiglu_mxfp4(counts, K, f):
+def test_gemm_swiglu_mxfp4(counts, K, f, tile128):
     res, q, s = _problem(counts, K, 2 * f, seed=K + f + 201)
-    say(f"mxfp4 gemm SWIGLU counts={counts} K={K} f={f}")
+    say(f"mxfp4 gemm SWIGLU counts={counts} K={K} f={f} tile128={tile128}")
     args = (res["xq"], res["xq_s"], q, s, res["counts"], res["offsets"])
-    h32 = ops.grouped_gemm(*args, ops.EPI_SWIGLU_F32, mxfp4=True)
-    hq, hs = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8, mxfp4=True)
+    h32 = ops.grouped_gemm(*args, ops.EPI_SWIGLU_F32, mxfp4=True, tile128=tile128)
+    hq, hs = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8, mxfp4=True, tile128=tile128)
     GU = _ref(res, q, s)
     h_ref = OL.silu(of32(GU[:, :f])) * of32(GU[:, f:])
     rows = _real_rows(res)

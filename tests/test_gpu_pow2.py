@@ -105,32 +105,34 @@ def _real_rows(res):
     return np.concatenate([np.arange(o[e], o[e] + c[e]) for e in range(len(c))]).astype(np.int64)
 
 
+@pytest.mark.parametrize("tile128", [False, True])
 @pytest.mark.parametrize("counts,K,N", [([0, 1, 130, 300], 256, 512), ([128, 256, 5, 0, 77, 129], 384, 256),
                                         ([40], 128, 128), ([200, 3], 640, 384)])
-def test_gemm_store_pow2(counts, K, N):
+def test_gemm_store_pow2(counts, K, N, tile128):
     res, wq, ws = _problem(counts, K, N, seed=K + N + 100)
-    say(f"pow2 gemm STORE counts={counts} K={K} N={N}")
+    say(f"pow2 gemm STORE counts={counts} K={K} N={N} tile128={tile128}")
     args = (res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"])
-    acc = ops.grouped_gemm(*args, ops.EPI_STORE_F32, pow2=True)
-    y = ops.grouped_gemm(*args, ops.EPI_STORE_BF16, pow2=True)
+    acc = ops.grouped_gemm(*args, ops.EPI_STORE_F32, pow2=True, tile128=tile128)
+    y = ops.grouped_gemm(*args, ops.EPI_STORE_BF16, pow2=True, tile128=tile128)
     c, o = npi(res["counts"]), npi(res["offsets"])
     ref = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, npi(wq), npi(ws))
     rows = _real_rows(res)
     assert rel_fro(np64(acc)[rows], ref[rows]) <= ACC_TOL
     assert rel_fro(np64(y)[rows], obf16(ref[rows])) <= TOL
     # the fp32-scale kernel on the same (power-of-two) scales sums the same terms
-    acc32 = ops.grouped_gemm(*args, ops.EPI_STORE_F32)
+    acc32 = ops.grouped_gemm(*args, ops.EPI_STORE_F32, tile128=tile128)
     assert rel_fro(np64(acc)[rows], np64(acc32)[rows]) <= ACC_TOL
 
 
+@pytest.mark.parametrize("tile128", [False, True])
 @pytest.mark.parametrize("counts,K,f", [([0, 1, 130, 300], 256, 256), ([129, 64], 384, 384), ([256], 128, 128)])
-def test_gemm_swiglu_pow2(counts, K, f):
+def test_gemm_swiglu_pow2(counts, K, f, tile128):
     res, wq, ws = _problem(counts, K, 2 * f, seed=K + f + 101)
-    say(f"pow2 gemm SWIGLU counts={counts} K={K} f={f}")
+    say(f"pow2 gemm SWIGLU counts={counts} K={K} f={f} tile128={tile128}")
     args = (res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"])
-    h32 = ops.grouped_gemm(*args, ops.EPI_SWIGLU_F32, pow2=True)
-    hq, hs = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8, pow2=True)
-    hq2, hs2, gu = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8_SAVE, pow2=True)
+    h32 = ops.grouped_gemm(*args, ops.EPI_SWIGLU_F32, pow2=True, tile128=tile128)
+    hq, hs = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8, pow2=True, tile128=tile128)
+    hq2, hs2, gu = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8_SAVE, pow2=True, tile128=tile128)
     c, o = npi(res["counts"]), npi(res["offsets"])
     GU = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, npi(wq), npi(ws))
     f_ = GU.shape[1] // 2
