@@ -94,7 +94,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     constexpr int SROWS = BN / 8;          // B scales loaded per wave
     constexpr int NLD = ASEG + BSEG + 2;   // DMA instructions per wave per stage (+ A and B scales)
     constexpr int NST = 2 * NI;            // 16-byte stores per wave per tile
-    static_assert(SROWS <= 64 && NLD + 2 * NST < 64, "DMA lanes, vmcnt range");
+    static_assert(SROWS <= 64 && 2 * NLD + 2 * NST < 64, "DMA lanes, vmcnt range");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
     int* const tab = reinterpret_cast<int*>(smem + SM::TAB);
@@ -221,20 +221,34 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         return g.dW + (int64_t)e * M * N + (int64_t)p.mt * WBM * N + (int64_t)p.nt * BN;
     };
 
+    // Waves 0-3 (one per SIMD) issue every stage's DMA: each moves its own
+    // share and that of wave + 4 (A rows 4*ASEG*8 further, B rows 4*BSEG*8,
+    // scales as the A rows), so waves 4-7 never stall on a DMA issue and keep
+    // the matrix cores busy meanwhile.  Waves 4-7 issue no loads and so wait
+    // for none: a stage is published by the barrier that follows the DMA
+    // waves' own vmcnt wait.
+    const bool dma_wave = wave < 4;
     auto issue = [&](auto stage_c, int kb, const Src& s) {
         constexpr int stage = decltype(stage_c)::value;
+        if (!dma_wave) return;
         const uint32_t sA = sbase + (uint32_t)(stage * SM::STAGE);
         const uint32_t sB = sA + SM::A_BYTES;
         const uint32_t sSA = sB + SM::B_BYTES;
         const uint32_t sSB = sSA + SM::SA_BYTES;
         const uint8_t* a = s.a + (int64_t)kb * M * WBK;
         const uint8_t* b = s.b + (int64_t)kb * N * WBK;
+        static_for<0, 2>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;  // 0: own share, 1: wave + 4's
+            const int w = wave + 4 * h;
 #pragma unroll
-        for (int i = 0; i < ASEG; ++i) dma16s(a + i * 1024, seg_off, sA + (wave * ASEG + i) * 1024);
+            for (int i = 0; i < ASEG; ++i)
+                dma16s(a + (h * 4 * ASEG * 8) * WBK + i * 1024, seg_off, sA + (w * ASEG + i) * 1024);
 #pragma unroll
-        for (int i = 0; i < BSEG; ++i) dma16s(b + i * 1024, seg_off, sB + (wave * BSEG + i) * 1024);
-        if (lane < 16) dma4s(s.sa + (int64_t)kb * M, sa_off, sSA + wave * 64);
-        if (lane < SROWS) dma4s(s.sb + (int64_t)kb * N, sb_off, sSB + wave * SROWS * 4);
+            for (int i = 0; i < BSEG; ++i)
+                dma16s(b + (h * 4 * BSEG * 8) * WBK + i * 1024, seg_off, sB + (w * BSEG + i) * 1024);
+            if (lane < 16) dma4s(s.sa + (int64_t)kb * M, sa_off + h * 64 * 4, sSA + w * 64);
+            if (lane < SROWS) dma4s(s.sb + (int64_t)kb * N + h * 4 * SROWS, sb_off, sSB + w * SROWS * 4);
+        });
     };
 
     // issue cursor: the K step two ahead of the one being waited for
@@ -384,14 +398,17 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         issue_next(S0{});
         // vector-memory ops issued after the stage the next step waits for:
         // stores two steps back, the next stage's loads, stores one step back
-        int yng = issue_next(S1{}) ? NLD : 0;
+        // (a DMA wave issues 2 * NLD loads per stage, the others none)
+        constexpr int NLD2 = 2 * NLD;
+        int yng = issue_next(S1{}) ? NLD2 : 0;
         int ns1 = 0;  // NST if the previous step issued stores
         auto wait_stage = [&]() {
-            if (yng == NLD) wait_vmcnt<NLD>();  // no stores in flight: the common case
-            else wait_younger<NLD, NST>(yng);
+            if (!dma_wave) return;
+            if (yng == NLD2) wait_vmcnt<NLD2>();  // no stores in flight: the common case
+            else wait_younger<NLD2, NST>(yng);
         };
         auto account = [&](bool iss, bool sto) {
-            yng = ns1 + (iss ? NLD : 0) + (sto ? NST : 0);
+            yng = ns1 + (iss ? NLD2 : 0) + (sto ? NST : 0);
             ns1 = sto ? NST : 0;
         };
         Pos cp = p0;  // tile of the block being computed
