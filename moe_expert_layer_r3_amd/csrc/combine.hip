@@ -75,8 +75,12 @@ __global__ __launch_bounds__(CBLOCK) void combine_kernel(const uint16_t* __restr
 // j: dY = fp32(w_j * dy) quantised 1x128 (the tile amax of the rounded
 // products is fp32(|w_j| * amax|dy|) because rounding is monotonic), and the
 // partial dot <dy, Y_r> for d_gate.  Per local slot (a uniform branch) the
-// group's Y tile loads are issued together before any is used.
-constexpr int TPG = 7;
+// group's Y tile loads are issued together before any is used.  Two tiles per
+// group and pass (four passes over d = 7168) keep the kernel at about 70
+// registers, so enough tokens are in flight per CU to hide the row latency:
+// measured at the training shape, 7 tiles per pass (one pass, 168 registers)
+// 190 us, 4 tiles 166 us, 2 tiles 156 us.
+constexpr int TPG = 2;
 template <bool P2>
 __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __restrict__ dy,
                                                              const uint16_t* __restrict__ y_perm,
@@ -85,10 +89,19 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
                                                              uint8_t* __restrict__ dyq, float* __restrict__ dyq_s,
                                                              float* __restrict__ d_gate, int64_t row_cap) {
     __shared__ float part[CBLOCK / 64][CMAXK];
+    __shared__ int slot_row[CMAXK];
+    __shared__ float slot_w[CMAXK];
     const int64_t t = blockIdx.x;
     const int sub = threadIdx.x & 15, grp = threadIdx.x >> 4;  // 8 groups of 16 lanes
     const int wave = threadIdx.x >> 6;
     const int ntile = d >> 7;
+    // the token's slots (rows and weights) are staged in LDS once, while the
+    // dy row loads: no slot then waits on a global load of its own row index
+    if (threadIdx.x < k) {
+        slot_row[threadIdx.x] = pair_row[t * k + threadIdx.x];
+        slot_w[threadIdx.x] = w[t * k + threadIdx.x];
+    }
+    bool staged = false;
     for (int t0 = 0; t0 < ntile; t0 += (CBLOCK / 16) * TPG) {
         float v[TPG][8], am[TPG];
 #pragma unroll
@@ -108,13 +121,19 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
             for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[q][i]));
             am[q] = group_max<16>(m);
         }
-        // one body for all slots (kept rolled: the quantiser makes it long)
+        if (!staged) {
+            __syncthreads();
+            staged = true;
+        }
+        // one body for all slots (kept rolled: the quantiser makes it long);
+        // a slot that is not local costs a skipped branch only
 #pragma unroll 1
         for (int j = 0; j < k; ++j) {
-            const int64_t r = pair_row[t * k + j];  // uniform
+            const int64_t r = slot_row[j];  // uniform
+            if (r < 0) continue;
             float dot = 0.f;
-            if (r >= 0) {
-                const float wj = w[t * k + j];
+            {
+                const float wj = slot_w[j];
                 uint4 ys[TPG];
 #pragma unroll
                 for (int q = 0; q < TPG; ++q) {
@@ -157,8 +176,9 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
     if (threadIdx.x < k) {
         const int j = threadIdx.x;
         float s = 0.f;
-        for (int wv = 0; wv < CBLOCK / 64; ++wv) s += part[wv][j];
-        d_gate[t * k + j] = pair_row[t * k + j] >= 0 ? s : 0.f;
+        if (slot_row[j] >= 0)
+            for (int wv = 0; wv < CBLOCK / 64; ++wv) s += part[wv][j];
+        d_gate[t * k + j] = s;
     }
 }
 
