@@ -133,6 +133,9 @@ def test_gemm_validation():
     assert call(a10=1) == -1             # SWIGLU_Q8 without out_s
     assert call(a10=1, a8=384, a13=FAKE) == -2    # SwiGLU needs N % 256
     assert call(a0=None) == -1
+    # the 128 x 256 tile flag is recognised: the same argument checks still apply
+    assert call(a10=0x400, a8=100) == -2 and call(a10=0x401) == -1 and call(a10=0x409) == -3
+    assert ops.GEMM_TILE128 == 0x400
 
 
 def test_combine_validation():
