@@ -632,9 +632,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 
 // ------------------------------------------------------------------ 256 x 256
 // The same product on 256 x 256 block tiles.  A K step then moves 64 KB of
-// operands for 16.8 MFLOP instead of 48 KB for 8.4 MFLOP: 1.5x fewer line
-// requests per MFMA, which is what bounds the 128-row tile (a CU keeps about
-// 120 line requests in flight).  Eight waves (two per SIMD) as 2 (M) x 4 (N),
+// operands for 16.8 MFLOP instead of 48 KB for 8.4 MFLOP (1.5x fewer bytes
+// per MFMA from L2 and 25% fewer LDS fragment bytes).  Measured, the gain is
+// smaller than that (hot-spot GEMM1 10%, ep8 GEMM1 2%): with every operand
+// an L2 hit the kernel is only ~15% faster, while leaving out the global ->
+// LDS DMA altogether makes it ~35% faster, so the DMA path, not bandwidth,
+// bounds it.  Eight waves (two per SIMD) as 2 (M) x 4 (N),
 // each 128 x 64: its 128 accumulators leave no room for the ping-pong's
 // all-fragments-at-once phase, so a wave holds its four B fragments of the K
 // step and streams the eight A fragments, one 16-row subtile at a time, each
@@ -644,7 +647,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 // stage just read and publishes the next one, whose DMA was issued a step
 // earlier, so a single vmcnt(0) per step suffices and loads may be skipped
 // freely (A rows beyond the expert's padded segment are never fetched, and a
-// wave whose rows are all padding issues no MFMAs).
+// wave whose rows are all padding issues no MFMAs).  Waves 0-3 issue all of
+// a step's DMA (below), so waves 4-7 never stall on it.
 constexpr int WBM = 256;
 constexpr int WBN = 256;
 #ifndef MOE_WIDE_DMA_WAVES
@@ -834,7 +838,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
     const int s_row = (wave >> 2) * 128 + (lane & 7) * 16 + 4 * (wave & 3) + ((lane >> 3) & 3);
     const uint32_t s_off = (uint32_t)(s_row * 4);
 
-    // B operand (and its scales) of K block kb into stage st
+    // issue_b / issue_a: the B (weights, with their fp4 scales) and A
+    // (activations, with their scales) operands of a K block into a stage.
     // The DMA of a K step is issued by MOE_WIDE_DMA_WAVES waves: waves 0-3
     // (the default), one per SIMD, each also moving the share of wave + 4
     // (its A rows are 128 further, its B rows 128 further, or 64 for the
