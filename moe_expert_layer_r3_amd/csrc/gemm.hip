@@ -736,9 +736,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                                : SM::A_BYTES + (wn * 64 + l15) * 128 + ((c0 ^ l7) << 4);
     const uint32_t b_rd1 = SM::A_BYTES + (wn * 64 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
     const uint32_t bq_rd = SM::A_BYTES + SM::B_BYTES + SM::S_BYTES + (wn * 64 + l15) * 4 + c0;
-    // A scales of a stage: slot wm*128 + l15*8 + mi holds row wm*128 + mi*16 +
-    // l15, so a lane's eight row scales are 32 contiguous bytes
-    const uint32_t s_rd = SM::A_BYTES + SM::B_BYTES + (wm * 128 + l15 * 8) * 4;
+    // A scales of a stage in row order (one 1 KB DMA per K step): a lane's
+    // eight rows wm*128 + mi*16 + l15 are 64 bytes apart
+    const uint32_t s_rd = SM::A_BYTES + SM::B_BYTES + (wm * 128 + l15) * 4;
 
     struct Tile {
         int64_t row0, real_end, a_lim;  // first row, end of real rows, end of fetchable rows
@@ -833,10 +833,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         b_off0 = a_off0;
     }
     const uint32_t bs_off = (uint32_t)(lane * 4);
-    // A scales: lane l < 32 of wave w fills slot 32w + l, i.e. row
-    // (w >> 2)*128 + (l & 7)*16 + 4*(w & 3) + (l >> 3)
-    const int s_row = (wave >> 2) * 128 + (lane & 7) * 16 + 4 * (wave & 3) + ((lane >> 3) & 3);
-    const uint32_t s_off = (uint32_t)(s_row * 4);
+    // A scales: the tile's 256 row scales of a K block are 1 KB contiguous
+    // (K-block-major layout): wave 0 moves them with one 16-byte-per-lane
+    // DMA, lane l rows 4l .. 4l + 3 (a 128-row boundary never splits them)
+    const uint32_t s_off = (uint32_t)(lane * 16);
 
     // issue_b / issue_a: the B (weights, with their fp4 scales) and A
     // (activations, with their scales) operands of a K block into a stage.
@@ -873,11 +873,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (i < na) dma16s(ab, a_off0 + (uint32_t)(8 * i * K), sA + (w * 4 + i) * 1024);
-            if (lane < 32 && ti.row0 + s_row + row_off < ti.a_lim)
-                dma4s(ti.s_base + (int64_t)kr * g.row_cap + row_off, s_off, sA + SM::A_BYTES + SM::B_BYTES + w * 128);
         };
         if (dma_self) one(wave, ti.na, 0);
         if (dma_pair) one(wave + 4, ti.na_p, 128);
+        if (wave == 0 && ti.row0 + 4 * lane < ti.a_lim)
+            dma16s(ti.s_base + (int64_t)kr * g.row_cap, s_off, sA + SM::A_BYTES + SM::B_BYTES);
     };
     auto krot = [&](int kb, const Tile& ti) {
         int kr = kb + ti.rot;
@@ -925,11 +925,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         };
         auto read_scales = [&](uint32_t ps, uint32_t bsa) {
             const v2u sbv = lds8<0>(bsa);
-            const u32x4 lo = lds16<0>(ps), hi = lds16<16>(ps);
             sbx = sbv.x;
             sby = sbv.y;
-            sav[0] = lo.x; sav[1] = lo.y; sav[2] = lo.z; sav[3] = lo.w;
-            sav[4] = hi.x; sav[5] = hi.y; sav[6] = hi.z; sav[7] = hi.w;
+            static_for<0, 8>([&](auto mc) {
+                constexpr int mi = decltype(mc)::value;
+                sav[mi] = lds4<mi * 64>(ps);
+            });
         };
         auto read_a = [&](auto mc, uint32_t pa0, uint32_t pa1) {
             constexpr int mi = decltype(mc)::value;
