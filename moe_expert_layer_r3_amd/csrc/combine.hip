@@ -97,7 +97,7 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
     const int ntile = d >> 7;
     // the token's slots (rows and weights) are staged in LDS once, while the
     // dy row loads: no slot then waits on a global load of its own row index
-    if (threadIdx.x < k) {
+    if ((int)threadIdx.x < k) {
         slot_row[threadIdx.x] = pair_row[t * k + threadIdx.x];
         slot_w[threadIdx.x] = w[t * k + threadIdx.x];
     }
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
         }
     }
     __syncthreads();
-    if (threadIdx.x < k) {
+    if ((int)threadIdx.x < k) {
         const int j = threadIdx.x;
         float s = 0.f;
         if (slot_row[j] >= 0)
