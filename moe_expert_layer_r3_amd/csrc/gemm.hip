@@ -1090,17 +1090,35 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                     *reinterpret_cast<v4f*>(out + r * N + ep.n0 + wn * 64 + ni * 16 + 4 * lg) = acc[mi][ni];
             }
         } else if constexpr (EPI == MOE_EPI_STORE_BF16) {
+            // two cross-lane swaps per pair of n-subtiles regroup a row's
+            // columns so that lane group lg holds columns 8lg .. 8lg + 7 of
+            // each 32-column pair: one 16-byte store where the MFMA layout
+            // gives two 8-byte ones (half the store instructions, each of
+            // which costs the texture addresser as much as a 1 KB load).  The
+            // swaps run on every lane; only the stores skip padding rows.
             uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
                 const int64_t r = ep.row0 + wm * 128 + mi * 16 + l15;
-                if (r >= ep.real_end) continue;
+                uint32_t x[NI], y[NI];  // columns (0, 1) and (2, 3) of each subtile, packed bf16
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni) {
                     const v4f a = acc[mi][ni];
-                    *reinterpret_cast<v2u*>(out + r * N + ep.n0 + wn * 64 + ni * 16 + 4 * lg) =
-                        v2u{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w)};
+                    x[ni] = pack_bf16x2(a.x, a.y);
+                    y[ni] = pack_bf16x2(a.z, a.w);
                 }
+#pragma unroll
+                for (int ni = 0; ni < NI; ni += 2) {
+                    swap32(x[ni], x[ni + 1]);
+                    swap32(y[ni], y[ni + 1]);
+                    swap16(x[ni], x[ni + 1]);
+                    swap16(y[ni], y[ni + 1]);
+                }
+                if (r >= ep.real_end) continue;
+#pragma unroll
+                for (int h = 0; h < NI / 2; ++h)
+                    *reinterpret_cast<u32x4*>(out + r * N + ep.n0 + wn * 64 + 32 * h + 8 * lg) =
+                        u32x4{x[2 * h], y[2 * h], x[2 * h + 1], y[2 * h + 1]};
             }
         } else if constexpr (is_swiglu(EPI)) {
             const int hcol0 = ep.nt * 128;
