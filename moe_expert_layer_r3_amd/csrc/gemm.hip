@@ -1144,18 +1144,35 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 for (int mi = 0; mi < MI; ++mi) {
                     const int64_t r = ep.row0 + wm * 128 + mi * 16 + l15;
                     float m = 0.f;
+                    if constexpr (EPI == MOE_EPI_SWIGLU_Q8_SAVE) {
+                        // G and U as bf16, regrouped like the bf16 store
+                        // epilogue: one 16-byte store each per lane and row
+                        uint32_t gx[2], gy[2], ux[2], uy[2];
+#pragma unroll
+                        for (int ni = 0; ni < 2; ++ni) {
+                            const v4f gv = acc[mi][ni], uv = acc[mi][ni + 2];
+                            gx[ni] = pack_bf16x2(gv.x, gv.y);
+                            gy[ni] = pack_bf16x2(gv.z, gv.w);
+                            ux[ni] = pack_bf16x2(uv.x, uv.y);
+                            uy[ni] = pack_bf16x2(uv.z, uv.w);
+                        }
+                        swap32(gx[0], gx[1]);
+                        swap32(gy[0], gy[1]);
+                        swap32(ux[0], ux[1]);
+                        swap32(uy[0], uy[1]);
+                        swap16(gx[0], gx[1]);
+                        swap16(gy[0], gy[1]);
+                        swap16(ux[0], ux[1]);
+                        swap16(uy[0], uy[1]);
+                        if (r < ep.real_end) {
+                            const int hc = hcol0 + wn * 32 + 8 * lg;
+                            *reinterpret_cast<u32x4*>(out2 + r * N + hc) = u32x4{gx[0], gy[0], gx[1], gy[1]};
+                            *reinterpret_cast<u32x4*>(out2 + r * N + f + hc) = u32x4{ux[0], uy[0], ux[1], uy[1]};
+                        }
+                    }
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni) {
                         const v4f gv = acc[mi][ni], uv = acc[mi][ni + 2];
-                        if constexpr (EPI == MOE_EPI_SWIGLU_Q8_SAVE) {
-                            if (r < ep.real_end) {
-                                const int hc = hcol0 + wn * 32 + ni * 16 + 4 * lg;
-                                *reinterpret_cast<v2u*>(out2 + r * N + hc) =
-                                    v2u{pack_bf16x2(gv.x, gv.y), pack_bf16x2(gv.z, gv.w)};
-                                *reinterpret_cast<v2u*>(out2 + r * N + f + hc) =
-                                    v2u{pack_bf16x2(uv.x, uv.y), pack_bf16x2(uv.z, uv.w)};
-                            }
-                        }
                         v4f h;
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
@@ -1174,17 +1191,21 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 for (int mi = 0; mi < MI; ++mi) {
                     const int rt = wm * 128 + mi * 16 + l15;
                     const int64_t r = ep.row0 + rt;
-                    if (r >= ep.real_end) continue;
                     const float am = fmaxf(fmaxf(rowmax[0][rt], rowmax[1][rt]), fmaxf(rowmax[2][rt], rowmax[3][rt]));
                     const TileScale ts = tile_scale_t<P2>(am);
-                    if (lg == 0 && wn == 0) g.out_s[(int64_t)ep.nt * g.row_cap + r] = ts.s;
+                    // the 4-code groups regrouped like the bf16 epilogue's
+                    // column pairs: 8 consecutive codes per lane, one store
+                    uint32_t z[2];
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni) {
-                        const int hc = hcol0 + wn * 32 + ni * 16 + 4 * lg;
                         const v4f hv = acc[mi][ni + 2];
-                        *reinterpret_cast<uint32_t*>(out + r * f + hc) =
-                            cvt_e4m3x4(hv.x * ts.inv, hv.y * ts.inv, hv.z * ts.inv, hv.w * ts.inv);
+                        z[ni] = cvt_e4m3x4(hv.x * ts.inv, hv.y * ts.inv, hv.z * ts.inv, hv.w * ts.inv);
                     }
+                    swap32(z[0], z[1]);
+                    swap16(z[0], z[1]);
+                    if (r >= ep.real_end) continue;
+                    if (lg == 0 && wn == 0) g.out_s[(int64_t)ep.nt * g.row_cap + r] = ts.s;
+                    *reinterpret_cast<v2u*>(out + r * f + hcol0 + wn * 32 + 8 * lg) = v2u{z[0], z[1]};
                 }
             }
         }
