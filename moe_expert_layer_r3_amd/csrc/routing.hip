@@ -87,10 +87,22 @@ __global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ l
     const bool live = row < T;
     const float* src = logits + (live ? row : 0) * E;
     float v[VPL];
+    if (VPL % 4 == 0 && E % 4 == 0 && lane * VPL + VPL <= E) {
+        // the lane's whole run is in the row and 16-byte aligned
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int e = lane * VPL + i;
-        v[i] = e < E ? src[e] : -INFINITY;
+        for (int c = 0; c < VPL / 4; ++c) {
+            const float4 q = reinterpret_cast<const float4*>(src + lane * VPL)[c];
+            v[4 * c] = q.x;
+            v[4 * c + 1] = q.y;
+            v[4 * c + 2] = q.z;
+            v[4 * c + 3] = q.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int e = lane * VPL + i;
+            v[i] = e < E ? src[e] : -INFINITY;
+        }
     }
     uint32_t taken = 0;
     float my_val = 0.f;
