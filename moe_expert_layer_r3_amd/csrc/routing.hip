@@ -197,23 +197,36 @@ __global__ __launch_bounds__(256) void replay_kernel(const int32_t* __restrict__
     if (flags && status) atomicOr(status, flags);
 }
 
-// d_logits row per block: zero the row, then add the k slot contributions in
-// slot order (a repeated id sums its slots).
+// One wave per token row of d_logits: the token's k slots are uniform loads,
+// each slot's contribution w_j (g_j - <w, g>) is formed once, and every lane
+// writes its elements of the row (64 consecutive floats per store), each the
+// sum of the contributions whose slot holds that id, in slot order (a
+// repeated id sums its slots).
 __global__ __launch_bounds__(256) void gate_backward_kernel(const float* __restrict__ d_gate,
                                                             const float* __restrict__ w,
-                                                            const int32_t* __restrict__ ids, int k, int E,
-                                                            float* __restrict__ d_logits) {
-    const int64_t t = blockIdx.x;
+                                                            const int32_t* __restrict__ ids, int64_t T,
+                                                            int k, int E, float* __restrict__ d_logits) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j)
+        if (j < k) dot += w[t * k + j] * d_gate[t * k + j];
+    int id[MAXK];
+    float c[MAXK];
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j) {
+        id[j] = j < k ? ids[t * k + j] : -1;
+        c[j] = j < k ? w[t * k + j] * (d_gate[t * k + j] - dot) : 0.f;
+    }
     float* out = d_logits + t * E;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = 0.f;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float dot = 0.f;
-        for (int j = 0; j < k; ++j) dot += w[t * k + j] * d_gate[t * k + j];
-        for (int j = 0; j < k; ++j) {
-            int e = ids[t * k + j];
-            if (e >= 0 && e < E) out[e] += w[t * k + j] * (d_gate[t * k + j] - dot);
-        }
+    for (int e = lane; e < E; e += 64) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < MAXK; ++j)
+            if (id[j] == e) acc += c[j];
+        out[e] = acc;
     }
 }
 
@@ -312,7 +325,7 @@ extern "C" int moe_gate_backward(const float* d_gate, const float* w, const int3
                 "gate_backward: bad T/k/E");
     if (T == 0) return MOE_OK;
     MOE_REQUIRE(d_gate && w && ids && d_logits, MOE_ERR_NULL, "gate_backward: NULL argument");
-    gate_backward_kernel<<<dim3((unsigned)T), dim3(256), 0, stream>>>(d_gate, w, ids, k, E, d_logits);
+    gate_backward_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream>>>(d_gate, w, ids, T, k, E, d_logits);
     MOE_LAUNCH_CHECK("gate_backward_kernel");
     return MOE_OK;
 }
