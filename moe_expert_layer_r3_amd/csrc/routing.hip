@@ -312,7 +312,8 @@ extern "C" int moe_replay_load(const int32_t* rec, int32_t n_layers, int32_t k, 
     if (T == 0) return MOE_OK;
     MOE_REQUIRE(rec && logits && ids && w, MOE_ERR_NULL, "replay_load: NULL rec/logits/ids/w");
     const int64_t S = seq_len;
-    dim3 block(256), grid((unsigned)((T + 255) / 256));
+    // one wave per block: a 16384-token chunk spreads over 256 CUs, not 64
+    dim3 block(64), grid((unsigned)((T + 63) / 64));
     replay_kernel<<<grid, block, 0, stream>>>(rec + (int64_t)layer * k * S, k, S, s0, T, logits, E, ids, w,
                                               dev_status);
     MOE_LAUNCH_CHECK("replay_kernel");
