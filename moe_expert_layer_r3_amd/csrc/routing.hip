@@ -10,10 +10,32 @@ namespace moe {
 
 constexpr int MAXK = 16;
 
+// Selection key of (logit x, expert e): one 64-bit integer whose order is the
+// routing order (value descending, then id ascending), so a pick is a plain
+// unsigned max and every key of a row is distinct.
+//   high word: the float's bits mapped monotonically to unsigned (negative
+//              values bit-inverted, positive ones with the sign bit set); x is
+//              canonicalised by adding +0 first, so -0 and +0 share a key and
+//              fall back to the id order, as IEEE comparison has them equal;
+//              NaN takes 1, below every number (NaN sorts last)
+//   low word : ~e, larger for the lower id
+// Key 0 means "no candidate" (a lane slot past E).  Because the picks come out
+// in strictly descending key order, the values still available in a round are
+// exactly those below the previous pick: no per-value taken flags.
+__device__ __forceinline__ uint64_t route_key(float x, int e) {
+    const uint32_t u = __float_as_uint(x + 0.0f);
+    uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    if (x != x) hi = 1u;
+    return ((uint64_t)hi << 32) | (uint32_t)~e;
+}
+__device__ __forceinline__ float route_key_value(uint64_t key) {
+    const uint32_t hi = (uint32_t)(key >> 32);
+    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+}
+__device__ __forceinline__ int route_key_id(uint64_t key) { return (int)~(uint32_t)key; }
+
 // One wavefront per token row.  Lane l holds logits l, l+64, ... (VPL values);
-// k rounds of a wave-wide arg-max under the key (value desc, id asc) pick the
-// slots in order.  IEEE comparison makes -0 and +0 equal, so they fall back to
-// the id order.
+// k rounds of a wave-wide arg-max over route_key pick the slots in order.
 template <int VPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                    int k, int32_t* __restrict__ ids, float* __restrict__ w,
@@ -22,45 +44,27 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (row >= T) return;
     const float* src = logits + row * E;
-    float v[VPL];
+    uint64_t key[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        int e = lane + 64 * i;
-        v[i] = e < E ? src[e] : -INFINITY;
+        const int e = lane + 64 * i;
+        key[i] = e < E ? route_key(src[e], e) : 0ull;
     }
-    uint32_t taken = 0;
-    float my_val = 0.f;
-    int my_id = 0;
+    uint64_t thr = ~0ull, mine = 0ull;
     for (int s = 0; s < k; ++s) {
-        // lane-local best among untaken values; ids grow with i, so '>' keeps the lower id
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
+        uint64_t b = 0ull;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            int e = lane + 64 * i;
-            bool ok = e < E && !((taken >> i) & 1u);
-            if (ok && (bi == 0x7FFFFFFF || v[i] > bv)) {
-                bv = v[i];
-                bi = e;
-            }
-        }
+        for (int i = 0; i < VPL; ++i) b = (key[i] < thr && key[i] > b) ? key[i] : b;
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) {
-            float ov = __shfl_xor(bv, m);
-            int oi = __shfl_xor(bi, m);
-            bool take = (oi != 0x7FFFFFFF) &&
-                        (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
-            if (take) {
-                bv = ov;
-                bi = oi;
-            }
+            const uint64_t o = __shfl_xor(b, m);
+            b = o > b ? o : b;
         }
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        if (lane == s) {
-            my_val = bv;
-            my_id = bi;
-        }
+        thr = b;
+        if (lane == s) mine = b;
     }
+    const float my_val = route_key_value(mine);
+    const int my_id = route_key_id(mine);
     // softmax over the selection; slot 0 holds the max
     float m = __shfl(my_val, 0);
     float ex = lane < k ? expf(my_val - m) : 0.f;
@@ -75,8 +79,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 
 // Sixteen lanes per token row, for E <= 16 * VPL <= 256: lane l of a group
 // holds logits VPL*l .. VPL*l + VPL - 1 (a contiguous run), and k rounds of a
-// 16-lane arg-max under the same key (value desc, id asc) pick the slots in
-// order; a round is VPL local compares and four shuffles instead of six.
+// 16-lane arg-max over route_key pick the slots in order; a round is VPL local
+// compares and four shuffles instead of six.
 template <int VPL>
 __global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                      int k, int32_t* __restrict__ ids, float* __restrict__ w,
@@ -104,38 +108,27 @@ __global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ l
             v[i] = e < E ? src[e] : -INFINITY;
         }
     }
-    uint32_t taken = 0;
-    float my_val = 0.f;
-    int my_id = 0;
-    for (int s = 0; s < k; ++s) {
-        // lane-local best among untaken values; ids grow with i, so '>' keeps the lower id
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
+    uint64_t key[VPL];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int e = lane * VPL + i;
-            const bool ok = e < E && !((taken >> i) & 1u);
-            if (ok && (bi == 0x7FFFFFFF || v[i] > bv)) {
-                bv = v[i];
-                bi = e;
-            }
-        }
+    for (int i = 0; i < VPL; ++i) {
+        const int e = lane * VPL + i;
+        key[i] = e < E ? route_key(v[i], e) : 0ull;
+    }
+    uint64_t thr = ~0ull, mine = 0ull;
+    for (int s = 0; s < k; ++s) {
+        uint64_t b = 0ull;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) b = (key[i] < thr && key[i] > b) ? key[i] : b;
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, 16);
-            const int oi = __shfl_xor(bi, m, 16);
-            const bool take = (oi != 0x7FFFFFFF) && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
-            if (take) {
-                bv = ov;
-                bi = oi;
-            }
+            const uint64_t o = __shfl_xor(b, m, 16);
+            b = o > b ? o : b;
         }
-        if (bi / VPL == lane) taken |= 1u << (bi % VPL);
-        if (lane == s) {
-            my_val = bv;
-            my_id = bi;
-        }
+        thr = b;
+        if (lane == s) mine = b;
     }
+    const float my_val = route_key_value(mine);
+    const int my_id = route_key_id(mine);
     // softmax over the selection; slot 0 holds the max
     const float m = __shfl(my_val, 0, 16);
     const float ex = lane < k ? expf(my_val - m) : 0.f;

@@ -88,10 +88,22 @@ def test_quant_128x128_and_transpose():
 # ------------------------------------------------------------------ routing
 
 @pytest.mark.parametrize("T,E,k,mode", [(1000, 256, 8, "normal"), (333, 200, 16, "normal"), (65, 8, 2, "normal"),
-                                        (7, 1, 1, "normal"), (257, 64, 6, "ties"), (40, 130, 5, "zeros")])
+                                        (7, 1, 1, "normal"), (257, 64, 6, "ties"), (40, 130, 5, "zeros"),
+                                        (300, 64, 6, "special"), (200, 256, 8, "special"),
+                                        (50, 300, 5, "special"), (64, 1000, 16, "normal")])
 def test_topk(T, E, k, mode):
     rng = np.random.default_rng(T * 7 + E)
-    if mode == "ties":
+    if mode == "special":
+        # NaN sorts after every number, -inf after every finite value, -0 ties +0
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        u = rng.random((T, E))
+        lg[u < 0.3] = np.nan
+        lg[(u >= 0.3) & (u < 0.4)] = -np.inf
+        lg[(u >= 0.4) & (u < 0.5)] = np.float32(-0.0)
+        lg[(u >= 0.5) & (u < 0.6)] = np.float32(0.0)
+        lg[: T // 4, : E - 3] = np.nan             # rows where NaN or -inf reach the selection
+        lg[T // 4: T // 2, 4:] = -np.inf
+    elif mode == "ties":
         lg = rng.integers(0, 3, (T, E)).astype(np.float32)
     elif mode == "zeros":
         lg = np.where(rng.random((T, E)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
@@ -102,7 +114,10 @@ def test_topk(T, E, k, mode):
     ids, w = ops.route_topk(gpu(lg), k)
     rids, rw = OR.topk(lg, k)
     assert np.array_equal(npi(ids), rids)
-    assert np.max(np.abs(np64(w) - rw)) <= 1e-6
+    gw = np64(w)
+    assert np.array_equal(np.isnan(gw), np.isnan(rw))
+    ok = ~np.isnan(rw)
+    assert np.max(np.abs(gw[ok] - rw[ok]), initial=0.0) <= 1e-6
 
 
 def test_capture_replay_roundtrip():

@@ -35,6 +35,23 @@ def test_topk_ties_and_signed_zero():
     assert np.all(w == np.float32(1.0 / 3.0))
 
 
+def test_topk_nan_and_infinities():
+    # NaN after every number, NaNs by id; -inf after every finite value; a NaN
+    # in the selection makes the token's gates NaN, -inf gets gate 0
+    nan, inf = np.nan, np.inf
+    lg = np.array([[nan, 1.0, -inf, nan, -2.0, 0.5],
+                   [-inf, -inf, 3.0, nan, -inf, -1.0]], dtype=np.float32)
+    ids, w = R.topk(lg, 5)
+    assert list(ids[0]) == [1, 5, 4, 2, 0]
+    assert list(ids[1]) == [2, 5, 0, 1, 4]
+    assert np.all(np.isnan(w[0]))
+    # gates are fp32-valued: within one fp32 rounding of the exact value
+    assert abs(w[1, 0] - 1.0 / (1.0 + np.exp(-4.0))) < 6e-8 and np.all(w[1, 2:] == 0.0)
+    with np.errstate(invalid="ignore"):
+        ids, w = R.topk(lg, 6)
+    assert list(ids[0]) == [1, 5, 4, 2, 0, 3]
+
+
 def test_topk_invariants():
     rng = np.random.default_rng(2)
     lg = rng.standard_normal((200, 64)).astype(np.float32)
