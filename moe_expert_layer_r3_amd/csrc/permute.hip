@@ -192,6 +192,7 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
 // passes of 256 lanes x 8 columns) before any store.
 constexpr int GQ_THREADS = 256;
 constexpr int GQ_LOADS = 4;
+constexpr int GQ_SPEC = 2;   // loads issued before the slots are known
 
 template <bool P2>
 __global__ __launch_bounds__(GQ_THREADS) void gather_quant_kernel(const uint16_t* __restrict__ x, int64_t T,
@@ -202,12 +203,13 @@ __global__ __launch_bounds__(GQ_THREADS) void gather_quant_kernel(const uint16_t
                                                                   float* __restrict__ xq_s, int64_t row_cap) {
     const int64_t t = blockIdx.x;
     const uint16_t* xr = x + t * d;
-    // the row's first pass is loaded together with the routing slots instead
-    // of after them: one memory latency per token instead of two (a token
-    // without local slots reads its row for nothing)
+    // the first GQ_SPEC loads of the row are issued together with the routing
+    // slots instead of after them (a token with local slots waits one memory
+    // latency, not two); the rest of the first pass follows once the slots
+    // show the token has a local row, so a token without one reads only those
     uint4 raw[GQ_LOADS];
 #pragma unroll
-    for (int i = 0; i < GQ_LOADS; ++i) {
+    for (int i = 0; i < GQ_SPEC; ++i) {
         const int col = (i * GQ_THREADS + threadIdx.x) * 8;
         if (col < d) raw[i] = *reinterpret_cast<const uint4*>(xr + col);
     }
@@ -219,6 +221,11 @@ __global__ __launch_bounds__(GQ_THREADS) void gather_quant_kernel(const uint16_t
         any |= r[j] >= 0;
     }
     if (!any) return;
+#pragma unroll
+    for (int i = GQ_SPEC; i < GQ_LOADS; ++i) {
+        const int col = (i * GQ_THREADS + threadIdx.x) * 8;
+        if (col < d) raw[i] = *reinterpret_cast<const uint4*>(xr + col);
+    }
     const int sub = threadIdx.x & 15;
     for (int c0 = 0; c0 < d; c0 += GQ_LOADS * GQ_THREADS * 8) {
         if (c0 > 0) {
