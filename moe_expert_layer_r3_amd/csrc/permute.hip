@@ -142,9 +142,10 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
         uint64_t active = __ballot(le >= 0);
         while (active) {
             int leader = __ffsll((unsigned long long)active) - 1;
-            int e = __shfl(le, leader);
+            int e = __builtin_amdgcn_readlane(le, leader);  // leader is wave-uniform: no LDS trip
             uint64_t m = __ballot(le == e) & active;
-            if (lane == leader) run[wave][e] += __popcll(m);
+            // LDS add with no return value: the loop never waits on LDS
+            if (lane == leader) atomicAdd(&run[wave][e], (int)__popcll(m));
             active &= ~m;
         }
     }
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
         uint64_t active = __ballot(le >= 0);
         while (active) {
             int leader = __ffsll((unsigned long long)active) - 1;
-            int e = __shfl(le, leader);
+            int e = __builtin_amdgcn_readlane(le, leader);  // leader is wave-uniform: no LDS trip
             uint64_t m = __ballot(le == e) & active;
             int before = run[wave][e];
             if (le == e) row = base[e] + before + __popcll(m & lt_mask);
