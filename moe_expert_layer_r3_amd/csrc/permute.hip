@@ -68,7 +68,7 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
                 if (lane >= o) x += y;
             }
             if (c < nchunk) chunk_counts[(int64_t)c * L + e] = carry + x - v;
-            carry += __shfl(x, 63);
+            carry += __builtin_amdgcn_readlane(x, 63);
         }
         if (lane == 0) tot[e] = carry;
     }

@@ -66,10 +66,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     const float my_val = route_key_value(mine);
     const int my_id = route_key_id(mine);
     // softmax over the selection; slot 0 holds the max
-    float m = __shfl(my_val, 0);
+    float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
     float ex = lane < k ? expf(my_val - m) : 0.f;
     float sum = 0.f;
-    for (int j = 0; j < k; ++j) sum += __shfl(ex, j);  // ascending slot order
+    for (int j = 0; j < k; ++j)  // ascending slot order; j is uniform: a register read, no LDS trip
+        sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
     if (lane < k) {
         ids[row * k + lane] = my_id;
         w[row * k + lane] = ex / sum;
@@ -133,7 +134,12 @@ __global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ l
     const float m = __shfl(my_val, 0, 16);
     const float ex = lane < k ? expf(my_val - m) : 0.f;
     float sum = 0.f;
-    for (int j = 0; j < k; ++j) sum += __shfl(ex, j, 16);  // ascending slot order
+    // ascending slot order; all shuffles issued before the first add
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j) {
+        const float o = __shfl(ex, j, 16);
+        if (j < k) sum += o;
+    }
     if (live && lane < k) {
         ids[row * k + lane] = my_id;
         w[row * k + lane] = ex / sum;
