@@ -34,6 +34,15 @@ __device__ __forceinline__ float route_key_value(uint64_t key) {
 }
 __device__ __forceinline__ int route_key_id(uint64_t key) { return (int)~(uint32_t)key; }
 
+// A key moved across the 16-lane row by a DPP pattern (no LDS trip).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_key(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
 // One wavefront per token row.  Lane l holds logits l, l+64, ... (VPL values);
 // k rounds of a wave-wide arg-max over route_key pick the slots in order.
 template <int VPL>
@@ -120,11 +129,12 @@ __global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ l
         uint64_t b = 0ull;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) b = (key[i] < thr && key[i] > b) ? key[i] : b;
-#pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) {
-            const uint64_t o = __shfl_xor(b, m, 16);
-            b = o > b ? o : b;
-        }
+        // max over the 16-lane group: swap neighbours, swap pairs (each lane
+        // then holds its quad's max), mirror within 8 lanes, mirror within 16
+        b = umax64(b, dpp_key<0xB1>(b));
+        b = umax64(b, dpp_key<0x4E>(b));
+        b = umax64(b, dpp_key<0x141>(b));
+        b = umax64(b, dpp_key<0x140>(b));
         thr = b;
         if (lane == s) mine = b;
     }
