@@ -12,6 +12,14 @@ from . import ops
 from .ops import _call, _p, _stream
 
 
+def _check(t, shape, dtype, name):
+    """Caller tensors must match the plan's sizes: the kernels index them by the
+    plan's T, d, E, and a smaller tensor would be read past its end."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
 def weight_buffers(L, d, f, device="cuda", transpose=False):
     """Preallocated FP8 weight codes and scales for quantize_weights(out=...)."""
     u8, f32 = torch.uint8, torch.float32
@@ -32,6 +40,9 @@ def quantize_weights(W13, W2, transpose=False, out=None, pow2=False, mxfp4=False
     E8M0 codes (both K-block-major), and alike for W2.
     ``out`` (from weight_buffers) receives the result without allocating."""
     L, f2, d = W13.shape
+    # the output buffers are sized from W13: W2 must be its [L, d, f] partner
+    _check(W13, (L, f2, d), torch.bfloat16, "W13")
+    _check(W2, (L, d, f2 // 2), torch.bfloat16, "W2")
     if mxfp4:
         e = lambda shape: torch.empty(shape, dtype=torch.uint8, device=W13.device)
         f = f2 // 2
@@ -93,14 +104,22 @@ class ForwardPlan:
 
     # each stage is one C-ABI call on the current stream
     def route(self, logits):
+        _check(logits, (self.T, self.E), torch.float32, "logits")
         _call("moe_route_topk", _p(logits), self.T, self.E, self.k, _p(self.ids), _p(self.w), _stream())
 
     def replay(self, rec, layer, s0, logits):
         NL, k, S = rec.shape
+        # ids and w hold (T, self.k): a record of another top_k would be
+        # written past their end on the device
+        if k != self.k:
+            raise ValueError(f"record top_k {k} differs from the plan's k {self.k}")
+        _check(rec, (NL, self.k, S), torch.int32, "record")
+        _check(logits, (self.T, self.E), torch.float32, "logits")
         _call("moe_replay_load", _p(rec), NL, k, S, layer, s0, self.T, _p(logits), self.E, _p(self.ids),
               _p(self.w), _p(self.status), _stream())
 
     def permute(self, x):
+        _check(x, (self.T, self.d), torch.bfloat16, "x")
         _call("moe_permute", _p(self.ids), self.T, self.k, self.e0, self.L, self.rcap, _p(self.counts),
               _p(self.offsets), _p(self.row_pair), _p(self.pair_row), _p(x), self.d, None, _p(self.xq),
               _p(self.xq_s), self.sflag, _p(self.ws), self.ws.numel(), _p(self.status), _stream())
@@ -200,10 +219,12 @@ class TrainPlan(ForwardPlan):
         self.d_logits = torch.empty((T, E), dtype=f32, device=dv)
 
     def combine_bwd(self, dy):
+        _check(dy, (self.T, self.d), torch.bfloat16, "dy")
         _call("moe_combine_backward", _p(dy), _p(self.Y), _p(self.pair_row), _p(self.w), self.T, self.k, self.d,
               self.rcap, _p(self.dyq), _p(self.dyq_s), _p(self.d_gate), self.sflag, _stream())
 
     def dy_quant_t(self, dy):
+        _check(dy, (self.T, self.d), torch.bfloat16, "dy")
         _call("moe_quant_fp8_rows_t", _p(dy), _p(self.w), _p(self.row_pair), _p(self.offsets), self.L, self.rcap,
               self.k, self.d, _p(self.dyqT), _p(self.dyqT_s), self.sflag, _stream())
 
@@ -229,6 +250,7 @@ class TrainPlan(ForwardPlan):
               _p(self.dx), _stream())
 
     def x_quant_t(self, x):
+        _check(x, (self.T, self.d), torch.bfloat16, "x")
         _call("moe_quant_fp8_rows_t", _p(x), None, _p(self.row_pair), _p(self.offsets), self.L, self.rcap,
               self.k, self.d, _p(self.xqT), _p(self.xqT_s), self.sflag, _stream())
 

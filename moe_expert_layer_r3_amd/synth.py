@@ -70,12 +70,13 @@ def rng(cfg, tid, *sub):
     return np.random.default_rng([0, cfg, tid, *sub])
 
 
-def _normal_bf16_rows(cfg, tid, sub, rows, cols, std, out):
-    """Fill torch bf16 ``out`` [rows, cols] from per-ROW_BLOCK streams."""
+def _normal_bf16_rows(cfg, tid, sub, rows, cols, std, out, b0=0):
+    """Fill torch bf16 ``out`` [rows, cols] from per-ROW_BLOCK streams (row
+    block b of ``out`` from stream b0 + b)."""
     def blk(b):
         r0 = b * ROW_BLOCK
         r1 = min(rows, r0 + ROW_BLOCK)
-        z = rng(cfg, tid, *sub, b).standard_normal((r1 - r0, cols), dtype=np.float32)
+        z = rng(cfg, tid, *sub, b0 + b).standard_normal((ROW_BLOCK, cols), dtype=np.float32)[:r1 - r0]
         if std != 1.0:
             z *= np.float32(std)
         out[r0:r1] = torch.from_numpy(z).to(torch.bfloat16)
@@ -117,10 +118,13 @@ def x(w: Workload, layer=0, t0=0, T=None):
     return out
 
 
-def dy(w: Workload):
-    """bf16 torch tensor [T, d] upstream gradient."""
-    out = torch.empty((w.T, w.d), dtype=torch.bfloat16)
-    return _normal_bf16_rows(w.cfg, TID_DY, (), w.T, w.d, 1.0, out)
+def dy(w: Workload, t0=0, T=None):
+    """bf16 torch tensor [T, d] upstream gradient of tokens t0 .. t0+T-1; t0 must
+    be a multiple of 1024."""
+    T = w.T if T is None else T
+    assert t0 % ROW_BLOCK == 0
+    out = torch.empty((T, w.d), dtype=torch.bfloat16)
+    return _normal_bf16_rows(w.cfg, TID_DY, (), T, w.d, 1.0, out, b0=t0 // ROW_BLOCK)
 
 
 def expert_weights(w: Workload, which, e, layer=0):

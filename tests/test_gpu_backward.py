@@ -19,6 +19,7 @@ from oracle.numerics import bf16 as obf16, f32 as of32
 from moe_expert_layer_r3_amd import layer as ML
 from moe_expert_layer_r3_amd import ops, synth
 from gpu_util import DEV, bf16_tensor, gpu, ids_for_counts, np64, npi, rel_fro, say
+import layer_checks as LC
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -455,9 +456,214 @@ def test_layer_train_full_size_sampled(pow2):
     c, o, rp, pr = OD.permute_index(ids, wl.e0, wl.L)
     assert np.array_equal(npi(plan.counts), c) and np.array_equal(npi(plan.offsets), o)
     assert np.array_equal(npi(plan.pair_row), pr)
-    say("train: indices bit-exact; checking sampled stages")
-    del W13, W2
+    say("train: indices bit-exact; forward stages (GEMM1 saving G/U, GEMM2, combine) on sampled rows")
+    h32 = LC.gemm1_h32(plan.xq, plan.xq_s, wts["w13q"], wts["w13s"], plan.counts, plan.offsets, pow2=pow2)
+    LC.check_layer_forward(wl, x, W13, W2, plan, h32, (0, 13, 31), wts=wts, pow2=pow2, save_gu=True, n_rows=16,
+                           tok_stride=131, tag="train")
+    del h32, W13, W2
+    say("train: backward stages on sampled rows")
     _check_stages(plan, wts, x.to(DEV), dy.to(DEV), wl,
                   rows_of=lambda seg: seg[:: max(1, len(seg) // 16)], experts=(0, 13, 31),
                   feat_of=lambda m: np.arange(0, m, m // 32), pow2=pow2)
     say("train sampled parity ok")
+
+
+# ------------------------------------------------------------------ determinism
+
+def _plan_tensors(plan):
+    """Every device buffer a training step writes (the status word and the
+    permute workspace aside)."""
+    out = {n: t for n, t in vars(plan).items() if isinstance(t, torch.Tensor) and n not in ("status", "ws")}
+    out.update({f"sb.{n}": t for n, t in plan.sb.items()})
+    return out
+
+
+def _poison(tensors):
+    for t in tensors.values():
+        if t.dtype.is_floating_point:
+            t.fill_(-7.0e30)
+        elif t.dtype == torch.uint8:
+            t.fill_(0xA5)
+        else:
+            t.fill_(-123456789)
+
+
+def test_train_step_run_twice_bitwise():
+    """The full training step (T=16384, d=7168, f=2048, 32 of 256 experts,
+    top-8) twice on the same inputs, every buffer overwritten with the same
+    poison before each run: every output, intermediate and index buffer is
+    bitwise equal (the path has no order-dependent atomics), so no element is
+    left unwritten in one run and written in the other."""
+    wl = synth.WORKLOADS["train"]
+    say("run twice: inputs")
+    x = synth.x(wl).to(DEV)
+    lg = gpu(synth.logits(wl))
+    dy = synth.dy(wl).to(DEV)
+    wts = ML.quantize_weights(synth.weights(wl, "w13").to(DEV), synth.weights(wl, "w2").to(DEV), transpose=True)
+    plan = ML.TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, e0=wl.e0, device=DEV)
+    bufs = _plan_tensors(plan)
+    runs = []
+    for i in range(2):
+        _poison(bufs)
+        plan.status.zero_()
+        plan.forward(x, lg, wts)
+        plan.backward(x, dy, wts)
+        torch.cuda.synchronize()
+        say(f"run twice: run {i} done")
+        runs.append({n: t.clone() for n, t in bufs.items()} if i == 0 else bufs)
+    assert int(plan.status.item()) == 0
+    differ = [n for n in bufs if not torch.equal(runs[0][n], runs[1][n])]
+    assert not differ, f"buffers differ between two runs: {differ}"
+
+
+# ------------------------------------------------------------------ end to end against the oracle's own chain
+
+_E4M3_GRID = None
+
+
+def _grid_index(codes):
+    """Position of each e4m3 code's value in the sorted grid of finite e4m3
+    values (both zeros share one position)."""
+    global _E4M3_GRID
+    from oracle.numerics import e4m3_decode
+    if _E4M3_GRID is None:
+        allv = e4m3_decode(np.arange(256, dtype=np.uint8))
+        _E4M3_GRID = np.unique(allv[np.isfinite(allv)])
+    return np.searchsorted(_E4M3_GRID, e4m3_decode(codes))
+
+
+def _flips(name, q_gpu, s_gpu, q_ref, s_ref, v_gpu, v_ref, tile_axis, exempt=None):
+    """Compare two FP8 quantisations of nearly equal values (the GPU chain's
+    fp32 values and the oracle chain's): codes and scales, tiles of 128 along
+    tile_axis.  Every differing code of a tile whose scale agrees must be the
+    e4m3 neighbour of the other (one rounding decision on the other side of a
+    midpoint), and the two underlying values must differ by no more than 1e-4
+    of the tile's largest magnitude: the flips come from the fp32-vs-fp64
+    values, not from the quantiser.  ``exempt`` marks elements computed from a
+    bf16 value that itself rounded one bf16 step apart in the two chains (the
+    saved G and U): they are only counted.  Returns
+    (differing codes, codes, tiles whose scale differs)."""
+    q_gpu, q_ref = np.asarray(q_gpu), np.asarray(q_ref)
+    v_gpu, v_ref = np.asarray(v_gpu, np.float64), np.asarray(v_ref, np.float64)
+    s_gpu, s_ref = np.asarray(s_gpu, np.float64), np.asarray(s_ref, np.float64)
+    exempt = np.zeros(np.shape(q_gpu), bool) if exempt is None else np.asarray(exempt)
+    if tile_axis == 0:
+        q_gpu, q_ref, v_gpu, v_ref, s_gpu, s_ref = q_gpu.T, q_ref.T, v_gpu.T, v_ref.T, s_gpu.T, s_ref.T
+        exempt = exempt.T
+    rows, cols = q_gpu.shape
+    amax = np.repeat(np.max(np.abs(v_ref).reshape(rows, cols // 128, 128), axis=2), 128, axis=1)
+    diff = q_gpu != q_ref
+    own = diff & ~exempt
+    nd, nx = int(np.count_nonzero(own)), int(np.count_nonzero(diff & exempt))
+    if nd:
+        step = np.abs(_grid_index(q_gpu[own]) - _grid_index(q_ref[own]))
+        assert np.all(step == 1), f"{name}: a code differs by more than one e4m3 step"
+    close = (np.abs(v_gpu - v_ref) <= 1e-4 * amax) | exempt
+    assert np.all(close), f"{name}: fp32 values differ by more than 1e-4 of their tile max"
+    ns = int(np.count_nonzero(s_gpu != s_ref))
+    say(f"  {name}: {nd} of {diff.size} codes one e4m3 step apart, {nx} more downstream of a saved G/U "
+        f"bf16 flip; {ns} of {s_gpu.size} tile scales differ")
+    return nd, diff.size, ns
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_tiny_train_end_to_end_explained(pow2):
+    """Why the GPU chain differs from the oracle's own FP8 chain end to end
+    (a few 1e-3 on dx and dW13) while every stage meets 2e-3:
+      1. at every FP8 quantisation point, the two chains' fp32 values agree to
+         1e-4 of the tile maximum, and every differing code is one e4m3 step
+         from the oracle's (a rounding decision at a midpoint), counted here;
+      2. the oracle run on the GPU's codes at those points reproduces every GPU
+         output (y, dx, dW2, dW13, d_logits) within 2e-3.
+    So the end-to-end difference is the effect of those few one-step code
+    flips (each moves an element by 1/16 to 1/8 of its value), and the 1e-2
+    end-to-end bound asserted below rests on this, not on the kernels."""
+    wl = synth.WORKLOADS["tiny"]
+    lg = synth.logits(wl)
+    x = synth.x(wl)
+    dy = synth.dy(wl)
+    W13 = synth.weights(wl, "w13")
+    W2 = synth.weights(wl, "w2")
+    say(f"tiny train end to end, pow2={pow2}")
+    plan, wts = _train_gpu(wl, x.to(DEV), gpu(lg), W13.to(DEV), W2.to(DEV), dy.to(DEV), pow2=pow2)
+    ids, w = OR.topk(lg, wl.k)
+    wq = OL.quantize_weights(np64(W13), np64(W2), pow2=pow2)
+    fw = OL.forward(np64(x), ids, w, 0, wl.L, wq, pow2=pow2)
+    bw = OL.backward(fw, np64(dy), ids, w, wl.E, wq, pow2=pow2)
+    n = int(npi(plan.offsets)[-1])
+    rp = npi(plan.row_pair)[:n]
+    real = rp >= 0
+    rr = np.flatnonzero(real)
+    f = wl.f
+    # the GPU's own fp32 values at the fused quantisers
+    h32 = np64(LC.gemm1_h32(plan.xq, plan.xq_s, wts["w13q"], wts["w13s"], plan.counts, plan.offsets, pow2=pow2))
+    ins = ops.swiglu_backward(plan.dH, plan.gu, plan.row_pair, plan.offsets, wl.L, plan.rcap, inspect=True,
+                              pow2=pow2)
+    dgu32, H32 = np64(ins["dgu"])[:n], np64(ins["h"])[:n]
+    dgu32[~real] = 0.0
+    H32[~real] = 0.0
+    # the saved bf16 G, U: a rounding point of its own.  The GPU rounds its own
+    # fp32 accumulators (the STORE_F32 dump of the same GEMM), which agree with
+    # the oracle's fp64 G, U to 1e-4 of the row maximum; a saved value differs
+    # from the oracle's only by the one bf16 step of a midpoint between them.
+    gu32 = np64(ops.grouped_gemm(plan.xq, plan.xq_s, wts["w13q"], wts["w13s"], plan.counts, plan.offsets,
+                                 ops.EPI_STORE_F32, pow2=pow2))[:n]
+    GU_o = np.concatenate([fw["G"], fw["U"]], axis=1)[:n]
+    assert np.array_equal(np64(plan.gu)[rr], obf16(gu32[rr]))
+    rmax = np.max(np.abs(GU_o[rr]), axis=1, keepdims=True)
+    assert np.all(np.abs(gu32[rr] - GU_o[rr]) <= 1e-4 * rmax)
+    gu_ref = obf16(GU_o)
+    gu_flip = (np64(plan.gu)[:n] != gu_ref) & real[:, None]
+    lo, hi = np.minimum(gu32, GU_o)[gu_flip], np.maximum(gu32, GU_o)[gu_flip]
+    mid = (np64(plan.gu)[:n][gu_flip] + gu_ref[gu_flip]) / 2          # the bf16 midpoint between the two
+    assert np.all((lo <= mid) & (mid <= hi))
+    pair_flip = gu_flip[:, :f] | gu_flip[:, f:]
+    say(f"  saved G/U bf16: {int(np.count_nonzero(gu_flip))} of {gu_flip[rr].size} values one bf16 step apart, "
+        "each at a midpoint between the GPU's fp32 value and the oracle's")
+    act = lambda v: OQ.quant_1x128(v, pow2=pow2)
+    act_t = lambda v: OQ.quant_128x1_t(v, real, pow2=pow2)
+    say("1. code flips at each quantisation point (GPU chain vs oracle chain)")
+    # h, 1x128 (forward)
+    hq_o, hs_o = fw["ha"]
+    _flips("h 1x128", npi(plan.hq)[rr], npi(plan.hq_s).T[rr], hq_o[rr], hs_o[rr], h32[rr], fw["h"][rr], 1)
+    # dGU 1x128 and 128x1, H 128x1 (backward)
+    q1, s1 = act(bw["dGU"])
+    ex2 = np.concatenate([pair_flip, pair_flip], axis=1)
+    _flips("dGU 1x128", npi(plan.sb["dgu_q"])[rr], npi(plan.sb["dgu_s"]).T[rr], q1[rr], s1[rr], dgu32[rr],
+           bw["dGU"][rr], 1, exempt=ex2[rr])
+    qt, st = act_t(bw["dGU"])
+    _flips("dGU 128x1", npi(ops.untile_t(plan.sb["dgu_qT"]))[:, :n], npi(plan.sb["dgu_sT"])[:n // 128].T, qt, st,
+           dgu32.T, bw["dGU"].T, 1, exempt=ex2.T)
+    qh, sh = act_t(np.where(real[:, None], bw["Hr"], 0.0))
+    _flips("H 128x1", npi(ops.untile_t(plan.sb["h_qT"]))[:, :n], npi(plan.sb["h_sT"])[:n // 128].T, qh, sh,
+           H32.T, np.where(real[:, None], bw["Hr"], 0.0).T, 1, exempt=pair_flip.T)
+    # reproducible inputs quantise identically
+    assert np.array_equal(npi(plan.xq)[rr], fw["Xa"][0][rr])
+    assert np.array_equal(npi(plan.dyq)[rr], act(bw["dYp"])[0][rr])
+    say("2. the oracle on the GPU's codes reproduces every GPU output within 2e-3")
+    c, o = npi(plan.counts), npi(plan.offsets)
+    pr = npi(plan.pair_row)
+    Y_o = obf16(OG.grouped_forward(npi(plan.hq), npi(plan.hq_s).T, c, o, wq[1][0], wq[1][1]))
+    y_o = OD.combine(Y_o, pr, w)
+    dX_o = obf16(OG.grouped_dgrad(npi(plan.sb["dgu_q"]), npi(plan.sb["dgu_s"]).T, c, o, wq[0][0], wq[0][1]))
+    dx_o = OD.combine(dX_o, pr, None)
+    gq = lambda qT, sT: (npi(ops.untile_t(qT))[:, :n], npi(sT)[:n // 128].T)
+    dW2_o = obf16(OG.grouped_wgrad(*gq(plan.dyqT, plan.dyqT_s), *gq(plan.sb["h_qT"], plan.sb["h_sT"]), c, o))
+    dW13_o = obf16(OG.grouped_wgrad(*gq(plan.sb["dgu_qT"], plan.sb["dgu_sT"]), *gq(plan.xqT, plan.xqT_s), c, o))
+    Yg = np64(plan.Y)
+    d_gate_o = np.zeros((wl.T, wl.k))
+    loc = pr >= 0
+    d_gate_o[loc] = np.sum(np64(dy)[np.nonzero(loc)[0]] * Yg[pr[loc]], axis=1)
+    dl_o = OR.gate_backward(d_gate_o, w, ids, wl.E)
+    for name, got, ref_codes, ref_own in (("y", plan.y, y_o, fw["y"]), ("dx", plan.dx, dx_o, bw["dx"]),
+                                          ("dW2", plan.dW2, dW2_o, bw["dW2"]),
+                                          ("dW13", plan.dW13, dW13_o, bw["dW13"]),
+                                          ("d_logits", plan.d_logits, dl_o, bw["d_logits"])):
+        g = np64(got)
+        e_codes = rel_fro(g, ref_codes)
+        e_own = rel_fro(g, ref_own)
+        e_between = rel_fro(ref_codes, ref_own)
+        say(f"  {name}: GPU vs oracle on GPU codes {e_codes:.2e}; GPU vs oracle's own chain {e_own:.2e}; "
+            f"oracle on GPU codes vs oracle's own chain {e_between:.2e}")
+        assert e_codes <= TOL, name
+        assert e_own <= 1e-2, name

@@ -17,6 +17,7 @@ from oracle import routing as OR
 from oracle.numerics import bf16 as obf16, e4m3_encode, f32 as of32
 from moe_expert_layer_r3_amd import ops, synth
 from gpu_util import DEV, bf16_tensor, gpu, ids_for_counts, np64, npi, rel_fro, say
+import layer_checks as LC
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -295,14 +296,19 @@ def test_combine():
     rcap = res["row_cap"]
     Y = obf16(rng.standard_normal((rcap, d)))
     say("combine weighted and unweighted")
-    y = ops.combine(bf16_tensor(Y), res["pair_row"], gpu(w.astype(np.float32)))
+    w32 = w.astype(np.float32)
+    y = ops.combine(bf16_tensor(Y), res["pair_row"], gpu(w32))
     pr = npi(res["pair_row"])
     ref = OD.combine(Y, pr, w)
     assert rel_fro(np64(y), ref) <= TOL
     none = np.all(pr < 0, axis=1)
     assert none.any() and np.all(np64(y)[none] == 0)
+    # per element: one bf16 rounding of the fp32 slot-order sum
+    flips = LC.check_combine_elementwise(np64(y), Y, pr, w32.astype(np.float64))
     y1 = ops.combine(bf16_tensor(Y), res["pair_row"], None)
     assert rel_fro(np64(y1), OD.combine(Y, pr, None)) <= TOL
+    flips1 = LC.check_combine_elementwise(np64(y1), Y, pr, None)
+    say(f"combine: {flips} / {flips1} elements one bf16 step from bf16(exact)")
 
 
 # ------------------------------------------------------------------ whole layer
@@ -338,49 +344,9 @@ def test_layer_tiny_forward():
 
 def test_layer_ep8_full_size_sampled():
     """T=8192, d=7168, f=2048, 32 of 256 experts, top-8 -- the full EP=8 share,
-    launched exactly as the benchmark launches it; outputs checked on samples."""
-    wl = synth.WORKLOADS["ep8"]
-    say("ep8: generating inputs")
-    lg = synth.logits(wl)
-    x = synth.x(wl)
-    W13 = synth.weights(wl, "w13")
-    W2 = synth.weights(wl, "w2")
-    say("ep8: GPU forward")
-    out = _layer_forward_gpu(x.to(DEV), gpu(lg), W13.to(DEV), W2.to(DEV), wl.k, wl.e0, wl.L)
-    torch.cuda.synchronize()
-    ids, w = OR.topk(lg, wl.k)
-    assert np.array_equal(npi(out["ids"]), ids)
-    assert np.max(np.abs(np64(out["w"]) - w)) <= 1e-6
-    c, o, rp, pr = OD.permute_index(ids, wl.e0, wl.L)
-    res = out["res"]
-    assert np.array_equal(npi(res["counts"]), c) and np.array_equal(npi(res["offsets"]), o)
-    assert np.array_equal(npi(res["pair_row"]), pr)
-    n = int(o[-1])
-    assert np.array_equal(npi(res["row_pair"])[:n], rp)
-    say("ep8: indices bit-exact; checking weights and sampled GEMM rows")
-    xs_np = np64(x)
-    for e in (0, 17):
-        rq, rs = OQ.quant_128x128(np64(W13[e:e + 1]))
-        assert np.array_equal(npi(out["wq13"][e]), rq[0]) and np.array_equal(npi(out["ws13"][e]).astype(np.float64), rs[0])
-        rq2, rs2 = OQ.quant_128x128(np64(W2[e:e + 1]))
-        assert np.array_equal(npi(out["wq2"][e]), rq2[0])
-        rows = np.arange(o[e], o[e] + c[e])[:: max(1, c[e] // 24)]
-        toks = rp[rows] // wl.k
-        xq, xsc = OQ.quant_1x128(xs_np[toks])
-        assert np.array_equal(npi(res["xq"])[rows], xq)
-        GU = OG.blockscaled_matmul(xq, xsc, rq[0], OG.expand_weight_scales(rs[0]))
-        h = OL.silu(of32(GU[:, :wl.f])) * of32(GU[:, wl.f:])
-        hq_g = npi(out["hq"])[rows]
-        hs_g = npi(out["hs"]).T[rows].astype(np.float64)
-        deq_g = OQ.dequant_1x128(hq_g, hs_g)
-        assert rel_fro(deq_g, h) <= 0.05            # FP8 of h itself: a few percent
-        Yref = obf16(OG.blockscaled_matmul(hq_g, hs_g, rq2[0], OG.expand_weight_scales(rs2[0])))
-        assert rel_fro(np64(out["Y"])[rows], Yref) <= TOL
-    toks = np.arange(0, wl.T, 97)
-    Yg = np64(out["Y"])
-    yref = OD.combine(Yg, pr[toks], w[toks])
-    assert rel_fro(np64(out["y"])[toks], yref) <= TOL
-    say("ep8 sampled parity ok")
+    launched exactly as the benchmark launches it; outputs checked on samples
+    that include every segment's last rows and 128/256-row tile boundaries."""
+    LC.full_size_forward_check(synth.WORKLOADS["ep8"], experts=(0, 17, 31))
 
 
 def test_forward_graph_replay():
@@ -418,36 +384,4 @@ def test_layer_hotspot_full_size_sampled():
     coldest local expert 156): experts of 63 and 2 M-tiles through the same
     launch as the benchmark's hotspot leg; GEMM rows sampled from the hottest,
     a middle and the coldest expert, across the whole segment."""
-    wl = synth.WORKLOADS["hotspot"]
-    say("hotspot: generating inputs")
-    lg = synth.logits(wl)
-    x = synth.x(wl)
-    W13 = synth.weights(wl, "w13")
-    W2 = synth.weights(wl, "w2")
-    say("hotspot: GPU forward")
-    out = _layer_forward_gpu(x.to(DEV), gpu(lg), W13.to(DEV), W2.to(DEV), wl.k, wl.e0, wl.L)
-    torch.cuda.synchronize()
-    ids, w = OR.topk(lg, wl.k)
-    assert np.array_equal(npi(out["ids"]), ids)
-    c, o, rp, pr = OD.permute_index(ids, wl.e0, wl.L)
-    res = out["res"]
-    assert np.array_equal(npi(res["counts"]), c) and np.array_equal(npi(res["offsets"]), o)
-    xs_np = np64(x)
-    for e in (0, int(np.argsort(c)[len(c) // 2]), int(np.argmin(c))):
-        say(f"hotspot: expert {e} ({c[e]} rows)")
-        rq, rs = OQ.quant_128x128(np64(W13[e:e + 1]))
-        rq2, rs2 = OQ.quant_128x128(np64(W2[e:e + 1]))
-        rows = np.arange(o[e], o[e] + c[e])[:: max(1, c[e] // 20)]
-        xq, xsc = OQ.quant_1x128(xs_np[rp[rows] // wl.k])
-        assert np.array_equal(npi(res["xq"])[rows], xq)
-        GU = OG.blockscaled_matmul(xq, xsc, rq[0], OG.expand_weight_scales(rs[0]))
-        h = OL.silu(of32(GU[:, :wl.f])) * of32(GU[:, wl.f:])
-        hq_g = npi(out["hq"])[rows]
-        hs_g = npi(out["hs"]).T[rows].astype(np.float64)
-        assert rel_fro(OQ.dequant_1x128(hq_g, hs_g), h) <= 0.05
-        Yref = obf16(OG.blockscaled_matmul(hq_g, hs_g, rq2[0], OG.expand_weight_scales(rs2[0])))
-        assert rel_fro(np64(out["Y"])[rows], Yref) <= TOL
-    toks = np.arange(0, wl.T, 61)
-    yref = OD.combine(np64(out["Y"]), pr[toks], w[toks])
-    assert rel_fro(np64(out["y"])[toks], yref) <= TOL
-    say("hotspot sampled parity ok")
+    LC.full_size_forward_check(synth.WORKLOADS["hotspot"], experts=None, n_rows=20, tok_stride=61)

@@ -11,7 +11,6 @@ import pytest
 import torch
 
 from oracle import blockfp8 as OQ
-from oracle import dispatch as OD
 from oracle import layer as OL
 from oracle import mxfp4 as MX
 from oracle import routing as OR
@@ -19,6 +18,7 @@ from oracle.numerics import bf16 as obf16, f32 as of32
 from moe_expert_layer_r3_amd import ops, synth
 from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights
 from gpu_util import DEV, bf16_tensor, gpu, ids_for_counts, np64, npi, rel_fro, say
+import layer_checks as LC
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -131,36 +131,7 @@ def test_layer_ep8_full_size_sampled_mxfp4():
     """The EP=8 share (T=8192, d=7168, f=2048, 32 of 256 experts, top-8) with
     MXFP4 weights through ForwardPlan, as the benchmark runs it; sampled rows
     of two experts and of the combine against the oracle."""
-    wl = synth.WORKLOADS["ep8"]
-    say("mxfp4 ep8: GPU forward")
-    lg, x, W13, W2, wts, plan, y = _plan_forward(wl)
-    ids, w = OR.topk(lg, wl.k)
-    assert np.array_equal(npi(plan.ids), ids)
-    c, o, rp, pr = OD.permute_index(ids, wl.e0, wl.L)
-    assert np.array_equal(npi(plan.offsets), o)
-    xs_np = np64(x)
-    say("mxfp4 ep8: checking sampled rows")
-    for e in (0, 17):
-        c13, s13 = MX.quant_mx(np64(W13[e]))
-        assert np.array_equal(MX.unpack(ops.mx_codes_rows(wts["w13q"][e:e + 1])[0]), c13)
-        assert np.array_equal(ops.mx_scales_rows(wts["w13s"][e:e + 1])[0], s13)
-        c2, s2 = MX.quant_mx(np64(W2[e]))
-        assert np.array_equal(MX.unpack(ops.mx_codes_rows(wts["w2q"][e:e + 1])[0]), c2)
-        assert np.array_equal(ops.mx_scales_rows(wts["w2s"][e:e + 1])[0], s2)
-        rows = np.arange(o[e], o[e] + c[e])[:: max(1, c[e] // 24)]
-        xq, xsc = OQ.quant_1x128(xs_np[rp[rows] // wl.k], pow2=True)
-        assert np.array_equal(npi(plan.xq)[rows], xq)
-        GU = MX.matmul(xq, xsc, c13, s13)
-        h = OL.silu(of32(GU[:, :wl.f])) * of32(GU[:, wl.f:])
-        hq_g = npi(plan.hq)[rows]
-        hs_g = npi(plan.hq_s).T[rows].astype(np.float64)
-        assert rel_fro(OQ.dequant_1x128(hq_g, hs_g), h) <= 0.05
-        Yref = obf16(MX.matmul(hq_g, hs_g, c2, s2))
-        assert rel_fro(np64(plan.Y)[rows], Yref) <= TOL
-    toks = np.arange(0, wl.T, 97)
-    yref = OD.combine(np64(plan.Y), pr[toks], w[toks])
-    assert rel_fro(np64(y)[toks], yref) <= TOL
-    say("mxfp4 ep8 sampled parity ok")
+    LC.full_size_forward_check(synth.WORKLOADS["ep8"], experts=(0, 17, 31), mxfp4=True)
 
 
 # ------------------------------------------------------------------ training with MXFP4 weights

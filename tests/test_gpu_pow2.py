@@ -18,6 +18,7 @@ from oracle.numerics import bf16 as obf16, f32 as of32
 from moe_expert_layer_r3_amd import ops, synth
 from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights
 from gpu_util import DEV, bf16_tensor, gpu, ids_for_counts, np64, npi, rel_fro, say
+import layer_checks as LC
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -177,34 +178,4 @@ def test_layer_ep8_full_size_sampled_pow2():
     """The full EP=8 share (T=8192, d=7168, f=2048, 32 of 256 experts, top-8)
     through ForwardPlan with power-of-two scales, as the benchmark runs it;
     sampled rows of two experts and of the combine against the oracle."""
-    wl = synth.WORKLOADS["ep8"]
-    say("pow2 ep8: GPU forward")
-    lg, x, W13, W2, wts, plan, y = _plan_forward(wl, True)
-    ids, w = OR.topk(lg, wl.k)
-    assert np.array_equal(npi(plan.ids), ids)
-    c, o, rp, pr = OD.permute_index(ids, wl.e0, wl.L)
-    assert np.array_equal(npi(plan.offsets), o)
-    xs_np = np64(x)
-    say("pow2 ep8: checking sampled rows")
-    for e in (0, 17):
-        rq, rs = OQ.quant_128x128(np64(W13[e:e + 1]), pow2=True)
-        assert np.array_equal(npi(wts["w13q"][e]), rq[0])
-        assert np.array_equal(npi(wts["w13s"][e]).astype(np.float64), rs[0])
-        rq2, rs2 = OQ.quant_128x128(np64(W2[e:e + 1]), pow2=True)
-        assert np.array_equal(npi(wts["w2q"][e]), rq2[0])
-        rows = np.arange(o[e], o[e] + c[e])[:: max(1, c[e] // 24)]
-        xq, xsc = OQ.quant_1x128(xs_np[rp[rows] // wl.k], pow2=True)
-        assert np.array_equal(npi(plan.xq)[rows], xq)
-        assert np.array_equal(npi(plan.xq_s).T[rows].astype(np.float64), xsc)
-        GU = OG.blockscaled_matmul(xq, xsc, rq[0], OG.expand_weight_scales(rs[0]))
-        h = OL.silu(of32(GU[:, :wl.f])) * of32(GU[:, wl.f:])
-        hq_g = npi(plan.hq)[rows]
-        hs_g = npi(plan.hq_s).T[rows].astype(np.float64)
-        assert np.all(np.frexp(hs_g)[0] == 0.5)
-        assert rel_fro(OQ.dequant_1x128(hq_g, hs_g), h) <= 0.05
-        Yref = obf16(OG.blockscaled_matmul(hq_g, hs_g, rq2[0], OG.expand_weight_scales(rs2[0])))
-        assert rel_fro(np64(plan.Y)[rows], Yref) <= TOL
-    toks = np.arange(0, wl.T, 97)
-    yref = OD.combine(np64(plan.Y), pr[toks], w[toks])
-    assert rel_fro(np64(y)[toks], yref) <= TOL
-    say("pow2 ep8 sampled parity ok")
+    LC.full_size_forward_check(synth.WORKLOADS["ep8"], experts=(0, 17, 31), pow2=True)
