@@ -1,36 +1,36 @@
 """Benchmark of the MoE expert layer on one MI355X.
 
-Headline step = one forward pass of the layer on the EP=8 share of a 256-expert
-top-8 layer (T=8192 tokens, d=7168, f=2048 SwiGLU, local experts 0-31): top-k
-routing, the expert-grouped permutation with fused 1x128 FP8 quantisation,
-grouped GEMM1 with the fused SwiGLU + quantisation epilogue, grouped GEMM2,
-weighted combine.  Weights are static there: quantised once before the timed
-region, that cost reported separately.  Inputs are seeded synthetic tensors
-already resident in HBM when timing starts.  The step is timed twice: launched
-eagerly with HIP events around every stage (the per-kernel times and the
-roofline come from these), then captured once into a HIP graph and replayed
-(the same kernels without per-launch host cost; this gives ms_per_step and the
-throughput, ms_per_step_eager the eager figure).
+Headline step = one training step of the layer on the EP=8 share of a
+256-expert top-8 layer (T=16384 tokens, d=7168, f=2048 SwiGLU, local experts
+0-31): the expert weights re-quantised to 128x128 FP8 blocks (they change every
+optimizer step), top-k routing, the expert-grouped permutation with fused 1x128
+quantisation, grouped GEMM1 with the fused SwiGLU + quantisation epilogue
+saving bf16 G/U, grouped GEMM2, the weighted combine, then the backward:
+combine backward (dY 1x128 + d_gate), dY and x re-quantised 128x1 along tokens,
+dgrad through W2 + SwiGLU backward (dGU 1x128 / 128x1, H 128x1), dgrad through
+W13 + unpermute-sum, both wgrad products and the gate backward.  Inputs are
+seeded synthetic tensors already resident in HBM; two input sets of 0.49 GB
+(x, logits, dy) alternate between steps, so no step finds its inputs in the
+256 MB last-level cache.  The step is timed twice: launched eagerly with HIP
+events around every stage (per-kernel times and the roofline come from these),
+and captured into a HIP graph per input set and replayed (ms_per_step and the
+throughput; the same kernels without per-launch host cost).
 
-Further legs, reported as sub-objects of the same JSON line:
+Further legs, reported as sub-objects of the same JSON line, each with the
+roofline of its dominant kernel:
+  ep8      forward of the T=8192 share (three rotating input sets)
   hotspot  the same forward with Zipf-skewed routing (unequal expert loads)
-  pow2     the headline forward with power-of-two (UE8M0) tile scales, which
-           the block-scaled MFMA applies itself (no VALU rescale)
-  mxfp4    the headline forward with MXFP4 expert weights (4-bit E2M1, one
-           E8M0 scale per 32 values) and power-of-two FP8 activations
-  train    forward + backward at T=16384 (dgrad and wgrad GEMMs on FP8 operands
-           re-quantised along their contraction axis), weights re-quantised
-           every step (the step time is also given without that part)
-  train_pow2  the same step with power-of-two tile scales throughout
-  train_mxfp4  the same step with MXFP4 weights in the forward and dgrad GEMMs
   replay   Router Replay of a recorded [4, 8, 131072] id tensor: every layer's
            131072 tokens in 16384-token chunks, each layer with its own weights
+  pow2 / mxfp4            the ep8 forward with power-of-two (UE8M0) tile scales /
+                          MXFP4 expert weights
+  train_pow2 / train_mxfp4  the training step with those variants
 
-Prints one JSON line.  Besides the throughput it reports the roofline fraction
-of the headline step's dominant kernel (grouped GEMM1, HBM-bound at this shape)
-from HIP events recorded on the launch stream, and the oracle's throughput on
-the host cores (a bounded sample: all tokens routed and permuted, expert work
-for 2 of the 32 local experts, extrapolated linearly in the number of experts)."""
+The oracle (plain numpy fp64, CPU) is timed first, before any GPU use, on the
+host cores: the whole training step (routing, permutation, forward, backward)
+for the first --cpu-tokens tokens of the headline workload over all 32 local
+experts, the rate reported as measured (no extrapolation); its 128x128 weight
+quantisation runs in an untimed setup, one expert per process."""
 
 import argparse
 import json
@@ -44,6 +44,7 @@ import torch
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 METRIC = "MoE-layer tokens/s + FP8 grouped-GEMM TFLOP/s (% of MFMA peak)"
+HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def parse():
@@ -51,14 +52,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ep8", choices=["ep8", "hotspot"],
-                    help="workload of the headline forward step")
-    ap.add_argument("--legs", default="hotspot,pow2,mxfp4,train,train_pow2,train_mxfp4,replay",
-                    help="comma-separated extra legs (hotspot, pow2, mxfp4, train, train_pow2, train_mxfp4, "
-                         "replay) or 'none'")
-    ap.add_argument("--train-steps", type=int, default=5)
+    ap.add_argument("--legs", default="ep8,hotspot,replay,pow2,mxfp4,train_pow2,train_mxfp4",
+                    help="comma-separated extra legs (ep8, hotspot, replay, pow2, mxfp4, train_pow2, "
+                         "train_mxfp4) or 'none'")
     ap.add_argument("--replay-passes", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="tokens of the headline workload the oracle runs in the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -79,57 +79,56 @@ def copy_calibration():
 
 # ---------------------------------------------------------------- algorithmic work
 
-def gemm_algorithmic(P, L, d, f, mxfp4=False):
-    """Algorithmic FLOPs and HBM bytes of the two forward grouped GEMMs for P local
-    pairs.  mxfp4: weights are 4-bit codes plus one scale byte per 32 values."""
-    def wbytes(n, k):
-        return n * k // 2 + n * (k // 32) if mxfp4 else n * k + (n // 128) * (k // 128) * 4
-    g1_flops = 2.0 * P * d * (2 * f)
-    g2_flops = 2.0 * P * f * d
-    g1_bytes = (L * wbytes(2 * f, d)                                      # W13 codes + scales
-                + P * d + P * (d // 128) * 4                             # Xq + scales
-                + P * f + P * (f // 128) * 4)                            # hq + scales
-    g2_bytes = (L * wbytes(d, f)
-                + P * f + P * (f // 128) * 4
-                + P * d * 2)                                             # Y bf16
-    return g1_flops, g1_bytes, g2_flops, g2_bytes
+def _wbytes(n, k, mxfp4):
+    """Bytes of one [n, k] weight matrix: FP8 codes + 128x128 fp32 scales, or
+    E2M1 codes + one E8M0 scale byte per 32 values."""
+    return n * k // 2 + n * (k // 32) if mxfp4 else n * k + (n // 128) * (k // 128) * 4
 
 
-def train_gemm_flops(P, d, f):
-    """FLOPs of the six grouped GEMMs of a training step (P local pairs)."""
-    return {"gemm1": 4.0 * P * d * f, "gemm2": 2.0 * P * d * f,
-            "dgrad2": 2.0 * P * d * f, "dgrad1": 4.0 * P * d * f,
-            "wgrad2": 2.0 * P * d * f, "wgrad13": 4.0 * P * d * f}
+def _q(n):
+    """FP8 codes of n elements + fp32 scales per 128 (1x128 or 128x1 tiles)."""
+    return n + n // 128 * 4
 
 
-def train_gemm_bytes(P, R, L, d, f, mxfp4=False):
-    """Algorithmic HBM bytes of the six grouped GEMMs of a training step: P local
-    pairs, R expert-grouped rows (segments padded to 128, the wgrad contraction).
-    FP8 operands count 1 byte per element plus fp32 scales per 128 elements;
-    MXFP4 weights half a byte per element plus one scale byte per 32."""
-    q = lambda n: n + n // 128 * 4                 # FP8 codes + 1x128 / 128x1 scales
-    if mxfp4:
-        w = lambda n: n // 2 + n // 32             # E2M1 codes + E8M0 scales
-    else:
-        w = lambda n: n + n // (128 * 128) * 4     # FP8 codes + 128x128 scales
-    return {"gemm1": w(L * 2 * f * d) + q(P * d) + q(P * f) + P * 2 * f * 2,   # + saved bf16 [G, U]
-            "gemm2": w(L * d * f) + q(P * f) + P * d * 2,
-            "dgrad2": q(P * d) + w(L * d * f) + P * f * 4,                     # dH fp32
-            "dgrad1": q(P * 2 * f) + w(L * 2 * f * d) + P * d * 2,             # dX bf16
-            "wgrad2": q(R * d) + q(R * f) + L * d * f * 2,                     # dW2 bf16
-            "wgrad13": q(R * 2 * f) + q(R * d) + L * 2 * f * d * 2}            # dW13 bf16
+def forward_work(P, L, d, f, mxfp4=False):
+    """Algorithmic FLOPs and HBM bytes of the two forward grouped GEMMs for P
+    local pairs (padding rows not counted)."""
+    return {"gemm1": (4.0 * P * d * f, L * _wbytes(2 * f, d, mxfp4) + _q(P * d) + _q(P * f)),
+            "gemm2": (2.0 * P * d * f, L * _wbytes(d, f, mxfp4) + _q(P * f) + P * d * 2)}
 
 
-def roofline_of(flops, nbytes, ms):
-    """Roofline entry of one kernel: bound by whichever floor (MFMA or HBM) is longer."""
+def train_work(P, R, L, d, f, mxfp4=False):
+    """Algorithmic FLOPs and HBM bytes of the six grouped GEMMs of a training
+    step: P local pairs, R expert-grouped rows (segments padded to 128, the wgrad
+    contraction)."""
+    w = lambda n, k: L * _wbytes(n, k, mxfp4)
+    return {"gemm1": (4.0 * P * d * f, w(2 * f, d) + _q(P * d) + _q(P * f) + P * 2 * f * 2),   # + saved bf16 G/U
+            "gemm2": (2.0 * P * d * f, w(d, f) + _q(P * f) + P * d * 2),
+            "dgrad2": (2.0 * P * d * f, _q(P * d) + w(f, d) + P * f * 4),                      # dH fp32
+            "dgrad1": (4.0 * P * d * f, _q(P * 2 * f) + w(d, 2 * f) + P * d * 2),              # dX bf16
+            "wgrad2": (2.0 * P * d * f, _q(R * d) + _q(R * f) + L * d * f * 2),                # dW2 bf16
+            "wgrad13": (4.0 * P * d * f, _q(R * 2 * f) + _q(R * d) + L * 2 * f * d * 2)}       # dW13 bf16
+
+
+def roofline_of(kernel, flops, nbytes, ms, workload):
+    """Roofline entry of one kernel: bound by whichever floor (MFMA or HBM) is
+    longer; traffic = HBM bytes per launch measured by rocprofv3 counters when a
+    profile of this kernel's current code exists."""
     t_mfma = flops / (FP8_PEAK_TFLOPS * 1e12)
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     t = ms * 1e-3
     if t_hbm >= t_mfma:
-        return {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": t_hbm / t}
-    return {"bound": "mfma", "achieved": flops / t / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": t_mfma / t}
+        r = {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": t_hbm / t}
+    else:
+        r = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": t_mfma / t}
+    r["traffic"] = measured_traffic(kernel, workload)
+    r["kernel"] = kernel
+    r["algorithmic_bytes"] = nbytes
+    r["flops"] = flops
+    r["ms"] = ms
+    return r
 
 
 def code_sha256(paths):
@@ -148,15 +147,15 @@ def code_sha256(paths):
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None when the kernel code changed since then."""
-    here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", f"gemm1_{workload}_traffic.json")
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (profiles/<kernel>_<workload>_traffic.json), or None when
+    there is none or the kernel's code changed since it was taken."""
+    path = os.path.join(HERE, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(here, "moe_expert_layer_r3_amd", "csrc")
+    src = os.path.join(HERE, "moe_expert_layer_r3_amd", "csrc")
     if code_sha256([os.path.join(src, f) for f in rec["sources"]]) != rec["code_sha256"]:
         return None
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
@@ -176,19 +175,27 @@ def free():
     torch.cuda.empty_cache()
 
 
-# ---------------------------------------------------------------- forward leg
+def timed(fn, steps):
+    """Wall time per call of fn over `steps` calls, bracketed by device syncs."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
-def forward_leg(wl, steps, warmup, dev, pow2=False, mxfp4=False):
+
+# ---------------------------------------------------------------- forward legs
+
+def forward_leg(wl, steps, warmup, dev, pow2=False, mxfp4=False, sets=3):
     from moe_expert_layer_r3_amd import synth
     from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights, weight_buffers
 
-    lg = synth.logits(wl)
-    x = synth.x(wl)
-    W13 = synth.weights(wl, "w13")
-    W2 = synth.weights(wl, "w2")
-    lg_d = torch.from_numpy(lg).to(dev)
-    x_d = x.to(dev)
-    W13_d, W2_d = W13.to(dev), W2.to(dev)
+    # `sets` input sets (x, logits) of distinct seeded token blocks, rotated
+    # across steps: 3 x 125 MB at the ep8 shape, past the last-level cache
+    xs = [synth.x(wl, t0=i * wl.T).to(dev) for i in range(sets)]
+    lgs = [torch.from_numpy(synth.logits(wl, t0=i * wl.T)).to(dev) for i in range(sets)]
+    W13_d, W2_d = synth.weights(wl, "w13").to(dev), synth.weights(wl, "w2").to(dev)
 
     # weight quantisation (once per weight version), timed on its own
     wts = None if mxfp4 else weight_buffers(wl.L, wl.d, wl.f, dev)
@@ -205,115 +212,121 @@ def forward_leg(wl, steps, warmup, dev, pow2=False, mxfp4=False):
     free()
 
     plan = ForwardPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev, pow2=pow2, mxfp4=mxfp4)
-    for _ in range(warmup):
-        plan.forward(x_d, lg_d, wts)
+    for i in range(warmup):
+        plan.forward(xs[i % sets], lgs[i % sets], wts)
     ev = stage_events(plan.STAGES, steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        plan.forward(x_d, lg_d, wts, events={n: ev[n][s] for n in plan.STAGES})
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_eager = (t1 - t0) * 1e3 / steps
+    ms_eager = timed(lambda i: plan.forward(xs[i % sets], lgs[i % sets], wts,
+                                            events={n: ev[n][i] for n in plan.STAGES}), steps)
     kern = mean_ms(ev)
-    # the same step captured once into a HIP graph and replayed: the kernels are
-    # identical, the per-launch host cost and the gaps between launches go away
-    graph = plan.capture(x_d, lg_d, wts)
-    for _ in range(warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / steps
-    del graph
+    # the same step captured once per input set into a HIP graph and replayed:
+    # the kernels are identical, the per-launch host cost goes away
+    graphs = [plan.capture(xs[i], lgs[i], wts) for i in range(sets)]
+    for i in range(warmup):
+        graphs[i % sets].replay()
+    ms = timed(lambda i: graphs[i % sets].replay(), steps)
+    del graphs
+    Ps = []
+    for i in range(sets):                      # pair count of every input set
+        plan.forward(xs[i], lgs[i], wts)
+        Ps.append(int(plan.counts.sum().item()))
     counts = plan.counts.cpu().numpy()
-    P = int(counts.sum())
-    g1f, g1b, g2f, g2b = gemm_algorithmic(P, wl.L, wl.d, wl.f, mxfp4=mxfp4)
-    g1_s, g2_s = kern["gemm1"] * 1e-3, kern["gemm2"] * 1e-3
+    P = float(np.mean(Ps))
+    work = forward_work(P, wl.L, wl.d, wl.f, mxfp4=mxfp4)
+    name = wl.name + ("_pow2" if pow2 else "") + ("_mxfp4" if mxfp4 else "")
+    gem = {n: {"ms": kern[n], "tflops": fl / (kern[n] * 1e-3) / 1e12, "gbs": by / (kern[n] * 1e-3) / 1e9,
+               "flops": fl, "bytes": by} for n, (fl, by) in work.items()}
+    g_fl = sum(fl for fl, _ in work.values())
+    g_ms = sum(kern[n] for n in work)
     res = {
         "tokens_per_s": wl.T / (ms * 1e-3),
         "ms_per_step": ms,
         "ms_per_step_eager": ms_eager,
         "kernel_ms": kern,
         "weight_quant_ms": wquant_ms,
-        "local_pairs": P,
+        "local_pairs": Ps,
         "expert_counts": {"max": int(counts.max()), "mean": float(counts.mean()), "min": int(counts.min())},
-        "gemm1": {"tflops": g1f / g1_s / 1e12, "gbs": g1b / g1_s / 1e9, "bytes": g1b, "flops": g1f},
-        "gemm2": {"tflops": g2f / g2_s / 1e12, "gbs": g2b / g2_s / 1e9, "bytes": g2b, "flops": g2f},
-        "gemm_tflops": (g1f + g2f) / (g1_s + g2_s) / 1e12,
+        "gemms": gem,
+        "gemm_tflops": g_fl / (g_ms * 1e-3) / 1e12,
+        "gemm_mfma_frac": g_fl / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+        "input_sets": sets,
+        "roofline": roofline_of("gemm1", *work["gemm1"], kern["gemm1"], name),
     }
-    res["gemm_mfma_frac"] = res["gemm_tflops"] / FP8_PEAK_TFLOPS
-    del plan, wts, lg_d, x_d
+    del plan, wts, xs, lgs
     free()
-    return res, (lg, x, W13, W2)
+    return res
 
 
-# ---------------------------------------------------------------- training leg
+# ---------------------------------------------------------------- training step
 
-def train_leg(steps, warmup, dev, pow2=False, mxfp4=False):
+def train_leg(steps, warmup, dev, pow2=False, mxfp4=False, sets=2):
     from moe_expert_layer_r3_amd import synth
-    from moe_expert_layer_r3_amd.layer import TrainPlan, quantize_weights, weight_buffers
+    from moe_expert_layer_r3_amd.layer import TrainPlan, capture_graph, quantize_weights, weight_buffers
 
     wl = synth.WORKLOADS["train"]
-    lg_d = torch.from_numpy(synth.logits(wl)).to(dev)
-    x_d = synth.x(wl).to(dev)
-    dy_d = synth.dy(wl).to(dev)
+    # `sets` input sets (x, logits, dy: 0.49 GB each) of distinct seeded token
+    # blocks, alternating between steps
+    xs = [synth.x(wl, t0=i * wl.T).to(dev) for i in range(sets)]
+    lgs = [torch.from_numpy(synth.logits(wl, t0=i * wl.T)).to(dev) for i in range(sets)]
+    dys = [synth.dy(wl, t0=i * wl.T).to(dev) for i in range(sets)]
     W13_d = synth.weights(wl, "w13").to(dev)
     W2_d = synth.weights(wl, "w2").to(dev)
     wts = None if mxfp4 else weight_buffers(wl.L, wl.d, wl.f, dev, transpose=True)
     wts = quantize_weights(W13_d, W2_d, transpose=True, out=wts, pow2=pow2, mxfp4=mxfp4)
     plan = TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev, pow2=pow2, mxfp4=mxfp4)
 
-    def step(events=None):
+    def step(i, events=None):
         if events is not None:
             events["weight_quant"][0].record()
         quantize_weights(W13_d, W2_d, transpose=True, out=wts, pow2=pow2, mxfp4=mxfp4)
         if events is not None:
             events["weight_quant"][1].record()
-        plan.forward(x_d, lg_d, wts, events=events)
-        plan.backward(x_d, dy_d, wts, events=events)
+        plan.forward(xs[i % sets], lgs[i % sets], wts, events=events)
+        plan.backward(xs[i % sets], dys[i % sets], wts, events=events)
 
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(i)
     names = ("weight_quant",) + plan.STAGES + plan.BWD_STAGES
     ev = stage_events(names, steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        step({n: ev[n][s] for n in names})
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / steps
+    ms_eager = timed(lambda i: step(i, {n: ev[n][i] for n in names}), steps)
     kern = mean_ms(ev)
-    P = int(plan.counts.sum().item())
-    R = int(plan.offsets[-1].item())
-    fl = train_gemm_flops(P, wl.d, wl.f)
-    by = train_gemm_bytes(P, R, wl.L, wl.d, wl.f, mxfp4=mxfp4)
-    gemm_ms = sum(kern[n] for n in fl)
-    per = {n: {"ms": kern[n], "tflops": fl[n] / (kern[n] * 1e-3) / 1e12,
-               "mfma_frac": fl[n] / (kern[n] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
-               "gbs": by[n] / (kern[n] * 1e-3) / 1e9, "flops": fl[n], "bytes": by[n],
-               "roofline": roofline_of(fl[n], by[n], kern[n])} for n in fl}
-    top = max(fl, key=lambda n: kern[n])
+    graphs = [capture_graph(lambda i=i: step(i)) for i in range(sets)]
+    for i in range(warmup):
+        graphs[i % sets].replay()
+    ms = timed(lambda i: graphs[i % sets].replay(), steps)
+    del graphs
+    Ps, Rs = [], []
+    for i in range(sets):
+        step(i)
+        Ps.append(int(plan.counts.sum().item()))
+        Rs.append(int(plan.offsets[-1].item()))
+    P, R = float(np.mean(Ps)), float(np.mean(Rs))
+    work = train_work(P, R, wl.L, wl.d, wl.f, mxfp4=mxfp4)
+    name = "train" + ("_pow2" if pow2 else "") + ("_mxfp4" if mxfp4 else "")
+    gem = {n: {"ms": kern[n], "tflops": fl / (kern[n] * 1e-3) / 1e12,
+               "mfma_frac": fl / (kern[n] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+               "gbs": by / (kern[n] * 1e-3) / 1e9, "flops": fl, "bytes": by} for n, (fl, by) in work.items()}
+    g_fl = sum(fl for fl, _ in work.values())
+    g_ms = sum(kern[n] for n in work)
+    top = max(work, key=lambda n: kern[n])
     res = {
-        "workload": f"train: T={wl.T}, d={wl.d}, f={wl.f}, {wl.L} of {wl.E} experts local, top-{wl.k}, "
+        "workload": f"{name}: T={wl.T}, d={wl.d}, f={wl.f}, {wl.L} of {wl.E} experts local, top-{wl.k}, "
                     "forward + backward, weights re-quantised each step"
                     + (", power-of-two (UE8M0) tile scales" if pow2 else "")
                     + (", MXFP4 weights (forward and dgrad), FP8 power-of-two activations" if mxfp4 else ""),
         "tokens_per_s": wl.T / (ms * 1e-3),
         "ms_per_step": ms,
+        "ms_per_step_eager": ms_eager,
         "ms_per_step_excl_weight_quant": ms - kern["weight_quant"],
-        "local_pairs": P,
+        "local_pairs": Ps,
+        "rows": Rs,
         "kernel_ms": kern,
-        "gemms": per,
-        "gemm_tflops": sum(fl.values()) / (gemm_ms * 1e-3) / 1e12,
-        "roofline": dict(kernel=top, **per[top]["roofline"], traffic=None),
+        "gemms": gem,
+        "gemm_tflops": g_fl / (g_ms * 1e-3) / 1e12,
+        "gemm_mfma_frac": g_fl / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+        "input_sets": sets,
+        "roofline": roofline_of(top, *work[top], kern[top], name),
     }
-    res["gemm_mfma_frac"] = res["gemm_tflops"] / FP8_PEAK_TFLOPS
-    del plan, wts, lg_d, x_d, dy_d, W13_d, W2_d
+    del plan, wts, xs, lgs, dys, W13_d, W2_d
     free()
     return res
 
@@ -325,8 +338,12 @@ def replay_leg(passes, dev):
     from moe_expert_layer_r3_amd.layer import ForwardPlan, quantize_weights, weight_buffers
 
     wl = synth.WORKLOADS["replay"]
-    rec_d = torch.from_numpy(synth.replay_record(wl)).to(dev)
+    rec = synth.replay_record(wl)
+    rec_d = torch.from_numpy(rec).to(dev)
     nchunk = wl.seq_len // wl.T
+    # local pairs of every chunk, straight from the record
+    loc = (rec >= wl.e0) & (rec < wl.e0 + wl.L)
+    P = loc.reshape(wl.n_layers, wl.k, nchunk, wl.T).sum(axis=(1, 3))          # [layer, chunk]
     layers = []
     for l in range(wl.n_layers):
         wts = weight_buffers(wl.L, wl.d, wl.f, dev)
@@ -347,21 +364,24 @@ def replay_leg(passes, dev):
 
     one_pass()
     ev = stage_events(plan.STAGES, passes * wl.n_layers * nchunk)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(passes):
-        one_pass(ev, i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / passes
+    ms = timed(lambda i: one_pass(ev, i), passes)
     flags = int(plan.status.item())
+    kern = mean_ms(ev)
+    work = forward_work(float(P.mean()), wl.L, wl.d, wl.f)
+    g_fl = sum(fl for fl, _ in work.values())
+    g_ms = sum(kern[n] for n in work)
     res = {
         "workload": f"replay: record [{wl.n_layers}, {wl.k}, {wl.seq_len}] Zipf({wl.rec_zipf}) ids, "
                     f"{wl.T}-token chunks, d={wl.d}, f={wl.f}, {wl.L} of {wl.E} experts local, forward",
         "layer_tokens_per_s": wl.n_layers * wl.seq_len / (ms * 1e-3),
         "ms_per_pass": ms,
-        "kernel_ms_per_chunk": mean_ms(ev),
+        "kernel_ms_per_chunk": kern,
+        "local_pairs_per_chunk": {"mean": float(P.mean()), "min": int(P.min()), "max": int(P.max()),
+                                  "total": int(P.sum())},
+        "gemm_tflops": g_fl / (g_ms * 1e-3) / 1e12,
+        "gemm_mfma_frac": g_fl / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
         "status_flags": flags,
+        "roofline": roofline_of("gemm1", *work["gemm1"], kern["gemm1"], "replay"),
     }
     del plan, layers, rec_d
     free()
@@ -370,42 +390,73 @@ def replay_leg(passes, dev):
 
 # ---------------------------------------------------------------- host baseline
 
-def cpu_baseline(wl, lg, x_bf16, W13, W2):
-    """The oracle on the host: routing + permutation for all tokens, expert work
-    (gather, quantise, GEMMs, SwiGLU, combine) for 2 of the L local experts,
-    extrapolated to L experts."""
-    from oracle import blockfp8 as OQ, dispatch as OD, gemm as OG, layer as OL, routing as OR
-    from oracle.numerics import bf16, f32
-    Ls = 2
-    xs = x_bf16.float().numpy().astype(np.float64)
-    w13 = W13[:Ls].float().numpy().astype(np.float64)
-    w2 = W2[:Ls].float().numpy().astype(np.float64)
-    wq13 = OQ.quant_128x128(w13)
-    wq2 = OQ.quant_128x128(w2)
+def _oracle_expert_weights(args):
+    """One expert's 128x128 FP8 weights quantised by the oracle (process-pool
+    worker of the baseline's untimed setup)."""
+    from moe_expert_layer_r3_amd import synth
+    from oracle import blockfp8 as OQ
+    wname, e = args
+    wl = synth.WORKLOADS[wname]
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    a = OQ.quant_128x128(f64(synth.expert_weights(wl, "w13", e))[None])
+    b = OQ.quant_128x128(f64(synth.expert_weights(wl, "w2", e))[None])
+    return a[0][0], a[1][0], b[0][0], b[1][0]
+
+
+def cpu_baseline(Ts):
+    """The oracle's training step on the host, for the first Ts tokens of the
+    headline workload and all its local experts.  Must run before the GPU is
+    initialised (the setup forks a process pool)."""
+    from concurrent.futures import ProcessPoolExecutor
+    from moe_expert_layer_r3_amd import synth
+    from oracle import layer as OL, routing as OR
+
+    wl = synth.WORKLOADS["train"]
+    ncores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    ids, w = OR.topk(lg, wl.k)
-    c, o, rp, pr = OD.permute_index(ids, wl.e0, wl.L)
+    with ProcessPoolExecutor(min(ncores, 16, wl.L)) as ex:
+        parts = list(ex.map(_oracle_expert_weights, [(wl.name, e) for e in range(wl.L)]))
+    wq = ((np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts])),
+          (np.stack([p[2] for p in parts]), np.stack([p[3] for p in parts])))
+    del parts
+    setup_s = time.perf_counter() - t0
+    lg = synth.logits(wl, T=Ts)
+    x = synth.x(wl, T=Ts).float().numpy().astype(np.float64)
+    dy = synth.dy(wl, T=Ts).float().numpy().astype(np.float64)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = ncores
     t1 = time.perf_counter()
-    # expert part for experts 0..Ls-1 (their rows only)
-    c2, o2, rp2, pr2 = OD.permute_index(ids, wl.e0, Ls)
-    Xp = OD.gather_rows(xs, rp2, wl.k)
-    Xq, Xs = OQ.quant_1x128(Xp)
-    GU = OG.grouped_forward(Xq, Xs, c2, o2, wq13[0], wq13[1])
-    h = f32(OL.silu(f32(GU[:, :wl.f])) * f32(GU[:, wl.f:]))
-    hq, hs = OQ.quant_1x128(h)
-    Y = bf16(OG.grouped_forward(hq, hs, c2, o2, wq2[0], wq2[1]))
-    OD.combine(Y, pr2, w)
+    ids, w = OR.topk(lg, wl.k)
+    fw = OL.forward(x, ids, w, wl.e0, wl.L, wq)
     t2 = time.perf_counter()
-    est = (t1 - t0) + (t2 - t1) * (wl.L / Ls)
+    OL.backward(fw, dy, ids, w, wl.E, wq)
+    t3 = time.perf_counter()
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     return {
-        "value": wl.T / est,
+        "value": Ts / (t3 - t1),
         "unit": "tokens/s",
-        "cores": len(os.sched_getaffinity(0)),
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"{wl.name} workload: routing and permutation of all {wl.T} tokens timed "
-                   f"({t1 - t0:.2f} s); expert work for {Ls} of {wl.L} local experts timed "
-                   f"({t2 - t1:.2f} s) and scaled x{wl.L // Ls}; weight quantisation excluded "
-                   f"(static weights, as on the GPU)"),
+        "sample": (f"train workload, tokens 0-{Ts - 1} ({int(fw['counts'].sum())} local pairs) through the whole "
+                   f"training step over all {wl.L} local experts: top-k, permutation, forward, backward with "
+                   f"both wgrad products and the gate backward, timed as run ({t3 - t1:.1f} s: forward "
+                   f"{t2 - t1:.1f} s, backward {t3 - t2:.1f} s), no extrapolation; the oracle's 128x128 weight "
+                   f"quantisation ran before, untimed ({setup_s:.1f} s in a process pool). Much of the "
+                   f"backward's time is per-step work that does not scale with tokens (bf16 rounding of the fp64 "
+                   f"weight gradients), so the rate at T={wl.T} would be higher."),
+        "cpu_model": model,
+        "host_cores": ncores,
+        "seconds": t3 - t1,
     }
 
 
@@ -418,13 +469,17 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the expert-parallel exchange across GPUs is not part of it", file=sys.stderr)
         sys.exit(2)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_tokens)          # before any GPU use (the setup forks)
+        print(f"# cpu baseline done ({cpu['seconds']:.1f} s)", file=sys.stderr, flush=True)
     from moe_expert_layer_r3_amd import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = synth.WORKLOADS[args.workload]
-    head, inputs = forward_leg(wl, args.steps, args.warmup, dev)
-    g1 = head["gemm1"]
+    wl = synth.WORKLOADS["train"]
+    head = train_leg(args.steps, args.warmup, dev)
+    print("# headline training step done", file=sys.stderr, flush=True)
     out = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -438,49 +493,45 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8-e4m3 (fp32 accumulate, bf16 activations)",
         "data": "synthetic (seeded normals; random-init N(0,0.02) expert weights)",
-        "config": {"workload": f"{wl.name}: one EP=8 share of a 256-expert top-8 MoE layer forward",
-                   "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "local_experts": wl.L, "top_k": wl.k,
-                   "local_pairs": head["local_pairs"]},
-        "roofline": {"bound": "hbm", "kernel": "grouped GEMM1 + SwiGLU + quant (gemm_wide_kernel<1,false,false>, 256x256 tiles)",
-                     "achieved": g1["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": g1["gbs"] / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(wl.name)},
+        "config": {"workload": head["workload"], "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E,
+                   "local_experts": wl.L, "top_k": wl.k, "local_pairs": head["local_pairs"]},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
         "gemm_tflops": head["gemm_tflops"],
         "gemm_mfma_frac": head["gemm_mfma_frac"],
         "ms_per_step_eager": head["ms_per_step_eager"],
+        "ms_per_step_excl_weight_quant": head["ms_per_step_excl_weight_quant"],
         "kernel_ms": head["kernel_ms"],
-        "weight_quant_ms": head["weight_quant_ms"],
-        "expert_counts": head["expert_counts"],
+        "gemms": head["gemms"],
+        "input_sets": head["input_sets"],
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, *inputs)
-    del inputs
+    if cpu is None:
+        del out["cpu_baseline"]
     legs = [] if args.legs == "none" else [s for s in args.legs.split(",") if s]
     out["legs"] = {}
     for leg in legs:
-        if leg == "hotspot" and args.workload != "hotspot":
-            r, _ = forward_leg(synth.WORKLOADS["hotspot"], args.steps, args.warmup, dev)
-            r["workload"] = "hotspot: ep8 shape, logits biased -1.2 ln(e+1) (expert 0 hottest), forward"
-            out["legs"]["hotspot"] = r
+        if leg in ("ep8", "hotspot"):
+            r = forward_leg(synth.WORKLOADS[leg], args.steps, args.warmup, dev)
+            r["workload"] = {"ep8": "ep8: T=8192 share of a 256-expert top-8 layer, forward",
+                             "hotspot": "hotspot: ep8 shape, logits biased -1.2 ln(e+1) (expert 0 hottest), "
+                                        "forward"}[leg]
         elif leg == "pow2":
-            r, _ = forward_leg(wl, args.steps, args.warmup, dev, pow2=True)
-            r["workload"] = (f"{wl.name} forward with power-of-two (UE8M0) tile scales applied by the "
-                             "block-scaled MFMA (a variant; the headline uses fp32 scales)")
-            out["legs"]["pow2"] = r
+            r = forward_leg(synth.WORKLOADS["ep8"], args.steps, args.warmup, dev, pow2=True)
+            r["workload"] = ("ep8 forward with power-of-two (UE8M0) tile scales applied by the block-scaled MFMA "
+                             "(a variant; the other legs use fp32 scales)")
         elif leg == "mxfp4":
-            r, _ = forward_leg(wl, args.steps, args.warmup, dev, mxfp4=True)
-            r["workload"] = (f"{wl.name} forward with MXFP4 expert weights (E2M1, E8M0 scale per 32 values) and "
-                             "power-of-two FP8 activations (a variant; the headline uses FP8 weights)")
-            out["legs"]["mxfp4"] = r
-        elif leg == "train":
-            out["legs"]["train"] = train_leg(args.train_steps, 2, dev)
+            r = forward_leg(synth.WORKLOADS["ep8"], args.steps, args.warmup, dev, mxfp4=True)
+            r["workload"] = ("ep8 forward with MXFP4 expert weights (E2M1, E8M0 scale per 32 values) and "
+                             "power-of-two FP8 activations (a variant)")
         elif leg == "train_pow2":
-            out["legs"]["train_pow2"] = train_leg(args.train_steps, 2, dev, pow2=True)
+            r = train_leg(args.steps, args.warmup, dev, pow2=True)
         elif leg == "train_mxfp4":
-            out["legs"]["train_mxfp4"] = train_leg(args.train_steps, 2, dev, mxfp4=True)
+            r = train_leg(args.steps, args.warmup, dev, mxfp4=True)
         elif leg == "replay":
-            out["legs"]["replay"] = replay_leg(args.replay_passes, dev)
+            r = replay_leg(args.replay_passes, dev)
         else:
             raise SystemExit(f"unknown leg {leg}")
+        out["legs"][leg] = r
         print(f"# leg {leg} done", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 

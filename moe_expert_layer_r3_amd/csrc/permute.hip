@@ -288,11 +288,13 @@ extern "C" int moe_permute_workspace(int64_t T, int32_t k, int32_t L, size_t* by
     return MOE_OK;
 }
 
-extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L, int64_t row_cap,
-                           int32_t* counts, int32_t* offsets, int32_t* row_pair, int32_t* pair_row,
-                           const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq, float* xq_s,
-                           int32_t quant_flags, void* ws, size_t ws_bytes, int32_t* dev_status,
-                           hipStream_t stream) {
+// Validation and launches shared by moe_permute and moe_permute_noalloc; the
+// chunk counts live in `chunk` (nchunk * L int32), written in full by the hist
+// kernel before the scan and the scatter read them.
+static int permute_check(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L, int64_t row_cap,
+                         int32_t* counts, int32_t* offsets, int32_t* row_pair, int32_t* pair_row,
+                         const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq, float* xq_s,
+                         int32_t quant_flags) {
     MOE_REQUIRE(T >= 0 && T <= ((int64_t)1 << 31) / 16, MOE_ERR_SHAPE, "permute: bad T=%lld", (long long)T);
     MOE_REQUIRE(k >= 1 && k <= 16, MOE_ERR_SHAPE, "permute: k=%d outside [1, 16]", k);
     MOE_REQUIRE(L >= 1 && L <= MAXL && e0 >= 0, MOE_ERR_SHAPE, "permute: L=%d outside [1, 1024] or e0<0", L);
@@ -309,13 +311,15 @@ extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0,
     } else {
         MOE_REQUIRE(!x_perm && !xq, MOE_ERR_NULL, "permute: x_perm/xq given without x");
     }
-    size_t need = 0;
-    moe_permute_workspace(T, k, L, &need);
-    MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "permute: workspace %zu < %zu bytes", ws_bytes, need);
+    return MOE_OK;
+}
 
+static int permute_launch(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L, int64_t row_cap,
+                          int32_t* counts, int32_t* offsets, int32_t* row_pair, int32_t* pair_row,
+                          const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq, float* xq_s,
+                          int32_t quant_flags, int32_t* chunk, int32_t* dev_status, hipStream_t stream) {
     const int64_t P = T * k;
     const int nchunk = (int)perm_chunks(T, k);
-    int32_t* chunk = static_cast<int32_t*>(ws);
     if (nchunk > 0) {
         perm_hist_kernel<<<dim3(nchunk), dim3(PBLOCK), 0, stream>>>(ids, P, e0, L, chunk);
         MOE_LAUNCH_CHECK("perm_hist_kernel");
@@ -336,4 +340,19 @@ extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0,
         MOE_LAUNCH_CHECK("gather_quant_kernel");
     }
     return MOE_OK;
+}
+
+extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L, int64_t row_cap,
+                           int32_t* counts, int32_t* offsets, int32_t* row_pair, int32_t* pair_row,
+                           const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq, float* xq_s,
+                           int32_t quant_flags, void* ws, size_t ws_bytes, int32_t* dev_status,
+                           hipStream_t stream) {
+    int rc = permute_check(ids, T, k, e0, L, row_cap, counts, offsets, row_pair, pair_row, x, d, x_perm, xq, xq_s,
+                           quant_flags);
+    if (rc != MOE_OK) return rc;
+    size_t need = 0;
+    moe_permute_workspace(T, k, L, &need);
+    MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "permute: workspace %zu < %zu bytes", ws_bytes, need);
+    return permute_launch(ids, T, k, e0, L, row_cap, counts, offsets, row_pair, pair_row, x, d, x_perm, xq, xq_s,
+                          quant_flags, static_cast<int32_t*>(ws), dev_status, stream);
 }

@@ -170,16 +170,24 @@ class ForwardPlan:
         pass is capturable; graph.replay() reruns it on whatever x, logits and
         weights the buffers hold at that time, without per-launch host cost.
         ``warmup`` eager passes run first on the capture's side stream."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for _ in range(warmup):
-                self.forward(x, logits, wts, replay=replay)
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            self.forward(x, logits, wts, replay=replay)
-        return graph
+        return capture_graph(lambda: self.forward(x, logits, wts, replay=replay), warmup)
+
+
+def capture_graph(fn, warmup=1):
+    """Record the launches ``fn`` issues on the current stream into a HIP graph
+    (torch.cuda.CUDAGraph), after ``warmup`` eager calls on a side stream.  fn
+    must only launch library kernels on preallocated buffers: no allocation,
+    host synchronisation or memset."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
 
 
 class TrainPlan(ForwardPlan):

@@ -667,3 +667,43 @@ def test_tiny_train_end_to_end_explained(pow2):
             f"oracle on GPU codes vs oracle's own chain {e_between:.2e}")
         assert e_codes <= TOL, name
         assert e_own <= 1e-2, name
+
+
+def test_train_step_graph_replay():
+    """The training step as the benchmark replays it: weights re-quantised,
+    forward and backward captured into one HIP graph per input set.  Each
+    replay, with eager steps and synchronisations in between and every buffer
+    poisoned first, writes bit for bit what the eager step writes on the same
+    inputs."""
+    wl = synth.WORKLOADS["train"]
+    say("train graph: inputs")
+    xs = [synth.x(wl, t0=i * wl.T).to(DEV) for i in range(2)]
+    lgs = [gpu(synth.logits(wl, t0=i * wl.T)) for i in range(2)]
+    dys = [synth.dy(wl, t0=i * wl.T).to(DEV) for i in range(2)]
+    W13 = synth.weights(wl, "w13").to(DEV)
+    W2 = synth.weights(wl, "w2").to(DEV)
+    wts = ML.weight_buffers(wl.L, wl.d, wl.f, DEV, transpose=True)
+    plan = ML.TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, e0=wl.e0, device=DEV)
+
+    def step(i):
+        ML.quantize_weights(W13, W2, transpose=True, out=wts)
+        plan.forward(xs[i], lgs[i], wts)
+        plan.backward(xs[i], dys[i], wts)
+
+    say("train graph: capture")
+    graphs = [ML.capture_graph(lambda i=i: step(i)) for i in range(2)]
+    bufs = _plan_tensors(plan)
+    bufs.update({f"wts.{n}": t for n, t in wts.items()})
+    for it in (1, 0, 1, 0):
+        _poison(bufs)
+        step(it)
+        torch.cuda.synchronize()
+        ref = {n: t.clone() for n, t in bufs.items()}
+        _poison(bufs)
+        graphs[it].replay()
+        torch.cuda.synchronize()
+        say(f"train graph: replay with input set {it}")
+        differ = [n for n in bufs if not torch.equal(bufs[n], ref[n])]
+        assert not differ, f"graph replay differs from the eager step in {differ}"
+        del ref
+    assert int(plan.status.item()) == 0
