@@ -139,6 +139,27 @@ int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L,
                 int32_t quant_flags, void* ws, size_t ws_bytes, int32_t* dev_status,
                 hipStream_t stream);
 
+/* Largest workspace, in bytes, that moe_permute_noalloc can serve from its
+ * device scratch: moe_permute_noalloc accepts (T, k, L) iff
+ * moe_permute_workspace(T, k, L) <= this (e.g. T*k <= 8M pairs at L = 32). */
+#define MOE_PERMUTE_NOALLOC_MAX_WS (1 << 20)
+
+/* moe_permute without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, outputs and errors as moe_permute;
+ * the workspace is a fixed device array of MOE_PERMUTE_NOALLOC_MAX_WS bytes
+ * inside the library (one per GPU, held until the process ends).  Larger
+ * (T, k, L) return MOE_ERR_WORKSPACE before anything is launched.  The call
+ * allocates nothing; its first call on a device looks up that device's copy of
+ * the array (a HIP symbol lookup, no allocation).  Every call on one GPU shares
+ * the array: calls that overlap on one GPU (different streams) race and must
+ * be serialised by the caller.                                               */
+int moe_permute_noalloc(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L,
+                        int64_t row_cap, int32_t* counts, int32_t* offsets,
+                        int32_t* row_pair, int32_t* pair_row,
+                        const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq, float* xq_s,
+                        int32_t quant_flags, int32_t* dev_status, hipStream_t stream);
+
 /* ---- block-scaled FP8 quantisation [FP8] -------------------------------- */
 
 enum { MOE_TILE_1x128 = 0, MOE_TILE_128x128 = 1 };

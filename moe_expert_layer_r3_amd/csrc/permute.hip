@@ -16,6 +16,8 @@
 // Chunks are small (1024 pairs) so that even a few thousand tokens spread the
 // index work over many workgroups; every step is latency-bound, not
 // bandwidth-bound.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace moe {
@@ -355,4 +357,59 @@ extern "C" int moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t e0,
     MOE_REQUIRE(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "permute: workspace %zu < %zu bytes", ws_bytes, need);
     return permute_launch(ids, T, k, e0, L, row_cap, counts, offsets, row_pair, pair_row, x, d, x_perm, xq, xq_s,
                           quant_flags, static_cast<int32_t*>(ws), dev_status, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+//
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops): the chunk counts live in this file-scope
+// device array instead of a caller workspace.  Each GPU holds its own copy
+// until the process ends; every call on a GPU shares it, so calls that overlap
+// on one GPU (concurrent streams) race.  Nothing in it needs clearing: the
+// hist kernel writes every count the scan and scatter read.
+namespace moe {
+constexpr size_t PERMUTE_SCRATCH_BYTES = MOE_PERMUTE_NOALLOC_MAX_WS;
+static __device__ __align__(256) int32_t scratch[PERMUTE_SCRATCH_BYTES / sizeof(int32_t)];
+
+// Device address of `scratch` on the current device, looked up once per device
+// (the array's name in host code is only a stand-in for the symbol).
+static int scratch_address(int32_t** out) {
+    constexpr int MAXDEV = 64;
+    static int32_t* ptrs[MAXDEV] = {};
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    MOE_REQUIRE(e == hipSuccess, MOE_ERR_HIP, "permute_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    MOE_REQUIRE(dev >= 0 && dev < MAXDEV, MOE_ERR_UNSUPPORTED, "permute_noalloc: device %d >= %d", dev, MAXDEV);
+    std::lock_guard<std::mutex> lk(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        MOE_REQUIRE(e == hipSuccess && p, MOE_ERR_HIP, "permute_noalloc: hipGetSymbolAddress: %s",
+                    hipGetErrorString(e));
+        ptrs[dev] = static_cast<int32_t*>(p);
+    }
+    *out = ptrs[dev];
+    return MOE_OK;
+}
+}  // namespace moe
+
+extern "C" int moe_permute_noalloc(const int32_t* ids, int64_t T, int32_t k, int32_t e0, int32_t L,
+                                   int64_t row_cap, int32_t* counts, int32_t* offsets, int32_t* row_pair,
+                                   int32_t* pair_row, const uint16_t* x, int32_t d, uint16_t* x_perm, uint8_t* xq,
+                                   float* xq_s, int32_t quant_flags, int32_t* dev_status, hipStream_t stream) {
+    int rc = permute_check(ids, T, k, e0, L, row_cap, counts, offsets, row_pair, pair_row, x, d, x_perm, xq, xq_s,
+                           quant_flags);
+    if (rc != MOE_OK) return rc;
+    size_t need = 0;
+    moe_permute_workspace(T, k, L, &need);
+    MOE_REQUIRE(need <= PERMUTE_SCRATCH_BYTES, MOE_ERR_WORKSPACE,
+                "permute_noalloc: T=%lld, k=%d, L=%d need %zu bytes of chunk counts, more than the %zu bytes of "
+                "its device scratch (use moe_permute with a workspace)",
+                (long long)T, k, L, need, PERMUTE_SCRATCH_BYTES);
+    int32_t* chunk = nullptr;
+    rc = scratch_address(&chunk);
+    if (rc != MOE_OK) return rc;
+    return permute_launch(ids, T, k, e0, L, row_cap, counts, offsets, row_pair, pair_row, x, d, x_perm, xq, xq_s,
+                          quant_flags, chunk, dev_status, stream);
 }

@@ -46,6 +46,8 @@ _SIGS = {
     "moe_permute_workspace": (ctypes.c_int, [_I64, _I32, _I32, ctypes.POINTER(_SZ)]),
     "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P,
                                    _P, _I32, _P, _P, _P, _I32, _P, _SZ, _P, _P]),
+    "moe_permute_noalloc": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P,
+                                           _P, _I32, _P, _P, _P, _I32, _P, _P]),
     "moe_quant_fp8": (ctypes.c_int, [_P, _I32, _I64, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
     "moe_quant_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "moe_quant_fp8_rows_t": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _P, _P, _I32, _P]),
