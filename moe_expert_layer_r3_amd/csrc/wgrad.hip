@@ -57,6 +57,7 @@ struct WgradArgs {
     int64_t row_cap;
     int M;
     int N;
+    int nfast;  // 1: n-tiles vary fastest in the tile order (B is the smaller operand)
     uint16_t* dW;
 };
 
@@ -177,26 +178,32 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     const uint32_t sa_off = (uint32_t)(((wave >> 2) * 64 + (lane & 3) * 16 + (wave & 3) * 4 + ((lane & 15) >> 2)) * 4);
     const uint32_t sb_off = (uint32_t)((lane & (SROWS - 1)) * 4);
 
-    // A tile is (j, nt, mt): the j-th expert with rows, n-tile, m-tile (m
-    // fastest: neighbours share B).  Workgroup lb takes tiles lb, lb + G, ...;
-    // the step G is split into carries so that no division runs per tile.
+    // A tile is (j, s, f): the j-th expert with rows, then a slow and a fast
+    // tile index.  The fast index runs over the smaller operand's tiles
+    // (m-tiles when M <= N, else n-tiles): the tiles one XCD runs side by side
+    // then share one tile of the larger operand and sweep the smaller one,
+    // which stays in that XCD's L2 from one round of tiles to the next.
+    // Workgroup lb takes tiles lb, lb + G, ...; the step G is split into
+    // carries so that no division runs per tile.
     struct Pos {
-        int j, nt, mt;
+        int j, s, f;
     };
-    const int Gj = G / TPE, Gr = G - Gj * TPE, Gnt = Gr / MT, Gmt = Gr - Gnt * MT;
+    const bool nfast = g.nfast != 0;
+    const int FT = nfast ? NT : MT, ST = nfast ? MT : NT;
+    const int Gj = G / TPE, Gr = G - Gj * TPE, Gs = Gr / FT, Gf = Gr - Gs * FT;
     auto step_pos = [&](Pos& p) {
-        p.mt += Gmt;
-        int c = p.mt >= MT ? 1 : 0;
-        p.mt -= c * MT;
-        p.nt += Gnt + c;
-        c = p.nt >= NT ? 1 : 0;
-        p.nt -= c * NT;
+        p.f += Gf;
+        int c = p.f >= FT ? 1 : 0;
+        p.f -= c * FT;
+        p.s += Gs + c;
+        c = p.s >= ST ? 1 : 0;
+        p.s -= c * ST;
         p.j += Gj + c;
     };
     Pos p0;
     p0.j = lb / TPE;
-    p0.nt = (lb - p0.j * TPE) / MT;
-    p0.mt = lb - p0.j * TPE - p0.nt * MT;
+    p0.s = (lb - p0.j * TPE) / FT;
+    p0.f = lb - p0.j * TPE - p0.s * FT;
     auto nkb_of = [&](const Pos& p) -> int {
         return p.j < Lne ? (__builtin_amdgcn_readfirstlane(tab_x[p.j]) >> 10) : 0;
     };
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         const float* sb;   // this wave's B scales, first token block
     };
     auto src_of = [&](const Pos& p) {
-        const int nt = p.nt, mt = p.mt;
+        const int nt = nfast ? p.f : p.s, mt = nfast ? p.s : p.f;
         const int64_t lo = __builtin_amdgcn_readfirstlane(tab_lo[p.j]);
         Src s;
         s.a = g.aT + ((lo / WBK) * M + (int64_t)mt * WBM + wave * ASEG * 8) * WBK;
@@ -218,7 +225,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     };
     auto dst_of = [&](const Pos& p) -> uint16_t* {
         const int e = __builtin_amdgcn_readfirstlane(tab_x[p.j]) & 1023;
-        return g.dW + (int64_t)e * M * N + (int64_t)p.mt * WBM * N + (int64_t)p.nt * BN;
+        const int nt = nfast ? p.f : p.s, mt = nfast ? p.s : p.f;
+        return g.dW + (int64_t)e * M * N + (int64_t)mt * WBM * N + (int64_t)nt * BN;
     };
 
     // Waves 0-3 (one per SIMD) issue every stage's DMA: each moves its own
@@ -521,7 +529,7 @@ extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, 
     MOE_REQUIRE((int64_t)L * (M / WBM) * (N / 128) < ((int64_t)1 << 31), MOE_ERR_SHAPE,
                 "grouped_gemm_wgrad: too many tiles");
     MOE_REQUIRE(aT && aT_s && bT && bT_s && offsets && dW, MOE_ERR_NULL, "grouped_gemm_wgrad: NULL argument");
-    WgradArgs a{aT, aT_s, bT, bT_s, offsets, L, row_cap, M, N, dW};
+    WgradArgs a{aT, aT_s, bT, bT_s, offsets, L, row_cap, M, N, N < M ? 1 : 0, dW};
     const int grid = (num_cus() + 7) / 8 * 8;  // persistent, one block per CU
     auto go = [&](auto kern) { kern<<<dim3(grid), dim3(WTHREADS), 0, stream>>>(a); };
     if (N % 256 == 0)
