@@ -810,12 +810,17 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         ti.rot = ((mt & 1) * 2 + (nt & 3) * 2) % nkb;
         return ti;
     };
+    // the tile's two B scale rows (nkb <= GMAXKB <= 2 * GTHREADS: one load
+    // per thread, from a uniform base, so no per-lane 64-bit pointer is formed)
+    static_assert(GMAXKB <= 2 * GTHREADS, "one B scale per thread");
     auto stage_bscale = [&](const Tile& ti) {
         if constexpr (WF4) return;
-        for (int i = tid; i < 2 * nkb; i += GTHREADS) {
-            const int kb = i >> 1, which = i & 1;
-            bscale[kb][which] = (which ? ti.bs_hi : ti.bs_lo)[kb];
-        }
+        // waves 0-3: the low row, 4-7: the high one; the index comes from the
+        // wave (uniform) and the lane id (recomputed), not a live register
+        const int half = wave >> 2;
+        const float* src = half ? ti.bs_hi : ti.bs_lo;
+        const int kb = (wave & 3) * 64 + (int)__lane_id();
+        if (kb < nkb) bscale[kb][half] = src[kb];
     };
     const uint32_t bs_rd = lds_addr(&bscale[0][0]);
     const bool second_blk = !is_swiglu(EPI) && wn >= 2;

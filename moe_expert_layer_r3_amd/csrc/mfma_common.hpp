@@ -82,6 +82,10 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
 // this point, and no register copy is made (the copy opaque() needs costs a
 // v_mov per address per use).
 __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
+// The same for a wave-uniform value kept in an SGPR: an address formed from it
+// after this point cannot be hoisted out of the loop that contains it (per
+// stage address pairs held across a loop cost a VGPR each).
+__device__ __forceinline__ void pin_s(uint32_t& v) { asm volatile("" : "+s"(v)); }
 
 // Workgroup barrier that the instruction scheduler may not move any
 // instruction across: phases separated by it (MFMA work on one side, LDS reads

@@ -207,6 +207,12 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     auto nkb_of = [&](const Pos& p) -> int {
         return p.j < Lne ? (__builtin_amdgcn_readfirstlane(tab_x[p.j]) >> 10) : 0;
     };
+    // The tiles an XCD runs side by side share one tile of the larger
+    // operand; each starts its K loop at a different token block (its fast
+    // index modulo the block count), so that they do not all request the same
+    // lines of the shared tile at once.  Only the order of the fp32 block sums
+    // changes.
+    auto rot_of = [&](const Pos& p, int nkb) -> int { return nkb > 0 ? p.f % nkb : 0; };
     struct Src {
         const uint8_t* a;  // this wave's first A row at the segment start
         const uint8_t* b;
@@ -259,18 +265,21 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         });
     };
 
-    // issue cursor: the K step two ahead of the one being waited for
+    // issue cursor: the K step two ahead of the one being waited for (i_kb
+    // counts the tile's steps, i_kr is the token block it reads)
     Pos ip = p0;
-    int i_kb = 0, i_nkb = nkb_of(ip);
+    int i_kb = 0, i_nkb = nkb_of(ip), i_kr = rot_of(ip, i_nkb);
     Src isrc{};
     if (ip.j < Lne) isrc = src_of(ip);
     auto issue_next = [&](auto stage_c) -> bool {
         if (ip.j >= Lne) return false;
-        issue(stage_c, i_kb, isrc);
+        issue(stage_c, i_kr, isrc);
+        if (++i_kr == i_nkb) i_kr = 0;
         if (++i_kb == i_nkb) {
             step_pos(ip);
             i_kb = 0;
             i_nkb = nkb_of(ip);
+            i_kr = rot_of(ip, i_nkb);
             if (ip.j < Lne) isrc = src_of(ip);
         }
         return true;
@@ -511,6 +520,363 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     }
 }
 
+
+// ---------------------------------------------------------------- 256 x 256 tiles
+//
+// The same products with power-of-two scales on 256 x 256 tiles (M and N
+// multiples of 256).  A K step moves 64 KB of operands (a token block's 256 A
+// rows and 256 B rows, each a contiguous 32 KB piece) for twice the MFMA work
+// of a 128 x 256 tile's 48 KB.  The K step is the forward grouped GEMM's
+// 256 x 256 one: 8 waves as 2 (M) x 4 (N) of 128 x 64, eight 16-row subtiles
+// streamed from LDS while the wave's four B fragments stay in registers, two
+// 66 KB stages, and one barrier per step before its last subtile that both
+// frees the stage just read and publishes the next.  The per-row scales of
+// both operands are E8M0 exponents the block-scaled MFMA applies.  Waves 0-3
+// issue all DMA (their own share and that of wave + 4); the next tile's first
+// step is issued before the epilogue stores, and the waits that follow count
+// those stores instead of draining them.
+// With fp32 scales the factor sA[m] * sB[n] of every partial costs eight VALU
+// operations per MFMA (four column scales per lane), as long as the MFMA
+// itself; at this tile size the registers for them do not fit next to the
+// accumulators without spilling, and the 128 x 256 kernel above (the same
+// speed then, measured) takes those products.
+struct WideWgradSmem {
+    static constexpr int A_BYTES = 256 * WBK;
+    static constexpr int B_BYTES = 256 * WBK;
+    static constexpr int SA_BYTES = 256 * 4;
+    static constexpr int SB_BYTES = 256 * 4;
+    static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+    static constexpr int TAB = 2 * STAGE;  // experts with rows: count, packed id|nkb, lo
+    static constexpr int TOTAL = TAB + (1 + 2 * WMAXL) * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS");
+};
+
+__global__ __launch_bounds__(WTHREADS, 1) void wgrad_wide_kernel(WgradArgs g) {
+    using SM = WideWgradSmem;
+    constexpr int MI = 8, NI = 4;  // 16 x 16 subtiles of a wave's 128 x 64
+    constexpr int NST = 2 * MI;    // 16-byte stores per wave per tile
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
+    int* const tab = reinterpret_cast<int*>(smem + SM::TAB);
+    int* const tab_x = tab + 1;           // e | nkb << 10
+    int* const tab_lo = tab + 1 + WMAXL;  // first row of the segment
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int64_t rcap = g.row_cap;
+    const int M = g.M, N = g.N;
+    const int MT = M / 256, NT = N / 256, TPE = MT * NT;
+    const int G = gridDim.x;
+    const int lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+
+    // experts with at least one token block, in order
+    if (wave == 0) {
+        int cnt = 0;
+        for (int c = 0; c < g.L; c += 64) {
+            const int e = c + lane;
+            int64_t lo = 0, hi = 0;
+            if (e < g.L) {
+                lo = g.offsets[e];
+                hi = g.offsets[e + 1];
+                lo = lo < 0 ? 0 : (lo > rcap ? rcap : lo);
+                hi = hi > rcap ? rcap : hi;
+            }
+            const int nkb = hi > lo ? (int)((hi - lo) / WBK) : 0;
+            const uint64_t m = __ballot(nkb > 0);
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (nkb > 0) {
+                tab_x[cnt + below] = e | (nkb << 10);
+                tab_lo[cnt + below] = (int)lo;
+            }
+            cnt += __popcll(m);
+        }
+        if (lane == 0) tab[0] = cnt;
+    }
+    __syncthreads();
+    const int Lne = __builtin_amdgcn_readfirstlane(tab[0]);
+
+    // tile order (j, s, f) as in wgrad_fp8_kernel: the fast index runs over
+    // the smaller operand's tiles
+    struct Pos {
+        int j, s, f;
+    };
+    const bool nfast = g.nfast != 0;
+    const int FT = nfast ? NT : MT, ST = nfast ? MT : NT;
+    const int Gj = G / TPE, Gr = G - Gj * TPE, Gs = Gr / FT, Gf = Gr - Gs * FT;
+    auto step_pos = [&](Pos& p) {
+        p.f += Gf;
+        int c = p.f >= FT ? 1 : 0;
+        p.f -= c * FT;
+        p.s += Gs + c;
+        c = p.s >= ST ? 1 : 0;
+        p.s -= c * ST;
+        p.j += Gj + c;
+    };
+    Pos cp;
+    cp.j = lb / TPE;
+    cp.s = (lb - cp.j * TPE) / FT;
+    cp.f = lb - cp.j * TPE - cp.s * FT;
+
+    // fragment reads (stage-relative): lane l holds row l & 15 of a 16-row
+    // fragment, K chunks c0 and c0 + 4 (c0 = l >> 4) of the 128-byte block,
+    // stored at chunk c ^ (row & 7)
+    const int l15 = lane & 15, l7 = lane & 7, c0 = lane >> 4;
+    const uint32_t a_rd0 = (wm * 128 + l15) * 128 + ((c0 ^ l7) << 4);
+    const uint32_t a_rd1 = (wm * 128 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    const uint32_t b_rd0 = SM::A_BYTES + (wn * 64 + l15) * 128 + ((c0 ^ l7) << 4);
+    const uint32_t b_rd1 = SM::A_BYTES + (wn * 64 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    // scales: the A row and the B row whose K chunk the lane holds, rows
+    // wm*128 + mi*16 + l15 and wn*64 + ni*16 + l15 (64 bytes apart per subtile)
+    const uint32_t sa_rd = SM::A_BYTES + SM::B_BYTES + (wm * 128 + l15) * 4;
+    const uint32_t sb_rd = SM::A_BYTES + SM::B_BYTES + SM::SA_BYTES + (wn * 64 + l15) * 4;
+
+    // DMA: a 1 KB segment is 8 rows of one token block; lane l moves chunk
+    // (l & 7) ^ (l >> 3) of row l >> 3 to LDS byte l * 16 (the swizzle above).
+    // The lane offsets are formed where a step is issued (not held in
+    // registers across the K loop).
+    auto seg_off_of = [&]() {
+        const uint32_t l = (uint32_t)__lane_id();
+        return ((l >> 3) * WBK) | ((((l & 7) ^ (l >> 3))) << 4);
+    };
+    // epilogue: byte offset in the tile of this lane's 16 bytes of row
+    // wm*128 + l15 after the regrouping (columns wn*64 + 8*c0 .. +7; the
+    // lane's other 16 bytes are 64 further, each 16-row subtile 16*N*2)
+    const uint32_t o_lane0 = (uint32_t)(((wm * 128 + l15) * N + wn * 64 + 8 * c0) * 2);
+
+    struct Src {
+        const uint8_t* a;  // the tile's first A row, first token block of the segment
+        const uint8_t* b;
+        const float* sa;
+        const float* sb;
+        int nkb;
+        int rot;  // first token block of the K loop
+    };
+    // The tiles an XCD runs side by side share one tile of the larger operand;
+    // each starts its K loop at a different token block (its fast index
+    // modulo the block count), so that they do not all request the same
+    // lines of the shared tile at once (queueing on the same L2 channels).
+    // Only the order of the fp32 block sums changes.
+    auto src_of = [&](const Pos& p) {
+        const int nt = nfast ? p.f : p.s, mt = nfast ? p.s : p.f;
+        const int x = __builtin_amdgcn_readfirstlane(tab_x[p.j]);
+        const int64_t blk0 = __builtin_amdgcn_readfirstlane(tab_lo[p.j]) / WBK;
+        Src s;
+        s.a = g.aT + (blk0 * M + (int64_t)mt * 256) * WBK;
+        s.b = g.bT + (blk0 * N + (int64_t)nt * 256) * WBK;
+        s.sa = g.aT_s + blk0 * M + (int64_t)mt * 256;
+        s.sb = g.bT_s + blk0 * N + (int64_t)nt * 256;
+        s.nkb = x >> 10;
+        s.rot = p.f % s.nkb;
+        return s;
+    };
+    auto dst_of = [&](const Pos& p) -> uint16_t* {
+        const int nt = nfast ? p.f : p.s, mt = nfast ? p.s : p.f;
+        const int e = __builtin_amdgcn_readfirstlane(tab_x[p.j]) & 1023;
+        return g.dW + (int64_t)e * M * N + (int64_t)mt * 256 * N + (int64_t)nt * 256;
+    };
+
+    const bool dma_wave = wave < 4;
+    // step kb of a tile into the stage at LDS address sA
+    auto issue = [&](uint32_t sA, int kb, const Src& sr) {
+        if (!dma_wave) return;
+        const uint32_t sB = sA + SM::A_BYTES;
+        kb += sr.rot;
+        if (kb >= sr.nkb) kb -= sr.nkb;
+        const uint8_t* a = sr.a + (int64_t)kb * M * WBK;
+        const uint8_t* b = sr.b + (int64_t)kb * N * WBK;
+        const uint32_t seg_off = seg_off_of();
+        const uint32_t s16_off = (uint32_t)__lane_id() * 16;
+        static_for<0, 2>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const int w = wave + 4 * h;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dma16s(a + (w * 32 + 8 * i) * WBK, seg_off, sA + (w * 4 + i) * 1024);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dma16s(b + (w * 32 + 8 * i) * WBK, seg_off, sB + (w * 4 + i) * 1024);
+        });
+        if (wave == 0) dma16s(sr.sa + (int64_t)kb * M, s16_off, sB + SM::B_BYTES);
+        if (wave == 1) dma16s(sr.sb + (int64_t)kb * N, s16_off, sB + SM::B_BYTES + SM::SA_BYTES);
+    };
+    auto lds_barrier = [&]() {
+        wait_lgkm0();
+        phase_barrier();
+    };
+
+    const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+    v4f acc[MI][NI];
+    v8i bfr[NI];
+    int eb[NI];        // E8M0 exponents of the lane's B rows
+    v8i afc;           // the current subtile's A fragment ...
+    uint32_t sac;      // ... and the A scale of its row (bits), read one subtile ahead
+    auto read_b = [&](auto nc, uint32_t pb0, uint32_t pb1) {
+        constexpr int ni = decltype(nc)::value;
+        bfr[ni] = join8(lds16<ni * 2048>(pb0), lds16<ni * 2048>(pb1));
+    };
+    auto read_a = [&](auto mc, uint32_t pa0, uint32_t pa1) {
+        constexpr int mi = decltype(mc)::value;
+        return join8(lds16<mi * 2048>(pa0), lds16<mi * 2048>(pa1));
+    };
+    auto read_sa = [&](auto mc, uint32_t psa) {
+        constexpr int mi = decltype(mc)::value;
+        return lds4<mi * 64>(psa);
+    };
+    // positive powers of two: the E8M0 code is the fp32 exponent field
+    auto read_sb = [&](uint32_t psb) {
+        static_for<0, NI>([&](auto nc) {
+            constexpr int ni = decltype(nc)::value;
+            eb[ni] = (int)(lds4<ni * 64>(psb) >> 23);
+        });
+    };
+    // every operand of a step, from the stage at LDS address sX
+    auto read_step = [&](uint32_t sX) {
+        pin_s(sX);
+        uint32_t pb0 = sX + b_rd0, pb1 = sX + b_rd1, psa = sX + sa_rd, psb = sX + sb_rd;
+        uint32_t pa0 = sX + a_rd0, pa1 = sX + a_rd1;
+        pin(pb0); pin(pb1); pin(psa); pin(psb); pin(pa0); pin(pa1);
+        static_for<0, NI>([&](auto nc) { read_b(nc, pb0, pb1); });
+        read_sb(psb);
+        afc = read_a(std::integral_constant<int, 0>{}, pa0, pa1);
+        sac = read_sa(std::integral_constant<int, 0>{}, psa);
+    };
+    // four MFMAs of subtile mi, the scales applied by the matrix core
+    auto subtile = [&](auto mc, const v8i& af, uint32_t sab) {
+        const int ea = (int)(sab >> 23);
+        static_for<0, NI>([&](auto nc) {
+            constexpr int ni = decltype(nc)::value;
+            acc[decltype(mc)::value][ni] = mfma16x16x128_e8m0(bfr[ni], af, acc[decltype(mc)::value][ni], eb[ni], ea);
+        });
+    };
+
+    // stores issued after the DMA of the step the next wait is for (the
+    // previous tile's epilogue), so that the wait does not drain them
+    bool stores_out = false;
+    Src cs{};
+    bool have = cp.j < Lne;
+    if (have) {
+        cs = src_of(cp);
+        issue(sbase, 0, cs);
+    }
+    while (have) {
+        const int nkb = cs.nkb;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = zero4;
+
+        // one K step from stage st; see gemm_wide_kernel for the schedule
+        auto kstep = [&](auto st_c, int kb) {
+            constexpr int st = decltype(st_c)::value;
+            uint32_t sA = sbase + (uint32_t)(st * SM::STAGE);
+            uint32_t sN = sbase + (uint32_t)((st ^ 1) * SM::STAGE);
+            pin_s(sA);
+            pin_s(sN);
+            {
+                uint32_t pa0 = sA + a_rd0, pa1 = sA + a_rd1, psa = sA + sa_rd;
+                pin(pa0); pin(pa1); pin(psa);
+                static_for<0, MI - 1>([&](auto mc) {
+                    constexpr int mi = decltype(mc)::value;
+                    const v8i afn = read_a(std::integral_constant<int, mi + 1>{}, pa0, pa1);
+                    const uint32_t san = read_sa(std::integral_constant<int, mi + 1>{}, psa);
+                    subtile(mc, afc, sac);
+                    __builtin_amdgcn_sched_barrier(0);
+                    afc = afn;
+                    sac = san;
+                });
+            }
+            // step kb + 1 has landed (the stores of the previous tile's
+            // epilogue, a step older, with it)
+            wait_vmcnt<0>();
+            lds_barrier();
+            if (kb + 2 < nkb) issue(sA, kb + 2, cs);
+            {
+                uint32_t pb0 = sN + b_rd0, pb1 = sN + b_rd1;
+                pin(pb0); pin(pb1);
+                constexpr int mi = MI - 1;
+                const int ea = (int)(sac >> 23);
+                static_for<0, NI>([&](auto nc) {
+                    constexpr int ni = decltype(nc)::value;
+                    acc[mi][ni] = mfma16x16x128_e8m0(bfr[ni], afc, acc[mi][ni], eb[ni], ea);
+                    read_b(nc, pb0, pb1);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                // the next step's scales and first A fragment (unused values
+                // after a tile's last step)
+                uint32_t psa = sN + sa_rd, psb = sN + sb_rd, pa0 = sN + a_rd0, pa1 = sN + a_rd1;
+                pin(psa); pin(psb); pin(pa0); pin(pa1);
+                read_sb(psb);
+                afc = read_a(std::integral_constant<int, 0>{}, pa0, pa1);
+                sac = read_sa(std::integral_constant<int, 0>{}, psa);
+            }
+        };
+
+        // stage 0 (step 0) has landed: step 1 goes out, step 0's operands are
+        // read.  The previous tile's stores, issued after step 0's DMA, may
+        // stay in flight (a wave that issues no DMA has only those).
+        if (stores_out) wait_vmcnt<NST>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (nkb > 1) issue(sbase + SM::STAGE, 1, cs);
+        read_step(sbase);
+        for (int kb0 = 0; kb0 < nkb; kb0 += 2) {
+            kstep(std::integral_constant<int, 0>{}, kb0);
+            if (kb0 + 1 < nkb) kstep(std::integral_constant<int, 1>{}, kb0 + 1);
+        }
+        // the next tile's first step goes out now and overlaps the epilogue
+        uint16_t* dst = dst_of(cp);
+        step_pos(cp);
+        have = cp.j < Lne;
+        if (have) {
+            cs = src_of(cp);
+            issue(sbase, 0, cs);
+        }
+        // bf16 from the accumulators; two cross-lane swaps per pair of
+        // n-subtiles give each lane 8 consecutive columns (one 16-byte store)
+        uint8_t* d = reinterpret_cast<uint8_t*>(dst);
+        uint32_t o_lane = o_lane0;  // 32-bit lane offset; the row block is a uniform base
+        pin(o_lane);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            uint8_t* drow = d + (int64_t)mi * 16 * N * 2;
+            uint32_t x[NI], y[NI];
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const v4f a = acc[mi][ni];
+                x[ni] = cvt_bf16x2(a.x, a.y);
+                y[ni] = cvt_bf16x2(a.z, a.w);
+            }
+#pragma unroll
+            for (int ni = 0; ni < NI; ni += 2) {
+                swap32(x[ni], x[ni + 1]);
+                swap32(y[ni], y[ni + 1]);
+                swap16(x[ni], x[ni + 1]);
+                swap16(y[ni], y[ni + 1]);
+            }
+#pragma unroll
+            for (int h = 0; h < NI / 2; ++h)
+                *reinterpret_cast<u32x4*>(drow + o_lane + 64 * h) = u32x4{x[2 * h], y[2 * h], x[2 * h + 1], y[2 * h + 1]};
+        }
+        stores_out = true;
+    }
+
+    // experts without rows: dW = 0
+    {
+        const int64_t chunks = (int64_t)M * N / 8;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        int j = 0;
+        for (int e = 0; e < g.L; ++e) {
+            if (j < Lne && (__builtin_amdgcn_readfirstlane(tab_x[j]) & 1023) == e) {
+                ++j;
+                continue;
+            }
+            uint16_t* dz = g.dW + (int64_t)e * M * N;
+            for (int64_t c = (int64_t)blockIdx.x * WTHREADS + tid; c < chunks; c += (int64_t)G * WTHREADS)
+                *reinterpret_cast<u32x4*>(dz + c * 8) = z;
+        }
+    }
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -518,8 +884,9 @@ using namespace moe;
 extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8_t* bT,
                                           const float* bT_s, const int32_t* offsets, int32_t L, int64_t row_cap,
                                           int32_t M, int32_t N, uint16_t* dW, int32_t flags, hipStream_t stream) {
-    MOE_REQUIRE(flags == 0 || flags == MOE_SCALE_POW2, MOE_ERR_UNSUPPORTED, "grouped_gemm_wgrad: unknown flags 0x%x",
-                flags);
+    MOE_REQUIRE((flags & ~(MOE_SCALE_POW2 | MOE_GEMM_TILE128)) == 0, MOE_ERR_UNSUPPORTED,
+                "grouped_gemm_wgrad: unknown flags 0x%x", flags);
+    const bool p2 = (flags & MOE_SCALE_POW2) != 0;
     MOE_REQUIRE(L >= 1 && L <= WMAXL, MOE_ERR_SHAPE, "grouped_gemm_wgrad: L=%d outside [1, %d]", L, WMAXL);
     // segment starts are kept as 32-bit values on the device
     MOE_REQUIRE(row_cap >= 0 && row_cap % WBK == 0 && row_cap < ((int64_t)1 << 31), MOE_ERR_SHAPE,
@@ -532,10 +899,12 @@ extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, 
     WgradArgs a{aT, aT_s, bT, bT_s, offsets, L, row_cap, M, N, N < M ? 1 : 0, dW};
     const int grid = (num_cus() + 7) / 8 * 8;  // persistent, one block per CU
     auto go = [&](auto kern) { kern<<<dim3(grid), dim3(WTHREADS), 0, stream>>>(a); };
-    if (N % 256 == 0)
-        flags ? go(wgrad_fp8_kernel<256, true>) : go(wgrad_fp8_kernel<256, false>);
+    if (p2 && M % 256 == 0 && N % 256 == 0 && !(flags & MOE_GEMM_TILE128))
+        go(wgrad_wide_kernel);
+    else if (N % 256 == 0)
+        p2 ? go(wgrad_fp8_kernel<256, true>) : go(wgrad_fp8_kernel<256, false>);
     else
-        flags ? go(wgrad_fp8_kernel<128, true>) : go(wgrad_fp8_kernel<128, false>);
+        p2 ? go(wgrad_fp8_kernel<128, true>) : go(wgrad_fp8_kernel<128, false>);
     MOE_LAUNCH_CHECK("wgrad_fp8_kernel");
     return MOE_OK;
 }

@@ -345,13 +345,14 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     return res
 
 
-def grouped_gemm_wgrad(aT, aT_s, bT, bT_s, offsets, L, rcap, out=None, pow2=False):
+def grouped_gemm_wgrad(aT, aT_s, bT, bT_s, offsets, L, rcap, out=None, pow2=False, tile128=False):
     """dW [L, M, N] bf16 from the 128x1-quantised block-transposed operands
-    aT [rcap/128, M, 128], bT [rcap/128, N, 128]."""
+    aT [rcap/128, M, 128], bT [rcap/128, N, 128].  tile128: 128 x 256 tiles
+    instead of 256 x 256 ones where M and N allow the latter."""
     M, N = aT.shape[1], bT.shape[1]
     dW = torch.empty((L, M, N), dtype=torch.bfloat16, device=_dev(aT)) if out is None else out
     _call("moe_grouped_gemm_fp8_wgrad", _p(aT), _p(aT_s), _p(bT), _p(bT_s), _p(offsets), L, rcap, M, N, _p(dW),
-          _flag(pow2), _stream(aT.device))
+          _flag(pow2) | (GEMM_TILE128 if tile128 else 0), _stream(aT.device))
     return dW
 
 
