@@ -58,6 +58,7 @@ struct WgradArgs {
     int M;
     int N;
     int nfast;  // 1: n-tiles vary fastest in the tile order (B is the smaller operand)
+    int gf;     // fast-index tiles per group (divides that index's tile count)
     uint16_t* dW;
 };
 
@@ -180,17 +181,26 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
 
     // A tile is (j, s, f): the j-th expert with rows, then a slow and a fast
     // tile index.  The fast index runs over the smaller operand's tiles
-    // (m-tiles when M <= N, else n-tiles): the tiles one XCD runs side by side
-    // then share one tile of the larger operand and sweep the smaller one,
-    // which stays in that XCD's L2 from one round of tiles to the next.
+    // (m-tiles when M <= N, else n-tiles), in groups of gf tiles, and the slow
+    // index over the larger operand's tiles within a group: the 32 tiles one
+    // XCD runs side by side cover a block of gf x 32/gf tiles, whose operand
+    // tiles (about 1.2 MB at the training shape) stay in that XCD's L2 next
+    // to the tiles' output stream.
     // Workgroup lb takes tiles lb, lb + G, ...; the step G is split into
     // carries so that no division runs per tile.
     struct Pos {
         int j, s, f;
     };
     const bool nfast = g.nfast != 0;
-    const int FT = nfast ? NT : MT, ST = nfast ? MT : NT;
+    const int ST0 = nfast ? MT : NT;
+    const int FT = g.gf, ST = ((nfast ? NT : MT) / FT) * ST0;
     const int Gj = G / TPE, Gr = G - Gj * TPE, Gs = Gr / FT, Gf = Gr - Gs * FT;
+    // (s, f) -> tile: s = group * ST0 + slow tile, fast tile = group * FT + f
+    auto tile_of = [&](const Pos& p, int& mt, int& nt) {
+        const int grp = p.s / ST0, sl = p.s - grp * ST0, fa = grp * FT + p.f;
+        nt = nfast ? fa : sl;
+        mt = nfast ? sl : fa;
+    };
     auto step_pos = [&](Pos& p) {
         p.f += Gf;
         int c = p.f >= FT ? 1 : 0;
@@ -220,7 +230,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         const float* sb;   // this wave's B scales, first token block
     };
     auto src_of = [&](const Pos& p) {
-        const int nt = nfast ? p.f : p.s, mt = nfast ? p.s : p.f;
+        int mt, nt;
+        tile_of(p, mt, nt);
         const int64_t lo = __builtin_amdgcn_readfirstlane(tab_lo[p.j]);
         Src s;
         s.a = g.aT + ((lo / WBK) * M + (int64_t)mt * WBM + wave * ASEG * 8) * WBK;
@@ -231,7 +242,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     };
     auto dst_of = [&](const Pos& p) -> uint16_t* {
         const int e = __builtin_amdgcn_readfirstlane(tab_x[p.j]) & 1023;
-        const int nt = nfast ? p.f : p.s, mt = nfast ? p.s : p.f;
+        int mt, nt;
+        tile_of(p, mt, nt);
         return g.dW + (int64_t)e * M * N + (int64_t)mt * WBM * N + (int64_t)nt * BN;
     };
 
@@ -603,8 +615,15 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_wide_kernel(WgradArgs g) {
         int j, s, f;
     };
     const bool nfast = g.nfast != 0;
-    const int FT = nfast ? NT : MT, ST = nfast ? MT : NT;
+    const int ST0 = nfast ? MT : NT;
+    const int FT = g.gf, ST = ((nfast ? NT : MT) / FT) * ST0;
     const int Gj = G / TPE, Gr = G - Gj * TPE, Gs = Gr / FT, Gf = Gr - Gs * FT;
+    // (s, f) -> tile: s = group * ST0 + slow tile, fast tile = group * FT + f
+    auto tile_of = [&](const Pos& p, int& mt, int& nt) {
+        const int grp = p.s / ST0, sl = p.s - grp * ST0, fa = grp * FT + p.f;
+        nt = nfast ? fa : sl;
+        mt = nfast ? sl : fa;
+    };
     auto step_pos = [&](Pos& p) {
         p.f += Gf;
         int c = p.f >= FT ? 1 : 0;
@@ -659,7 +678,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_wide_kernel(WgradArgs g) {
     // lines of the shared tile at once (queueing on the same L2 channels).
     // Only the order of the fp32 block sums changes.
     auto src_of = [&](const Pos& p) {
-        const int nt = nfast ? p.f : p.s, mt = nfast ? p.s : p.f;
+        int mt, nt;
+        tile_of(p, mt, nt);
         const int x = __builtin_amdgcn_readfirstlane(tab_x[p.j]);
         const int64_t blk0 = __builtin_amdgcn_readfirstlane(tab_lo[p.j]) / WBK;
         Src s;
@@ -672,7 +692,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_wide_kernel(WgradArgs g) {
         return s;
     };
     auto dst_of = [&](const Pos& p) -> uint16_t* {
-        const int nt = nfast ? p.f : p.s, mt = nfast ? p.s : p.f;
+        int mt, nt;
+        tile_of(p, mt, nt);
         const int e = __builtin_amdgcn_readfirstlane(tab_x[p.j]) & 1023;
         return g.dW + (int64_t)e * M * N + (int64_t)mt * 256 * N + (int64_t)nt * 256;
     };
@@ -896,10 +917,18 @@ extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, 
     MOE_REQUIRE((int64_t)L * (M / WBM) * (N / 128) < ((int64_t)1 << 31), MOE_ERR_SHAPE,
                 "grouped_gemm_wgrad: too many tiles");
     MOE_REQUIRE(aT && aT_s && bT && bT_s && offsets && dW, MOE_ERR_NULL, "grouped_gemm_wgrad: NULL argument");
-    WgradArgs a{aT, aT_s, bT, bT_s, offsets, L, row_cap, M, N, N < M ? 1 : 0, dW};
+    const bool wide = p2 && M % 256 == 0 && N % 256 == 0 && !(flags & MOE_GEMM_TILE128);
+    const int BMt = wide ? 256 : WBM, BNt = (wide || N % 256 == 0) ? 256 : 128;
+    const int nfast = N < M ? 1 : 0;
+    // The fast index runs in groups of 8 tiles when its count allows: the 32
+    // tiles an XCD runs side by side then cover 8 x 4 tiles, so they read 8
+    // tiles of one operand and 4 of the other instead of all of one.
+    const int ft = nfast ? N / BNt : M / BMt;
+    const int gf = (ft > 8 && ft % 8 == 0) ? 8 : ft;
+    WgradArgs a{aT, aT_s, bT, bT_s, offsets, L, row_cap, M, N, nfast, gf, dW};
     const int grid = (num_cus() + 7) / 8 * 8;  // persistent, one block per CU
     auto go = [&](auto kern) { kern<<<dim3(grid), dim3(WTHREADS), 0, stream>>>(a); };
-    if (p2 && M % 256 == 0 && N % 256 == 0 && !(flags & MOE_GEMM_TILE128))
+    if (wide)
         go(wgrad_wide_kernel);
     else if (N % 256 == 0)
         p2 ? go(wgrad_fp8_kernel<256, true>) : go(wgrad_fp8_kernel<256, false>);

@@ -5,7 +5,13 @@
   python -m moe_expert_layer_r3_amd.prof_summary counters <results.db> [scale]
       per-kernel average of each collected counter per dispatch (the rocprofv3
       FETCH_SIZE / WRITE_SIZE unit is KiB); `scale` multiplies the values (the
-      calibration factor from a plain copy of known size)."""
+      calibration factor from a plain copy of known size)
+  python -m moe_expert_layer_r3_amd.prof_summary split <results.db> <name-part> <n> [count]
+      launches of the kernels whose name contains <name-part>, in dispatch
+      order (the first `count` of them), grouped by position modulo n: for a
+      kernel launched n times per step with different shapes (the two weight
+      gradient products, say), the average duration of each launch of a step,
+      and of each collected counter when the database holds counters"""
 
 import sqlite3
 import sys
@@ -31,9 +37,43 @@ def counters(path, scale=1.0):
         print(f"{ctr:12s} {n:3d} {a:14.1f} {a * scale:14.1f}  {name}")
 
 
+def split(path, part, n, count=None):
+    db = sqlite3.connect(path)
+    tables = {r[0] for r in db.execute("select name from sqlite_master where type in ('table', 'view')")}
+    if "kernels" in tables:
+        rows = db.execute("select name, duration from kernels where name like ? order by start",
+                          (f"%{part}%",)).fetchall()
+        rows = rows[:count] if count else rows
+        print(f"{'pos':>3} {'n':>3} {'avg_ns':>12}  kernel")
+        for i in range(n):
+            sel = rows[i::n]
+            if sel:
+                avg = sum(d for _, d in sel) / len(sel)
+                print(f"{i:3d} {len(sel):3d} {avg:12.0f}  {sel[0][0][:100]}")
+    if "counters_collection" in tables:
+        rows = db.execute("select dispatch_id, counter_name, value, kernel_name from counters_collection "
+                          "where kernel_name like ? order by dispatch_id", (f"%{part}%",)).fetchall()
+        disp = {}
+        for d, c, v, k in rows:
+            e = disp.setdefault(d, {"kernel": k})
+            e[c] = e.get(c, 0.0) + v
+        ds = sorted(disp)
+        ds = ds[:count] if count else ds
+        print(f"{'pos':>3} {'n':>3} {'counter':14s} {'avg/dispatch':>14}  kernel")
+        for i in range(n):
+            sel = [disp[d] for d in ds[i::n]]
+            if not sel:
+                continue
+            for c in sorted(k for k in sel[0] if k != "kernel"):
+                avg = sum(e.get(c, 0.0) for e in sel) / len(sel)
+                print(f"{i:3d} {len(sel):3d} {c:14s} {avg:14.1f}  {sel[0]['kernel'][:80]}")
+
+
 if __name__ == "__main__":
     mode, path = sys.argv[1], sys.argv[2]
     if mode == "trace":
         trace(path)
+    elif mode == "split":
+        split(path, sys.argv[3], int(sys.argv[4]), int(sys.argv[5]) if len(sys.argv) > 5 else None)
     else:
         counters(path, float(sys.argv[3]) if len(sys.argv) > 3 else 1.0)
