@@ -131,22 +131,6 @@ def roofline_of(kernel, flops, nbytes, ms, workload):
     return r
 
 
-def code_sha256(paths):
-    """sha256 of the sources' code: comments and blank lines removed, each line
-    stripped, so that a comment edit does not orphan a profile while any
-    change to the code does."""
-    import hashlib
-    import re
-    h = hashlib.sha256()
-    for p in paths:
-        text = re.sub(r"/\*.*?\*/", "", open(p).read(), flags=re.S)
-        for line in text.splitlines():
-            line = re.sub(r"//.*", "", line).strip()
-            if line:
-                h.update(line.encode() + b"\n")
-    return h.hexdigest()
-
-
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of a kernel from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary (profiles/<kernel>_<workload>_traffic.json), or None when
@@ -156,6 +140,7 @@ def measured_traffic(kernel, workload):
         return None
     rec = json.load(open(path))
     src = os.path.join(HERE, "moe_expert_layer_r3_amd", "csrc")
+    from moe_expert_layer_r3_amd.prof_summary import code_sha256
     if code_sha256([os.path.join(src, f) for f in rec["sources"]]) != rec["code_sha256"]:
         return None
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]

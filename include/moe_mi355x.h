@@ -341,12 +341,47 @@ int moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, const int32
                          uint8_t* dyq, float* dyq_s, float* d_gate, int32_t flags,
                          hipStream_t stream);
 
+/* Combine backward on the expert-grouped rows ("RL at 1T scale", section "FP8
+ * Training": each backward GEMM operand quantised along its contraction axis):
+ * one pass over dy and y_perm gives, for every real row r of the grouped layout
+ * (pair p = row_pair[r] >= 0, token t = p / k, slot j = p % k):
+ *     dY[r, :] = fp32(w[p] * dy[t, :])
+ *       -> 1x128 e4m3:  dyq [row_cap, d] u8, dyq_s [d/128, row_cap] fp32
+ *                       (as moe_combine_backward; padding rows not written)
+ *       -> 128x1 e4m3 along rows, block-transposed: dyqT [row_cap/128, d, 128] u8,
+ *                       dyqT_s [row_cap/128, d] fp32 (as moe_quant_fp8_rows_t
+ *                       with w; padding rows count as 0)
+ *     gate_part [row_cap, MOE_GATE_PARTS] fp32: entry (r, g) is the fp32 partial
+ *       sum of dy[t, n] * y_perm[r, n] over the columns n of group g (groups of
+ *       whole 128-column chunks; how many depends on d only); written for real
+ *       rows and the groups d has, read back by moe_gate_backward_parts.
+ * Rows at and past offsets[L] are not touched.  dy [T, d] bf16, y_perm
+ * [row_cap, d] bf16 (the forward's expert outputs), w [T*k] fp32, row_pair
+ * [row_cap], offsets [L+1] as written by moe_permute; d % 128 == 0,
+ * row_cap % 128 == 0, row_cap * d and T * d below 2^31 (MOE_ERR_SHAPE).
+ * flags: 0, or MOE_SCALE_POW2 for power-of-two scales on both copies.        */
+#define MOE_GATE_PARTS 16
+int moe_combine_backward_rows(const uint16_t* dy, const uint16_t* y_perm, const float* w,
+                              const int32_t* row_pair, const int32_t* offsets, int64_t T,
+                              int32_t L, int64_t row_cap, int32_t k, int32_t d, uint8_t* dyq, float* dyq_s,
+                              uint8_t* dyqT, float* dyqT_s, float* gate_part, int32_t flags,
+                              hipStream_t stream);
+
 /* Backward of the softmax over the selected logits (complete when every expert
  * is local; under expert parallelism d_gate must first be summed over GPUs):
  *     d_logits[t, ids[t, j]] += w[t, j] * (d_gate[t, j] - sum_j' w[t, j'] d_gate[t, j'])
  * and 0 at unselected experts.  d_logits [T, E] fp32.                          */
 int moe_gate_backward(const float* d_gate, const float* w, const int32_t* ids, int64_t T,
                       int32_t k, int32_t E, float* d_logits, hipStream_t stream);
+
+/* The same from the partials of moe_combine_backward_rows: first
+ *     d_gate[t, j] = sum over the groups g of gate_part[pair_row[t, j], g]
+ * (summed in a fixed order; 0 for non-local slots), written to d_gate [T, k],
+ * then d_logits as moe_gate_backward.  d is the feature width the partials
+ * were taken over; pair_row [T, k] as written by moe_permute.                  */
+int moe_gate_backward_parts(const float* gate_part, const int32_t* pair_row, int64_t row_cap,
+                            int32_t d, const float* w, const int32_t* ids, int64_t T, int32_t k,
+                            int32_t E, float* d_gate, float* d_logits, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -182,6 +182,170 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
     }
 }
 
+
+// Combine backward on the expert-grouped rows, with both FP8 copies of dY.
+// Block (column group g, row block b of 128 rows), 512 threads; the group is
+// `cpb` 128-wide column chunks, taken one after the other.  Thread (wave wv,
+// lane l) owns rows 4*rq .. 4*rq + 3 of the block, rq = 4*wv + l/16, and
+// columns 8*cg .. 8*cg + 7 of the chunk, cg = l % 16.  Per chunk:
+//   * the 4 rows of dy it needs are gathered (row r holds pair row_pair[r],
+//     token row_pair[r] / k) and the 4 rows of y_perm read, all loads issued
+//     before any use; <dy_t, Y_r> over the chunk's 128 columns is added to the
+//     row's partial (fp32: 8-term chains, then the 16 lanes of the row);
+//   * dY = fp32(w * dy): a row's 1x128 tile is the 16 lanes of the row
+//     (maximum over 8 values, then over those lanes), stored as 8-byte words
+//     of one 128-byte run; padding rows are not written;
+//   * a column's 128x1 tile is the thread's 4 rows, the wave's 4 row quads
+//     (lanes 16 apart) and the 8 waves through LDS; its codes go through a
+//     transposed LDS tile to 16-byte stores of 128-byte columns (padding rows
+//     count as 0).
+// The row's partial over the group's columns is written to
+// gate_part[r * MOE_GATE_PARTS + g]; moe_gate_backward_parts sums the groups.
+constexpr int CBR_THREADS = 512;
+template <bool P2>
+__global__ __launch_bounds__(CBR_THREADS) void combine_bwd_rows_kernel(
+    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ y_perm, const float* __restrict__ w,
+    const int32_t* __restrict__ row_pair, const int32_t* __restrict__ offsets, int L, int64_t row_cap, int k, int d,
+    int cpb, uint8_t* __restrict__ dyq, float* __restrict__ dyq_s, uint8_t* __restrict__ dyqT,
+    float* __restrict__ dyqT_s, float* __restrict__ gate_part) {
+    __shared__ __attribute__((aligned(16))) float cmax[CBR_THREADS / 64][128];
+    __shared__ __attribute__((aligned(16))) float cinv[128];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_t[128][128 + 8];
+    const int64_t b = blockIdx.y;
+    const int grp = blockIdx.x;
+    int64_t total = offsets[L];
+    if (total > row_cap) total = row_cap;
+    if (b * 128 >= total) return;  // whole block leaves together
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = lane & 15, rq = wave * 4 + (lane >> 4);
+    const int c8 = cg * 8;
+    const int nchunk = d >> 7;
+    // element offsets fit 32 bits (checked on the host: T*d and row_cap*d < 2^31)
+    const uint32_t r0 = (uint32_t)b * 128 + rq * 4;  // the thread's first row
+    const int4 pa = *reinterpret_cast<const int4*>(row_pair + r0);
+    const int p[4] = {pa.x, pa.y, pa.z, pa.w};
+    float wp[4];
+    uint32_t tok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        wp[j] = p[j] >= 0 ? w[p[j]] : 0.f;
+        tok[j] = p[j] >= 0 ? (uint32_t)(p[j] / k) * (uint32_t)d : 0u;
+    }
+    const uint32_t row0 = r0 * (uint32_t)d;
+    float dot[4] = {0.f, 0.f, 0.f, 0.f};
+
+    const int cc_end = min(nchunk, (grp + 1) * cpb);
+#pragma unroll 1
+    for (int cc = grp * cpb; cc < cc_end; ++cc) {
+        const uint32_t col = (uint32_t)cc * 128 + c8;
+        uint4 rd[4], ry[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            rd[j] = make_uint4(0, 0, 0, 0);
+            ry[j] = make_uint4(0, 0, 0, 0);
+            if (p[j] >= 0) {
+                rd[j] = *reinterpret_cast<const uint4*>(dy + (tok[j] + col));
+                ry[j] = *reinterpret_cast<const uint4*>(y_perm + (row0 + (uint32_t)j * d + col));
+            }
+        }
+        float v[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j][0] = bf16_lo(rd[j].x); v[j][1] = bf16_hi(rd[j].x);
+            v[j][2] = bf16_lo(rd[j].y); v[j][3] = bf16_hi(rd[j].y);
+            v[j][4] = bf16_lo(rd[j].z); v[j][5] = bf16_hi(rd[j].z);
+            v[j][6] = bf16_lo(rd[j].w); v[j][7] = bf16_hi(rd[j].w);
+            float s = v[j][0] * bf16_lo(ry[j].x);
+            s = fmaf(v[j][1], bf16_hi(ry[j].x), s);
+            s = fmaf(v[j][2], bf16_lo(ry[j].y), s);
+            s = fmaf(v[j][3], bf16_hi(ry[j].y), s);
+            s = fmaf(v[j][4], bf16_lo(ry[j].z), s);
+            s = fmaf(v[j][5], bf16_hi(ry[j].z), s);
+            s = fmaf(v[j][6], bf16_lo(ry[j].w), s);
+            s = fmaf(v[j][7], bf16_hi(ry[j].w), s);
+            dot[j] += s;
+        }
+        // dY = fp32(w * dy); maxima of the rows (1x128) and of the columns (128x1)
+        float am[8], rm[4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            rm[j] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[j][i] = wp[j] * v[j][i];
+                const float a = fabsf(v[j][i]);
+                am[i] = fmaxf(am[i], a);
+                rm[j] = fmaxf(rm[j], a);
+            }
+        }
+        // 1x128 tiles of the thread's rows: lane cg computes the scale of row
+        // cg % 4 of its quad and the quad's lanes read the four back
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rm[j] = group_max<16>(rm[j]);
+        const TileScale ts_own = tile_scale_t<P2>(cg & 2 ? (cg & 1 ? rm[3] : rm[2]) : (cg & 1 ? rm[1] : rm[0]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float inv = __shfl(ts_own.inv, (lane & 48) + j);
+            if (p[j] >= 0) {
+                uint2 o;
+                o.x = cvt_e4m3x4(v[j][0] * inv, v[j][1] * inv, v[j][2] * inv, v[j][3] * inv);
+                o.y = cvt_e4m3x4(v[j][4] * inv, v[j][5] * inv, v[j][6] * inv, v[j][7] * inv);
+                *reinterpret_cast<uint2*>(dyq + (row0 + (uint32_t)j * d + col)) = o;
+            }
+        }
+        if (cg < 4 && p[cg & 3] >= 0) dyq_s[(uint32_t)cc * (uint32_t)row_cap + r0 + cg] = ts_own.s;  // K-block-major
+        // 128x1 tiles of the chunk's columns: maxima over the thread's rows, the
+        // wave's row quads and (through LDS) the waves; thread c < 128 forms
+        // column c's scale
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            am[i] = fmaxf(am[i], __shfl_xor(am[i], 16));
+            am[i] = fmaxf(am[i], __shfl_xor(am[i], 32));
+        }
+        if (lane < 16) {
+            *reinterpret_cast<float4*>(&cmax[wave][c8]) = make_float4(am[0], am[1], am[2], am[3]);
+            *reinterpret_cast<float4*>(&cmax[wave][c8 + 4]) = make_float4(am[4], am[5], am[6], am[7]);
+        }
+        __syncthreads();
+        if (tid < 128) {
+            float m = cmax[0][tid];
+#pragma unroll
+            for (int wv = 1; wv < CBR_THREADS / 64; ++wv) m = fmaxf(m, cmax[wv][tid]);
+            const TileScale ts = tile_scale_t<P2>(m);
+            cinv[tid] = ts.inv;
+            dyqT_s[(uint32_t)b * d + (uint32_t)cc * 128 + tid] = ts.s;  // token-block-major
+        }
+        __syncthreads();
+        const float4 i0 = *reinterpret_cast<const float4*>(&cinv[c8]);
+        const float4 i1 = *reinterpret_cast<const float4*>(&cinv[c8 + 4]);
+        const float ci[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<uint32_t*>(&tile_t[c8 + i][rq * 4]) =
+                cvt_e4m3x4(v[0][i] * ci[i], v[1][i] * ci[i], v[2][i] * ci[i], v[3][i] * ci[i]);
+        __syncthreads();
+        for (int idx = tid; idx < 128 * 8; idx += CBR_THREADS) {
+            const int c = idx >> 3, part = (idx & 7) * 16;
+            const uint4 val = *reinterpret_cast<const uint4*>(&tile_t[c][part]);
+            *reinterpret_cast<uint4*>(dyqT + ((((uint32_t)b * d + (uint32_t)cc * 128 + c) << 7) + part)) = val;
+        }
+    }
+    // the rows' partials over this group's columns; lane cg == j writes row j's
+    float own = 0.f;
+    bool real_own = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float s = group_sum<16>(dot[j]);
+        if (cg == j) {
+            own = s;
+            real_own = p[j] >= 0;
+        }
+    }
+    if (real_own) gate_part[(r0 + cg) * MOE_GATE_PARTS + grp] = own;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -213,5 +377,34 @@ extern "C" int moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, 
     };
     flags ? go(combine_bwd_kernel<true>) : go(combine_bwd_kernel<false>);
     MOE_LAUNCH_CHECK("combine_bwd_kernel");
+    return MOE_OK;
+}
+
+extern "C" int moe_combine_backward_rows(const uint16_t* dy, const uint16_t* y_perm, const float* w,
+                                         const int32_t* row_pair, const int32_t* offsets, int64_t T, int32_t L,
+                                         int64_t row_cap,
+                                         int32_t k, int32_t d, uint8_t* dyq, float* dyq_s, uint8_t* dyqT,
+                                         float* dyqT_s, float* gate_part, int32_t flags, hipStream_t stream) {
+    MOE_REQUIRE(flags == 0 || flags == MOE_SCALE_POW2, MOE_ERR_UNSUPPORTED,
+                "combine_backward_rows: unknown flags 0x%x", flags);
+    MOE_REQUIRE(L >= 1 && L <= 1024 && k >= 1 && k <= CMAXK, MOE_ERR_SHAPE, "combine_backward_rows: bad L/k");
+    MOE_REQUIRE(row_cap >= 0 && row_cap % 128 == 0 && row_cap <= 0x7FFFFFFF, MOE_ERR_SHAPE,
+                "combine_backward_rows: row_cap=%lld must be a multiple of 128", (long long)row_cap);
+    MOE_REQUIRE(d > 0 && d % 128 == 0, MOE_ERR_SHAPE, "combine_backward_rows: d=%d must be a multiple of 128", d);
+    if (row_cap == 0) return MOE_OK;
+    MOE_REQUIRE(dy && y_perm && w && row_pair && offsets && dyq && dyq_s && dyqT && dyqT_s && gate_part, MOE_ERR_NULL,
+                "combine_backward_rows: NULL argument");
+    MOE_REQUIRE(row_cap / 128 <= 65535, MOE_ERR_SHAPE, "combine_backward_rows: row_cap too large");
+    // 32-bit element offsets in the kernel: the dyqT byte offsets are the largest (row_cap * d)
+    MOE_REQUIRE(row_cap * d < ((int64_t)1 << 31) && T >= 0 && T * d < ((int64_t)1 << 31), MOE_ERR_SHAPE,
+                "combine_backward_rows: row_cap * d and T * d must stay below 2^31");
+    const int cpb = gate_chunks_per_group(d);
+    dim3 grid((unsigned)gate_groups(d), (unsigned)(row_cap / 128));
+    auto go = [&](auto kern) {
+        kern<<<grid, CBR_THREADS, 0, stream>>>(dy, y_perm, w, row_pair, offsets, L, row_cap, k, d, cpb, dyq, dyq_s, dyqT,
+                                       dyqT_s, gate_part);
+    };
+    flags ? go(combine_bwd_rows_kernel<true>) : go(combine_bwd_rows_kernel<false>);
+    MOE_LAUNCH_CHECK("combine_bwd_rows_kernel");
     return MOE_OK;
 }

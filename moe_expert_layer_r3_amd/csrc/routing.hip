@@ -211,23 +211,54 @@ __global__ __launch_bounds__(256) void replay_kernel(const int32_t* __restrict__
 // writes its elements of the row (64 consecutive floats per store), each the
 // sum of the contributions whose slot holds that id, in slot order (a
 // repeated id sums its slots).
-__global__ __launch_bounds__(256) void gate_backward_kernel(const float* __restrict__ d_gate,
+template <bool PARTS>
+__global__ __launch_bounds__(256) void gate_backward_kernel(const float* __restrict__ d_gate_in,
+                                                            const float* __restrict__ part,
+                                                            const int32_t* __restrict__ pair_row, int ngroups,
                                                             const float* __restrict__ w,
                                                             const int32_t* __restrict__ ids, int64_t T,
-                                                            int k, int E, float* __restrict__ d_logits) {
+                                                            int k, int E, float* __restrict__ d_gate_out,
+                                                            float* __restrict__ d_logits) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
+    float dg[MAXK];
+    if constexpr (PARTS) {
+        // four slots at a time: lanes 16q .. 16q + 15 sum the group partials
+        // of slot 4*it + q (a fixed butterfly order), read back uniformly
+#pragma unroll
+        for (int it = 0; it < MAXK / 4; ++it) {
+            if (4 * it < k) {
+                const int j = 4 * it + (lane >> 4), g = lane & 15;
+                float v = 0.f;
+                if (j < k && g < ngroups) {
+                    const int r = pair_row[t * k + j];
+                    if (r >= 0) v = part[(int64_t)r * MOE_GATE_PARTS + g];
+                }
+                v = group_sum<16>(v);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dg[4 * it + q] = __shfl(v, 16 * q);
+                const float mine = __shfl(v, 16 * (lane & 3));
+                if ((lane >> 2) == it && lane < k) d_gate_out[t * k + lane] = mine;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dg[4 * it + q] = 0.f;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < MAXK; ++j) dg[j] = j < k ? d_gate_in[t * k + j] : 0.f;
+    }
     float dot = 0.f;
 #pragma unroll
     for (int j = 0; j < MAXK; ++j)
-        if (j < k) dot += w[t * k + j] * d_gate[t * k + j];
+        if (j < k) dot += w[t * k + j] * dg[j];
     int id[MAXK];
     float c[MAXK];
 #pragma unroll
     for (int j = 0; j < MAXK; ++j) {
         id[j] = j < k ? ids[t * k + j] : -1;
-        c[j] = j < k ? w[t * k + j] * (d_gate[t * k + j] - dot) : 0.f;
+        c[j] = j < k ? w[t * k + j] * (dg[j] - dot) : 0.f;
     }
     float* out = d_logits + t * E;
     for (int e = lane; e < E; e += 64) {
@@ -335,7 +366,24 @@ extern "C" int moe_gate_backward(const float* d_gate, const float* w, const int3
                 "gate_backward: bad T/k/E");
     if (T == 0) return MOE_OK;
     MOE_REQUIRE(d_gate && w && ids && d_logits, MOE_ERR_NULL, "gate_backward: NULL argument");
-    gate_backward_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream>>>(d_gate, w, ids, T, k, E, d_logits);
+    gate_backward_kernel<false><<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream>>>(
+        d_gate, nullptr, nullptr, 0, w, ids, T, k, E, nullptr, d_logits);
+    MOE_LAUNCH_CHECK("gate_backward_kernel");
+    return MOE_OK;
+}
+
+extern "C" int moe_gate_backward_parts(const float* gate_part, const int32_t* pair_row, int64_t row_cap, int32_t d,
+                                       const float* w, const int32_t* ids, int64_t T, int32_t k, int32_t E,
+                                       float* d_gate, float* d_logits, hipStream_t stream) {
+    MOE_REQUIRE(T >= 0 && k >= 1 && k <= MAXK && E >= 1 && E <= 1024, MOE_ERR_SHAPE,
+                "gate_backward_parts: bad T/k/E");
+    MOE_REQUIRE(d > 0 && d % 128 == 0, MOE_ERR_SHAPE, "gate_backward_parts: d=%d must be a multiple of 128", d);
+    MOE_REQUIRE(row_cap >= 0, MOE_ERR_SHAPE, "gate_backward_parts: bad row_cap");
+    if (T == 0) return MOE_OK;
+    MOE_REQUIRE(pair_row && w && ids && d_gate && d_logits && (row_cap == 0 || gate_part), MOE_ERR_NULL,
+                "gate_backward_parts: NULL argument");
+    gate_backward_kernel<true><<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream>>>(
+        nullptr, gate_part, pair_row, gate_groups(d), w, ids, T, k, E, d_gate, d_logits);
     MOE_LAUNCH_CHECK("gate_backward_kernel");
     return MOE_OK;
 }

@@ -195,7 +195,7 @@ class TrainPlan(ForwardPlan):
 
     Backward ("RL at 1T scale", section "FP8 Training": every backward GEMM operand
     is block-quantised along that GEMM's contraction axis):
-      combine backward -> dY (1x128 FP8) and d_gate;  dY 128x1 (transposed)
+      combine backward -> dY 1x128 and 128x1 (transposed) FP8, gate partials
       dgrad GEMM through W2 (fp32 dH) -> SwiGLU backward -> [dG, dU] 1x128 and
       128x1, recomputed H 128x1;  dgrad GEMM through W13 -> dX -> unpermute-sum dx
       x 128x1 (transposed);  wgrad GEMMs dW2 = dY^T H, dW13 = [dG, dU]^T X
@@ -211,6 +211,7 @@ class TrainPlan(ForwardPlan):
         self.d_gate = torch.empty((T, k), dtype=f32, device=dv)
         self.dyqT = torch.empty((R // 128, d, 128), dtype=u8, device=dv)  # block-transposed
         self.dyqT_s = torch.empty((R // 128, d), dtype=f32, device=dv)  # token-block-major
+        self.gate_part = torch.empty((R, ops.GATE_PARTS), dtype=f32, device=dv)
         self.dH = torch.empty((R, f), dtype=f32, device=dv)
         self.sb = dict(dgu_q=torch.empty((R, 2 * f), dtype=u8, device=dv),
                        dgu_s=torch.empty((2 * f // 128, R), dtype=f32, device=dv),
@@ -227,14 +228,12 @@ class TrainPlan(ForwardPlan):
         self.d_logits = torch.empty((T, E), dtype=f32, device=dv)
 
     def combine_bwd(self, dy):
+        """dY = w * dy on the grouped rows, 1x128 and 128x1 (transposed), and the
+        gate partials, from one pass over dy and Y."""
         _check(dy, (self.T, self.d), torch.bfloat16, "dy")
-        _call("moe_combine_backward", _p(dy), _p(self.Y), _p(self.pair_row), _p(self.w), self.T, self.k, self.d,
-              self.rcap, _p(self.dyq), _p(self.dyq_s), _p(self.d_gate), self.sflag, _stream())
-
-    def dy_quant_t(self, dy):
-        _check(dy, (self.T, self.d), torch.bfloat16, "dy")
-        _call("moe_quant_fp8_rows_t", _p(dy), _p(self.w), _p(self.row_pair), _p(self.offsets), self.L, self.rcap,
-              self.k, self.d, _p(self.dyqT), _p(self.dyqT_s), self.sflag, _stream())
+        _call("moe_combine_backward_rows", _p(dy), _p(self.Y), _p(self.w), _p(self.row_pair), _p(self.offsets),
+              self.T, self.L, self.rcap, self.k, self.d, _p(self.dyq), _p(self.dyq_s), _p(self.dyqT), _p(self.dyqT_s),
+              _p(self.gate_part), self.sflag, _stream())
 
     def dgrad2(self, wts):
         _call("moe_grouped_gemm_fp8", _p(self.dyq), _p(self.dyq_s), _p(wts["w2qT"]), _p(wts["w2sT"]),
@@ -273,11 +272,11 @@ class TrainPlan(ForwardPlan):
               _stream())
 
     def gate_bwd(self):
-        _call("moe_gate_backward", _p(self.d_gate), _p(self.w), _p(self.ids), self.T, self.k, self.E,
-              _p(self.d_logits), _stream())
+        _call("moe_gate_backward_parts", _p(self.gate_part), _p(self.pair_row), self.rcap, self.d, _p(self.w),
+              _p(self.ids), self.T, self.k, self.E, _p(self.d_gate), _p(self.d_logits), _stream())
 
-    BWD_STAGES = ("combine_bwd", "dy_quant_t", "dgrad2", "swiglu_bwd", "dgrad1", "unpermute", "x_quant_t",
-              "wgrad2", "wgrad13", "gate_bwd")
+    BWD_STAGES = ("combine_bwd", "dgrad2", "swiglu_bwd", "dgrad1", "unpermute", "x_quant_t", "wgrad2", "wgrad13",
+                  "gate_bwd")
 
     def backward(self, x, dy, wts, events=None):
         """Backward of the last ``forward`` for upstream gradient dy [T, d] bf16;
@@ -290,7 +289,6 @@ class TrainPlan(ForwardPlan):
             else:
                 fn(*a)
         rec("combine_bwd", self.combine_bwd, dy)
-        rec("dy_quant_t", self.dy_quant_t, dy)
         rec("dgrad2", self.dgrad2, wts)
         rec("swiglu_bwd", self.swiglu_bwd)
         rec("dgrad1", self.dgrad1, wts)

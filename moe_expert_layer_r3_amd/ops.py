@@ -59,7 +59,12 @@ _SIGS = {
     "moe_unpermute_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I64, _P, _P]),
     "moe_combine_backward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _I64, _P, _P, _P, _I32, _P]),
     "moe_gate_backward": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_combine_backward_rows": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I32, _I64, _I32, _I32, _P, _P, _P, _P,
+                                                 _P, _I32, _P]),
+    "moe_gate_backward_parts": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _I64, _I32, _I32, _P, _P, _P]),
 }
+
+GATE_PARTS = 16  # MOE_GATE_PARTS
 
 
 def lib():
@@ -165,6 +170,17 @@ def gate_backward(d_gate, w, ids, E):
     out = torch.empty((T, E), dtype=torch.float32, device=_dev(ids))
     _call("moe_gate_backward", _p(d_gate), _p(w), _p(ids), T, k, E, _p(out), _stream(ids.device))
     return out
+
+
+def gate_backward_parts(gate_part, pair_row, rcap, d, w, ids, E):
+    """(d_gate [T, k], d_logits [T, E]) from the partials of combine_backward_rows."""
+    T, k = ids.shape
+    dev = _dev(ids)
+    d_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    out = torch.empty((T, E), dtype=torch.float32, device=dev)
+    _call("moe_gate_backward_parts", _p(gate_part), _p(pair_row), rcap, d, _p(w), _p(ids), T, k, E, _p(d_gate),
+          _p(out), _stream(dev))
+    return d_gate, out
 
 
 # ---------------------------------------------------------------- dispatch
@@ -392,6 +408,24 @@ def combine(y_perm, pair_row, w, rcap=None):
     y = torch.empty((T, d), dtype=torch.bfloat16, device=_dev(pair_row))
     _call("moe_unpermute_combine", _p(y_perm), _p(pair_row), _p(w), T, k, d, rcap, _p(y), _stream(y.device))
     return y
+
+
+def combine_backward_rows(dy, y_perm, w, row_pair, offsets, L, rcap, k, pow2=False):
+    """Both FP8 copies of dY = w * dy on the expert-grouped rows and the gate
+    partials: (dyq [rcap, d], dyq_s [d/128, rcap], dyqT [rcap/128, d, 128],
+    dyqT_s [rcap/128, d], gate_part [rcap, GATE_PARTS])."""
+    _contig(dy, torch.bfloat16, "dy")
+    d = dy.shape[1]
+    dev = _dev(dy)
+    dyq = torch.empty((rcap, d), dtype=torch.uint8, device=dev)
+    dys = torch.empty((d // 128, rcap), dtype=torch.float32, device=dev)
+    dyqT = torch.empty((rcap // 128, d, 128), dtype=torch.uint8, device=dev)
+    dyqT_s = torch.empty((rcap // 128, d), dtype=torch.float32, device=dev)
+    part = torch.empty((rcap, GATE_PARTS), dtype=torch.float32, device=dev)
+    _call("moe_combine_backward_rows", _p(dy), _p(y_perm), _p(w), _p(row_pair), _p(offsets), dy.shape[0], L, rcap, k,
+          d, _p(dyq),
+          _p(dys), _p(dyqT), _p(dyqT_s), _p(part), _flag(pow2), _stream(dev))
+    return dyq, dys, dyqT, dyqT_s, part
 
 
 def combine_backward(dy, y_perm, pair_row, w, rcap=None, quant=True, pow2=False):

@@ -11,10 +11,38 @@
       order (the first `count` of them), grouped by position modulo n: for a
       kernel launched n times per step with different shapes (the two weight
       gradient products, say), the average duration of each launch of a step,
-      and of each collected counter when the database holds counters"""
+      and of each collected counter when the database holds counters
+  python -m moe_expert_layer_r3_amd.prof_summary traffic <fetch.db> <write.db> <copy_fetch.db>
+          <copy_write.db> <name-part> <n> <pos> <key> <workload> <sources> <out.json>
+      HBM bytes per launch of one kernel (the launches at position <pos> modulo
+      <n> among those whose name contains <name-part>): FETCH_SIZE and
+      WRITE_SIZE per dispatch, each scaled so that a plain 1 GiB device copy
+      (the copy databases) reads as 1 GiB; written as JSON with the sha256 of
+      the kernel's sources (comma-separated names under csrc/), which bench.py
+      checks before it reports the figure"""
 
+import json
+import os
+import re
 import sqlite3
 import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def code_sha256(paths):
+    """sha256 of the sources' code: comments and blank lines removed, each line
+    stripped, so that a comment edit does not orphan a profile while any
+    change to the code does."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        text = re.sub(r"/\*.*?\*/", "", open(p).read(), flags=re.S)
+        for line in text.splitlines():
+            line = re.sub(r"//.*", "", line).strip()
+            if line:
+                h.update(line.encode() + b"\n")
+    return h.hexdigest()
 
 
 def trace(path):
@@ -69,9 +97,47 @@ def split(path, part, n, count=None):
                 print(f"{i:3d} {len(sel):3d} {c:14s} {avg:14.1f}  {sel[0]['kernel'][:80]}")
 
 
+def _per_dispatch(path, counter, part):
+    db = sqlite3.connect(path)
+    rows = db.execute("select dispatch_id, sum(value) from counters_collection where counter_name = ? and "
+                      "kernel_name like ? group by dispatch_id order by dispatch_id",
+                      (counter, f"%{part}%")).fetchall()
+    return [v for _, v in rows]
+
+
+def traffic(fetch_db, write_db, cfetch_db, cwrite_db, part, n, pos, key, workload, sources, out):
+    gib_kib = float(1 << 20)  # 1 GiB in the counters' KiB
+    cf = [v for v in _per_dispatch(cfetch_db, "FETCH_SIZE", "copyBuffer") if v > 0.25 * gib_kib]
+    cw = [v for v in _per_dispatch(cwrite_db, "WRITE_SIZE", "copyBuffer") if v > 0.25 * gib_kib]
+    if not cf or not cw:
+        raise SystemExit("no 1 GiB copy dispatch in the calibration databases")
+    fs, ws = gib_kib / (sum(cf) / len(cf)), gib_kib / (sum(cw) / len(cw))
+    f = _per_dispatch(fetch_db, "FETCH_SIZE", part)[pos::n]
+    w = _per_dispatch(write_db, "WRITE_SIZE", part)[pos::n]
+    srcs = sources.split(",")
+    rec = {
+        "kernel": key,
+        "workload": workload,
+        "match": f"launches {pos} mod {n} of kernels named like '{part}'",
+        "dispatches": [len(f), len(w)],
+        "sources": srcs,
+        "code_sha256": code_sha256([os.path.join(CSRC, x) for x in srcs]),
+        "fetch_bytes_per_launch": sum(f) / len(f) * fs * 1024.0,
+        "write_bytes_per_launch": sum(w) / len(w) * ws * 1024.0,
+        "fetch_scale": fs,
+        "write_scale": ws,
+    }
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 if __name__ == "__main__":
     mode, path = sys.argv[1], sys.argv[2]
-    if mode == "trace":
+    if mode == "traffic":
+        a = sys.argv[2:]
+        traffic(a[0], a[1], a[2], a[3], a[4], int(a[5]), int(a[6]), a[7], a[8], a[9], a[10])
+    elif mode == "trace":
         trace(path)
     elif mode == "split":
         split(path, sys.argv[3], int(sys.argv[4]), int(sys.argv[5]) if len(sys.argv) > 5 else None)

@@ -99,6 +99,54 @@ def test_combine_backward(pow2):
     assert np.all(g[~loc] == 0.0)
 
 
+@pytest.mark.parametrize("counts,k,d,pow2", [
+    ([0, 1, 130, 300, 128, 0, 77], 6, 512, False),     # one column group, ragged segments, empty experts
+    ([0, 1, 130, 300, 128, 0, 77], 6, 512, True),
+    ([255, 3, 129, 0, 600], 8, 2176, False),           # 17 chunks: 5 groups, the last one chunk wide
+    ([40, 0, 97], 2, 128, True),                        # one chunk
+])
+def test_combine_backward_rows(counts, k, d, pow2):
+    """dY = fp32(w * dy) on the grouped rows quantised 1x128 and 128x1 from one
+    pass, and d_gate / d_logits from its per-group partials."""
+    E, e0 = 40, 3
+    ids, res, rp, rng = _perm(counts, k, E, e0, seed=61 + d + k)
+    T, L = ids.shape[0], len(counts)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    rcap = res["row_cap"]
+    Y = obf16(rng.standard_normal((rcap, d)))
+    dy = _bf16_rows(rng, T, d)
+    dy[3, :] = 0.0
+    say(f"combine backward rows counts={counts} k={k} d={d} pow2={pow2}")
+    dyq, dys, dyqT, dyqT_s, part = ops.combine_backward_rows(bf16_tensor(dy), bf16_tensor(Y), gpu(w),
+                                                             res["row_pair"], res["offsets"], L, rcap, k,
+                                                             pow2=pow2)
+    d_gate, d_logits = ops.gate_backward_parts(part, res["pair_row"], rcap, d, gpu(w), gpu(ids), E)
+    n = int(npi(res["offsets"])[-1])
+    real = rp >= 0
+    rows = np.flatnonzero(real)
+    t, j = rp[real] // k, rp[real] % k
+    dY = of32(w[t, j][:, None].astype(np.float64) * dy[t])
+    rq, rs = OQ.quant_1x128(dY, pow2=pow2)
+    assert np.array_equal(npi(dyq)[rows], rq)
+    assert np.array_equal(npi(dys).T[rows].astype(np.float64), rs)
+    v = np.zeros((n, d))
+    v[real] = dY
+    tq, ts = OQ.quant_128x1_t(v, real, pow2=pow2)
+    assert np.array_equal(npi(ops.untile_t(dyqT))[:, :n], tq)
+    assert np.array_equal(npi(dyqT_s)[:n // 128].T.astype(np.float64), ts)
+    pr = npi(res["pair_row"])
+    loc = pr >= 0
+    prod = dy[np.nonzero(loc)[0]] * Y[pr[loc]]
+    g = np64(d_gate)
+    bound = 1e-6 * np.sum(np.abs(prod), axis=1) + 1e-30
+    assert np.all(np.abs(g[loc] - np.sum(prod, axis=1)) <= bound)
+    assert np.all(g[~loc] == 0.0)
+    dl = OR.gate_backward(g, w, ids, E)
+    gmax = np.max(np.abs(g), axis=1, keepdims=True)
+    assert np.all(np.abs(np64(d_logits) - dl) <= 1e-6 * gmax + 1e-30)
+
+
 # ------------------------------------------------------------------ SwiGLU backward
 
 def _swiglu_ref(dH, G, U):
