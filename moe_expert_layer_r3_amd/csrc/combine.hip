@@ -2,6 +2,7 @@
 // Expert Parallelism" and "Expert Parallel": per-layer combine after the
 // experts) and its backward.
 #include "common.hpp"
+#include "gate_parts.hpp"
 
 namespace moe {
 
@@ -190,7 +191,8 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
 // columns 8*cg .. 8*cg + 7 of the chunk, cg = l % 16.  Per chunk:
 //   * the 4 rows of dy it needs are gathered (row r holds pair row_pair[r],
 //     token row_pair[r] / k) and the 4 rows of y_perm read, all loads issued
-//     before any use; <dy_t, Y_r> over the chunk's 128 columns is added to the
+//     together and those of the next chunk issued before this chunk is
+//     quantised; <dy_t, Y_r> over the chunk's 128 columns is added to the
 //     row's partial (fp32: 8-term chains, then the 16 lanes of the row);
 //   * dY = fp32(w * dy): a row's 1x128 tile is the 16 lanes of the row
 //     (maximum over 8 values, then over those lanes), stored as 8-byte words
@@ -234,11 +236,10 @@ __global__ __launch_bounds__(CBR_THREADS) void combine_bwd_rows_kernel(
     const uint32_t row0 = r0 * (uint32_t)d;
     float dot[4] = {0.f, 0.f, 0.f, 0.f};
 
-    const int cc_end = min(nchunk, (grp + 1) * cpb);
-#pragma unroll 1
-    for (int cc = grp * cpb; cc < cc_end; ++cc) {
+    // the next chunk's rows are loaded while the current one is quantised
+    uint4 rd[4], ry[4];
+    auto load = [&](int cc) {
         const uint32_t col = (uint32_t)cc * 128 + c8;
-        uint4 rd[4], ry[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             rd[j] = make_uint4(0, 0, 0, 0);
@@ -248,6 +249,12 @@ __global__ __launch_bounds__(CBR_THREADS) void combine_bwd_rows_kernel(
                 ry[j] = *reinterpret_cast<const uint4*>(y_perm + (row0 + (uint32_t)j * d + col));
             }
         }
+    };
+    const int cc_end = min(nchunk, (grp + 1) * cpb);
+    load(grp * cpb);
+#pragma unroll 1
+    for (int cc = grp * cpb; cc < cc_end; ++cc) {
+        const uint32_t col = (uint32_t)cc * 128 + c8;
         float v[4][8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -265,6 +272,7 @@ __global__ __launch_bounds__(CBR_THREADS) void combine_bwd_rows_kernel(
             s = fmaf(v[j][7], bf16_hi(ry[j].w), s);
             dot[j] += s;
         }
+        if (cc + 1 < cc_end) load(cc + 1);
         // dY = fp32(w * dy); maxima of the rows (1x128) and of the columns (128x1)
         float am[8], rm[4];
 #pragma unroll

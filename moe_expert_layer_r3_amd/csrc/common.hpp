@@ -135,16 +135,4 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// Column groups of the gate-gradient partials (moe_combine_backward_rows):
-// groups of at least 4 chunks of 128 columns, at most MOE_GATE_PARTS groups
-__host__ __device__ inline int gate_chunks_per_group(int d) {
-    const int nchunk = d / 128;
-    const int c = (nchunk + MOE_GATE_PARTS - 1) / MOE_GATE_PARTS;
-    return c < 4 ? 4 : c;
-}
-__host__ __device__ inline int gate_groups(int d) {
-    const int c = gate_chunks_per_group(d);
-    return (d / 128 + c - 1) / c;
-}
-
 }  // namespace moe

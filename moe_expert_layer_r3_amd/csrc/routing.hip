@@ -5,6 +5,7 @@
 // payload [num_layers, top_k, seq_len] stays on the device and is consumed by
 // device kernels only.
 #include "common.hpp"
+#include "gate_parts.hpp"
 
 namespace moe {
 
