@@ -255,14 +255,15 @@ def train_leg(steps, warmup, dev, pow2=False, mxfp4=False, sets=2):
     dys = [synth.dy(wl, t0=i * wl.T).to(dev) for i in range(sets)]
     W13_d = synth.weights(wl, "w13").to(dev)
     W2_d = synth.weights(wl, "w2").to(dev)
-    wts = None if mxfp4 else weight_buffers(wl.L, wl.d, wl.f, dev, transpose=True)
-    wts = quantize_weights(W13_d, W2_d, transpose=True, out=wts, pow2=pow2, mxfp4=mxfp4)
     plan = TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, wl.e0, device=dev, pow2=pow2, mxfp4=mxfp4)
+    tw = plan.transpose_weights  # FP8: the dgrad products read the forward weights, no transposed copy
+    wts = None if mxfp4 else weight_buffers(wl.L, wl.d, wl.f, dev, transpose=tw)
+    wts = quantize_weights(W13_d, W2_d, transpose=tw, out=wts, pow2=pow2, mxfp4=mxfp4)
 
     def step(i, events=None):
         if events is not None:
             events["weight_quant"][0].record()
-        quantize_weights(W13_d, W2_d, transpose=True, out=wts, pow2=pow2, mxfp4=mxfp4)
+        quantize_weights(W13_d, W2_d, transpose=tw, out=wts, pow2=pow2, mxfp4=mxfp4)
         if events is not None:
             events["weight_quant"][1].record()
         plan.forward(xs[i % sets], lgs[i % sets], wts, events=events)

@@ -179,6 +179,14 @@ enum { MOE_WEIGHT_MXFP4 = 0x200 };
  * N % 256 != 0 the 128 x 128 tile is used either way).  The result is the same
  * up to the order of the fp32 block sums.                                     */
 enum { MOE_GEMM_TILE128 = 0x400 };
+/* OR'ed into moe_grouped_gemm_fp8's epilogue (STORE_BF16 or STORE_F32, FP8
+ * weights, N % 256 == 0, not with MOE_GEMM_TILE128): b is [L, K, N] with b_s
+ * [L, K/128, N/128], i.e. the product reads b[e, k, n] where it would read
+ * b[e, n, k].  This is how a dgrad product reads the forward weights [out, in]
+ * (K = out, N = in) and their moe_quant_fp8 scales without a transposed copy
+ * ("RL at 1T scale", section "FP8 Training": each GEMM operand quantised along
+ * its contraction axis; the 128x128 weight tiles serve both directions).    */
+enum { MOE_GEMM_B_KN = 0x800 };
 
 /* Quantise src viewed as `groups` matrices of [rows, cols] (row stride ld
  * elements, group stride rows*ld) to OCP e4m3 with one fp32 scale per tile:

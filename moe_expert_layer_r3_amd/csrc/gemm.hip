@@ -666,11 +666,32 @@ struct WideSmem {
     static constexpr int TOTAL = 2 * STAGE;
 };
 
-template <int EPI, bool P2, bool WF4>
+// B operand read from a 64-bit transposing LDS load (gfx950
+// ds_read_b64_tr_b8).  Within each 16-lane group the 16 addresses name 8-byte
+// pieces P[s] (s = lane % 16) and lane i receives byte (i % 8) of
+// P[2j + i / 8] as its byte j (measured): with P[2j + h] = bytes 8h .. 8h + 7 of
+// K-row k0 + j of a [K][N]-ordered tile, lane i holds column i at K values
+// k0 .. k0 + 7, in order, which is the MFMA operand's layout.
+template <int OFF>
+__device__ __forceinline__ v2u lds_tr8(uint32_t addr) {
+    typedef int v2i_t __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i_t* lds_v2i_ptr;
+    const v2i_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ptr)(uintptr_t)(addr + OFF));
+    return v2u{(uint32_t)r.x, (uint32_t)r.y};
+}
+
+// BKN: the weights come as [L, K, N] with scales [L, K/128, N/128] (the forward
+// weights [out, in] of a dgrad product, which contracts over `out`), read
+// without a transposed copy.  A K step's B tile is 128 K-rows of 256 bytes in
+// LDS, row k's 16-byte chunk c stored at chunk c ^ f(k), f(k) = (k & 7) |
+// ((k >> 4) & 1) << 3: the 32 rows one transposing load touches then spread
+// over all 64 banks twice, the minimum for 512 bytes.
+template <int EPI, bool P2, bool WF4, bool BKN = false>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
     using SM = WideSmem<WF4>;
     constexpr int MI = 8, NI = 4;  // 16 x 16 subtiles of a wave's 128 x 64
     static_assert(!WF4 || P2, "MXFP4 weights take the hardware-scale path");
+    static_assert(!BKN || (!WF4 && !is_swiglu(EPI)), "[K, N] weights: FP8 dgrad products only");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
     __shared__ int tile_base[GMAXL + 1];
@@ -732,9 +753,19 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
     const uint32_t a_rd0 = (wm * 128 + l15) * 128 + ((c0 ^ l7) << 4);
     const uint32_t a_rd1 = (wm * 128 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
     const int sw4 = ((l15 >> 1) ^ (l15 >> 3)) & 3;
-    const uint32_t b_rd0 = WF4 ? SM::A_BYTES + (wn * 64 + l15) * 64 + ((c0 ^ sw4) << 4)
-                               : SM::A_BYTES + (wn * 64 + l15) * 128 + ((c0 ^ l7) << 4);
-    const uint32_t b_rd1 = SM::A_BYTES + (wn * 64 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    uint32_t b_rd0, b_rd1;
+    if constexpr (BKN) {
+        // K-row 16*c0 + l15/2 (+ 8, 64, 72 for the other three loads),
+        // bytes 8*(l15 & 1) of the fragment's 16-column chunk; b_rd1 holds
+        // 16 * ((4*wn) ^ f) and fragment ni's chunk term is b_rd1 ^ 16*ni
+        const int fk = (l15 >> 1) | ((c0 & 1) << 3);
+        b_rd0 = SM::A_BYTES + (16 * c0 + (l15 >> 1)) * 256 + 8 * (l15 & 1);
+        b_rd1 = (uint32_t)(16 * ((4 * wn) ^ fk));
+    } else {
+        b_rd0 = WF4 ? SM::A_BYTES + (wn * 64 + l15) * 64 + ((c0 ^ sw4) << 4)
+                    : SM::A_BYTES + (wn * 64 + l15) * 128 + ((c0 ^ l7) << 4);
+        b_rd1 = SM::A_BYTES + (wn * 64 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    }
     const uint32_t bq_rd = SM::A_BYTES + SM::B_BYTES + SM::S_BYTES + (wn * 64 + l15) * 4 + c0;
     // A scales of a stage in row order (one 1 KB DMA per K step): a lane's
     // eight rows wm*128 + mi*16 + l15 are 64 bytes apart
@@ -793,7 +824,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         } else {
             brow_w = ti.n0 + wave * 32;
         }
-        ti.b_base = WF4 ? g.b + ((int64_t)e * nkb * N + brow_w) * 64 : g.b + ((int64_t)e * N + brow_w) * K;
+        if constexpr (BKN)
+            ti.b_base = g.b + (int64_t)e * K * N + ti.n0;  // K-row 0, the tile's first column
+        else
+            ti.b_base = WF4 ? g.b + ((int64_t)e * nkb * N + brow_w) * 64 : g.b + ((int64_t)e * N + brow_w) * K;
         ti.bsm = reinterpret_cast<const uint8_t*>(g.b_s) + ((int64_t)e * nkb * N + brow_w) * 4;
         ti.s_base = g.a_s + ti.row0;
         const float* bsx = g.b_s + (int64_t)e * (N / 128) * nkb;
@@ -805,8 +839,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
             blk0 = ti.n0 / 128;
             blk1 = blk0 + 1;
         }
-        ti.bs_lo = bsx + (int64_t)blk0 * nkb;
-        ti.bs_hi = bsx + (int64_t)blk1 * nkb;
+        // [N/128, K/128] scales: a block's K run is contiguous; [K/128, N/128]
+        // (BKN): it has stride N/128 (stage_bscale)
+        ti.bs_lo = bsx + (BKN ? (int64_t)blk0 : (int64_t)blk0 * nkb);
+        ti.bs_hi = bsx + (BKN ? (int64_t)blk1 : (int64_t)blk1 * nkb);
         ti.rot = ((mt & 1) * 2 + (nt & 3) * 2) % nkb;
         return ti;
     };
@@ -820,7 +856,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         const int half = wave >> 2;
         const float* src = half ? ti.bs_hi : ti.bs_lo;
         const int kb = (wave & 3) * 64 + (int)__lane_id();
-        if (kb < nkb) bscale[kb][half] = src[kb];
+        if (kb < nkb) bscale[kb][half] = src[BKN ? kb * (N / 128) : kb];
     };
     const uint32_t bs_rd = lds_addr(&bscale[0][0]);
     const bool second_blk = !is_swiglu(EPI) && wn >= 2;
@@ -863,6 +899,19 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 for (int i = 0; i < 2; ++i) dma16s(bb, b_off0 + 1024 * i, sB + (w * 2 + i) * 1024);
                 if (lane < 32)
                     dma4s(ti.bsm + (int64_t)kr * N * 4 + brow_off * 4, bs_off, sB + SM::B_BYTES + SM::S_BYTES + w * 128);
+            } else if constexpr (BKN) {
+                // K-rows 16w .. 16w + 15 of the step, 4 per 1 KB segment:
+                // lane l fills chunk position l % 16 of row 16w + 4i + l/16
+                // with the global chunk (l % 16) ^ f(row)
+                const uint8_t* bb = ti.b_base + ((int64_t)kr * GBK + 16 * w) * N;
+                const uint32_t l = (uint32_t)__lane_id();
+                const uint32_t rsub = l >> 4, pos = l & 15, fw = (uint32_t)((w & 1) << 3);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t fk = (uint32_t)(4 * (i & 1)) + rsub + fw;
+                    dma16s(bb, (uint32_t)((4 * i) * N) + rsub * (uint32_t)N + ((pos ^ fk) << 4),
+                           sB + (w * 4 + i) * 1024);
+                }
             } else {
                 const uint8_t* bb = ti.b_base + kr * GBK + brow_off * K;
 #pragma unroll
@@ -924,6 +973,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 const u32x4 z4 = {0u, 0u, 0u, 0u};
                 bfr[ni] = join8(lds16<ni * 1024>(pb0), z4);
                 eb4[ni] = (int)lds1<ni * 64>(pbs);
+            } else if constexpr (BKN) {
+                // K values 16c0 .. +7, +8 .. +15, 16c0 + 64 .. +71, +72 .. +79
+                const uint32_t pa = pb0 + (b_rd1 ^ (uint32_t)(16 * ni));
+                const v2u r0 = lds_tr8<0>(pa), r1 = lds_tr8<2048>(pa);
+                const v2u r2 = lds_tr8<16384>(pa), r3 = lds_tr8<18432>(pa);
+                bfr[ni] = v8i{(int)r0.x, (int)r0.y, (int)r1.x, (int)r1.y, (int)r2.x, (int)r2.y, (int)r3.x, (int)r3.y};
             } else {
                 bfr[ni] = join8(lds16<ni * 2048>(pb0), lds16<ni * 2048>(pb1));
             }
@@ -1220,9 +1275,19 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
 }
 
 template <int EPI>
-static int launch_wide(const GemmArgs& a, bool p2, bool wf4, hipStream_t stream) {
+static int launch_wide(const GemmArgs& a, bool p2, bool wf4, hipStream_t stream, bool bkn = false) {
     const int ncu = num_cus();
     const int grid = (ncu + 7) / 8 * 8;
+    if constexpr (EPI == MOE_EPI_STORE_BF16 || EPI == MOE_EPI_STORE_F32) {
+        if (bkn) {
+            if (p2)
+                gemm_wide_kernel<EPI, true, false, true><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+            else
+                gemm_wide_kernel<EPI, false, false, true><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+            MOE_LAUNCH_CHECK("gemm_wide_kernel");
+            return MOE_OK;
+        }
+    }
     if (wf4)
         gemm_wide_kernel<EPI, true, true><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
     else if (p2)
@@ -1234,9 +1299,9 @@ static int launch_wide(const GemmArgs& a, bool p2, bool wf4, hipStream_t stream)
 }
 
 template <int BN, int EPI>
-static int launch_gemm(const GemmArgs& a, bool p2, bool wf4, bool wide, hipStream_t stream) {
+static int launch_gemm(const GemmArgs& a, bool p2, bool wf4, bool wide, hipStream_t stream, bool bkn = false) {
     if constexpr (BN == 256) {
-        if (wide) return launch_wide<EPI>(a, p2, wf4, stream);
+        if (wide) return launch_wide<EPI>(a, p2, wf4, stream, bkn);
     }
     const int ncu = num_cus();
     const int grid = (ncu + 7) / 8 * 8;  // one 512-thread block per CU (LDS bound), persistent
@@ -1262,8 +1327,13 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
     const bool p2 = (epilogue & MOE_SCALE_POW2) != 0;
     const bool wf4 = (epilogue & MOE_WEIGHT_MXFP4) != 0;
     const bool tile128 = (epilogue & MOE_GEMM_TILE128) != 0;
-    epilogue &= ~(MOE_SCALE_POW2 | MOE_WEIGHT_MXFP4 | MOE_GEMM_TILE128);
+    const bool bkn = (epilogue & MOE_GEMM_B_KN) != 0;
+    epilogue &= ~(MOE_SCALE_POW2 | MOE_WEIGHT_MXFP4 | MOE_GEMM_TILE128 | MOE_GEMM_B_KN);
     MOE_REQUIRE(!wf4 || p2, MOE_ERR_UNSUPPORTED, "grouped_gemm: MXFP4 weights need MOE_SCALE_POW2 activations");
+    MOE_REQUIRE(!bkn || (!wf4 && !tile128 && N % 256 == 0 &&
+                         (epilogue == MOE_EPI_STORE_BF16 || epilogue == MOE_EPI_STORE_F32)),
+                MOE_ERR_UNSUPPORTED,
+                "grouped_gemm: [K, N] weights need FP8 weights, 256 x 256 tiles (N %% 256 == 0) and a store epilogue");
     MOE_REQUIRE(L >= 1 && L <= GMAXL, MOE_ERR_SHAPE, "grouped_gemm: L=%d outside [1, 1024]", L);
     MOE_REQUIRE(row_cap >= 0 && row_cap % GBM == 0 && row_cap <= 0x7FFFFFFF, MOE_ERR_SHAPE,
                 "grouped_gemm: row_cap=%lld must be a multiple of 128", (long long)row_cap);
@@ -1285,10 +1355,10 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
     const bool wide = N % 256 == 0;
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
-            return wide ? launch_gemm<256, MOE_EPI_STORE_BF16>(ga, p2, wf4, !tile128, stream)
+            return wide ? launch_gemm<256, MOE_EPI_STORE_BF16>(ga, p2, wf4, !tile128, stream, bkn)
                         : launch_gemm<128, MOE_EPI_STORE_BF16>(ga, p2, wf4, !tile128, stream);
         case MOE_EPI_STORE_F32:
-            return wide ? launch_gemm<256, MOE_EPI_STORE_F32>(ga, p2, wf4, !tile128, stream)
+            return wide ? launch_gemm<256, MOE_EPI_STORE_F32>(ga, p2, wf4, !tile128, stream, bkn)
                         : launch_gemm<128, MOE_EPI_STORE_F32>(ga, p2, wf4, !tile128, stream);
         case MOE_EPI_SWIGLU_Q8:
             return launch_gemm<256, MOE_EPI_SWIGLU_Q8>(ga, p2, wf4, !tile128, stream);

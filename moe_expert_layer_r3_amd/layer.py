@@ -203,6 +203,12 @@ class TrainPlan(ForwardPlan):
 
     def __init__(self, T, d, f, E, L, k, e0=0, device="cuda", pow2=False, mxfp4=False):
         super().__init__(T, d, f, E, L, k, e0=e0, device=device, save_gu=True, pow2=pow2, mxfp4=mxfp4)
+        # FP8 weights with d, f multiples of 256: the dgrad products read the
+        # forward weights [out, in] as their [K, N] operand, so no transposed
+        # copy is made; otherwise (MXFP4, or other shapes) they read the copies
+        # quantize_weights(transpose=True) writes
+        self.weights_kn = not mxfp4 and d % 256 == 0 and f % 256 == 0
+        self.transpose_weights = not self.weights_kn
         dv = device
         f32, u8, b16 = torch.float32, torch.uint8, torch.bfloat16
         R = self.rcap
@@ -235,10 +241,16 @@ class TrainPlan(ForwardPlan):
               self.T, self.L, self.rcap, self.k, self.d, _p(self.dyq), _p(self.dyq_s), _p(self.dyqT), _p(self.dyqT_s),
               _p(self.gate_part), self.sflag, _stream())
 
+    def _dgrad_weights(self, wts, name):
+        if self.weights_kn:
+            return wts[name + "q"], wts[name + "s"], ops.GEMM_B_KN
+        return wts[name + "qT"], wts[name + "sT"], 0
+
     def dgrad2(self, wts):
-        _call("moe_grouped_gemm_fp8", _p(self.dyq), _p(self.dyq_s), _p(wts["w2qT"]), _p(wts["w2sT"]),
-              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.f, self.d, ops.EPI_STORE_F32 | self.gflag,
-              None,
+        b, b_s, kn = self._dgrad_weights(wts, "w2")
+        _call("moe_grouped_gemm_fp8", _p(self.dyq), _p(self.dyq_s), _p(b), _p(b_s),
+              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.f, self.d,
+              ops.EPI_STORE_F32 | self.gflag | kn, None,
               _p(self.dH), None, None, None, None, None, _stream())
 
     def swiglu_bwd(self):
@@ -248,9 +260,10 @@ class TrainPlan(ForwardPlan):
               _p(s["h_qT"]), _p(s["h_sT"]), None, None, self.sflag, _stream())
 
     def dgrad1(self, wts):
-        _call("moe_grouped_gemm_fp8", _p(self.sb["dgu_q"]), _p(self.sb["dgu_s"]), _p(wts["w13qT"]),
-              _p(wts["w13sT"]), _p(self.counts), _p(self.offsets), self.L, self.rcap, self.d, 2 * self.f,
-              ops.EPI_STORE_BF16 | self.gflag, None, _p(self.dX), None, None, None, None, None, _stream())
+        b, b_s, kn = self._dgrad_weights(wts, "w13")
+        _call("moe_grouped_gemm_fp8", _p(self.sb["dgu_q"]), _p(self.sb["dgu_s"]), _p(b), _p(b_s),
+              _p(self.counts), _p(self.offsets), self.L, self.rcap, self.d, 2 * self.f,
+              ops.EPI_STORE_BF16 | self.gflag | kn, None, _p(self.dX), None, None, None, None, None, _stream())
 
     def unpermute(self):
         _call("moe_unpermute_combine", _p(self.dX), _p(self.pair_row), None, self.T, self.k, self.d, self.rcap,
@@ -280,7 +293,8 @@ class TrainPlan(ForwardPlan):
 
     def backward(self, x, dy, wts, events=None):
         """Backward of the last ``forward`` for upstream gradient dy [T, d] bf16;
-        wts must hold the transposed weight copies (quantize_weights(transpose=True))."""
+        wts must hold the transposed weight copies (quantize_weights(transpose=True))
+        when ``self.transpose_weights``."""
         def rec(name, fn, *a):
             if events is not None and name in events:
                 events[name][0].record()

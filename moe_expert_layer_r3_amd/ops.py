@@ -19,6 +19,7 @@ TILE_1x128, TILE_128x128 = 0, 1
 SCALE_POW2 = 0x100  # power-of-two (UE8M0) tile scales, OR'ed into tile / epilogue
 WEIGHT_MXFP4 = 0x200  # MXFP4 weights, OR'ed (with SCALE_POW2) into a GEMM epilogue
 GEMM_TILE128 = 0x400  # 128 x 256 GEMM tiles instead of 256 x 256, OR'ed into a GEMM epilogue
+GEMM_B_KN = 0x800     # weights given as [L, K, N] (a dgrad product on the forward weights), OR'ed likewise
 SRC_BF16, SRC_F32 = 0, 1
 FLAG_BAD_ID, FLAG_DUP_ID, FLAG_ROW_CAP = 1, 2, 4
 ROW_ALIGN = 128
@@ -316,7 +317,7 @@ def quant_rows_t(src, w, row_pair, offsets, L, rcap, k, pow2=False):
 # ---------------------------------------------------------------- GEMMs
 
 def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_in=None, rcap=None, pow2=False,
-                 mxfp4=False, tile128=False):
+                 mxfp4=False, tile128=False, b_kn=False):
     """Per-expert blockwise-scaled FP8 GEMM over the expert-grouped rows.
 
     a [rcap, K] u8, a_s [K/128, rcap]; b [L, N, K] u8, b_s [L, N/128, K/128].
@@ -324,6 +325,8 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     SwiGLU epilogues then also quantise h with power-of-two scales).
     mxfp4: b [L, K/128, N, 64] and b_s [L, K/128, N, 4] from quant_mxfp4 (implies pow2).
     tile128: 128 x 256 block tiles instead of 256 x 256 (N % 256 == 0).
+    b_kn: b [L, K, N], b_s [L, K/128, N/128] (the forward weights of a dgrad
+    product, read without a transposed copy; FP8, store epilogues, N % 256 == 0).
     Returns the epilogue's outputs: STORE_BF16 -> y; STORE_F32 -> acc;
     SWIGLU_Q8 -> (hq, hq_s); SWIGLU_Q8_SAVE -> (hq, hq_s, gu);
     SWIGLU_F32 -> h."""
@@ -332,6 +335,8 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
         L, kb, N, _ = b.shape
         K = kb * 128
         pow2 = True
+    elif b_kn:
+        L, K, N = b.shape
     else:
         L, N, K = b.shape
     dev = _dev(a)
@@ -356,7 +361,8 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     else:
         raise ValueError(f"unknown epilogue {epilogue}")
     _call("moe_grouped_gemm_fp8", _p(a), _p(a_s), _p(b), _p(b_s), _p(counts), _p(offsets), L, rcap, N, K,
-          epilogue | _flag(pow2) | (WEIGHT_MXFP4 if mxfp4 else 0) | (GEMM_TILE128 if tile128 else 0), _p(epi_in), _p(out), _p(out_s), _p(out2), _p(out2_s), _p(out3), _p(out3_s),
+          epilogue | _flag(pow2) | (WEIGHT_MXFP4 if mxfp4 else 0) | (GEMM_TILE128 if tile128 else 0)
+          | (GEMM_B_KN if b_kn else 0), _p(epi_in), _p(out), _p(out_s), _p(out2), _p(out2_s), _p(out3), _p(out3_s),
           _stream(dev))
     return res
 

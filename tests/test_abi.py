@@ -136,6 +136,13 @@ def test_gemm_validation():
     # the 128 x 256 tile flag is recognised: the same argument checks still apply
     assert call(a10=0x400, a8=100) == -2 and call(a10=0x401) == -1 and call(a10=0x409) == -3
     assert ops.GEMM_TILE128 == 0x400
+    # [K, N] weights: store epilogues with FP8 weights and 256 x 256 tiles only
+    assert ops.GEMM_B_KN == 0x800
+    assert call(a10=0x800, a8=384) == -3            # N % 256
+    assert call(a10=0x801, a13=FAKE) == -3          # SwiGLU epilogue
+    assert call(a10=0xC00) == -3                    # with the 128 x 256 tile
+    assert call(a10=0xB00) == -3                    # MXFP4 weights
+    assert call(a10=0x803, a0=None) == -1           # accepted flags; the NULL check follows
 
 
 def test_combine_validation():
@@ -145,6 +152,25 @@ def test_combine_validation():
     assert _rc("moe_combine_backward", FAKE, FAKE, FAKE, FAKE, 10, 2, 128, 256, FAKE, None, FAKE, 0, None)[0] == -1
     assert _rc("moe_combine_backward", FAKE, FAKE, FAKE, FAKE, 10, 2, 128, 256, FAKE, FAKE, FAKE, 3, None)[0] == -3
     assert _rc("moe_gate_backward", FAKE, FAKE, FAKE, 10, 2, 2000, FAKE, None)[0] == -2
+    R = "moe_combine_backward_rows"
+    ok = [FAKE] * 5 + [100, 8, 1024, 2, 256] + [FAKE] * 5
+    assert _rc(R, *ok, 0x200, None)[0] == -3                                       # unknown flags
+    bad = list(ok)
+    bad[9] = 200
+    assert _rc(R, *bad, 0, None)[0] == -2                                          # d % 128
+    bad = list(ok)
+    bad[7] = 1000
+    assert _rc(R, *bad, 0, None)[0] == -2                                          # row_cap % 128
+    bad = list(ok)
+    bad[7], bad[9] = 1 << 20, 4096
+    assert _rc(R, *bad, 0, None)[0] == -2                                          # row_cap * d >= 2^31
+    bad = list(ok)
+    bad[14] = None
+    assert _rc(R, *bad, 0x100, None)[0] == -1                                      # gate_part NULL
+    GP = "moe_gate_backward_parts"
+    assert _rc(GP, FAKE, FAKE, 1024, 200, FAKE, FAKE, 10, 2, 64, FAKE, FAKE, None)[0] == -2   # d % 128
+    assert _rc(GP, FAKE, FAKE, 1024, 256, FAKE, FAKE, 10, 17, 64, FAKE, FAKE, None)[0] == -2  # k
+    assert _rc(GP, FAKE, None, 1024, 256, FAKE, FAKE, 10, 2, 64, FAKE, FAKE, None)[0] == -1
 
 
 def test_backward_validation():

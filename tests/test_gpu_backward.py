@@ -208,11 +208,13 @@ def test_swiglu_backward(counts, f, pow2):
 
 # ------------------------------------------------------------------ dgrad GEMM (transposed weights)
 
+@pytest.mark.parametrize("kn", [False, True])
 @pytest.mark.parametrize("counts,K,N,pow2", [([0, 1, 130, 300], 256, 512, False), ([77, 128], 384, 256, False),
-                                             ([77, 128], 384, 256, True)])
-def test_gemm_dgrad(counts, K, N, pow2):
+                                             ([77, 128], 384, 256, True), ([300, 0, 5, 260], 1024, 768, True)])
+def test_gemm_dgrad(counts, K, N, pow2, kn):
     """acc[r] = dY[r] @ W[e] for W [L, K, N] given in its forward [out=K, in=N]
-    layout; the GEMM reads the transposed copy written by the 128x128 quantiser."""
+    layout; the GEMM reads the transposed copy written by the 128x128 quantiser,
+    or (kn) the forward codes and scales themselves as its [K, N] operand."""
     k, E, e0 = 4, 32, 0
     ids, res, rp, rng = _perm(counts, k, E, e0, seed=K + N + 5)
     L = len(counts)
@@ -224,12 +226,21 @@ def test_gemm_dgrad(counts, K, N, pow2):
     wq, ws, wqT, wsT = ops.quant_fp8(bf16_tensor(W), tile=ops.TILE_128x128, transpose=True, pow2=pow2)
     say(f"gemm dgrad counts={counts} K={K} N={N} pow2={pow2}")
     # the GEMM reads activation scales K-block-major
-    acc = ops.grouped_gemm(aq, as_.t().contiguous(), wqT, wsT, res["counts"], res["offsets"], ops.EPI_STORE_F32,
-                           pow2=pow2)
+    if kn:
+        acc = ops.grouped_gemm(aq, as_.t().contiguous(), wq, ws, res["counts"], res["offsets"], ops.EPI_STORE_F32,
+                               pow2=pow2, b_kn=True)
+        # the bf16 store epilogue reads the same operands
+        y = ops.grouped_gemm(aq, as_.t().contiguous(), wq, ws, res["counts"], res["offsets"], ops.EPI_STORE_BF16,
+                             pow2=pow2, b_kn=True)
+    else:
+        acc = ops.grouped_gemm(aq, as_.t().contiguous(), wqT, wsT, res["counts"], res["offsets"], ops.EPI_STORE_F32,
+                               pow2=pow2)
     c, o = npi(res["counts"]), npi(res["offsets"])
     ref = OG.grouped_dgrad(npi(aq), npi(as_), c, o, npi(wq), npi(ws))
     rows = np.concatenate([np.arange(o[e], o[e] + c[e]) for e in range(L)]).astype(np.int64)
     assert rel_fro(np64(acc)[rows], ref[rows]) <= ACC_TOL
+    if kn:
+        assert rel_fro(np64(y)[rows], obf16(ref[rows])) <= TOL
 
 
 # ------------------------------------------------------------------ wgrad GEMM
@@ -321,7 +332,7 @@ def test_gate_backward():
 
 def _train_gpu(wl, x, lg, W13, W2, dy, pow2=False):
     plan = ML.TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, e0=wl.e0, device=DEV, pow2=pow2)
-    wts = ML.quantize_weights(W13, W2, transpose=True, pow2=pow2)
+    wts = ML.quantize_weights(W13, W2, transpose=plan.transpose_weights, pow2=pow2)
     plan.forward(x, lg, wts)
     plan.backward(x, dy, wts)
     torch.cuda.synchronize()
@@ -392,7 +403,9 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
         rq, rs = OQ.quant_1x128(of32(w[t, j][:, None] * dys), pow2=pow2)
         assert np.array_equal(dyq, rq) and np.array_equal(dyq_s, rs)
         # dgrad through W2 (transposed copy [f, d]), fp32 accumulators
-        ref_dH = OG.blockscaled_matmul(dyq, dyq_s, npi(wts["w2qT"][e]), OG.expand_weight_scales(npi(wts["w2sT"][e])))
+        # the dgrad products' weights: the forward codes and scales transposed
+        w2T, w2sT = npi(wts["w2q"][e]).T, npi(wts["w2s"][e]).T
+        ref_dH = OG.blockscaled_matmul(dyq, dyq_s, w2T, OG.expand_weight_scales(w2sT))
         dH = _rows(plan.dH, rows)
         assert rel_fro(dH, ref_dH) <= ACC_TOL
         # SwiGLU backward on the GPU's dH and saved bf16 G, U
@@ -404,8 +417,8 @@ def _check_stages(plan, wts, x, dy, wl, rows_of=None, experts=None, feat_of=None
         q1, s1 = OQ.quant_1x128(dgu32, pow2=pow2)
         assert np.array_equal(dgu_q, q1) and np.array_equal(dgu_s, s1)
         # dgrad through W13 (transposed copy [d, 2f]), bf16
-        ref_dX = OG.blockscaled_matmul(dgu_q, dgu_s, npi(wts["w13qT"][e]),
-                                       OG.expand_weight_scales(npi(wts["w13sT"][e])))
+        ref_dX = OG.blockscaled_matmul(dgu_q, dgu_s, npi(wts["w13q"][e]).T,
+                                       OG.expand_weight_scales(npi(wts["w13s"][e]).T))
         assert rel_fro(_rows(plan.dX, rows), obf16(ref_dX)) <= TOL
     # unpermute-sum of dX, the gate gradient and d_logits on sampled tokens
     toks = np.arange(0, wl.T, max(1, wl.T // 512))
@@ -551,8 +564,9 @@ def test_train_step_run_twice_bitwise():
     x = synth.x(wl).to(DEV)
     lg = gpu(synth.logits(wl))
     dy = synth.dy(wl).to(DEV)
-    wts = ML.quantize_weights(synth.weights(wl, "w13").to(DEV), synth.weights(wl, "w2").to(DEV), transpose=True)
     plan = ML.TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, e0=wl.e0, device=DEV)
+    wts = ML.quantize_weights(synth.weights(wl, "w13").to(DEV), synth.weights(wl, "w2").to(DEV),
+                              transpose=plan.transpose_weights)
     bufs = _plan_tensors(plan)
     runs = []
     for i in range(2):
@@ -745,11 +759,11 @@ def test_train_step_graph_replay():
     dys = [synth.dy(wl, t0=i * wl.T).to(DEV) for i in range(2)]
     W13 = synth.weights(wl, "w13").to(DEV)
     W2 = synth.weights(wl, "w2").to(DEV)
-    wts = ML.weight_buffers(wl.L, wl.d, wl.f, DEV, transpose=True)
     plan = ML.TrainPlan(wl.T, wl.d, wl.f, wl.E, wl.L, wl.k, e0=wl.e0, device=DEV)
+    wts = ML.weight_buffers(wl.L, wl.d, wl.f, DEV, transpose=plan.transpose_weights)
 
     def step(i):
-        ML.quantize_weights(W13, W2, transpose=True, out=wts)
+        ML.quantize_weights(W13, W2, transpose=plan.transpose_weights, out=wts)
         plan.forward(xs[i], lgs[i], wts)
         plan.backward(xs[i], dys[i], wts)
 
