@@ -243,6 +243,23 @@ int moe_quant_fp8_rows_t(const uint16_t* src, const float* w, const int32_t* row
                          int64_t cols, uint8_t* qT, float* sT, int32_t flags,
                          hipStream_t stream);
 
+/* Both quantisations of the expert-grouped rows from one read: the rows v of
+ * moe_quant_fp8_rows_t (v[r, c] = fp32(w[p] * src[p / k, c]) for p =
+ * row_pair[r], w == NULL: v = src[p / k, c]) quantised
+ *   1x128 along the columns:  q [row_cap, cols] u8, q_s [cols/128, row_cap] fp32
+ *                             (K-block-major; padding rows not written), as the
+ *                             gather of moe_permute writes xq for w == NULL
+ *   128x1 along the rows:     qT, qT_s exactly as moe_quant_fp8_rows_t
+ * ("RL at 1T scale", section "FP8 Training": the forward GEMM and the wgrad
+ * product contract x over different axes).  Rows at and past offsets[L] are
+ * not touched.  src [T, cols] bf16; cols % 128 == 0, row_cap % 128 == 0,
+ * row_cap * cols and T * cols below 2^31 (MOE_ERR_SHAPE).
+ * flags: 0, or MOE_SCALE_POW2 for power-of-two scales on both copies.        */
+int moe_quant_fp8_rows_both(const uint16_t* src, const float* w, const int32_t* row_pair,
+                            const int32_t* offsets, int64_t T, int32_t L, int64_t row_cap, int32_t k,
+                            int32_t cols, uint8_t* q, float* q_s, uint8_t* qT, float* qT_s,
+                            int32_t flags, hipStream_t stream);
+
 /* ---- grouped GEMM [FP8] ------------------------------------------------- */
 
 enum {

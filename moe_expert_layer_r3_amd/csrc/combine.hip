@@ -184,28 +184,33 @@ __global__ __launch_bounds__(CBLOCK) void combine_bwd_kernel(const uint16_t* __r
 }
 
 
-// Combine backward on the expert-grouped rows, with both FP8 copies of dY.
+// Rows of the expert-grouped layout gathered from a [T, d] source (row r holds
+// pair row_pair[r], token row_pair[r] / k), scaled by w[pair] if given, and
+// quantised twice from one read: 1x128 along the features (row-major) and
+// 128x1 along the rows (block-transposed).  GATE: the combine backward, with
+// dy as the source, w required, and the partial dots <dy_t, Y_r> of the gate
+// gradient taken on the way.
 // Block (column group g, row block b of 128 rows), 512 threads; the group is
 // `cpb` 128-wide column chunks, taken one after the other.  Thread (wave wv,
 // lane l) owns rows 4*rq .. 4*rq + 3 of the block, rq = 4*wv + l/16, and
 // columns 8*cg .. 8*cg + 7 of the chunk, cg = l % 16.  Per chunk:
-//   * the 4 rows of dy it needs are gathered (row r holds pair row_pair[r],
-//     token row_pair[r] / k) and the 4 rows of y_perm read, all loads issued
-//     together and those of the next chunk issued before this chunk is
-//     quantised; <dy_t, Y_r> over the chunk's 128 columns is added to the
-//     row's partial (fp32: 8-term chains, then the 16 lanes of the row);
-//   * dY = fp32(w * dy): a row's 1x128 tile is the 16 lanes of the row
+//   * the 4 source rows it needs are gathered (and, GATE, the 4 rows of
+//     y_perm read), all loads issued together and those of the next chunk
+//     issued before this chunk is quantised; GATE: <dy_t, Y_r> over the
+//     chunk's 128 columns is added to the row's partial (fp32: 8-term chains,
+//     then the 16 lanes of the row);
+//   * v = fp32(w * src): a row's 1x128 tile is the 16 lanes of the row
 //     (maximum over 8 values, then over those lanes), stored as 8-byte words
 //     of one 128-byte run; padding rows are not written;
 //   * a column's 128x1 tile is the thread's 4 rows, the wave's 4 row quads
 //     (lanes 16 apart) and the 8 waves through LDS; its codes go through a
 //     transposed LDS tile to 16-byte stores of 128-byte columns (padding rows
 //     count as 0).
-// The row's partial over the group's columns is written to
+// GATE: the row's partial over the group's columns is written to
 // gate_part[r * MOE_GATE_PARTS + g]; moe_gate_backward_parts sums the groups.
 constexpr int CBR_THREADS = 512;
-template <bool P2>
-__global__ __launch_bounds__(CBR_THREADS) void combine_bwd_rows_kernel(
+template <bool P2, bool GATE>
+__global__ __launch_bounds__(CBR_THREADS) void rows_quant2_kernel(
     const uint16_t* __restrict__ dy, const uint16_t* __restrict__ y_perm, const float* __restrict__ w,
     const int32_t* __restrict__ row_pair, const int32_t* __restrict__ offsets, int L, int64_t row_cap, int k, int d,
     int cpb, uint8_t* __restrict__ dyq, float* __restrict__ dyq_s, uint8_t* __restrict__ dyqT,
@@ -230,7 +235,7 @@ __global__ __launch_bounds__(CBR_THREADS) void combine_bwd_rows_kernel(
     uint32_t tok[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        wp[j] = p[j] >= 0 ? w[p[j]] : 0.f;
+        wp[j] = p[j] >= 0 ? (GATE || w ? w[p[j]] : 1.f) : 0.f;
         tok[j] = p[j] >= 0 ? (uint32_t)(p[j] / k) * (uint32_t)d : 0u;
     }
     const uint32_t row0 = r0 * (uint32_t)d;
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(CBR_THREADS) void combine_bwd_rows_kernel(
             ry[j] = make_uint4(0, 0, 0, 0);
             if (p[j] >= 0) {
                 rd[j] = *reinterpret_cast<const uint4*>(dy + (tok[j] + col));
-                ry[j] = *reinterpret_cast<const uint4*>(y_perm + (row0 + (uint32_t)j * d + col));
+                if constexpr (GATE) ry[j] = *reinterpret_cast<const uint4*>(y_perm + (row0 + (uint32_t)j * d + col));
             }
         }
     };
@@ -262,15 +267,17 @@ __global__ __launch_bounds__(CBR_THREADS) void combine_bwd_rows_kernel(
             v[j][2] = bf16_lo(rd[j].y); v[j][3] = bf16_hi(rd[j].y);
             v[j][4] = bf16_lo(rd[j].z); v[j][5] = bf16_hi(rd[j].z);
             v[j][6] = bf16_lo(rd[j].w); v[j][7] = bf16_hi(rd[j].w);
-            float s = v[j][0] * bf16_lo(ry[j].x);
-            s = fmaf(v[j][1], bf16_hi(ry[j].x), s);
-            s = fmaf(v[j][2], bf16_lo(ry[j].y), s);
-            s = fmaf(v[j][3], bf16_hi(ry[j].y), s);
-            s = fmaf(v[j][4], bf16_lo(ry[j].z), s);
-            s = fmaf(v[j][5], bf16_hi(ry[j].z), s);
-            s = fmaf(v[j][6], bf16_lo(ry[j].w), s);
-            s = fmaf(v[j][7], bf16_hi(ry[j].w), s);
-            dot[j] += s;
+            if constexpr (GATE) {
+                float s = v[j][0] * bf16_lo(ry[j].x);
+                s = fmaf(v[j][1], bf16_hi(ry[j].x), s);
+                s = fmaf(v[j][2], bf16_lo(ry[j].y), s);
+                s = fmaf(v[j][3], bf16_hi(ry[j].y), s);
+                s = fmaf(v[j][4], bf16_lo(ry[j].z), s);
+                s = fmaf(v[j][5], bf16_hi(ry[j].z), s);
+                s = fmaf(v[j][6], bf16_lo(ry[j].w), s);
+                s = fmaf(v[j][7], bf16_hi(ry[j].w), s);
+                dot[j] += s;
+            }
         }
         if (cc + 1 < cc_end) load(cc + 1);
         // dY = fp32(w * dy); maxima of the rows (1x128) and of the columns (128x1)
@@ -340,6 +347,7 @@ __global__ __launch_bounds__(CBR_THREADS) void combine_bwd_rows_kernel(
             *reinterpret_cast<uint4*>(dyqT + ((((uint32_t)b * d + (uint32_t)cc * 128 + c) << 7) + part)) = val;
         }
     }
+    if constexpr (!GATE) return;
     // the rows' partials over this group's columns; lane cg == j writes row j's
     float own = 0.f;
     bool real_own = false;
@@ -412,7 +420,35 @@ extern "C" int moe_combine_backward_rows(const uint16_t* dy, const uint16_t* y_p
         kern<<<grid, CBR_THREADS, 0, stream>>>(dy, y_perm, w, row_pair, offsets, L, row_cap, k, d, cpb, dyq, dyq_s, dyqT,
                                        dyqT_s, gate_part);
     };
-    flags ? go(combine_bwd_rows_kernel<true>) : go(combine_bwd_rows_kernel<false>);
-    MOE_LAUNCH_CHECK("combine_bwd_rows_kernel");
+    flags ? go(rows_quant2_kernel<true, true>) : go(rows_quant2_kernel<false, true>);
+    MOE_LAUNCH_CHECK("rows_quant2_kernel");
+    return MOE_OK;
+}
+
+extern "C" int moe_quant_fp8_rows_both(const uint16_t* src, const float* w, const int32_t* row_pair,
+                                       const int32_t* offsets, int64_t T, int32_t L, int64_t row_cap, int32_t k,
+                                       int32_t cols, uint8_t* q, float* q_s, uint8_t* qT, float* qT_s,
+                                       int32_t flags, hipStream_t stream) {
+    MOE_REQUIRE(flags == 0 || flags == MOE_SCALE_POW2, MOE_ERR_UNSUPPORTED, "quant_fp8_rows_both: unknown flags 0x%x",
+                flags);
+    MOE_REQUIRE(L >= 1 && L <= 1024 && k >= 1 && k <= CMAXK, MOE_ERR_SHAPE, "quant_fp8_rows_both: bad L/k");
+    MOE_REQUIRE(row_cap >= 0 && row_cap % 128 == 0 && row_cap <= 0x7FFFFFFF, MOE_ERR_SHAPE,
+                "quant_fp8_rows_both: row_cap=%lld must be a multiple of 128", (long long)row_cap);
+    MOE_REQUIRE(cols > 0 && cols % 128 == 0, MOE_ERR_SHAPE, "quant_fp8_rows_both: cols=%d must be a multiple of 128",
+                cols);
+    if (row_cap == 0) return MOE_OK;
+    MOE_REQUIRE(src && row_pair && offsets && q && q_s && qT && qT_s, MOE_ERR_NULL,
+                "quant_fp8_rows_both: NULL argument");
+    MOE_REQUIRE(row_cap / 128 <= 65535, MOE_ERR_SHAPE, "quant_fp8_rows_both: row_cap too large");
+    MOE_REQUIRE(row_cap * cols < ((int64_t)1 << 31) && T >= 0 && T * cols < ((int64_t)1 << 31), MOE_ERR_SHAPE,
+                "quant_fp8_rows_both: row_cap * cols and T * cols must stay below 2^31");
+    const int cpb = gate_chunks_per_group(cols);
+    dim3 grid((unsigned)gate_groups(cols), (unsigned)(row_cap / 128));
+    auto go = [&](auto kern) {
+        kern<<<grid, CBR_THREADS, 0, stream>>>(src, nullptr, w, row_pair, offsets, L, row_cap, k, cols, cpb, q, q_s,
+                                               qT, qT_s, nullptr);
+    };
+    flags ? go(rows_quant2_kernel<true, false>) : go(rows_quant2_kernel<false, false>);
+    MOE_LAUNCH_CHECK("rows_quant2_kernel");
     return MOE_OK;
 }

@@ -198,7 +198,8 @@ class TrainPlan(ForwardPlan):
       combine backward -> dY 1x128 and 128x1 (transposed) FP8, gate partials
       dgrad GEMM through W2 (fp32 dH) -> SwiGLU backward -> [dG, dU] 1x128 and
       128x1, recomputed H 128x1;  dgrad GEMM through W13 -> dX -> unpermute-sum dx
-      x 128x1 (transposed);  wgrad GEMMs dW2 = dY^T H, dW13 = [dG, dU]^T X
+      (x 128x1, transposed, made with the forward's 1x128 copy);  wgrad GEMMs
+      dW2 = dY^T H, dW13 = [dG, dU]^T X
       softmax-over-selection backward -> d_logits."""
 
     def __init__(self, T, d, f, E, L, k, e0=0, device="cuda", pow2=False, mxfp4=False):
@@ -232,6 +233,16 @@ class TrainPlan(ForwardPlan):
         self.dW2 = torch.empty((L, d, f), dtype=b16, device=dv)
         self.dW13 = torch.empty((L, 2 * f, d), dtype=b16, device=dv)
         self.d_logits = torch.empty((T, E), dtype=f32, device=dv)
+
+    def permute(self, x):
+        """Index kernels, then x's rows quantised 1x128 (GEMM1) and 128x1
+        (the dW13 product) from one read."""
+        _check(x, (self.T, self.d), torch.bfloat16, "x")
+        _call("moe_permute", _p(self.ids), self.T, self.k, self.e0, self.L, self.rcap, _p(self.counts),
+              _p(self.offsets), _p(self.row_pair), _p(self.pair_row), None, self.d, None, None, None, self.sflag,
+              _p(self.ws), self.ws.numel(), _p(self.status), _stream())
+        _call("moe_quant_fp8_rows_both", _p(x), None, _p(self.row_pair), _p(self.offsets), self.T, self.L, self.rcap,
+              self.k, self.d, _p(self.xq), _p(self.xq_s), _p(self.xqT), _p(self.xqT_s), self.sflag, _stream())
 
     def combine_bwd(self, dy):
         """dY = w * dy on the grouped rows, 1x128 and 128x1 (transposed), and the
@@ -269,11 +280,6 @@ class TrainPlan(ForwardPlan):
         _call("moe_unpermute_combine", _p(self.dX), _p(self.pair_row), None, self.T, self.k, self.d, self.rcap,
               _p(self.dx), _stream())
 
-    def x_quant_t(self, x):
-        _check(x, (self.T, self.d), torch.bfloat16, "x")
-        _call("moe_quant_fp8_rows_t", _p(x), None, _p(self.row_pair), _p(self.offsets), self.L, self.rcap,
-              self.k, self.d, _p(self.xqT), _p(self.xqT_s), self.sflag, _stream())
-
     def wgrad2(self):
         _call("moe_grouped_gemm_fp8_wgrad", _p(self.dyqT), _p(self.dyqT_s), _p(self.sb["h_qT"]),
               _p(self.sb["h_sT"]), _p(self.offsets), self.L, self.rcap, self.d, self.f, _p(self.dW2), self.sflag,
@@ -288,8 +294,7 @@ class TrainPlan(ForwardPlan):
         _call("moe_gate_backward_parts", _p(self.gate_part), _p(self.pair_row), self.rcap, self.d, _p(self.w),
               _p(self.ids), self.T, self.k, self.E, _p(self.d_gate), _p(self.d_logits), _stream())
 
-    BWD_STAGES = ("combine_bwd", "dgrad2", "swiglu_bwd", "dgrad1", "unpermute", "x_quant_t", "wgrad2", "wgrad13",
-                  "gate_bwd")
+    BWD_STAGES = ("combine_bwd", "dgrad2", "swiglu_bwd", "dgrad1", "unpermute", "wgrad2", "wgrad13", "gate_bwd")
 
     def backward(self, x, dy, wts, events=None):
         """Backward of the last ``forward`` for upstream gradient dy [T, d] bf16;
@@ -307,7 +312,6 @@ class TrainPlan(ForwardPlan):
         rec("swiglu_bwd", self.swiglu_bwd)
         rec("dgrad1", self.dgrad1, wts)
         rec("unpermute", self.unpermute)
-        rec("x_quant_t", self.x_quant_t, x)
         rec("wgrad2", self.wgrad2)
         rec("wgrad13", self.wgrad13)
         rec("gate_bwd", self.gate_bwd)

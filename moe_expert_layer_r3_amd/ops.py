@@ -63,6 +63,8 @@ _SIGS = {
     "moe_combine_backward_rows": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I32, _I64, _I32, _I32, _P, _P, _P, _P,
                                                  _P, _I32, _P]),
     "moe_gate_backward_parts": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _I64, _I32, _I32, _P, _P, _P]),
+    "moe_quant_fp8_rows_both": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I64, _I32, _I32, _P, _P, _P, _P, _I32,
+                                               _P]),
 }
 
 GATE_PARTS = 16  # MOE_GATE_PARTS
@@ -414,6 +416,22 @@ def combine(y_perm, pair_row, w, rcap=None):
     y = torch.empty((T, d), dtype=torch.bfloat16, device=_dev(pair_row))
     _call("moe_unpermute_combine", _p(y_perm), _p(pair_row), _p(w), T, k, d, rcap, _p(y), _stream(y.device))
     return y
+
+
+def quant_rows_both(src, w, row_pair, offsets, L, rcap, k, pow2=False):
+    """The expert-grouped rows of src (times w per pair if given) quantised
+    1x128 and 128x1 from one read: (q [rcap, cols], q_s [cols/128, rcap],
+    qT [rcap/128, cols, 128], qT_s [rcap/128, cols])."""
+    _contig(src, torch.bfloat16, "src")
+    cols = src.shape[1]
+    dev = _dev(src)
+    q = torch.empty((rcap, cols), dtype=torch.uint8, device=dev)
+    qs = torch.empty((cols // 128, rcap), dtype=torch.float32, device=dev)
+    qT = torch.empty((rcap // 128, cols, 128), dtype=torch.uint8, device=dev)
+    qT_s = torch.empty((rcap // 128, cols), dtype=torch.float32, device=dev)
+    _call("moe_quant_fp8_rows_both", _p(src), _p(w), _p(row_pair), _p(offsets), src.shape[0], L, rcap, k, cols,
+          _p(q), _p(qs), _p(qT), _p(qT_s), _flag(pow2), _stream(dev))
+    return q, qs, qT, qT_s
 
 
 def combine_backward_rows(dy, y_perm, w, row_pair, offsets, L, rcap, k, pow2=False):

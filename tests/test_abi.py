@@ -167,6 +167,15 @@ def test_combine_validation():
     bad = list(ok)
     bad[14] = None
     assert _rc(R, *bad, 0x100, None)[0] == -1                                      # gate_part NULL
+    B = "moe_quant_fp8_rows_both"
+    okb = [FAKE, None, FAKE, FAKE, 100, 8, 1024, 2, 256, FAKE, FAKE, FAKE, FAKE]
+    assert _rc(B, *okb, 0x200, None)[0] == -3                                      # unknown flags
+    bad = list(okb)
+    bad[8] = 200
+    assert _rc(B, *bad, 0, None)[0] == -2                                          # cols % 128
+    bad = list(okb)
+    bad[11] = None
+    assert _rc(B, *bad, 0, None)[0] == -1                                          # qT NULL
     GP = "moe_gate_backward_parts"
     assert _rc(GP, FAKE, FAKE, 1024, 200, FAKE, FAKE, 10, 2, 64, FAKE, FAKE, None)[0] == -2   # d % 128
     assert _rc(GP, FAKE, FAKE, 1024, 256, FAKE, FAKE, 10, 17, 64, FAKE, FAKE, None)[0] == -2  # k

@@ -66,6 +66,34 @@ def test_quant_rows_t(weighted, pow2):
     assert np.array_equal(npi(sT)[:n // 128].T.astype(np.float64), rs)
 
 
+@pytest.mark.parametrize("weighted,pow2,cols", [(False, False, 384), (True, False, 640), (False, True, 2176)])
+def test_quant_rows_both(weighted, pow2, cols):
+    """The grouped rows quantised 1x128 (as the permutation's gather writes xq)
+    and 128x1 (as quant_rows_t writes) from one read."""
+    counts, k, E, e0 = [0, 1, 130, 300, 128, 257], 4, 40, 3
+    ids, res, rp, rng = _perm(counts, k, E, e0, seed=41 + cols + weighted)
+    T = ids.shape[0]
+    src = _bf16_rows(rng, T, cols)
+    src[5, :] = 0.0
+    w = rng.random((T, k)).astype(np.float32) if weighted else None
+    say(f"quant_rows_both weighted={weighted} pow2={pow2} cols={cols}")
+    rcap = res["row_cap"]
+    q, qs, qT, qTs = ops.quant_rows_both(bf16_tensor(src), None if w is None else gpu(w), res["row_pair"],
+                                         res["offsets"], len(counts), rcap, k, pow2=pow2)
+    n = int(npi(res["offsets"])[-1])
+    real = rp >= 0
+    rows = np.flatnonzero(real)
+    p = rp[real]
+    v = np.zeros((n, cols))
+    v[real] = src[p // k] if w is None else of32(w.reshape(-1)[p][:, None].astype(np.float64) * src[p // k])
+    rq, rs = OQ.quant_1x128(v[real], pow2=pow2)
+    assert np.array_equal(npi(q)[rows], rq)
+    assert np.array_equal(npi(qs).T[rows].astype(np.float64), rs)
+    tq, ts = OQ.quant_128x1_t(v, real, pow2=pow2)
+    assert np.array_equal(npi(ops.untile_t(qT))[:, :n], tq)
+    assert np.array_equal(npi(qTs)[:n // 128].T.astype(np.float64), ts)
+
+
 # ------------------------------------------------------------------ combine backward
 
 @pytest.mark.parametrize("pow2", [False, True])
