@@ -637,10 +637,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 // smaller than that (hot-spot GEMM1 10%, ep8 GEMM1 2%): with every operand
 // an L2 hit the kernel is only ~15% faster, while leaving out the global ->
 // LDS DMA altogether makes it ~35% faster, so the DMA path, not bandwidth,
-// bounds it.  Eight waves (two per SIMD) as 2 (M) x 4 (N),
-// each 128 x 64: its 128 accumulators leave no room for the ping-pong's
+// bounds it.  The block tile is 288 x 256: an expert's rows take
+// ceil(rows / 288) m-tiles, so the 400-576 rows of a training-shape expert
+// stream its weights twice where 256-row tiles need three passes (the third
+// for a tail of a few rows), and the 228-293 rows of an ep8 expert mostly fit
+// one.  Eight waves (two per SIMD) as 2 (M) x 4 (N),
+// each 144 x 64: its 144 accumulators leave no room for the ping-pong's
 // all-fragments-at-once phase, so a wave holds its four B fragments of the K
-// step and streams the eight A fragments, one 16-row subtile at a time, each
+// step and streams the nine A fragments, one 16-row subtile at a time, each
 // followed by its four MFMAs (and, with fp32 scales, their rescale).  The two
 // waves of a SIMD interleave on their own.  Two LDS stages (64 KB each) and
 // one barrier per K step, placed before the step's last subtile: it frees the
@@ -649,14 +653,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 // freely (A rows beyond the expert's padded segment are never fetched, and a
 // wave whose rows are all padding issues no MFMAs).  Waves 0-3 issue all of
 // a step's DMA (below), so waves 4-7 never stall on it.
-constexpr int WBM = 256;
+// The tile height is a template parameter (MIT 16-row subtiles per wave: 9
+// for 288 rows, 8 for 256): the variants whose 144-row wave tiles would spill
+// registers (the SwiGLU epilogues with FP8 weights) keep 256-row tiles, where
+// spilling costs far more than the taller tile saves.
 constexpr int WBN = 256;
-#ifndef MOE_WIDE_DMA_WAVES
-#define MOE_WIDE_DMA_WAVES 4
-#endif
-static_assert(MOE_WIDE_DMA_WAVES == 8 || MOE_WIDE_DMA_WAVES == 4, "DMA waves: 8 or 4");
 
-template <bool WF4>
+template <bool WF4, int WBM>
 struct WideSmem {
     static constexpr int A_BYTES = WBM * GBK;
     static constexpr int B_BYTES = WBN * (WF4 ? GBK / 2 : GBK);
@@ -686,10 +689,14 @@ __device__ __forceinline__ v2u lds_tr8(uint32_t addr) {
 // LDS, row k's 16-byte chunk c stored at chunk c ^ f(k), f(k) = (k & 7) |
 // ((k >> 4) & 1) << 3: the 32 rows one transposing load touches then spread
 // over all 64 banks twice, the minimum for 512 bytes.
-template <int EPI, bool P2, bool WF4, bool BKN = false>
+template <int EPI, bool P2, bool WF4, bool BKN, int MIT>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
-    using SM = WideSmem<WF4>;
-    constexpr int MI = 8, NI = 4;  // 16 x 16 subtiles of a wave's 128 x 64
+    constexpr int MI = MIT, NI = 4;  // 16 x 16 subtiles of a wave's (16 MI) x 64
+    constexpr int WWR = 16 * MI;     // rows of a wave tile
+    constexpr int WBM = 2 * WWR;     // rows of a block tile
+    constexpr int WASEG = WBM / 32;  // 1 KB A segments (8 rows) per DMA wave and K step
+    static_assert(MI == 8 || MI == 9, "256- or 288-row tiles");
+    using SM = WideSmem<WF4, WBM>;
     static_assert(!WF4 || P2, "MXFP4 weights take the hardware-scale path");
     static_assert(!BKN || (!WF4 && !is_swiglu(EPI)), "[K, N] weights: FP8 dgrad products only");
 
@@ -707,7 +714,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
     const int NT = N / WBN;
     const int f = N / 2;
 
-    // ---- tile list: per expert ceil(padded rows / 256) m-tiles x NT n-tiles
+    // ---- tile list: per expert ceil(real rows / 288) m-tiles x NT n-tiles
     {
         int loc[2];
         int sum = 0;
@@ -719,7 +726,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 int64_t lo = g.offsets[e], hi = g.offsets[e + 1];
                 if (lo > g.row_cap) lo = g.row_cap;
                 if (hi > g.row_cap) hi = g.row_cap;
-                m = hi > lo ? (int)((hi - lo + WBM - 1) / WBM) : 0;
+                int64_t rows = g.counts[e];
+                if (rows > hi - lo) rows = hi - lo;
+                m = rows > 0 ? (int)((rows + WBM - 1) / WBM) : 0;
             }
             loc[i] = m;
             sum += m;
@@ -748,10 +757,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
     // fragment read offsets (stage-relative), as in the 128-row kernel with
-    // 128-row wave tiles: A row wm*128 + mi*16 + l15, B row wn*64 + ni*16 + l15
+    // 144-row wave tiles: A row wm*144 + mi*16 + l15, B row wn*64 + ni*16 + l15
     const int l15 = lane & 15, l7 = lane & 7, c0 = lane >> 4;
-    const uint32_t a_rd0 = (wm * 128 + l15) * 128 + ((c0 ^ l7) << 4);
-    const uint32_t a_rd1 = (wm * 128 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
+    const uint32_t a_rd0 = (wm * WWR + l15) * 128 + ((c0 ^ l7) << 4);
+    const uint32_t a_rd1 = (wm * WWR + l15) * 128 + (((c0 + 4) ^ l7) << 4);
     const int sw4 = ((l15 >> 1) ^ (l15 >> 3)) & 3;
     uint32_t b_rd0, b_rd1;
     if constexpr (BKN) {
@@ -767,9 +776,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         b_rd1 = SM::A_BYTES + (wn * 64 + l15) * 128 + (((c0 + 4) ^ l7) << 4);
     }
     const uint32_t bq_rd = SM::A_BYTES + SM::B_BYTES + SM::S_BYTES + (wn * 64 + l15) * 4 + c0;
-    // A scales of a stage in row order (one 1 KB DMA per K step): a lane's
-    // eight rows wm*128 + mi*16 + l15 are 64 bytes apart
-    const uint32_t s_rd = SM::A_BYTES + SM::B_BYTES + (wm * 128 + l15) * 4;
+    // A scales of a stage in row order (1152 bytes per K step): a lane's nine
+    // rows wm*144 + mi*16 + l15 are 64 bytes apart
+    const uint32_t s_rd = SM::A_BYTES + SM::B_BYTES + (wm * WWR + l15) * 4;
 
     struct Tile {
         int64_t row0, real_end, a_lim;  // first row, end of real rows, end of fetchable rows
@@ -781,9 +790,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         const float* bs_lo;
         const float* bs_hi;
         int rot;
-        int na;                         // A DMA segments of this wave inside a_lim (0..4)
-        int na_p;                       // the same for wave + 4 (issued by this wave when DMA_WAVES == 4)
-        int nmi;                        // 16-row subtiles of this wave with real rows (0..8)
+        int na;                         // A DMA segments of this (DMA) wave inside a_lim (0..WASEG)
+        int nmi;                        // 16-row subtiles of this wave with real rows (0..MI)
     };
     auto tile_at = [&](int t) {
         int lo = 0, hi = L;
@@ -808,16 +816,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         ti.a_lim = lim;
         if (ti.real_end > lim) ti.real_end = lim;
         {
-            const int64_t left = lim - (ti.row0 + wave * 32);  // rows of this wave's DMA share inside the limit
-            ti.na = left <= 0 ? 0 : (left >= 32 ? 4 : (int)(left / 8));
-            const int64_t left_p = left - 128;
-            ti.na_p = left_p <= 0 ? 0 : (left_p >= 32 ? 4 : (int)(left_p / 8));
-            const int64_t real = ti.real_end - (ti.row0 + wm * 128);
-            ti.nmi = real <= 0 ? 0 : (real >= 128 ? MI : (int)((real + 15) / 16));
+            // DMA wave w (0-3) moves A rows [72w, 72w + 72) of the tile: the
+            // segments of them inside the limit (a multiple of 8 rows away)
+            const int64_t left = lim - (ti.row0 + (wave & 3) * 8 * WASEG);
+            ti.na = left <= 0 ? 0 : (left >= 8 * WASEG ? WASEG : (int)(left / 8));
+            const int64_t real = ti.real_end - (ti.row0 + wm * WWR);
+            ti.nmi = real <= 0 ? 0 : (real >= WWR ? MI : (int)((real + 15) / 16));
         }
         ti.nt = nt;
         ti.n0 = nt * WBN;
-        ti.a_base = g.a + (ti.row0 + wave * 32) * K;
+        ti.a_base = g.a + (ti.row0 + (wave & 3) * 8 * WASEG) * K;
         int brow_w;
         if constexpr (is_swiglu(EPI)) {
             brow_w = ((wave & 1) ? f : 0) + nt * 128 + (wave >> 1) * 32;
@@ -874,22 +882,22 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         b_off0 = a_off0;
     }
     const uint32_t bs_off = (uint32_t)(lane * 4);
-    // A scales: the tile's 256 row scales of a K block are 1 KB contiguous
-    // (K-block-major layout): wave 0 moves them with one 16-byte-per-lane
-    // DMA, lane l rows 4l .. 4l + 3 (a 128-row boundary never splits them)
+    // A scales: the tile's 288 row scales of a K block are 1152 contiguous
+    // bytes (K-block-major layout): wave 0 moves rows 4l .. 4l + 3 with one
+    // 16-byte-per-lane DMA, lanes 0-7 of wave 1 the last 32 rows (a 128-row
+    // boundary never splits a lane's four)
     const uint32_t s_off = (uint32_t)(lane * 16);
 
     // issue_b / issue_a: the B (weights, with their fp4 scales) and A
     // (activations, with their scales) operands of a K block into a stage.
-    // The DMA of a K step is issued by MOE_WIDE_DMA_WAVES waves: waves 0-3
-    // (the default), one per SIMD, each also moving the share of wave + 4
-    // (its A rows are 128 further, its B rows 128 further, or 64 for the
-    // interleaved SwiGLU blocks), so that waves 4-7 never stall on a DMA
-    // issue and keep the matrix cores busy meanwhile (measured 2-7% faster
-    // than all eight waves issuing their own share); or all eight waves.
+    // Waves 0-3, one per SIMD, issue all of a step's DMA: each its own B
+    // share and that of wave + 4 (B rows 128 further, or 64 for the
+    // interleaved SwiGLU blocks) and a quarter of the A rows, so that waves
+    // 4-7 never stall on a DMA issue and keep the matrix cores busy meanwhile
+    // (measured 2-7% faster than all eight waves issuing their own share).
     constexpr int BROW_P = is_swiglu(EPI) ? 64 : 128;
-    const bool dma_self = MOE_WIDE_DMA_WAVES == 8 || wave < 4;
-    const bool dma_pair = MOE_WIDE_DMA_WAVES == 4 && wave < 4;
+    const bool dma_self = wave < 4;
+    const bool dma_pair = wave < 4;
     auto issue_b = [&](uint32_t sA, int kr, const Tile& ti) {
         const uint32_t sB = sA + SM::A_BYTES;
         auto one = [&](int w, int64_t brow_off) {
@@ -922,16 +930,21 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         if (dma_pair) one(wave + 4, BROW_P);
     };
     auto issue_a = [&](uint32_t sA, int kr, const Tile& ti) {
-        auto one = [&](int w, int na, int64_t row_off) {
-            const uint8_t* ab = ti.a_base + kr * GBK + row_off * K;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (i < na) dma16s(ab, a_off0 + (uint32_t)(8 * i * K), sA + (w * 4 + i) * 1024);
-        };
-        if (dma_self) one(wave, ti.na, 0);
-        if (dma_pair) one(wave + 4, ti.na_p, 128);
+        if (dma_self) {
+            // segments in groups of four: the group's row offset goes on the
+            // wave-uniform base, so only four per-lane offsets are formed
+            const uint8_t* ab = ti.a_base + kr * GBK;
+            static_for<0, WASEG>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                if (i < ti.na)
+                    dma16s(ab + (int64_t)(32 * (i / 4)) * K, a_off0 + (uint32_t)(8 * (i % 4) * K),
+                           sA + (wave * WASEG + i) * 1024);
+            });
+        }
         if (wave == 0 && ti.row0 + 4 * lane < ti.a_lim)
             dma16s(ti.s_base + (int64_t)kr * g.row_cap, s_off, sA + SM::A_BYTES + SM::B_BYTES);
+        if (wave == 1 && lane < (WBM - 256) / 4 && ti.row0 + 256 + 4 * lane < ti.a_lim)
+            dma16s(ti.s_base + (int64_t)kr * g.row_cap + 256, s_off, sA + SM::A_BYTES + SM::B_BYTES + 1024);
     };
     auto krot = [&](int kb, const Tile& ti) {
         int kr = kb + ti.rot;
@@ -964,7 +977,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         // fp4 scale codes), A and B scales, and the first A fragment.
         v8i bfr[NI];
         int eb4[NI];
-        uint32_t sav[8];
+        uint32_t sav[MI];
         uint32_t sbx = 0, sby = 0;
         v8i afc;
         auto read_b = [&](auto nc, uint32_t pb0, uint32_t pb1, uint32_t pbs) {
@@ -987,7 +1000,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
             const v2u sbv = lds8<0>(bsa);
             sbx = sbv.x;
             sby = sbv.y;
-            static_for<0, 8>([&](auto mc) {
+            static_for<0, MI>([&](auto mc) {
                 constexpr int mi = decltype(mc)::value;
                 sav[mi] = lds4<mi * 64>(ps);
             });
@@ -1143,7 +1156,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
             float* out = static_cast<float*>(g.out);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
-                const int64_t r = ep.row0 + wm * 128 + mi * 16 + l15;
+                const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15;
                 if (r >= ep.real_end) continue;
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni)
@@ -1159,7 +1172,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
             uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
-                const int64_t r = ep.row0 + wm * 128 + mi * 16 + l15;
+                const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15;
                 uint32_t x[NI], y[NI];  // columns (0, 1) and (2, 3) of each subtile, packed bf16
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni) {
@@ -1186,7 +1199,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 float* out = static_cast<float*>(g.out);
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi) {
-                    const int64_t r = ep.row0 + wm * 128 + mi * 16 + l15;
+                    const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15;
                     if (r >= ep.real_end) continue;
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni) {
@@ -1202,7 +1215,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 uint16_t* out2 = static_cast<uint16_t*>(g.out2);
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi) {
-                    const int64_t r = ep.row0 + wm * 128 + mi * 16 + l15;
+                    const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15;
                     float m = 0.f;
                     if constexpr (EPI == MOE_EPI_SWIGLU_Q8_SAVE) {
                         // G and U as bf16, regrouped like the bf16 store
@@ -1243,13 +1256,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                     }
                     m = fmaxf(m, __shfl_xor(m, 16));
                     m = fmaxf(m, __shfl_xor(m, 32));
-                    if (lg == 0) rowmax[wn][wm * 128 + mi * 16 + l15] = m;
+                    if (lg == 0) rowmax[wn][wm * WWR + mi * 16 + l15] = m;
                 }
                 lds_barrier();
                 uint8_t* out = static_cast<uint8_t*>(g.out);
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi) {
-                    const int rt = wm * 128 + mi * 16 + l15;
+                    const int rt = wm * WWR + mi * 16 + l15;
                     const int64_t r = ep.row0 + rt;
                     const float am = fmaxf(fmaxf(rowmax[0][rt], rowmax[1][rt]), fmaxf(rowmax[2][rt], rowmax[3][rt]));
                     const TileScale ts = tile_scale_t<P2>(am);
@@ -1274,26 +1287,40 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
     }
 }
 
+// 288-row tiles where the variant compiles without spills (checked with
+// -Rpass-analysis=kernel-resource-usage), 256-row ones otherwise
+// (the SWIGLU_F32 inspection variant takes the height of the SwiGLU
+// epilogues it stands in for: the tile's m index sets the K loop's start, and
+// so the fp32 summation order that the dumped h must share bit for bit)
+template <int EPI, bool P2, bool WF4, bool BKN>
+constexpr int wide_mi() {
+    if constexpr (EPI == MOE_EPI_SWIGLU_Q8 || EPI == MOE_EPI_SWIGLU_Q8_SAVE || EPI == MOE_EPI_SWIGLU_F32)
+        return WF4 ? 9 : 8;
+    else return 9;
+}
+
+template <int EPI, bool P2, bool WF4, bool BKN>
+static void go_wide(const GemmArgs& a, int grid, hipStream_t stream) {
+    gemm_wide_kernel<EPI, P2, WF4, BKN, wide_mi<EPI, P2, WF4, BKN>()><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+}
+
 template <int EPI>
 static int launch_wide(const GemmArgs& a, bool p2, bool wf4, hipStream_t stream, bool bkn = false) {
     const int ncu = num_cus();
     const int grid = (ncu + 7) / 8 * 8;
     if constexpr (EPI == MOE_EPI_STORE_BF16 || EPI == MOE_EPI_STORE_F32) {
         if (bkn) {
-            if (p2)
-                gemm_wide_kernel<EPI, true, false, true><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
-            else
-                gemm_wide_kernel<EPI, false, false, true><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+            p2 ? go_wide<EPI, true, false, true>(a, grid, stream) : go_wide<EPI, false, false, true>(a, grid, stream);
             MOE_LAUNCH_CHECK("gemm_wide_kernel");
             return MOE_OK;
         }
     }
     if (wf4)
-        gemm_wide_kernel<EPI, true, true><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+        go_wide<EPI, true, true, false>(a, grid, stream);
     else if (p2)
-        gemm_wide_kernel<EPI, true, false><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+        go_wide<EPI, true, false, false>(a, grid, stream);
     else
-        gemm_wide_kernel<EPI, false, false><<<dim3(grid), dim3(GTHREADS), 0, stream>>>(a);
+        go_wide<EPI, false, false, false>(a, grid, stream);
     MOE_LAUNCH_CHECK("gemm_wide_kernel");
     return MOE_OK;
 }
