@@ -654,9 +654,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_fp8_kernel(GemmArgs g) {
 // wave whose rows are all padding issues no MFMAs).  Waves 0-3 issue all of
 // a step's DMA (below), so waves 4-7 never stall on it.
 // The tile height is a template parameter (MIT 16-row subtiles per wave: 9
-// for 288 rows, 8 for 256): the variants whose 144-row wave tiles would spill
-// registers (the SwiGLU epilogues with FP8 weights) keep 256-row tiles, where
-// spilling costs far more than the taller tile saves.
+// for 288 rows, 8 for 256); wide_mi() below picks it per variant.
 constexpr int WBN = 256;
 
 template <bool WF4, int WBM>
@@ -977,7 +975,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         // fp4 scale codes), A and B scales, and the first A fragment.
         v8i bfr[NI];
         int eb4[NI];
-        uint32_t sav[MI];
+        uint32_t sac = 0;  // A scale of the current subtile's rows (this lane's)
         uint32_t sbx = 0, sby = 0;
         v8i afc;
         auto read_b = [&](auto nc, uint32_t pb0, uint32_t pb1, uint32_t pbs) {
@@ -996,14 +994,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 bfr[ni] = join8(lds16<ni * 2048>(pb0), lds16<ni * 2048>(pb1));
             }
         };
+        // the step's B block scales and subtile 0's A scale; the A scale of
+        // subtile mi + 1 is read with its fragment while mi multiplies
         auto read_scales = [&](uint32_t ps, uint32_t bsa) {
             const v2u sbv = lds8<0>(bsa);
             sbx = sbv.x;
             sby = sbv.y;
-            static_for<0, MI>([&](auto mc) {
-                constexpr int mi = decltype(mc)::value;
-                sav[mi] = lds4<mi * 64>(ps);
-            });
+            sac = lds4<0>(ps);
         };
         auto read_a = [&](auto mc, uint32_t pa0, uint32_t pa1) {
             constexpr int mi = decltype(mc)::value;
@@ -1020,10 +1017,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         };
         // four MFMAs of 16-row subtile mi on fragment af; with fp32 scales
         // their fresh partials are rescaled into the accumulators
-        auto subtile = [&](auto mc, const v8i& af) {
+        auto subtile = [&](auto mc, const v8i& af, uint32_t sa_bits) {
             constexpr int mi = decltype(mc)::value;
             if constexpr (P2) {
-                const int ea = (int)(sav[mi] >> 23);
+                const int ea = (int)(sa_bits >> 23);
                 const int eb0 = (int)((second_blk ? sby : sbx) >> 23), eb1 = (int)(sby >> 23);
                 static_for<0, NI>([&](auto nc) {
                     constexpr int ni = decltype(nc)::value;
@@ -1034,7 +1031,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                         acc[mi][ni] = mfma16x16x128_e8m0(bfr[ni], af, acc[mi][ni], second ? eb1 : eb0, ea);
                 });
             } else {
-                const float sa = __uint_as_float(sav[mi]);
+                const float sa = __uint_as_float(sa_bits);
                 const float s0 = sa * __uint_as_float(second_blk ? sby : sbx);
                 const float s1 = sa * __uint_as_float(sby);
                 v4f p[NI];
@@ -1068,14 +1065,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
             const uint32_t sA = sbase + (uint32_t)(st * SM::STAGE);
             const uint32_t sN = sbase + (uint32_t)((st ^ 1) * SM::STAGE);
             if (nmi > 0) {
-                uint32_t pa0 = sA + a_rd0, pa1 = sA + a_rd1;
-                pin(pa0); pin(pa1);
+                uint32_t pa0 = sA + a_rd0, pa1 = sA + a_rd1, ps = sA + s_rd;
+                pin(pa0); pin(pa1); pin(ps);
                 static_for<0, MI - 1>([&](auto mc) {
                     constexpr int mi = decltype(mc)::value;
                     const v8i afn = read_a(std::integral_constant<int, mi + 1>{}, pa0, pa1);
-                    subtile(mc, afc);
+                    const uint32_t san = lds4<(mi + 1) * 64>(ps);
+                    subtile(mc, afc, sac);
                     __builtin_amdgcn_sched_barrier(0);
                     afc = afn;
+                    sac = san;
                 });
             }
             wait_vmcnt<0>();
@@ -1092,7 +1091,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 pin(pb0); pin(pb1); pin(pbs);
                 constexpr int mi = MI - 1;
                 if constexpr (P2) {
-                    const int ea = (int)(sav[mi] >> 23);
+                    const int ea = (int)(sac >> 23);
                     const int eb0 = (int)((second_blk ? sby : sbx) >> 23), eb1 = (int)(sby >> 23);
                     static_for<0, NI>([&](auto nc) {
                         constexpr int ni = decltype(nc)::value;
@@ -1105,7 +1104,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                         __builtin_amdgcn_sched_barrier(0);
                     });
                 } else {
-                    const float sa = __uint_as_float(sav[mi]);
+                    const float sa = __uint_as_float(sac);
                     const float s0 = sa * __uint_as_float(second_blk ? sby : sbx);
                     const float s1 = sa * __uint_as_float(sby);
                     v4f p[NI];
@@ -1287,16 +1286,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
     }
 }
 
-// 288-row tiles where the variant compiles without spills (checked with
-// -Rpass-analysis=kernel-resource-usage), 256-row ones otherwise
-// (the SWIGLU_F32 inspection variant takes the height of the SwiGLU
-// epilogues it stands in for: the tile's m index sets the K loop's start, and
-// so the fp32 summation order that the dumped h must share bit for bit)
+// Every variant takes 288-row tiles.  The SwiGLU epilogues with FP8 weights
+// compile with 2-6 spilled registers, all of them saved before the K loop and
+// restored in the epilogue (once per tile), which costs nothing measurable.
 template <int EPI, bool P2, bool WF4, bool BKN>
 constexpr int wide_mi() {
-    if constexpr (EPI == MOE_EPI_SWIGLU_Q8 || EPI == MOE_EPI_SWIGLU_Q8_SAVE || EPI == MOE_EPI_SWIGLU_F32)
-        return WF4 ? 9 : 8;
-    else return 9;
+    return 9;
 }
 
 template <int EPI, bool P2, bool WF4, bool BKN>
