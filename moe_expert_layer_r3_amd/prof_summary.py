@@ -19,7 +19,17 @@
       WRITE_SIZE per dispatch, each scaled so that a plain 1 GiB device copy
       (the copy databases) reads as 1 GiB; written as JSON with the sha256 of
       the kernel's sources (comma-separated names under csrc/), which bench.py
-      checks before it reports the figure"""
+      checks before it reports the figure
+  python -m moe_expert_layer_r3_amd.prof_summary derived <results.db> [<results.db> ...] -- <name-part> <n> <pos>
+      per-launch averages of the counters collected over one or more runs (the
+      launches at position <pos> modulo <n> among kernels named like
+      <name-part>) and the figures derived from them: shader cycles per
+      launch (GRBM_GUI_ACTIVE counts on each of the 8 XCDs), MFMA busy share of
+      the SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES is 32 cycles per 16x16x128
+      MFMA, over 1024 SIMDs), wait shares of the wave cycles, texture
+      addresser busy share (256 TAs), L2 read latency, L1 -> L2 read bytes per
+      clock and CU (128-byte requests), VALU instructions per MFMA, LDS bank
+      conflict share"""
 
 import json
 import os
@@ -132,9 +142,53 @@ def traffic(fetch_db, write_db, cfetch_db, cwrite_db, part, n, pos, key, workloa
     print(json.dumps(rec, indent=1))
 
 
+def derived(paths, part, n, pos):
+    tot = {}
+    for path in paths:
+        db = sqlite3.connect(path)
+        rows = db.execute("select dispatch_id, counter_name, sum(value) from counters_collection "
+                          "where kernel_name like ? group by dispatch_id, counter_name order by dispatch_id",
+                          (f"%{part}%",)).fetchall()
+        disp = {}
+        for d, c, v in rows:
+            disp.setdefault(d, {})[c] = v
+        ds = sorted(disp)[pos::n]
+        for c in sorted({c for d in ds for c in disp[d]}):
+            vals = [disp[d][c] for d in ds if c in disp[d]]
+            tot.setdefault(c, []).extend(vals)
+    a = {c: sum(v) / len(v) for c, v in tot.items()}
+    for c in sorted(a):
+        print(f"  {c:32s} {a[c]:16.1f}   ({len(tot[c])} launches)")
+    g = a.get("GRBM_GUI_ACTIVE")
+    if g:
+        cyc = g / 8.0
+        print(f"  shader cycles per launch           {cyc:16.0f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in a:
+            print(f"  MFMA busy share of SIMD cycles     {a['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * cyc):16.3f}")
+        if "TA_TA_BUSY_sum" in a:
+            print(f"  texture addresser busy share       {a['TA_TA_BUSY_sum'] / (256 * cyc):16.3f}")
+        if "TCP_TCC_READ_REQ_sum" in a:
+            print(f"  L1 -> L2 read bytes / clock / CU   {a['TCP_TCC_READ_REQ_sum'] * 128 / 256 / cyc:16.1f}")
+    if "SQ_WAVE_CYCLES" in a:
+        for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS"):
+            if c in a:
+                print(f"  {c + ' / wave cycles':34s} {a[c] / a['SQ_WAVE_CYCLES']:16.3f}")
+    if "TCP_TCC_READ_REQ_LATENCY_sum" in a and a.get("TCP_TCC_READ_REQ_sum"):
+        print(f"  L2 read latency (cycles)           {a['TCP_TCC_READ_REQ_LATENCY_sum'] / a['TCP_TCC_READ_REQ_sum']:16.0f}")
+    if "TCP_TCC_WRITE_REQ_LATENCY_sum" in a and a.get("TCP_TCC_WRITE_REQ_sum"):
+        print(f"  L2 write latency (cycles)          {a['TCP_TCC_WRITE_REQ_LATENCY_sum'] / a['TCP_TCC_WRITE_REQ_sum']:16.0f}")
+    if a.get("SQ_INSTS_MFMA"):
+        print(f"  VALU instructions per MFMA         {a.get('SQ_INSTS_VALU', 0) / a['SQ_INSTS_MFMA']:16.2f}")
+    if a.get("SQ_LDS_IDX_ACTIVE"):
+        print(f"  LDS bank conflict share            {a.get('SQ_LDS_BANK_CONFLICT', 0) / a['SQ_LDS_IDX_ACTIVE']:16.3f}")
+
+
 if __name__ == "__main__":
     mode, path = sys.argv[1], sys.argv[2]
-    if mode == "traffic":
+    if mode == "derived":
+        k = sys.argv.index("--")
+        derived(sys.argv[2:k], sys.argv[k + 1], int(sys.argv[k + 2]), int(sys.argv[k + 3]))
+    elif mode == "traffic":
         a = sys.argv[2:]
         traffic(a[0], a[1], a[2], a[3], a[4], int(a[5]), int(a[6]), a[7], a[8], a[9], a[10])
     elif mode == "trace":
