@@ -163,12 +163,16 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         rSA[st] = b + sa_rd;
         rSB[st] = b + sb_rd;
     }
-    // output: byte offset in the tile of this lane's first 16 bytes of row
-    // wm*64 + mi*16 + l15 after the regrouping in finish() (columns wn*WN + 8*lg
-    // .. +7; the next 16 bytes of the lane, if any, are 64 bytes further)
+    // output: byte offset in the tile of the lane's first 16-byte store of
+    // subtile mi after the regrouping in finish().  128-column tiles: row
+    // wm*64 + mi*16 + l15, columns wn*WN + 8*lg .. +7.  256-column tiles (a
+    // wave's row is one 128-byte line): row wm*64 + mi*16 + (l15 & ~1), bytes
+    // 64*(l15 & 1) + 16*lg of the wave's 128; the second store is the next row.
     uint32_t o_off[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) o_off[mi] = (uint32_t)(((wm * 64 + mi * 16 + l15) * N + wn * WN) * 2 + 16 * lg);
+    for (int mi = 0; mi < 4; ++mi)
+        o_off[mi] = NI == 4 ? (uint32_t)(((wm * 64 + mi * 16 + (l15 & ~1)) * N + wn * WN) * 2 + 64 * (l15 & 1) + 16 * lg)
+                            : (uint32_t)(((wm * 64 + mi * 16 + l15) * N + wn * WN) * 2 + 16 * lg);
 
     // DMA lane offset: swizzled chunk of row l/8 of a contiguous 1 KB segment
     // (8 rows of one token block); both operands share it
@@ -393,7 +397,15 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     // chunk q = 4c + lg of the wave's row.  Exchanging the chunk-slot bit c0
     // with lane-group bit 1 (swap32) and then with lane-group bit 0 (swap16)
     // leaves slot 2h + s holding chunk 8h + 2lg + s: 8 consecutive columns per
-    // lane for each h.
+    // lane for each h, piece P_h = bytes 64h + 16lg of row l15.
+    // 256-column tiles: a store that fills whole 128-byte lines moves about
+    // 1.5x the bytes per clock of one that writes half lines (measured, 8 rows
+    // x 128 B against 16 rows x 64 B per instruction), so the lanes of rows 2u
+    // and 2u + 1 trade pieces (DPP quad permute [1, 0, 3, 2]): the even lane
+    // passes P_1 and takes its partner's P_0, the odd lane the reverse.  Store
+    // 0 then writes row 2u whole (P_0 from the even lanes, P_1 from the odd
+    // ones), store 1 row 2u + 1.
+    const bool odd_row = (lane & 1) != 0;
     auto finish = [&](uint16_t* dst) {
         flush();
         uint8_t* d = reinterpret_cast<uint8_t*>(dst);
@@ -413,9 +425,17 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
                 swap16(x[c], x[c + 1]);
                 swap16(y[c], y[c + 1]);
             }
+            if constexpr (NI == 4) {
+                const u32x4 p0 = {x[0], y[0], x[1], y[1]}, p1 = {x[2], y[2], x[3], y[3]};
+                const u32x4 snd = odd_row ? p0 : p1;
+                u32x4 r;
 #pragma unroll
-            for (int h = 0; h < NI / 2; ++h)
-                *reinterpret_cast<u32x4*>(d + o_off[mi] + h * 64) = u32x4{x[2 * h], y[2 * h], x[2 * h + 1], y[2 * h + 1]};
+                for (int c = 0; c < 4; ++c) r[c] = (uint32_t)__builtin_amdgcn_mov_dpp((int)snd[c], 0xB1, 0xF, 0xF, false);
+                *reinterpret_cast<u32x4*>(d + o_off[mi]) = odd_row ? r : p0;
+                *reinterpret_cast<u32x4*>(d + o_off[mi] + 2 * N) = odd_row ? p1 : r;
+            } else {
+                *reinterpret_cast<u32x4*>(d + o_off[mi]) = u32x4{x[0], y[0], x[1], y[1]};
+            }
         });
         clear();
     };
@@ -659,10 +679,12 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_wide_kernel(WgradArgs g) {
         const uint32_t l = (uint32_t)__lane_id();
         return ((l >> 3) * WBK) | ((((l & 7) ^ (l >> 3))) << 4);
     };
-    // epilogue: byte offset in the tile of this lane's 16 bytes of row
-    // wm*128 + l15 after the regrouping (columns wn*64 + 8*c0 .. +7; the
-    // lane's other 16 bytes are 64 further, each 16-row subtile 16*N*2)
-    const uint32_t o_lane0 = (uint32_t)(((wm * 128 + l15) * N + wn * 64 + 8 * c0) * 2);
+    // epilogue: byte offset in the tile of the lane's first store of a 16-row
+    // subtile after the regrouping: row wm*128 + (l15 & ~1), bytes
+    // 64*(l15 & 1) + 16*c0 of the wave's 128 (its second store is the next
+    // row; each 16-row subtile is 16*N*2 further)
+    const uint32_t o_lane0 = (uint32_t)(((wm * 128 + (l15 & ~1)) * N + wn * 64) * 2 + 64 * (l15 & 1) + 16 * c0);
+    const bool odd_row = (l15 & 1) != 0;
 
     struct Src {
         const uint8_t* a;  // the tile's first A row, first token block of the segment
@@ -853,7 +875,9 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_wide_kernel(WgradArgs g) {
             issue(sbase, 0, cs);
         }
         // bf16 from the accumulators; two cross-lane swaps per pair of
-        // n-subtiles give each lane 8 consecutive columns (one 16-byte store)
+        // n-subtiles give each lane 8 consecutive columns (one 16-byte store),
+        // then the lanes of rows 2u and 2u + 1 trade halves so that each store
+        // writes whole 128-byte lines, as in wgrad_fp8_kernel's epilogue
         uint8_t* d = reinterpret_cast<uint8_t*>(dst);
         uint32_t o_lane = o_lane0;  // 32-bit lane offset; the row block is a uniform base
         pin(o_lane);
@@ -874,9 +898,13 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_wide_kernel(WgradArgs g) {
                 swap16(x[ni], x[ni + 1]);
                 swap16(y[ni], y[ni + 1]);
             }
+            const u32x4 p0 = {x[0], y[0], x[1], y[1]}, p1 = {x[2], y[2], x[3], y[3]};
+            const u32x4 snd = odd_row ? p0 : p1;
+            u32x4 r;
 #pragma unroll
-            for (int h = 0; h < NI / 2; ++h)
-                *reinterpret_cast<u32x4*>(drow + o_lane + 64 * h) = u32x4{x[2 * h], y[2 * h], x[2 * h + 1], y[2 * h + 1]};
+            for (int c = 0; c < 4; ++c) r[c] = (uint32_t)__builtin_amdgcn_mov_dpp((int)snd[c], 0xB1, 0xF, 0xF, false);
+            *reinterpret_cast<u32x4*>(drow + o_lane) = odd_row ? r : p0;
+            *reinterpret_cast<u32x4*>(drow + o_lane + 2 * N) = odd_row ? p1 : r;
         }
         stores_out = true;
     }
