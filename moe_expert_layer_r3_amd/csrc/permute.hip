@@ -9,7 +9,10 @@
 //   3. scatter : per chunk, rank every pair among the earlier pairs of its
 //                expert (wave ballots, in pair order) and write row_pair /
 //                pair_row -- deterministic, no order-dependent atomics; the
-//                per-expert row bases of the chunk are staged in LDS first
+//                per-expert row bases of the chunk are staged in LDS first.
+//                When the chunk counts are few (nchunk * L <= SCAN_FOLD), step
+//                2 runs inside this kernel instead: every block reads all
+//                chunk counts and forms its own bases and the offsets.
 //   4. gather  : one workgroup per token: its local rows are read once as
 //                uniform values, the row of x is read once, quantised to
 //                1x128 e4m3 once, and written to each of its local rows.
@@ -28,18 +31,41 @@ constexpr int PWAVES = PBLOCK / 64;
 constexpr int PER_WAVE = PCHUNK / PWAVES;  // 256 consecutive pairs per wave
 constexpr int MAXL = 1024;
 
+constexpr int SCAN_FOLD = 16384;   // chunk counts (int32) a scatter block reads to fold the scan in
+
+// Lanes of the wave whose local expert id equals this lane's (le >= 0): one
+// ballot per bit of the id (nb = bits of L - 1) instead of one per distinct id.
+// Lanes with le < 0 are in no mask.
+__device__ __forceinline__ uint64_t same_expert(int le, int nb) {
+    uint64_t m = __ballot(le >= 0);
+    for (int b = 0; b < nb; ++b) {
+        const bool bit = (le >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    return m;
+}
+__device__ __forceinline__ int expert_bits(int L) { return L > 1 ? 32 - __clz(L - 1) : 0; }
+
 __global__ __launch_bounds__(PBLOCK) void perm_hist_kernel(const int32_t* __restrict__ ids, int64_t P, int e0,
                                                            int L, int32_t* __restrict__ chunk_counts) {
     __shared__ int cnt[MAXL];
     for (int e = threadIdx.x; e < L; e += PBLOCK) cnt[e] = 0;
     __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int nb = expert_bits(L);
     const int64_t base = (int64_t)blockIdx.x * PCHUNK;
     for (int i = threadIdx.x; i < PCHUNK; i += PBLOCK) {
-        int64_t p = base + i;
+        const int64_t p = base + i;
+        int le = -1;
         if (p < P) {
-            int le = ids[p] - e0;
-            if (le >= 0 && le < L) atomicAdd(&cnt[le], 1);
+            le = ids[p] - e0;
+            if (le < 0 || le >= L) le = -1;
         }
+        // the first lane of each expert adds the wave's count (distinct addresses)
+        const uint64_t m = same_expert(le, nb);
+        if (le >= 0 && (m & lt_mask) == 0) atomicAdd(&cnt[le], (int)__popcll(m));
     }
     __syncthreads();
     for (int e = threadIdx.x; e < L; e += PBLOCK) chunk_counts[(int64_t)blockIdx.x * L + e] = cnt[e];
@@ -106,26 +132,31 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
     }
 }
 
+// FOLD: chunk_counts holds the raw counts of every chunk (nchunk * L <=
+// SCAN_FOLD); each block forms its chunk's bases and the 128-aligned offsets
+// itself, and block 0 writes counts, offsets, the padding rows and the row-cap
+// flag (what perm_scan_kernel does otherwise).  Without FOLD, chunk_counts
+// holds the scan's exclusive chunk prefixes.
+template <bool FOLD>
 __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __restrict__ ids, int64_t P, int e0,
-                                                              int L, int64_t row_cap,
-                                                              const int32_t* __restrict__ chunk_base,
-                                                              const int32_t* __restrict__ offsets,
+                                                              int L, int64_t row_cap, int nchunk,
+                                                              const int32_t* __restrict__ chunk_counts,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ row_pair,
-                                                              int32_t* __restrict__ pair_row) {
+                                                              int32_t* __restrict__ pair_row,
+                                                              int32_t* __restrict__ status) {
     // run[w][e]: pairs of expert e seen so far by wave w (first pass: totals);
     // base[e]: first row of this chunk's pairs of expert e
     __shared__ int run[PWAVES][MAXL];
     __shared__ int64_t base[MAXL];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int e = threadIdx.x; e < L; e += PBLOCK) {
-        for (int w = 0; w < PWAVES; ++w) run[w][e] = 0;
-        base[e] = (int64_t)offsets[e] + chunk_base[(int64_t)blockIdx.x * L + e];
-    }
-    __syncthreads();
     const int64_t wbase = (int64_t)blockIdx.x * PCHUNK + (int64_t)wave * PER_WAVE;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int nb = expert_bits(L);
 
-    // the wave's local expert ids, loaded once for both passes
+    // the wave's local expert ids, loaded once for both passes (issued before
+    // the bases are formed)
     int les[PER_WAVE / 64];
 #pragma unroll
     for (int it = 0; it < PER_WAVE / 64; ++it) {
@@ -137,19 +168,79 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
         }
         les[it] = le;
     }
-    // pass 1: per-wave totals per expert
+    for (int e = threadIdx.x; e < L; e += PBLOCK)
+        for (int w = 0; w < PWAVES; ++w) run[w][e] = 0;
+    if constexpr (FOLD) {
+        // per expert: its pairs in the chunks before this one (pre) and in all
+        // chunks (tot); thread (cs, e) sums chunks cs, cs + cstep, ...
+        __shared__ int pre[MAXL], tot[MAXL];
+        __shared__ int64_t wsum[PWAVES];
+        for (int e = threadIdx.x; e < L; e += PBLOCK) {
+            pre[e] = 0;
+            tot[e] = 0;
+        }
+        __syncthreads();
+        const int cstep = L <= PBLOCK ? PBLOCK / L : 1;
+        for (int e0t = 0; e0t < L; e0t += PBLOCK) {
+            const int e = e0t + (L <= PBLOCK ? (int)threadIdx.x % L : (int)threadIdx.x);
+            const int cs = L <= PBLOCK ? (int)threadIdx.x / L : 0;
+            if (e < L && cs < cstep) {
+                int a = 0, t = 0;
+                for (int c = cs; c < nchunk; c += cstep) {
+                    const int v = chunk_counts[(int64_t)c * L + e];
+                    t += v;
+                    a += c < (int)blockIdx.x ? v : 0;
+                }
+                atomicAdd(&pre[e], a);
+                atomicAdd(&tot[e], t);
+            }
+        }
+        __syncthreads();
+        // inclusive scan over experts of the 128-aligned segment sizes: each
+        // thread sums its run of consecutive experts, then a block scan
+        const int per = (L + PBLOCK - 1) / PBLOCK;
+        const int ea = threadIdx.x * per, eb = min(L, ea + per);
+        int64_t own = 0;
+        for (int e = ea; e < eb; ++e)
+            own += ((int64_t)tot[e] + MOE_ROW_ALIGN - 1) / MOE_ROW_ALIGN * MOE_ROW_ALIGN;
+        int64_t x = own;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        for (int w = 0; w < wave; ++w) x += wsum[w];
+        int64_t start = x - own;  // first row of expert ea
+        for (int e = ea; e < eb; ++e) {
+            const int c = tot[e];
+            const int64_t end = start + ((int64_t)c + MOE_ROW_ALIGN - 1) / MOE_ROW_ALIGN * MOE_ROW_ALIGN;
+            base[e] = start + pre[e];
+            if (blockIdx.x == 0) {
+                counts[e] = c;
+                offsets[e + 1] = (int32_t)(end > 0x7FFFFFFF ? 0x7FFFFFFF : end);
+                if (e == 0) offsets[0] = 0;
+                if (e == L - 1 && end > row_cap && status) atomicOr(status, MOE_FLAG_ROW_CAP);
+                for (int64_t r = start + c; r < end && r < row_cap; ++r) row_pair[r] = -1;  // < 128 rows
+            }
+            start = end;
+        }
+    } else {
+        for (int e = threadIdx.x; e < L; e += PBLOCK)
+            base[e] = (int64_t)offsets[e] + chunk_counts[(int64_t)blockIdx.x * L + e];
+    }
+    __syncthreads();
+
+    // pass 1: per-wave totals per expert; the first lane of each expert adds
+    // the count (distinct addresses within an instruction)
+    uint64_t mk[PER_WAVE / 64];
 #pragma unroll
     for (int it = 0; it < PER_WAVE / 64; ++it) {
         const int le = les[it];
-        uint64_t active = __ballot(le >= 0);
-        while (active) {
-            int leader = __ffsll((unsigned long long)active) - 1;
-            int e = __builtin_amdgcn_readlane(le, leader);  // leader is wave-uniform: no LDS trip
-            uint64_t m = __ballot(le == e) & active;
-            // LDS add with no return value: the loop never waits on LDS
-            if (lane == leader) atomicAdd(&run[wave][e], (int)__popcll(m));
-            active &= ~m;
-        }
+        mk[it] = same_expert(le, nb);
+        if (le >= 0 && (mk[it] & lt_mask) == 0) run[wave][le] += (int)__popcll(mk[it]);
+        __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
     // exclusive prefix over waves, per expert
@@ -162,24 +253,22 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
         }
     }
     __syncthreads();
-    // pass 2: ranks in pair order, write rows
+    // pass 2: ranks in pair order (earlier waves, earlier iterations, earlier
+    // lanes), write rows
 #pragma unroll
     for (int it = 0; it < PER_WAVE / 64; ++it) {
         const int64_t p = wbase + it * 64 + lane;
         const int le = les[it];
+        const uint64_t m = mk[it];
         int64_t row = -1;
-        uint64_t active = __ballot(le >= 0);
-        while (active) {
-            int leader = __ffsll((unsigned long long)active) - 1;
-            int e = __builtin_amdgcn_readlane(le, leader);  // leader is wave-uniform: no LDS trip
-            uint64_t m = __ballot(le == e) & active;
-            int before = run[wave][e];
-            if (le == e) row = base[e] + before + __popcll(m & lt_mask);
-            __builtin_amdgcn_wave_barrier();
-            if (lane == leader) run[wave][e] = before + __popcll(m);
-            __builtin_amdgcn_wave_barrier();
-            active &= ~m;
+        int before = 0;
+        if (le >= 0) {
+            before = run[wave][le];
+            row = base[le] + before + __popcll(m & lt_mask);
         }
+        __builtin_amdgcn_wave_barrier();
+        if (le >= 0 && (m & lt_mask) == 0) run[wave][le] = before + (int)__popcll(m);
+        __builtin_amdgcn_wave_barrier();
         if (p < P) {
             if (row >= row_cap) row = -1;
             pair_row[p] = (int32_t)row;
@@ -326,13 +415,19 @@ static int permute_launch(const int32_t* ids, int64_t T, int32_t k, int32_t e0, 
         perm_hist_kernel<<<dim3(nchunk), dim3(PBLOCK), 0, stream>>>(ids, P, e0, L, chunk);
         MOE_LAUNCH_CHECK("perm_hist_kernel");
     }
-    perm_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(chunk, nchunk, L, row_cap, counts, offsets, row_pair,
-                                                         dev_status);
-    MOE_LAUNCH_CHECK("perm_scan_kernel");
-    if (nchunk > 0) {
-        perm_scatter_kernel<<<dim3(nchunk), dim3(PBLOCK), 0, stream>>>(ids, P, e0, L, row_cap, chunk, offsets,
-                                                                       row_pair, pair_row);
+    if (nchunk > 0 && (int64_t)nchunk * L <= SCAN_FOLD) {
+        perm_scatter_kernel<true><<<dim3(nchunk), dim3(PBLOCK), 0, stream>>>(
+            ids, P, e0, L, row_cap, nchunk, chunk, counts, offsets, row_pair, pair_row, dev_status);
         MOE_LAUNCH_CHECK("perm_scatter_kernel");
+    } else {
+        perm_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(chunk, nchunk, L, row_cap, counts, offsets, row_pair,
+                                                             dev_status);
+        MOE_LAUNCH_CHECK("perm_scan_kernel");
+        if (nchunk > 0) {
+            perm_scatter_kernel<false><<<dim3(nchunk), dim3(PBLOCK), 0, stream>>>(
+                ids, P, e0, L, row_cap, nchunk, chunk, counts, offsets, row_pair, pair_row, dev_status);
+            MOE_LAUNCH_CHECK("perm_scatter_kernel");
+        }
     }
     if (x && T > 0) {
         auto go = [&](auto kern) {

@@ -187,8 +187,11 @@ def _check_permute(ids, e0, L, x=None):
     return res
 
 
+# the last case has more chunk counts (157 chunks x 1000 experts) than a
+# scatter block folds in, so it takes the separate scan kernel
 @pytest.mark.parametrize("T,E,k,e0,L", [(8192, 256, 8, 0, 32), (5000, 256, 8, 96, 32), (1, 8, 2, 0, 8),
-                                        (4097, 16, 3, 4, 8), (300, 8, 2, 0, 8), (20000, 512, 4, 500, 12)])
+                                        (4097, 16, 3, 4, 8), (300, 8, 2, 0, 8), (20000, 512, 4, 500, 12),
+                                        (20000, 1024, 8, 0, 1000)])
 def test_permute_topk_routes(T, E, k, e0, L):
     rng = np.random.default_rng(T + L)
     lg = rng.standard_normal((T, E)).astype(np.float32)
