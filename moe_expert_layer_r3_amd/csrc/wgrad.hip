@@ -60,7 +60,54 @@ struct WgradArgs {
     int nfast;  // 1: n-tiles vary fastest in the tile order (B is the smaller operand)
     int gf;     // fast-index tiles per group (divides that index's tile count)
     uint16_t* dW;
+    int kb_min, kb_max;  // this launch takes the experts with kb_min..kb_max token blocks
+    int zfill;           // 1: this launch also writes dW = 0 for experts without rows
 };
+
+// Experts whose segment holds kb_min .. kb_max token blocks, in order (wave
+// 0): tab[0] = their count, tab_x[i] = e | nkb << 10, tab_lo[i] = first row.
+__device__ __forceinline__ void build_expert_table(const WgradArgs& g, int64_t rcap, int wave, int lane, int* tab,
+                                                   int* tab_x, int* tab_lo) {
+    if (wave != 0) return;
+    int cnt = 0;
+    for (int c = 0; c < g.L; c += 64) {
+        const int e = c + lane;
+        int64_t lo = 0, hi = 0;
+        if (e < g.L) {
+            lo = g.offsets[e];
+            hi = g.offsets[e + 1];
+            lo = lo < 0 ? 0 : (lo > rcap ? rcap : lo);
+            hi = hi > rcap ? rcap : hi;
+        }
+        const int nkb = hi > lo ? (int)((hi - lo) / WBK) : 0;
+        const bool take = nkb > 0 && nkb >= g.kb_min && nkb <= g.kb_max;
+        const uint64_t m = __ballot(take);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (take) {
+            tab_x[cnt + below] = e | (nkb << 10);
+            tab_lo[cnt + below] = (int)lo;
+        }
+        cnt += __popcll(m);
+    }
+    if (lane == 0) tab[0] = cnt;
+}
+
+// dW = 0 for the experts without a token block (when this launch owns the fill)
+__device__ __forceinline__ void zero_fill_empty(const WgradArgs& g, int tid) {
+    if (!g.zfill) return;
+    const int64_t rcap = g.row_cap;
+    const int64_t chunks = (int64_t)g.M * g.N / 8;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int e = 0; e < g.L; ++e) {
+        int64_t lo = g.offsets[e], hi = g.offsets[e + 1];
+        lo = lo < 0 ? 0 : (lo > rcap ? rcap : lo);
+        hi = hi > rcap ? rcap : hi;
+        if (hi - lo >= WBK) continue;
+        uint16_t* d = g.dW + (int64_t)e * g.M * g.N;
+        for (int64_t c = (int64_t)blockIdx.x * WTHREADS + tid; c < chunks; c += (int64_t)gridDim.x * WTHREADS)
+            *reinterpret_cast<u32x4*>(d + c * 8) = z;
+    }
+}
 
 template <int BN>
 struct WgradSmem {
@@ -113,29 +160,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
     const int lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-    // experts with at least one token block, in order
-    if (wave == 0) {
-        int cnt = 0;
-        for (int c = 0; c < g.L; c += 64) {
-            const int e = c + lane;
-            int64_t lo = 0, hi = 0;
-            if (e < g.L) {
-                lo = g.offsets[e];
-                hi = g.offsets[e + 1];
-                lo = lo < 0 ? 0 : (lo > rcap ? rcap : lo);
-                hi = hi > rcap ? rcap : hi;
-            }
-            const int nkb = hi > lo ? (int)((hi - lo) / WBK) : 0;
-            const uint64_t m = __ballot(nkb > 0);
-            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (nkb > 0) {
-                tab_x[cnt + below] = e | (nkb << 10);
-                tab_lo[cnt + below] = (int)lo;
-            }
-            cnt += __popcll(m);
-        }
-        if (lane == 0) tab[0] = cnt;
-    }
+    // experts of this launch (token block counts kb_min..kb_max), in order
+    build_expert_table(g, rcap, wave, lane, tab, tab_x, tab_lo);
     __syncthreads();
     const int Lne = __builtin_amdgcn_readfirstlane(tab[0]);
     const int total = Lne * TPE;  // tiles with K work, expert-major, then n-tile, m-tile fastest
@@ -535,21 +561,363 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
         }
     }
 
-    // experts without rows: dW = 0
-    {
-        const int64_t chunks = (int64_t)M * N / 8;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        int j = 0;
-        for (int e = 0; e < g.L; ++e) {
-            if (j < Lne && (__builtin_amdgcn_readfirstlane(tab_x[j]) & 1023) == e) {
-                ++j;
-                continue;
+    zero_fill_empty(g, tid);
+}
+
+
+// ---------------------------------------------------------------- A resident
+//
+// fp32 scales on 128 x 256 tiles for experts with at most ARES_KB token
+// blocks.  A unit of work is (expert, m-tile): the unit's A operand, all of
+// the expert's token blocks (16 KB of codes and 512 B of row scales each), is
+// moved into LDS once and stays there while the unit sweeps its n-tiles; only
+// B streams, through a two-stage ring of 33 KB stages.  A K step then moves
+// 32 KB instead of 48, and the 32 workgroups of an XCD, running m-tiles of
+// one expert, read the same B tiles at about the same time.  The K step, the
+// ping-pong groups, the epilogue and the waits are those of wgrad_fp8_kernel
+// with a ring two stages deep (the DMA of a step goes out one step ahead).
+// At the first step of a unit both groups wait at one more barrier while the
+// DMA waves replace the A region: every read of the old one ends before the
+// step's first barrier.
+constexpr int ARES_KB = 5;
+struct AresSmem {
+    static constexpr int A_BLK = WBM * WBK;       // 16 KB of codes per token block
+    static constexpr int SA_BLK = WBM * 4;        // its 128 row scales
+    static constexpr int SA0 = ARES_KB * A_BLK;   // the scales follow the codes
+    static constexpr int RING = SA0 + ARES_KB * SA_BLK;
+    static constexpr int B_BYTES = 256 * WBK;
+    static constexpr int SB_BYTES = 256 * 4;
+    static constexpr int STAGE = B_BYTES + SB_BYTES;
+    static constexpr int TAB = RING + 2 * STAGE;  // experts: count, packed id|nkb, lo
+    static constexpr int TOTAL = TAB + (1 + 2 * WMAXL) * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS");
+};
+
+__global__ __launch_bounds__(WTHREADS, 1) void wgrad_ares_kernel(WgradArgs g) {
+    using SM = AresSmem;
+    constexpr int BN = 256, WN = 64, NI = 4;
+    constexpr int ASEG = WBM / 64;   // 1 KB A segments per wave share and block
+    constexpr int BSEG = BN / 64;    // 1 KB B segments per wave share and stage
+    constexpr int SROWS = BN / 8;    // B scales per wave share
+    constexpr int NLD2 = 2 * (BSEG + 1);  // B DMA instructions of a DMA wave per stage
+    constexpr int NST = 2 * NI;      // 16-byte stores per wave per tile
+    static_assert(NLD2 + NST < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
+    int* const tab = reinterpret_cast<int*>(smem + SM::TAB);
+    int* const tab_x = tab + 1;           // e | nkb << 10
+    int* const tab_lo = tab + 1 + WMAXL;  // first row of the segment
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int64_t rcap = g.row_cap;
+    const int M = g.M, N = g.N;
+    const int MT = M / WBM, NT = N / BN;
+    const int G = gridDim.x;
+    const int lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+
+    build_expert_table(g, rcap, wave, lane, tab, tab_x, tab_lo);
+    __syncthreads();
+    const int Lne = __builtin_amdgcn_readfirstlane(tab[0]);
+    const int units = Lne * MT;  // (expert, m-tile), expert-major
+
+    // fragment reads (lane l: row l & 15 of a fragment, K chunks g and g + 4
+    // of the 128-byte block, g = l >> 4; swizzled chunk c ^ (row & 7)); A from
+    // block kr of the resident region, B from a ring stage
+    const int l15 = lane & 15, l7 = lane & 7, lg = lane >> 4;
+    const uint32_t a_rd0 = sbase + (wm * 64 + l15) * 128 + ((lg ^ l7) << 4);
+    const uint32_t a_rd1 = sbase + (wm * 64 + l15) * 128 + (((lg + 4) ^ l7) << 4);
+    // A scales: the 16 bytes at slot wm*64 + 4*l15 of a block hold rows
+    // wm*64 + mi*16 + l15 (mi = 0..3); B scales: 4 consecutive columns per read
+    const uint32_t sa_rd = sbase + SM::SA0 + (wm * 64 + l15 * 4) * 4;
+    uint32_t rB0[2], rB1[2], rSB[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const uint32_t b = sbase + SM::RING + (uint32_t)(st * SM::STAGE);
+        rB0[st] = b + (wn * WN + l15) * 128 + ((lg ^ l7) << 4);
+        rB1[st] = b + (wn * WN + l15) * 128 + (((lg + 4) ^ l7) << 4);
+        rSB[st] = b + SM::B_BYTES + (wn * WN + 4 * lg) * 4;
+    }
+    // output: the lane's first 16-byte store of subtile mi (whole 128-byte
+    // lines, as in wgrad_fp8_kernel): row wm*64 + mi*16 + (l15 & ~1), bytes
+    // 64*(l15 & 1) + 16*lg of the wave's 128; the second store is the next row
+    uint32_t o_off[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+        o_off[mi] = (uint32_t)(((wm * 64 + mi * 16 + (l15 & ~1)) * N + wn * WN) * 2 + 64 * (l15 & 1) + 16 * lg);
+    const int lr = lane >> 3;
+    const uint32_t seg_off = (uint32_t)(lr * WBK + (((lane & 7) ^ lr) << 4));
+    const uint32_t sa_off = (uint32_t)(((wave >> 2) * 64 + (lane & 3) * 16 + (wave & 3) * 4 + ((lane & 15) >> 2)) * 4);
+    const uint32_t sb_off = (uint32_t)((lane & (SROWS - 1)) * 4);
+
+    // step cursor: unit u (this workgroup's units are lb, lb + G, ...), n-tile
+    // nt, step i of the tile's K loop; the K loop starts at block rot = m-tile
+    // mod nkb, so that the m-tiles an XCD runs side by side do not request
+    // the same lines of their shared B tile at once (only the order of the
+    // fp32 block sums changes)
+    struct Cur {
+        int u, nt, i, nkb, rot, mt;
+        int64_t blk0;  // first token block of the expert's segment
+        int e;
+    };
+    // (the divisions run once per unit; their results are wave-uniform and
+    // kept in scalar registers)
+    auto unit_at = [&](Cur& c, int u) {
+        c.u = u;
+        c.nt = 0;
+        c.i = 0;
+        if (u >= units) return;
+        const int j = __builtin_amdgcn_readfirstlane(u / MT);
+        c.mt = __builtin_amdgcn_readfirstlane(u - j * MT);
+        const int x = __builtin_amdgcn_readfirstlane(tab_x[j]);
+        c.e = x & 1023;
+        c.nkb = x >> 10;
+        c.rot = __builtin_amdgcn_readfirstlane(c.mt % c.nkb);
+        c.blk0 = __builtin_amdgcn_readfirstlane(tab_lo[j]) / WBK;
+    };
+    // advance one K step; true when the step entered a new unit
+    auto advance = [&](Cur& c) -> bool {
+        if (++c.i < c.nkb) return false;
+        c.i = 0;
+        if (++c.nt < NT) return false;
+        unit_at(c, c.u + G);
+        return true;
+    };
+    auto kr_of = [&](const Cur& c) { int k = c.i + c.rot; return k >= c.nkb ? k - c.nkb : k; };
+
+    const bool dma_wave = wave < 4;
+    // the unit's A blocks into the resident region (DMA waves: their own share
+    // and that of wave + 4, as in wgrad_fp8_kernel)
+    auto issue_a = [&](const Cur& c) {
+        if (!dma_wave) return;
+        const uint8_t* a = g.aT + ((c.blk0 * M + (int64_t)c.mt * WBM + wave * ASEG * 8) * WBK);
+        const float* sa = g.aT_s + c.blk0 * M + (int64_t)c.mt * WBM;
+        for (int kb = 0; kb < c.nkb; ++kb) {
+            const uint32_t sA = sbase + (uint32_t)(kb * SM::A_BLK), sSA = sbase + SM::SA0 + (uint32_t)(kb * SM::SA_BLK);
+            static_for<0, 2>([&](auto hc) {
+                constexpr int h = decltype(hc)::value;
+                const int w = wave + 4 * h;
+#pragma unroll
+                for (int i = 0; i < ASEG; ++i)
+                    dma16s(a + (int64_t)kb * M * WBK + (h * 4 * ASEG * 8) * WBK + i * 1024, seg_off,
+                           sA + (w * ASEG + i) * 1024);
+                if (lane < 16) dma4s(sa + (int64_t)kb * M, sa_off + h * 64 * 4, sSA + w * 64);
+            });
+        }
+    };
+    // B block kr of (unit, n-tile) into ring stage st
+    auto issue_b = [&](int st, const Cur& c) {
+        if (!dma_wave) return;
+        const int kr = kr_of(c);
+        const uint8_t* b = g.bT + (((c.blk0 + kr) * N + (int64_t)c.nt * BN + wave * BSEG * 8) * WBK);
+        const float* sb = g.bT_s + (c.blk0 + kr) * N + (int64_t)c.nt * BN + wave * SROWS;
+        const uint32_t sB = sbase + SM::RING + (uint32_t)(st * SM::STAGE), sSB = sB + SM::B_BYTES;
+        static_for<0, 2>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const int w = wave + 4 * h;
+#pragma unroll
+            for (int i = 0; i < BSEG; ++i)
+                dma16s(b + (h * 4 * BSEG * 8) * WBK + i * 1024, seg_off, sB + (w * BSEG + i) * 1024);
+            if (lane < SROWS) dma4s(sb + h * 4 * SROWS, sb_off, sSB + w * SROWS * 4);
+        });
+    };
+    auto dst_of = [&](const Cur& c) -> uint16_t* {
+        return g.dW + (int64_t)c.e * M * N + (int64_t)c.mt * WBM * N + (int64_t)c.nt * BN;
+    };
+
+    const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+    v4f acc[4][NI];
+    v8i af[4], bfr[NI];
+    float sa[4];  // A scales of the loaded block (rows of this lane)
+    v4f sb[NI];   // B scales of the loaded block (4 columns per n-subtile)
+    v4f ring[4];  // raw partials awaiting their rescale
+    auto clear = [&]() {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = zero4;
+            ring[mi] = zero4;
+        }
+    };
+    clear();
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) sa[mi] = 0.f;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) sb[ni] = zero4;
+    auto flush = [&]() {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) acc[mi][NI - 1] += ring[mi] * (sa[mi] * sb[NI - 1]);
+    };
+    auto load = [&](auto st_c, int kr) {
+        constexpr int st = decltype(st_c)::value;
+        uint32_t pa0 = a_rd0 + (uint32_t)(kr * SM::A_BLK), pa1 = a_rd1 + (uint32_t)(kr * SM::A_BLK);
+        uint32_t psa = sa_rd + (uint32_t)(kr * SM::SA_BLK);
+        pin(pa0);
+        pin(pa1);
+        pin(psa);
+        pin(rB0[st]);
+        pin(rB1[st]);
+        pin(rSB[st]);
+        const uint32_t pb0 = rB0[st], pb1 = rB1[st], psb = rSB[st];
+        const u32x4 sa4 = lds16<0>(psa);
+        u32x4 sbn[NI];
+        static_for<0, NI>([&](auto nc) {
+            constexpr int ni = decltype(nc)::value;
+            sbn[ni] = lds16<ni * 64>(psb);
+        });
+        static_for<0, 4>([&](auto ic) {
+            constexpr int mi = decltype(ic)::value;
+            af[mi] = join8(lds16<mi * 2048>(pa0), lds16<mi * 2048>(pa1));
+        });
+        static_for<0, NI>([&](auto nc) {
+            constexpr int ni = decltype(nc)::value;
+            bfr[ni] = join8(lds16<ni * 2048>(pb0), lds16<ni * 2048>(pb1));
+        });
+        flush();  // with the previous block's scales
+        const uint32_t sav[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) sa[mi] = __uint_as_float(sav[mi]);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) sb[ni] = __builtin_bit_cast(v4f, sbn[ni]);
+        wait_lgkm0();
+    };
+    auto compute = [&]() {
+        static_for<0, 4 * NI>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int ni = j / 4, mi = j % 4;
+            if constexpr (j >= 4) acc[mi][ni - 1] += ring[mi] * (sa[mi] * sb[ni - 1]);
+            ring[mi] = mfma16x16x128(bfr[ni], af[mi]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    const bool odd_row = (lane & 1) != 0;
+    auto finish = [&](uint16_t* dst) {
+        flush();
+        uint8_t* d = reinterpret_cast<uint8_t*>(dst);
+        static_for<0, 4>([&](auto ic) {
+            constexpr int mi = decltype(ic)::value;
+            uint32_t x[NI], y[NI];
+#pragma unroll
+            for (int c = 0; c < NI; ++c) {
+                const v4f a = acc[mi][c];
+                x[c] = cvt_bf16x2(a.x, a.y);
+                y[c] = cvt_bf16x2(a.z, a.w);
             }
-            uint16_t* d = g.dW + (int64_t)e * M * N;
-            for (int64_t c = (int64_t)blockIdx.x * WTHREADS + tid; c < chunks; c += (int64_t)G * WTHREADS)
-                *reinterpret_cast<u32x4*>(d + c * 8) = z;
+#pragma unroll
+            for (int c = 0; c < NI; c += 2) {
+                swap32(x[c], x[c + 1]);
+                swap32(y[c], y[c + 1]);
+                swap16(x[c], x[c + 1]);
+                swap16(y[c], y[c + 1]);
+            }
+            const u32x4 p0 = {x[0], y[0], x[1], y[1]}, p1 = {x[2], y[2], x[3], y[3]};
+            const u32x4 snd = odd_row ? p0 : p1;
+            u32x4 r;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) r[c] = (uint32_t)__builtin_amdgcn_mov_dpp((int)snd[c], 0xB1, 0xF, 0xF, false);
+            *reinterpret_cast<u32x4*>(d + o_off[mi]) = odd_row ? r : p0;
+            *reinterpret_cast<u32x4*>(d + o_off[mi] + 2 * N) = odd_row ? p1 : r;
+        });
+        clear();
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    Cur ic;  // issue cursor: the step after the one being loaded
+    unit_at(ic, lb);
+    if (ic.u < units) {
+        // prologue: the first unit's A and step 0's B (stage 0)
+        issue_a(ic);
+        issue_b(0, ic);
+        advance(ic);
+        // DMA waves: stores issued after the B DMA the next wait is for
+        // (group 0: its finish one step back)
+        int yng = 0;
+        auto wait_stage = [&]() {
+            if (!dma_wave) return;
+            if (yng == 0) wait_vmcnt<0>();
+            else wait_vmcnt<NST>();
+        };
+        // the B of the next step goes out (DMA waves), into stage st
+        auto issue_next = [&](int st) -> bool {
+            if (ic.u >= units) return false;
+            issue_b(st, ic);
+            advance(ic);
+            return true;
+        };
+        Cur lc;  // the step being loaded
+        unit_at(lc, lb);
+        Cur cc = lc;  // the step being computed
+        // one step; false after the last one
+        if (wave < 4) {
+            // group 0: wait, (A of a new unit,) issue, load | compute (and store a finished tile)
+            auto step = [&](auto st_c, bool sw) -> bool {
+                constexpr int st = decltype(st_c)::value;
+                wait_stage();
+                phase_barrier();
+                if (sw) {
+                    issue_a(lc);
+                    wait_vmcnt<0>();
+                    phase_barrier();
+                }
+                issue_next(st ^ 1);
+                load(st_c, kr_of(lc));
+                phase_barrier();
+                compute();
+                const bool last_k = cc.i + 1 == cc.nkb;
+                uint16_t* dst = dst_of(cc);
+                advance(cc);
+                yng = 0;
+                if (last_k) {
+                    finish(dst);
+                    yng = NST;
+                }
+                return cc.u < units;
+            };
+            bool more = true, sw = false;
+            while (more) {
+                more = step(S0{}, sw);
+                sw = advance(lc);
+                if (more) {
+                    more = step(S1{}, sw);
+                    sw = advance(lc);
+                }
+            }
+        } else {
+            // group 1, half a step behind: (A of a new unit,) compute the
+            // previous block (and store a finished tile) | load
+            // (one loop exit: the live-out fragments and accumulators keep
+            // their registers)
+            bool sw = false;
+            auto step = [&](auto st_c, auto prev_c) -> bool {
+                phase_barrier();
+                if (sw) phase_barrier();
+                if constexpr (decltype(prev_c)::value) {
+                    compute();
+                    const bool last_k = cc.i + 1 == cc.nkb;
+                    uint16_t* dst = dst_of(cc);
+                    advance(cc);
+                    if (last_k) finish(dst);
+                }
+                phase_barrier();
+                load(st_c, kr_of(lc));
+                sw = advance(lc);
+                return lc.u < units;
+            };
+            using NoPrev = std::false_type;
+            using Prev = std::true_type;
+            bool more = step(S0{}, NoPrev{});
+            while (more) {
+                more = step(S1{}, Prev{});
+                if (more) more = step(S0{}, Prev{});
+            }
+            compute();  // the last block, loaded by the last step
+            finish(dst_of(cc));
         }
     }
+    zero_fill_empty(g, tid);
 }
 
 
@@ -603,29 +971,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_wide_kernel(WgradArgs g) {
     const int lb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-    // experts with at least one token block, in order
-    if (wave == 0) {
-        int cnt = 0;
-        for (int c = 0; c < g.L; c += 64) {
-            const int e = c + lane;
-            int64_t lo = 0, hi = 0;
-            if (e < g.L) {
-                lo = g.offsets[e];
-                hi = g.offsets[e + 1];
-                lo = lo < 0 ? 0 : (lo > rcap ? rcap : lo);
-                hi = hi > rcap ? rcap : hi;
-            }
-            const int nkb = hi > lo ? (int)((hi - lo) / WBK) : 0;
-            const uint64_t m = __ballot(nkb > 0);
-            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (nkb > 0) {
-                tab_x[cnt + below] = e | (nkb << 10);
-                tab_lo[cnt + below] = (int)lo;
-            }
-            cnt += __popcll(m);
-        }
-        if (lane == 0) tab[0] = cnt;
-    }
+    // experts of this launch (token block counts kb_min..kb_max), in order
+    build_expert_table(g, rcap, wave, lane, tab, tab_x, tab_lo);
     __syncthreads();
     const int Lne = __builtin_amdgcn_readfirstlane(tab[0]);
 
@@ -909,21 +1256,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_wide_kernel(WgradArgs g) {
         stores_out = true;
     }
 
-    // experts without rows: dW = 0
-    {
-        const int64_t chunks = (int64_t)M * N / 8;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        int j = 0;
-        for (int e = 0; e < g.L; ++e) {
-            if (j < Lne && (__builtin_amdgcn_readfirstlane(tab_x[j]) & 1023) == e) {
-                ++j;
-                continue;
-            }
-            uint16_t* dz = g.dW + (int64_t)e * M * N;
-            for (int64_t c = (int64_t)blockIdx.x * WTHREADS + tid; c < chunks; c += (int64_t)G * WTHREADS)
-                *reinterpret_cast<u32x4*>(dz + c * 8) = z;
-        }
-    }
+    zero_fill_empty(g, tid);
 }
 
 }  // namespace moe
@@ -953,15 +1286,29 @@ extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, 
     // tiles of one operand and 4 of the other instead of all of one.
     const int ft = nfast ? N / BNt : M / BMt;
     const int gf = (ft > 8 && ft % 8 == 0) ? 8 : ft;
-    WgradArgs a{aT, aT_s, bT, bT_s, offsets, L, row_cap, M, N, nfast, gf, dW};
+    WgradArgs a{aT, aT_s, bT, bT_s, offsets, L, row_cap, M, N, nfast, gf, dW, 1, 0x7FFFFFFF, 1};
     const int grid = (num_cus() + 7) / 8 * 8;  // persistent, one block per CU
-    auto go = [&](auto kern) { kern<<<dim3(grid), dim3(WTHREADS), 0, stream>>>(a); };
-    if (wide)
-        go(wgrad_wide_kernel);
-    else if (N % 256 == 0)
-        p2 ? go(wgrad_fp8_kernel<256, true>) : go(wgrad_fp8_kernel<256, false>);
-    else
-        p2 ? go(wgrad_fp8_kernel<128, true>) : go(wgrad_fp8_kernel<128, false>);
+    auto go = [&](auto kern, const WgradArgs& args) { kern<<<dim3(grid), dim3(WTHREADS), 0, stream>>>(args); };
+    if (wide) {
+        go(wgrad_wide_kernel, a);
+    } else if (!p2 && N % 256 == 0 && !(flags & MOE_GEMM_TILE128)) {
+        // experts of at most ARES_KB token blocks keep their A operand in LDS;
+        // any longer ones (only possible when row_cap allows) stream both
+        WgradArgs ar = a;
+        ar.kb_max = ARES_KB;
+        go(wgrad_ares_kernel, ar);
+        MOE_LAUNCH_CHECK("wgrad_ares_kernel");
+        if (row_cap / WBK > ARES_KB) {
+            WgradArgs as = a;
+            as.kb_min = ARES_KB + 1;
+            as.zfill = 0;
+            go(wgrad_fp8_kernel<256, false>, as);
+        }
+    } else if (N % 256 == 0) {
+        p2 ? go(wgrad_fp8_kernel<256, true>, a) : go(wgrad_fp8_kernel<256, false>, a);
+    } else {
+        p2 ? go(wgrad_fp8_kernel<128, true>, a) : go(wgrad_fp8_kernel<128, false>, a);
+    }
     MOE_LAUNCH_CHECK("wgrad_fp8_kernel");
     return MOE_OK;
 }
