@@ -567,8 +567,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
 
 // ---------------------------------------------------------------- A resident
 //
-// fp32 scales on 128 x 256 tiles for experts with at most ARES_KB token
-// blocks.  A unit of work is (expert, m-tile): the unit's A operand, all of
+// 128 x 256 tiles for experts with at most ARES_KB token blocks (fp32 scales,
+// or P2: the E8M0 exponents applied by the block-scaled MFMA).  A unit of work is (expert, m-tile): the unit's A operand, all of
 // the expert's token blocks (16 KB of codes and 512 B of row scales each), is
 // moved into LDS once and stays there while the unit sweeps its n-tiles; only
 // B streams, through a two-stage ring of 33 KB stages.  A K step then moves
@@ -593,6 +593,7 @@ struct AresSmem {
     static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
+template <bool P2>
 __global__ __launch_bounds__(WTHREADS, 1) void wgrad_ares_kernel(WgradArgs g) {
     using SM = AresSmem;
     constexpr int BN = 256, WN = 64, NI = 4;
@@ -638,7 +639,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_ares_kernel(WgradArgs g) {
         const uint32_t b = sbase + SM::RING + (uint32_t)(st * SM::STAGE);
         rB0[st] = b + (wn * WN + l15) * 128 + ((lg ^ l7) << 4);
         rB1[st] = b + (wn * WN + l15) * 128 + (((lg + 4) ^ l7) << 4);
-        rSB[st] = b + SM::B_BYTES + (wn * WN + 4 * lg) * 4;
+        // (P2: the scale of the B row whose K chunk the lane holds)
+        rSB[st] = b + SM::B_BYTES + (wn * WN + (P2 ? l15 : 4 * lg)) * 4;
     }
     // output: the lane's first 16-byte store of subtile mi (whole 128-byte
     // lines, as in wgrad_fp8_kernel): row wm*64 + mi*16 + (l15 & ~1), bytes
@@ -733,6 +735,11 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_ares_kernel(WgradArgs g) {
     float sa[4];  // A scales of the loaded block (rows of this lane)
     v4f sb[NI];   // B scales of the loaded block (4 columns per n-subtile)
     v4f ring[4];  // raw partials awaiting their rescale
+    int ea[4], eb[NI];  // P2: E8M0 exponents of the lane's A rows and B rows
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) ea[mi] = 127;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) eb[ni] = 127;
     auto clear = [&]() {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
@@ -747,6 +754,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_ares_kernel(WgradArgs g) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) sb[ni] = zero4;
     auto flush = [&]() {
+        if constexpr (P2) return;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) acc[mi][NI - 1] += ring[mi] * (sa[mi] * sb[NI - 1]);
     };
@@ -763,9 +771,13 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_ares_kernel(WgradArgs g) {
         const uint32_t pb0 = rB0[st], pb1 = rB1[st], psb = rSB[st];
         const u32x4 sa4 = lds16<0>(psa);
         u32x4 sbn[NI];
+        uint32_t sb1[NI];
         static_for<0, NI>([&](auto nc) {
             constexpr int ni = decltype(nc)::value;
-            sbn[ni] = lds16<ni * 64>(psb);
+            if constexpr (P2)
+                sb1[ni] = lds4<ni * 64>(psb);
+            else
+                sbn[ni] = lds16<ni * 64>(psb);
         });
         static_for<0, 4>([&](auto ic) {
             constexpr int mi = decltype(ic)::value;
@@ -777,13 +789,29 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_ares_kernel(WgradArgs g) {
         });
         flush();  // with the previous block's scales
         const uint32_t sav[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+        if constexpr (P2) {
+            // positive powers of two: the E8M0 code is the exponent field
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) sa[mi] = __uint_as_float(sav[mi]);
+            for (int mi = 0; mi < 4; ++mi) ea[mi] = (int)(sav[mi] >> 23);
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) sb[ni] = __builtin_bit_cast(v4f, sbn[ni]);
+            for (int ni = 0; ni < NI; ++ni) eb[ni] = (int)(sb1[ni] >> 23);
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) sa[mi] = __uint_as_float(sav[mi]);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) sb[ni] = __builtin_bit_cast(v4f, sbn[ni]);
+        }
         wait_lgkm0();
     };
     auto compute = [&]() {
+        if constexpr (P2) {
+            static_for<0, 4 * NI>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                constexpr int ni = j / 4, mi = j % 4;
+                acc[mi][ni] = mfma16x16x128_e8m0(bfr[ni], af[mi], acc[mi][ni], eb[ni], ea[mi]);
+            });
+            return;
+        }
         static_for<0, 4 * NI>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             constexpr int ni = j / 4, mi = j % 4;
@@ -1291,18 +1319,18 @@ extern "C" int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, 
     auto go = [&](auto kern, const WgradArgs& args) { kern<<<dim3(grid), dim3(WTHREADS), 0, stream>>>(args); };
     if (wide) {
         go(wgrad_wide_kernel, a);
-    } else if (!p2 && N % 256 == 0 && !(flags & MOE_GEMM_TILE128)) {
+    } else if (N % 256 == 0 && !(flags & MOE_GEMM_TILE128)) {
         // experts of at most ARES_KB token blocks keep their A operand in LDS;
         // any longer ones (only possible when row_cap allows) stream both
         WgradArgs ar = a;
         ar.kb_max = ARES_KB;
-        go(wgrad_ares_kernel, ar);
+        p2 ? go(wgrad_ares_kernel<true>, ar) : go(wgrad_ares_kernel<false>, ar);
         MOE_LAUNCH_CHECK("wgrad_ares_kernel");
         if (row_cap / WBK > ARES_KB) {
             WgradArgs as = a;
             as.kb_min = ARES_KB + 1;
             as.zfill = 0;
-            go(wgrad_fp8_kernel<256, false>, as);
+            p2 ? go(wgrad_fp8_kernel<256, true>, as) : go(wgrad_fp8_kernel<256, false>, as);
         }
     } else if (N % 256 == 0) {
         p2 ? go(wgrad_fp8_kernel<256, true>, a) : go(wgrad_fp8_kernel<256, false>, a);
