@@ -24,13 +24,19 @@
 //     a new tile never starts on an empty pipeline;
 //   * a finished tile is stored straight from registers while the next
 //     tile's loads are in flight.  Two cross-lane swaps first regroup each
-//     row's columns so that a lane holds 8 consecutive bf16 and every 16-byte
-//     store fills whole 64-byte segments (the MFMA layout would give 32-byte
-//     pieces, twice the write requests).  Stores and loads share the wave's
-//     vector-memory counter, so every wait counts the stores issued after the
-//     awaited stage and never drains them;
+//     row's columns so that a lane holds 8 consecutive bf16, and a pair
+//     exchange between the lanes of adjacent rows lets every store
+//     instruction write whole 128-byte lines.  Stores and loads share the
+//     wave's vector-memory counter, so every wait counts the stores issued
+//     after the awaited stage and never drains them;
 //   * tiles of experts without rows are not in the stream: their dW = 0 is
 //     written by a plain fill after it.
+// Three kernels share this: the streaming one (wgrad_fp8_kernel, both
+// operands through the ring), one that keeps an m-tile's A operand in LDS
+// for experts of up to ARES_KB token blocks (wgrad_ares_kernel: only B
+// streams), and 256 x 256 tiles for power-of-two scales (wgrad_wide_kernel).
+// Where the A-resident kernel applies, a second launch of the streaming one
+// takes the experts with more token blocks.
 // The K step itself is the forward grouped GEMM's: 8 waves in two ping-pong
 // groups (one of each per SIMD), conflict-free swizzled fragments,
 // weights-first MFMA operand order; both operands carry per-row scales, so the
@@ -567,9 +573,10 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
 
 // ---------------------------------------------------------------- A resident
 //
-// 128 x 256 tiles for experts with at most ARES_KB token blocks (fp32 scales,
-// or P2: the E8M0 exponents applied by the block-scaled MFMA).  A unit of work is (expert, m-tile): the unit's A operand, all of
-// the expert's token blocks (16 KB of codes and 512 B of row scales each), is
+// 128 x 256 tiles for experts with at most ARES_KB token blocks (fp32
+// scales, or P2: the E8M0 exponents applied by the block-scaled MFMA).  A
+// unit of work is (expert, m-tile): the unit's A operand, all of the
+// expert's token blocks (16 KB of codes and 512 B of row scales each), is
 // moved into LDS once and stays there while the unit sweeps its n-tiles; only
 // B streams, through a two-stage ring of 33 KB stages.  A K step then moves
 // 32 KB instead of 48, and the 32 workgroups of an XCD, running m-tiles of
