@@ -56,13 +56,20 @@ __global__ __launch_bounds__(PBLOCK) void perm_hist_kernel(const int32_t* __rest
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int nb = expert_bits(L);
     const int64_t base = (int64_t)blockIdx.x * PCHUNK;
-    for (int i = threadIdx.x; i < PCHUNK; i += PBLOCK) {
-        const int64_t p = base + i;
-        int le = -1;
-        if (p < P) {
-            le = ids[p] - e0;
-            if (le < 0 || le >= L) le = -1;
-        }
+    // all of the thread's ids are requested before any is used (a pair past P
+    // reads the last pair's id and is dropped)
+    constexpr int IT = PCHUNK / PBLOCK;
+    int les[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int64_t p = base + it * PBLOCK + threadIdx.x;
+        les[it] = ids[p < P ? p : P - 1];
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int64_t p = base + it * PBLOCK + threadIdx.x;
+        int le = les[it] - e0;
+        if (p >= P || le < 0 || le >= L) le = -1;
         // the first lane of each expert adds the wave's count (distinct addresses)
         const uint64_t m = same_expert(le, nb);
         if (le >= 0 && (m & lt_mask) == 0) atomicAdd(&cnt[le], (int)__popcll(m));
@@ -155,17 +162,20 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int nb = expert_bits(L);
 
-    // the wave's local expert ids, loaded once for both passes (issued before
-    // the bases are formed)
+    // the wave's local expert ids, loaded once for both passes: every load is
+    // issued before any is used and before the bases are formed (a pair past
+    // P reads the last pair's id and is dropped)
     int les[PER_WAVE / 64];
 #pragma unroll
     for (int it = 0; it < PER_WAVE / 64; ++it) {
         const int64_t p = wbase + it * 64 + lane;
-        int le = -1;
-        if (p < P) {
-            le = ids[p] - e0;
-            if (le < 0 || le >= L) le = -1;
-        }
+        les[it] = ids[p < P ? p : P - 1];
+    }
+#pragma unroll
+    for (int it = 0; it < PER_WAVE / 64; ++it) {
+        const int64_t p = wbase + it * 64 + lane;
+        int le = les[it] - e0;
+        if (p >= P || le < 0 || le >= L) le = -1;
         les[it] = le;
     }
     for (int e = threadIdx.x; e < L; e += PBLOCK)
@@ -185,11 +195,24 @@ __global__ __launch_bounds__(PBLOCK) void perm_scatter_kernel(const int32_t* __r
             const int e = e0t + (L <= PBLOCK ? (int)threadIdx.x % L : (int)threadIdx.x);
             const int cs = L <= PBLOCK ? (int)threadIdx.x / L : 0;
             if (e < L && cs < cstep) {
+                // 16 chunk counts requested at a time (indices past the last
+                // chunk read the last one and are not added)
+                constexpr int CB = 16;
                 int a = 0, t = 0;
-                for (int c = cs; c < nchunk; c += cstep) {
-                    const int v = chunk_counts[(int64_t)c * L + e];
-                    t += v;
-                    a += c < (int)blockIdx.x ? v : 0;
+                for (int c0 = cs; c0 < nchunk; c0 += CB * cstep) {
+                    int v[CB];
+#pragma unroll
+                    for (int j = 0; j < CB; ++j) {
+                        const int c = c0 + j * cstep;
+                        v[j] = chunk_counts[(int64_t)(c < nchunk ? c : nchunk - 1) * L + e];
+                    }
+#pragma unroll
+                    for (int j = 0; j < CB; ++j) {
+                        const int c = c0 + j * cstep;
+                        const int w = c < nchunk ? v[j] : 0;
+                        t += w;
+                        a += c < (int)blockIdx.x ? w : 0;
+                    }
                 }
                 atomicAdd(&pre[e], a);
                 atomicAdd(&tot[e], t);

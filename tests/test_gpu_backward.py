@@ -304,7 +304,10 @@ _MANY = [(i * 37) % 300 if i % 7 else 0 for i in range(40)]
     ([128, 256, 0, 5], 128, 128, True, False), (_MANY, 512, 1024, True, False),
     ([0, 1, 130, 300, 700], 512, 256, False, False), ([0, 1, 130, 300, 700], 512, 256, True, False),
     ([0, 1, 130, 300], 256, 512, False, True), (_MANY, 512, 1024, False, True), (_MANY, 512, 1024, True, True),
-    ([0, 1, 130, 300, 700], 384, 512, True, False)])
+    ([0, 1, 130, 300, 700], 384, 512, True, False),
+    # 640 (expert, m-tile) units: the 128 x 256 kernels' persistent workgroups
+    # take two or three each and switch units mid-stream
+    (_MANY, 2048, 256, False, False), (_MANY, 1920, 256, True, False)])
 def test_wgrad(counts, M, N, pow2, tile128):
     k = 2 if len(counts) <= 8 else 8
     E, e0 = max(16, len(counts) + k), 0
