@@ -88,11 +88,39 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     }
 }
 
+// Keys sorted descending in place: Batcher's odd-even merge sort, a fixed
+// network of compare-exchanges (63 for N = 16) that unrolls to straight-line
+// code with independent exchanges at each level.
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&key)[N]) {
+#pragma unroll
+    for (int p = 1; p < N; p <<= 1) {
+#pragma unroll
+        for (int q = p; q >= 1; q >>= 1) {
+#pragma unroll
+            for (int j = q % p; j <= N - 1 - q; j += 2 * q) {
+#pragma unroll
+                for (int i = 0; i <= (q - 1 < N - j - q - 1 ? q - 1 : N - j - q - 1); ++i) {
+                    if ((i + j) / (2 * p) == (i + j + q) / (2 * p)) {
+                        const uint64_t a = key[i + j], b = key[i + j + q];
+                        const bool sw = b > a;
+                        key[i + j] = sw ? b : a;
+                        key[i + j + q] = sw ? a : b;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Sixteen lanes per token row, for E <= 16 * VPL <= 256: lane l of a group
-// holds logits VPL*l .. VPL*l + VPL - 1 (a contiguous run), and k rounds of a
-// 16-lane arg-max over route_key pick the slots in order; a round is VPL local
-// compares and four shuffles instead of six.
-template <int VPL>
+// holds logits VPL*l .. VPL*l + VPL - 1 (a contiguous run) and sorts their
+// route_keys descending.  Pick s is then the 16-lane max of the lanes' first
+// keys (four DPP steps), and the lane that held it moves its next key up: the
+// picks are the row's keys in descending order, one max chain of four steps
+// per pick instead of a scan of VPL keys.  A lane gives up at most k keys, so
+// KT >= min(k, VPL) of its sorted keys are kept.
+template <int VPL, int KT>
 __global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                      int k, int32_t* __restrict__ ids, float* __restrict__ w,
                                                      int32_t* __restrict__ rec, int64_t rec_stride, int64_t s0) {
@@ -125,18 +153,29 @@ __global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ l
         const int e = lane * VPL + i;
         key[i] = e < E ? route_key(v[i], e) : 0ull;
     }
-    uint64_t thr = ~0ull, mine = 0ull;
-    for (int s = 0; s < k; ++s) {
-        uint64_t b = 0ull;
+    sort_desc<VPL>(key);
+    uint64_t h[KT];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) b = (key[i] < thr && key[i] > b) ? key[i] : b;
+    for (int i = 0; i < KT; ++i) h[i] = key[i];
+    uint64_t mine = 0ull;
+    for (int s = 0; s < k; ++s) {
         // max over the 16-lane group: swap neighbours, swap pairs (each lane
         // then holds its quad's max), mirror within 8 lanes, mirror within 16
+        uint64_t b = h[0];
         b = umax64(b, dpp_key<0xB1>(b));
         b = umax64(b, dpp_key<0x4E>(b));
         b = umax64(b, dpp_key<0x141>(b));
         b = umax64(b, dpp_key<0x140>(b));
-        thr = b;
+        // keys are distinct: one lane held b (past the row's keys all hold 0).
+        // The move is a bit blend under an all-ones mask that the optimiser
+        // cannot see through (as selects on the flag it becomes per-lane
+        // index arithmetic with select chains over all KT keys)
+        uint32_t m32 = h[0] == b ? ~0u : 0u;
+        asm volatile("" : "+v"(m32));
+        const uint64_t m = ((uint64_t)m32 << 32) | m32;
+#pragma unroll
+        for (int i = 0; i + 1 < KT; ++i) h[i] = (h[i + 1] & m) | (h[i] & ~m);
+        h[KT - 1] &= ~m;
         if (lane == s) mine = b;
     }
     const float my_val = route_key_value(mine);
@@ -281,16 +320,21 @@ static int launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int
     if (E <= 256) {
         dim3 grid16((unsigned)((T + 15) / 16)), block16(256);
         const int vpl = (E + 15) / 16;
+        auto go = [&](auto kern) {
+            kern<<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+        };
         if (vpl <= 1)
-            topk16_kernel<1><<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+            go(topk16_kernel<1, 1>);
         else if (vpl <= 2)
-            topk16_kernel<2><<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+            go(topk16_kernel<2, 2>);
         else if (vpl <= 4)
-            topk16_kernel<4><<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+            go(topk16_kernel<4, 4>);
         else if (vpl <= 8)
-            topk16_kernel<8><<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+            go(topk16_kernel<8, 8>);
+        else if (k <= 8)
+            go(topk16_kernel<16, 8>);
         else
-            topk16_kernel<16><<<grid16, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+            go(topk16_kernel<16, 16>);
         MOE_LAUNCH_CHECK("topk16_kernel");
         return MOE_OK;
     }
