@@ -187,6 +187,16 @@ enum { MOE_GEMM_TILE128 = 0x400 };
  * ("RL at 1T scale", section "FP8 Training": each GEMM operand quantised along
  * its contraction axis; the 128x128 weight tiles serve both directions).    */
 enum { MOE_GEMM_B_KN = 0x800 };
+/* OR'ed into moe_grouped_gemm_fp8's epilogue (a SwiGLU epilogue, FP8 weights,
+ * not with MOE_GEMM_TILE128): an expert whose last 288-row m-tile would hold
+ * at most 32 rows gets those rows from a K-split product instead (fp32
+ * partials of 4 K blocks each, summed in K order in a second launch, then the
+ * same epilogue), so that no workgroup runs a whole K loop for a few rows.
+ * out3 is then the caller's workspace of moe_grouped_gemm_thin_workspace
+ * bytes (device memory, fp32-aligned); calls that share one workspace must
+ * not overlap.  Results differ from the plain product only in the order of
+ * the fp32 block sums of those rows. */
+enum { MOE_GEMM_THIN_SPLIT = 0x1000 };
 
 /* Quantise src viewed as `groups` matrices of [rows, cols] (row stride ld
  * elements, group stride rows*ld) to OCP e4m3 with one fp32 scale per tile:
@@ -298,6 +308,11 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const uint8_t* b, c
                          const uint16_t* epi_in, void* out, float* out_s,
                          void* out2, float* out2_s, void* out3, float* out3_s,
                          hipStream_t stream);
+
+/* Workspace bytes for MOE_GEMM_THIN_SPLIT with L experts, N = 2f and K:
+ * L * (N/256) * ceil(K/512) * 32 KB (fp32 partials of every expert's
+ * n-tiles and K runs).  N % 256 == 0, K % 128 == 0 (MOE_ERR_SHAPE). */
+int moe_grouped_gemm_thin_workspace(int32_t L, int32_t N, int32_t K, size_t* bytes);
 
 /* Weight-gradient grouped GEMM: for every local expert e,
  *     dW[e][m, n] = sum over the 128-row token blocks b of e's padded segment:

@@ -42,6 +42,7 @@
 //     fragment is the 16 bytes of K block lane/16 and its scale byte, and the
 //     MFMA runs in the mixed fp4 x fp8 form.  Half the weight bytes per step.
 #include "mfma_common.hpp"
+#include "gemm_thin.hpp"
 
 namespace moe {
 
@@ -74,6 +75,7 @@ struct GemmArgs {
     float* out2_s;
     void* out3;
     float* out3_s;
+    int thin;  // 1: thin last m-tiles are left to the K-split launches (gemm_thin.hip)
 };
 constexpr bool is_swiglu(int epi) {
     return epi == MOE_EPI_SWIGLU_Q8 || epi == MOE_EPI_SWIGLU_Q8_SAVE || epi == MOE_EPI_SWIGLU_F32;
@@ -697,10 +699,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
     using SM = WideSmem<WF4, WBM>;
     static_assert(!WF4 || P2, "MXFP4 weights take the hardware-scale path");
     static_assert(!BKN || (!WF4 && !is_swiglu(EPI)), "[K, N] weights: FP8 dgrad products only");
+    static_assert(!is_swiglu(EPI) || WBM == THIN_WBM, "thin-tile rule of the SwiGLU products");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[SM::TOTAL];
     __shared__ int tile_base[GMAXL + 1];
-    __shared__ int scan_tmp[GTHREADS];
+    __shared__ int64_t scan_tmp[GTHREADS];  // per-thread m-tiles (low word), thin tiles (high word)
     __shared__ float rowmax[4][WBM];
     __shared__ __attribute__((aligned(8))) float bscale[GMAXKB][2];
 
@@ -712,14 +715,17 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
     const int NT = N / WBN;
     const int f = N / 2;
 
-    // ---- tile list: per expert ceil(real rows / 288) m-tiles x NT n-tiles
+    // ---- tile list: per expert ceil(real rows / 288) m-tiles x NT n-tiles.
+    // g.thin: when the experts' thin last m-tiles (thin_rows_of) would add a
+    // round of tiles for the G workgroups, they are left out here and the
+    // K-split launches (gemm_thin.hip, the same rule) take them.
     {
-        int loc[2];
-        int sum = 0;
+        int loc[2], tloc[2];
+        int64_t sum = 0;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int e = tid * 2 + i;
-            int m = 0;
+            int m = 0, t = 0;
             if (e < L) {
                 int64_t lo = g.offsets[e], hi = g.offsets[e + 1];
                 if (lo > g.row_cap) lo = g.row_cap;
@@ -727,26 +733,31 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 int64_t rows = g.counts[e];
                 if (rows > hi - lo) rows = hi - lo;
                 m = rows > 0 ? (int)((rows + WBM - 1) / WBM) : 0;
+                t = (is_swiglu(EPI) && g.thin && thin_rows_of(rows) > 0) ? 1 : 0;
             }
             loc[i] = m;
-            sum += m;
+            tloc[i] = t;
+            sum += m + ((int64_t)t << 32);
         }
         scan_tmp[tid] = sum;
         __syncthreads();
         for (int off = 1; off < GTHREADS; off <<= 1) {
-            int add = tid >= off ? scan_tmp[tid - off] : 0;
+            const int64_t add = tid >= off ? scan_tmp[tid - off] : 0;
             __syncthreads();
             scan_tmp[tid] += add;
             __syncthreads();
         }
-        int run = scan_tmp[tid] - sum;
+        const int64_t tot = scan_tmp[GTHREADS - 1];
+        const bool split = thin_split_active((int)(tot & 0xFFFFFFFF), (int)(tot >> 32), NT, (int)gridDim.x);
+        const int64_t before = scan_tmp[tid] - sum;
+        int run = (int)(before & 0xFFFFFFFF) - (split ? (int)(before >> 32) : 0);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int e = tid * 2 + i;
             if (e < L) tile_base[e] = run * NT;
-            run += loc[i];
+            run += loc[i] - (split ? tloc[i] : 0);
         }
-        if (tid == 0) tile_base[L] = scan_tmp[GTHREADS - 1] * NT;
+        if (tid == 0) tile_base[L] = ((int)(tot & 0xFFFFFFFF) - (split ? (int)(tot >> 32) : 0)) * NT;
         __syncthreads();
     }
     const int total = tile_base[L];
@@ -1350,7 +1361,8 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
     const bool wf4 = (epilogue & MOE_WEIGHT_MXFP4) != 0;
     const bool tile128 = (epilogue & MOE_GEMM_TILE128) != 0;
     const bool bkn = (epilogue & MOE_GEMM_B_KN) != 0;
-    epilogue &= ~(MOE_SCALE_POW2 | MOE_WEIGHT_MXFP4 | MOE_GEMM_TILE128 | MOE_GEMM_B_KN);
+    const bool thin = (epilogue & MOE_GEMM_THIN_SPLIT) != 0;
+    epilogue &= ~(MOE_SCALE_POW2 | MOE_WEIGHT_MXFP4 | MOE_GEMM_TILE128 | MOE_GEMM_B_KN | MOE_GEMM_THIN_SPLIT);
     MOE_REQUIRE(!wf4 || p2, MOE_ERR_UNSUPPORTED, "grouped_gemm: MXFP4 weights need MOE_SCALE_POW2 activations");
     MOE_REQUIRE(!bkn || (!wf4 && !tile128 && N % 256 == 0 &&
                          (epilogue == MOE_EPI_STORE_BF16 || epilogue == MOE_EPI_STORE_F32)),
@@ -1372,8 +1384,12 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
                 "grouped_gemm: SWIGLU_Q8_SAVE needs out_s and out2");
     MOE_REQUIRE((row_cap / GBM) * (N / 128) < ((int64_t)1 << 31), MOE_ERR_SHAPE,
                 "grouped_gemm: row_cap * N too large for the tile list");
+    MOE_REQUIRE(!thin || (swiglu && !wf4 && !tile128), MOE_ERR_UNSUPPORTED,
+                "grouped_gemm: MOE_GEMM_THIN_SPLIT needs a SwiGLU epilogue, FP8 weights and 288-row tiles");
+    MOE_REQUIRE(!thin || out3, MOE_ERR_NULL, "grouped_gemm: MOE_GEMM_THIN_SPLIT needs the workspace in out3");
     if (row_cap == 0) return MOE_OK;
-    GemmArgs ga{a, a_s, b, b_s, counts, offsets, L, row_cap, N, K, epi_in, out, out_s, out2, out2_s, out3, out3_s};
+    GemmArgs ga{a, a_s, b, b_s, counts, offsets, L, row_cap, N, K, epi_in, out, out_s, out2, out2_s, out3, out3_s,
+                thin ? 1 : 0};
     const bool wide = N % 256 == 0;
     switch (epilogue) {
         case MOE_EPI_STORE_BF16:
@@ -1383,11 +1399,25 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* a_s, const ui
             return wide ? launch_gemm<256, MOE_EPI_STORE_F32>(ga, p2, wf4, !tile128, stream, bkn)
                         : launch_gemm<128, MOE_EPI_STORE_F32>(ga, p2, wf4, !tile128, stream);
         case MOE_EPI_SWIGLU_Q8:
-            return launch_gemm<256, MOE_EPI_SWIGLU_Q8>(ga, p2, wf4, !tile128, stream);
         case MOE_EPI_SWIGLU_Q8_SAVE:
-            return launch_gemm<256, MOE_EPI_SWIGLU_Q8_SAVE>(ga, p2, wf4, !tile128, stream);
-        case MOE_EPI_SWIGLU_F32:
-            return launch_gemm<256, MOE_EPI_SWIGLU_F32>(ga, p2, wf4, !tile128, stream);
+        case MOE_EPI_SWIGLU_F32: {
+            const int rc = epilogue == MOE_EPI_SWIGLU_Q8
+                               ? launch_gemm<256, MOE_EPI_SWIGLU_Q8>(ga, p2, wf4, !tile128, stream)
+                           : epilogue == MOE_EPI_SWIGLU_Q8_SAVE
+                               ? launch_gemm<256, MOE_EPI_SWIGLU_Q8_SAVE>(ga, p2, wf4, !tile128, stream)
+                               : launch_gemm<256, MOE_EPI_SWIGLU_F32>(ga, p2, wf4, !tile128, stream);
+            if (rc != MOE_OK || !thin) return rc;
+            return moe_thin_launch(a, a_s, b, b_s, counts, offsets, L, row_cap, N, K, epilogue, p2,
+                                   static_cast<float*>(out3), out, out_s, out2, stream);
+        }
     }
     return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm: epilogue %d", epilogue);
+}
+
+extern "C" int moe_grouped_gemm_thin_workspace(int32_t L, int32_t N, int32_t K, size_t* bytes) {
+    MOE_REQUIRE(bytes, MOE_ERR_NULL, "grouped_gemm_thin_workspace: NULL bytes");
+    MOE_REQUIRE(L >= 1 && L <= GMAXL && N > 0 && N % 256 == 0 && K > 0 && K % 128 == 0 && K / 128 <= GMAXKB,
+                MOE_ERR_SHAPE, "grouped_gemm_thin_workspace: bad L=%d, N=%d or K=%d", L, N, K);
+    *bytes = moe_thin_workspace_bytes(L, N, K);
+    return MOE_OK;
 }

@@ -166,10 +166,11 @@ __global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ l
         b = umax64(b, dpp_key<0x4E>(b));
         b = umax64(b, dpp_key<0x141>(b));
         b = umax64(b, dpp_key<0x140>(b));
-        // keys are distinct: one lane held b (past the row's keys all hold 0).
-        // The move is a bit blend under an all-ones mask that the optimiser
-        // cannot see through (as selects on the flag it becomes per-lane
-        // index arithmetic with select chains over all KT keys)
+        // keys are distinct, so exactly one lane held b (a lane whose keys
+        // ran out holds 0, and with k <= E no pick is 0).  The move is a bit
+        // blend under an all-ones mask that the optimiser cannot see through
+        // (as selects on the flag it becomes per-lane index arithmetic with
+        // select chains over all KT keys)
         uint32_t m32 = h[0] == b ? ~0u : 0u;
         asm volatile("" : "+v"(m32));
         const uint64_t m = ((uint64_t)m32 << 32) | m32;

@@ -99,6 +99,8 @@ class ForwardPlan:
         self.hq = torch.empty((R, f), dtype=u8, device=dv)
         self.hq_s = torch.empty((f // 128, R), dtype=f32, device=dv)
         self.gu = torch.empty((R, 2 * f), dtype=b16, device=dv) if save_gu else None
+        # workspace of GEMM1's K-split thin m-tiles (FP8 weights)
+        self.thin_ws = None if mxfp4 else torch.empty(ops.thin_workspace(L, 2 * f, d), dtype=u8, device=dv)
         self.Y = torch.empty((R, d), dtype=b16, device=dv)
         self.y = torch.empty((T, d), dtype=b16, device=dv)
 
@@ -126,9 +128,10 @@ class ForwardPlan:
 
     def gemm1(self, wts):
         epi = ops.EPI_SWIGLU_Q8_SAVE if self.gu is not None else ops.EPI_SWIGLU_Q8
+        thin = ops.GEMM_THIN_SPLIT if self.thin_ws is not None else 0
         _call("moe_grouped_gemm_fp8", _p(self.xq), _p(self.xq_s), _p(wts["w13q"]), _p(wts["w13s"]),
-              _p(self.counts), _p(self.offsets), self.L, self.rcap, 2 * self.f, self.d, epi | self.gflag, None,
-              _p(self.hq), _p(self.hq_s), _p(self.gu), None, None, None, _stream())
+              _p(self.counts), _p(self.offsets), self.L, self.rcap, 2 * self.f, self.d, epi | self.gflag | thin, None,
+              _p(self.hq), _p(self.hq_s), _p(self.gu), None, _p(self.thin_ws), None, _stream())
 
     def gemm2(self, wts):
         _call("moe_grouped_gemm_fp8", _p(self.hq), _p(self.hq_s), _p(wts["w2q"]), _p(wts["w2s"]),

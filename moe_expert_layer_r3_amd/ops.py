@@ -20,6 +20,7 @@ SCALE_POW2 = 0x100  # power-of-two (UE8M0) tile scales, OR'ed into tile / epilog
 WEIGHT_MXFP4 = 0x200  # MXFP4 weights, OR'ed (with SCALE_POW2) into a GEMM epilogue
 GEMM_TILE128 = 0x400  # 128 x 256 GEMM tiles instead of 256 x 256, OR'ed into a GEMM epilogue
 GEMM_B_KN = 0x800     # weights given as [L, K, N] (a dgrad product on the forward weights), OR'ed likewise
+GEMM_THIN_SPLIT = 0x1000  # thin last 288-row m-tiles of a SwiGLU product split along K (workspace in out3)
 SRC_BF16, SRC_F32 = 0, 1
 FLAG_BAD_ID, FLAG_DUP_ID, FLAG_ROW_CAP = 1, 2, 4
 ROW_ALIGN = 128
@@ -54,6 +55,7 @@ _SIGS = {
     "moe_quant_fp8_rows_t": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _I64, _P, _P, _I32, _P]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32,
                                             _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_grouped_gemm_thin_workspace": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "moe_grouped_gemm_fp8_wgrad": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _I32, _P]),
     "moe_swiglu_backward": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                            _I32, _P]),
@@ -194,6 +196,13 @@ def permute_workspace(T, k, L):
     return n.value
 
 
+def thin_workspace(L, N, K):
+    """Bytes of the workspace of a SwiGLU product with GEMM_THIN_SPLIT."""
+    n = _SZ(0)
+    _call("moe_grouped_gemm_thin_workspace", L, N, K, ctypes.byref(n))
+    return n.value
+
+
 def permute(ids, e0, L, rcap=None, x=None, x_perm=False, quant=True, status=None, ws=None, pow2=False):
     """Expert-grouped permutation (+ optional fused gather / 1x128 quant of x,
     with power-of-two scales when pow2).
@@ -319,7 +328,7 @@ def quant_rows_t(src, w, row_pair, offsets, L, rcap, k, pow2=False):
 # ---------------------------------------------------------------- GEMMs
 
 def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_in=None, rcap=None, pow2=False,
-                 mxfp4=False, tile128=False, b_kn=False):
+                 mxfp4=False, tile128=False, b_kn=False, thin_ws=None):
     """Per-expert blockwise-scaled FP8 GEMM over the expert-grouped rows.
 
     a [rcap, K] u8, a_s [K/128, rcap]; b [L, N, K] u8, b_s [L, N/128, K/128].
@@ -331,7 +340,10 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
     product, read without a transposed copy; FP8, store epilogues, N % 256 == 0).
     Returns the epilogue's outputs: STORE_BF16 -> y; STORE_F32 -> acc;
     SWIGLU_Q8 -> (hq, hq_s); SWIGLU_Q8_SAVE -> (hq, hq_s, gu);
-    SWIGLU_F32 -> h."""
+    SWIGLU_F32 -> h.
+    thin_ws (SwiGLU epilogues, FP8 weights, 288-row tiles): a device buffer of
+    thin_workspace(L, N, K) bytes; thin last m-tiles (at most 32 rows) are then
+    computed split along K."""
     rcap = a.shape[0] if rcap is None else rcap
     if mxfp4:
         L, kb, N, _ = b.shape
@@ -362,10 +374,14 @@ def grouped_gemm(a, a_s, b, b_s, counts, offsets, epilogue=EPI_STORE_BF16, epi_i
         res = out
     else:
         raise ValueError(f"unknown epilogue {epilogue}")
+    if thin_ws is not None:
+        if thin_ws.numel() * thin_ws.element_size() < thin_workspace(L, N, K):
+            raise ValueError("thin_ws is smaller than thin_workspace(L, N, K)")
+        out3 = thin_ws
     _call("moe_grouped_gemm_fp8", _p(a), _p(a_s), _p(b), _p(b_s), _p(counts), _p(offsets), L, rcap, N, K,
           epilogue | _flag(pow2) | (WEIGHT_MXFP4 if mxfp4 else 0) | (GEMM_TILE128 if tile128 else 0)
-          | (GEMM_B_KN if b_kn else 0), _p(epi_in), _p(out), _p(out_s), _p(out2), _p(out2_s), _p(out3), _p(out3_s),
-          _stream(dev))
+          | (GEMM_B_KN if b_kn else 0) | (GEMM_THIN_SPLIT if thin_ws is not None else 0), _p(epi_in), _p(out),
+          _p(out_s), _p(out2), _p(out2_s), _p(out3), _p(out3_s), _stream(dev))
     return res
 
 

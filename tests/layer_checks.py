@@ -48,10 +48,12 @@ def rows_of(t, rows):
     return np64(sub) if sub.is_floating_point() else npi(sub)
 
 
-def gemm1_h32(xq, xq_s, w13q, w13s, counts, offsets, pow2=False, mxfp4=False):
+def gemm1_h32(xq, xq_s, w13q, w13s, counts, offsets, pow2=False, mxfp4=False, thin_ws=None):
     """The GPU's fp32 h = silu(G) * U before quantisation: the same grouped GEMM
-    with the SWIGLU_F32 inspection epilogue."""
-    return ops.grouped_gemm(xq, xq_s, w13q, w13s, counts, offsets, ops.EPI_SWIGLU_F32, pow2=pow2, mxfp4=mxfp4)
+    with the SWIGLU_F32 inspection epilogue (and, with the plan's thin_ws, the
+    same K-split path for thin last m-tiles as the plan's GEMM1)."""
+    return ops.grouped_gemm(xq, xq_s, w13q, w13s, counts, offsets, ops.EPI_SWIGLU_F32, pow2=pow2, mxfp4=mxfp4,
+                            thin_ws=thin_ws)
 
 
 def expert_weights_checked(e, W13e, W2e, wts=None, pow2=False, mxfp4=False):
@@ -207,7 +209,7 @@ def full_size_forward_check(wl, experts, pow2=False, mxfp4=False, n_rows=24, tok
     if experts is None:
         experts = (int(np.argmax(c)), int(np.argsort(c)[len(c) // 2]), int(np.argmin(c)))
     h32 = gemm1_h32(plan.xq, plan.xq_s, wts["w13q"], wts["w13s"], plan.counts, plan.offsets,
-                    pow2=pow2 or mxfp4, mxfp4=mxfp4)
+                    pow2=pow2 or mxfp4, mxfp4=mxfp4, thin_ws=plan.thin_ws)
     check_layer_forward(wl, x, W13, W2, plan, h32, experts, wts=wts, pow2=pow2, mxfp4=mxfp4,
                         n_rows=n_rows, tok_stride=tok_stride, tag=wl.name)
     say(f"{wl.name} sampled parity ok")

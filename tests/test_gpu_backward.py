@@ -554,7 +554,8 @@ def test_layer_train_full_size_sampled(pow2):
     assert np.array_equal(npi(plan.counts), c) and np.array_equal(npi(plan.offsets), o)
     assert np.array_equal(npi(plan.pair_row), pr)
     say("train: indices bit-exact; forward stages (GEMM1 saving G/U, GEMM2, combine) on sampled rows")
-    h32 = LC.gemm1_h32(plan.xq, plan.xq_s, wts["w13q"], wts["w13s"], plan.counts, plan.offsets, pow2=pow2)
+    h32 = LC.gemm1_h32(plan.xq, plan.xq_s, wts["w13q"], wts["w13s"], plan.counts, plan.offsets, pow2=pow2,
+                       thin_ws=plan.thin_ws)
     LC.check_layer_forward(wl, x, W13, W2, plan, h32, (0, 13, 31), wts=wts, pow2=pow2, save_gu=True, n_rows=16,
                            tok_stride=131, tag="train")
     del h32, W13, W2
@@ -720,7 +721,8 @@ def test_tiny_train_end_to_end_explained(pow2):
     act_t = lambda v: OQ.quant_128x1_t(v, real, pow2=pow2)
     say("1. rounding points fed by identical FP8 operands")
     assert np.array_equal(npi(plan.xq)[rr], fw["Xa"][0][rr])
-    h32 = np64(LC.gemm1_h32(plan.xq, plan.xq_s, wts["w13q"], wts["w13s"], plan.counts, plan.offsets, pow2=pow2))
+    h32 = np64(LC.gemm1_h32(plan.xq, plan.xq_s, wts["w13q"], wts["w13s"], plan.counts, plan.offsets, pow2=pow2,
+                            thin_ws=plan.thin_ws))
     hq_o, hs_o = fw["ha"]
     _flips("h 1x128", npi(plan.hq)[rr], npi(plan.hq_s).T[rr], hq_o[rr], hs_o[rr], h32[rr], fw["h"][rr], 1)
     # the saved bf16 G, U: the GPU rounds its own fp32 accumulators (the

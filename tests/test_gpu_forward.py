@@ -238,6 +238,42 @@ def _gemm_problem(counts, K, N, seed, e0=0, E=64, k=8):
     return res, wq, ws, L
 
 
+def _ids_exact(counts, k, E, rng):
+    """ids [T, k], T = ceil(sum / k), distinct per token, whose local experts
+    0..L-1 receive exactly `counts` pairs (any number of experts may share a
+    token): the sorted multiset of local labels is dealt column-wise over the
+    tokens, so an expert's at most T labels land on distinct tokens, and the
+    free slots take distinct non-local experts."""
+    L = len(counts)
+    n = sum(counts)
+    T = max(-(-n // k), max(counts), 1)
+    assert E - L >= k
+    ids = np.full((T, k), -1, dtype=np.int32)
+    labels = np.repeat(np.arange(L, dtype=np.int32), counts)
+    for p, e in enumerate(labels):
+        ids[p % T, p // T] = e
+    pool = np.arange(L, E, dtype=np.int32)
+    for t in range(T):
+        free = ids[t] < 0
+        ids[t, free] = rng.choice(pool, int(free.sum()), replace=False)
+        rng.shuffle(ids[t])
+    return ids
+
+
+def _gemm_problem_exact(counts, K, N, seed, E=128, k=8):
+    """_gemm_problem with exactly `counts` rows per expert for any number of experts."""
+    rng = np.random.default_rng(seed)
+    L = len(counts)
+    ids = _ids_exact(counts, k, E, rng)
+    T = ids.shape[0]
+    x = obf16(rng.standard_normal((T, K)))
+    res = ops.permute(gpu(ids), 0, L, x=bf16_tensor(x))
+    assert np.array_equal(npi(res["counts"]), np.asarray(counts))
+    W = obf16(rng.standard_normal((L, N, K)) * 0.02)
+    wq, ws = ops.quant_fp8(bf16_tensor(W), tile=ops.TILE_128x128)
+    return res, wq, ws, L
+
+
 def _real_rows(res):
     o = npi(res["offsets"])
     c = npi(res["counts"])
@@ -305,6 +341,84 @@ def test_gemm_swiglu(counts, K, f, tile128):
     assert np.array_equal(npi(hs).T[rows].astype(np.float64), sref)
     assert np.array_equal(npi(hq2)[rows], npi(hq)[rows]) and np.array_equal(npi(hs2).T[rows], npi(hs).T[rows])
     assert rel_fro(np64(gu)[rows], obf16(GU[rows])) <= TOL
+
+
+def _thin_rows(res):
+    """Rows of the thin last m-tiles: an expert's last 288-row tile holding at
+    most 32 rows (the whole expert when it has at most 32)."""
+    o, c = npi(res["offsets"]), npi(res["counts"])
+    out = []
+    for e in range(len(c)):
+        r = int(c[e])
+        if r == 0:
+            continue
+        last = r - 288 * ((r + 287) // 288 - 1)
+        if last <= 32:
+            out.extend(range(int(o[e]) + r - last, int(o[e]) + r))
+    return np.array(out, dtype=np.int64)
+
+
+def _main_grid():
+    """Workgroups of the persistent grouped GEMM: one per CU, a multiple of 8."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    return (ncu + 7) // 8 * 8
+
+
+def _thin_round_counts(f):
+    """Expert sizes whose thin last m-tiles add a round of tiles to the main
+    product's grid: G / NT experts' worth of full 288-row tiles, then an
+    expert of 289 rows (one full tile and a 1-row thin one) and one of 5."""
+    nt = 2 * f // 256
+    return [288] * (_main_grid() // nt - 1) + [289, 5]
+
+
+# GEMM_THIN_SPLIT: thin last m-tiles (at most 32 rows past a multiple of 288,
+# or an expert of at most 32 rows).  Where they add a round of tiles ("round"
+# cases, sized from the grid) they come from the K-split launches (K = 640 is
+# two runs of 4 K blocks, the last one partial; K = 1152 three); otherwise
+# the main product keeps them.  Against the oracle, and against the plain
+# product, whose other rows must come out bit for bit the same.
+@pytest.mark.parametrize("counts,K,f", [([300, 289, 320, 5, 577, 0, 288, 33], 1024, 256),
+                                        ([300, 289, 320, 5, 577, 0, 288, 33], 2176, 128),
+                                        ([31, 865, 600], 1152, 256),
+                                        ("round", 640, 4096), ("round", 1152, 1024)])
+def test_gemm_swiglu_thin_split(counts, K, f):
+    split = counts == "round"
+    if split:
+        res, wq, ws, L = _gemm_problem_exact(_thin_round_counts(f), K, 2 * f, seed=K + f + 7)
+    else:
+        res, wq, ws, L = _gemm_problem(counts, K, 2 * f, seed=K + f + 7)
+    say(f"gemm SWIGLU thin split counts={counts} K={K} f={f}")
+    args = (res["xq"], res["xq_s"], wq, ws, res["counts"], res["offsets"])
+    tw = torch.empty(ops.thin_workspace(L, 2 * f, K), dtype=torch.uint8, device=DEV)
+    h32 = ops.grouped_gemm(*args, ops.EPI_SWIGLU_F32, thin_ws=tw)
+    hq, hs = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8, thin_ws=tw)
+    hq2, hs2, gu = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8_SAVE, thin_ws=tw)
+    h32_plain = ops.grouped_gemm(*args, ops.EPI_SWIGLU_F32)
+    hq_plain, hs_plain = ops.grouped_gemm(*args, ops.EPI_SWIGLU_Q8)
+    c, o = npi(res["counts"]), npi(res["offsets"])
+    GU = OG.grouped_forward(npi(res["xq"]), npi(res["xq_s"]).T, c, o, npi(wq), npi(ws))
+    G, U = of32(GU[:, :f]), of32(GU[:, f:])
+    h_ref = OL.silu(G) * U
+    rows, thin = _real_rows(res), _thin_rows(res)
+    assert thin.size > 0
+    assert rel_fro(np64(h32)[rows], h_ref[rows]) <= ACC_TOL
+    assert rel_fro(np64(h32)[thin], h_ref[thin]) <= ACC_TOL
+    qref, sref = OQ.quant_1x128(np64(h32)[rows])
+    assert np.array_equal(npi(hq)[rows], qref)
+    assert np.array_equal(npi(hs).T[rows].astype(np.float64), sref)
+    assert np.array_equal(npi(hq2)[rows], npi(hq)[rows]) and np.array_equal(npi(hs2).T[rows], npi(hs).T[rows])
+    assert rel_fro(np64(gu)[rows], obf16(GU[rows])) <= TOL
+    assert rel_fro(np64(gu)[thin], obf16(GU[thin])) <= TOL
+    # rows outside the thin tiles come from the same tiles of the main product
+    rest = np.setdiff1d(rows, thin)
+    assert np.array_equal(npi(h32)[rest].view(np.int32), npi(h32_plain)[rest].view(np.int32))
+    assert np.array_equal(npi(hq)[rest], npi(hq_plain)[rest])
+    assert np.array_equal(npi(hs).T[rest], npi(hs_plain).T[rest])
+    # the thin rows: from the K-split launches (another order of the fp32
+    # block sums) exactly in the "round" cases, else from the main product
+    same = np.array_equal(npi(h32)[thin].view(np.int32), npi(h32_plain)[thin].view(np.int32))
+    assert same != split
 
 
 # ------------------------------------------------------------------ combine

@@ -62,7 +62,8 @@ def test_replay_chunk_full_size(record, layer, chunk):
     say(f"replay layer {layer} chunk {chunk}: {int(c.sum())} local pairs (counts {c.max()}..{c.min()}), "
         "indices bit-exact")
     experts = (int(np.argmax(c)), int(np.argsort(c)[len(c) // 2]), int(np.argmin(c)))
-    h32 = LC.gemm1_h32(plan.xq, plan.xq_s, wts["w13q"], wts["w13s"], plan.counts, plan.offsets)
+    h32 = LC.gemm1_h32(plan.xq, plan.xq_s, wts["w13q"], wts["w13s"], plan.counts, plan.offsets,
+                       thin_ws=plan.thin_ws)
     LC.check_layer_forward(wl, x, W13, W2, plan, h32, experts, wts=wts, n_rows=16, tok_stride=211,
                            tag=f"replay l{layer} c{chunk}")
 
