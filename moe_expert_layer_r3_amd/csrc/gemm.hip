@@ -1161,12 +1161,17 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
             issue_a(sbase, krot(0, cur), cur);
         }
 
-        const int lg = lane >> 4;
+        // the epilogue's lane indices, from an opaque copy of the lane id: its
+        // per-lane row and address terms are then formed here, once per tile,
+        // instead of being hoisted above the K loop, where they held registers
+        // through it (the SwiGLU variants spilled them)
+        const int lane_e = (int)opaque((uint32_t)lane);
+        const int lg = lane_e >> 4, l15e = lane_e & 15;
         if constexpr (EPI == MOE_EPI_STORE_F32) {
             float* out = static_cast<float*>(g.out);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
-                const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15;
+                const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15e;
                 if (r >= ep.real_end) continue;
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni)
@@ -1182,7 +1187,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
             uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
-                const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15;
+                const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15e;
                 uint32_t x[NI], y[NI];  // columns (0, 1) and (2, 3) of each subtile, packed bf16
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni) {
@@ -1209,7 +1214,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 float* out = static_cast<float*>(g.out);
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi) {
-                    const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15;
+                    const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15e;
                     if (r >= ep.real_end) continue;
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni) {
@@ -1225,7 +1230,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 uint16_t* out2 = static_cast<uint16_t*>(g.out2);
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi) {
-                    const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15;
+                    const int64_t r = ep.row0 + wm * WWR + mi * 16 + l15e;
                     float m = 0.f;
                     if constexpr (EPI == MOE_EPI_SWIGLU_Q8_SAVE) {
                         // G and U as bf16, regrouped like the bf16 store
@@ -1266,13 +1271,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                     }
                     m = fmaxf(m, __shfl_xor(m, 16));
                     m = fmaxf(m, __shfl_xor(m, 32));
-                    if (lg == 0) rowmax[wn][wm * WWR + mi * 16 + l15] = m;
+                    if (lg == 0) rowmax[wn][wm * WWR + mi * 16 + l15e] = m;
                 }
                 lds_barrier();
                 uint8_t* out = static_cast<uint8_t*>(g.out);
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi) {
-                    const int rt = wm * WWR + mi * 16 + l15;
+                    const int rt = wm * WWR + mi * 16 + l15e;
                     const int64_t r = ep.row0 + rt;
                     const float am = fmaxf(fmaxf(rowmax[0][rt], rowmax[1][rt]), fmaxf(rowmax[2][rt], rowmax[3][rt]));
                     const TileScale ts = tile_scale_t<P2>(am);
@@ -1297,9 +1302,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
     }
 }
 
-// Every variant takes 288-row tiles.  The SwiGLU epilogues with FP8 weights
-// compile with 2-6 spilled registers, all of them saved before the K loop and
-// restored in the epilogue (once per tile), which costs nothing measurable.
+// Every variant takes 288-row tiles and compiles without spilled registers
+// (218-250 VGPRs).
 template <int EPI, bool P2, bool WF4, bool BKN>
 constexpr int wide_mi() {
     return 9;
