@@ -198,6 +198,149 @@ __global__ __launch_bounds__(256) void topk16_kernel(const float* __restrict__ l
     }
 }
 
+// The same routing order as a double.  For ord = the high word of route_key
+// (the float's order-preserving bits, NaN -> 1) the 64-bit pattern
+// 2^62 + ord * 2^30 + (1023 - e) is a positive, normal, finite IEEE double
+// (its exponent field is 0x400 + the top ten bits of ord, at most 0x7FE
+// because no non-NaN float maps above 0xFF800000), and such doubles order as
+// their bit patterns do: by ord, then by the lower id.  A compare-exchange is
+// then one v_max_f64 and one v_min_f64, with no lane mask and no select.
+// 0.0 marks "no candidate" and sits below every key.  Needs e < 1024.
+__device__ __forceinline__ double route_dkey(float x, int e) {
+    const uint32_t u = __float_as_uint(x + 0.0f);
+    uint32_t ord = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+    ord = x != x ? 1u : ord;
+    const uint32_t hi = __builtin_amdgcn_alignbit(1u, ord, 2);  // 0x40000000 | ord >> 2
+    const uint32_t lo = (ord << 30) | (uint32_t)(1023 - e);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint32_t route_dkey_ord(double d) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, d);
+    return ((uint32_t)(b >> 32) << 2) | ((uint32_t)b >> 30);
+}
+__device__ __forceinline__ int route_dkey_id(double d) {
+    return 1023 - (int)((uint32_t)__builtin_bit_cast(uint64_t, d) & 0x3FFu);
+}
+__device__ __forceinline__ float route_ord_value(uint32_t ord) {
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+__device__ __forceinline__ void dce(double& a, double& b) {
+    const double x = a, y = b;
+    a = __builtin_fmax(x, y);
+    b = __builtin_fmin(x, y);
+}
+
+// Eight keys sorted descending: Batcher's odd-even merge sort (19 exchanges).
+__device__ __forceinline__ void dsort8(double* k) {
+#pragma unroll
+    for (int p = 1; p < 8; p <<= 1)
+#pragma unroll
+        for (int q = p; q >= 1; q >>= 1)
+#pragma unroll
+            for (int j = q % p; j <= 7 - q; j += 2 * q)
+#pragma unroll
+                for (int i = 0; i <= (q - 1 < 7 - j - q ? q - 1 : 7 - j - q); ++i)
+                    if ((i + j) / (2 * p) == (i + j + q) / (2 * p)) dce(k[i + j], k[i + j + q]);
+}
+
+// The eight largest of two descending runs of eight, descending: the
+// elementwise max of a and b reversed holds exactly the top eight of the
+// union as a bitonic sequence, which three half-cleaner stages sort.
+__device__ __forceinline__ void dmerge8(double* a, const double* b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fmax(a[i], b[7 - i]);
+#pragma unroll
+    for (int s = 4; s >= 1; s >>= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if ((i & s) == 0) dce(a[i], a[i + s]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_dkey(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Eight lanes per token row, for 128 < E <= 256 and k <= 8.  Lane p of a
+// group holds the 32 logits 32j + 4p + c (j < 8, c < 4): each of its eight
+// 16-byte loads is one eighth of a 128-byte run of the row that the group
+// reads whole.  The lane sorts its keys in four runs of eight and merges them
+// down to its top eight; three exchanges across the group (DPP xor 1, xor 2,
+// mirror within 8) each merge a lane's top eight with a partner's holding the
+// other half of the candidates, after which every lane of the group holds
+// the row's top eight in order.  Lane p keeps slot p.
+template <bool FULL>
+__global__ __launch_bounds__(256) void topk_merge_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                         int k, int32_t* __restrict__ ids, float* __restrict__ w,
+                                                         int32_t* __restrict__ rec, int64_t rec_stride,
+                                                         int64_t s0) {
+    const int p = threadIdx.x & 7;
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 3) + (threadIdx.x >> 3);
+    // every lane takes part in the exchanges; rows past T compute on row 0 and store nothing
+    const bool live = row < T;
+    const float* src = logits + (live ? row : 0) * E;
+    double g[32];
+    if (FULL) {
+        // E == 256: every lane's 32 candidates are in the row
+        float4 q[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[j] = *reinterpret_cast<const float4*>(src + 32 * j + 4 * p);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int e = 32 * j + 4 * p;
+            g[4 * j] = route_dkey(q[j].x, e);
+            g[4 * j + 1] = route_dkey(q[j].y, e + 1);
+            g[4 * j + 2] = route_dkey(q[j].z, e + 2);
+            g[4 * j + 3] = route_dkey(q[j].w, e + 3);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            const int e = 32 * (r >> 2) + 4 * p + (r & 3);
+            const int ec = e < E ? e : E - 1;
+            const uint64_t b = __builtin_bit_cast(uint64_t, route_dkey(src[ec], ec));
+            g[r] = __builtin_bit_cast(double, e < E ? b : 0ull);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dsort8(g + 8 * r);
+    dmerge8(g, g + 8);
+    dmerge8(g + 16, g + 24);
+    dmerge8(g, g + 16);
+    double o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = dpp_dkey<0xB1>(g[i]);  // lane xor 1
+    dmerge8(g, o);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = dpp_dkey<0x4E>(g[i]);  // lane xor 2
+    dmerge8(g, o);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = dpp_dkey<0x141>(g[i]);  // lane 7 - p
+    dmerge8(g, o);
+    double mine = g[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mine = p == i ? g[i] : mine;
+    const float m = route_ord_value(route_dkey_ord(g[0]));
+    const float my_val = route_ord_value(route_dkey_ord(mine));
+    const float ex = p < k ? expf(my_val - m) : 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float o2 = __shfl(ex, j, 8);
+        if (j < k) sum += o2;
+    }
+    if (live && p < k) {
+        const int my_id = route_dkey_id(mine);
+        ids[row * k + p] = my_id;
+        w[row * k + p] = ex / sum;
+        if (rec) rec[(int64_t)p * rec_stride + s0 + row] = my_id;
+    }
+}
+
 // One thread per token: read the k recorded ids (coalesced along the sequence
 // for each slot), validate, gather the k logits, softmax.
 __global__ __launch_bounds__(256) void replay_kernel(const int32_t* __restrict__ rec, int k, int64_t S,
@@ -332,8 +475,13 @@ static int launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int
             go(topk16_kernel<4, 4>);
         else if (vpl <= 8)
             go(topk16_kernel<8, 8>);
-        else if (k <= 8)
-            go(topk16_kernel<16, 8>);
+        else if (k <= 8) {
+            dim3 grid8((unsigned)((T + 31) / 32));
+            if (E == 256)
+                topk_merge_kernel<true><<<grid8, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+            else
+                topk_merge_kernel<false><<<grid8, block16, 0, stream>>>(logits, T, E, k, ids, w, rec, rec_stride, s0);
+        }
         else
             go(topk16_kernel<16, 16>);
         MOE_LAUNCH_CHECK("topk16_kernel");

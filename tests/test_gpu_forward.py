@@ -91,7 +91,9 @@ def test_quant_128x128_and_transpose():
 @pytest.mark.parametrize("T,E,k,mode", [(1000, 256, 8, "normal"), (333, 200, 16, "normal"), (65, 8, 2, "normal"),
                                         (7, 1, 1, "normal"), (257, 64, 6, "ties"), (40, 130, 5, "zeros"),
                                         (300, 64, 6, "special"), (200, 256, 8, "special"),
-                                        (50, 300, 5, "special"), (64, 1000, 16, "normal")])
+                                        (50, 300, 5, "special"), (64, 1000, 16, "normal"),
+                                        (513, 256, 8, "ties"), (77, 200, 3, "ties"), (64, 256, 1, "normal"),
+                                        (45, 252, 8, "special"), (100, 129, 8, "normal"), (96, 256, 7, "zeros")])
 def test_topk(T, E, k, mode):
     rng = np.random.default_rng(T * 7 + E)
     if mode == "special":
