@@ -8,6 +8,15 @@
 
 namespace moe {
 
+// Workgroups are dealt to the chip's 8 XCDs in turn (workgroup i to XCD i % 8).
+// For a grid of n tiles with n % 8 == 0, the tile that workgroup bid takes so
+// that XCD x runs the x-th contiguous eighth of the tiles in order: tiles that
+// are neighbours in memory then run side by side in one XCD (and its L2)
+// rather than spread over all eight.
+__device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t n) {
+    return (n & 7) ? bid : (bid & 7) * (n >> 3) + (bid >> 3);
+}
+
 // ---------------------------------------------------------------- host side
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();

@@ -62,7 +62,11 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restri
     __shared__ __attribute__((aligned(16))) uint8_t tile_t[128][128 + 8];
     const int64_t rb_n = rows >> 7, cb_n = cols >> 7;
     const int64_t g = blockIdx.z;
-    const int64_t rb = blockIdx.y, cb = blockIdx.x;
+    // tiles in row-major order, contiguous per XCD: the tiles one XCD runs side
+    // by side cover whole rows of the source (adjacent 256-byte pieces of each
+    // row) instead of every eighth piece
+    const int64_t lin = xcd_tile((int64_t)blockIdx.y * cb_n + blockIdx.x, rb_n * cb_n);
+    const int64_t rb = lin / cb_n, cb = lin - rb * cb_n;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = lane & 15, rq = wave * 4 + (lane >> 4);
     const int c8 = cg * 8;
