@@ -36,7 +36,8 @@ struct SwigluBwdArgs {
     float* h_f32;
 };
 
-// One block per (128-row block, 128-column block of f); 256 threads.  Thread
+// One block per (128-row block, 128-column block of f), the column block the
+// grid's fast index; 256 threads.  Thread
 // (wave w, lane l) covers rows 8*rq .. 8*rq + 7 of the block, rq = 4w + l/16,
 // and columns 8*cg .. +7 of the f-block, cg = l % 16, for all three results:
 //   * the 16 lanes of a row share its 1x128 tiles (a 16-lane max);
@@ -50,7 +51,9 @@ template <bool P2>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs a) {
     __shared__ __attribute__((aligned(16))) float cmax[3][4][128];
     __shared__ __attribute__((aligned(16))) uint8_t tile_t[3][128][128 + 8];
-    const int64_t b = blockIdx.x, cb = blockIdx.y;
+    // column blocks fastest: workgroups launched together take neighbouring
+    // column blocks of the same rows
+    const int64_t b = blockIdx.y, cb = blockIdx.x;
     int64_t total = a.offsets[a.L];
     if (total > a.row_cap) total = a.row_cap;
     if (b * 128 >= total) return;  // whole block leaves together
@@ -203,7 +206,8 @@ extern "C" int moe_swiglu_backward(const float* dH, const uint16_t* gu, const in
     if (row_cap == 0) return MOE_OK;
     SwigluBwdArgs args{dH, gu, row_pair, offsets, L, row_cap, f, dgu_q, dgu_s, dgu_qT, dgu_sT,
                        h_qT, h_sT, dgu_f32, h_f32};
-    const dim3 grid((unsigned)(row_cap / 128), (unsigned)(f / 128));
+    MOE_REQUIRE(row_cap / 128 <= 65535, MOE_ERR_SHAPE, "swiglu_backward: row_cap too large");
+    const dim3 grid((unsigned)(f / 128), (unsigned)(row_cap / 128));
     if (flags)
         swiglu_bwd_kernel<true><<<grid, 256, 0, stream>>>(args);
     else
