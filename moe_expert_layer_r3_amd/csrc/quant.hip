@@ -93,7 +93,9 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restri
         uint2 out;
         out.x = cvt_e4m3x4(v[j][0] * ts.inv, v[j][1] * ts.inv, v[j][2] * ts.inv, v[j][3] * ts.inv);
         out.y = cvt_e4m3x4(v[j][4] * ts.inv, v[j][5] * ts.inv, v[j][6] * ts.inv, v[j][7] * ts.inv);
-        *reinterpret_cast<uint2*>(q + qbase + (rb * 128 + rq * 8 + j) * cols + cb * 128 + c8) = out;
+        // streaming store: the codes are not read again before they leave the caches
+        __builtin_nontemporal_store(((uint64_t)out.y << 32) | out.x,
+                                    reinterpret_cast<uint64_t*>(q + qbase + (rb * 128 + rq * 8 + j) * cols + cb * 128 + c8));
     }
     if (tid == 0) {
         s[(g * rb_n + rb) * cb_n + cb] = ts.s;
