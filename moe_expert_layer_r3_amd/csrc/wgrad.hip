@@ -48,6 +48,11 @@
 
 namespace moe {
 
+// dW leaves with streaming (non-temporal) stores: it is written once and not
+// read again in the step, so its lines need not stay dirty in L2 and the
+// last-level cache for the kernels that follow
+__device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
 constexpr int WBM = 128;  // tile rows (M); tile columns BN = 256 or 128
 constexpr int WBK = 128;  // tokens per K step (one quantisation block)
 constexpr int WTHREADS = 512;
@@ -111,7 +116,7 @@ __device__ __forceinline__ void zero_fill_empty(const WgradArgs& g, int tid) {
         if (hi - lo >= WBK) continue;
         uint16_t* d = g.dW + (int64_t)e * g.M * g.N;
         for (int64_t c = (int64_t)blockIdx.x * WTHREADS + tid; c < chunks; c += (int64_t)gridDim.x * WTHREADS)
-            *reinterpret_cast<u32x4*>(d + c * 8) = z;
+            st_stream(reinterpret_cast<u32x4*>(d + c * 8), z);
     }
 }
 
@@ -463,10 +468,10 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_fp8_kernel(WgradArgs g) {
                 u32x4 r;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) r[c] = (uint32_t)__builtin_amdgcn_mov_dpp((int)snd[c], 0xB1, 0xF, 0xF, false);
-                *reinterpret_cast<u32x4*>(d + o_off[mi]) = odd_row ? r : p0;
-                *reinterpret_cast<u32x4*>(d + o_off[mi] + 2 * N) = odd_row ? p1 : r;
+                st_stream(reinterpret_cast<u32x4*>(d + o_off[mi]), odd_row ? r : p0);
+                st_stream(reinterpret_cast<u32x4*>(d + o_off[mi] + 2 * N), odd_row ? p1 : r);
             } else {
-                *reinterpret_cast<u32x4*>(d + o_off[mi]) = u32x4{x[0], y[0], x[1], y[1]};
+                st_stream(reinterpret_cast<u32x4*>(d + o_off[mi]), u32x4{x[0], y[0], x[1], y[1]});
             }
         });
         clear();
@@ -852,8 +857,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_ares_kernel(WgradArgs g) {
             u32x4 r;
 #pragma unroll
             for (int c = 0; c < 4; ++c) r[c] = (uint32_t)__builtin_amdgcn_mov_dpp((int)snd[c], 0xB1, 0xF, 0xF, false);
-            *reinterpret_cast<u32x4*>(d + o_off[mi]) = odd_row ? r : p0;
-            *reinterpret_cast<u32x4*>(d + o_off[mi] + 2 * N) = odd_row ? p1 : r;
+            st_stream(reinterpret_cast<u32x4*>(d + o_off[mi]), odd_row ? r : p0);
+            st_stream(reinterpret_cast<u32x4*>(d + o_off[mi] + 2 * N), odd_row ? p1 : r);
         });
         clear();
     };
@@ -1285,8 +1290,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void wgrad_wide_kernel(WgradArgs g) {
             u32x4 r;
 #pragma unroll
             for (int c = 0; c < 4; ++c) r[c] = (uint32_t)__builtin_amdgcn_mov_dpp((int)snd[c], 0xB1, 0xF, 0xF, false);
-            *reinterpret_cast<u32x4*>(drow + o_lane) = odd_row ? r : p0;
-            *reinterpret_cast<u32x4*>(drow + o_lane + 2 * N) = odd_row ? p1 : r;
+            st_stream(reinterpret_cast<u32x4*>(drow + o_lane), odd_row ? r : p0);
+            st_stream(reinterpret_cast<u32x4*>(drow + o_lane + 2 * N), odd_row ? p1 : r);
         }
         stores_out = true;
     }
