@@ -79,7 +79,8 @@ int64_t moe_row_cap(int64_t T, int32_t k, int32_t L);
  * by the lower expert id, with IEEE comparison (-0 == +0); ids[t, 0] is the
  * largest.  Gates w[t, j] = softmax of the k selected logits (the full softmax
  * renormalised over the selection).  Logits must be finite.
- * Outputs: ids [T, k] int32, w [T, k] fp32.  T = 0 is a no-op.             */
+ * Outputs: ids [T, k] int32, w [T, k] fp32.  T = 0 is a no-op.
+ * MOE_ERR_SHAPE unless 0 <= T <= 2^33, 1 <= E <= 1024, 1 <= k <= min(16, E).  */
 int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
                    int32_t* ids, float* w, hipStream_t stream);
 

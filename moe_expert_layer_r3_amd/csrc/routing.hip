@@ -505,7 +505,9 @@ static int launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, int
 }
 
 static int check_topk_args(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids, float* w) {
-    MOE_REQUIRE(T >= 0 && T <= (int64_t)1 << 40, MOE_ERR_SHAPE, "route_topk: bad T=%lld", (long long)T);
+    // up to 2^33 rows: every launch shape (at least 4 rows per workgroup)
+    // stays within the 2^31 - 1 workgroups of a grid dimension
+    MOE_REQUIRE(T >= 0 && T <= (int64_t)1 << 33, MOE_ERR_SHAPE, "route_topk: bad T=%lld", (long long)T);
     MOE_REQUIRE(E >= 1 && E <= 1024, MOE_ERR_SHAPE, "route_topk: E=%d outside [1, 1024]", E);
     MOE_REQUIRE(k >= 1 && k <= MAXK && k <= E, MOE_ERR_SHAPE, "route_topk: k=%d outside [1, min(16, E)]", k);
     MOE_REQUIRE(T == 0 || (logits && ids && w), MOE_ERR_NULL, "route_topk: NULL logits/ids/w");
