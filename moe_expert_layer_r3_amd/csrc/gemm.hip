@@ -799,6 +799,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         const float* bs_lo;
         const float* bs_hi;
         int rot;
+        int bnt;                        // 1: the expert has one m-tile, so no other tile reads these weight rows
         int na;                         // A DMA segments of this (DMA) wave inside a_lim (0..WASEG)
         int nmi;                        // 16-row subtiles of this wave with real rows (0..MI)
     };
@@ -861,6 +862,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         ti.bs_lo = bsx + (BKN ? (int64_t)blk0 : (int64_t)blk0 * nkb);
         ti.bs_hi = bsx + (BKN ? (int64_t)blk1 : (int64_t)blk1 * nkb);
         ti.rot = ((mt & 1) * 2 + (nt & 3) * 2) % nkb;
+        ti.bnt = mt_e == 1;
         return ti;
     };
     // the tile's two B scale rows (nkb <= GMAXKB <= 2 * GTHREADS: one load
@@ -931,8 +933,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
                 }
             } else {
                 const uint8_t* bb = ti.b_base + kr * GBK + brow_off * K;
+                // weight rows that only this tile reads (one m-tile in the
+                // expert) stream past the caches: measured 2-3% faster at that
+                // shape, and 4-5% slower where a second m-tile re-reads them
+                if (ti.bnt) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dma16s(bb, b_off0 + (uint32_t)(8 * i * K), sB + (w * 4 + i) * 1024);
+                    for (int i = 0; i < 4; ++i) dma16s_nt(bb, b_off0 + (uint32_t)(8 * i * K), sB + (w * 4 + i) * 1024);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dma16s(bb, b_off0 + (uint32_t)(8 * i * K), sB + (w * 4 + i) * 1024);
+                }
             }
         };
         if (dma_self) one(wave, 0);

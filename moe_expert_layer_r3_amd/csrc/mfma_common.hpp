@@ -33,6 +33,10 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
+// the same with the non-temporal hint, for operand bytes no other tile reads
+__device__ __forceinline__ void dma16s_nt(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
 __device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, uint32_t lds) {
     asm volatile("global_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
