@@ -914,8 +914,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_wide_kernel(GemmArgs g) {
         auto one = [&](int w, int64_t brow_off) {
             if constexpr (WF4) {
                 const uint8_t* bb = ti.b_base + (int64_t)kr * N * 64 + brow_off * 64;
+                if (ti.bnt) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i) dma16s(bb, b_off0 + 1024 * i, sB + (w * 2 + i) * 1024);
+                    for (int i = 0; i < 2; ++i) dma16s_nt(bb, b_off0 + 1024 * i, sB + (w * 2 + i) * 1024);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) dma16s(bb, b_off0 + 1024 * i, sB + (w * 2 + i) * 1024);
+                }
                 if (lane < 32)
                     dma4s(ti.bsm + (int64_t)kr * N * 4 + brow_off * 4, bs_off, sB + SM::B_BYTES + SM::S_BYTES + w * 128);
             } else if constexpr (BKN) {
