@@ -350,7 +350,8 @@ int moe_grouped_gemm_fp8_wgrad(const uint8_t* aT, const float* aT_s, const uint8
  *                                                      the fp32 values quantised
  * Padding rows (row_pair < 0) are 0 in the 128x1 tiles and are not written in
  * the row-major outputs; rows at and past offsets[L] are not touched at all.
- *   dH [row_cap, f] fp32, gu [row_cap, 2f] bf16, row_pair [row_cap]; f % 128 == 0.
+ *   dH [row_cap, f] fp32, gu [row_cap, 2f] bf16, row_pair [row_cap]; f % 128 == 0,
+ *   row_cap % 128 == 0 and row_cap / 128 <= 65535 (MOE_ERR_SHAPE otherwise).
  * flags: 0, or MOE_SCALE_POW2 for power-of-two scales on every output.        */
 int moe_swiglu_backward(const float* dH, const uint16_t* gu, const int32_t* row_pair,
                         const int32_t* offsets, int32_t L, int64_t row_cap, int32_t f,
